@@ -1,0 +1,168 @@
+"""Float64 CPU oracle for the Hyena long-convolution chain.
+
+TEST INFRASTRUCTURE ONLY.  The test suite, the package smoke check and the
+benchmark's CPU-baseline leg are the only code allowed to import this module.
+The GPU library never imports, links or calls it, and it imports nothing from
+the GPU package.  The arithmetic lives in ``oracle.c`` (plain C, OpenMP over
+independent (batch, channel) units); this module only builds it with gcc and
+marshals numpy float64 arrays through ctypes.
+
+Functions follow the pages cited in ``oracle.c``:
+  * ``causal_conv(z, h, D, method)``  -- [P2] "The primitive" / [P1] "FFTConv"
+  * ``hyena1d(u, gates, h, D, method)`` -- [P1] "The Hyena operator", [P2]
+    "The Toeplitz picture" (gate after each convolution)
+  * ``conv2d`` / ``hyena2d`` -- [P3] "How HyenaND works", non-causal zero-padded
+    2D convolution on the native grid
+  * ``fft`` -- [P2] "Counting the cost" radix-2 FFT
+  * ``circular_conv`` -- [P2] "Linear vs circular" (the unpadded contrast)
+
+Every function has at least one pin in ``tests/test_oracle_pins.py`` that does
+not go through this code (printed worked example, numpy routines, closed
+forms, invariants).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lock = threading.Lock()
+_lib = None
+
+DIRECT = 0
+FFT = 1
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle.c into liboracle.so with gcc (-O2, OpenMP)."""
+    if force or not os.path.exists(_LIB_PATH):
+        tmp = _LIB_PATH + ".tmp"
+        cmd = ["gcc", "-O2", "-std=c99", "-fopenmp", "-fPIC", "-shared",
+               "-o", tmp, _SRC, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(_LIB_PATH) or (
+                    os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC)):
+                build(force=True)
+            lib = ctypes.CDLL(_LIB_PATH)
+            i64, i32, p = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p
+            lib.oracle_fft.argtypes = [i64, p, p, ctypes.c_int]
+            lib.oracle_fft.restype = ctypes.c_int
+            lib.oracle_causal_conv_direct.argtypes = [i64, i64, i64, p, p, p, p]
+            lib.oracle_causal_conv_direct.restype = None
+            lib.oracle_causal_conv_fft.argtypes = [i64, i64, i64, p, p, p, p]
+            lib.oracle_causal_conv_fft.restype = ctypes.c_int
+            lib.oracle_circular_conv_fft.argtypes = [i64, i64, i64, p, p, p]
+            lib.oracle_circular_conv_fft.restype = ctypes.c_int
+            lib.oracle_hyena1d.argtypes = [i64, i64, i64, i32, p, p, p, p, p, i32]
+            lib.oracle_hyena1d.restype = ctypes.c_int
+            lib.oracle_conv2d_direct.argtypes = [i64, i64, i64, i64, p, p, p, p]
+            lib.oracle_conv2d_direct.restype = None
+            lib.oracle_conv2d_fft.argtypes = [i64, i64, i64, i64, p, p, p, p]
+            lib.oracle_conv2d_fft.restype = ctypes.c_int
+            lib.oracle_hyena2d.argtypes = [i64, i64, i64, i64, i32, p, p, p, p, p, i32]
+            lib.oracle_hyena2d.restype = ctypes.c_int
+            _lib = lib
+    return _lib
+
+
+def _f64(a) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(a, dtype=np.float64))
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def fft(x, inverse: bool = False) -> np.ndarray:
+    """Unscaled radix-2 DFT of a complex vector (sign -1 forward, +1 inverse)."""
+    x = np.asarray(x, dtype=np.complex128)
+    re = np.ascontiguousarray(x.real.copy())
+    im = np.ascontiguousarray(x.imag.copy())
+    rc = _load().oracle_fft(re.size, _ptr(re), _ptr(im), +1 if inverse else -1)
+    if rc != 0:
+        raise ValueError("length must be a power of two")
+    return re + 1j * im
+
+
+def causal_conv(z, h, D, method: int = DIRECT) -> np.ndarray:
+    """w[b,t,c] = sum_{s<=t} h[c,s] z[b,t-s,c] + D[c] z[b,t,c]; z [B,N,d], h [d,N]."""
+    z, h, D = _f64(z), _f64(h), _f64(D)
+    B, N, d = z.shape
+    assert h.shape == (d, N) and D.shape == (d,)
+    w = np.empty_like(z)
+    lib = _load()
+    if method == DIRECT:
+        lib.oracle_causal_conv_direct(B, N, d, _ptr(z), _ptr(h), _ptr(D), _ptr(w))
+    else:
+        if lib.oracle_causal_conv_fft(B, N, d, _ptr(z), _ptr(h), _ptr(D), _ptr(w)) != 0:
+            raise MemoryError("oracle_causal_conv_fft failed")
+    return w
+
+
+def circular_conv(z, h) -> np.ndarray:
+    """Unpadded length-N circular convolution (the wrap-around contrast)."""
+    z, h = _f64(z), _f64(h)
+    B, N, d = z.shape
+    w = np.empty_like(z)
+    if _load().oracle_circular_conv_fft(B, N, d, _ptr(z), _ptr(h), _ptr(w)) != 0:
+        raise ValueError("N must be a power of two")
+    return w
+
+
+def hyena1d(u, gates, h, D, method: int = DIRECT) -> np.ndarray:
+    """Order-N chain: u [B,N,d], gates [order,B,N,d], h [order,d,N], D [order,d]."""
+    u, gates, h, D = _f64(u), _f64(gates), _f64(h), _f64(D)
+    B, N, d = u.shape
+    order = gates.shape[0]
+    assert gates.shape == (order, B, N, d)
+    assert h.shape == (order, d, N) and D.shape == (order, d)
+    y = np.empty_like(u)
+    rc = _load().oracle_hyena1d(B, N, d, order, _ptr(u), _ptr(gates), _ptr(h), _ptr(D),
+                                _ptr(y), method)
+    if rc != 0:
+        raise MemoryError("oracle_hyena1d failed")
+    return y
+
+
+def conv2d(z, K, D, method: int = DIRECT) -> np.ndarray:
+    """Non-causal 2D conv: z [B,X,Y,d], K [d,2X-1,2Y-1] (offset (i,j) at (i+X-1,j+Y-1))."""
+    z, K, D = _f64(z), _f64(K), _f64(D)
+    B, X, Y, d = z.shape
+    assert K.shape == (d, 2 * X - 1, 2 * Y - 1) and D.shape == (d,)
+    w = np.empty_like(z)
+    lib = _load()
+    if method == DIRECT:
+        lib.oracle_conv2d_direct(B, X, Y, d, _ptr(z), _ptr(K), _ptr(D), _ptr(w))
+    else:
+        if lib.oracle_conv2d_fft(B, X, Y, d, _ptr(z), _ptr(K), _ptr(D), _ptr(w)) != 0:
+            raise MemoryError("oracle_conv2d_fft failed")
+    return w
+
+
+def hyena2d(u, gates, K, D, method: int = DIRECT) -> np.ndarray:
+    """2D chain: u [B,X,Y,d], gates [order,B,X,Y,d], K [order,d,2X-1,2Y-1], D [order,d]."""
+    u, gates, K, D = _f64(u), _f64(gates), _f64(K), _f64(D)
+    B, X, Y, d = u.shape
+    order = gates.shape[0]
+    assert gates.shape == (order, B, X, Y, d)
+    assert K.shape == (order, d, 2 * X - 1, 2 * Y - 1) and D.shape == (order, d)
+    y = np.empty_like(u)
+    rc = _load().oracle_hyena2d(B, X, Y, d, order, _ptr(u), _ptr(gates), _ptr(K), _ptr(D),
+                                _ptr(y), method)
+    if rc != 0:
+        raise MemoryError("oracle_hyena2d failed")
+    return y

@@ -1,0 +1,368 @@
+/*
+ * oracle.c -- plain float64 CPU reference for the Hyena operator's long
+ * convolution chain (1D causal and 2D non-causal).
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the GPU library links, includes or
+ * calls this file, and this file uses nothing from the GPU library.  Only the
+ * test suite, the package smoke check and the benchmark's CPU-baseline leg may
+ * load it.  It is deliberately slow and literal: every function is the
+ * definition written out, with no blocking, fusion or reordering beyond what
+ * the definition states.
+ *
+ * Sources (the pages this follows):
+ *   [P1] "Week 11: Hyena, Long Convolution, and Linear Attention", sections
+ *        "The Hyena operator" (order-N chain of long convolutions and gates)
+ *        and "FFTConv" (causal sum plus the feedthrough b_d u_{b,t,d};
+ *        zero-pad to twice the length, multiply spectra, invert, truncate).
+ *   [P2] "Hyena -- Long Convolutions Math", sections "The primitive" (causal
+ *        sum, depthwise over channels), "The Toeplitz picture" (order-2 form
+ *        x2 . (h2 * (x1 . (h1 * v)))), "The convolution theorem" and
+ *        "Linear vs circular" (padding to 2N rounded up to a power of two,
+ *        keep the first N outputs), "Counting the cost" (radix-2 FFT).
+ *   [P3] "How HyenaND works", section "The convolution theorem (FFT)" (the
+ *        ND FFT convolution on the native grid) and the worked trace's
+ *        zero padding with is_causal=False (non-causal linear 2D conv).
+ *
+ * Layouts (row-major, channels last):
+ *   1D: z, u, gates[n], y : [B][N][d];  h : [order][d][N];  D : [order][d]
+ *   2D: z, u, gates[n], y : [B][X][Y][d];
+ *       K : [order][d][2X-1][2Y-1], tap at signed offset (i, j) stored at
+ *       index (i + X - 1, j + Y - 1);  D : [order][d]
+ *
+ * Parity pins (all in tests/): the printed worked example of [P2] "Linear vs
+ * circular"; numpy.convolve / numpy.fft / the O(M^2) DFT definition; closed
+ * forms (impulse, step response of a damped sinusoid, extreme tap, 2D delta
+ * shifts, separable kernels); invariants (causality, linearity, shift
+ * equivariance, channel independence); direct vs FFT routes.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#ifndef M_PI
+#define M_PI 3.14159265358979323846
+#endif
+
+static int64_t next_pow2(int64_t n)
+{
+    int64_t m = 1;
+    while (m < n) m <<= 1;
+    return m;
+}
+
+static int is_pow2(int64_t n) { return n > 0 && (n & (n - 1)) == 0; }
+
+/* ------------------------------------------------------------------------ */
+/* Radix-2 FFT ([P2] "Counting the cost")                                    */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * In-place iterative radix-2 decimation-in-time DFT of length n (a power of
+ * two).  sign = -1 computes X[k] = sum_t x[t] exp(-2 pi i k t / n);
+ * sign = +1 computes the same sum with exp(+2 pi i k t / n) (no 1/n scale).
+ * Bit-reversal permutation first, then log2(n) butterfly stages.  Every
+ * twiddle is computed from its own angle with cos/sin in double; there is no
+ * recurrence.  Returns 0, or -1 if n is not a power of two.
+ */
+int oracle_fft(int64_t n, double* re, double* im, int sign)
+{
+    if (!is_pow2(n)) return -1;
+    /* bit reversal */
+    for (int64_t i = 1, j = 0; i < n; ++i) {
+        int64_t bit = n >> 1;
+        for (; j & bit; bit >>= 1) j ^= bit;
+        j ^= bit;
+        if (i < j) {
+            double t = re[i]; re[i] = re[j]; re[j] = t;
+            t = im[i]; im[i] = im[j]; im[j] = t;
+        }
+    }
+    for (int64_t len = 2; len <= n; len <<= 1) {
+        int64_t half = len >> 1;
+        for (int64_t start = 0; start < n; start += len) {
+            for (int64_t k = 0; k < half; ++k) {
+                double ang = sign * 2.0 * M_PI * (double)k / (double)len;
+                double wr = cos(ang), wi = sin(ang);
+                int64_t a = start + k, b = start + k + half;
+                double tr = re[b] * wr - im[b] * wi;
+                double ti = re[b] * wi + im[b] * wr;
+                re[b] = re[a] - tr;
+                im[b] = im[a] - ti;
+                re[a] += tr;
+                im[a] += ti;
+            }
+        }
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* 1D causal depthwise convolution with skip                                 */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * Direct sum ([P2] "The primitive"; [P1] "FFTConv" equation):
+ *   w[b,t,c] = sum_{s=0}^{t} h[c,s] * z[b,t-s,c]  +  D[c] * z[b,t,c]
+ * summed in ascending s.  h holds N taps per channel; tap s multiplies the
+ * input s steps in the past (s = 0 is the current token).
+ */
+void oracle_causal_conv_direct(int64_t B, int64_t N, int64_t d, const double* z,
+                               const double* h, const double* D, double* w)
+{
+#pragma omp parallel for collapse(2) schedule(dynamic)
+    for (int64_t b = 0; b < B; ++b)
+        for (int64_t c = 0; c < d; ++c)
+            for (int64_t t = 0; t < N; ++t) {
+                double acc = 0.0;
+                for (int64_t s = 0; s <= t; ++s)
+                    acc += h[c * N + s] * z[(b * N + (t - s)) * d + c];
+                w[(b * N + t) * d + c] = acc + D[c] * z[(b * N + t) * d + c];
+            }
+}
+
+/*
+ * The same result through the convolution theorem ([P2] "The convolution
+ * theorem", "Linear vs circular"; [P1] "FFTConv"): pad z[b,:,c] and h[c,:]
+ * with zeros to M = the power of two >= 2N, transform both, multiply bin by
+ * bin, invert with the 1/M scale, keep the first N outputs, add D[c] z.
+ * Real data is carried as complex with zero imaginary part.
+ */
+int oracle_causal_conv_fft(int64_t B, int64_t N, int64_t d, const double* z,
+                           const double* h, const double* D, double* w)
+{
+    const int64_t M = next_pow2(2 * N);
+    int fail = 0;
+#pragma omp parallel
+    {
+        double* xr = (double*)malloc(sizeof(double) * M);
+        double* xi = (double*)malloc(sizeof(double) * M);
+        double* hr = (double*)malloc(sizeof(double) * M);
+        double* hi = (double*)malloc(sizeof(double) * M);
+        if (!xr || !xi || !hr || !hi) {
+#pragma omp atomic write
+            fail = 1;
+        } else {
+#pragma omp for collapse(2) schedule(dynamic)
+            for (int64_t b = 0; b < B; ++b)
+                for (int64_t c = 0; c < d; ++c) {
+                    for (int64_t t = 0; t < M; ++t) {
+                        xr[t] = t < N ? z[(b * N + t) * d + c] : 0.0;
+                        hr[t] = t < N ? h[c * N + t] : 0.0;
+                        xi[t] = 0.0;
+                        hi[t] = 0.0;
+                    }
+                    oracle_fft(M, xr, xi, -1);
+                    oracle_fft(M, hr, hi, -1);
+                    for (int64_t k = 0; k < M; ++k) {
+                        double pr = xr[k] * hr[k] - xi[k] * hi[k];
+                        double pi = xr[k] * hi[k] + xi[k] * hr[k];
+                        xr[k] = pr;
+                        xi[k] = pi;
+                    }
+                    oracle_fft(M, xr, xi, +1);
+                    for (int64_t t = 0; t < N; ++t)
+                        w[(b * N + t) * d + c] =
+                            xr[t] / (double)M + D[c] * z[(b * N + t) * d + c];
+                }
+        }
+        free(xr); free(xi); free(hr); free(hi);
+    }
+    return fail ? -1 : 0;
+}
+
+/*
+ * Length-N circular convolution with no padding, kept only to show what the
+ * padding prevents ([P2] "Linear vs circular": the wrapped term at t = 0).
+ *   w[b,t,c] = sum_{s=0}^{N-1} h[c,(t-s) mod N] * z[b,s,c]   (N a power of 2)
+ */
+int oracle_circular_conv_fft(int64_t B, int64_t N, int64_t d, const double* z,
+                             const double* h, double* w)
+{
+    if (!is_pow2(N)) return -1;
+    double* xr = (double*)malloc(sizeof(double) * N);
+    double* xi = (double*)malloc(sizeof(double) * N);
+    double* hr = (double*)malloc(sizeof(double) * N);
+    double* hi = (double*)malloc(sizeof(double) * N);
+    if (!xr || !xi || !hr || !hi) { free(xr); free(xi); free(hr); free(hi); return -1; }
+    for (int64_t b = 0; b < B; ++b)
+        for (int64_t c = 0; c < d; ++c) {
+            for (int64_t t = 0; t < N; ++t) {
+                xr[t] = z[(b * N + t) * d + c]; xi[t] = 0.0;
+                hr[t] = h[c * N + t];          hi[t] = 0.0;
+            }
+            oracle_fft(N, xr, xi, -1);
+            oracle_fft(N, hr, hi, -1);
+            for (int64_t k = 0; k < N; ++k) {
+                double pr = xr[k] * hr[k] - xi[k] * hi[k];
+                double pi = xr[k] * hi[k] + xi[k] * hr[k];
+                xr[k] = pr; xi[k] = pi;
+            }
+            oracle_fft(N, xr, xi, +1);
+            for (int64_t t = 0; t < N; ++t) w[(b * N + t) * d + c] = xr[t] / (double)N;
+        }
+    free(xr); free(xi); free(hr); free(hi);
+    return 0;
+}
+
+/*
+ * Order-N Hyena chain ([P1] "The Hyena operator"; [P2] "The Toeplitz
+ * picture", order-2 form):
+ *   z_0 = u;  z_n = gates[n-1] . (h_n * z_{n-1} + D_n z_{n-1});  y = z_order
+ * The gate multiplies the output of each convolution (gate n after conv n).
+ * method 0 = direct sum, 1 = FFT route.  Returns 0 on success.
+ */
+int oracle_hyena1d(int64_t B, int64_t N, int64_t d, int32_t order, const double* u,
+                   const double* gates, const double* h, const double* D, double* y,
+                   int32_t method)
+{
+    const int64_t E = B * N * d;
+    double* z = (double*)malloc(sizeof(double) * E);
+    double* w = (double*)malloc(sizeof(double) * E);
+    if (!z || !w) { free(z); free(w); return -1; }
+    memcpy(z, u, sizeof(double) * E);
+    int rc = 0;
+    for (int32_t n = 0; n < order && rc == 0; ++n) {
+        const double* hn = h + (int64_t)n * d * N;
+        const double* Dn = D + (int64_t)n * d;
+        if (method == 0)
+            oracle_causal_conv_direct(B, N, d, z, hn, Dn, w);
+        else
+            rc = oracle_causal_conv_fft(B, N, d, z, hn, Dn, w);
+        const double* g = gates + (int64_t)n * E;
+        for (int64_t i = 0; i < E; ++i) z[i] = g[i] * w[i];
+    }
+    if (rc == 0) memcpy(y, z, sizeof(double) * E);
+    free(z); free(w);
+    return rc;
+}
+
+/* ------------------------------------------------------------------------ */
+/* 2D non-causal convolution with skip ([P3])                                */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * Direct sum over the whole grid (linear, zero outside the grid, "same"
+ * output positions):
+ *   w[b,p,q,c] = sum_{p'<X} sum_{q'<Y} K[c][p-p'][q-q'] z[b,p',q',c] + D[c] z[b,p,q,c]
+ * where K[c][i][j] is the tap at signed offset (i, j).
+ */
+void oracle_conv2d_direct(int64_t B, int64_t X, int64_t Y, int64_t d, const double* z,
+                          const double* K, const double* D, double* w)
+{
+    const int64_t KX = 2 * X - 1, KY = 2 * Y - 1;
+#pragma omp parallel for collapse(3) schedule(dynamic)
+    for (int64_t b = 0; b < B; ++b)
+        for (int64_t c = 0; c < d; ++c)
+            for (int64_t p = 0; p < X; ++p)
+                for (int64_t q = 0; q < Y; ++q) {
+                    double acc = 0.0;
+                    for (int64_t pp = 0; pp < X; ++pp)
+                        for (int64_t qq = 0; qq < Y; ++qq)
+                            acc += K[(c * KX + (p - pp + X - 1)) * KY + (q - qq + Y - 1)] *
+                                   z[((b * X + pp) * Y + qq) * d + c];
+                    const int64_t o = ((b * X + p) * Y + q) * d + c;
+                    w[o] = acc + D[c] * z[o];
+                }
+}
+
+/*
+ * The same through the 2D convolution theorem: grid and taps placed in a
+ * P1 x P2 periodic array, P1 = power of two >= 2X, P2 = power of two >= 2Y;
+ * the tap at offset (i, j) goes to (i mod P1, j mod P2).  2D DFT = 1D DFTs
+ * along rows, then along columns.  Bin-by-bin product, inverse with 1/(P1 P2),
+ * keep [0,X) x [0,Y), add D z.  Because P1 >= 2X - 1 and P2 >= 2Y - 1 no
+ * offset that reaches the kept window aliases onto another.
+ */
+static void fft2d(int64_t P1, int64_t P2, double* re, double* im, int sign,
+                  double* colr, double* coli)
+{
+    for (int64_t r = 0; r < P1; ++r) oracle_fft(P2, re + r * P2, im + r * P2, sign);
+    for (int64_t col = 0; col < P2; ++col) {
+        for (int64_t r = 0; r < P1; ++r) { colr[r] = re[r * P2 + col]; coli[r] = im[r * P2 + col]; }
+        oracle_fft(P1, colr, coli, sign);
+        for (int64_t r = 0; r < P1; ++r) { re[r * P2 + col] = colr[r]; im[r * P2 + col] = coli[r]; }
+    }
+}
+
+int oracle_conv2d_fft(int64_t B, int64_t X, int64_t Y, int64_t d, const double* z,
+                      const double* K, const double* D, double* w)
+{
+    const int64_t P1 = next_pow2(2 * X), P2 = next_pow2(2 * Y);
+    const int64_t KX = 2 * X - 1, KY = 2 * Y - 1;
+    const int64_t S = P1 * P2;
+    int fail = 0;
+#pragma omp parallel
+    {
+        double* xr = (double*)malloc(sizeof(double) * S);
+        double* xi = (double*)malloc(sizeof(double) * S);
+        double* kr = (double*)malloc(sizeof(double) * S);
+        double* ki = (double*)malloc(sizeof(double) * S);
+        double* cr = (double*)malloc(sizeof(double) * P1);
+        double* ci = (double*)malloc(sizeof(double) * P1);
+        if (!xr || !xi || !kr || !ki || !cr || !ci) {
+#pragma omp atomic write
+            fail = 1;
+        } else {
+#pragma omp for collapse(2) schedule(dynamic)
+            for (int64_t b = 0; b < B; ++b)
+                for (int64_t c = 0; c < d; ++c) {
+                    memset(xr, 0, sizeof(double) * S); memset(xi, 0, sizeof(double) * S);
+                    memset(kr, 0, sizeof(double) * S); memset(ki, 0, sizeof(double) * S);
+                    for (int64_t p = 0; p < X; ++p)
+                        for (int64_t q = 0; q < Y; ++q)
+                            xr[p * P2 + q] = z[((b * X + p) * Y + q) * d + c];
+                    for (int64_t i = -(X - 1); i <= X - 1; ++i)
+                        for (int64_t j = -(Y - 1); j <= Y - 1; ++j) {
+                            int64_t ri = (i + P1) % P1, rj = (j + P2) % P2;
+                            kr[ri * P2 + rj] = K[(c * KX + (i + X - 1)) * KY + (j + Y - 1)];
+                        }
+                    fft2d(P1, P2, xr, xi, -1, cr, ci);
+                    fft2d(P1, P2, kr, ki, -1, cr, ci);
+                    for (int64_t k = 0; k < S; ++k) {
+                        double pr = xr[k] * kr[k] - xi[k] * ki[k];
+                        double pi = xr[k] * ki[k] + xi[k] * kr[k];
+                        xr[k] = pr; xi[k] = pi;
+                    }
+                    fft2d(P1, P2, xr, xi, +1, cr, ci);
+                    for (int64_t p = 0; p < X; ++p)
+                        for (int64_t q = 0; q < Y; ++q) {
+                            const int64_t o = ((b * X + p) * Y + q) * d + c;
+                            w[o] = xr[p * P2 + q] / (double)S + D[c] * z[o];
+                        }
+                }
+        }
+        free(xr); free(xi); free(kr); free(ki); free(cr); free(ci);
+    }
+    return fail ? -1 : 0;
+}
+
+/*
+ * Order-N chain on a 2D grid: the same gating structure as the 1D chain,
+ * with the non-causal 2D convolution in place of the causal 1D one.
+ */
+int oracle_hyena2d(int64_t B, int64_t X, int64_t Y, int64_t d, int32_t order, const double* u,
+                   const double* gates, const double* K, const double* D, double* y,
+                   int32_t method)
+{
+    const int64_t E = B * X * Y * d;
+    const int64_t KS = (2 * X - 1) * (2 * Y - 1);
+    double* z = (double*)malloc(sizeof(double) * E);
+    double* w = (double*)malloc(sizeof(double) * E);
+    if (!z || !w) { free(z); free(w); return -1; }
+    memcpy(z, u, sizeof(double) * E);
+    int rc = 0;
+    for (int32_t n = 0; n < order && rc == 0; ++n) {
+        const double* Kn = K + (int64_t)n * d * KS;
+        const double* Dn = D + (int64_t)n * d;
+        if (method == 0)
+            oracle_conv2d_direct(B, X, Y, d, z, Kn, Dn, w);
+        else
+            rc = oracle_conv2d_fft(B, X, Y, d, z, Kn, Dn, w);
+        const double* g = gates + (int64_t)n * E;
+        for (int64_t i = 0; i < E; ++i) z[i] = g[i] * w[i];
+    }
+    if (rc == 0) memcpy(y, z, sizeof(double) * E);
+    free(z); free(w);
+    return rc;
+}

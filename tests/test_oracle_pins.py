@@ -1,0 +1,443 @@
+"""Pins for the float64 oracle against things that do not go through its code.
+
+Each test names the passage of the pages (or the mathematical fact) it checks:
+the printed worked example, numpy/scipy library routines, the DFT definition,
+closed forms, and the invariants the pages state.  A plausible slip in the
+oracle (dropped skip term, wrong FFT sign, missing padding, off-by-one lag,
+gate applied before instead of after, transposed 2D offset) fails at least one.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+import scipy.linalg
+import scipy.signal
+
+import oracle
+from long_convolution_sequence_rfft_amd import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rel(a, b):
+    a = np.asarray(a)
+    b = np.asarray(b)
+    scale = max(np.max(np.abs(b)), 1e-300)
+    return float(np.max(np.abs(a - b)) / scale)
+
+
+def _damped(N, d, rng, alpha=(1e-3, 5e-2)):
+    t = np.arange(N)
+    w = rng.uniform(0, np.pi, d)
+    phi = rng.uniform(0, 2 * np.pi, d)
+    a = rng.uniform(*alpha, d)
+    return np.sin(w[:, None] * t + phi[:, None]) * np.exp(-a[:, None] * t), w, phi, a
+
+
+# --------------------------------------------------------------------------
+# The printed worked example ("Hyena -- Long Convolutions Math", section
+# "Linear vs circular: the padding that preserves causality")
+# --------------------------------------------------------------------------
+
+def _worked():
+    with open(os.path.join(GOLDEN, "worked_example.json")) as f:
+        return json.load(f)
+
+
+@pytest.mark.parametrize("method", [oracle.DIRECT, oracle.FFT])
+def test_worked_example_linear(method):
+    g = _worked()
+    x = np.array(g["x"]).reshape(1, 4, 1)
+    h = np.array(g["h"]).reshape(1, 4)
+    w = oracle.causal_conv(x, h, np.zeros(1), method)
+    np.testing.assert_allclose(w.ravel(), g["y"], rtol=0, atol=1e-15)
+    # the same through the chain with an all-ones gate and no skip
+    y = oracle.hyena1d(x, np.ones((1, 1, 4, 1)), h[None], np.zeros((1, 1)), method)
+    np.testing.assert_allclose(y.ravel(), g["y"], rtol=0, atol=1e-15)
+
+
+def test_worked_example_circular_wraps():
+    g = _worked()
+    x = np.array(g["x"]).reshape(1, 4, 1)
+    h = np.array(g["h"]).reshape(1, 4)
+    wc = oracle.circular_conv(x, h)
+    assert abs(wc[0, 0, 0] - g["circular_y0"]) < 1e-15
+    # and the padded route does not wrap
+    assert abs(oracle.causal_conv(x, h, np.zeros(1), oracle.FFT)[0, 0, 0] - g["y"][0]) < 1e-15
+
+
+# --------------------------------------------------------------------------
+# FFT vs numpy (pocketfft) and vs the DFT definition
+# ("Hyena -- Long Convolutions Math", "The convolution theorem")
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("M", [1, 2, 4, 8, 64, 1024, 4096])
+def test_fft_matches_numpy(M):
+    rng = np.random.default_rng(M)
+    x = rng.standard_normal(M) + 1j * rng.standard_normal(M)
+    assert _rel(oracle.fft(x), np.fft.fft(x)) < 1e-13
+    assert _rel(oracle.fft(x, inverse=True), np.fft.ifft(x) * M) < 1e-13
+
+
+@pytest.mark.parametrize("M", [2, 8, 32, 128])
+def test_fft_matches_dft_definition(M):
+    rng = np.random.default_rng(100 + M)
+    x = rng.standard_normal(M) + 1j * rng.standard_normal(M)
+    k = np.arange(M)
+    F = np.exp(-2j * np.pi * np.outer(k, k) / M)
+    assert _rel(oracle.fft(x), F @ x) < 1e-12
+    assert _rel(oracle.fft(x, inverse=True), np.conj(F) @ x) < 1e-12
+
+
+def test_fft_rejects_non_power_of_two():
+    with pytest.raises(ValueError):
+        oracle.fft(np.ones(6))
+
+
+# --------------------------------------------------------------------------
+# Causal convolution vs library routines and the Toeplitz picture
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("method", [oracle.DIRECT, oracle.FFT])
+@pytest.mark.parametrize("N", [1, 2, 3, 5, 16, 100, 256])
+def test_causal_conv_matches_numpy_convolve(method, N):
+    rng = np.random.default_rng(N)
+    B, d = 2, 3
+    z = rng.standard_normal((B, N, d))
+    h = rng.standard_normal((d, N))
+    D = rng.standard_normal(d)
+    w = oracle.causal_conv(z, h, D, method)
+    ref = np.empty_like(z)
+    for b in range(B):
+        for c in range(d):
+            ref[b, :, c] = np.convolve(h[c], z[b, :, c])[:N] + D[c] * z[b, :, c]
+    assert _rel(w, ref) < 1e-12
+
+
+@pytest.mark.parametrize("method", [oracle.DIRECT, oracle.FFT])
+def test_causal_conv_equals_lower_triangular_toeplitz(method):
+    # "The Toeplitz picture": S_h[t, tau] = h_{t - tau} for t >= tau, else 0
+    rng = np.random.default_rng(7)
+    N, d = 256, 2
+    h = rng.standard_normal((d, N))
+    z = rng.standard_normal((1, N, d))
+    w = oracle.causal_conv(z, h, np.zeros(d), method)
+    for c in range(d):
+        S = scipy.linalg.toeplitz(h[c], np.zeros(N))
+        assert np.all(np.triu(S, 1) == 0)
+        assert _rel(w[0, :, c], S @ z[0, :, c]) < 1e-13
+
+
+@pytest.mark.parametrize("method", [oracle.DIRECT, oracle.FFT])
+def test_order2_matrix_form(method):
+    # y = D_{x2} S_{h2} D_{x1} S_{h1} v with the skip terms: diag(g2)(S2 + D2 I) diag(g1)(S1 + D1 I) u
+    rng = np.random.default_rng(11)
+    B, N, d = 2, 128, 3
+    u = rng.standard_normal((B, N, d))
+    gates = rng.standard_normal((2, B, N, d))
+    h = rng.standard_normal((2, d, N))
+    D = rng.standard_normal((2, d))
+    y = oracle.hyena1d(u, gates, h, D, method)
+    for b in range(B):
+        for c in range(d):
+            S1 = scipy.linalg.toeplitz(h[0, c], np.zeros(N)) + D[0, c] * np.eye(N)
+            S2 = scipy.linalg.toeplitz(h[1, c], np.zeros(N)) + D[1, c] * np.eye(N)
+            ref = np.diag(gates[1, b, :, c]) @ S2 @ np.diag(gates[0, b, :, c]) @ S1 @ u[b, :, c]
+            assert _rel(y[b, :, c], ref) < 1e-12
+
+
+def test_gate_applies_after_the_convolution():
+    # Swapping the order (gate before conv) must give a different answer.
+    rng = np.random.default_rng(12)
+    N = 32
+    u = rng.standard_normal((1, N, 1))
+    g = rng.standard_normal((1, 1, N, 1))
+    h = rng.standard_normal((1, 1, N))
+    y = oracle.hyena1d(u, g, h, np.zeros((1, 1)))
+    after = g[0, 0, :, 0] * np.convolve(h[0, 0], u[0, :, 0])[:N]
+    before = np.convolve(h[0, 0], g[0, 0, :, 0] * u[0, :, 0])[:N]
+    assert _rel(y[0, :, 0], after) < 1e-13
+    assert _rel(y[0, :, 0], before) > 1e-3
+
+
+# --------------------------------------------------------------------------
+# Brute force on tiny inputs: direct vs FFT vs explicit Toeplitz, every element
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("N", list(range(1, 17)))
+def test_tiny_brute_force(N):
+    rng = np.random.default_rng(1000 + N)
+    for B, d in [(1, 1), (2, 2), (1, 3)]:
+        u = rng.standard_normal((B, N, d))
+        gates = rng.standard_normal((2, B, N, d))
+        h = rng.standard_normal((2, d, N))
+        D = rng.standard_normal((2, d))
+        y0 = oracle.hyena1d(u, gates, h, D, oracle.DIRECT)
+        y1 = oracle.hyena1d(u, gates, h, D, oracle.FFT)
+        ref = np.empty_like(u)
+        for b in range(B):
+            for c in range(d):
+                z = u[b, :, c]
+                for n in range(2):
+                    acc = np.zeros(N)
+                    for t in range(N):
+                        for s in range(t + 1):
+                            acc[t] += h[n, c, s] * z[t - s]
+                    z = gates[n, b, :, c] * (acc + D[n, c] * z)
+                ref[b, :, c] = z
+        assert _rel(y0, ref) < 1e-13
+        assert _rel(y1, ref) < 1e-12
+
+
+# --------------------------------------------------------------------------
+# Direct vs FFT route ("machine precision on random inputs across shapes")
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("k", range(2, 12))
+def test_direct_vs_fft_routes(k):
+    N = 2 ** k
+    inp = synth.make_1d(B=2, N=N, d=3, order=2, seed=k)
+    u, g, h, D = inp.f64()
+    y0 = oracle.hyena1d(u, g, h, D, oracle.DIRECT)
+    y1 = oracle.hyena1d(u, g, h, D, oracle.FFT)
+    assert _rel(y1, y0) < 1e-12
+
+
+# --------------------------------------------------------------------------
+# Closed forms
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("method", [oracle.DIRECT, oracle.FFT])
+def test_impulse_response(method):
+    rng = np.random.default_rng(3)
+    N, d = 512, 4
+    h, *_ = _damped(N, d, rng)
+    D = rng.standard_normal(d)
+    z = np.zeros((1, N, d))
+    z[0, 0, :] = 1.0
+    w = oracle.causal_conv(z, h, D, method)
+    ref = h.T.copy()
+    ref[0] += D
+    assert _rel(w[0], ref) < 1e-13
+
+
+@pytest.mark.parametrize("N,method", [(4096, oracle.DIRECT), (4096, oracle.FFT),
+                                      (65536, oracle.FFT)])
+def test_step_response_damped_sinusoid(N, method):
+    # h_s = sin(w s + phi) e^{-a s} = Im(e^{i phi} r^s), r = e^{-a + i w};
+    # the partial sum over s <= t is Im(e^{i phi} (1 - r^{t+1}) / (1 - r)).
+    rng = np.random.default_rng(N)
+    d = 3
+    h, w, phi, a = _damped(N, d, rng, alpha=(1e-6, 1e-4))
+    D = rng.standard_normal(d)
+    z = np.ones((1, N, d))
+    out = oracle.causal_conv(z, h, D, method)
+    t = np.arange(N)
+    for c in range(d):
+        r = np.exp(-a[c] + 1j * w[c])
+        closed = np.imag(np.exp(1j * phi[c]) * (1 - r ** (t + 1)) / (1 - r)) + D[c]
+        assert _rel(out[0, :, c], closed) < 1e-10
+
+
+@pytest.mark.parametrize("method", [oracle.DIRECT, oracle.FFT])
+def test_extreme_tap_does_not_wrap(method):
+    # h = delta at lag N-1: only the last output sees x_0; nothing wraps to early t.
+    rng = np.random.default_rng(5)
+    N, d = 1024, 2
+    h = np.zeros((d, N))
+    h[:, N - 1] = 1.0
+    z = rng.standard_normal((1, N, d))
+    w = oracle.causal_conv(z, h, np.zeros(d), method)
+    assert np.max(np.abs(w[0, :N - 1])) < 1e-12
+    np.testing.assert_allclose(w[0, N - 1], z[0, 0], rtol=1e-12)
+
+
+# --------------------------------------------------------------------------
+# Invariants ("The primitive": causal, shift-equivariant, depthwise)
+# --------------------------------------------------------------------------
+
+def _chain_inputs(seed, B=2, N=256, d=3, order=2):
+    inp = synth.make_1d(B=B, N=N, d=d, order=order, seed=seed)
+    return inp.f64()
+
+
+@pytest.mark.parametrize("method", [oracle.DIRECT, oracle.FFT])
+def test_causality(method):
+    u, g, h, D = _chain_inputs(21)
+    y = oracle.hyena1d(u, g, h, D, method)
+    for tau in [0, 1, 100, 255]:
+        u2 = u.copy()
+        u2[:, tau, :] += 3.0
+        y2 = oracle.hyena1d(u2, g, h, D, method)
+        if method == oracle.DIRECT:
+            assert np.array_equal(y2[:, :tau], y[:, :tau])
+        elif tau > 0:
+            assert np.max(np.abs(y2[:, :tau] - y[:, :tau])) <= 1e-13 * np.max(np.abs(y))
+        assert np.max(np.abs(y2[:, tau:] - y[:, tau:])) > 0
+
+
+@pytest.mark.parametrize("method", [oracle.DIRECT, oracle.FFT])
+def test_linearity_in_u(method):
+    u, g, h, D = _chain_inputs(22)
+    v = np.random.default_rng(23).standard_normal(u.shape)
+    a, b = 0.75, -1.5
+    lhs = oracle.hyena1d(a * u + b * v, g, h, D, method)
+    rhs = a * oracle.hyena1d(u, g, h, D, method) + b * oracle.hyena1d(v, g, h, D, method)
+    assert _rel(lhs, rhs) < 1e-12
+
+
+@pytest.mark.parametrize("method", [oracle.DIRECT, oracle.FFT])
+def test_shift_equivariance(method):
+    u, g, h, D = _chain_inputs(24)
+    s = 37
+    us = np.zeros_like(u)
+    us[:, s:] = u[:, :-s]
+    gs = np.zeros_like(g)
+    gs[:, :, s:] = g[:, :, :-s]
+    y = oracle.hyena1d(u, g, h, D, method)
+    ys = oracle.hyena1d(us, gs, h, D, method)
+    tol = 0.0 if method == oracle.DIRECT else 1e-12 * np.max(np.abs(y))
+    assert np.max(np.abs(ys[:, s:] - y[:, :-s])) <= tol
+    assert np.max(np.abs(ys[:, :s])) <= tol
+
+
+def test_channel_independence():
+    u, g, h, D = _chain_inputs(25, d=5)
+    perm = np.array([3, 0, 4, 1, 2])
+    y = oracle.hyena1d(u, g, h, D)
+    yp = oracle.hyena1d(u[..., perm], g[..., perm], h[:, perm], D[:, perm])
+    assert np.array_equal(yp, y[..., perm])
+
+
+# --------------------------------------------------------------------------
+# Reductions
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("method", [oracle.DIRECT, oracle.FFT])
+def test_zero_filter_leaves_gated_skip(method):
+    u, g, h, D = _chain_inputs(26, order=1)
+    y = oracle.hyena1d(u, g, np.zeros_like(h), D, method)
+    ref = g[0] * (D[0][None, None, :] * u)
+    if method == oracle.DIRECT:
+        assert np.array_equal(y, ref)
+    else:
+        assert _rel(y, ref) < 1e-14
+
+
+def test_unit_gates_compose_into_one_filter():
+    # with all gates 1 the order-2 chain is one causal filter (h1 + D1 d) * (h2 + D2 d)
+    u, g, h, D = _chain_inputs(27, B=1, N=200)
+    ones = np.ones_like(g)
+    y = oracle.hyena1d(u, ones, h, D, oracle.FFT)
+    N = u.shape[1]
+    for c in range(u.shape[2]):
+        f1 = h[0, c].copy(); f1[0] += D[0, c]
+        f2 = h[1, c].copy(); f2[0] += D[1, c]
+        comp = np.convolve(f1, f2)[:N]
+        ref = np.convolve(comp, u[0, :, c])[:N]
+        assert _rel(y[0, :, c], ref) < 1e-11
+
+
+# --------------------------------------------------------------------------
+# 2D ("How HyenaND works": ND FFT convolution, zero padding, non-causal)
+# --------------------------------------------------------------------------
+
+def _scipy_same(z, Kc):
+    X, Y = z.shape
+    full = scipy.signal.convolve2d(z, Kc)
+    return full[X - 1:2 * X - 1, Y - 1:2 * Y - 1]
+
+
+@pytest.mark.parametrize("method", [oracle.DIRECT, oracle.FFT])
+@pytest.mark.parametrize("X,Y", [(1, 1), (2, 3), (4, 4), (8, 8), (5, 7)])
+def test_conv2d_matches_scipy(method, X, Y):
+    rng = np.random.default_rng(X * 31 + Y)
+    B, d = 2, 3
+    z = rng.standard_normal((B, X, Y, d))
+    K = rng.standard_normal((d, 2 * X - 1, 2 * Y - 1))
+    D = rng.standard_normal(d)
+    w = oracle.conv2d(z, K, D, method)
+    for b in range(B):
+        for c in range(d):
+            ref = _scipy_same(z[b, :, :, c], K[c]) + D[c] * z[b, :, :, c]
+            assert _rel(w[b, :, :, c], ref) < 1e-12
+
+
+@pytest.mark.parametrize("X,i0,j0", [(8, 7, -7), (8, -7, 7), (8, 3, 0),
+                                     (256, 255, -255), (256, -255, 255), (256, 17, -3)])
+def test_conv2d_delta_kernel_shifts_without_wrap(X, i0, j0):
+    Y = X
+    rng = np.random.default_rng(abs(X + i0 * 3 + j0) + 1)
+    z = rng.standard_normal((1, X, Y, 1))
+    K = np.zeros((1, 2 * X - 1, 2 * Y - 1))
+    K[0, i0 + X - 1, j0 + Y - 1] = 1.0
+    methods = [oracle.FFT] if X > 32 else [oracle.DIRECT, oracle.FFT]
+    ref = np.zeros((X, Y))
+    # w[p,q] = z[p - i0, q - j0] where that lies on the grid, zero elsewhere
+    ps, qs = np.meshgrid(np.arange(X), np.arange(Y), indexing="ij")
+    src_p, src_q = ps - i0, qs - j0
+    ok = (src_p >= 0) & (src_p < X) & (src_q >= 0) & (src_q < Y)
+    ref[ok] = z[0, src_p[ok], src_q[ok], 0]
+    for m in methods:
+        w = oracle.conv2d(z, K, np.zeros(1), m)
+        assert np.max(np.abs(w[0, :, :, 0] - ref)) < 1e-12
+
+
+def test_conv2d_separable_kernel_reduces_to_1d():
+    rng = np.random.default_rng(77)
+    X, Y = 16, 12
+    a = rng.standard_normal(2 * X - 1)
+    bvec = rng.standard_normal(2 * Y - 1)
+    K = np.outer(a, bvec)[None]
+    z = rng.standard_normal((1, X, Y, 1))
+    w = oracle.conv2d(z, K, np.zeros(1), oracle.FFT)[0, :, :, 0]
+    # non-causal 1D conv along each axis ("same" window): np.convolve then crop
+    tmp = np.stack([np.convolve(bvec, z[0, p, :, 0])[Y - 1:2 * Y - 1] for p in range(X)])
+    ref = np.stack([np.convolve(a, tmp[:, q])[X - 1:2 * X - 1] for q in range(Y)], axis=1)
+    assert _rel(w, ref) < 1e-12
+
+
+def test_conv2d_direct_vs_fft_trace_shape():
+    # the worked-trace shape of "How HyenaND works": B=2, 32x32 grid, 64 channels
+    inp = synth.make_2d(B=2, X=32, Y=32, d=64, order=1, sigma_range=(2.0, 16.0), seed=3)
+    u, g, K, D = inp.f64()
+    w0 = oracle.conv2d(u, K[0], D[0], oracle.DIRECT)
+    w1 = oracle.conv2d(u, K[0], D[0], oracle.FFT)
+    assert _rel(w1, w0) < 1e-12
+
+
+def test_hyena2d_chain_direct_vs_fft_and_by_hand():
+    inp = synth.make_2d(B=1, X=8, Y=8, d=3, order=2, sigma_range=(1.0, 4.0), seed=4)
+    u, g, K, D = inp.f64()
+    y0 = oracle.hyena2d(u, g, K, D, oracle.DIRECT)
+    y1 = oracle.hyena2d(u, g, K, D, oracle.FFT)
+    assert _rel(y1, y0) < 1e-12
+    for c in range(3):
+        z = u[0, :, :, c]
+        for n in range(2):
+            z = g[n, 0, :, :, c] * (_scipy_same(z, K[n, c]) + D[n, c] * z)
+        assert _rel(y0[0, :, :, c], z) < 1e-12
+
+
+# --------------------------------------------------------------------------
+# Input generator sanity (not the method: the storage rounding it feeds)
+# --------------------------------------------------------------------------
+
+def test_bf16_rounding_is_nearest_even():
+    x = np.array([1.0, 1.00390625, 1.005859375, -2.5, 3.0e-5, 65504.0], dtype=np.float32)
+    bits = synth.f32_to_bf16_bits(x)
+    back = synth.bf16_bits_to_f32(bits)
+    # 1 + 2^-8 is a tie between 1 and 1 + 2^-7: rounds to the even mantissa (1.0)
+    assert back[1] == np.float32(1.0)
+    # 1 + 1.5 * 2^-8 rounds up to 1 + 2^-7
+    assert back[2] == np.float32(1.0078125)
+    assert np.all(np.abs(back - x) <= np.abs(x) * 2.0 ** -8)
+
+
+def test_inputs_are_seeded_and_reproducible():
+    a = synth.make_config(0)
+    b = synth.make_config(0)
+    assert np.array_equal(a.u, b.u) and np.array_equal(a.h, b.h)
+    c = synth.make_config(0, seed=100)
+    assert not np.array_equal(a.u, c.u)
