@@ -1,0 +1,160 @@
+/*
+ * hyena.h -- C ABI of the MI355X (gfx950) Hyena long-convolution library.
+ *
+ * What it computes.  The order-N Hyena chain of "Week 11: Hyena, Long
+ * Convolution, and Linear Attention", section "The Hyena operator", in the
+ * order-2 form of "Hyena -- Long Convolutions Math", section "The Toeplitz
+ * picture" (y = x2 . (h2 * (x1 . (h1 * v)))), with the per-channel
+ * feedthrough of the FFTConv equation ([P1] section "FFTConv"):
+ *
+ *   z_0 = u
+ *   z_n[b,t,c] = gate_n[b,t,c] * ( sum_{s=0}^{t} h_n[c,s] z_{n-1}[b,t-s,c]
+ *                                  + D_n[c] z_{n-1}[b,t,c] ),   n = 1..order
+ *   y = z_order
+ *
+ * Each convolution is evaluated through the convolution theorem on a length
+ * M = (power of two >= 2N) zero-padded transform, keeping the first N
+ * outputs ("Hyena -- Long Convolutions Math", sections "The convolution
+ * theorem" and "Linear vs circular").  With ndims = 2 the convolution is the
+ * non-causal linear 2D convolution of "How HyenaND works" (section "The
+ * convolution theorem (FFT)"; worked trace with zero padding and
+ * is_causal=False): taps at every signed offset (i, j), |i| <= X-1,
+ * |j| <= Y-1, output kept on the input grid.
+ *
+ * Layouts (row-major, channels last; d is the fastest axis):
+ *   u, gates[n], y : [B][N][d] (ndims = 1) or [B][X][Y][d] (ndims = 2)
+ *   h              : [order][d][N] (ndims = 1);
+ *                    [order][d][2X-1][2Y-1] (ndims = 2), the tap at offset
+ *                    (i, j) stored at index (i + X - 1, j + Y - 1)
+ *   D              : float32 [order][d]
+ *   H (spectrum)   : opaque, spectrum_bytes long, laid out in the order the
+ *                    forward kernels consume it (see hyena_spectrum_export)
+ * io_dtype applies to u, gates, y and h; spectrum_dtype to H.  All arithmetic
+ * is float32; bfloat16 values are widened exactly and stored with
+ * round-to-nearest-even.
+ *
+ * Ownership and streams.  Every device buffer is owned by the caller and must
+ * stay alive until the work enqueued on the stream has finished.  The library
+ * never allocates device memory; it owns only host memory inside the plan.
+ * All device work is enqueued on the given hipStream_t (passed as void*; NULL
+ * is the null stream) with no host synchronisation.  The workspace holds
+ * twiddle tables (written by hyena_workspace_init) and, on the multi-pass
+ * paths, the intermediate spectra; it must not be shared by calls that run
+ * concurrently.
+ *
+ * Errors.  Argument problems are reported before anything is enqueued and
+ * leave every output untouched; hyena_last_error() then returns a
+ * thread-local description.  HYENA_ERR_DEVICE reports a failed launch;
+ * faults inside a kernel surface at the caller's next synchronisation.
+ *
+ * Thread safety.  A plan is immutable after creation except for its record of
+ * initialised workspaces, which is internally locked; plans may be shared by
+ * host threads.  The forward pass uses no atomics, so the same plan and inputs
+ * give bitwise-identical y.
+ */
+#ifndef HYENA_MI355X_H
+#define HYENA_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct hyena_plan_s* hyena_plan_t;
+
+typedef enum hyena_status {
+    HYENA_OK = 0,
+    HYENA_ERR_INVALID_ARGUMENT = 1, /* null/misaligned/overlapping pointer, bad size */
+    HYENA_ERR_UNSUPPORTED = 2,      /* shape, order, dtype or path not supported */
+    HYENA_ERR_WORKSPACE = 3,        /* workspace not initialised for this plan */
+    HYENA_ERR_DEVICE = 4            /* a HIP launch or query failed */
+} hyena_status;
+
+typedef enum hyena_dtype {
+    HYENA_F32 = 0,
+    HYENA_BF16 = 1
+} hyena_dtype;
+
+/* Which kernel family runs the transform.  AUTO picks: LDS1D when ndims = 1
+ * and M <= 16384, FOURSTEP1D when ndims = 1 and M > 16384, ROWCOL2D when
+ * ndims = 2.  FOURSTEP1D may be forced for any M >= 1024 (tests use this to
+ * check it against the single-pass kernels at small N). */
+typedef enum hyena_path {
+    HYENA_PATH_AUTO = 0,
+    HYENA_PATH_LDS1D = 1,
+    HYENA_PATH_FOURSTEP1D = 2,
+    HYENA_PATH_ROWCOL2D = 3
+} hyena_path;
+
+/*
+ * Create a plan.  B >= 1 batch rows, d >= 1 channels, 1 <= order <= 8.
+ * ndims = 1: dims = {N}, 4 <= N <= 65536 (any N; M is the power of two
+ *            >= 2N; N == the N argument).
+ * ndims = 2: dims = {X, Y}, X and Y powers of two in [4, 512]; N must equal
+ *            X * Y.
+ * io_dtype, spectrum_dtype: hyena_dtype values.  path: hyena_path value.
+ * On success *plan receives a new plan (release with hyena_plan_destroy).
+ * This call touches no GPU state.
+ */
+hyena_status hyena_plan_create(hyena_plan_t* plan, int64_t B, int64_t N, int64_t d,
+                               int32_t order, const int64_t* dims, int32_t ndims,
+                               int32_t io_dtype, int32_t spectrum_dtype, int32_t path);
+
+/* Sizes in bytes of the spectrum buffer H and of the workspace, and the path
+ * the plan resolved to (any output pointer may be NULL). */
+hyena_status hyena_plan_query(hyena_plan_t plan, size_t* spectrum_bytes,
+                              size_t* workspace_bytes, int32_t* path);
+
+/* Write the plan's twiddle tables into a caller-allocated workspace of at
+ * least workspace_bytes (16-byte aligned).  Required once per (plan,
+ * workspace) before hyena_filter_spectrum or hyena_forward use it. */
+hyena_status hyena_workspace_init(hyena_plan_t plan, void* workspace, void* stream);
+
+/*
+ * Filter spectrum ("Hyena -- Long Convolutions Math", section "The
+ * convolution theorem": the transform of h is the filter's transfer
+ * function).  Reads h (io_dtype, layout above) and writes H
+ * (spectrum_bytes, spectrum_dtype) in the forward kernels' native order with
+ * the 1/M inverse scale folded in.  D is not part of H; it is applied by
+ * hyena_forward.  H stays valid for any call with a plan of the same shape
+ * and dtypes.
+ */
+hyena_status hyena_filter_spectrum(hyena_plan_t plan, const void* h, void* H,
+                                   void* workspace, void* stream);
+
+/*
+ * Forward chain.  u: input (io_dtype).  gates: host array of `order` device
+ * pointers (io_dtype), gate n applied after convolution n.  H: spectrum from
+ * hyena_filter_spectrum.  D: float32 [order][d] feedthrough.  y: output
+ * (io_dtype); y must not overlap u, any gate, H, D or the workspace.  All
+ * device pointers 16-byte aligned.
+ */
+hyena_status hyena_forward(hyena_plan_t plan, const void* u, const void* const* gates,
+                           const void* H, const float* D, void* y, void* workspace,
+                           void* stream);
+
+/*
+ * Test/inspection helper: expand H into natural-order transfer functions,
+ * complex64 (re, im) pairs, unscaled (the plain DFT of the zero-padded
+ * filter).  ndims = 1: [order][d][M/2 + 1] bins k = 0..M/2.
+ * ndims = 2: [order][d][P1][P2/2 + 1] with P1 = 2X, P2 = 2Y.
+ */
+hyena_status hyena_spectrum_export(hyena_plan_t plan, const void* H, void* natural,
+                                   void* stream);
+
+/* Release a plan (NULL is accepted). */
+hyena_status hyena_plan_destroy(hyena_plan_t plan);
+
+/* Static text for a status code. */
+const char* hyena_status_string(hyena_status status);
+
+/* Thread-local text describing the last error raised on this thread. */
+const char* hyena_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HYENA_MI355X_H */

@@ -1,0 +1,189 @@
+// api.hip -- the extern "C" entry points declared in include/hyena.h.
+// Validation happens here, before anything is enqueued; the launchers in
+// lds1d.hip, fourstep.hip and rowcol2d.hip only enqueue kernels.
+#include <hip/hip_runtime.h>
+
+#include <new>
+
+#include "plan.h"
+
+namespace hy {
+const char* last_error_text();
+}
+
+struct hyena_plan_s {
+    hy::Plan p;
+};
+
+using hy::fail;
+
+namespace {
+
+bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; }
+
+size_t io_bytes(const hy::Plan& p)
+{
+    return (size_t)p.B * (size_t)p.N * (size_t)p.d * (p.io_dtype == HYENA_F32 ? 4u : 2u);
+}
+
+size_t filter_bytes(const hy::Plan& p)
+{
+    const size_t taps = p.ndims == 1 ? (size_t)p.N : (size_t)(2 * p.X - 1) * (size_t)(2 * p.Y - 1);
+    return (size_t)p.order * (size_t)p.d * taps * (p.io_dtype == HYENA_F32 ? 4u : 2u);
+}
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb)
+{
+    const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+    return a0 < b0 + nb && b0 < a0 + na;
+}
+
+hyena_status check_ws(const hy::Plan& p, const void* ws)
+{
+    if (ws == nullptr) return fail(HYENA_ERR_INVALID_ARGUMENT, "workspace is NULL");
+    if (!aligned16(ws)) return fail(HYENA_ERR_INVALID_ARGUMENT, "workspace is not 16-byte aligned");
+    std::lock_guard<std::mutex> lock(p.mu);
+    if (p.ready_ws.count(ws) == 0)
+        return fail(HYENA_ERR_WORKSPACE, "workspace was not initialised with hyena_workspace_init for this plan");
+    return HYENA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+hyena_status hyena_plan_create(hyena_plan_t* plan, int64_t B, int64_t N, int64_t d,
+                               int32_t order, const int64_t* dims, int32_t ndims,
+                               int32_t io_dtype, int32_t spectrum_dtype, int32_t path)
+{
+    if (plan == nullptr) return fail(HYENA_ERR_INVALID_ARGUMENT, "plan output pointer is NULL");
+    hyena_plan_s* s = new (std::nothrow) hyena_plan_s;
+    if (s == nullptr) return fail(HYENA_ERR_INVALID_ARGUMENT, "out of host memory");
+    const hyena_status st =
+        hy::plan_build(s->p, B, N, d, order, dims, ndims, io_dtype, spectrum_dtype, path);
+    if (st != HYENA_OK) {
+        delete s;
+        return st;
+    }
+    *plan = s;
+    return HYENA_OK;
+}
+
+hyena_status hyena_plan_query(hyena_plan_t plan, size_t* spectrum_bytes, size_t* workspace_bytes,
+                              int32_t* path)
+{
+    if (plan == nullptr) return fail(HYENA_ERR_INVALID_ARGUMENT, "plan is NULL");
+    if (spectrum_bytes) *spectrum_bytes = plan->p.spectrum_bytes;
+    if (workspace_bytes) *workspace_bytes = plan->p.workspace_bytes;
+    if (path) *path = plan->p.path;
+    return HYENA_OK;
+}
+
+hyena_status hyena_workspace_init(hyena_plan_t plan, void* workspace, void* stream)
+{
+    if (plan == nullptr) return fail(HYENA_ERR_INVALID_ARGUMENT, "plan is NULL");
+    if (workspace == nullptr) return fail(HYENA_ERR_INVALID_ARGUMENT, "workspace is NULL");
+    if (!aligned16(workspace))
+        return fail(HYENA_ERR_INVALID_ARGUMENT, "workspace is not 16-byte aligned");
+    const hyena_status st = hy::launch_tw_init(plan->p, workspace, stream);
+    if (st != HYENA_OK) return st;
+    std::lock_guard<std::mutex> lock(plan->p.mu);
+    plan->p.ready_ws.insert(workspace);
+    return HYENA_OK;
+}
+
+hyena_status hyena_filter_spectrum(hyena_plan_t plan, const void* h, void* H, void* workspace,
+                                   void* stream)
+{
+    if (plan == nullptr) return fail(HYENA_ERR_INVALID_ARGUMENT, "plan is NULL");
+    const hy::Plan& p = plan->p;
+    if (h == nullptr || H == nullptr) return fail(HYENA_ERR_INVALID_ARGUMENT, "h or H is NULL");
+    if (!aligned16(h) || !aligned16(H))
+        return fail(HYENA_ERR_INVALID_ARGUMENT, "h and H must be 16-byte aligned");
+    if (overlaps(h, filter_bytes(p), H, p.spectrum_bytes))
+        return fail(HYENA_ERR_INVALID_ARGUMENT, "H overlaps h");
+    hyena_status st = check_ws(p, workspace);
+    if (st != HYENA_OK) return st;
+    if (overlaps(workspace, p.workspace_bytes, H, p.spectrum_bytes))
+        return fail(HYENA_ERR_INVALID_ARGUMENT, "H overlaps the workspace");
+    switch (p.path) {
+        case HYENA_PATH_LDS1D: return hy::launch_lds1d_spectrum(p, h, H, workspace, stream);
+        case HYENA_PATH_FOURSTEP1D: return hy::launch_fourstep_spectrum(p, h, H, workspace, stream);
+        case HYENA_PATH_ROWCOL2D: return hy::launch_rowcol2d_spectrum(p, h, H, workspace, stream);
+        default: return fail(HYENA_ERR_UNSUPPORTED, "unknown path");
+    }
+}
+
+hyena_status hyena_forward(hyena_plan_t plan, const void* u, const void* const* gates,
+                           const void* H, const float* D, void* y, void* workspace, void* stream)
+{
+    if (plan == nullptr) return fail(HYENA_ERR_INVALID_ARGUMENT, "plan is NULL");
+    const hy::Plan& p = plan->p;
+    if (u == nullptr || gates == nullptr || H == nullptr || D == nullptr || y == nullptr)
+        return fail(HYENA_ERR_INVALID_ARGUMENT, "a required pointer is NULL");
+    if (!aligned16(u) || !aligned16(H) || !aligned16(D) || !aligned16(y))
+        return fail(HYENA_ERR_INVALID_ARGUMENT, "u, H, D and y must be 16-byte aligned");
+    const size_t nio = io_bytes(p);
+    const size_t nD = (size_t)p.order * (size_t)p.d * 4u;
+    for (int n = 0; n < p.order; ++n) {
+        if (gates[n] == nullptr) return fail(HYENA_ERR_INVALID_ARGUMENT, "a gate pointer is NULL");
+        if (!aligned16(gates[n]))
+            return fail(HYENA_ERR_INVALID_ARGUMENT, "gate pointers must be 16-byte aligned");
+        if (overlaps(y, nio, gates[n], nio))
+            return fail(HYENA_ERR_INVALID_ARGUMENT, "y overlaps a gate");
+    }
+    if (overlaps(y, nio, u, nio)) return fail(HYENA_ERR_INVALID_ARGUMENT, "y overlaps u");
+    if (overlaps(y, nio, H, p.spectrum_bytes)) return fail(HYENA_ERR_INVALID_ARGUMENT, "y overlaps H");
+    if (overlaps(y, nio, D, nD)) return fail(HYENA_ERR_INVALID_ARGUMENT, "y overlaps D");
+    hyena_status st = check_ws(p, workspace);
+    if (st != HYENA_OK) return st;
+    if (overlaps(y, nio, workspace, p.workspace_bytes))
+        return fail(HYENA_ERR_INVALID_ARGUMENT, "y overlaps the workspace");
+    switch (p.path) {
+        case HYENA_PATH_LDS1D:
+            return hy::launch_lds1d_forward(p, u, gates, H, D, y, workspace, stream);
+        case HYENA_PATH_FOURSTEP1D:
+            return hy::launch_fourstep_forward(p, u, gates, H, D, y, workspace, stream);
+        case HYENA_PATH_ROWCOL2D:
+            return hy::launch_rowcol2d_forward(p, u, gates, H, D, y, workspace, stream);
+        default: return fail(HYENA_ERR_UNSUPPORTED, "unknown path");
+    }
+}
+
+hyena_status hyena_spectrum_export(hyena_plan_t plan, const void* H, void* natural, void* stream)
+{
+    if (plan == nullptr) return fail(HYENA_ERR_INVALID_ARGUMENT, "plan is NULL");
+    if (H == nullptr || natural == nullptr)
+        return fail(HYENA_ERR_INVALID_ARGUMENT, "H or output is NULL");
+    if (!aligned16(H) || !aligned16(natural))
+        return fail(HYENA_ERR_INVALID_ARGUMENT, "H and output must be 16-byte aligned");
+    const hy::Plan& p = plan->p;
+    switch (p.path) {
+        case HYENA_PATH_LDS1D: return hy::launch_lds1d_export(p, H, natural, stream);
+        case HYENA_PATH_FOURSTEP1D: return hy::launch_fourstep_export(p, H, natural, stream);
+        case HYENA_PATH_ROWCOL2D: return hy::launch_rowcol2d_export(p, H, natural, stream);
+        default: return fail(HYENA_ERR_UNSUPPORTED, "unknown path");
+    }
+}
+
+hyena_status hyena_plan_destroy(hyena_plan_t plan)
+{
+    delete plan;
+    return HYENA_OK;
+}
+
+const char* hyena_status_string(hyena_status status)
+{
+    switch (status) {
+        case HYENA_OK: return "HYENA_OK";
+        case HYENA_ERR_INVALID_ARGUMENT: return "HYENA_ERR_INVALID_ARGUMENT";
+        case HYENA_ERR_UNSUPPORTED: return "HYENA_ERR_UNSUPPORTED";
+        case HYENA_ERR_WORKSPACE: return "HYENA_ERR_WORKSPACE";
+        case HYENA_ERR_DEVICE: return "HYENA_ERR_DEVICE";
+        default: return "HYENA_ERR_UNKNOWN";
+    }
+}
+
+const char* hyena_last_error(void) { return hy::last_error_text(); }
+
+}  // extern "C"

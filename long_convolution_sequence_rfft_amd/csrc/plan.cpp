@@ -1,0 +1,175 @@
+// plan.cpp -- argument validation, path choice and byte layouts.  Pure host
+// code: no HIP runtime call is made here, so plans can be created and
+// inspected on a machine without a GPU.
+#include <string>
+
+#include "plan.h"
+
+namespace hy {
+
+namespace {
+thread_local std::string g_last_error;
+
+bool is_pow2(int64_t n) { return n > 0 && (n & (n - 1)) == 0; }
+int64_t next_pow2(int64_t n)
+{
+    int64_t m = 1;
+    while (m < n) m <<= 1;
+    return m;
+}
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+void add_segment(Plan& p, int64_t& off, int64_t ns, int64_t radix)
+{
+    TwSegment& s = p.seg[p.nseg++];
+    s.off = off;
+    s.ns = (int32_t)ns;
+    s.radix = (int32_t)radix;
+    off += radix * ns;
+}
+}  // namespace
+
+void set_error(const std::string& msg) { g_last_error = msg; }
+hyena_status fail(hyena_status s, const std::string& msg)
+{
+    g_last_error = msg;
+    return s;
+}
+const char* last_error_text() { return g_last_error.c_str(); }
+
+// Four-step split of a 1D transform of length M into columns of length M1
+// (sample t = M2 * n1 + n2) and rows of length M2.
+static void fourstep_split(int64_t M, int64_t& M1, int64_t& M2)
+{
+    // columns carry the zero-padded half, rows are kept short enough for one
+    // workgroup to hold a mirrored pair of them in LDS
+    M1 = 512;
+    while (M1 > 32 && M / M1 < 32) M1 >>= 1;
+    M2 = M / M1;
+}
+
+hyena_status plan_build(Plan& p, int64_t B, int64_t N, int64_t d, int32_t order,
+                        const int64_t* dims, int32_t ndims, int32_t io_dtype,
+                        int32_t spec_dtype, int32_t path)
+{
+    if (B < 1) return fail(HYENA_ERR_INVALID_ARGUMENT, "B must be >= 1");
+    if (d < 1) return fail(HYENA_ERR_INVALID_ARGUMENT, "d must be >= 1");
+    if (N < 1) return fail(HYENA_ERR_INVALID_ARGUMENT, "N must be >= 1");
+    if (dims == nullptr) return fail(HYENA_ERR_INVALID_ARGUMENT, "dims is NULL");
+    if (order < 1 || order > kMaxOrder)
+        return fail(HYENA_ERR_UNSUPPORTED, "order must be in 1..8");
+    if (io_dtype != HYENA_F32 && io_dtype != HYENA_BF16)
+        return fail(HYENA_ERR_UNSUPPORTED, "unknown io_dtype");
+    if (spec_dtype != HYENA_F32 && spec_dtype != HYENA_BF16)
+        return fail(HYENA_ERR_UNSUPPORTED, "unknown spectrum_dtype");
+    if (io_dtype == HYENA_F32 && spec_dtype == HYENA_BF16)
+        return fail(HYENA_ERR_UNSUPPORTED, "a bfloat16 spectrum needs bfloat16 io");
+    if (path < HYENA_PATH_AUTO || path > HYENA_PATH_ROWCOL2D)
+        return fail(HYENA_ERR_UNSUPPORTED, "unknown path");
+    if (ndims != 1 && ndims != 2) return fail(HYENA_ERR_UNSUPPORTED, "ndims must be 1 or 2");
+    // per-row element offsets are 32-bit inside the kernels
+    if ((double)N * (double)d * 4.0 >= 2147483648.0)
+        return fail(HYENA_ERR_UNSUPPORTED, "N * d * 4 must stay below 2^31 bytes");
+
+    p.B = B;
+    p.N = N;
+    p.d = d;
+    p.order = order;
+    p.ndims = ndims;
+    p.io_dtype = io_dtype;
+    p.spec_dtype = spec_dtype;
+    p.npairs = (d + 1) / 2;
+    p.spec_entry_bytes = spec_dtype == HYENA_F32 ? 16 : 8;
+    p.nseg = 0;
+    int64_t off = 0;
+
+    if (ndims == 1) {
+        if (dims[0] != N) return fail(HYENA_ERR_INVALID_ARGUMENT, "dims[0] must equal N");
+        if (N < 4 || N > kFourStepMaxM / 2)
+            return fail(HYENA_ERR_UNSUPPORTED, "1D sequence length must be in 4..65536");
+        p.M = next_pow2(2 * N);
+        if (path == HYENA_PATH_AUTO) path = p.M <= kLdsMaxM ? HYENA_PATH_LDS1D : HYENA_PATH_FOURSTEP1D;
+        if (path == HYENA_PATH_ROWCOL2D)
+            return fail(HYENA_ERR_UNSUPPORTED, "ROWCOL2D needs ndims = 2");
+        if (path == HYENA_PATH_LDS1D && p.M > kLdsMaxM)
+            return fail(HYENA_ERR_UNSUPPORTED, "LDS1D path holds transforms up to 16384 points");
+        if (path == HYENA_PATH_FOURSTEP1D && p.M < 1024)
+            return fail(HYENA_ERR_UNSUPPORTED, "FOURSTEP1D needs a transform of >= 1024 points");
+        p.path = path;
+        p.spec_entries_per_pair = p.M / 2;
+        if (path == HYENA_PATH_LDS1D) {
+            const int M = (int)p.M;
+            p.R0 = lds1d_r0(M);
+            p.R1 = lds1d_r1(M);
+            p.RL = lds1d_rl(M);
+            add_segment(p, off, p.R0, p.R1);         // forward middle pass
+            add_segment(p, off, p.M / p.RL, p.RL);   // forward last pass
+            add_segment(p, off, p.RL, p.R1);         // inverse middle pass
+            add_segment(p, off, p.M / p.R0, p.R0);   // inverse last pass
+        } else {
+            fourstep_split(p.M, p.M1, p.M2);
+            // column transforms (length M1) and row transforms (length M2) each
+            // use the single-workgroup radix plan of their own length; plus the
+            // inter-step twiddle W_M^{n2 k1}
+            const int m1 = (int)p.M1, m2 = (int)p.M2;
+            add_segment(p, off, lds1d_r0(m1), lds1d_r1(m1));
+            add_segment(p, off, p.M1 / lds1d_rl(m1), lds1d_rl(m1));
+            add_segment(p, off, lds1d_rl(m1), lds1d_r1(m1));
+            add_segment(p, off, p.M1 / lds1d_r0(m1), lds1d_r0(m1));
+            add_segment(p, off, lds1d_r0(m2), lds1d_r1(m2));
+            add_segment(p, off, p.M2 / lds1d_rl(m2), lds1d_rl(m2));
+            add_segment(p, off, lds1d_rl(m2), lds1d_r1(m2));
+            add_segment(p, off, p.M2 / lds1d_r0(m2), lds1d_r0(m2));
+            add_segment(p, off, p.M2, p.M1);  // W_M^{n2 k1}: ns = M2 (n2), radix = M1 (k1)
+        }
+    } else {
+        const int64_t X = dims[0], Y = dims[1];
+        if (!is_pow2(X) || !is_pow2(Y) || X < 4 || Y < 4 || X > 512 || Y > 512)
+            return fail(HYENA_ERR_UNSUPPORTED, "2D grid sides must be powers of two in 4..512");
+        if (X * Y != N) return fail(HYENA_ERR_INVALID_ARGUMENT, "N must equal X * Y");
+        if (path == HYENA_PATH_AUTO) path = HYENA_PATH_ROWCOL2D;
+        if (path != HYENA_PATH_ROWCOL2D)
+            return fail(HYENA_ERR_UNSUPPORTED, "2D grids use the ROWCOL2D path");
+        p.path = path;
+        p.X = X;
+        p.Y = Y;
+        p.P1 = 2 * X;
+        p.P2 = 2 * Y;
+        p.spec_entries_per_pair = p.P1 * p.P2 / 2;
+        const int m1 = (int)p.P1, m2 = (int)p.P2;
+        add_segment(p, off, lds1d_r0(m1), lds1d_r1(m1));
+        add_segment(p, off, p.P1 / lds1d_rl(m1), lds1d_rl(m1));
+        add_segment(p, off, lds1d_rl(m1), lds1d_r1(m1));
+        add_segment(p, off, p.P1 / lds1d_r0(m1), lds1d_r0(m1));
+        add_segment(p, off, lds1d_r0(m2), lds1d_r1(m2));
+        add_segment(p, off, p.P2 / lds1d_rl(m2), lds1d_rl(m2));
+        add_segment(p, off, lds1d_rl(m2), lds1d_r1(m2));
+        add_segment(p, off, p.P2 / lds1d_r0(m2), lds1d_r0(m2));
+    }
+
+    p.tw_elems = off;
+    p.tw_bytes = align_up((size_t)off * 8, 256);
+    p.spectrum_bytes = (size_t)p.order * (size_t)p.npairs * (size_t)p.spec_entries_per_pair *
+                       p.spec_entry_bytes;
+
+    // intermediate spectra of the multi-pass paths: one complex64 value per
+    // transform point of the zero-padded half that is kept, for a chunk of
+    // channel pairs that is walked through all passes before the next chunk
+    p.inter_offset = p.tw_bytes;
+    p.inter_bytes = 0;
+    p.chunk_pairs = 0;
+    if (p.path == HYENA_PATH_FOURSTEP1D || p.path == HYENA_PATH_ROWCOL2D) {
+        const int64_t per_pair = p.path == HYENA_PATH_FOURSTEP1D ? p.M * 8 : p.P2 * p.X * 8;
+        // keep the chunk's intermediate near 96 MiB so it stays in the 256 MB
+        // last-level cache while it is re-read
+        int64_t chunk = (int64_t)(96ll << 20) / per_pair;
+        if (chunk < 1) chunk = 1;
+        if (chunk > B * p.npairs) chunk = B * p.npairs;
+        p.chunk_pairs = chunk;
+        p.inter_bytes = align_up((size_t)(chunk * per_pair), 256);
+    }
+    p.workspace_bytes = p.inter_offset + p.inter_bytes;
+    return HYENA_OK;
+}
+
+}  // namespace hy

@@ -1,0 +1,115 @@
+// plan.h -- host-side plan shared by the C-ABI layer and the kernel launchers.
+//
+// The plan is plain data: shape, dtypes, the resolved path, the radix
+// decomposition of each transform and the byte layout of the spectrum and of
+// the workspace.  Building it needs no GPU (plan.cpp has no HIP calls).
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <mutex>
+#include <set>
+#include <string>
+
+#include "../../include/hyena.h"
+
+namespace hy {
+
+constexpr int kMaxOrder = 8;
+constexpr int kMaxTwSegments = 12;
+constexpr int64_t kLdsMaxM = 16384;       // largest transform held in one workgroup's LDS
+constexpr int64_t kFourStepMaxM = 131072; // largest 1D transform (N = 65536)
+
+// Radix plan of the single-workgroup transform of length M (8 <= M <= 16384):
+// 32 complex values per thread (M >= 64), forward passes R0, R1, RL with
+// RL = 16 so that the last pass gives each thread two butterflies.
+constexpr int lds1d_pts(int M) { return M >= 64 ? 32 : M; }
+constexpr int lds1d_rl(int M) { return lds1d_pts(M) / 2; }
+constexpr int lds1d_rest(int M) { return M / lds1d_rl(M); }
+constexpr int lds1d_r0(int M)
+{
+    return lds1d_rest(M) <= 32 ? lds1d_rest(M) : lds1d_rest(M) <= 512 ? lds1d_rest(M) / 16 : 32;
+}
+constexpr int lds1d_r1(int M)
+{
+    return lds1d_rest(M) <= 32 ? 1 : lds1d_rest(M) <= 512 ? 16 : 32;
+}
+
+// One twiddle table, thread-contiguous: tw[off + k * radix + r] =
+// exp(-2 pi i r k / (ns * radix)), r = 0..radix-1, k = 0..ns-1.  A butterfly's
+// radix twiddles are one aligned run, read with 16-byte loads from one address.
+struct TwSegment {
+    int64_t off;    // in float2 elements from the workspace base
+    int32_t ns;
+    int32_t radix;
+};
+
+struct Plan {
+    // shape
+    int64_t B = 0, N = 0, d = 0;
+    int32_t order = 0;
+    int32_t ndims = 1;
+    int64_t X = 0, Y = 0;  // 2D grid
+    int32_t io_dtype = HYENA_F32, spec_dtype = HYENA_F32;
+    int32_t path = HYENA_PATH_AUTO;
+
+    int64_t M = 0;       // 1D transform length (power of two >= 2N)
+    int64_t npairs = 0;  // channel pairs (two real channels per complex transform)
+
+    // LDS1D: forward radices R0, R1 (1 if absent), RL; inverse runs them reversed.
+    int32_t R0 = 0, R1 = 1, RL = 0;
+
+    // FOURSTEP1D: M = M1 * M2; columns of length M1 (time index t = M2 n1 + n2),
+    // rows of length M2.  ROWCOL2D: P1 = 2X (columns), P2 = 2Y (rows).
+    int64_t M1 = 0, M2 = 0;
+    int64_t P1 = 0, P2 = 0;
+    int64_t chunk_pairs = 0;  // channel pairs per pass over the intermediate buffer
+
+    // twiddle tables
+    TwSegment seg[kMaxTwSegments];
+    int32_t nseg = 0;
+    int64_t tw_elems = 0;  // float2 elements
+
+    // byte layout
+    size_t spec_entry_bytes = 0;  // one (P, Q) entry: 16 (f32) or 8 (bf16)
+    int64_t spec_entries_per_pair = 0;
+    size_t spectrum_bytes = 0;
+    size_t tw_bytes = 0;
+    size_t inter_offset = 0;  // workspace offset of the intermediate buffer
+    size_t inter_bytes = 0;
+    size_t workspace_bytes = 0;
+
+    // record of workspaces that hold this plan's twiddles
+    mutable std::mutex mu;
+    std::set<const void*> ready_ws;
+};
+
+// Implemented in plan.cpp (pure host code).
+hyena_status plan_build(Plan& p, int64_t B, int64_t N, int64_t d, int32_t order,
+                        const int64_t* dims, int32_t ndims, int32_t io_dtype,
+                        int32_t spec_dtype, int32_t path);
+void set_error(const std::string& msg);
+hyena_status fail(hyena_status s, const std::string& msg);
+
+// Implemented in the .hip launchers.
+hyena_status launch_tw_init(const Plan& p, void* ws, void* stream);
+hyena_status launch_lds1d_spectrum(const Plan& p, const void* h, void* H, const void* ws, void* stream);
+hyena_status launch_lds1d_forward(const Plan& p, const void* u, const void* const* gates,
+                                  const void* H, const float* D, void* y, const void* ws,
+                                  void* stream);
+hyena_status launch_lds1d_export(const Plan& p, const void* H, void* out, void* stream);
+
+hyena_status launch_fourstep_spectrum(const Plan& p, const void* h, void* H, void* ws, void* stream);
+hyena_status launch_fourstep_forward(const Plan& p, const void* u, const void* const* gates,
+                                     const void* H, const float* D, void* y, void* ws,
+                                     void* stream);
+hyena_status launch_fourstep_export(const Plan& p, const void* H, void* out, void* stream);
+
+hyena_status launch_rowcol2d_spectrum(const Plan& p, const void* h, void* H, void* ws, void* stream);
+hyena_status launch_rowcol2d_forward(const Plan& p, const void* u, const void* const* gates,
+                                     const void* H, const float* D, void* y, void* ws,
+                                     void* stream);
+hyena_status launch_rowcol2d_export(const Plan& p, const void* H, void* out, void* stream);
+
+}  // namespace hy

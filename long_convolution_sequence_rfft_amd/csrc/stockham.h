@@ -1,0 +1,371 @@
+// stockham.h -- one length-L complex transform held by a group of threads,
+// radix passes in registers, exchanges through LDS (Stockham autosort: no
+// bit-reversal pass), plus the channel-pair spectral product.
+//
+// A radix-R pass with sub-transform length NS reads butterfly j's inputs at
+// j + r L/R, multiplies input r by W_{NS R}^{r k} (k = j mod NS), takes a
+// length-R DFT and writes output s to (j - k) R + k + s NS; after the last
+// pass the transform is in natural order.  The passes are R0, R1 (optional),
+// RL forward and RL, R1, R0 inverse, so the inverse's last pass leaves each
+// thread holding exactly the time samples the next forward pass starts from.
+//
+// The convolution theorem and the 2N zero padding that keeps the cyclic
+// product causal follow "Hyena -- Long Convolutions Math", sections "The
+// convolution theorem" and "Linear vs circular".
+#pragma once
+
+#include "fft_device.h"
+#include "plan.h"
+
+namespace hy {
+
+template <int L>
+struct FftShape {
+    static constexpr int PTS = lds1d_pts(L);  // complex values per thread
+    static constexpr int T = L / PTS;         // threads per transform
+    static constexpr int RL = lds1d_rl(L);
+    static constexpr int R0 = lds1d_r0(L);
+    static constexpr int R1 = lds1d_r1(L);
+    static constexpr int Q0 = PTS / R0;  // butterflies per thread in the R0 pass
+    static constexpr int Q1 = PTS / R1;
+    static constexpr int LW = lds_words(L);
+    static_assert(R0 * R1 * RL == L, "radix plan");
+    static_assert(RL * 2 == PTS, "last pass must give two butterflies per thread");
+};
+
+// ---------------------------------------------------------------------------
+// storage access (float32 or bfloat16 stored as uint16_t)
+// ---------------------------------------------------------------------------
+template <typename IO>
+__device__ __forceinline__ float ld1(const IO* p)
+{
+    if constexpr (sizeof(IO) == 4) return *p;
+    else return bf16_to_f32(*p);
+}
+
+template <typename IO>
+__device__ __forceinline__ void st1(IO* p, float v)
+{
+    if constexpr (sizeof(IO) == 4) *p = v;
+    else *p = f32_to_bf16(v);
+}
+
+// Channel pair (c, c+1) of a channels-last row.  EVEN: d is even, so the
+// pair is one aligned 8-byte (f32) or 4-byte (bf16) access.
+template <typename IO, bool EVEN>
+__device__ __forceinline__ float2 load_pair(const IO* row, bool has_b)
+{
+    if constexpr (EVEN) {
+        if constexpr (sizeof(IO) == 4) {
+            return *reinterpret_cast<const float2*>(row);
+        } else {
+            const uint32_t w = *reinterpret_cast<const uint32_t*>(row);
+            return make_float2(__uint_as_float(w << 16), __uint_as_float(w & 0xffff0000u));
+        }
+    } else {
+        return make_float2(ld1<IO>(row), has_b ? ld1<IO>(row + 1) : 0.0f);
+    }
+}
+
+template <typename IO, bool EVEN>
+__device__ __forceinline__ void store_pair(IO* row, float2 v, bool has_b)
+{
+    if constexpr (EVEN) {
+        if constexpr (sizeof(IO) == 4) {
+            *reinterpret_cast<float2*>(row) = v;
+        } else {
+            const uint32_t w = (uint32_t)f32_to_bf16(v.x) | ((uint32_t)f32_to_bf16(v.y) << 16);
+            *reinterpret_cast<uint32_t*>(row) = w;
+        }
+    } else {
+        st1<IO>(row, v.x);
+        if (has_b) st1<IO>(row + 1, v.y);
+    }
+}
+
+// One spectrum entry (P, Q): a float4 for f32, four bfloat16 in 8 bytes.
+template <typename SP>
+__device__ __forceinline__ void load_entry(const SP* spec, int64_t e, float2& P, float2& Q)
+{
+    if constexpr (sizeof(SP) == 4) {
+        const float4 r = reinterpret_cast<const float4*>(spec)[e];
+        P = make_float2(r.x, r.y);
+        Q = make_float2(r.z, r.w);
+    } else {
+        const uint2 r = reinterpret_cast<const uint2*>(spec)[e];
+        P = make_float2(__uint_as_float(r.x << 16), __uint_as_float(r.x & 0xffff0000u));
+        Q = make_float2(__uint_as_float(r.y << 16), __uint_as_float(r.y & 0xffff0000u));
+    }
+}
+
+template <typename SP>
+__device__ __forceinline__ void store_entry(SP* spec, int64_t e, float2 P, float2 Q)
+{
+    if constexpr (sizeof(SP) == 4) {
+        reinterpret_cast<float4*>(spec)[e] = make_float4(P.x, P.y, Q.x, Q.y);
+    } else {
+        uint2 r;
+        r.x = (uint32_t)f32_to_bf16(P.x) | ((uint32_t)f32_to_bf16(P.y) << 16);
+        r.y = (uint32_t)f32_to_bf16(Q.x) | ((uint32_t)f32_to_bf16(Q.y) << 16);
+        reinterpret_cast<uint2*>(spec)[e] = r;
+    }
+}
+
+// Elements of one spectrum entry, in units of SP (four reals per entry).
+constexpr int kEntryElems = 4;
+
+// ---------------------------------------------------------------------------
+// pass pieces
+// ---------------------------------------------------------------------------
+// Every access below is lpad(A + c) with a run-time A and a compile-time c.
+// For these Stockham patterns A mod 32 + c mod 32 < 32 always holds (reads:
+// A = j < L/R and c a multiple of L/R, L/R a power of two; writes: A is the
+// output base and c = s NS, both aligned to NS R or to 32), so
+// lpad(A + c) = lpad(A) + c + c/32 and c becomes an instruction offset.
+template <int R, int NS>
+__device__ __forceinline__ void lds_write(float* sre, float* sim, const float2* v, int j)
+{
+    const int k = j & (NS - 1);
+    const int pb = lpad((j - k) * R + k);
+#pragma unroll
+    for (int s = 0; s < R; ++s) {
+        const int c = s * NS;
+        const int i = pb + c + (c >> 5);
+        sre[i] = v[s].x;
+        sim[i] = v[s].y;
+    }
+}
+
+template <int R, int L>
+__device__ __forceinline__ void lds_read(const float* sre, const float* sim, float2* v, int j)
+{
+    const int pb = lpad(j);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int c = r * (L / R);
+        const int i = pb + c + (c >> 5);
+        v[r] = make_float2(sre[i], sim[i]);
+    }
+}
+
+// Twiddles of butterfly k: the run tab[k R .. k R + R) (entry 0 is 1).
+template <int R, int DIR>
+__device__ __forceinline__ void apply_tw(float2* v, const float2* tab, int k)
+{
+    const float4* t = reinterpret_cast<const float4*>(tab + k * R);
+#pragma unroll
+    for (int i = 0; i < R / 2; ++i) {
+        const float4 w = t[i];
+        if (i > 0) v[2 * i] = ctw<DIR>(v[2 * i], make_float2(w.x, w.y));
+        v[2 * i + 1] = ctw<DIR>(v[2 * i + 1], make_float2(w.z, w.w));
+    }
+}
+
+// Twiddle-table offsets (float2 units) of one transform length.
+struct TwOffsets {
+    int32_t f1, fL, i1, i0;
+};
+
+// Forward transform.  On entry v holds the R0-pass inputs of butterflies
+// tau + q T (values r < R0/2; the upper half is the zero padding and is never
+// read).  On return v[0..RL) and v[RL..2RL) hold the outputs of last-pass
+// butterflies j1 and j2: bins j1 + s L/RL and j2 + s L/RL.
+// sync_first: LDS may still be read by the previous step (WAR barrier).
+template <int L>
+__device__ __forceinline__ void fwd_transform(float2* v, float* sre, float* sim, const float2* tw,
+                                              TwOffsets o, int tau, int j1, int j2,
+                                              bool sync_first)
+{
+    using S = FftShape<L>;
+    constexpr int T = S::T, R0 = S::R0, R1 = S::R1, RL = S::RL;
+#pragma unroll
+    for (int q = 0; q < S::Q0; ++q) dft<R0, -1, true, false>(&v[q * R0]);
+    if (sync_first) __syncthreads();
+#pragma unroll
+    for (int q = 0; q < S::Q0; ++q) lds_write<R0, 1>(sre, sim, &v[q * R0], tau + q * T);
+    __syncthreads();
+    if constexpr (R1 > 1) {
+#pragma unroll
+        for (int q = 0; q < S::Q1; ++q) lds_read<R1, L>(sre, sim, &v[q * R1], tau + q * T);
+#pragma unroll
+        for (int q = 0; q < S::Q1; ++q) {
+            const int j = tau + q * T;
+            apply_tw<R1, -1>(&v[q * R1], tw + o.f1, j & (R0 - 1));
+            dft<R1, -1>(&v[q * R1]);
+        }
+        __syncthreads();
+#pragma unroll
+        for (int q = 0; q < S::Q1; ++q) lds_write<R1, R0>(sre, sim, &v[q * R1], tau + q * T);
+        __syncthreads();
+    }
+    lds_read<RL, L>(sre, sim, &v[0], j1);
+    lds_read<RL, L>(sre, sim, &v[RL], j2);
+    apply_tw<RL, -1>(&v[0], tw + o.fL, j1);
+    apply_tw<RL, -1>(&v[RL], tw + o.fL, j2);
+    dft<RL, -1>(&v[0]);
+    dft<RL, -1>(&v[RL]);
+}
+
+// Inverse transform (unscaled) from the last-pass registers (butterflies j1,
+// j2) back to the R0-pass layout: v[q R0 + s], s < R0/2, is sample
+// tau + q T + s L/R0.  Only the first half of the samples is produced.
+template <int L>
+__device__ __forceinline__ void inv_transform(float2* v, float* sre, float* sim, const float2* tw,
+                                              TwOffsets o, int tau, int j1, int j2)
+{
+    using S = FftShape<L>;
+    constexpr int T = S::T, R0 = S::R0, R1 = S::R1, RL = S::RL;
+    dft<RL, +1>(&v[0]);
+    dft<RL, +1>(&v[RL]);
+    __syncthreads();
+    lds_write<RL, 1>(sre, sim, &v[0], j1);
+    lds_write<RL, 1>(sre, sim, &v[RL], j2);
+    __syncthreads();
+    if constexpr (R1 > 1) {
+#pragma unroll
+        for (int q = 0; q < S::Q1; ++q) lds_read<R1, L>(sre, sim, &v[q * R1], tau + q * T);
+#pragma unroll
+        for (int q = 0; q < S::Q1; ++q) {
+            const int j = tau + q * T;
+            apply_tw<R1, +1>(&v[q * R1], tw + o.i1, j & (RL - 1));
+            dft<R1, +1>(&v[q * R1]);
+        }
+        __syncthreads();
+#pragma unroll
+        for (int q = 0; q < S::Q1; ++q) lds_write<R1, RL>(sre, sim, &v[q * R1], tau + q * T);
+        __syncthreads();
+    }
+#pragma unroll
+    for (int q = 0; q < S::Q0; ++q) {
+        const int j = tau + q * T;
+        lds_read<R0, L>(sre, sim, &v[q * R0], j);
+        apply_tw<R0, +1>(&v[q * R0], tw + o.i0, j);
+        dft<R0, +1, false, true>(&v[q * R0]);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Channel-pair spectral product.  Two real channels a, b ride in one complex
+// signal z = a + i b.  With Z = DFT(z), the spectrum of a*ha + i (b*hb) is
+//   Y[k] = Z[k] P[k] + conj(Z[-k]) Q[k],  P = (Ha + Hb)/2,  Q = (Ha - Hb)/2,
+// because DFT(a) = (Z[k] + conj Z[-k])/2 and DFT(b) = (Z[k] - conj Z[-k])/2i.
+// A bin and its mirror are computed together from one (P, Q) entry:
+//   Y[-k] = Z[-k] conj(P[k]) + conj(Z[k]) conj(Q[k]).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void pair_product(float2& zp, float2& zm, float2 P, float2 Q)
+{
+    const float ypx = fmaf(zp.x, P.x, fmaf(-zp.y, P.y, fmaf(zm.x, Q.x, zm.y * Q.y)));
+    const float ypy = fmaf(zp.x, P.y, fmaf(zp.y, P.x, fmaf(zm.x, Q.y, -zm.y * Q.x)));
+    const float ymx = fmaf(zm.x, P.x, fmaf(zm.y, P.y, fmaf(zp.x, Q.x, -zp.y * Q.y)));
+    const float ymy = fmaf(zm.y, P.x, fmaf(-zm.x, P.y, fmaf(-zp.x, Q.y, -zp.y * Q.x)));
+    zp = make_float2(ypx, ypy);
+    zm = make_float2(ymx, ymy);
+}
+
+// A self-mirrored bin (k = -k): P and Q are real.
+__device__ __forceinline__ float2 self_product(float2 z, float P, float Q)
+{
+    return make_float2(z.x * (P + Q), z.y * (P - Q));
+}
+
+// Filter side: from Z = DFT(ha + i hb) at a bin and its mirror, the entry
+// ((Ha + Hb), (Ha - Hb)) * scale with Ha = (zp + conj zm)/2, Hb = (zp - conj zm)/2i.
+__device__ __forceinline__ void entry_from_pair(float2 zp, float2 zm, float scale, float2& P,
+                                                float2& Q)
+{
+    const float2 Ha = make_float2(0.5f * (zp.x + zm.x), 0.5f * (zp.y - zm.y));
+    const float2 Hb = make_float2(0.5f * (zp.y + zm.y), -0.5f * (zp.x - zm.x));
+    P = make_float2((Ha.x + Hb.x) * scale, (Ha.y + Hb.y) * scale);
+    Q = make_float2((Ha.x - Hb.x) * scale, (Ha.y - Hb.y) * scale);
+}
+
+// Mirror-paired product on the last-pass registers of one length-L transform.
+// Entry e of thread tau sits at entry index e T + tau.
+//   tau > 0: last-pass butterflies tau and 2T - tau; entry e pairs output e of
+//            the first with output RL-1-e of the second; the bin <= L/2 is
+//            the first's for e < RL/2, the second's otherwise.
+//   tau = 0: butterflies 0 and T; entry 0 packs the self-mirrored bins 0 and
+//            L/2 (real P, Q), entries 1..RL/2-1 pair outputs (e, RL-e) of
+//            butterfly 0, entries RL/2.. pair outputs (s, RL-1-s) of butterfly T.
+// dp, dq: real offsets added to every P and Q (the folded feedthrough).
+template <int L, typename SP>
+__device__ __forceinline__ void spectral_product(float2* v, const SP* spec, int tau, float dp,
+                                                 float dq)
+{
+    using S = FftShape<L>;
+    constexpr int T = S::T, RL = S::RL;
+    if (tau != 0) {
+#pragma unroll
+        for (int e = 0; e < RL; ++e) {
+            float2 P, Q;
+            load_entry(spec, e * T + tau, P, Q);
+            P.x += dp;
+            Q.x += dq;
+            if (e < RL / 2) pair_product(v[e], v[2 * RL - 1 - e], P, Q);
+            else pair_product(v[2 * RL - 1 - e], v[e], P, Q);
+        }
+    } else {
+        float2 P, Q;
+        load_entry(spec, 0, P, Q);
+        v[0] = self_product(v[0], P.x + dp, Q.x + dq);
+        v[RL / 2] = self_product(v[RL / 2], P.y + dp, Q.y + dq);
+#pragma unroll
+        for (int e = 1; e < RL / 2; ++e) {
+            load_entry(spec, e * T, P, Q);
+            P.x += dp;
+            Q.x += dq;
+            pair_product(v[e], v[RL - e], P, Q);
+        }
+#pragma unroll
+        for (int e = RL / 2; e < RL; ++e) {
+            const int s = e - RL / 2;
+            load_entry(spec, e * T, P, Q);
+            P.x += dp;
+            Q.x += dq;
+            pair_product(v[RL + s], v[2 * RL - 1 - s], P, Q);
+        }
+    }
+}
+
+// Filter side of the same layout: write the entries of one transform.
+template <int L, typename SP>
+__device__ __forceinline__ void store_spectrum_entries(const float2* v, SP* spec, int tau,
+                                                       float scale)
+{
+    using S = FftShape<L>;
+    constexpr int T = S::T, RL = S::RL;
+    float2 P, Q;
+    if (tau != 0) {
+#pragma unroll
+        for (int e = 0; e < RL; ++e) {
+            if (e < RL / 2) entry_from_pair(v[e], v[2 * RL - 1 - e], scale, P, Q);
+            else entry_from_pair(v[2 * RL - 1 - e], v[e], scale, P, Q);
+            store_entry(spec, e * T + tau, P, Q);
+        }
+    } else {
+        const float2 z0 = v[0], zh = v[RL / 2];
+        store_entry(spec, 0, make_float2((z0.x + z0.y) * scale, (zh.x + zh.y) * scale),
+                    make_float2((z0.x - z0.y) * scale, (zh.x - zh.y) * scale));
+#pragma unroll
+        for (int e = 1; e < RL / 2; ++e) {
+            entry_from_pair(v[e], v[RL - e], scale, P, Q);
+            store_entry(spec, e * T, P, Q);
+        }
+#pragma unroll
+        for (int e = RL / 2; e < RL; ++e) {
+            const int s = e - RL / 2;
+            entry_from_pair(v[RL + s], v[2 * RL - 1 - s], scale, P, Q);
+            store_entry(spec, e * T, P, Q);
+        }
+    }
+}
+
+// Bin of entry (tau, e) of a length-L transform (entry (0, 0) also holds L/2).
+__host__ __device__ inline int64_t entry_bin(int64_t L, int64_t T, int64_t tau, int64_t e)
+{
+    const int64_t RL = L / (2 * T);
+    if (tau == 0) return e < RL / 2 ? e * 2 * T : T + (e - RL / 2) * 2 * T;
+    return e < RL / 2 ? tau + e * 2 * T : (2 * T - tau) + (RL - 1 - e) * 2 * T;
+}
+
+}  // namespace hy

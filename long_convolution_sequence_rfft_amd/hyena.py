@@ -1,0 +1,237 @@
+"""ctypes binding to ``libhyena_mi355x.so`` (the C ABI of include/hyena.h).
+
+The functions below carry the C names and only marshal arguments: every step
+of the computation runs in the library's HIP kernels.  ``Plan`` is a small
+convenience wrapper that takes torch tensors (torch provides device memory
+and the current HIP stream) and calls the same entry points.
+
+There is no fallback: if the library is missing, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libhyena_mi355x.so")
+
+HYENA_OK = 0
+HYENA_ERR_INVALID_ARGUMENT = 1
+HYENA_ERR_UNSUPPORTED = 2
+HYENA_ERR_WORKSPACE = 3
+HYENA_ERR_DEVICE = 4
+
+HYENA_F32 = 0
+HYENA_BF16 = 1
+
+HYENA_PATH_AUTO = 0
+HYENA_PATH_LDS1D = 1
+HYENA_PATH_FOURSTEP1D = 2
+HYENA_PATH_ROWCOL2D = 3
+
+EXPORTED_SYMBOLS = (
+    "hyena_plan_create", "hyena_plan_query", "hyena_workspace_init", "hyena_filter_spectrum",
+    "hyena_forward", "hyena_spectrum_export", "hyena_plan_destroy", "hyena_status_string",
+    "hyena_last_error",
+)
+
+_lock = threading.Lock()
+_lib = None
+
+
+class HyenaError(RuntimeError):
+    def __init__(self, status: int, where: str, detail: str):
+        super().__init__(f"{where}: {status_name(status)}: {detail}")
+        self.status = status
+
+
+def load():
+    """Load the HIP library (raises if it has not been built)."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise RuntimeError(
+                    f"{LIB_PATH} is missing: build it with "
+                    "long_convolution_sequence_rfft_amd.build.build()")
+            lib = ctypes.CDLL(LIB_PATH)
+            i64, i32, p, sz = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t
+            lib.hyena_plan_create.argtypes = [ctypes.POINTER(p), i64, i64, i64, i32,
+                                              ctypes.POINTER(i64), i32, i32, i32, i32]
+            lib.hyena_plan_query.argtypes = [p, ctypes.POINTER(sz), ctypes.POINTER(sz),
+                                             ctypes.POINTER(i32)]
+            lib.hyena_workspace_init.argtypes = [p, p, p]
+            lib.hyena_filter_spectrum.argtypes = [p, p, p, p, p]
+            lib.hyena_forward.argtypes = [p, p, ctypes.POINTER(p), p, p, p, p, p]
+            lib.hyena_spectrum_export.argtypes = [p, p, p, p]
+            lib.hyena_plan_destroy.argtypes = [p]
+            lib.hyena_status_string.argtypes = [ctypes.c_int]
+            lib.hyena_status_string.restype = ctypes.c_char_p
+            lib.hyena_last_error.argtypes = []
+            lib.hyena_last_error.restype = ctypes.c_char_p
+            for name in ("hyena_plan_create", "hyena_plan_query", "hyena_workspace_init",
+                         "hyena_filter_spectrum", "hyena_forward", "hyena_spectrum_export",
+                         "hyena_plan_destroy"):
+                getattr(lib, name).restype = ctypes.c_int
+            _lib = lib
+    return _lib
+
+
+def status_name(status: int) -> str:
+    return load().hyena_status_string(int(status)).decode()
+
+
+def hyena_last_error() -> str:
+    return load().hyena_last_error().decode()
+
+
+def hyena_status_string(status: int) -> str:
+    return status_name(status)
+
+
+def _check(status: int, where: str):
+    if status != HYENA_OK:
+        raise HyenaError(status, where, hyena_last_error())
+
+
+# --------------------------------------------------------------------------
+# C entry points (raw pointers as Python ints)
+# --------------------------------------------------------------------------
+
+def hyena_plan_create(B, N, d, order, dims, io_dtype=HYENA_F32, spectrum_dtype=None,
+                      path=HYENA_PATH_AUTO, check=True):
+    """Returns (status, plan handle or None)."""
+    lib = load()
+    if spectrum_dtype is None:
+        spectrum_dtype = io_dtype
+    dims_arr = (ctypes.c_int64 * max(1, len(dims)))(*[int(x) for x in dims])
+    h = ctypes.c_void_p()
+    st = lib.hyena_plan_create(ctypes.byref(h), int(B), int(N), int(d), int(order), dims_arr,
+                               len(dims), int(io_dtype), int(spectrum_dtype), int(path))
+    if check:
+        _check(st, "hyena_plan_create")
+    return st, (h.value if st == HYENA_OK else None)
+
+
+def hyena_plan_query(plan):
+    spec = ctypes.c_size_t()
+    ws = ctypes.c_size_t()
+    path = ctypes.c_int32()
+    _check(load().hyena_plan_query(plan, ctypes.byref(spec), ctypes.byref(ws), ctypes.byref(path)),
+           "hyena_plan_query")
+    return spec.value, ws.value, path.value
+
+
+def hyena_workspace_init(plan, workspace, stream=0):
+    return load().hyena_workspace_init(plan, workspace, stream)
+
+
+def hyena_filter_spectrum(plan, h, H, workspace, stream=0):
+    return load().hyena_filter_spectrum(plan, h, H, workspace, stream)
+
+
+def hyena_forward(plan, u, gates, H, D, y, workspace, stream=0):
+    arr = (ctypes.c_void_p * max(1, len(gates)))(*gates)
+    return load().hyena_forward(plan, u, arr, H, D, y, workspace, stream)
+
+
+def hyena_spectrum_export(plan, H, natural, stream=0):
+    return load().hyena_spectrum_export(plan, H, natural, stream)
+
+
+def hyena_plan_destroy(plan):
+    return load().hyena_plan_destroy(plan)
+
+
+# --------------------------------------------------------------------------
+# torch convenience wrapper (device memory and stream plumbing only)
+# --------------------------------------------------------------------------
+
+class Plan:
+    """One plan plus its workspace on a torch device.
+
+    ``dims`` is ``(N,)`` for sequences or ``(X, Y)`` for grids.  Tensors are
+    float32 or bfloat16 (io), channels last; see include/hyena.h for layouts.
+    """
+
+    def __init__(self, B, d, order, dims, io_dtype=HYENA_F32, spectrum_dtype=None,
+                 path=HYENA_PATH_AUTO, device="cuda"):
+        import torch
+        self.torch = torch
+        N = 1
+        for v in dims:
+            N *= int(v)
+        self.B, self.N, self.d, self.order, self.dims = int(B), N, int(d), int(order), tuple(dims)
+        self.io_dtype = io_dtype
+        self.spectrum_dtype = io_dtype if spectrum_dtype is None else spectrum_dtype
+        _, self.handle = hyena_plan_create(B, N, d, order, dims, io_dtype, self.spectrum_dtype,
+                                           path)
+        self.spectrum_bytes, self.workspace_bytes, self.path = hyena_plan_query(self.handle)
+        dev = torch.device(device)
+        if dev.type == "cuda" and dev.index is None:
+            dev = torch.device("cuda", torch.cuda.current_device())
+        self.device = dev
+        self.workspace = torch.empty(max(self.workspace_bytes, 256), dtype=torch.uint8,
+                                     device=self.device)
+        _check(hyena_workspace_init(self.handle, self.workspace.data_ptr(), self.stream()),
+               "hyena_workspace_init")
+
+    def stream(self):
+        return self.torch.cuda.current_stream(self.device).cuda_stream
+
+    @property
+    def torch_io_dtype(self):
+        return self.torch.float32 if self.io_dtype == HYENA_F32 else self.torch.bfloat16
+
+    def _io(self, t, name):
+        if t.dtype != self.torch_io_dtype or not t.is_contiguous() or t.device != self.device:
+            raise ValueError(f"{name} must be a contiguous {self.torch_io_dtype} tensor on "
+                             f"{self.device}")
+        return t
+
+    def spectrum(self, h, H=None):
+        h = self._io(h, "h")
+        if H is None:
+            H = self.torch.empty(self.spectrum_bytes, dtype=self.torch.uint8, device=self.device)
+        _check(hyena_filter_spectrum(self.handle, h.data_ptr(), H.data_ptr(),
+                                     self.workspace.data_ptr(), self.stream()),
+               "hyena_filter_spectrum")
+        return H
+
+    def forward(self, u, gates, H, D, y=None):
+        u = self._io(u, "u")
+        gates = [self._io(g, "gate") for g in gates]
+        if len(gates) != self.order:
+            raise ValueError("need one gate per filter")
+        if D.dtype != self.torch.float32 or not D.is_contiguous():
+            raise ValueError("D must be contiguous float32 [order, d]")
+        if y is None:
+            y = self.torch.empty_like(u)
+        _check(hyena_forward(self.handle, u.data_ptr(), [g.data_ptr() for g in gates],
+                             H.data_ptr(), D.data_ptr(), y.data_ptr(), self.workspace.data_ptr(),
+                             self.stream()),
+               "hyena_forward")
+        return y
+
+    def export_spectrum(self, H):
+        if len(self.dims) == 1:
+            M = 1
+            while M < 2 * self.N:
+                M *= 2
+            shape = (self.order, self.d, M // 2 + 1, 2)
+        else:
+            X, Y = self.dims
+            shape = (self.order, self.d, 2 * X, Y + 1, 2)
+        out = self.torch.zeros(shape, dtype=self.torch.float32, device=self.device)
+        _check(hyena_spectrum_export(self.handle, H.data_ptr(), out.data_ptr(), self.stream()),
+               "hyena_spectrum_export")
+        return out
+
+    def __del__(self):
+        try:
+            if getattr(self, "handle", None):
+                hyena_plan_destroy(self.handle)
+                self.handle = None
+        except Exception:
+            pass

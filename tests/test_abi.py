@@ -1,0 +1,175 @@
+"""The C-ABI library: it loads, exports every symbol include/hyena.h
+declares, and its host-side validation returns the documented status codes
+(no GPU work is started by any of these calls)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from long_convolution_sequence_rfft_amd import hyena
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _header_functions():
+    text = open(os.path.join(ROOT, "include", "hyena.h")).read()
+    return sorted(set(re.findall(r"\b(hyena_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = hyena.load()
+    names = _header_functions()
+    assert set(names) == set(hyena.EXPORTED_SYMBOLS)
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_status_strings():
+    assert hyena.hyena_status_string(0) == "HYENA_OK"
+    assert hyena.hyena_status_string(3) == "HYENA_ERR_WORKSPACE"
+    assert hyena.hyena_status_string(99) == "HYENA_ERR_UNKNOWN"
+
+
+@pytest.mark.parametrize("args,code", [
+    (dict(B=0, N=8, d=2, order=1, dims=[8]), hyena.HYENA_ERR_INVALID_ARGUMENT),
+    (dict(B=1, N=8, d=0, order=1, dims=[8]), hyena.HYENA_ERR_INVALID_ARGUMENT),
+    (dict(B=1, N=8, d=2, order=0, dims=[8]), hyena.HYENA_ERR_UNSUPPORTED),
+    (dict(B=1, N=8, d=2, order=9, dims=[8]), hyena.HYENA_ERR_UNSUPPORTED),
+    (dict(B=1, N=8, d=2, order=1, dims=[4]), hyena.HYENA_ERR_INVALID_ARGUMENT),
+    (dict(B=1, N=2, d=2, order=1, dims=[2]), hyena.HYENA_ERR_UNSUPPORTED),
+    (dict(B=1, N=65537, d=2, order=1, dims=[65537]), hyena.HYENA_ERR_UNSUPPORTED),
+    (dict(B=1, N=64, d=2, order=1, dims=[8, 8], path=hyena.HYENA_PATH_LDS1D),
+     hyena.HYENA_ERR_UNSUPPORTED),
+    (dict(B=1, N=60, d=2, order=1, dims=[6, 10]), hyena.HYENA_ERR_UNSUPPORTED),
+    (dict(B=1, N=64, d=2, order=1, dims=[8, 4]), hyena.HYENA_ERR_INVALID_ARGUMENT),
+    (dict(B=1, N=16384, d=2, order=1, dims=[16384], path=hyena.HYENA_PATH_LDS1D),
+     hyena.HYENA_ERR_UNSUPPORTED),
+    (dict(B=1, N=256, d=2, order=1, dims=[256], path=hyena.HYENA_PATH_FOURSTEP1D),
+     hyena.HYENA_ERR_UNSUPPORTED),
+    (dict(B=1, N=64, d=2, order=1, dims=[64], io_dtype=hyena.HYENA_F32,
+          spectrum_dtype=hyena.HYENA_BF16), hyena.HYENA_ERR_UNSUPPORTED),
+    (dict(B=1, N=64, d=2, order=1, dims=[64], io_dtype=7), hyena.HYENA_ERR_UNSUPPORTED),
+    (dict(B=1, N=64, d=2, order=1, dims=[64], path=9), hyena.HYENA_ERR_UNSUPPORTED),
+])
+def test_plan_create_rejects(args, code):
+    st, plan = hyena.hyena_plan_create(check=False, **args)
+    assert st == code, hyena.hyena_last_error()
+    assert plan is None
+    assert hyena.hyena_last_error()
+
+
+def test_plan_create_null_output_pointer():
+    lib = hyena.load()
+    dims = (ctypes.c_int64 * 1)(8)
+    assert lib.hyena_plan_create(None, 1, 8, 2, 1, dims, 1, 0, 0, 0) == \
+        hyena.HYENA_ERR_INVALID_ARGUMENT
+
+
+@pytest.mark.parametrize("N,path,M", [(4, 1, 8), (256, 1, 512), (2048, 1, 4096),
+                                      (5000, 1, 16384), (8192, 1, 16384), (65536, 2, 131072),
+                                      (16385, 2, 65536)])
+def test_path_choice_and_sizes(N, path, M):
+    _, plan = hyena.hyena_plan_create(2, N, 6, 2, [N])
+    spec, ws, p = hyena.hyena_plan_query(plan)
+    assert p == path
+    assert spec == 2 * 3 * (M // 2) * 16  # order * pairs * M/2 entries * 16 bytes
+    assert ws >= 256
+    hyena.hyena_plan_destroy(plan)
+
+
+def test_2d_plan_sizes():
+    _, plan = hyena.hyena_plan_create(1, 256 * 256, 256, 2, [256, 256])
+    spec, ws, p = hyena.hyena_plan_query(plan)
+    assert p == hyena.HYENA_PATH_ROWCOL2D
+    assert spec == 2 * 128 * (512 * 512 // 2) * 16
+    hyena.hyena_plan_destroy(plan)
+
+
+def test_bf16_spectrum_halves_bytes():
+    _, p32 = hyena.hyena_plan_create(2, 8192, 768, 2, [8192], hyena.HYENA_BF16, hyena.HYENA_F32)
+    _, p16 = hyena.hyena_plan_create(2, 8192, 768, 2, [8192], hyena.HYENA_BF16, hyena.HYENA_BF16)
+    assert hyena.hyena_plan_query(p32)[0] == 2 * hyena.hyena_plan_query(p16)[0]
+    # the headline accounting: 2N reals per channel and filter at 2 bytes
+    assert hyena.hyena_plan_query(p16)[0] == 2 * 768 * 2 * 8192 * 2
+    hyena.hyena_plan_destroy(p32)
+    hyena.hyena_plan_destroy(p16)
+
+
+class _Fake:
+    """Aligned, distinct, never-dereferenced addresses: validation fails first."""
+    base = 1 << 40
+
+    @classmethod
+    def ptr(cls, i):
+        return cls.base + i * (1 << 32)
+
+
+def _plan(N=64, d=4, order=2):
+    _, plan = hyena.hyena_plan_create(1, N, d, order, [N])
+    return plan
+
+
+def test_forward_validation_codes():
+    plan = _plan()
+    f = _Fake.ptr
+    u, g0, g1, H, D, y, ws = (f(i) for i in range(7))
+    # null pointers
+    assert hyena.hyena_forward(plan, None, [g0, g1], H, D, y, ws) == hyena.HYENA_ERR_INVALID_ARGUMENT
+    assert hyena.hyena_forward(plan, u, [g0, None], H, D, y, ws) == hyena.HYENA_ERR_INVALID_ARGUMENT
+    assert hyena.hyena_forward(plan, u, [g0, g1], H, D, y, None) == hyena.HYENA_ERR_INVALID_ARGUMENT
+    # misaligned
+    assert hyena.hyena_forward(plan, u + 4, [g0, g1], H, D, y, ws) == hyena.HYENA_ERR_INVALID_ARGUMENT
+    # y overlapping u, a gate, H
+    assert hyena.hyena_forward(plan, u, [g0, g1], H, D, u + 16, ws) == hyena.HYENA_ERR_INVALID_ARGUMENT
+    assert hyena.hyena_forward(plan, u, [g0, g1], H, D, g1, ws) == hyena.HYENA_ERR_INVALID_ARGUMENT
+    assert hyena.hyena_forward(plan, u, [g0, g1], H, D, H + 32, ws) == hyena.HYENA_ERR_INVALID_ARGUMENT
+    # valid pointers but the workspace was never initialised for this plan
+    assert hyena.hyena_forward(plan, u, [g0, g1], H, D, y, ws) == hyena.HYENA_ERR_WORKSPACE
+    assert "hyena_workspace_init" in hyena.hyena_last_error()
+    assert hyena.hyena_filter_spectrum(plan, u, H, ws) == hyena.HYENA_ERR_WORKSPACE
+    assert hyena.hyena_filter_spectrum(plan, None, H, ws) == hyena.HYENA_ERR_INVALID_ARGUMENT
+    assert hyena.hyena_workspace_init(plan, None) == hyena.HYENA_ERR_INVALID_ARGUMENT
+    assert hyena.hyena_workspace_init(plan, ws + 8) == hyena.HYENA_ERR_INVALID_ARGUMENT
+    assert hyena.hyena_spectrum_export(plan, None, y) == hyena.HYENA_ERR_INVALID_ARGUMENT
+    assert hyena.hyena_forward(None, u, [g0, g1], H, D, y, ws) == hyena.HYENA_ERR_INVALID_ARGUMENT
+    assert hyena.hyena_plan_destroy(plan) == hyena.HYENA_OK
+    assert hyena.hyena_plan_destroy(None) == hyena.HYENA_OK
+
+
+def test_last_error_is_thread_local():
+    import threading
+    st, _ = hyena.hyena_plan_create(0, 8, 2, 1, [8], check=False)
+    main_msg = hyena.hyena_last_error()
+    seen = {}
+
+    def other():
+        hyena.hyena_plan_create(1, 8, 2, 99, [8], check=False)
+        seen["msg"] = hyena.hyena_last_error()
+
+    t = threading.Thread(target=other)
+    t.start()
+    t.join()
+    assert "order" in seen["msg"]
+    assert hyena.hyena_last_error() == main_msg
+
+
+def test_plans_can_be_created_from_many_threads():
+    import threading
+    errs = []
+
+    def work():
+        try:
+            for N in (64, 1000, 8192, 65536):
+                _, p = hyena.hyena_plan_create(2, N, 10, 2, [N])
+                hyena.hyena_plan_query(p)
+                hyena.hyena_plan_destroy(p)
+        except Exception as e:  # pragma: no cover
+            errs.append(e)
+
+    ts = [threading.Thread(target=work) for _ in range(8)]
+    for t in ts:
+        t.start()
+    for t in ts:
+        t.join()
+    assert not errs
