@@ -1,0 +1,372 @@
+#!/usr/bin/env python3
+"""Throughput of the Hyena long-convolution chain forward on one MI355X.
+
+One step = one ``hyena_forward`` call (every stage of the order-N chain:
+transform, spectral product with feedthrough, inverse, gate) over one batch of
+synthetic inputs already resident in HBM.  Filter spectra are computed once
+before timing (``hyena_filter_spectrum`` is timed separately and reported).
+
+Prints one JSON line.  ``value`` is token*channels per second of the headline
+workload (B=2, N=8192, d=768, order 2, bfloat16 storage, float32 arithmetic);
+the other workloads are reported under ``workloads``.  Inputs rotate over
+several buffer sets so that the working set of the timed loop exceeds the
+256 MB last-level cache.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--only NAME]
+                    [--no-cpu-baseline] [--copy-calibration-mb MB]
+"""
+from __future__ import annotations
+
+import argparse
+import glob
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "Hyena FFTConv fwd token·channels/s + HBM GB/s (% peak) at N=8K and 64K"
+HBM_PEAK_GBPS = 8000.0
+# float32 vector peak with packed-FP32 instructions disabled:
+# 256 CUs x 4 SIMDs x 16 lanes x 2 flop (FMA) x 2.4 GHz
+ALU_PEAK_TFLOPS = 256 * 4 * 16 * 2 * 2.4e9 / 1e12
+HEADLINE = 2
+ORDER_OF_RUN = [2, 1, 3, 4]
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------------------
+# accounting (algorithmic bytes and flops per forward)
+# ---------------------------------------------------------------------------
+
+def io_bytes(dtype):
+    return 2 if dtype == "bf16" else 4
+
+
+def algorithmic_bytes(cfg, spec_dtype):
+    """(2 + order) activations (u, gates, y) + order spectra (2N reals per
+    channel, 4XY in 2D) + order*d feedthrough scalars; each read or written once."""
+    s_io = io_bytes(cfg["dtype"])
+    s_sp = io_bytes(spec_dtype)
+    order, d, B = cfg["order"], cfg["d"], cfg["B"]
+    if cfg["kind"] == "1d":
+        tokens = B * cfg["N"]
+        spec_reals = 2 * cfg["N"]
+    else:
+        tokens = B * cfg["X"] * cfg["Y"]
+        spec_reals = 4 * cfg["X"] * cfg["Y"]
+    return (2 + order) * tokens * d * s_io + order * d * spec_reals * s_sp + order * d * 4
+
+
+def transform_points(cfg):
+    if cfg["kind"] == "1d":
+        M = 1
+        while M < 2 * cfg["N"]:
+            M *= 2
+        return M
+    return 4 * cfg["X"] * cfg["Y"]
+
+
+def algorithmic_flops(cfg):
+    """Radix-2 model: 5 M log2 M per complex length-M transform, halved for
+    real data; a forward and an inverse per stage; 9 flops per output for the
+    spectral product, feedthrough and gate."""
+    M = transform_points(cfg)
+    tokens = cfg["B"] * (cfg["N"] if cfg["kind"] == "1d" else cfg["X"] * cfg["Y"])
+    per_tc = cfg["order"] * (2 * 5 * (M / 2) * math.log2(M) / (M / 2) + 9)
+    return per_tc * tokens * cfg["d"]
+
+
+def kernel_source_sha():
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "long_convolution_sequence_rfft_amd", "csrc", "*"))):
+        with open(f, "rb") as fh:
+            h.update(os.path.basename(f).encode())
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(name):
+    """HBM bytes per forward from the committed rocprofv3 counter summary, or
+    None if the kernels changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path)).get(name)
+    except Exception:
+        return None
+    if not rec or rec.get("kernel_source_sha") != kernel_source_sha():
+        return None
+    return rec.get("hbm_bytes_per_forward")
+
+
+# ---------------------------------------------------------------------------
+# GPU timing
+# ---------------------------------------------------------------------------
+
+def make_inputs(idx, seed):
+    from long_convolution_sequence_rfft_amd import synth
+    return synth.make_config(idx, seed=seed)
+
+
+def run_workload(idx, steps, warmup, min_rotation_bytes=600 << 20):
+    import torch
+    from long_convolution_sequence_rfft_amd import hyena, synth
+    from long_convolution_sequence_rfft_amd.synth import CONFIGS, CONFIG_NAMES
+
+    cfg = dict(CONFIGS[idx])
+    name = CONFIG_NAMES[idx]
+    io = hyena.HYENA_F32 if cfg["dtype"] == synth.F32 else hyena.HYENA_BF16
+    spec_dtype = io
+    dims = (cfg["N"],) if cfg["kind"] == "1d" else (cfg["X"], cfg["Y"])
+    log(f"[bench] {name}: building plan")
+    try:
+        plan = hyena.Plan(cfg["B"], cfg["d"], cfg["order"], dims, io_dtype=io,
+                          spectrum_dtype=spec_dtype)
+    except hyena.HyenaError as e:
+        log(f"[bench] {name}: skipped ({e})")
+        return None
+    t0 = time.time()
+    inp = make_inputs(idx, seed=idx)
+    log(f"[bench] {name}: inputs synthesised in {time.time() - t0:.1f}s")
+
+    def dev(a):
+        if cfg["dtype"] == synth.BF16:
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+    h = dev(inp.h)
+    D = torch.from_numpy(inp.D).cuda()
+    # filter spectrum, timed separately
+    try:
+        H = plan.spectrum(h)
+    except hyena.HyenaError as e:
+        log(f"[bench] {name}: skipped ({e})")
+        return None
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(3):
+        plan.spectrum(h, H)
+    e1.record()
+    torch.cuda.synchronize()
+    spectrum_ms = e0.elapsed_time(e1) / 3
+    del h
+
+    bytes_alg = algorithmic_bytes(cfg, "bf16" if spec_dtype == hyena.HYENA_BF16 else "f32")
+    nsets = max(1, min(4, int(math.ceil(min_rotation_bytes / bytes_alg))))
+    sets = []
+    for s in range(nsets):
+        u = dev(inp.u)
+        gates = [dev(inp.gates[n]) for n in range(cfg["order"])]
+        Hs = H if s == 0 else H.clone()
+        sets.append((u, gates, Hs, torch.empty_like(u)))
+    del inp
+
+    def step(i):
+        u, gates, Hs, y = sets[i % nsets]
+        plan.forward(u, gates, Hs, D, y)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    # whole-job time over exactly `steps` forwards
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(steps):
+        step(i)
+    stop.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(stop)
+    # per-launch durations (events on the stream the kernels are launched on)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    evs[0].record()
+    for i in range(steps):
+        step(i)
+        evs[i + 1].record()
+    torch.cuda.synchronize()
+    per = np.array([evs[i].elapsed_time(evs[i + 1]) for i in range(steps)])
+
+    tokens = cfg["B"] * (cfg["N"] if cfg["kind"] == "1d" else cfg["X"] * cfg["Y"])
+    tc = tokens * cfg["d"]
+    ms = total_ms / steps
+    fwd_ms = float(np.mean(per))
+    flops = algorithmic_flops(cfg)
+    res = {
+        "workload": name,
+        "path": {1: "LDS1D", 2: "FOURSTEP1D", 3: "ROWCOL2D"}[plan.path],
+        "B": cfg["B"], "d": cfg["d"], "order": cfg["order"],
+        "dims": list(dims), "storage": cfg["dtype"],
+        "spectrum": "bf16" if spec_dtype == hyena.HYENA_BF16 else "f32",
+        "ms_per_step": ms,
+        "tc_per_s": tc / (ms * 1e-3),
+        "forward_ms_mean": fwd_ms,
+        "forward_ms_p10": float(np.percentile(per, 10)),
+        "forward_ms_p90": float(np.percentile(per, 90)),
+        "spectrum_ms": spectrum_ms,
+        "rotation_sets": nsets,
+        "algorithmic_bytes": bytes_alg,
+        "algorithmic_flops": flops,
+        "hbm_GBps": bytes_alg / (fwd_ms * 1e-3) / 1e9,
+        "hbm_frac": bytes_alg / (fwd_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+        "alu_TFLOPs": flops / (fwd_ms * 1e-3) / 1e12,
+        "alu_frac": flops / (fwd_ms * 1e-3) / 1e12 / ALU_PEAK_TFLOPS,
+        "launches_per_forward": 1 if plan.path == 1 else None,
+    }
+    log(f"[bench] {name}: {ms * 1e3:.1f} us/step, {res['tc_per_s'] / 1e9:.1f} G tc/s, "
+        f"{res['hbm_GBps']:.0f} GB/s ({100 * res['hbm_frac']:.1f}% HBM), "
+        f"{res['alu_TFLOPs']:.1f} TFLOP/s ({100 * res['alu_frac']:.1f}% fp32 VALU)")
+    del sets, H
+    torch.cuda.empty_cache()
+    return res
+
+
+def roofline_of(res):
+    t_hbm = res["algorithmic_bytes"] / (HBM_PEAK_GBPS * 1e9)
+    t_alu = res["algorithmic_flops"] / (ALU_PEAK_TFLOPS * 1e12)
+    traffic = load_traffic(res["workload"])
+    if t_alu >= t_hbm:
+        return {"bound": "alu", "achieved": round(res["alu_TFLOPs"], 3),
+                "peak": round(ALU_PEAK_TFLOPS, 2), "unit": "TFLOP/s",
+                "frac": round(res["alu_frac"], 4), "traffic": traffic}
+    return {"bound": "hbm", "achieved": round(res["hbm_GBps"], 1), "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s", "frac": round(res["hbm_frac"], 4), "traffic": traffic}
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the float64 oracle on a bounded sample of the same workload
+# ---------------------------------------------------------------------------
+
+def cpu_baseline(idx, max_channels):
+    import oracle
+    from long_convolution_sequence_rfft_amd.synth import CONFIGS
+    cfg = CONFIGS[idx]
+    inp = make_inputs(idx, seed=idx)
+    ch = np.arange(min(max_channels, cfg["d"]))
+    u, g, h, D = inp.f64()
+    u, g, D = np.ascontiguousarray(u[..., ch]), np.ascontiguousarray(g[..., ch]), D[:, ch]
+    h = np.ascontiguousarray(h[:, ch])
+    method = oracle.DIRECT if (cfg["kind"] == "1d" and cfg["N"] <= 2048) else oracle.FFT
+    t0 = time.time()
+    if cfg["kind"] == "1d":
+        oracle.hyena1d(u, g, h, D, method)
+        tokens = cfg["B"] * cfg["N"]
+    else:
+        oracle.hyena2d(u, g, h, D, method)
+        tokens = cfg["B"] * cfg["X"] * cfg["Y"]
+    dt = time.time() - t0
+    tc = tokens * len(ch)
+    return {"value": tc / dt, "unit": "token·channels/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"{len(ch)} of {cfg['d']} channels, all {tokens} tokens per channel, "
+                      f"{'direct Toeplitz sum' if method == oracle.DIRECT else 'radix-2 FFT'}"
+                      f" route, float64; {dt:.1f} s wall"}
+
+
+# ---------------------------------------------------------------------------
+
+def copy_calibration(mb):
+    """A plain device copy of known size, so counter runs can scale FETCH_SIZE /
+    WRITE_SIZE to bytes."""
+    import torch
+    n = (mb << 20) // 4
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    b.copy_(a)
+    torch.cuda.synchronize()
+    log(f"[bench] copy calibration: {mb} MiB read + {mb} MiB written")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--only", type=str, default=None, help="run only this workload name")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-channels", type=int, default=96)
+    ap.add_argument("--copy-calibration-mb", type=int, default=0)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; the path shards over "
+                          "channels with no communication (see DESIGN.md), but no multi-GPU "
+                          "run is provided", "n_gpus": args.gpus}), flush=True)
+        sys.exit(2)
+
+    import torch
+    from long_convolution_sequence_rfft_amd.synth import CONFIG_NAMES
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}), flush=True)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+
+    if args.copy_calibration_mb:
+        copy_calibration(args.copy_calibration_mb)
+
+    results = {}
+    for idx in ORDER_OF_RUN:
+        if args.only and CONFIG_NAMES[idx] != args.only and str(idx) != args.only:
+            continue
+        r = run_workload(idx, args.steps, args.warmup)
+        if r is not None:
+            results[idx] = r
+
+    head_idx = HEADLINE if HEADLINE in results else (next(iter(results)) if results else None)
+    if head_idx is None:
+        print(json.dumps({"error": "no workload ran"}), flush=True)
+        sys.exit(1)
+    head = results[head_idx]
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] CPU baseline (oracle) ...")
+        cpu = cpu_baseline(head_idx, args.cpu_channels)
+        log(f"[bench] oracle: {cpu['value'] / 1e6:.2f} M tc/s on {cpu['cores']} threads")
+
+    workloads = {}
+    for idx, r in results.items():
+        w = dict(r)
+        w["roofline"] = roofline_of(r)
+        workloads[r["workload"]] = w
+    line = {
+        "metric": METRIC,
+        "value": head["tc_per_s"],
+        "unit": "token·channels/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": head["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded; damped-sinusoid filters, N(0,1) activations)",
+        "config": {"workload": head["workload"], "B": head["B"], "dims": head["dims"],
+                   "d": head["d"], "order": head["order"], "storage": head["storage"],
+                   "spectrum": head["spectrum"], "path": head["path"],
+                   "parallelism": "single GPU"},
+        "hbm": {"achieved": round(head["hbm_GBps"], 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(head["hbm_frac"], 4)},
+        "roofline": roofline_of(head),
+        "cpu_baseline": cpu,
+        "workloads": workloads,
+        "kernel_source_sha": kernel_source_sha(),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -15,20 +15,22 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(os.path.dirname(HERE), "_build")
 LIB = os.path.join(HERE, "libhyena_mi355x.so")
-SOURCES = ["api.hip", "lds1d.hip", "lds1d_f32.hip", "lds1d_bf16.hip", "fourstep.hip",
-           "rowcol2d.hip", "plan.cpp"]
+SOURCES = ["api.hip", "lds1d.hip", "lds1d_f32.hip", "lds1d_bf16.hip", "multipass.hip",
+           "multipass_outer_f32.hip", "multipass_outer_bf16.hip", "multipass_inner.hip",
+           "plan.cpp"]
+INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-          "-Wno-unused-command-line-argument", "-I", os.path.join(os.path.dirname(HERE), "include")]
+          "-Wno-unused-command-line-argument", "-I", INCLUDE]
 
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, src + ".o")
     cmd = [HIPCC] + COMMON + ["-c", os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".cpp"):
-        cmd = [HIPCC, "-O2", "-std=c++17", "-fPIC", "-x", "c++", "-c",
+        cmd = [HIPCC, "-O2", "-std=c++17", "-fPIC", "-x", "c++", "-I", INCLUDE, "-c",
                os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:

@@ -24,10 +24,10 @@ __global__ void hyena_tw_init(float2* tw, TwInitArgs a)
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= a.total) return;
     for (int s = 0; s < a.nseg; ++s) {
-        const int64_t len = (int64_t)a.seg[s].radix * a.seg[s].ns;
+        const int64_t len = (int64_t)(a.seg[s].radix - 1) * a.seg[s].ns;
         if (i >= a.seg[s].off && i < a.seg[s].off + len) {
             const int64_t loc = i - a.seg[s].off;
-            const int64_t k = loc / a.seg[s].radix, r = loc % a.seg[s].radix;
+            const int64_t r = loc / a.seg[s].ns + 1, k = loc % a.seg[s].ns;
             const int64_t L = (int64_t)a.seg[s].ns * a.seg[s].radix;
             const int64_t m = (r * k) % L;
             double sn, cs;

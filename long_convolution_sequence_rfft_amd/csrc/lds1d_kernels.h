@@ -45,14 +45,15 @@ struct Lds1dSpecArgs {
 // FULL: N == M/2 (no sample of the live half is past the end of the sequence).
 // EVEN: d is even (channel pairs are aligned wide accesses).
 template <int M, typename IO, typename SP, bool FAST>
-__global__ void __launch_bounds__(FftShape<M>::T)
+__global__ void __launch_bounds__(FftShape<M>::T, 2)
 hyena_lds1d_forward(Lds1dFwdArgs a)
 {
     using S = FftShape<M>;
     constexpr int T = S::T, PTS = S::PTS, R0 = S::R0;
-    constexpr bool EVEN = FAST, FULL = FAST;
+    constexpr bool EVEN = FAST;
     __shared__ float sre[S::LW];
     __shared__ float sim[S::LW];
+    __shared__ float sxs[4 * S::RL];
 
     const int tau = threadIdx.x;
     const int64_t lin = xcd_remap(blockIdx.x, a.nblocks);
@@ -66,61 +67,87 @@ hyena_lds1d_forward(Lds1dFwdArgs a)
     const int j1 = tau, j2 = tau ? 2 * T - tau : T;
     const float inv2M = 0.5f / (float)M;
 
+    // Sample t = tau + q T + r (M/R0) of channel pair (c0, c0+1) of row b.
+    // FAST: the row offset splits into a per-lane part (tau + q T) d and a
+    // uniform part r (M/R0) d, so every access is scalar base + 32-bit offset.
+    const IO* ubase = static_cast<const IO*>(a.u) + row0;
     float2 v[PTS];
-    {
-        const IO* u = static_cast<const IO*>(a.u) + row0;
 #pragma unroll
-        for (int q = 0; q < S::Q0; ++q)
+    for (int q = 0; q < S::Q0; ++q) {
+        const uint32_t lane_off = (uint32_t)(tau + q * T) * dd * (uint32_t)sizeof(IO);
 #pragma unroll
-            for (int r = 0; r < R0 / 2; ++r) {
+        for (int r = 0; r < R0 / 2; ++r) {
+            if constexpr (FAST) {
+                v[q * R0 + r] = widen_pair<IO>(load_pair_raw(ubase + (size_t)r * (M / R0) * dd, lane_off));
+            } else {
                 const uint32_t t = tau + q * T + r * (M / R0);
-                v[q * R0 + r] = (FULL || t < N) ? load_pair<IO, EVEN>(u + t * dd, has_b)
-                                                : make_float2(0.0f, 0.0f);
+                v[q * R0 + r] = t < N ? load_pair<IO, EVEN>(ubase + (size_t)t * dd, has_b)
+                                      : make_float2(0.0f, 0.0f);
             }
+        }
     }
 
     for (int n = 0; n < a.order; ++n) {
-        fwd_transform<M>(v, sre, sim, a.tw, a.tw_off, tau, j1, j2, n > 0);
+        const SP* spec = static_cast<const SP*>(a.spec) +
+                         ((int64_t)n * a.npairs + p) * (int64_t)(M / 2) * kEntryElems;
+        typename EntryRaw<SP>::type ent[S::RL];
+        fwd_transform<M>(v, sre, sim, a.tw, a.tw_off, tau, j1, j2, n > 0,
+                         [&] { load_entries<M, SP>(ent, spec, tau); });
 
         const float Da = a.D[(int64_t)n * a.d + c0];
         const float Db = has_b ? a.D[(int64_t)n * a.d + c0 + 1] : 0.0f;
-        const SP* spec = static_cast<const SP*>(a.spec) +
-                         ((int64_t)n * a.npairs + p) * (int64_t)(M / 2) * kEntryElems;
-        spectral_product<M, SP>(v, spec, tau, (Da + Db) * inv2M, (Da - Db) * inv2M);
-
-        inv_transform<M>(v, sre, sim, a.tw, a.tw_off, tau, j1, j2);
+        spectral_product<M, SP>(v, ent, tau, (Da + Db) * inv2M, (Da - Db) * inv2M, sxs);
 
         const IO* g = static_cast<const IO*>(a.gates[n]) + row0;
+        typename PairRaw<IO>::type graw[S::Q0][R0 / 2];
+        float2 gv[S::Q0][R0 / 2];
+        inv_transform<M>(v, sre, sim, a.tw, a.tw_off, tau, j1, j2, [&] {
+#pragma unroll
+            for (int q = 0; q < S::Q0; ++q) {
+                const uint32_t lane_off = (uint32_t)(tau + q * T) * dd * (uint32_t)sizeof(IO);
+#pragma unroll
+                for (int r = 0; r < R0 / 2; ++r) {
+                    if constexpr (FAST) {
+                        graw[q][r] = load_pair_raw(g + (size_t)r * (M / R0) * dd, lane_off);
+                    } else {
+                        const uint32_t t = tau + q * T + r * (M / R0);
+                        gv[q][r] = t < N ? load_pair<IO, EVEN>(g + (size_t)t * dd, has_b)
+                                         : make_float2(0.0f, 0.0f);
+                    }
+                }
+            }
+        });
 #pragma unroll
         for (int q = 0; q < S::Q0; ++q)
 #pragma unroll
             for (int r = 0; r < R0 / 2; ++r) {
-                const uint32_t t = tau + q * T + r * (M / R0);
+                const float2 gg = FAST ? widen_pair<IO>(graw[q][r]) : gv[q][r];
                 float2& x = v[q * R0 + r];
-                if (FULL || t < N) {
-                    const float2 gv = load_pair<IO, EVEN>(g + t * dd, has_b);
-                    x = make_float2(x.x * gv.x, x.y * gv.y);
-                } else {
-                    x = make_float2(0.0f, 0.0f);
-                }
+                x = make_float2(x.x * gg.x, x.y * gg.y);
             }
     }
 
-    IO* y = static_cast<IO*>(a.y) + row0;
+    IO* ybase = static_cast<IO*>(a.y) + row0;
 #pragma unroll
-    for (int q = 0; q < S::Q0; ++q)
+    for (int q = 0; q < S::Q0; ++q) {
+        const uint32_t lane_off = (uint32_t)(tau + q * T) * dd * (uint32_t)sizeof(IO);
 #pragma unroll
         for (int r = 0; r < R0 / 2; ++r) {
-            const uint32_t t = tau + q * T + r * (M / R0);
-            if (FULL || t < N) store_pair<IO, EVEN>(y + t * dd, v[q * R0 + r], has_b);
+            if constexpr (FAST) {
+                store_pair_at(ybase + (size_t)r * (M / R0) * dd, lane_off, v[q * R0 + r]);
+            } else {
+                const uint32_t t = tau + q * T + r * (M / R0);
+                if (t < N) store_pair<IO, EVEN>(ybase + (size_t)t * dd, v[q * R0 + r], has_b);
+            }
         }
+    }
 }
 
 // Filter spectrum: one workgroup per (filter n, channel pair).
 // Z = DFT_M(pad(h_a + i h_b)); entries ((Ha + Hb), (Ha - Hb)) / (2M), the
 // 1/M of the unscaled inverse transform folded in.
 template <int M, typename IO, typename SP>
-__global__ void __launch_bounds__(FftShape<M>::T)
+__global__ void __launch_bounds__(FftShape<M>::T, 2)
 hyena_lds1d_spectrum(Lds1dSpecArgs a)
 {
     using S = FftShape<M>;
@@ -148,7 +175,7 @@ hyena_lds1d_spectrum(Lds1dSpecArgs a)
             v[q * R0 + r] = make_float2(live ? ld1<IO>(ha + t) : 0.0f,
                                         (live && has_b) ? ld1<IO>(hb + t) : 0.0f);
         }
-    fwd_transform<M>(v, sre, sim, a.tw, a.tw_off, tau, j1, j2, false);
+    fwd_transform<M>(v, sre, sim, a.tw, a.tw_off, tau, j1, j2, false, [] {});
     SP* spec = static_cast<SP*>(a.spec) + lin * (int64_t)(M / 2) * kEntryElems;
     store_spectrum_entries<M, SP>(v, spec, tau, 0.5f / (float)M);
 }

@@ -1,0 +1,317 @@
+// multipass.hip -- launch side of the four-step (1D, transforms longer than
+// 16384 points, or forced) and row-column (2D) paths: chunk loop over channel
+// pairs, per-length dispatch, and the spectrum export.
+#include "multipass_kernels.h"
+
+namespace hy {
+
+HY_MP_LENGTHS(HY_MP_OUTER_INST, float, extern)
+HY_MP_LENGTHS(HY_MP_OUTER_INST, uint16_t, extern)
+HY_MP_LENGTHS(HY_MP_INNER_INST, float, extern)
+HY_MP_LENGTHS(HY_MP_INNER_INST, uint16_t, extern)
+
+namespace {
+
+int threads_per_transform(int L) { return L / lds1d_pts(L); }
+
+TwOffsets offsets_at(const Plan& p, int first)
+{
+    TwOffsets o;
+    o.f1 = (int32_t)p.seg[first + 0].off;
+    o.fL = (int32_t)p.seg[first + 1].off;
+    o.i1 = (int32_t)p.seg[first + 2].off;
+    o.i0 = (int32_t)p.seg[first + 3].off;
+    return o;
+}
+
+// Geometry common to all passes of a plan (chunk fields filled per launch).
+MpGeom base_geom(const Plan& p)
+{
+    MpGeom g{};
+    g.N = p.N;
+    g.d = p.d;
+    g.npairs = p.npairs;
+    g.B = p.B;
+    g.four_step = p.path == HYENA_PATH_FOURSTEP1D;
+    if (g.four_step) {
+        g.La = (int32_t)p.M1;
+        g.Lb = (int32_t)p.M2;
+        g.Lb_live = (int32_t)p.M2;
+        g.sa = p.M2;  // t = M2 n1 + n2
+        g.so = 1;
+        g.tw_step = p.seg[8].off;
+    } else {
+        g.La = (int32_t)p.P2;
+        g.Lb = (int32_t)p.P1;
+        g.Lb_live = (int32_t)p.X;
+        g.sa = 1;  // t = Y p + q
+        g.so = p.Y;
+        g.tw_step = 0;
+    }
+    int kp = 1;
+    while (kp < 16 && kp < p.npairs) kp <<= 1;
+    g.kp_log2 = 0;
+    while ((1 << g.kp_log2) < kp) ++g.kp_log2;
+    g.groups_per_b = (int32_t)((p.npairs + kp - 1) / kp);
+    g.tw_a = offsets_at(p, 0);
+    g.tw_b = offsets_at(p, 4);
+    return g;
+}
+
+template <typename IO>
+hyena_status outer_go(int L, int mode, bool half_spec, const OuterArgs& a, int64_t nb, hipStream_t s)
+{
+    switch (L) {
+#define HY_CASE(LL, A_, B_)                                                                 \
+    case LL:                                                                                \
+        if (mode == OUTER_IN) return mp_outer_launch<LL, IO, OUTER_IN, true>(a, nb, s);     \
+        if (mode == OUTER_MID) return mp_outer_launch<LL, IO, OUTER_MID, true>(a, nb, s);   \
+        if (mode == OUTER_OUT) return mp_outer_launch<LL, IO, OUTER_OUT, true>(a, nb, s);   \
+        if (half_spec) return mp_outer_launch<LL, IO, OUTER_SPEC, true>(a, nb, s);          \
+        return mp_outer_launch<LL, IO, OUTER_SPEC, false>(a, nb, s);
+        HY_MP_LENGTHS(HY_CASE, 0, 0)
+#undef HY_CASE
+        default: return fail(HYENA_ERR_UNSUPPORTED, "multi-pass: unsupported outer length");
+    }
+}
+
+template <typename SP>
+hyena_status inner_go(int L, int mode, bool half_b, const InnerArgs& a, int64_t nb, hipStream_t s)
+{
+    switch (L) {
+#define HY_CASE(LL, A_, B_)                                                                   \
+    case LL:                                                                                  \
+        if (mode == INNER_SPEC) return mp_inner_launch<LL, SP, INNER_SPEC, false>(a, nb, s);  \
+        if (half_b) return mp_inner_launch<LL, SP, INNER_CHAIN, true>(a, nb, s);              \
+        return mp_inner_launch<LL, SP, INNER_CHAIN, false>(a, nb, s);
+        HY_MP_LENGTHS(HY_CASE, 0, 0)
+#undef HY_CASE
+        default: return fail(HYENA_ERR_UNSUPPORTED, "multi-pass: unsupported inner length");
+    }
+}
+
+hyena_status outer(const Plan& p, int mode, bool half_spec, const OuterArgs& a, int64_t nb,
+                   hipStream_t s)
+{
+    return p.io_dtype == HYENA_F32 ? outer_go<float>(a.g.La, mode, half_spec, a, nb, s)
+                                   : outer_go<uint16_t>(a.g.La, mode, half_spec, a, nb, s);
+}
+
+hyena_status inner(const Plan& p, int mode, const InnerArgs& a, int64_t nb, hipStream_t s)
+{
+    const bool half_b = !a.g.four_step;
+    return p.spec_dtype == HYENA_F32 ? inner_go<float>(a.g.Lb, mode, half_b, a, nb, s)
+                                     : inner_go<uint16_t>(a.g.Lb, mode, half_b, a, nb, s);
+}
+
+size_t io_size(const Plan& p) { return p.io_dtype == HYENA_F32 ? 4 : 2; }
+
+// SP elements of one filter's spectrum
+int64_t spec_elems_per_filter(const Plan& p)
+{
+    return p.npairs * p.spec_entries_per_pair * kEntryElems;
+}
+
+hyena_status mp_forward(const Plan& p, const void* u, const void* const* gates, const void* H,
+                        const float* D, void* y, void* ws, void* stream)
+{
+    const hipStream_t s = (hipStream_t)stream;
+    MpGeom g = base_geom(p);
+    const int KP = 1 << g.kp_log2;
+    const int C = (512 / threads_per_transform(g.La)) / KP;
+    const int U = (512 / threads_per_transform(g.Lb)) / 2;
+    const int64_t col_blocks = (g.Lb_live + C - 1) / C;
+    const int64_t unit_blocks = (g.La / 2 + U - 1) / U;
+    const int64_t total_groups = (int64_t)p.B * g.groups_per_b;
+    int64_t chunk_groups = p.chunk_pairs / KP;
+    if (chunk_groups < 1) chunk_groups = 1;
+    float2* F = reinterpret_cast<float2*>(static_cast<char*>(ws) + p.inter_offset);
+    const float2* tw = static_cast<const float2*>(ws);
+    const size_t esz = p.spec_dtype == HYENA_F32 ? 4 : 2;
+    g.pair_bytes = p.fwd_pair_bytes;
+    for (int64_t g0 = 0; g0 < total_groups; g0 += chunk_groups) {
+        g.group0 = g0;
+        g.ngroups = total_groups - g0 < chunk_groups ? total_groups - g0 : chunk_groups;
+        OuterArgs oa{};
+        oa.g = g;
+        oa.act = u;
+        oa.F = F;
+        oa.tw = tw;
+        hyena_status st = outer(p, OUTER_IN, true, oa, col_blocks * g.ngroups, s);
+        if (st != HYENA_OK) return st;
+        for (int n = 0; n < p.order; ++n) {
+            InnerArgs ia{};
+            ia.g = g;
+            ia.F = F;
+            ia.spec = static_cast<const char*>(H) + (size_t)n * spec_elems_per_filter(p) * esz;
+            ia.D = D + (int64_t)n * p.d;
+            ia.tw = tw;
+            st = inner(p, INNER_CHAIN, ia, unit_blocks * g.ngroups * KP, s);
+            if (st != HYENA_OK) return st;
+            oa.act = gates[n];
+            oa.out = y;
+            st = outer(p, n + 1 < p.order ? OUTER_MID : OUTER_OUT, true, oa, col_blocks * g.ngroups, s);
+            if (st != HYENA_OK) return st;
+        }
+    }
+    return HYENA_OK;
+}
+
+hyena_status mp_spectrum(const Plan& p, const void* h, void* H, void* ws, void* stream)
+{
+    const hipStream_t s = (hipStream_t)stream;
+    MpGeom g = base_geom(p);
+    g.B = 1;  // filters have no batch axis
+    const int KP = 1 << g.kp_log2;
+    const int C = (512 / threads_per_transform(g.La)) / KP;
+    const int U = (512 / threads_per_transform(g.Lb)) / 2;
+    const int64_t col_blocks = (g.Lb + C - 1) / C;
+    const int64_t unit_blocks = (g.La / 2 + U - 1) / U;
+    const int64_t total_groups = g.groups_per_b;
+    int64_t chunk_groups = (int64_t)(p.inter_bytes / (size_t)(p.spec_pair_bytes * KP));
+    if (chunk_groups < 1) chunk_groups = 1;
+    float2* F = reinterpret_cast<float2*>(static_cast<char*>(ws) + p.inter_offset);
+    const float2* tw = static_cast<const float2*>(ws);
+    const size_t esz = p.spec_dtype == HYENA_F32 ? 4 : 2;
+    const int64_t taps = p.ndims == 1 ? p.N : (2 * p.X - 1) * (2 * p.Y - 1);
+    g.pair_bytes = p.spec_pair_bytes;
+    for (int n = 0; n < p.order; ++n) {
+        for (int64_t g0 = 0; g0 < total_groups; g0 += chunk_groups) {
+            g.group0 = g0;
+            g.ngroups = total_groups - g0 < chunk_groups ? total_groups - g0 : chunk_groups;
+            OuterArgs oa{};
+            oa.g = g;
+            oa.filt = static_cast<const char*>(h) + (size_t)n * p.d * taps * io_size(p);
+            oa.F = F;
+            oa.tw = tw;
+            hyena_status st = outer(p, OUTER_SPEC, g.four_step != 0, oa, col_blocks * g.ngroups, s);
+            if (st != HYENA_OK) return st;
+            InnerArgs ia{};
+            ia.g = g;
+            ia.F = F;
+            ia.spec_out = static_cast<char*>(H) + (size_t)n * spec_elems_per_filter(p) * esz;
+            ia.tw = tw;
+            st = inner(p, INNER_SPEC, ia, unit_blocks * g.ngroups * KP, s);
+            if (st != HYENA_OK) return st;
+        }
+    }
+    return HYENA_OK;
+}
+
+// One thread per entry (n, pair, unit kk, e); writes natural-order unscaled
+// transfer functions.  1D: [order][d][M/2 + 1]; 2D: [order][d][P1][P2/2 + 1].
+template <typename SP>
+__global__ void hyena_mp_export(const SP* spec, float2* out, int64_t npairs, int64_t d, int La,
+                                int Lb, int four_step, int64_t total)
+{
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= total) return;
+    const int64_t per_pair = (int64_t)(La / 2) * Lb;
+    const int64_t np = i / per_pair;
+    const int64_t rem = i - np * per_pair;
+    const int kk = (int)(rem / Lb), e = (int)(rem % Lb);
+    const int64_t n = np / npairs, p = np - n * npairs;
+    const int64_t c0 = 2 * p;
+    const bool has_b = c0 + 1 < d;
+    float2 P, Q;
+    load_entry(spec, i, P, Q);
+    const float M = (float)La * (float)Lb;
+    const float2 ha = make_float2((P.x + Q.x) * M, (P.y + Q.y) * M);
+    const float2 hb = make_float2((P.x - Q.x) * M, (P.y - Q.y) * M);
+    if (four_step) {
+        const int64_t Mtot = (int64_t)La * Lb, half = Mtot / 2;
+        float2* oa = out + (n * d + c0) * (half + 1);
+        float2* ob = oa + (half + 1);
+        auto put = [&](int64_t k, float2 va, float2 vb) {
+            if (k > half) {
+                k = Mtot - k;
+                va.y = -va.y;
+                vb.y = -vb.y;
+            }
+            oa[k] = va;
+            if (has_b) ob[k] = vb;
+        };
+        if (kk > 0) {
+            put(kk + (int64_t)La * e, ha, hb);
+        } else if (e == 0) {
+            put(0, make_float2(ha.x, 0.0f), make_float2(hb.x, 0.0f));
+            put(half, make_float2(ha.y, 0.0f), make_float2(hb.y, 0.0f));
+        } else if (e < Lb / 2) {
+            put((int64_t)La * e, ha, hb);
+        } else {
+            put(La / 2 + (int64_t)La * (e - Lb / 2), ha, hb);
+        }
+    } else {
+        const int W = La / 2 + 1;  // kq = 0 .. P2/2
+        float2* oa = out + (n * d + c0) * (int64_t)Lb * W;
+        float2* ob = oa + (int64_t)Lb * W;
+        auto put = [&](int kp, int kq, float2 va, float2 vb) {
+            oa[(int64_t)kp * W + kq] = va;
+            if (has_b) ob[(int64_t)kp * W + kq] = vb;
+        };
+        auto conj2 = [](float2 v) { return make_float2(v.x, -v.y); };
+        if (kk > 0) {
+            put(e, kk, ha, hb);
+        } else if (e == 0 || e == Lb / 2) {
+            const int kq = e == 0 ? 0 : La / 2;
+            put(0, kq, make_float2(ha.x, 0.0f), make_float2(hb.x, 0.0f));
+            put(Lb / 2, kq, make_float2(ha.y, 0.0f), make_float2(hb.y, 0.0f));
+        } else {
+            const int kq = e < Lb / 2 ? 0 : La / 2;
+            const int kp = e < Lb / 2 ? e : e - Lb / 2;
+            put(kp, kq, ha, hb);
+            put(Lb - kp, kq, conj2(ha), conj2(hb));
+        }
+    }
+}
+
+hyena_status mp_export(const Plan& p, const void* H, void* out, void* stream)
+{
+    const MpGeom g = base_geom(p);
+    const int64_t total = (int64_t)p.order * p.npairs * p.spec_entries_per_pair;
+    const int bs = 256;
+    const int64_t nb = (total + bs - 1) / bs;
+    if (p.spec_dtype == HYENA_F32)
+        hipLaunchKernelGGL(hyena_mp_export<float>, dim3((unsigned)nb), dim3(bs), 0,
+                           (hipStream_t)stream, (const float*)H, (float2*)out, p.npairs, p.d,
+                           g.La, g.Lb, g.four_step, total);
+    else
+        hipLaunchKernelGGL(hyena_mp_export<uint16_t>, dim3((unsigned)nb), dim3(bs), 0,
+                           (hipStream_t)stream, (const uint16_t*)H, (float2*)out, p.npairs, p.d,
+                           g.La, g.Lb, g.four_step, total);
+    const hipError_t e = hipGetLastError();
+    return e == hipSuccess ? HYENA_OK : fail(HYENA_ERR_DEVICE, hipGetErrorString(e));
+}
+
+}  // namespace
+
+hyena_status launch_fourstep_forward(const Plan& p, const void* u, const void* const* gates,
+                                     const void* H, const float* D, void* y, void* ws,
+                                     void* stream)
+{
+    return mp_forward(p, u, gates, H, D, y, ws, stream);
+}
+hyena_status launch_fourstep_spectrum(const Plan& p, const void* h, void* H, void* ws, void* stream)
+{
+    return mp_spectrum(p, h, H, ws, stream);
+}
+hyena_status launch_fourstep_export(const Plan& p, const void* H, void* out, void* stream)
+{
+    return mp_export(p, H, out, stream);
+}
+hyena_status launch_rowcol2d_forward(const Plan& p, const void* u, const void* const* gates,
+                                     const void* H, const float* D, void* y, void* ws,
+                                     void* stream)
+{
+    return mp_forward(p, u, gates, H, D, y, ws, stream);
+}
+hyena_status launch_rowcol2d_spectrum(const Plan& p, const void* h, void* H, void* ws, void* stream)
+{
+    return mp_spectrum(p, h, H, ws, stream);
+}
+hyena_status launch_rowcol2d_export(const Plan& p, const void* H, void* out, void* stream)
+{
+    return mp_export(p, H, out, stream);
+}
+
+}  // namespace hy

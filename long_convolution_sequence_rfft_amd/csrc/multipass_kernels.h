@@ -1,0 +1,454 @@
+// multipass_kernels.h -- the outer and inner passes of the four-step (1D) and
+// row-column (2D) paths; see multipass.h for the structure.
+#pragma once
+
+#include "multipass.h"
+
+namespace hy {
+
+enum OuterMode { OUTER_IN = 0, OUTER_MID = 1, OUTER_OUT = 2, OUTER_SPEC = 3 };
+enum InnerMode { INNER_CHAIN = 0, INNER_SPEC = 1 };
+
+// Transforms per workgroup and threads: 512 threads, one length-L transform
+// per FftShape<L>::T threads.
+template <int L>
+struct MpShape {
+    static constexpr int T = FftShape<L>::T;
+    static constexpr int NF = 512 / T;
+    static constexpr int LW = FftShape<L>::LW;
+};
+
+struct OuterArgs {
+    MpGeom g;
+    const void* act;   // u (IN), gate (MID, OUT)
+    void* out;         // y (OUT)
+    const void* filt;  // filter taps (SPEC), this filter index
+    float2* F;         // workspace intermediate of this chunk
+    const float2* tw;
+};
+
+struct InnerArgs {
+    MpGeom g;
+    float2* F;
+    const void* spec;  // spectrum of this filter index, entries [pair][unit][e] (CHAIN)
+    void* spec_out;    // same layout, written (SPEC)
+    const float* D;    // feedthrough of this filter index [d]
+    const float2* tw;
+};
+
+// Sample of channel pair (c0, c0+1) at activation row `row` (element offset).
+template <typename IO>
+__device__ __forceinline__ float2 act_load(const IO* base, int64_t row, int64_t c0, int64_t d)
+{
+    const IO* r = base + row * d + c0;
+    if (c0 + 1 < d) {
+        if ((d & 1) == 0) return load_pair<IO, true>(r, true);
+        return make_float2(ld1<IO>(r), ld1<IO>(r + 1));
+    }
+    return make_float2(ld1<IO>(r), 0.0f);
+}
+
+template <typename IO>
+__device__ __forceinline__ void act_store(IO* base, int64_t row, int64_t c0, int64_t d, float2 v)
+{
+    IO* r = base + row * d + c0;
+    if (c0 + 1 < d) {
+        if ((d & 1) == 0) {
+            store_pair<IO, true>(r, v, true);
+        } else {
+            st1<IO>(r, v.x);
+            st1<IO>(r + 1, v.y);
+        }
+    } else {
+        st1<IO>(r, v.x);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Outer pass.  Workgroup = KP pair slots x C outer columns (C KP = NF).
+// blockIdx.x = column block * ngroups + group-in-chunk.
+// ---------------------------------------------------------------------------
+template <int LA, typename IO, int MODE, bool HALF_SPEC>
+__global__ void __launch_bounds__(512) hyena_mp_outer(OuterArgs a)
+{
+    using S = FftShape<LA>;
+    using X = MpShape<LA>;
+    constexpr int TA = X::T, NF = X::NF, LW = X::LW, R0 = S::R0;
+    constexpr bool HALF_IN = MODE == OUTER_SPEC ? HALF_SPEC : true;
+    __shared__ float sre[NF * LW];
+    __shared__ float sim[NF * LW];
+
+    const MpGeom& g = a.g;
+    const int KP = 1 << g.kp_log2;
+    const int C = NF >> g.kp_log2;
+    const int f = threadIdx.x / TA;
+    const int tau = threadIdx.x - f * TA;
+    const int gi = blockIdx.x % g.ngroups;
+    const int cb = blockIdx.x / g.ngroups;
+    const int kp = f & (KP - 1);
+    const int o = cb * C + (f >> g.kp_log2);  // this transform's outer column
+    const int n_outer = MODE == OUTER_SPEC ? g.Lb : g.Lb_live;
+    const bool col_live = o < n_outer;
+    float* re = sre + f * LW;
+    float* im = sim + f * LW;
+    const int64_t group = g.group0 + gi;
+    int64_t b, p;
+    bool live;
+    pair_of_slot(g, group, kp, b, p, live);
+    float2* Fcol = a.F + ((int64_t)gi * KP + kp) * (g.pair_bytes / 8) + (int64_t)o * LA;
+    const float2* twstep = a.tw + g.tw_step + (int64_t)(o - 1) * LA;  // W_M^{o a'}, o >= 1
+
+    // cooperative move of activation rows between memory and the regions:
+    // index -> (pair kp', outer sample s, column c'); KP consecutive lanes
+    // cover one row's KP channel pairs (one cache line for KP = 16 f32).
+    auto tile_rows = [&](auto&& fn) {
+        const int total = (LA / 2) * C * KP;
+        for (int idx = threadIdx.x; idx < total; idx += 512) {
+            const int kq = idx & (KP - 1);
+            const int rest = idx >> g.kp_log2;
+            const int s = rest % (LA / 2);
+            const int cq = rest / (LA / 2);
+            const int fq = cq * KP + kq;
+            int64_t bq, pq;
+            bool lq;
+            pair_of_slot(g, group, kq, bq, pq, lq);
+            const int oq = cb * C + cq;
+            const int64_t t = g.sa * s + g.so * (int64_t)oq;
+            fn(fq, s, bq, pq, lq && oq < n_outer && t < g.N, bq * g.N + t);
+        }
+    };
+
+    float2 v[S::PTS];
+    if constexpr (MODE == OUTER_IN) {
+        const IO* u = static_cast<const IO*>(a.act);
+        tile_rows([&](int fq, int s, int64_t, int64_t pq, bool ok, int64_t row) {
+            const float2 x = ok ? act_load<IO>(u, row, 2 * pq, g.d) : make_float2(0.0f, 0.0f);
+            sre[fq * LW + lpad(s)] = x.x;
+            sim[fq * LW + lpad(s)] = x.y;
+        });
+        __syncthreads();
+        lds_to_regs<LA, true>(v, re, im, tau);
+        __syncthreads();
+    } else if constexpr (MODE == OUTER_SPEC) {
+        // filter taps straight from their channel-major layout (not timed)
+        const IO* h = static_cast<const IO*>(a.filt);
+        const int64_t c0 = 2 * p;
+#pragma unroll
+        for (int q = 0; q < S::Q0; ++q)
+#pragma unroll
+            for (int r = 0; r < (HALF_IN ? R0 / 2 : R0); ++r) {
+                const int s = tau + q * TA + r * (LA / R0);
+                float2 x = make_float2(0.0f, 0.0f);
+                if (live && col_live) {
+                    int64_t idx = -1, stride = 0;
+                    if (g.four_step) {
+                        const int64_t t = g.sa * s + g.so * o;
+                        if (t < g.N) idx = t;
+                        stride = g.N;
+                    } else {
+                        // periodic placement: tap offset (i, j) sits at (i mod P1, j mod P2);
+                        // row o = i mod P1, column s = j mod P2
+                        const int64_t X2 = g.Lb / 2, Y2 = LA / 2;
+                        const int64_t i = o < X2 ? o : o - g.Lb;
+                        const int64_t j = s < Y2 ? s : s - LA;
+                        if (o != X2 && s != Y2) idx = (i + X2 - 1) * (2 * Y2 - 1) + (j + Y2 - 1);
+                        stride = (2 * X2 - 1) * (2 * Y2 - 1);
+                    }
+                    if (idx >= 0) {
+                        x.x = ld1<IO>(h + c0 * stride + idx);
+                        if (c0 + 1 < g.d) x.y = ld1<IO>(h + (c0 + 1) * stride + idx);
+                    }
+                }
+                v[q * R0 + r] = x;
+            }
+    } else {
+        // MID / OUT: F column -> (conj twiddle) -> region, inverse outer DFT
+        for (int i = tau; i < LA; i += TA) {
+            float2 x = make_float2(0.0f, 0.0f);
+            if (col_live) {
+                x = Fcol[i];
+                if (g.four_step && o > 0) x = ctw<+1>(x, twstep[i]);
+            }
+            re[lpad(i)] = x.x;
+            im[lpad(i)] = x.y;
+        }
+        __syncthreads();
+        inv_lds_to_regs<LA, true>(v, re, im, a.tw, g.tw_a, tau);
+        // gate tile for the live outer samples
+        __syncthreads();
+        const IO* gate = static_cast<const IO*>(a.act);
+        tile_rows([&](int fq, int s, int64_t, int64_t pq, bool ok, int64_t row) {
+            const float2 x = ok ? act_load<IO>(gate, row, 2 * pq, g.d) : make_float2(0.0f, 0.0f);
+            sre[fq * LW + lpad(s)] = x.x;
+            sim[fq * LW + lpad(s)] = x.y;
+        });
+        __syncthreads();
+#pragma unroll
+        for (int q = 0; q < S::Q0; ++q)
+#pragma unroll
+            for (int r = 0; r < R0 / 2; ++r) {
+                const int i = lpad(tau + q * TA + r * (LA / R0));
+                float2& x = v[q * R0 + r];
+                x = make_float2(x.x * re[i], x.y * im[i]);
+            }
+        __syncthreads();
+        if constexpr (MODE == OUTER_OUT) {
+            regs_to_lds<LA, true>(v, re, im, tau);
+            __syncthreads();
+            IO* y = static_cast<IO*>(a.out);
+            tile_rows([&](int fq, int s, int64_t, int64_t pq, bool ok, int64_t row) {
+                if (ok) act_store<IO>(y, row, 2 * pq, g.d,
+                                      make_float2(sre[fq * LW + lpad(s)], sim[fq * LW + lpad(s)]));
+            });
+            return;
+        }
+    }
+
+    // forward outer DFT -> natural-order bins -> (twiddle) -> F column
+    fwd_regs_to_lds<LA, HALF_IN>(v, re, im, a.tw, g.tw_a, tau);
+    __syncthreads();
+    if (!col_live) return;
+    for (int i = tau; i < LA; i += TA) {
+        float2 x = make_float2(re[lpad(i)], im[lpad(i)]);
+        if (g.four_step && o > 0) x = ctw<-1>(x, twstep[i]);
+        Fcol[i] = x;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Inner pass.  Unit kk (1 <= kk < La/2) = outer columns (kk, La - kk): their
+// bins are each other's mirrors.  Unit 0 = outer columns 0 and La/2, each
+// mirrored onto itself.  Workgroup = one pair slot x U = NF/2 units;
+// transform f = 2u + side (side 0: column kk, side 1: its partner).
+// blockIdx.x = unit block * (pair slots in chunk) + slot.
+//
+// Mirror of inner bin e (length LB):
+//   four-step (t = M2 n1 + n2, k = k1 + M1 k2):
+//     unit kk > 0:  (kk, e)      <-> (La - kk, LB - 1 - e)
+//     column 0:     (0, e)       <-> (0, -e mod LB)
+//     column La/2:  (La/2, e)    <-> (La/2, LB - 1 - e)
+//   2D (bin (kp, kq), kq outer):
+//     unit kk > 0:  (kq=kk, e)   <-> (La - kk, -e mod LB)
+//     columns 0 and La/2: (kq, e) <-> (kq, -e mod LB)
+// Entry e of a unit (entries [pair][unit][e], e < LB):
+//   unit kk > 0: primary bin (kk, e).
+//   unit 0, four-step: e = 0 packs the real bins (0,0) and (0,LB/2);
+//     0 < e < LB/2: primary (0, e); e >= LB/2: primary (La/2, e - LB/2).
+//   unit 0, 2D: e = 0 packs (0,0),(0,LB/2) of column 0; 0 < e < LB/2:
+//     primary (0, e); e = LB/2 packs (La/2: 0, LB/2); e > LB/2: primary
+//     (La/2, e - LB/2).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void unit_pairing(bool four_step, int kk, int e, int LB, int& fa, int& ka,
+                                             int& fb, int& kb, int& self)
+{
+    // fa/fb: side (0 or 1), ka/kb: bin index; self: 0 = pair, 1 = packed self bins (ka, kb in side fa)
+    self = 0;
+    if (kk > 0) {
+        fa = 0;
+        ka = e;
+        fb = 1;
+        kb = four_step ? LB - 1 - e : (LB - e) & (LB - 1);
+        return;
+    }
+    if (four_step) {
+        if (e == 0) {
+            fa = fb = 0;
+            ka = 0;
+            kb = LB / 2;
+            self = 1;
+        } else if (e < LB / 2) {
+            fa = fb = 0;
+            ka = e;
+            kb = LB - e;
+        } else {
+            fa = fb = 1;
+            ka = e - LB / 2;
+            kb = LB - 1 - ka;
+        }
+    } else {
+        if (e == 0 || e == LB / 2) {
+            fa = fb = e == 0 ? 0 : 1;
+            ka = 0;
+            kb = LB / 2;
+            self = 1;
+        } else if (e < LB / 2) {
+            fa = fb = 0;
+            ka = e;
+            kb = LB - e;
+        } else {
+            fa = fb = 1;
+            ka = e - LB / 2;
+            kb = LB - ka;
+        }
+    }
+}
+
+template <int LB, typename SP, int MODE, bool HALF_B>
+__global__ void __launch_bounds__(512) hyena_mp_inner(InnerArgs a)
+{
+    using S = FftShape<LB>;
+    using X = MpShape<LB>;
+    constexpr int TB = X::T, NF = X::NF, LW = X::LW, U = NF / 2;
+    __shared__ float sre[NF * LW];
+    __shared__ float sim[NF * LW];
+
+    const MpGeom& g = a.g;
+    const int KP = 1 << g.kp_log2;
+    const int64_t nslots = g.ngroups * KP;
+    const int64_t slot = blockIdx.x % nslots;
+    const int ub = blockIdx.x / nslots;
+    const int kk0 = ub * U;
+    const int f = threadIdx.x / TB;
+    const int tau = threadIdx.x - f * TB;
+    float* re = sre + f * LW;
+    float* im = sim + f * LW;
+    const int La = g.La;
+    const int nlive = MODE == INNER_SPEC ? LB : g.Lb_live;
+    const int64_t group = g.group0 + slot / KP;
+    int64_t b, p;
+    bool live;
+    pair_of_slot(g, group, (int)(slot % KP), b, p, live);
+    float2* Fp = a.F + slot * (g.pair_bytes / 8);
+
+    // units of this workgroup: kk0 .. kk0 + nu - 1 (nu <= U)
+    const int nu = min(U, La / 2 - kk0);
+    auto col_of = [&](int u, int side) {
+        const int kk = kk0 + u;
+        return side == 0 ? kk : (kk == 0 ? La / 2 : La - kk);
+    };
+
+    // F[o][column] -> region of (u, side) at inner position o
+    const int total = nlive * nu * 2;
+    for (int idx = threadIdx.x; idx < total; idx += 512) {
+        const int u = idx % nu;
+        const int side = (idx / nu) & 1;
+        const int op = idx / (2 * nu);
+        const float2 x = Fp[(int64_t)op * La + col_of(u, side)];
+        const int fq = 2 * u + side;
+        sre[fq * LW + lpad(op)] = x.x;
+        sim[fq * LW + lpad(op)] = x.y;
+    }
+    __syncthreads();
+    constexpr bool HALF_LOAD = (MODE == INNER_CHAIN) && HALF_B;
+    float2 v[S::PTS];
+    lds_to_regs<LB, HALF_LOAD>(v, re, im, tau);
+    __syncthreads();
+    fwd_regs_to_lds<LB, HALF_LOAD>(v, re, im, a.tw, g.tw_b, tau);
+    __syncthreads();
+
+    // mirror-paired product (CHAIN) or entry computation (SPEC)
+    if ((f >> 1) < nu && live) {
+        const int u = f >> 1;
+        const int tu = (f & 1) * TB + tau;  // 0 .. 2 TB - 1
+        const int kk = kk0 + u;
+        float* ure = sre + (2 * u) * LW;
+        float* uim = sim + (2 * u) * LW;
+        const int64_t ebase = p * (int64_t)(La / 2) * LB + (int64_t)kk * LB;
+        float dp = 0.0f, dq = 0.0f;
+        if constexpr (MODE == INNER_CHAIN) {
+            const int64_t c0 = 2 * p;
+            const float Da = a.D[c0];
+            const float Db = c0 + 1 < g.d ? a.D[c0 + 1] : 0.0f;
+            // entries hold (Ha +- Hb) / (2M); the feedthrough adds D to every bin
+            const float inv2M = 0.5f / ((float)La * (float)LB);
+            dp = (Da + Db) * inv2M;
+            dq = (Da - Db) * inv2M;
+        }
+        for (int e = tu; e < LB; e += 2 * TB) {
+            int fa, ka, fb, kb, self;
+            unit_pairing(g.four_step != 0, kk, e, LB, fa, ka, fb, kb, self);
+            const int ia = fa * LW + lpad(ka), ib = fb * LW + lpad(kb);
+            float2 za = make_float2(ure[ia], uim[ia]);
+            float2 zb = make_float2(ure[ib], uim[ib]);
+            if constexpr (MODE == INNER_CHAIN) {
+                float2 P, Q;
+                load_entry(static_cast<const SP*>(a.spec), ebase + e, P, Q);
+                if (self) {
+                    za = self_product(za, P.x + dp, Q.x + dq);
+                    zb = self_product(zb, P.y + dp, Q.y + dq);
+                } else {
+                    P.x += dp;
+                    Q.x += dq;
+                    pair_product(za, zb, P, Q);
+                }
+                ure[ia] = za.x;
+                uim[ia] = za.y;
+                ure[ib] = zb.x;
+                uim[ib] = zb.y;
+            } else {
+                const float sc = 0.5f / ((float)La * (float)LB);
+                float2 P, Q;
+                if (self) {
+                    P = make_float2((za.x + za.y) * sc, (zb.x + zb.y) * sc);
+                    Q = make_float2((za.x - za.y) * sc, (zb.x - zb.y) * sc);
+                } else {
+                    entry_from_pair(za, zb, sc, P, Q);
+                }
+                store_entry(static_cast<SP*>(a.spec_out), ebase + e, P, Q);
+            }
+        }
+    }
+    if constexpr (MODE == INNER_SPEC) return;
+
+    __syncthreads();
+    inv_lds_to_regs<LB, HALF_B>(v, re, im, a.tw, g.tw_b, tau);
+    __syncthreads();
+    regs_to_lds<LB, HALF_B>(v, re, im, tau);
+    __syncthreads();
+    const int total_out = g.Lb_live * nu * 2;
+    for (int idx = threadIdx.x; idx < total_out; idx += 512) {
+        const int u = idx % nu;
+        const int side = (idx / nu) & 1;
+        const int op = idx / (2 * nu);
+        const int fq = 2 * u + side;
+        Fp[(int64_t)op * La + col_of(u, side)] =
+            make_float2(sre[fq * LW + lpad(op)], sim[fq * LW + lpad(op)]);
+    }
+}
+
+}  // namespace hy
+
+namespace hy {
+
+template <int LA, typename IO, int MODE, bool HALF_SPEC>
+hyena_status mp_outer_launch(const OuterArgs& a, int64_t nblocks, hipStream_t s)
+{
+    hipLaunchKernelGGL((hyena_mp_outer<LA, IO, MODE, HALF_SPEC>), dim3((unsigned)nblocks), dim3(512),
+                       0, s, a);
+    const hipError_t e = hipGetLastError();
+    return e == hipSuccess ? HYENA_OK : fail(HYENA_ERR_DEVICE, hipGetErrorString(e));
+}
+
+template <int LB, typename SP, int MODE, bool HALF_B>
+hyena_status mp_inner_launch(const InnerArgs& a, int64_t nblocks, hipStream_t s)
+{
+    hipLaunchKernelGGL((hyena_mp_inner<LB, SP, MODE, HALF_B>), dim3((unsigned)nblocks), dim3(512), 0,
+                       s, a);
+    const hipError_t e = hipGetLastError();
+    return e == hipSuccess ? HYENA_OK : fail(HYENA_ERR_DEVICE, hipGetErrorString(e));
+}
+
+#define HY_MP_LENGTHS(X, A, B) X(8, A, B) X(16, A, B) X(32, A, B) X(64, A, B) X(128, A, B) \
+    X(256, A, B) X(512, A, B) X(1024, A, B)
+
+#define HY_MP_OUTER_INST(L, IO, EXT)                                                          \
+    EXT template hyena_status mp_outer_launch<L, IO, OUTER_IN, true>(const OuterArgs&,        \
+                                                                     int64_t, hipStream_t);   \
+    EXT template hyena_status mp_outer_launch<L, IO, OUTER_MID, true>(const OuterArgs&,       \
+                                                                      int64_t, hipStream_t);  \
+    EXT template hyena_status mp_outer_launch<L, IO, OUTER_OUT, true>(const OuterArgs&,       \
+                                                                      int64_t, hipStream_t);  \
+    EXT template hyena_status mp_outer_launch<L, IO, OUTER_SPEC, true>(const OuterArgs&,      \
+                                                                       int64_t, hipStream_t); \
+    EXT template hyena_status mp_outer_launch<L, IO, OUTER_SPEC, false>(const OuterArgs&,     \
+                                                                        int64_t, hipStream_t);
+
+#define HY_MP_INNER_INST(L, SP, EXT)                                                          \
+    EXT template hyena_status mp_inner_launch<L, SP, INNER_CHAIN, true>(const InnerArgs&,     \
+                                                                        int64_t, hipStream_t); \
+    EXT template hyena_status mp_inner_launch<L, SP, INNER_CHAIN, false>(const InnerArgs&,    \
+                                                                         int64_t, hipStream_t); \
+    EXT template hyena_status mp_inner_launch<L, SP, INNER_SPEC, false>(const InnerArgs&,     \
+                                                                        int64_t, hipStream_t);
+
+}  // namespace hy

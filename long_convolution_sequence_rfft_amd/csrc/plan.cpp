@@ -25,7 +25,17 @@ void add_segment(Plan& p, int64_t& off, int64_t ns, int64_t radix)
     s.off = off;
     s.ns = (int32_t)ns;
     s.radix = (int32_t)radix;
-    off += radix * ns;
+    off += (radix - 1) * ns;
+}
+// The four tables of one transform length: forward middle pass, forward last
+// pass, inverse middle pass, inverse last pass.
+void add_transform_segments(Plan& p, int64_t& off, int64_t L)
+{
+    const int l = (int)L;
+    add_segment(p, off, lds1d_r0(l), lds1d_r1(l));
+    add_segment(p, off, L / lds1d_rl(l), lds1d_rl(l));
+    add_segment(p, off, lds1d_rl(l), lds1d_r1(l));
+    add_segment(p, off, L / lds1d_r0(l), lds1d_r0(l));
 }
 }  // namespace
 
@@ -102,25 +112,15 @@ hyena_status plan_build(Plan& p, int64_t B, int64_t N, int64_t d, int32_t order,
             p.R0 = lds1d_r0(M);
             p.R1 = lds1d_r1(M);
             p.RL = lds1d_rl(M);
-            add_segment(p, off, p.R0, p.R1);         // forward middle pass
-            add_segment(p, off, p.M / p.RL, p.RL);   // forward last pass
-            add_segment(p, off, p.RL, p.R1);         // inverse middle pass
-            add_segment(p, off, p.M / p.R0, p.R0);   // inverse last pass
+            add_transform_segments(p, off, p.M);
         } else {
             fourstep_split(p.M, p.M1, p.M2);
-            // column transforms (length M1) and row transforms (length M2) each
-            // use the single-workgroup radix plan of their own length; plus the
-            // inter-step twiddle W_M^{n2 k1}
-            const int m1 = (int)p.M1, m2 = (int)p.M2;
-            add_segment(p, off, lds1d_r0(m1), lds1d_r1(m1));
-            add_segment(p, off, p.M1 / lds1d_rl(m1), lds1d_rl(m1));
-            add_segment(p, off, lds1d_rl(m1), lds1d_r1(m1));
-            add_segment(p, off, p.M1 / lds1d_r0(m1), lds1d_r0(m1));
-            add_segment(p, off, lds1d_r0(m2), lds1d_r1(m2));
-            add_segment(p, off, p.M2 / lds1d_rl(m2), lds1d_rl(m2));
-            add_segment(p, off, lds1d_rl(m2), lds1d_r1(m2));
-            add_segment(p, off, p.M2 / lds1d_r0(m2), lds1d_r0(m2));
-            add_segment(p, off, p.M2, p.M1);  // W_M^{n2 k1}: ns = M2 (n2), radix = M1 (k1)
+            // outer (column, length M1) and inner (row, length M2) transforms use
+            // the single-workgroup radix plan of their own length; then the
+            // inter-step twiddle W_M^{n2 k1}, stored [n2 - 1][k1]
+            add_transform_segments(p, off, p.M1);
+            add_transform_segments(p, off, p.M2);
+            add_segment(p, off, p.M1, p.M2);
         }
     } else {
         const int64_t X = dims[0], Y = dims[1];
@@ -136,15 +136,9 @@ hyena_status plan_build(Plan& p, int64_t B, int64_t N, int64_t d, int32_t order,
         p.P1 = 2 * X;
         p.P2 = 2 * Y;
         p.spec_entries_per_pair = p.P1 * p.P2 / 2;
-        const int m1 = (int)p.P1, m2 = (int)p.P2;
-        add_segment(p, off, lds1d_r0(m1), lds1d_r1(m1));
-        add_segment(p, off, p.P1 / lds1d_rl(m1), lds1d_rl(m1));
-        add_segment(p, off, lds1d_rl(m1), lds1d_r1(m1));
-        add_segment(p, off, p.P1 / lds1d_r0(m1), lds1d_r0(m1));
-        add_segment(p, off, lds1d_r0(m2), lds1d_r1(m2));
-        add_segment(p, off, p.P2 / lds1d_rl(m2), lds1d_rl(m2));
-        add_segment(p, off, lds1d_rl(m2), lds1d_r1(m2));
-        add_segment(p, off, p.P2 / lds1d_r0(m2), lds1d_r0(m2));
+        // outer transforms run along q (length P2), inner along p (length P1)
+        add_transform_segments(p, off, p.P2);
+        add_transform_segments(p, off, p.P1);
     }
 
     p.tw_elems = off;
@@ -159,14 +153,22 @@ hyena_status plan_build(Plan& p, int64_t B, int64_t N, int64_t d, int32_t order,
     p.inter_bytes = 0;
     p.chunk_pairs = 0;
     if (p.path == HYENA_PATH_FOURSTEP1D || p.path == HYENA_PATH_ROWCOL2D) {
-        const int64_t per_pair = p.path == HYENA_PATH_FOURSTEP1D ? p.M * 8 : p.P2 * p.X * 8;
+        // per channel pair: the forward chain keeps F[o][a] for the live inner
+        // positions; the filter spectrum needs every inner position
+        const int64_t fwd_pair = p.path == HYENA_PATH_FOURSTEP1D ? p.M * 8 : p.X * p.P2 * 8;
+        const int64_t spec_pair = p.path == HYENA_PATH_FOURSTEP1D ? p.M * 8 : p.P1 * p.P2 * 8;
         // keep the chunk's intermediate near 96 MiB so it stays in the 256 MB
-        // last-level cache while it is re-read
-        int64_t chunk = (int64_t)(96ll << 20) / per_pair;
-        if (chunk < 1) chunk = 1;
-        if (chunk > B * p.npairs) chunk = B * p.npairs;
+        // last-level cache between passes; whole groups of 16 pairs
+        int64_t chunk = (int64_t)(96ll << 20) / fwd_pair;
+        chunk = chunk / 16 * 16;
+        if (chunk < 16) chunk = 16;
+        const int64_t total_slots = p.B * ((p.npairs + 15) / 16) * 16;
+        if (chunk > total_slots) chunk = total_slots;
         p.chunk_pairs = chunk;
-        p.inter_bytes = align_up((size_t)(chunk * per_pair), 256);
+        p.fwd_pair_bytes = fwd_pair;
+        p.spec_pair_bytes = spec_pair;
+        const int64_t need = chunk * (fwd_pair > spec_pair ? fwd_pair : spec_pair);
+        p.inter_bytes = align_up((size_t)need, 256);
     }
     p.workspace_bytes = p.inter_offset + p.inter_bytes;
     return HYENA_OK;

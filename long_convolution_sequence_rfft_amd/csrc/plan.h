@@ -12,7 +12,7 @@
 #include <set>
 #include <string>
 
-#include "../../include/hyena.h"
+#include "hyena.h"
 
 namespace hy {
 
@@ -36,9 +36,9 @@ constexpr int lds1d_r1(int M)
     return lds1d_rest(M) <= 32 ? 1 : lds1d_rest(M) <= 512 ? 16 : 32;
 }
 
-// One twiddle table, thread-contiguous: tw[off + k * radix + r] =
-// exp(-2 pi i r k / (ns * radix)), r = 0..radix-1, k = 0..ns-1.  A butterfly's
-// radix twiddles are one aligned run, read with 16-byte loads from one address.
+// One twiddle table, lane-coalesced: tw[off + (r - 1) * ns + k] =
+// exp(-2 pi i r k / (ns * radix)), r = 1..radix-1, k = 0..ns-1.  Neighbouring
+// lanes hold neighbouring k, so each load instruction reads one contiguous run.
 struct TwSegment {
     int64_t off;    // in float2 elements from the workspace base
     int32_t ns;
@@ -64,7 +64,9 @@ struct Plan {
     // rows of length M2.  ROWCOL2D: P1 = 2X (columns), P2 = 2Y (rows).
     int64_t M1 = 0, M2 = 0;
     int64_t P1 = 0, P2 = 0;
-    int64_t chunk_pairs = 0;  // channel pairs per pass over the intermediate buffer
+    int64_t chunk_pairs = 0;      // channel-pair slots per pass over the intermediate buffer
+    int64_t fwd_pair_bytes = 0;   // intermediate bytes per pair slot, forward chain
+    int64_t spec_pair_bytes = 0;  // intermediate bytes per pair slot, filter spectrum
 
     // twiddle tables
     TwSegment seg[kMaxTwSegments];

@@ -35,7 +35,22 @@ struct FftShape {
 
 // ---------------------------------------------------------------------------
 // storage access (float32 or bfloat16 stored as uint16_t)
+//
+// Global accesses take a wave-uniform base pointer and a 32-bit per-lane byte
+// offset, which maps onto the scalar-base + vector-offset addressing form
+// (one VGPR per access instead of a 64-bit address pair).
 // ---------------------------------------------------------------------------
+template <typename T>
+__device__ __forceinline__ const T& at_bytes(const void* base, uint32_t off)
+{
+    return *reinterpret_cast<const T*>(static_cast<const char*>(base) + off);
+}
+template <typename T>
+__device__ __forceinline__ T& at_bytes(void* base, uint32_t off)
+{
+    return *reinterpret_cast<T*>(static_cast<char*>(base) + off);
+}
+
 template <typename IO>
 __device__ __forceinline__ float ld1(const IO* p)
 {
@@ -80,6 +95,44 @@ __device__ __forceinline__ void store_pair(IO* row, float2 v, bool has_b)
     } else {
         st1<IO>(row, v.x);
         if (has_b) st1<IO>(row + 1, v.y);
+    }
+}
+
+// Raw channel-pair value as stored (float2 for f32, one dword for a bf16
+// pair); widened at use so prefetched values occupy as few VGPRs as possible.
+template <typename IO>
+struct PairRaw;
+template <>
+struct PairRaw<float> {
+    using type = float2;
+};
+template <>
+struct PairRaw<uint16_t> {
+    using type = uint32_t;
+};
+
+template <typename IO>
+__device__ __forceinline__ float2 widen_pair(const typename PairRaw<IO>::type& w)
+{
+    if constexpr (sizeof(IO) == 4) return w;
+    else return make_float2(__uint_as_float(w << 16), __uint_as_float(w & 0xffff0000u));
+}
+
+// EVEN pair at byte offset `off` from a uniform base.
+template <typename IO>
+__device__ __forceinline__ typename PairRaw<IO>::type load_pair_raw(const IO* base, uint32_t off)
+{
+    return at_bytes<typename PairRaw<IO>::type>(base, off);
+}
+
+template <typename IO>
+__device__ __forceinline__ void store_pair_at(IO* base, uint32_t off, float2 v)
+{
+    if constexpr (sizeof(IO) == 4) {
+        at_bytes<float2>(base, off) = v;
+    } else {
+        at_bytes<uint32_t>(base, off) =
+            (uint32_t)f32_to_bf16(v.x) | ((uint32_t)f32_to_bf16(v.y) << 16);
     }
 }
 
@@ -148,17 +201,26 @@ __device__ __forceinline__ void lds_read(const float* sre, const float* sim, flo
     }
 }
 
-// Twiddles of butterfly k: the run tab[k R .. k R + R) (entry 0 is 1).
-template <int R, int DIR>
-__device__ __forceinline__ void apply_tw(float2* v, const float2* tab, int k)
+// Twiddles of butterfly k of a pass with sub-transform length NS: input r
+// takes tab[(r - 1) NS + k].  Loaded into registers ahead of the barrier that
+// precedes the pass, so the load latency overlaps the LDS exchange.
+// `tab` is wave-uniform.  The empty asm re-defines it in place, so the
+// per-row bases tab + (r-1) NS are recomputed with scalar adds at each use
+// instead of being hoisted out of the order loop as VGPR address pairs.
+template <int R, int NS>
+__device__ __forceinline__ void load_tw(float2* w, const float2* tab, uint32_t k)
 {
-    const float4* t = reinterpret_cast<const float4*>(tab + k * R);
+    asm volatile("" : "+s"(tab));
+    const uint32_t koff = k * 8u;
 #pragma unroll
-    for (int i = 0; i < R / 2; ++i) {
-        const float4 w = t[i];
-        if (i > 0) v[2 * i] = ctw<DIR>(v[2 * i], make_float2(w.x, w.y));
-        v[2 * i + 1] = ctw<DIR>(v[2 * i + 1], make_float2(w.z, w.w));
-    }
+    for (int r = 1; r < R; ++r) w[r - 1] = at_bytes<float2>(tab + (r - 1) * NS, koff);
+}
+
+template <int R, int DIR>
+__device__ __forceinline__ void apply_tw(float2* v, const float2* w)
+{
+#pragma unroll
+    for (int r = 1; r < R; ++r) v[r] = ctw<DIR>(v[r], w[r - 1]);
 }
 
 // Twiddle-table offsets (float2 units) of one transform length.
@@ -171,37 +233,48 @@ struct TwOffsets {
 // read).  On return v[0..RL) and v[RL..2RL) hold the outputs of last-pass
 // butterflies j1 and j2: bins j1 + s L/RL and j2 + s L/RL.
 // sync_first: LDS may still be read by the previous step (WAR barrier).
-template <int L>
+// `prefetch` runs after the last exchange's reads (global loads for the
+// caller, whose latency then overlaps the last pass's arithmetic).
+// Every pass with Q > 1 butterflies per thread shares one twiddle set in the
+// R1 pass (T is a multiple of R0 whenever R1 > 1).
+template <int L, typename F>
 __device__ __forceinline__ void fwd_transform(float2* v, float* sre, float* sim, const float2* tw,
                                               TwOffsets o, int tau, int j1, int j2,
-                                              bool sync_first)
+                                              bool sync_first, F&& prefetch)
 {
     using S = FftShape<L>;
     constexpr int T = S::T, R0 = S::R0, R1 = S::R1, RL = S::RL;
+    constexpr int NSL = L / RL;
 #pragma unroll
     for (int q = 0; q < S::Q0; ++q) dft<R0, -1, true, false>(&v[q * R0]);
     if (sync_first) __syncthreads();
 #pragma unroll
     for (int q = 0; q < S::Q0; ++q) lds_write<R0, 1>(sre, sim, &v[q * R0], tau + q * T);
-    __syncthreads();
     if constexpr (R1 > 1) {
+        static_assert(T % R0 == 0, "shared R1-pass twiddles");
+        float2 w1[R1 - 1];
+        load_tw<R1, R0>(w1, tw + o.f1, tau & (R0 - 1));
+        __syncthreads();
 #pragma unroll
         for (int q = 0; q < S::Q1; ++q) lds_read<R1, L>(sre, sim, &v[q * R1], tau + q * T);
 #pragma unroll
         for (int q = 0; q < S::Q1; ++q) {
-            const int j = tau + q * T;
-            apply_tw<R1, -1>(&v[q * R1], tw + o.f1, j & (R0 - 1));
+            apply_tw<R1, -1>(&v[q * R1], w1);
             dft<R1, -1>(&v[q * R1]);
         }
         __syncthreads();
 #pragma unroll
         for (int q = 0; q < S::Q1; ++q) lds_write<R1, R0>(sre, sim, &v[q * R1], tau + q * T);
-        __syncthreads();
     }
+    float2 wa[RL - 1], wb[RL - 1];
+    load_tw<RL, NSL>(wa, tw + o.fL, j1);
+    load_tw<RL, NSL>(wb, tw + o.fL, j2);
+    __syncthreads();
     lds_read<RL, L>(sre, sim, &v[0], j1);
     lds_read<RL, L>(sre, sim, &v[RL], j2);
-    apply_tw<RL, -1>(&v[0], tw + o.fL, j1);
-    apply_tw<RL, -1>(&v[RL], tw + o.fL, j2);
+    apply_tw<RL, -1>(&v[0], wa);
+    apply_tw<RL, -1>(&v[RL], wb);
+    prefetch();
     dft<RL, -1>(&v[0]);
     dft<RL, -1>(&v[RL]);
 }
@@ -209,39 +282,48 @@ __device__ __forceinline__ void fwd_transform(float2* v, float* sre, float* sim,
 // Inverse transform (unscaled) from the last-pass registers (butterflies j1,
 // j2) back to the R0-pass layout: v[q R0 + s], s < R0/2, is sample
 // tau + q T + s L/R0.  Only the first half of the samples is produced.
-template <int L>
+// `prefetch` runs after the last exchange's reads (global loads for the
+// caller, e.g. the gate values, whose latency overlaps the last pass).
+template <int L, typename F>
 __device__ __forceinline__ void inv_transform(float2* v, float* sre, float* sim, const float2* tw,
-                                              TwOffsets o, int tau, int j1, int j2)
+                                              TwOffsets o, int tau, int j1, int j2, F&& prefetch)
 {
     using S = FftShape<L>;
     constexpr int T = S::T, R0 = S::R0, R1 = S::R1, RL = S::RL;
+    constexpr int NS0 = L / R0;
     dft<RL, +1>(&v[0]);
     dft<RL, +1>(&v[RL]);
     __syncthreads();
     lds_write<RL, 1>(sre, sim, &v[0], j1);
     lds_write<RL, 1>(sre, sim, &v[RL], j2);
-    __syncthreads();
     if constexpr (R1 > 1) {
+        static_assert(T % RL == 0, "shared R1-pass twiddles");
+        float2 w1[R1 - 1];
+        load_tw<R1, RL>(w1, tw + o.i1, tau & (RL - 1));
+        __syncthreads();
 #pragma unroll
         for (int q = 0; q < S::Q1; ++q) lds_read<R1, L>(sre, sim, &v[q * R1], tau + q * T);
 #pragma unroll
         for (int q = 0; q < S::Q1; ++q) {
-            const int j = tau + q * T;
-            apply_tw<R1, +1>(&v[q * R1], tw + o.i1, j & (RL - 1));
+            apply_tw<R1, +1>(&v[q * R1], w1);
             dft<R1, +1>(&v[q * R1]);
         }
         __syncthreads();
 #pragma unroll
         for (int q = 0; q < S::Q1; ++q) lds_write<R1, RL>(sre, sim, &v[q * R1], tau + q * T);
-        __syncthreads();
     }
+    float2 w0[S::Q0][R0 - 1];
+#pragma unroll
+    for (int q = 0; q < S::Q0; ++q) load_tw<R0, NS0>(w0[q], tw + o.i0, tau + q * T);
+    __syncthreads();
 #pragma unroll
     for (int q = 0; q < S::Q0; ++q) {
-        const int j = tau + q * T;
-        lds_read<R0, L>(sre, sim, &v[q * R0], j);
-        apply_tw<R0, +1>(&v[q * R0], tw + o.i0, j);
-        dft<R0, +1, false, true>(&v[q * R0]);
+        lds_read<R0, L>(sre, sim, &v[q * R0], tau + q * T);
+        apply_tw<R0, +1>(&v[q * R0], w0[q]);
     }
+    prefetch();
+#pragma unroll
+    for (int q = 0; q < S::Q0; ++q) dft<R0, +1, false, true>(&v[q * R0]);
 }
 
 // ---------------------------------------------------------------------------
@@ -279,8 +361,46 @@ __device__ __forceinline__ void entry_from_pair(float2 zp, float2 zm, float scal
     Q = make_float2((Ha.x - Hb.x) * scale, (Ha.y - Hb.y) * scale);
 }
 
+// Raw spectrum entry as loaded (widened at use): float4 or four bfloat16.
+template <typename SP>
+struct EntryRaw;
+template <>
+struct EntryRaw<float> {
+    using type = float4;
+};
+template <>
+struct EntryRaw<uint16_t> {
+    using type = uint2;
+};
+
+template <typename SP>
+__device__ __forceinline__ void widen_entry(const typename EntryRaw<SP>::type& r, float2& P,
+                                            float2& Q)
+{
+    if constexpr (sizeof(SP) == 4) {
+        P = make_float2(r.x, r.y);
+        Q = make_float2(r.z, r.w);
+    } else {
+        P = make_float2(__uint_as_float(r.x << 16), __uint_as_float(r.x & 0xffff0000u));
+        Q = make_float2(__uint_as_float(r.y << 16), __uint_as_float(r.y & 0xffff0000u));
+    }
+}
+
+// Entries e = 0..RL-1 of thread tau of one length-L transform (entry index
+// e T + tau: lanes read consecutive entries).
+template <int L, typename SP>
+__device__ __forceinline__ void load_entries(typename EntryRaw<SP>::type* ent, const SP* spec,
+                                             int tau)
+{
+    using S = FftShape<L>;
+    using Raw = typename EntryRaw<SP>::type;
+    const uint32_t off = (uint32_t)tau * (uint32_t)sizeof(Raw);
+#pragma unroll
+    for (int e = 0; e < S::RL; ++e)
+        ent[e] = at_bytes<Raw>(reinterpret_cast<const Raw*>(spec) + e * S::T, off);
+}
+
 // Mirror-paired product on the last-pass registers of one length-L transform.
-// Entry e of thread tau sits at entry index e T + tau.
 //   tau > 0: last-pass butterflies tau and 2T - tau; entry e pairs output e of
 //            the first with output RL-1-e of the second; the bin <= L/2 is
 //            the first's for e < RL/2, the second's otherwise.
@@ -288,42 +408,63 @@ __device__ __forceinline__ void entry_from_pair(float2 zp, float2 zm, float scal
 //            L/2 (real P, Q), entries 1..RL/2-1 pair outputs (e, RL-e) of
 //            butterfly 0, entries RL/2.. pair outputs (s, RL-1-s) of butterfly T.
 // dp, dq: real offsets added to every P and Q (the folded feedthrough).
+// Thread 0's pairing differs from everyone else's.  It only reads v inside
+// its branch and parks its results in a 4*RL-float LDS scratch `xs`; every
+// lane then runs the common pairing, and thread 0 finally overwrites all of
+// its registers from the scratch.  (A branch that rewrote v in a different
+// pattern would make the register array fall back to private memory.)
 template <int L, typename SP>
-__device__ __forceinline__ void spectral_product(float2* v, const SP* spec, int tau, float dp,
-                                                 float dq)
+__device__ __forceinline__ void spectral_product(float2* v, const typename EntryRaw<SP>::type* ent,
+                                                 int tau, float dp, float dq, float* xs)
 {
     using S = FftShape<L>;
-    constexpr int T = S::T, RL = S::RL;
-    if (tau != 0) {
-#pragma unroll
-        for (int e = 0; e < RL; ++e) {
-            float2 P, Q;
-            load_entry(spec, e * T + tau, P, Q);
-            P.x += dp;
-            Q.x += dq;
-            if (e < RL / 2) pair_product(v[e], v[2 * RL - 1 - e], P, Q);
-            else pair_product(v[2 * RL - 1 - e], v[e], P, Q);
-        }
-    } else {
-        float2 P, Q;
-        load_entry(spec, 0, P, Q);
-        v[0] = self_product(v[0], P.x + dp, Q.x + dq);
-        v[RL / 2] = self_product(v[RL / 2], P.y + dp, Q.y + dq);
+    constexpr int RL = S::RL;
+    float2 P, Q;
+    if (tau == 0) {
+        widen_entry<SP>(ent[0], P, Q);
+        const float2 y0 = self_product(v[0], P.x + dp, Q.x + dq);
+        const float2 yh = self_product(v[RL / 2], P.y + dp, Q.y + dq);
+        xs[0] = y0.x;
+        xs[1] = y0.y;
+        xs[RL] = yh.x;
+        xs[RL + 1] = yh.y;
 #pragma unroll
         for (int e = 1; e < RL / 2; ++e) {
-            load_entry(spec, e * T, P, Q);
+            widen_entry<SP>(ent[e], P, Q);
             P.x += dp;
             Q.x += dq;
-            pair_product(v[e], v[RL - e], P, Q);
+            float2 a = v[e], b = v[RL - e];
+            pair_product(a, b, P, Q);
+            xs[2 * e] = a.x;
+            xs[2 * e + 1] = a.y;
+            xs[2 * (RL - e)] = b.x;
+            xs[2 * (RL - e) + 1] = b.y;
         }
 #pragma unroll
         for (int e = RL / 2; e < RL; ++e) {
-            const int s = e - RL / 2;
-            load_entry(spec, e * T, P, Q);
+            const int s2 = e - RL / 2;
+            widen_entry<SP>(ent[e], P, Q);
             P.x += dp;
             Q.x += dq;
-            pair_product(v[RL + s], v[2 * RL - 1 - s], P, Q);
+            float2 a = v[RL + s2], b = v[2 * RL - 1 - s2];
+            pair_product(a, b, P, Q);
+            xs[2 * (RL + s2)] = a.x;
+            xs[2 * (RL + s2) + 1] = a.y;
+            xs[2 * (2 * RL - 1 - s2)] = b.x;
+            xs[2 * (2 * RL - 1 - s2) + 1] = b.y;
         }
+    }
+#pragma unroll
+    for (int e = 0; e < RL; ++e) {
+        widen_entry<SP>(ent[e], P, Q);
+        P.x += dp;
+        Q.x += dq;
+        if (e < RL / 2) pair_product(v[e], v[2 * RL - 1 - e], P, Q);
+        else pair_product(v[2 * RL - 1 - e], v[e], P, Q);
+    }
+    if (tau == 0) {
+#pragma unroll
+        for (int i = 0; i < 2 * RL; ++i) v[i] = make_float2(xs[2 * i], xs[2 * i + 1]);
     }
 }
 

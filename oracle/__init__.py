@@ -59,6 +59,8 @@ def _load():
                 build(force=True)
             lib = ctypes.CDLL(_LIB_PATH)
             i64, i32, p = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p
+            lib.oracle_num_threads.argtypes = []
+            lib.oracle_num_threads.restype = ctypes.c_int
             lib.oracle_fft.argtypes = [i64, p, p, ctypes.c_int]
             lib.oracle_fft.restype = ctypes.c_int
             lib.oracle_causal_conv_direct.argtypes = [i64, i64, i64, p, p, p, p]
@@ -85,6 +87,11 @@ def _f64(a) -> np.ndarray:
 
 def _ptr(a: np.ndarray):
     return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def num_threads() -> int:
+    """OpenMP threads the oracle's parallel loops use."""
+    return int(_load().oracle_num_threads())
 
 
 def fft(x, inverse: bool = False) -> np.ndarray:

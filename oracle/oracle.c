@@ -36,6 +36,7 @@
  * equivariance, channel independence); direct vs FFT routes.
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -43,6 +44,9 @@
 #ifndef M_PI
 #define M_PI 3.14159265358979323846
 #endif
+
+/* Threads the OpenMP loops below will use (reported beside oracle timings). */
+int oracle_num_threads(void) { return omp_get_max_threads(); }
 
 static int64_t next_pow2(int64_t n)
 {

@@ -1,0 +1,144 @@
+"""GPU parity of the multi-pass paths (four-step 1D and row-column 2D)
+against the float64 oracle, element by element, through the C ABI."""
+import numpy as np
+import pytest
+
+import oracle
+from long_convolution_sequence_rfft_amd import hyena, synth
+from gpu_util import oracle_ref, rel_err, run_gpu, say
+
+pytestmark = pytest.mark.gpu
+TOL_F32 = 1e-5
+TOL_F32_LONG = 5e-5   # fp32, N >= 64K
+TOL_BF16 = 1e-2
+FOUR = hyena.HYENA_PATH_FOURSTEP1D
+
+
+@pytest.mark.parametrize("N", [512, 1000, 2048, 4096, 8192])
+def test_fourstep_forced_small(N):
+    inp = synth.make_1d(B=2, N=N, d=6, order=2, alpha_range=(1e-4, 1e-2), seed=N)
+    y, plan, _ = run_gpu(inp, path=FOUR)
+    assert plan.path == FOUR
+    ref = oracle_ref(inp, method=oracle.DIRECT if N <= 1024 else oracle.FFT)
+    e = rel_err(y, ref)
+    say(f"four-step N={N} rel_err={e:.3e}")
+    assert e < TOL_F32
+
+
+def test_fourstep_agrees_with_single_workgroup_path():
+    inp = synth.make_1d(B=1, N=4096, d=8, order=2, seed=11)
+    y1, _, _ = run_gpu(inp, path=hyena.HYENA_PATH_LDS1D)
+    y2, _, _ = run_gpu(inp, path=FOUR)
+    assert rel_err(y2, y1) < 2e-6
+
+
+@pytest.mark.parametrize("N,d", [(16384, 4), (20000, 3), (32768, 2), (65536, 2)])
+def test_fourstep_long(N, d):
+    inp = synth.make_1d(B=1, N=N, d=d, order=2, alpha_range=(1e-6, 1e-4), seed=N + d)
+    y, plan, _ = run_gpu(inp)
+    assert plan.path == FOUR
+    ref = oracle_ref(inp, method=oracle.FFT)
+    e = rel_err(y, ref)
+    say(f"four-step N={N} d={d} rel_err={e:.3e}")
+    assert e < (TOL_F32 if N < 65536 else TOL_F32_LONG)
+
+
+@pytest.mark.parametrize("order,d", [(1, 5), (3, 7)])
+def test_fourstep_orders_odd_channels(order, d):
+    inp = synth.make_1d(B=2, N=2048, d=d, order=order, seed=order * 10 + d)
+    y, _, _ = run_gpu(inp, path=FOUR)
+    assert rel_err(y, oracle_ref(inp, method=oracle.FFT)) < TOL_F32
+
+
+def test_fourstep_bf16():
+    inp = synth.make_1d(B=1, N=16384, d=4, order=2, alpha_range=(1e-5, 1e-3), dtype=synth.BF16,
+                        seed=5)
+    y, _, _ = run_gpu(inp)
+    assert rel_err(y, oracle_ref(inp, method=oracle.FFT)) < TOL_BF16
+
+
+def test_fourstep_spectrum_export():
+    inp = synth.make_1d(B=1, N=16384, d=3, order=1, seed=6)
+    _, plan, H = run_gpu(inp)
+    nat = plan.export_spectrum(H).cpu().numpy().astype(np.float64)
+    nat = nat[..., 0] + 1j * nat[..., 1]
+    M = 32768
+    h64 = inp.f64()[2]
+    for c in range(3):
+        ref = oracle.fft(np.concatenate([h64[0, c], np.zeros(M - 16384)]))[:M // 2 + 1]
+        assert rel_err(nat[0, c], ref) < 2e-6
+
+
+@pytest.mark.parametrize("X,Y,d,order", [(4, 4, 2, 1), (8, 8, 3, 2), (4, 16, 4, 2), (16, 8, 6, 2),
+                                         (32, 32, 64, 1)])
+def test_rowcol2d_small(X, Y, d, order):
+    inp = synth.make_2d(B=2, X=X, Y=Y, d=d, order=order, sigma_range=(1.0, 8.0), seed=X + Y + d)
+    y, plan, _ = run_gpu(inp)
+    assert plan.path == hyena.HYENA_PATH_ROWCOL2D
+    ref = oracle_ref(inp, method=oracle.DIRECT if X * Y <= 256 else oracle.FFT)
+    e = rel_err(y, ref)
+    say(f"2D {X}x{Y} d={d} rel_err={e:.3e}")
+    assert e < TOL_F32
+
+
+@pytest.mark.parametrize("i0,j0", [(255, -255), (-255, 255), (17, -3)])
+def test_rowcol2d_delta_kernel_is_exact_shift(i0, j0):
+    X = Y = 256
+    inp = synth.make_2d(B=1, X=X, Y=Y, d=2, order=1, seed=abs(i0) + abs(j0))
+    inp.h[:] = 0.0
+    inp.h[0, :, i0 + X - 1, j0 + Y - 1] = 1.0
+    inp.gates[:] = 1.0
+    inp.D[:] = 0.0
+    y, _, _ = run_gpu(inp)
+    u = inp.u.astype(np.float64)
+    ref = np.zeros_like(u)
+    ps, qs = np.meshgrid(np.arange(X), np.arange(Y), indexing="ij")
+    sp, sq = ps - i0, qs - j0
+    ok = (sp >= 0) & (sp < X) & (sq >= 0) & (sq < Y)
+    ref[0][ok] = u[0][sp[ok], sq[ok]]
+    assert np.max(np.abs(y - ref)) < 1e-5 * np.max(np.abs(u))
+
+
+def test_rowcol2d_spectrum_export():
+    X, Y = 16, 8
+    inp = synth.make_2d(B=1, X=X, Y=Y, d=3, order=1, sigma_range=(1.0, 8.0), seed=8)
+    _, plan, H = run_gpu(inp)
+    nat = plan.export_spectrum(H).cpu().numpy().astype(np.float64)
+    nat = nat[..., 0] + 1j * nat[..., 1]
+    K = inp.f64()[2][0]
+    for c in range(3):
+        per = np.zeros((2 * X, 2 * Y))
+        for i in range(-(X - 1), X):
+            for j in range(-(Y - 1), Y):
+                per[i % (2 * X), j % (2 * Y)] = K[c, i + X - 1, j + Y - 1]
+        ref = np.fft.fft2(per)[:, :Y + 1]
+        assert rel_err(nat[0, c], ref) < 2e-6
+
+
+def test_multipass_deterministic_bitwise():
+    inp = synth.make_1d(B=1, N=32768, d=8, order=2, seed=9)
+    y1, plan, _ = run_gpu(inp)
+    y2, _, _ = run_gpu(inp, plan=plan)
+    assert np.array_equal(y1, y2)
+
+
+def test_full_size_64k_sampled():
+    inp = synth.make_config(3)
+    y, plan, _ = run_gpu(inp)
+    rng = np.random.default_rng(3)
+    ch = np.unique(np.concatenate([[0, 1, inp.d - 1], rng.choice(inp.d, 13, replace=False)]))
+    ref = oracle_ref(inp, channels=ch, method=oracle.FFT)
+    e = rel_err(y[..., ch], ref)
+    say(f"64K full-size sampled rel_err={e:.3e}")
+    assert e < TOL_F32_LONG
+
+
+def test_full_size_2d_sampled():
+    inp = synth.make_config(4)
+    y, plan, _ = run_gpu(inp)
+    rng = np.random.default_rng(4)
+    ch = np.unique(np.concatenate([[0, 1, inp.d - 1], rng.choice(inp.d, 5, replace=False)]))
+    ref = oracle_ref(inp, channels=ch, method=oracle.FFT)
+    e = rel_err(y[..., ch], ref)
+    say(f"2D 256x256 full-size sampled rel_err={e:.3e}")
+    assert e < TOL_F32
