@@ -114,11 +114,11 @@ hyena_status launch_lds1d_export(const Plan& p, const void* H, void* out, void* 
 namespace {
 
 template <typename IO, typename SP>
-hyena_status fwd_by_m(int64_t M, const Lds1dFwdArgs& a, bool fast, hipStream_t s)
+hyena_status fwd_by_m(int64_t M, const Lds1dFwdArgs& a, int mode, hipStream_t s)
 {
     switch (M) {
 #define HY_CASE(MM, I, S_) \
-    case MM: return lds1d_forward_launch<MM, IO, SP>(a, fast, s);
+    case MM: return lds1d_forward_launch<MM, IO, SP>(a, mode, s);
         HY_LDS1D_SIZES(HY_CASE, IO, SP)
 #undef HY_CASE
         default: return fail(HYENA_ERR_UNSUPPORTED, "LDS1D: unsupported transform length");
@@ -149,10 +149,74 @@ TwOffsets lds1d_offsets(const Plan& p)
 
 }  // namespace
 
+// ---------------------------------------------------------------------------
+// Pair-major staging: [B][N][d] channels last <-> [B][pairs][N] pair elements
+// (d even).  64 samples x one cache line of pairs per tile; both the row reads
+// and the run writes are contiguous.
+// ---------------------------------------------------------------------------
+struct StageArgs {
+    const void* src[kMaxOrder + 1];
+    void* dst[kMaxOrder + 1];
+    int64_t B, N, d, npairs;
+};
+
+template <typename IO, bool TO_PAIRMAJOR>
+__global__ void __launch_bounds__(256) hyena_stage_pairs(StageArgs a)
+{
+    using Raw = typename PairRaw<IO>::type;
+    constexpr int TP = 128 / (int)sizeof(Raw);  // pairs per 128-byte line
+    constexpr int TT = 64;                      // samples per tile
+    __shared__ Raw tile[TT][TP + 1];
+    const int64_t p0 = (int64_t)blockIdx.x * TP;
+    const int64_t t0 = (int64_t)blockIdx.y * TT;
+    const int64_t b = blockIdx.z % a.B;
+    const int s = blockIdx.z / a.B;
+    const Raw* src = static_cast<const Raw*>(a.src[s]);
+    Raw* dst = static_cast<Raw*>(a.dst[s]);
+    const int64_t P = a.npairs;
+    const int64_t rowpairs = a.d / 2;  // pair elements per channels-last row
+    for (int i = threadIdx.x; i < TT * TP; i += 256) {
+        if (TO_PAIRMAJOR) {
+            const int tr = i / TP, pc = i % TP;
+            const int64_t t = t0 + tr, p = p0 + pc;
+            if (t < a.N && p < P) tile[tr][pc] = src[(b * a.N + t) * rowpairs + p];
+        } else {
+            const int pc = i / TT, tr = i % TT;
+            const int64_t t = t0 + tr, p = p0 + pc;
+            if (t < a.N && p < P) tile[tr][pc] = src[(b * P + p) * a.N + t];
+        }
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < TT * TP; i += 256) {
+        if (TO_PAIRMAJOR) {
+            const int pc = i / TT, tr = i % TT;
+            const int64_t t = t0 + tr, p = p0 + pc;
+            if (t < a.N && p < P) dst[(b * P + p) * a.N + t] = tile[tr][pc];
+        } else {
+            const int tr = i / TP, pc = i % TP;
+            const int64_t t = t0 + tr, p = p0 + pc;
+            if (t < a.N && p < P) dst[(b * a.N + t) * rowpairs + p] = tile[tr][pc];
+        }
+    }
+}
+
+template <typename IO>
+hyena_status stage_launch(const StageArgs& a, int ntensors, bool to_pm, hipStream_t s)
+{
+    constexpr int TP = 128 / (int)sizeof(typename PairRaw<IO>::type);
+    const dim3 grid((unsigned)((a.npairs + TP - 1) / TP), (unsigned)((a.N + 63) / 64),
+                    (unsigned)(a.B * ntensors));
+    if (to_pm) hipLaunchKernelGGL((hyena_stage_pairs<IO, true>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((hyena_stage_pairs<IO, false>), grid, dim3(256), 0, s, a);
+    const hipError_t e = hipGetLastError();
+    return e == hipSuccess ? HYENA_OK : fail(HYENA_ERR_DEVICE, hipGetErrorString(e));
+}
+
 hyena_status launch_lds1d_forward(const Plan& p, const void* u, const void* const* gates,
                                   const void* H, const float* D, void* y, const void* ws,
                                   void* stream)
 {
+    const hipStream_t s = (hipStream_t)stream;
     Lds1dFwdArgs a{};
     a.u = u;
     for (int n = 0; n < p.order; ++n) a.gates[n] = gates[n];
@@ -163,14 +227,50 @@ hyena_status launch_lds1d_forward(const Plan& p, const void* u, const void* cons
     a.N = p.N;
     a.d = p.d;
     a.npairs = p.npairs;
-    a.nblocks = p.B * p.npairs;
     a.order = p.order;
     a.tw_off = lds1d_offsets(p);
-    const bool fast = (p.d % 2 == 0) && (p.N * 2 == p.M);
-    const hipStream_t s = (hipStream_t)stream;
-    if (p.io_dtype == HYENA_F32) return fwd_by_m<float, float>(p.M, a, fast, s);
-    if (p.spec_dtype == HYENA_BF16) return fwd_by_m<uint16_t, uint16_t>(p.M, a, fast, s);
-    return fwd_by_m<uint16_t, float>(p.M, a, fast, s);
+    const int mode = p.lds_io;
+    int64_t K = 1;
+    if (mode == IO_TILED) {
+        K = 16384 / p.M < 16 ? 16384 / p.M : 16;
+    }
+    a.nblocks = p.B * ((p.npairs + K - 1) / K);
+    StageArgs st{};
+    if (mode == IO_PAIRMAJOR) {
+        const size_t esz = p.io_dtype == HYENA_F32 ? 4 : 2;
+        const size_t tensor = (size_t)p.B * p.N * p.d * esz;
+        char* base = const_cast<char*>(static_cast<const char*>(ws)) + p.stage_offset;
+        st.B = p.B;
+        st.N = p.N;
+        st.d = p.d;
+        st.npairs = p.npairs;
+        st.src[0] = u;
+        st.dst[0] = base;
+        for (int n = 0; n < p.order; ++n) {
+            st.src[1 + n] = gates[n];
+            st.dst[1 + n] = base + (size_t)(1 + n) * tensor;
+        }
+        a.u = base;
+        for (int n = 0; n < p.order; ++n) a.gates[n] = base + (size_t)(1 + n) * tensor;
+        a.y = base + (size_t)(1 + p.order) * tensor;
+        const hyena_status r = p.io_dtype == HYENA_F32 ? stage_launch<float>(st, 1 + p.order, true, s)
+                                                       : stage_launch<uint16_t>(st, 1 + p.order, true, s);
+        if (r != HYENA_OK) return r;
+    }
+    hyena_status r;
+    if (p.io_dtype == HYENA_F32) r = fwd_by_m<float, float>(p.M, a, mode, s);
+    else if (p.spec_dtype == HYENA_BF16) r = fwd_by_m<uint16_t, uint16_t>(p.M, a, mode, s);
+    else r = fwd_by_m<uint16_t, float>(p.M, a, mode, s);
+    if (r != HYENA_OK || mode != IO_PAIRMAJOR) return r;
+    StageArgs out{};
+    out.B = p.B;
+    out.N = p.N;
+    out.d = p.d;
+    out.npairs = p.npairs;
+    out.src[0] = a.y;
+    out.dst[0] = y;
+    return p.io_dtype == HYENA_F32 ? stage_launch<float>(out, 1, false, s)
+                                   : stage_launch<uint16_t>(out, 1, false, s);
 }
 
 hyena_status launch_lds1d_spectrum(const Plan& p, const void* h, void* H, const void* ws,

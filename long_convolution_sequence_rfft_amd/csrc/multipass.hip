@@ -118,8 +118,8 @@ hyena_status mp_forward(const Plan& p, const void* u, const void* const* gates, 
     const hipStream_t s = (hipStream_t)stream;
     MpGeom g = base_geom(p);
     const int KP = 1 << g.kp_log2;
-    const int C = (512 / threads_per_transform(g.La)) / KP;
-    const int U = (512 / threads_per_transform(g.Lb)) / 2;
+    const int C = (kMpThreads / threads_per_transform(g.La)) / KP;
+    const int U = (kMpThreads / threads_per_transform(g.Lb)) / 2;
     const int64_t col_blocks = (g.Lb_live + C - 1) / C;
     const int64_t unit_blocks = (g.La / 2 + U - 1) / U;
     const int64_t total_groups = (int64_t)p.B * g.groups_per_b;
@@ -163,8 +163,8 @@ hyena_status mp_spectrum(const Plan& p, const void* h, void* H, void* ws, void* 
     MpGeom g = base_geom(p);
     g.B = 1;  // filters have no batch axis
     const int KP = 1 << g.kp_log2;
-    const int C = (512 / threads_per_transform(g.La)) / KP;
-    const int U = (512 / threads_per_transform(g.Lb)) / 2;
+    const int C = (kMpThreads / threads_per_transform(g.La)) / KP;
+    const int U = (kMpThreads / threads_per_transform(g.Lb)) / 2;
     const int64_t col_blocks = (g.Lb + C - 1) / C;
     const int64_t unit_blocks = (g.La / 2 + U - 1) / U;
     const int64_t total_groups = g.groups_per_b;

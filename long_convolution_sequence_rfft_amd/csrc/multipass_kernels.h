@@ -9,13 +9,19 @@ namespace hy {
 enum OuterMode { OUTER_IN = 0, OUTER_MID = 1, OUTER_OUT = 2, OUTER_SPEC = 3 };
 enum InnerMode { INNER_CHAIN = 0, INNER_SPEC = 1 };
 
-// Transforms per workgroup and threads: 512 threads, one length-L transform
-// per FftShape<L>::T threads.
+// Workgroup of kMpThreads threads, one length-L transform per
+// FftShape<L>::T threads.  256 threads and 16384 points (68 KB of LDS) per
+// workgroup let two workgroups share a CU, so one's barriers and memory
+// waits overlap the other's arithmetic.
+// Regions are RS = LW rounded up to an odd word count apart, so the staging
+// loops (adjacent lanes -> same position of adjacent transforms) spread
+// over the LDS banks.
+constexpr int kMpThreads = 256;
 template <int L>
 struct MpShape {
     static constexpr int T = FftShape<L>::T;
-    static constexpr int NF = 512 / T;
-    static constexpr int LW = FftShape<L>::LW;
+    static constexpr int NF = kMpThreads / T;
+    static constexpr int LW = FftShape<L>::LW | 1;
 };
 
 struct OuterArgs {
@@ -69,7 +75,7 @@ __device__ __forceinline__ void act_store(IO* base, int64_t row, int64_t c0, int
 // blockIdx.x = column block * ngroups + group-in-chunk.
 // ---------------------------------------------------------------------------
 template <int LA, typename IO, int MODE, bool HALF_SPEC>
-__global__ void __launch_bounds__(512) hyena_mp_outer(OuterArgs a)
+__global__ void __launch_bounds__(kMpThreads, 2) hyena_mp_outer(OuterArgs a)
 {
     using S = FftShape<LA>;
     using X = MpShape<LA>;
@@ -102,8 +108,11 @@ __global__ void __launch_bounds__(512) hyena_mp_outer(OuterArgs a)
     // index -> (pair kp', outer sample s, column c'); KP consecutive lanes
     // cover one row's KP channel pairs (one cache line for KP = 16 f32).
     auto tile_rows = [&](auto&& fn) {
-        const int total = (LA / 2) * C * KP;
-        for (int idx = threadIdx.x; idx < total; idx += 512) {
+        constexpr int total = (LA / 2) * NF;  // = (LA/2) C KP
+        static_assert(total % kMpThreads == 0, "tile split");
+#pragma unroll
+        for (int it = 0; it < total / kMpThreads; ++it) {
+            const int idx = (int)threadIdx.x + it * kMpThreads;
             const int kq = idx & (KP - 1);
             const int rest = idx >> g.kp_log2;
             const int s = rest % (LA / 2);
@@ -114,14 +123,14 @@ __global__ void __launch_bounds__(512) hyena_mp_outer(OuterArgs a)
             pair_of_slot(g, group, kq, bq, pq, lq);
             const int oq = cb * C + cq;
             const int64_t t = g.sa * s + g.so * (int64_t)oq;
-            fn(fq, s, bq, pq, lq && oq < n_outer && t < g.N, bq * g.N + t);
+            fn(it, fq, s, pq, lq && oq < n_outer && t < g.N, bq * g.N + t);
         }
     };
 
     float2 v[S::PTS];
     if constexpr (MODE == OUTER_IN) {
         const IO* u = static_cast<const IO*>(a.act);
-        tile_rows([&](int fq, int s, int64_t, int64_t pq, bool ok, int64_t row) {
+        tile_rows([&](int, int fq, int s, int64_t pq, bool ok, int64_t row) {
             const float2 x = ok ? act_load<IO>(u, row, 2 * pq, g.d) : make_float2(0.0f, 0.0f);
             sre[fq * LW + lpad(s)] = x.x;
             sim[fq * LW + lpad(s)] = x.y;
@@ -162,7 +171,16 @@ __global__ void __launch_bounds__(512) hyena_mp_outer(OuterArgs a)
                 v[q * R0 + r] = x;
             }
     } else {
-        // MID / OUT: F column -> (conj twiddle) -> region, inverse outer DFT
+        // MID / OUT.  The gate tile is fetched into registers first, so its
+        // latency overlaps the F column load and the inverse outer DFT.
+        constexpr int GT = (LA / 2) * NF / kMpThreads;  // tile elements per thread
+        static_assert(GT >= 1 && (LA / 2) * NF % kMpThreads == 0, "gate tile");
+        const IO* gate = static_cast<const IO*>(a.act);
+        float2 gval[GT];
+        tile_rows([&](int it, int, int, int64_t pq, bool ok, int64_t row) {
+            gval[it] = ok ? act_load<IO>(gate, row, 2 * pq, g.d) : make_float2(0.0f, 0.0f);
+        });
+        // F column -> (conj twiddle) -> region, inverse outer DFT
         for (int i = tau; i < LA; i += TA) {
             float2 x = make_float2(0.0f, 0.0f);
             if (col_live) {
@@ -174,13 +192,10 @@ __global__ void __launch_bounds__(512) hyena_mp_outer(OuterArgs a)
         }
         __syncthreads();
         inv_lds_to_regs<LA, true>(v, re, im, a.tw, g.tw_a, tau);
-        // gate tile for the live outer samples
         __syncthreads();
-        const IO* gate = static_cast<const IO*>(a.act);
-        tile_rows([&](int fq, int s, int64_t, int64_t pq, bool ok, int64_t row) {
-            const float2 x = ok ? act_load<IO>(gate, row, 2 * pq, g.d) : make_float2(0.0f, 0.0f);
-            sre[fq * LW + lpad(s)] = x.x;
-            sim[fq * LW + lpad(s)] = x.y;
+        tile_rows([&](int it, int fq, int s, int64_t, bool, int64_t) {
+            sre[fq * LW + lpad(s)] = gval[it].x;
+            sim[fq * LW + lpad(s)] = gval[it].y;
         });
         __syncthreads();
 #pragma unroll
@@ -196,7 +211,7 @@ __global__ void __launch_bounds__(512) hyena_mp_outer(OuterArgs a)
             regs_to_lds<LA, true>(v, re, im, tau);
             __syncthreads();
             IO* y = static_cast<IO*>(a.out);
-            tile_rows([&](int fq, int s, int64_t, int64_t pq, bool ok, int64_t row) {
+            tile_rows([&](int, int fq, int s, int64_t pq, bool ok, int64_t row) {
                 if (ok) act_store<IO>(y, row, 2 * pq, g.d,
                                       make_float2(sre[fq * LW + lpad(s)], sim[fq * LW + lpad(s)]));
             });
@@ -284,7 +299,7 @@ __device__ __forceinline__ void unit_pairing(bool four_step, int kk, int e, int 
 }
 
 template <int LB, typename SP, int MODE, bool HALF_B>
-__global__ void __launch_bounds__(512) hyena_mp_inner(InnerArgs a)
+__global__ void __launch_bounds__(kMpThreads, 2) hyena_mp_inner(InnerArgs a)
 {
     using S = FftShape<LB>;
     using X = MpShape<LB>;
@@ -317,9 +332,28 @@ __global__ void __launch_bounds__(512) hyena_mp_inner(InnerArgs a)
         return side == 0 ? kk : (kk == 0 ? La / 2 : La - kk);
     };
 
+    // this thread's share of the mirror-paired product: unit u, entries
+    // e = tu + i 2TB
+    constexpr int EPT = LB / (2 * TB);
+    const int u_me = f >> 1;
+    const int tu = (f & 1) * TB + tau;  // 0 .. 2 TB - 1
+    const int kk_me = kk0 + u_me;
+    const bool unit_ok = u_me < nu && live;
+    const int64_t ebase = p * (int64_t)(La / 2) * LB + (int64_t)kk_me * LB;
+    typename EntryRaw<SP>::type ent[EPT];
+    if constexpr (MODE == INNER_CHAIN) {
+        // entries first: their latency overlaps the F load and the forward DFT
+        if (unit_ok) {
+            using Raw = typename EntryRaw<SP>::type;
+#pragma unroll
+            for (int i = 0; i < EPT; ++i)
+                ent[i] = reinterpret_cast<const Raw*>(a.spec)[ebase + tu + i * 2 * TB];
+        }
+    }
+
     // F[o][column] -> region of (u, side) at inner position o
     const int total = nlive * nu * 2;
-    for (int idx = threadIdx.x; idx < total; idx += 512) {
+    for (int idx = threadIdx.x; idx < total; idx += kMpThreads) {
         const int u = idx % nu;
         const int side = (idx / nu) & 1;
         const int op = idx / (2 * nu);
@@ -337,13 +371,9 @@ __global__ void __launch_bounds__(512) hyena_mp_inner(InnerArgs a)
     __syncthreads();
 
     // mirror-paired product (CHAIN) or entry computation (SPEC)
-    if ((f >> 1) < nu && live) {
-        const int u = f >> 1;
-        const int tu = (f & 1) * TB + tau;  // 0 .. 2 TB - 1
-        const int kk = kk0 + u;
-        float* ure = sre + (2 * u) * LW;
-        float* uim = sim + (2 * u) * LW;
-        const int64_t ebase = p * (int64_t)(La / 2) * LB + (int64_t)kk * LB;
+    if (unit_ok) {
+        float* ure = sre + (2 * u_me) * LW;
+        float* uim = sim + (2 * u_me) * LW;
         float dp = 0.0f, dq = 0.0f;
         if constexpr (MODE == INNER_CHAIN) {
             const int64_t c0 = 2 * p;
@@ -354,15 +384,17 @@ __global__ void __launch_bounds__(512) hyena_mp_inner(InnerArgs a)
             dp = (Da + Db) * inv2M;
             dq = (Da - Db) * inv2M;
         }
-        for (int e = tu; e < LB; e += 2 * TB) {
+#pragma unroll
+        for (int i = 0; i < EPT; ++i) {
+            const int e = tu + i * 2 * TB;
             int fa, ka, fb, kb, self;
-            unit_pairing(g.four_step != 0, kk, e, LB, fa, ka, fb, kb, self);
+            unit_pairing(g.four_step != 0, kk_me, e, LB, fa, ka, fb, kb, self);
             const int ia = fa * LW + lpad(ka), ib = fb * LW + lpad(kb);
             float2 za = make_float2(ure[ia], uim[ia]);
             float2 zb = make_float2(ure[ib], uim[ib]);
             if constexpr (MODE == INNER_CHAIN) {
                 float2 P, Q;
-                load_entry(static_cast<const SP*>(a.spec), ebase + e, P, Q);
+                widen_entry<SP>(ent[i], P, Q);
                 if (self) {
                     za = self_product(za, P.x + dp, Q.x + dq);
                     zb = self_product(zb, P.y + dp, Q.y + dq);
@@ -396,7 +428,7 @@ __global__ void __launch_bounds__(512) hyena_mp_inner(InnerArgs a)
     regs_to_lds<LB, HALF_B>(v, re, im, tau);
     __syncthreads();
     const int total_out = g.Lb_live * nu * 2;
-    for (int idx = threadIdx.x; idx < total_out; idx += 512) {
+    for (int idx = threadIdx.x; idx < total_out; idx += kMpThreads) {
         const int u = idx % nu;
         const int side = (idx / nu) & 1;
         const int op = idx / (2 * nu);
@@ -413,7 +445,7 @@ namespace hy {
 template <int LA, typename IO, int MODE, bool HALF_SPEC>
 hyena_status mp_outer_launch(const OuterArgs& a, int64_t nblocks, hipStream_t s)
 {
-    hipLaunchKernelGGL((hyena_mp_outer<LA, IO, MODE, HALF_SPEC>), dim3((unsigned)nblocks), dim3(512),
+    hipLaunchKernelGGL((hyena_mp_outer<LA, IO, MODE, HALF_SPEC>), dim3((unsigned)nblocks), dim3(kMpThreads),
                        0, s, a);
     const hipError_t e = hipGetLastError();
     return e == hipSuccess ? HYENA_OK : fail(HYENA_ERR_DEVICE, hipGetErrorString(e));
@@ -422,7 +454,7 @@ hyena_status mp_outer_launch(const OuterArgs& a, int64_t nblocks, hipStream_t s)
 template <int LB, typename SP, int MODE, bool HALF_B>
 hyena_status mp_inner_launch(const InnerArgs& a, int64_t nblocks, hipStream_t s)
 {
-    hipLaunchKernelGGL((hyena_mp_inner<LB, SP, MODE, HALF_B>), dim3((unsigned)nblocks), dim3(512), 0,
+    hipLaunchKernelGGL((hyena_mp_inner<LB, SP, MODE, HALF_B>), dim3((unsigned)nblocks), dim3(kMpThreads), 0,
                        s, a);
     const hipError_t e = hipGetLastError();
     return e == hipSuccess ? HYENA_OK : fail(HYENA_ERR_DEVICE, hipGetErrorString(e));

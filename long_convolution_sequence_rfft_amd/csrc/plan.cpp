@@ -113,6 +113,11 @@ hyena_status plan_build(Plan& p, int64_t B, int64_t N, int64_t d, int32_t order,
             p.R1 = lds1d_r1(M);
             p.RL = lds1d_rl(M);
             add_transform_segments(p, off, p.M);
+            // activation access: staged pair-major in the workspace (measured
+            // faster than multi-pair workgroups with LDS tiles at 2K and 8K);
+            // odd d or N < M/2 take the per-lane path.
+            const bool fast = (d % 2 == 0) && (2 * N == p.M);
+            p.lds_io = !fast ? 0 : 2;
         } else {
             fourstep_split(p.M, p.M1, p.M2);
             // outer (column, length M1) and inner (row, length M2) transforms use
@@ -170,7 +175,13 @@ hyena_status plan_build(Plan& p, int64_t B, int64_t N, int64_t d, int32_t order,
         const int64_t need = chunk * (fwd_pair > spec_pair ? fwd_pair : spec_pair);
         p.inter_bytes = align_up((size_t)need, 256);
     }
-    p.workspace_bytes = p.inter_offset + p.inter_bytes;
+    if (p.path == HYENA_PATH_LDS1D && p.lds_io == 2) {
+        // u, every gate and y, pair-major
+        p.stage_offset = p.inter_offset + p.inter_bytes;
+        p.stage_bytes = align_up((size_t)(p.order + 2) * (size_t)B * (size_t)N * (size_t)d *
+                                     (io_dtype == HYENA_F32 ? 4u : 2u), 256);
+    }
+    p.workspace_bytes = p.inter_offset + p.inter_bytes + p.stage_bytes;
     return HYENA_OK;
 }
 

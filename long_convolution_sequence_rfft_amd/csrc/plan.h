@@ -59,6 +59,10 @@ struct Plan {
 
     // LDS1D: forward radices R0, R1 (1 if absent), RL; inverse runs them reversed.
     int32_t R0 = 0, R1 = 1, RL = 0;
+    // LDS1D activation access: 0 direct per-lane, 1 tiled K pairs per
+    // workgroup, 2 pair-major staging in the workspace (transposed in and out)
+    int32_t lds_io = 0;
+    size_t stage_offset = 0, stage_bytes = 0;  // pair-major staging in the workspace
 
     // FOURSTEP1D: M = M1 * M2; columns of length M1 (time index t = M2 n1 + n2),
     // rows of length M2.  ROWCOL2D: P1 = 2X (columns), P2 = 2Y (rows).

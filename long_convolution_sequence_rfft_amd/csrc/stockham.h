@@ -201,6 +201,33 @@ __device__ __forceinline__ void lds_read(const float* sre, const float* sim, flo
     }
 }
 
+// Natural positions j + r L/R for r < RN (RN <= R), j < L/R: the R0-pass
+// sample layout.  Same carry-free addressing as lds_read.
+template <int RN, int R, int L>
+__device__ __forceinline__ void lds_read_first(const float* sre, const float* sim, float2* v, int j)
+{
+    const int pb = lpad(j);
+#pragma unroll
+    for (int r = 0; r < RN; ++r) {
+        const int c = r * (L / R);
+        const int i = pb + c + (c >> 5);
+        v[r] = make_float2(sre[i], sim[i]);
+    }
+}
+
+template <int RN, int R, int L>
+__device__ __forceinline__ void lds_write_first(float* sre, float* sim, const float2* v, int j)
+{
+    const int pb = lpad(j);
+#pragma unroll
+    for (int r = 0; r < RN; ++r) {
+        const int c = r * (L / R);
+        const int i = pb + c + (c >> 5);
+        sre[i] = v[r].x;
+        sim[i] = v[r].y;
+    }
+}
+
 // Twiddles of butterfly k of a pass with sub-transform length NS: input r
 // takes tab[(r - 1) NS + k].  Loaded into registers ahead of the barrier that
 // precedes the pass, so the load latency overlaps the LDS exchange.
