@@ -95,19 +95,27 @@ def kernel_source_sha():
     return h.hexdigest()[:16]
 
 
-def load_traffic(name):
-    """HBM bytes per forward from the committed rocprofv3 counter summary, or
-    None if the kernels changed since the counters were taken."""
-    path = os.path.join(ROOT, "profiles", "traffic.json")
+def load_traffic(workload, kernel):
+    """Measured HBM bytes per launch of `kernel` (FETCH_SIZE + WRITE_SIZE,
+    each scaled by the plain copy kernel's reading) from the committed
+    rocprofv3 counter summary, or None if there is none for this kernel or the
+    kernel sources changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "traffic.txt")
     if not os.path.exists(path):
         return None
-    try:
-        rec = json.load(open(path)).get(name)
-    except Exception:
-        return None
-    if not rec or rec.get("kernel_source_sha") != kernel_source_sha():
-        return None
-    return rec.get("hbm_bytes_per_forward")
+    sha = None
+    for line in open(path):
+        line = line.rstrip("\n")
+        if line.startswith("# kernel_source_sha"):
+            sha = line.split()[-1]
+        if not line or line.startswith("#"):
+            continue
+        f = line.split("\t")
+        if len(f) >= 4 and f[0] == workload and f[1] == kernel:
+            if sha != kernel_source_sha():
+                return None
+            return int(float(f[2]) + float(f[3]))
+    return None
 
 
 # ---------------------------------------------------------------------------
@@ -180,7 +188,8 @@ def run_workload(idx, steps, warmup, min_rotation_bytes=600 << 20):
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
-    # whole-job time over exactly `steps` forwards
+    # Timed region: exactly `steps` forwards between two events on the launch
+    # stream (torch's current stream, which the plan launches on).
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record()
@@ -189,19 +198,26 @@ def run_workload(idx, steps, warmup, min_rotation_bytes=600 << 20):
     stop.record()
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(stop)
-    # per-launch durations (events on the stream the kernels are launched on)
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
-    evs[0].record()
+    # The same `steps` forwards again with every kernel launch bracketed by
+    # its own pair of events on that stream (hyena_timing_*): per-kernel
+    # launch durations.  The event markers add a few microseconds between
+    # launches, so the whole-job time above comes from the clean region.
+    hyena.hyena_timing_begin(steps * 64)
+    start2, stop2 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start2.record()
     for i in range(steps):
         step(i)
-        evs[i + 1].record()
+    stop2.record()
     torch.cuda.synchronize()
-    per = np.array([evs[i].elapsed_time(evs[i + 1]) for i in range(steps)])
+    kernels, dropped = hyena.hyena_timing_end()
+    hyena.hyena_timing_release()
+    traced_ms = start2.elapsed_time(stop2)
+    if dropped:
+        log(f"[bench] {name}: {dropped} launches not timed")
 
     tokens = cfg["B"] * (cfg["N"] if cfg["kind"] == "1d" else cfg["X"] * cfg["Y"])
     tc = tokens * cfg["d"]
     ms = total_ms / steps
-    fwd_ms = float(np.mean(per))
     flops = algorithmic_flops(cfg)
     res = {
         "workload": name,
@@ -211,18 +227,20 @@ def run_workload(idx, steps, warmup, min_rotation_bytes=600 << 20):
         "spectrum": "bf16" if spec_dtype == hyena.HYENA_BF16 else "f32",
         "ms_per_step": ms,
         "tc_per_s": tc / (ms * 1e-3),
-        "forward_ms_mean": fwd_ms,
-        "forward_ms_p10": float(np.percentile(per, 10)),
-        "forward_ms_p90": float(np.percentile(per, 90)),
         "spectrum_ms": spectrum_ms,
         "rotation_sets": nsets,
         "algorithmic_bytes": bytes_alg,
         "algorithmic_flops": flops,
-        "hbm_GBps": bytes_alg / (fwd_ms * 1e-3) / 1e9,
-        "hbm_frac": bytes_alg / (fwd_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
-        "alu_TFLOPs": flops / (fwd_ms * 1e-3) / 1e12,
-        "alu_frac": flops / (fwd_ms * 1e-3) / 1e12 / ALU_PEAK_TFLOPS,
-        "launches_per_forward": 1 if plan.path == 1 else None,
+        "hbm_GBps": bytes_alg / (ms * 1e-3) / 1e9,
+        "hbm_frac": bytes_alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+        "alu_TFLOPs": flops / (ms * 1e-3) / 1e12,
+        "alu_frac": flops / (ms * 1e-3) / 1e12 / ALU_PEAK_TFLOPS,
+        "traced_ms_per_step": traced_ms / steps,
+        "kernels": {k: {"launches_per_forward": v["launches"] / steps,
+                        "avg_launch_ms": v["total_ms"] / v["launches"],
+                        "ms_per_forward": v["total_ms"] / steps}
+                    for k, v in sorted(kernels.items(), key=lambda kv: -kv[1]["total_ms"])},
+        "cfg": cfg,
     }
     log(f"[bench] {name}: {ms * 1e3:.1f} us/step, {res['tc_per_s'] / 1e9:.1f} G tc/s, "
         f"{res['hbm_GBps']:.0f} GB/s ({100 * res['hbm_frac']:.1f}% HBM), "
@@ -232,16 +250,72 @@ def run_workload(idx, steps, warmup, min_rotation_bytes=600 << 20):
     return res
 
 
+def kernel_share(cfg, kernel):
+    """Algorithmic (flops, bytes) per forward attributed to one kernel.
+
+    Per token*channel and stage the flop model gives 5 log2 M to each of the
+    forward and the inverse transform and 9 to the spectral product,
+    feedthrough and gate; a multi-pass transform of length M = La * Lb
+    splits its 5 log2 M as 5 log2 La (outer pass) + 5 log2 Lb (inner pass).
+    Bytes: the activations, spectra and feedthrough a kernel consumes or
+    produces; staging copies move no algorithmic bytes."""
+    tc = cfg["B"] * cfg["d"] * (cfg["N"] if cfg["kind"] == "1d" else cfg["X"] * cfg["Y"])
+    s_io = io_bytes(cfg["dtype"])
+    s_sp = io_bytes(cfg["dtype"])
+    order, d = cfg["order"], cfg["d"]
+    spec = order * d * (2 * cfg["N"] if cfg["kind"] == "1d" else 4 * cfg["X"] * cfg["Y"]) * s_sp \
+        + order * d * 4
+    act = tc * s_io
+    M = transform_points(cfg)
+    short = kernel.split("<")[0].replace("hy::", "")
+    args = [a.strip() for a in kernel[kernel.index("<") + 1:kernel.rindex(">")].split(",")] \
+        if "<" in kernel else []
+    if short == "hyena_lds1d_forward":
+        return algorithmic_flops(cfg), algorithmic_bytes(cfg, cfg["dtype"])
+    if short == "hyena_mp_outer":
+        la, mode = int(args[0]), int(args[2])
+        lg = math.log2(la)
+        table = {0: (5 * lg, act),                                   # u -> forward outer
+                 1: ((order - 1) * (10 * lg + 1), (order - 1) * act),  # inverse, gate, forward
+                 2: (5 * lg + 1, 2 * act)}                            # inverse, gate -> y
+        if mode in table:
+            f, b = table[mode]
+            return f * tc, b
+        return 0.0, 0.0
+    if short == "hyena_mp_inner":
+        lb, mode = int(args[0]), int(args[2])
+        if mode == 0:
+            return order * (10 * math.log2(lb) + 8) * tc, spec
+        return 0.0, 0.0
+    return 0.0, 0.0
+
+
 def roofline_of(res):
-    t_hbm = res["algorithmic_bytes"] / (HBM_PEAK_GBPS * 1e9)
-    t_alu = res["algorithmic_flops"] / (ALU_PEAK_TFLOPS * 1e12)
-    traffic = load_traffic(res["workload"])
+    """Roofline of the workload's dominant kernel (largest time per forward):
+    its algorithmic flops or bytes per launch over its average launch duration,
+    both from the timed region."""
+    cfg = res["cfg"]
+    name, k = next(iter(res["kernels"].items()))
+    flops, nbytes = kernel_share(cfg, name)
+    per_launch_f = flops / k["launches_per_forward"]
+    per_launch_b = nbytes / k["launches_per_forward"]
+    sec = k["avg_launch_ms"] * 1e-3
+    traffic = load_traffic(res["workload"], name)
+    t_hbm = per_launch_b / (HBM_PEAK_GBPS * 1e9)
+    t_alu = per_launch_f / (ALU_PEAK_TFLOPS * 1e12)
+    out = {"kernel": name, "launches_per_forward": k["launches_per_forward"],
+           "avg_launch_us": round(k["avg_launch_ms"] * 1e3, 2)}
     if t_alu >= t_hbm:
-        return {"bound": "alu", "achieved": round(res["alu_TFLOPs"], 3),
-                "peak": round(ALU_PEAK_TFLOPS, 2), "unit": "TFLOP/s",
-                "frac": round(res["alu_frac"], 4), "traffic": traffic}
-    return {"bound": "hbm", "achieved": round(res["hbm_GBps"], 1), "peak": HBM_PEAK_GBPS,
-            "unit": "GB/s", "frac": round(res["hbm_frac"], 4), "traffic": traffic}
+        a = per_launch_f / sec / 1e12
+        out.update({"bound": "alu", "achieved": round(a, 3), "peak": round(ALU_PEAK_TFLOPS, 2),
+                    "unit": "TFLOP/s", "frac": round(a / ALU_PEAK_TFLOPS, 4)})
+    else:
+        a = per_launch_b / sec / 1e9
+        out.update({"bound": "hbm", "achieved": round(a, 1), "peak": HBM_PEAK_GBPS,
+                    "unit": "GB/s", "frac": round(a / HBM_PEAK_GBPS, 4)})
+    out["algorithmic_per_launch"] = {"flops": per_launch_f, "bytes": per_launch_b}
+    out["traffic"] = traffic
+    return out
 
 
 # ---------------------------------------------------------------------------
@@ -277,14 +351,15 @@ def cpu_baseline(idx, max_channels):
 # ---------------------------------------------------------------------------
 
 def copy_calibration(mb):
-    """A plain device copy of known size, so counter runs can scale FETCH_SIZE /
-    WRITE_SIZE to bytes."""
+    """A plain elementwise kernel of known traffic (reads mb MiB, writes mb MiB;
+    torch's negation kernel, a name no other kernel in the run carries), so
+    counter runs can scale FETCH_SIZE / WRITE_SIZE to bytes."""
     import torch
     n = (mb << 20) // 4
     a = torch.ones(n, dtype=torch.float32, device="cuda")
     b = torch.empty_like(a)
     torch.cuda.synchronize()
-    b.copy_(a)
+    torch.neg(a, out=b)
     torch.cuda.synchronize()
     log(f"[bench] copy calibration: {mb} MiB read + {mb} MiB written")
 
@@ -338,7 +413,7 @@ def main():
 
     workloads = {}
     for idx, r in results.items():
-        w = dict(r)
+        w = {k: v for k, v in r.items() if k != "cfg"}
         w["roofline"] = roofline_of(r)
         workloads[r["workload"]] = w
     line = {

@@ -144,6 +144,31 @@ hyena_status hyena_forward(hyena_plan_t plan, const void* u, const void* const* 
 hyena_status hyena_spectrum_export(hyena_plan_t plan, const void* H, void* natural,
                                    void* stream);
 
+/*
+ * Launch timing, a profiling aid that computes nothing.  After
+ * hyena_timing_begin(max_launches), every kernel that a hyena_* call made on
+ * this host thread enqueues is bracketed by two HIP timing events recorded on
+ * that call's stream, for the first max_launches launches (later launches run
+ * unrecorded and are counted as dropped).  The events are created by begin on
+ * the device current at that time; use the same device until the end.
+ *
+ * hyena_timing_end(&n_kernels, &dropped) stops recording, waits for the
+ * recorded events and groups the launch durations by kernel;
+ * hyena_timing_kernel(i, ...) reads group i (0 <= i < n_kernels): the kernel's
+ * name as the runtime's kernel trace prints it, without the leading return
+ * type and argument list (for example "hy::hyena_lds1d_forward<16384,
+ * unsigned short, unsigned short, 2>"), its launches, and the total, shortest
+ * and longest durations in milliseconds.  The name stays valid until the next
+ * begin or release.  hyena_timing_release() frees the events.  State is
+ * thread-local; the recorded events add one marker to the stream before and
+ * after each launch.
+ */
+hyena_status hyena_timing_begin(int32_t max_launches);
+hyena_status hyena_timing_end(int32_t* n_kernels, int64_t* dropped);
+hyena_status hyena_timing_kernel(int32_t i, const char** name, int64_t* launches,
+                                 double* total_ms, double* min_ms, double* max_ms);
+hyena_status hyena_timing_release(void);
+
 /* Release a plan (NULL is accepted). */
 hyena_status hyena_plan_destroy(hyena_plan_t plan);
 

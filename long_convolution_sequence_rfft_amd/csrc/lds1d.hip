@@ -48,8 +48,8 @@ hyena_status launch_tw_init(const Plan& p, void* ws, void* stream)
     a.total = p.tw_elems;
     const int bs = 256;
     const int64_t nb = (p.tw_elems + bs - 1) / bs;
-    hipLaunchKernelGGL(hyena_tw_init, dim3((unsigned)nb), dim3(bs), 0, (hipStream_t)stream,
-                       (float2*)ws, a);
+    HY_LAUNCH(kernel_label("hyena_tw_init"), hyena_tw_init, dim3((unsigned)nb), dim3(bs), 0,
+              (hipStream_t)stream, (float2*)ws, a);
     const hipError_t e = hipGetLastError();
     return e == hipSuccess ? HYENA_OK : fail(HYENA_ERR_DEVICE, hipGetErrorString(e));
 }
@@ -97,12 +97,12 @@ hyena_status launch_lds1d_export(const Plan& p, const void* H, void* out, void* 
     const int64_t nb = (total + bs - 1) / bs;
     const int64_t T = p.M / lds1d_pts((int)p.M);
     if (p.spec_dtype == HYENA_F32)
-        hipLaunchKernelGGL(hyena_lds1d_export<float>, dim3((unsigned)nb), dim3(bs), 0,
-                           (hipStream_t)stream, (const float*)H, (float2*)out, p.npairs, p.d,
+        HY_LAUNCH(kernel_label("hyena_lds1d_export", "float"), hyena_lds1d_export<float>,
+                  dim3((unsigned)nb), dim3(bs), 0, (hipStream_t)stream, (const float*)H, (float2*)out, p.npairs, p.d,
                            p.M, T, total);
     else
-        hipLaunchKernelGGL(hyena_lds1d_export<uint16_t>, dim3((unsigned)nb), dim3(bs), 0,
-                           (hipStream_t)stream, (const uint16_t*)H, (float2*)out, p.npairs,
+        HY_LAUNCH(kernel_label("hyena_lds1d_export", "unsigned short"), hyena_lds1d_export<uint16_t>,
+                  dim3((unsigned)nb), dim3(bs), 0, (hipStream_t)stream, (const uint16_t*)H, (float2*)out, p.npairs,
                            p.d, p.M, T, total);
     const hipError_t e = hipGetLastError();
     return e == hipSuccess ? HYENA_OK : fail(HYENA_ERR_DEVICE, hipGetErrorString(e));
@@ -206,8 +206,12 @@ hyena_status stage_launch(const StageArgs& a, int ntensors, bool to_pm, hipStrea
     constexpr int TP = 128 / (int)sizeof(typename PairRaw<IO>::type);
     const dim3 grid((unsigned)((a.npairs + TP - 1) / TP), (unsigned)((a.N + 63) / 64),
                     (unsigned)(a.B * ntensors));
-    if (to_pm) hipLaunchKernelGGL((hyena_stage_pairs<IO, true>), grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((hyena_stage_pairs<IO, false>), grid, dim3(256), 0, s, a);
+    if (to_pm)
+        HY_LAUNCH(kernel_label("hyena_stage_pairs", type_label<IO>(), true),
+                  (hyena_stage_pairs<IO, true>), grid, dim3(256), 0, s, a);
+    else
+        HY_LAUNCH(kernel_label("hyena_stage_pairs", type_label<IO>(), false),
+                  (hyena_stage_pairs<IO, false>), grid, dim3(256), 0, s, a);
     const hipError_t e = hipGetLastError();
     return e == hipSuccess ? HYENA_OK : fail(HYENA_ERR_DEVICE, hipGetErrorString(e));
 }

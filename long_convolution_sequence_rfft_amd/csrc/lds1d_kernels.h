@@ -285,15 +285,18 @@ template <int M, typename IO, typename SP>
 hyena_status lds1d_forward_launch(const Lds1dFwdArgs& a, int mode, hipStream_t s)
 {
     const dim3 grid((unsigned)a.nblocks);
+    const auto label = [&] {
+        return kernel_label("hyena_lds1d_forward", M, type_label<IO>(), type_label<SP>(), mode);
+    };
     if (mode == IO_TILED)
-        hipLaunchKernelGGL((hyena_lds1d_forward<M, IO, SP, IO_TILED>), grid,
-                           dim3(Lds1dBlock<M, IO_TILED>::THREADS), 0, s, a);
+        HY_LAUNCH(label(), (hyena_lds1d_forward<M, IO, SP, IO_TILED>), grid,
+                  dim3(Lds1dBlock<M, IO_TILED>::THREADS), 0, s, a);
     else if (mode == IO_PAIRMAJOR)
-        hipLaunchKernelGGL((hyena_lds1d_forward<M, IO, SP, IO_PAIRMAJOR>), grid,
-                           dim3(Lds1dBlock<M, IO_PAIRMAJOR>::THREADS), 0, s, a);
+        HY_LAUNCH(label(), (hyena_lds1d_forward<M, IO, SP, IO_PAIRMAJOR>), grid,
+                  dim3(Lds1dBlock<M, IO_PAIRMAJOR>::THREADS), 0, s, a);
     else
-        hipLaunchKernelGGL((hyena_lds1d_forward<M, IO, SP, IO_DIRECT>), grid,
-                           dim3(Lds1dBlock<M, IO_DIRECT>::THREADS), 0, s, a);
+        HY_LAUNCH(label(), (hyena_lds1d_forward<M, IO, SP, IO_DIRECT>), grid,
+                  dim3(Lds1dBlock<M, IO_DIRECT>::THREADS), 0, s, a);
     const hipError_t e = hipGetLastError();
     return e == hipSuccess ? HYENA_OK : fail(HYENA_ERR_DEVICE, hipGetErrorString(e));
 }
@@ -301,8 +304,9 @@ hyena_status lds1d_forward_launch(const Lds1dFwdArgs& a, int mode, hipStream_t s
 template <int M, typename IO, typename SP>
 hyena_status lds1d_spectrum_launch(const Lds1dSpecArgs& a, hipStream_t s)
 {
-    hipLaunchKernelGGL((hyena_lds1d_spectrum<M, IO, SP>), dim3((unsigned)a.nblocks),
-                       dim3(FftShape<M>::T), 0, s, a);
+    HY_LAUNCH(kernel_label("hyena_lds1d_spectrum", M, type_label<IO>(), type_label<SP>()),
+              (hyena_lds1d_spectrum<M, IO, SP>), dim3((unsigned)a.nblocks), dim3(FftShape<M>::T), 0, s,
+              a);
     const hipError_t e = hipGetLastError();
     return e == hipSuccess ? HYENA_OK : fail(HYENA_ERR_DEVICE, hipGetErrorString(e));
 }

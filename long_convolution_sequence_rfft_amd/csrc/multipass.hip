@@ -272,12 +272,12 @@ hyena_status mp_export(const Plan& p, const void* H, void* out, void* stream)
     const int bs = 256;
     const int64_t nb = (total + bs - 1) / bs;
     if (p.spec_dtype == HYENA_F32)
-        hipLaunchKernelGGL(hyena_mp_export<float>, dim3((unsigned)nb), dim3(bs), 0,
-                           (hipStream_t)stream, (const float*)H, (float2*)out, p.npairs, p.d,
+        HY_LAUNCH(kernel_label("hyena_mp_export", "float"), hyena_mp_export<float>, dim3((unsigned)nb),
+                  dim3(bs), 0, (hipStream_t)stream, (const float*)H, (float2*)out, p.npairs, p.d,
                            g.La, g.Lb, g.four_step, total);
     else
-        hipLaunchKernelGGL(hyena_mp_export<uint16_t>, dim3((unsigned)nb), dim3(bs), 0,
-                           (hipStream_t)stream, (const uint16_t*)H, (float2*)out, p.npairs, p.d,
+        HY_LAUNCH(kernel_label("hyena_mp_export", "unsigned short"), hyena_mp_export<uint16_t>,
+                  dim3((unsigned)nb), dim3(bs), 0, (hipStream_t)stream, (const uint16_t*)H, (float2*)out, p.npairs, p.d,
                            g.La, g.Lb, g.four_step, total);
     const hipError_t e = hipGetLastError();
     return e == hipSuccess ? HYENA_OK : fail(HYENA_ERR_DEVICE, hipGetErrorString(e));

@@ -445,8 +445,9 @@ namespace hy {
 template <int LA, typename IO, int MODE, bool HALF_SPEC>
 hyena_status mp_outer_launch(const OuterArgs& a, int64_t nblocks, hipStream_t s)
 {
-    hipLaunchKernelGGL((hyena_mp_outer<LA, IO, MODE, HALF_SPEC>), dim3((unsigned)nblocks), dim3(kMpThreads),
-                       0, s, a);
+    HY_LAUNCH(kernel_label("hyena_mp_outer", LA, type_label<IO>(), MODE, HALF_SPEC),
+              (hyena_mp_outer<LA, IO, MODE, HALF_SPEC>), dim3((unsigned)nblocks), dim3(kMpThreads),
+              0, s, a);
     const hipError_t e = hipGetLastError();
     return e == hipSuccess ? HYENA_OK : fail(HYENA_ERR_DEVICE, hipGetErrorString(e));
 }
@@ -454,8 +455,9 @@ hyena_status mp_outer_launch(const OuterArgs& a, int64_t nblocks, hipStream_t s)
 template <int LB, typename SP, int MODE, bool HALF_B>
 hyena_status mp_inner_launch(const InnerArgs& a, int64_t nblocks, hipStream_t s)
 {
-    hipLaunchKernelGGL((hyena_mp_inner<LB, SP, MODE, HALF_B>), dim3((unsigned)nblocks), dim3(kMpThreads), 0,
-                       s, a);
+    HY_LAUNCH(kernel_label("hyena_mp_inner", LB, type_label<SP>(), MODE, HALF_B),
+              (hyena_mp_inner<LB, SP, MODE, HALF_B>), dim3((unsigned)nblocks), dim3(kMpThreads), 0,
+              s, a);
     const hipError_t e = hipGetLastError();
     return e == hipSuccess ? HYENA_OK : fail(HYENA_ERR_DEVICE, hipGetErrorString(e));
 }

@@ -16,6 +16,7 @@
 
 #include "fft_device.h"
 #include "plan.h"
+#include "timing.h"
 
 namespace hy {
 

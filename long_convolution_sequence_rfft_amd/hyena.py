@@ -33,7 +33,8 @@ HYENA_PATH_ROWCOL2D = 3
 EXPORTED_SYMBOLS = (
     "hyena_plan_create", "hyena_plan_query", "hyena_workspace_init", "hyena_filter_spectrum",
     "hyena_forward", "hyena_spectrum_export", "hyena_plan_destroy", "hyena_status_string",
-    "hyena_last_error",
+    "hyena_last_error", "hyena_timing_begin", "hyena_timing_end", "hyena_timing_kernel",
+    "hyena_timing_release",
 )
 
 _lock = threading.Lock()
@@ -70,9 +71,16 @@ def load():
             lib.hyena_status_string.restype = ctypes.c_char_p
             lib.hyena_last_error.argtypes = []
             lib.hyena_last_error.restype = ctypes.c_char_p
+            lib.hyena_timing_begin.argtypes = [i32]
+            lib.hyena_timing_end.argtypes = [ctypes.POINTER(i32), ctypes.POINTER(i64)]
+            lib.hyena_timing_kernel.argtypes = [i32, ctypes.POINTER(ctypes.c_char_p),
+                                                ctypes.POINTER(i64)] + \
+                [ctypes.POINTER(ctypes.c_double)] * 3
+            lib.hyena_timing_release.argtypes = []
             for name in ("hyena_plan_create", "hyena_plan_query", "hyena_workspace_init",
                          "hyena_filter_spectrum", "hyena_forward", "hyena_spectrum_export",
-                         "hyena_plan_destroy"):
+                         "hyena_plan_destroy", "hyena_timing_begin", "hyena_timing_end",
+                         "hyena_timing_kernel", "hyena_timing_release"):
                 getattr(lib, name).restype = ctypes.c_int
             _lib = lib
     return _lib
@@ -142,6 +150,34 @@ def hyena_spectrum_export(plan, H, natural, stream=0):
 
 def hyena_plan_destroy(plan):
     return load().hyena_plan_destroy(plan)
+
+
+def hyena_timing_begin(max_launches):
+    _check(load().hyena_timing_begin(int(max_launches)), "hyena_timing_begin")
+
+
+def hyena_timing_end():
+    """Stop recording; returns ({kernel name: {launches, total_ms, min_ms,
+    max_ms}}, dropped launches)."""
+    lib = load()
+    n = ctypes.c_int32()
+    dropped = ctypes.c_int64()
+    _check(lib.hyena_timing_end(ctypes.byref(n), ctypes.byref(dropped)), "hyena_timing_end")
+    out = {}
+    for i in range(n.value):
+        name = ctypes.c_char_p()
+        launches = ctypes.c_int64()
+        tot, mn, mx = ctypes.c_double(), ctypes.c_double(), ctypes.c_double()
+        _check(lib.hyena_timing_kernel(i, ctypes.byref(name), ctypes.byref(launches),
+                                       ctypes.byref(tot), ctypes.byref(mn), ctypes.byref(mx)),
+               "hyena_timing_kernel")
+        out[name.value.decode()] = {"launches": launches.value, "total_ms": tot.value,
+                                    "min_ms": mn.value, "max_ms": mx.value}
+    return out, dropped.value
+
+
+def hyena_timing_release():
+    _check(load().hyena_timing_release(), "hyena_timing_release")
 
 
 # --------------------------------------------------------------------------

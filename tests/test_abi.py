@@ -173,3 +173,15 @@ def test_plans_can_be_created_from_many_threads():
     for t in ts:
         t.join()
     assert not errs
+
+
+def test_timing_argument_errors():
+    lib = hyena.load()
+    assert lib.hyena_timing_begin(0) == hyena.HYENA_ERR_INVALID_ARGUMENT
+    assert lib.hyena_timing_begin((1 << 20) + 1) == hyena.HYENA_ERR_INVALID_ARGUMENT
+    # nothing recorded: end reports no kernels, reading one is out of range
+    recs, dropped = hyena.hyena_timing_end()
+    assert recs == {} and dropped == 0
+    assert lib.hyena_timing_kernel(0, None, None, None, None, None) == hyena.HYENA_ERR_INVALID_ARGUMENT
+    assert "out of range" in hyena.hyena_last_error()
+    hyena.hyena_timing_release()

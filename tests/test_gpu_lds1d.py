@@ -137,3 +137,35 @@ def test_full_size_config_all_channels(cfg):
     e = rel_err(y, ref)
     say(f"config {cfg} all-channel rel_err={e:.3e}")
     assert e < (TOL_F32 if inp.dtype == synth.F32 else TOL_BF16)
+
+
+def test_launch_timing_records_every_kernel():
+    # per-launch timing: each forward on the pair-major LDS path is three
+    # launches (stage in, transform chain, stage out), all recorded by name
+    import torch
+    from long_convolution_sequence_rfft_amd import hyena
+    inp = synth.make_1d(B=2, N=2048, d=8, order=2, seed=8)
+    plan = hyena.Plan(2, 8, 2, (2048,))
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    H = plan.spectrum(dev(inp.h))
+    u, gates, D = dev(inp.u), [dev(g) for g in inp.gates], dev(inp.D)
+    y = torch.empty_like(u)
+    torch.cuda.synchronize()
+    say("[gpu] timing: 3 forwards with per-launch events")
+    hyena.hyena_timing_begin(16)
+    for _ in range(3):
+        plan.forward(u, gates, H, D, y)
+    recs, dropped = hyena.hyena_timing_end()
+    hyena.hyena_timing_release()
+    assert dropped == 0
+    assert sorted(recs) == ["hy::hyena_lds1d_forward<4096, float, float, 2>",
+                            "hy::hyena_stage_pairs<float, false>",
+                            "hy::hyena_stage_pairs<float, true>"]
+    for r in recs.values():
+        assert r["launches"] == 3
+        assert 0.0 < r["min_ms"] <= r["max_ms"] and r["total_ms"] >= 3 * r["min_ms"] * 0.999
+    # the timed launches computed the same result as an untimed forward
+    y_ref = torch.empty_like(u)
+    plan.forward(u, gates, H, D, y_ref)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y_ref)
