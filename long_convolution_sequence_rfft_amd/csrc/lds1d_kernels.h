@@ -82,9 +82,13 @@ hyena_lds1d_forward(Lds1dFwdArgs a)
     const int k = threadIdx.x / T;  // pair within the workgroup
     const int tau = threadIdx.x - k * T;
     const int64_t lin = xcd_remap(blockIdx.x, a.nblocks);
+    // batch row fastest: the B workgroups of one channel group run back to
+    // back on one XCD, so the group's spectrum is fetched from HBM once and
+    // then found in that XCD's L2
     const int64_t groups_per_b = (a.npairs + K - 1) / K;
-    const int64_t b = lin / groups_per_b;
-    const int64_t pg = lin - b * groups_per_b;
+    const int64_t nb = a.nblocks / groups_per_b;
+    const int64_t pg = lin / nb;
+    const int64_t b = lin - pg * nb;
     const int64_t p = pg * K + k;
     const bool live = p < a.npairs;
     const int64_t pc = live ? p : a.npairs - 1;  // clamped for address arithmetic

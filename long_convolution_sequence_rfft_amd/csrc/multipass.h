@@ -45,7 +45,9 @@ namespace hy {
 // Forward transform from registers (R0-pass inputs; HALF_IN: only r < R0/2
 // hold data, the rest is zero padding) to natural-order bins in the region.
 // The caller provides the WAR barrier before the first write when needed.
-template <int L, bool HALF_IN>
+// TO_REGS: stop after the last pass's arithmetic; v[q RL + s] then holds bin
+// (tau + q T) + s L/RL (lanes of one transform hold consecutive bins).
+template <int L, bool HALF_IN, bool TO_REGS = false>
 __device__ __forceinline__ void fwd_regs_to_lds(float2* v, float* sre, float* sim, const float2* tw,
                                                 TwOffsets o, int tau)
 {
@@ -82,6 +84,7 @@ __device__ __forceinline__ void fwd_regs_to_lds(float2* v, float* sre, float* si
         apply_tw<RL, -1>(&v[q * RL], wl[q]);
         dft<RL, -1>(&v[q * RL]);
     }
+    if constexpr (TO_REGS) return;
     __syncthreads();
     // last pass: NS = L/RL, so output s of butterfly j lands at j + s L/RL
 #pragma unroll
@@ -91,7 +94,9 @@ __device__ __forceinline__ void fwd_regs_to_lds(float2* v, float* sre, float* si
 // Inverse (unscaled) transform from natural-order bins in the region to the
 // R0-pass register layout.  HALF_OUT: only samples < L/2 are produced
 // (v[q R0 + s], s < R0/2).  The caller provides the RAW barrier before.
-template <int L, bool HALF_OUT>
+// FROM_REGS: the bins are already in registers, v[q RL + r] = bin
+// (tau + q T) + r L/RL (the layout fwd_regs_to_lds<..., true> leaves).
+template <int L, bool HALF_OUT, bool FROM_REGS = false>
 __device__ __forceinline__ void inv_lds_to_regs(float2* v, float* sre, float* sim, const float2* tw,
                                                 TwOffsets o, int tau)
 {
@@ -100,7 +105,7 @@ __device__ __forceinline__ void inv_lds_to_regs(float2* v, float* sre, float* si
     constexpr int QL = S::PTS / RL;
 #pragma unroll
     for (int q = 0; q < QL; ++q) {
-        lds_read<RL, L>(sre, sim, &v[q * RL], tau + q * T);
+        if constexpr (!FROM_REGS) lds_read<RL, L>(sre, sim, &v[q * RL], tau + q * T);
         dft<RL, +1>(&v[q * RL]);
     }
     __syncthreads();

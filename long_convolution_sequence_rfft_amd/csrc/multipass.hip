@@ -100,6 +100,9 @@ hyena_status outer(const Plan& p, int mode, bool half_spec, const OuterArgs& a, 
 hyena_status inner(const Plan& p, int mode, const InnerArgs& a, int64_t nb, hipStream_t s)
 {
     const bool half_b = !a.g.four_step;
+    // the inner kernels size their tile loops from (LB, HALF_B)
+    if (mode == INNER_CHAIN && a.g.Lb_live != (half_b ? a.g.Lb / 2 : a.g.Lb))
+        return fail(HYENA_ERR_UNSUPPORTED, "multi-pass: live inner rows do not match the kernel");
     return p.spec_dtype == HYENA_F32 ? inner_go<float>(a.g.Lb, mode, half_b, a, nb, s)
                                      : inner_go<uint16_t>(a.g.Lb, mode, half_b, a, nb, s);
 }

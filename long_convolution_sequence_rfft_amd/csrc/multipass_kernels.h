@@ -70,6 +70,61 @@ __device__ __forceinline__ void act_store(IO* base, int64_t row, int64_t c0, int
     }
 }
 
+// One outer column of F in the last-pass register layout of a length-L
+// transform: v[q RL + r] <-> bin (tau + q T) + r L/RL.  With `tw`, bins are
+// multiplied by the four-step twiddle twstep[bin] (conjugated for DIR = +1,
+// the inverse direction).  All loads are issued before any is used.
+template <int L, int DIR>
+__device__ __forceinline__ void load_column(float2* v, const float2* Fcol, const float2* twstep,
+                                            int tau, bool live, bool tw)
+{
+    using S = FftShape<L>;
+    constexpr int T = S::T, RL = S::RL, QL = S::PTS / RL;
+    if (!live) {
+#pragma unroll
+        for (int i = 0; i < S::PTS; ++i) v[i] = make_float2(0.0f, 0.0f);
+        return;
+    }
+#pragma unroll
+    for (int q = 0; q < QL; ++q)
+#pragma unroll
+        for (int r = 0; r < RL; ++r) v[q * RL + r] = Fcol[tau + q * T + r * (L / RL)];
+    if (tw) {
+        float2 w[S::PTS];
+#pragma unroll
+        for (int q = 0; q < QL; ++q)
+#pragma unroll
+            for (int r = 0; r < RL; ++r) w[q * RL + r] = twstep[tau + q * T + r * (L / RL)];
+#pragma unroll
+        for (int i = 0; i < S::PTS; ++i) v[i] = ctw<DIR>(v[i], w[i]);
+    }
+}
+
+template <int L>
+__device__ __forceinline__ void store_column(const float2* v, float2* Fcol, const float2* twstep,
+                                             int tau, bool tw)
+{
+    using S = FftShape<L>;
+    constexpr int T = S::T, RL = S::RL, QL = S::PTS / RL;
+    if (tw) {
+        float2 w[S::PTS];
+#pragma unroll
+        for (int q = 0; q < QL; ++q)
+#pragma unroll
+            for (int r = 0; r < RL; ++r) w[q * RL + r] = twstep[tau + q * T + r * (L / RL)];
+#pragma unroll
+        for (int q = 0; q < QL; ++q)
+#pragma unroll
+            for (int r = 0; r < RL; ++r)
+                Fcol[tau + q * T + r * (L / RL)] = ctw<-1>(v[q * RL + r], w[q * RL + r]);
+    } else {
+#pragma unroll
+        for (int q = 0; q < QL; ++q)
+#pragma unroll
+            for (int r = 0; r < RL; ++r) Fcol[tau + q * T + r * (L / RL)] = v[q * RL + r];
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Outer pass.  Workgroup = KP pair slots x C outer columns (C KP = NF).
 // blockIdx.x = column block * ngroups + group-in-chunk.
@@ -127,13 +182,20 @@ __global__ void __launch_bounds__(kMpThreads, 2) hyena_mp_outer(OuterArgs a)
         }
     };
 
+    // tile elements per thread in tile_rows
+    constexpr int GT = (LA / 2) * NF / kMpThreads;
     float2 v[S::PTS];
     if constexpr (MODE == OUTER_IN) {
+        // all tile loads are issued before the first LDS store, so their
+        // latencies overlap instead of adding up
         const IO* u = static_cast<const IO*>(a.act);
-        tile_rows([&](int, int fq, int s, int64_t pq, bool ok, int64_t row) {
-            const float2 x = ok ? act_load<IO>(u, row, 2 * pq, g.d) : make_float2(0.0f, 0.0f);
-            sre[fq * LW + lpad(s)] = x.x;
-            sim[fq * LW + lpad(s)] = x.y;
+        float2 xin[GT];
+        tile_rows([&](int it, int, int, int64_t pq, bool ok, int64_t row) {
+            xin[it] = ok ? act_load<IO>(u, row, 2 * pq, g.d) : make_float2(0.0f, 0.0f);
+        });
+        tile_rows([&](int it, int fq, int s, int64_t, bool, int64_t) {
+            sre[fq * LW + lpad(s)] = xin[it].x;
+            sim[fq * LW + lpad(s)] = xin[it].y;
         });
         __syncthreads();
         lds_to_regs<LA, true>(v, re, im, tau);
@@ -171,27 +233,18 @@ __global__ void __launch_bounds__(kMpThreads, 2) hyena_mp_outer(OuterArgs a)
                 v[q * R0 + r] = x;
             }
     } else {
-        // MID / OUT.  The gate tile is fetched into registers first, so its
-        // latency overlaps the F column load and the inverse outer DFT.
-        constexpr int GT = (LA / 2) * NF / kMpThreads;  // tile elements per thread
+        // MID / OUT.  F column -> (conj twiddle) -> registers in the layout
+        // of the inverse's first pass (lanes of a transform read consecutive
+        // bins).  The gate tile is fetched next, so its latency overlaps the
+        // inverse outer DFT.
         static_assert(GT >= 1 && (LA / 2) * NF % kMpThreads == 0, "gate tile");
+        load_column<LA, +1>(v, Fcol, twstep, tau, col_live, g.four_step && o > 0);
         const IO* gate = static_cast<const IO*>(a.act);
         float2 gval[GT];
         tile_rows([&](int it, int, int, int64_t pq, bool ok, int64_t row) {
             gval[it] = ok ? act_load<IO>(gate, row, 2 * pq, g.d) : make_float2(0.0f, 0.0f);
         });
-        // F column -> (conj twiddle) -> region, inverse outer DFT
-        for (int i = tau; i < LA; i += TA) {
-            float2 x = make_float2(0.0f, 0.0f);
-            if (col_live) {
-                x = Fcol[i];
-                if (g.four_step && o > 0) x = ctw<+1>(x, twstep[i]);
-            }
-            re[lpad(i)] = x.x;
-            im[lpad(i)] = x.y;
-        }
-        __syncthreads();
-        inv_lds_to_regs<LA, true>(v, re, im, a.tw, g.tw_a, tau);
+        inv_lds_to_regs<LA, true, true>(v, re, im, a.tw, g.tw_a, tau);
         __syncthreads();
         tile_rows([&](int it, int fq, int s, int64_t, bool, int64_t) {
             sre[fq * LW + lpad(s)] = gval[it].x;
@@ -219,15 +272,10 @@ __global__ void __launch_bounds__(kMpThreads, 2) hyena_mp_outer(OuterArgs a)
         }
     }
 
-    // forward outer DFT -> natural-order bins -> (twiddle) -> F column
-    fwd_regs_to_lds<LA, HALF_IN>(v, re, im, a.tw, g.tw_a, tau);
-    __syncthreads();
-    if (!col_live) return;
-    for (int i = tau; i < LA; i += TA) {
-        float2 x = make_float2(re[lpad(i)], im[lpad(i)]);
-        if (g.four_step && o > 0) x = ctw<-1>(x, twstep[i]);
-        Fcol[i] = x;
-    }
+    // forward outer DFT -> (twiddle) -> F column, straight from the last
+    // pass's registers (lanes of a transform hold consecutive bins)
+    fwd_regs_to_lds<LA, HALF_IN, true>(v, re, im, a.tw, g.tw_a, tau);
+    if (col_live) store_column<LA>(v, Fcol, twstep, tau, g.four_step && o > 0);
 }
 
 // ---------------------------------------------------------------------------
@@ -351,16 +399,43 @@ __global__ void __launch_bounds__(kMpThreads, 2) hyena_mp_inner(InnerArgs a)
         }
     }
 
-    // F[o][column] -> region of (u, side) at inner position o
-    const int total = nlive * nu * 2;
-    for (int idx = threadIdx.x; idx < total; idx += kMpThreads) {
-        const int u = idx % nu;
-        const int side = (idx / nu) & 1;
-        const int op = idx / (2 * nu);
-        const float2 x = Fp[(int64_t)op * La + col_of(u, side)];
-        const int fq = 2 * u + side;
-        sre[fq * LW + lpad(op)] = x.x;
-        sim[fq * LW + lpad(op)] = x.y;
+    // F[o][column] -> region of (u, side) at inner position o.  With all U
+    // units present (the usual case) the per-thread element count is a
+    // compile-time constant and every load is issued before the first use.
+    constexpr int NLIVE = MODE == INNER_SPEC ? LB : (HALF_B ? LB / 2 : LB);
+    constexpr int PER = NLIVE * 2 * U / kMpThreads;
+    static_assert(NLIVE * 2 * U % kMpThreads == 0, "inner tile split");
+    if (nu == U) {
+        float2 xin[PER];
+#pragma unroll
+        for (int it = 0; it < PER; ++it) {
+            const int idx = (int)threadIdx.x + it * kMpThreads;
+            const int u = idx % U;
+            const int side = (idx / U) & 1;
+            const int op = idx / (2 * U);
+            xin[it] = Fp[(int64_t)op * La + col_of(u, side)];
+        }
+#pragma unroll
+        for (int it = 0; it < PER; ++it) {
+            const int idx = (int)threadIdx.x + it * kMpThreads;
+            const int u = idx % U;
+            const int side = (idx / U) & 1;
+            const int op = idx / (2 * U);
+            const int fq = 2 * u + side;
+            sre[fq * LW + lpad(op)] = xin[it].x;
+            sim[fq * LW + lpad(op)] = xin[it].y;
+        }
+    } else {
+        const int total = nlive * nu * 2;
+        for (int idx = threadIdx.x; idx < total; idx += kMpThreads) {
+            const int u = idx % nu;
+            const int side = (idx / nu) & 1;
+            const int op = idx / (2 * nu);
+            const float2 x = Fp[(int64_t)op * La + col_of(u, side)];
+            const int fq = 2 * u + side;
+            sre[fq * LW + lpad(op)] = x.x;
+            sim[fq * LW + lpad(op)] = x.y;
+        }
     }
     __syncthreads();
     constexpr bool HALF_LOAD = (MODE == INNER_CHAIN) && HALF_B;
@@ -427,14 +502,35 @@ __global__ void __launch_bounds__(kMpThreads, 2) hyena_mp_inner(InnerArgs a)
     __syncthreads();
     regs_to_lds<LB, HALF_B>(v, re, im, tau);
     __syncthreads();
-    const int total_out = g.Lb_live * nu * 2;
-    for (int idx = threadIdx.x; idx < total_out; idx += kMpThreads) {
-        const int u = idx % nu;
-        const int side = (idx / nu) & 1;
-        const int op = idx / (2 * nu);
-        const int fq = 2 * u + side;
-        Fp[(int64_t)op * La + col_of(u, side)] =
-            make_float2(sre[fq * LW + lpad(op)], sim[fq * LW + lpad(op)]);
+    if (nu == U) {
+        float2 xout[PER];
+#pragma unroll
+        for (int it = 0; it < PER; ++it) {
+            const int idx = (int)threadIdx.x + it * kMpThreads;
+            const int u = idx % U;
+            const int side = (idx / U) & 1;
+            const int op = idx / (2 * U);
+            const int fq = 2 * u + side;
+            xout[it] = make_float2(sre[fq * LW + lpad(op)], sim[fq * LW + lpad(op)]);
+        }
+#pragma unroll
+        for (int it = 0; it < PER; ++it) {
+            const int idx = (int)threadIdx.x + it * kMpThreads;
+            const int u = idx % U;
+            const int side = (idx / U) & 1;
+            const int op = idx / (2 * U);
+            Fp[(int64_t)op * La + col_of(u, side)] = xout[it];
+        }
+    } else {
+        const int total_out = g.Lb_live * nu * 2;
+        for (int idx = threadIdx.x; idx < total_out; idx += kMpThreads) {
+            const int u = idx % nu;
+            const int side = (idx / nu) & 1;
+            const int op = idx / (2 * nu);
+            const int fq = 2 * u + side;
+            Fp[(int64_t)op * La + col_of(u, side)] =
+                make_float2(sre[fq * LW + lpad(op)], sim[fq * LW + lpad(op)]);
+        }
     }
 }
 
