@@ -160,12 +160,21 @@ struct StageArgs {
     int64_t B, N, d, npairs;
 };
 
+// Tile: kStageTT samples x one 128-byte line of pairs.  Each thread first
+// issues all of its loads, then writes LDS; after the barrier it reads all of
+// its LDS values, then stores, so the memory latencies of one thread overlap.
+constexpr int kStageTT = 128;
+
 template <typename IO, bool TO_PAIRMAJOR>
 __global__ void __launch_bounds__(256) hyena_stage_pairs(StageArgs a)
 {
     using Raw = typename PairRaw<IO>::type;
     constexpr int TP = 128 / (int)sizeof(Raw);  // pairs per 128-byte line
-    constexpr int TT = 64;                      // samples per tile
+    constexpr int TT = kStageTT;                // samples per tile
+    constexpr int PER = TT * TP / 256;          // elements per thread
+    static_assert(TT * TP % 256 == 0, "stage tile split");
+    // row stride TP + 1 elements: both the row-wise and the column-wise
+    // passes over the tile hit distinct banks
     __shared__ Raw tile[TT][TP + 1];
     const int64_t p0 = (int64_t)blockIdx.x * TP;
     const int64_t t0 = (int64_t)blockIdx.y * TT;
@@ -175,28 +184,58 @@ __global__ void __launch_bounds__(256) hyena_stage_pairs(StageArgs a)
     Raw* dst = static_cast<Raw*>(a.dst[s]);
     const int64_t P = a.npairs;
     const int64_t rowpairs = a.d / 2;  // pair elements per channels-last row
-    for (int i = threadIdx.x; i < TT * TP; i += 256) {
-        if (TO_PAIRMAJOR) {
-            const int tr = i / TP, pc = i % TP;
-            const int64_t t = t0 + tr, p = p0 + pc;
-            if (t < a.N && p < P) tile[tr][pc] = src[(b * a.N + t) * rowpairs + p];
-        } else {
-            const int pc = i / TT, tr = i % TT;
-            const int64_t t = t0 + tr, p = p0 + pc;
-            if (t < a.N && p < P) tile[tr][pc] = src[(b * P + p) * a.N + t];
-        }
+    const bool full = t0 + TT <= a.N && p0 + TP <= P;
+    // (tr, pc) of element k of this thread: row-wise (pairs fastest) for the
+    // channels-last side, column-wise (samples fastest) for the pair-major side
+    auto rowwise = [&](int k, int& tr, int& pc) {
+        const int i = (int)threadIdx.x + k * 256;
+        tr = i / TP;
+        pc = i % TP;
+    };
+    auto colwise = [&](int k, int& tr, int& pc) {
+        const int i = (int)threadIdx.x + k * 256;
+        pc = i / TT;
+        tr = i % TT;
+    };
+    auto src_index = [&](int tr, int pc) {
+        return TO_PAIRMAJOR ? (b * a.N + t0 + tr) * rowpairs + p0 + pc
+                            : (b * P + p0 + pc) * a.N + t0 + tr;
+    };
+    auto dst_index = [&](int tr, int pc) {
+        return TO_PAIRMAJOR ? (b * P + p0 + pc) * a.N + t0 + tr
+                            : (b * a.N + t0 + tr) * rowpairs + p0 + pc;
+    };
+    auto in_range = [&](int tr, int pc) { return full || (t0 + tr < a.N && p0 + pc < P); };
+
+    Raw x[PER];
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+        int tr, pc;
+        if (TO_PAIRMAJOR) rowwise(k, tr, pc);
+        else colwise(k, tr, pc);
+        if (in_range(tr, pc)) x[k] = src[src_index(tr, pc)];
+    }
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+        int tr, pc;
+        if (TO_PAIRMAJOR) rowwise(k, tr, pc);
+        else colwise(k, tr, pc);
+        tile[tr][pc] = x[k];
     }
     __syncthreads();
-    for (int i = threadIdx.x; i < TT * TP; i += 256) {
-        if (TO_PAIRMAJOR) {
-            const int pc = i / TT, tr = i % TT;
-            const int64_t t = t0 + tr, p = p0 + pc;
-            if (t < a.N && p < P) dst[(b * P + p) * a.N + t] = tile[tr][pc];
-        } else {
-            const int tr = i / TP, pc = i % TP;
-            const int64_t t = t0 + tr, p = p0 + pc;
-            if (t < a.N && p < P) dst[(b * a.N + t) * rowpairs + p] = tile[tr][pc];
-        }
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+        int tr, pc;
+        if (TO_PAIRMAJOR) colwise(k, tr, pc);
+        else rowwise(k, tr, pc);
+        x[k] = tile[tr][pc];
+    }
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+        int tr, pc;
+        if (TO_PAIRMAJOR) colwise(k, tr, pc);
+        else rowwise(k, tr, pc);
+        if (in_range(tr, pc)) dst[dst_index(tr, pc)] = x[k];
     }
 }
 
@@ -204,7 +243,7 @@ template <typename IO>
 hyena_status stage_launch(const StageArgs& a, int ntensors, bool to_pm, hipStream_t s)
 {
     constexpr int TP = 128 / (int)sizeof(typename PairRaw<IO>::type);
-    const dim3 grid((unsigned)((a.npairs + TP - 1) / TP), (unsigned)((a.N + 63) / 64),
+    const dim3 grid((unsigned)((a.npairs + TP - 1) / TP), (unsigned)((a.N + kStageTT - 1) / kStageTT),
                     (unsigned)(a.B * ntensors));
     if (to_pm)
         HY_LAUNCH(kernel_label("hyena_stage_pairs", type_label<IO>(), true),
