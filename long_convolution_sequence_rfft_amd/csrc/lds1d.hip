@@ -5,10 +5,13 @@
 
 namespace hy {
 
-// instantiated in lds1d_f32.hip / lds1d_bf16.hip
+// instantiated in lds1d_f32.hip / lds1d_bf16.hip / lds1d_real_*.hip
 HY_LDS1D_SIZES(HY_LDS1D_EXTERN, float, float)
 HY_LDS1D_SIZES(HY_LDS1D_EXTERN, uint16_t, uint16_t)
 HY_LDS1D_SIZES(HY_LDS1D_EXTERN, uint16_t, float)
+HY_LDS1D_REAL_SIZES(HY_LDS1D_REAL_EXTERN, float, float)
+HY_LDS1D_REAL_SIZES(HY_LDS1D_REAL_EXTERN, uint16_t, uint16_t)
+HY_LDS1D_REAL_SIZES(HY_LDS1D_REAL_EXTERN, uint16_t, float)
 
 // ---------------------------------------------------------------------------
 // Twiddle tables: double-precision roots of unity rounded once to float.
@@ -90,8 +93,52 @@ __global__ void hyena_lds1d_export(const SP* spec, float2* out, int64_t npairs, 
     if (has_b) ob[k] = make_float2((P.x - Q.x) * sc, (P.y - Q.y) * sc);
 }
 
+// Single-channel layout: entry (S, Dl) of bin k gives H[k] = L (S + Dl) and
+// H[L-k] = L conj(S - Dl); entry (0, 0) gives H[0], H[L] and H[L/2].
+template <typename SP>
+__global__ void hyena_lds1d_real_export(const SP* spec, float2* out, int64_t L, int64_t T,
+                                        int64_t total)
+{
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= total) return;
+    const int64_t half = L / 2;  // entries per channel
+    const int64_t nc = i / half;  // n * d + c
+    const int64_t rem = i - nc * half;
+    const int64_t e = rem / T, tau = rem - e * T;
+    float2 S, Dl;
+    load_entry(spec, i, S, Dl);
+    const float sc = (float)L;
+    float2* o = out + nc * (L + 1);
+    if (tau == 0 && e == 0) {
+        o[0] = make_float2((S.x + Dl.x) * sc, 0.0f);
+        o[L] = make_float2((S.x - Dl.x) * sc, 0.0f);
+        o[L / 2] = make_float2(S.y * sc, Dl.y * sc);
+        return;
+    }
+    const int64_t k = real_entry_bin(L, T, tau, e);
+    o[k] = make_float2((S.x + Dl.x) * sc, (S.y + Dl.y) * sc);
+    o[L - k] = make_float2((S.x - Dl.x) * sc, -(S.y - Dl.y) * sc);
+}
+
 hyena_status launch_lds1d_export(const Plan& p, const void* H, void* out, void* stream)
 {
+    if (p.lds_io == IO_REAL) {
+        const int64_t L = p.M / 2;
+        const int64_t total = (int64_t)p.order * p.d * (L / 2);
+        const int bs = 256;
+        const int64_t nb = (total + bs - 1) / bs;
+        const int64_t T = L / lds1d_pts((int)L);
+        if (p.spec_dtype == HYENA_F32)
+            HY_LAUNCH(kernel_label("hyena_lds1d_real_export", "float"), hyena_lds1d_real_export<float>,
+                      dim3((unsigned)nb), dim3(bs), 0, (hipStream_t)stream, (const float*)H,
+                      (float2*)out, L, T, total);
+        else
+            HY_LAUNCH(kernel_label("hyena_lds1d_real_export", "unsigned short"),
+                      hyena_lds1d_real_export<uint16_t>, dim3((unsigned)nb), dim3(bs), 0,
+                      (hipStream_t)stream, (const uint16_t*)H, (float2*)out, L, T, total);
+        const hipError_t e = hipGetLastError();
+        return e == hipSuccess ? HYENA_OK : fail(HYENA_ERR_DEVICE, hipGetErrorString(e));
+    }
     const int64_t total = (int64_t)p.order * p.npairs * (p.M / 2);
     const int bs = 256;
     const int64_t nb = (total + bs - 1) / bs;
@@ -137,6 +184,30 @@ hyena_status spec_by_m(int64_t M, const Lds1dSpecArgs& a, hipStream_t s)
     }
 }
 
+template <typename IO, typename SP>
+hyena_status real_fwd_by_l(int64_t L, const Lds1dFwdArgs& a, hipStream_t s)
+{
+    switch (L) {
+#define HY_CASE(LL, I, S_) \
+    case LL: return lds1d_real_forward_launch<LL, IO, SP>(a, s);
+        HY_LDS1D_REAL_SIZES(HY_CASE, IO, SP)
+#undef HY_CASE
+        default: return fail(HYENA_ERR_UNSUPPORTED, "LDS1D: unsupported single-channel length");
+    }
+}
+
+template <typename IO, typename SP>
+hyena_status real_spec_by_l(int64_t L, const Lds1dSpecArgs& a, hipStream_t s)
+{
+    switch (L) {
+#define HY_CASE(LL, I, S_) \
+    case LL: return lds1d_real_spectrum_launch<LL, IO, SP>(a, s);
+        HY_LDS1D_REAL_SIZES(HY_CASE, IO, SP)
+#undef HY_CASE
+        default: return fail(HYENA_ERR_UNSUPPORTED, "LDS1D: unsupported single-channel length");
+    }
+}
+
 TwOffsets lds1d_offsets(const Plan& p)
 {
     TwOffsets o;
@@ -150,43 +221,42 @@ TwOffsets lds1d_offsets(const Plan& p)
 }  // namespace
 
 // ---------------------------------------------------------------------------
-// Pair-major staging: [B][N][d] channels last <-> [B][pairs][N] pair elements
-// (d even).  64 samples x one cache line of pairs per tile; both the row reads
-// and the run writes are contiguous.
+// Staging transposes between channels-last [B][N][d] and column-major
+// [B][cols][N] runs, for an element E that is either a channel pair
+// (PairRaw, cols = d/2: pair-major) or one channel (IO, cols = d:
+// channel-major).  Tile: kStageTT samples x one 128-byte line of elements.
+// Each thread first issues all of its loads, then writes LDS; after the
+// barrier it reads all of its LDS values, then stores, so the memory
+// latencies of one thread overlap.
 // ---------------------------------------------------------------------------
 struct StageArgs {
     const void* src[kMaxOrder + 1];
     void* dst[kMaxOrder + 1];
-    int64_t B, N, d, npairs;
+    int64_t B, N, cols;
 };
 
-// Tile: kStageTT samples x one 128-byte line of pairs.  Each thread first
-// issues all of its loads, then writes LDS; after the barrier it reads all of
-// its LDS values, then stores, so the memory latencies of one thread overlap.
 constexpr int kStageTT = 128;
 
-template <typename IO, bool TO_PAIRMAJOR>
-__global__ void __launch_bounds__(256) hyena_stage_pairs(StageArgs a)
+template <typename E, bool TO_COLS>
+__global__ void __launch_bounds__(256) hyena_stage(StageArgs a)
 {
-    using Raw = typename PairRaw<IO>::type;
-    constexpr int TP = 128 / (int)sizeof(Raw);  // pairs per 128-byte line
-    constexpr int TT = kStageTT;                // samples per tile
-    constexpr int PER = TT * TP / 256;          // elements per thread
+    constexpr int TP = 128 / (int)sizeof(E);  // elements per 128-byte line
+    constexpr int TT = kStageTT;              // samples per tile
+    constexpr int PER = TT * TP / 256;        // elements per thread
     static_assert(TT * TP % 256 == 0, "stage tile split");
     // row stride TP + 1 elements: both the row-wise and the column-wise
-    // passes over the tile hit distinct banks
-    __shared__ Raw tile[TT][TP + 1];
+    // passes over the tile spread over the banks
+    __shared__ E tile[TT][TP + 1];
     const int64_t p0 = (int64_t)blockIdx.x * TP;
     const int64_t t0 = (int64_t)blockIdx.y * TT;
     const int64_t b = blockIdx.z % a.B;
     const int s = blockIdx.z / a.B;
-    const Raw* src = static_cast<const Raw*>(a.src[s]);
-    Raw* dst = static_cast<Raw*>(a.dst[s]);
-    const int64_t P = a.npairs;
-    const int64_t rowpairs = a.d / 2;  // pair elements per channels-last row
+    const E* src = static_cast<const E*>(a.src[s]);
+    E* dst = static_cast<E*>(a.dst[s]);
+    const int64_t P = a.cols;
     const bool full = t0 + TT <= a.N && p0 + TP <= P;
-    // (tr, pc) of element k of this thread: row-wise (pairs fastest) for the
-    // channels-last side, column-wise (samples fastest) for the pair-major side
+    // (tr, pc) of element k of this thread: row-wise (columns fastest) on the
+    // channels-last side, column-wise (samples fastest) on the other
     auto rowwise = [&](int k, int& tr, int& pc) {
         const int i = (int)threadIdx.x + k * 256;
         tr = i / TP;
@@ -198,27 +268,25 @@ __global__ void __launch_bounds__(256) hyena_stage_pairs(StageArgs a)
         tr = i % TT;
     };
     auto src_index = [&](int tr, int pc) {
-        return TO_PAIRMAJOR ? (b * a.N + t0 + tr) * rowpairs + p0 + pc
-                            : (b * P + p0 + pc) * a.N + t0 + tr;
+        return TO_COLS ? (b * a.N + t0 + tr) * P + p0 + pc : (b * P + p0 + pc) * a.N + t0 + tr;
     };
     auto dst_index = [&](int tr, int pc) {
-        return TO_PAIRMAJOR ? (b * P + p0 + pc) * a.N + t0 + tr
-                            : (b * a.N + t0 + tr) * rowpairs + p0 + pc;
+        return TO_COLS ? (b * P + p0 + pc) * a.N + t0 + tr : (b * a.N + t0 + tr) * P + p0 + pc;
     };
     auto in_range = [&](int tr, int pc) { return full || (t0 + tr < a.N && p0 + pc < P); };
 
-    Raw x[PER];
+    E x[PER];
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
         int tr, pc;
-        if (TO_PAIRMAJOR) rowwise(k, tr, pc);
+        if (TO_COLS) rowwise(k, tr, pc);
         else colwise(k, tr, pc);
         if (in_range(tr, pc)) x[k] = src[src_index(tr, pc)];
     }
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
         int tr, pc;
-        if (TO_PAIRMAJOR) rowwise(k, tr, pc);
+        if (TO_COLS) rowwise(k, tr, pc);
         else colwise(k, tr, pc);
         tile[tr][pc] = x[k];
     }
@@ -226,33 +294,170 @@ __global__ void __launch_bounds__(256) hyena_stage_pairs(StageArgs a)
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
         int tr, pc;
-        if (TO_PAIRMAJOR) colwise(k, tr, pc);
+        if (TO_COLS) colwise(k, tr, pc);
         else rowwise(k, tr, pc);
         x[k] = tile[tr][pc];
     }
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
         int tr, pc;
-        if (TO_PAIRMAJOR) colwise(k, tr, pc);
+        if (TO_COLS) colwise(k, tr, pc);
         else rowwise(k, tr, pc);
         if (in_range(tr, pc)) dst[dst_index(tr, pc)] = x[k];
     }
 }
 
-template <typename IO>
-hyena_status stage_launch(const StageArgs& a, int ntensors, bool to_pm, hipStream_t s)
+// bfloat16 channel-major staging for even d, moving 4 bytes per access on
+// both sides: two neighbouring channels of a channels-last row, or two
+// neighbouring samples of a channel-major run.  Tile: kStageTT samples x 64
+// channels; word (t, w) of the tile holds channels 2w, 2w+1 of sample t.
+template <bool TO_COLS>
+__global__ void __launch_bounds__(256) hyena_stage_bf16(StageArgs a)
 {
-    constexpr int TP = 128 / (int)sizeof(typename PairRaw<IO>::type);
-    const dim3 grid((unsigned)((a.npairs + TP - 1) / TP), (unsigned)((a.N + kStageTT - 1) / kStageTT),
+    constexpr int TT = kStageTT, TC = 64, TW = TC / 2;
+    constexpr int RS = TW + 1;  // words per tile row (odd: spreads the banks)
+    constexpr int PER = TT * TW / 256;
+    __shared__ uint32_t tile[TT * RS];
+    uint16_t* tile16 = reinterpret_cast<uint16_t*>(tile);
+    const int64_t c0 = (int64_t)blockIdx.x * TC;
+    const int64_t t0 = (int64_t)blockIdx.y * TT;
+    const int64_t b = blockIdx.z % a.B;
+    const int s = blockIdx.z / a.B;
+    const uint32_t* src = static_cast<const uint32_t*>(a.src[s]);
+    uint32_t* dst = static_cast<uint32_t*>(a.dst[s]);
+    const int64_t d = a.cols;
+    const bool full = t0 + TT <= a.N && c0 + TC <= d;
+    // channels-last side: word (tr, wc) = channels c0 + 2wc, +1 of sample t0 + tr
+    auto row_word = [&](int k, int& tr, int& wc) {
+        const int i = (int)threadIdx.x + k * 256;
+        tr = i / TW;
+        wc = i % TW;
+    };
+    // channel-major side: word (c, j) = samples t0 + 2j, +1 of channel c0 + c
+    auto run_word = [&](int k, int& c, int& j) {
+        const int i = (int)threadIdx.x + k * 256;
+        c = i / (TT / 2);
+        j = i % (TT / 2);
+    };
+    auto row_ok = [&](int tr, int wc) { return full || (t0 + tr < a.N && c0 + 2 * wc < d); };
+    auto run_ok = [&](int c, int j) { return full || (c0 + c < d && t0 + 2 * j < a.N); };
+    auto row_index = [&](int tr, int wc) { return ((b * a.N + t0 + tr) * d + c0) / 2 + wc; };
+    auto run_index = [&](int c, int j) { return ((b * d + c0 + c) * a.N + t0) / 2 + j; };
+
+    uint32_t x[PER];
+    if (TO_COLS) {
+#pragma unroll
+        for (int k = 0; k < PER; ++k) {
+            int tr, wc;
+            row_word(k, tr, wc);
+            x[k] = row_ok(tr, wc) ? src[row_index(tr, wc)] : 0u;
+        }
+#pragma unroll
+        for (int k = 0; k < PER; ++k) {
+            int tr, wc;
+            row_word(k, tr, wc);
+            tile[tr * RS + wc] = x[k];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < PER; ++k) {
+            int c, j;
+            run_word(k, c, j);
+            const uint32_t lo = tile16[(2 * j) * 2 * RS + c];
+            const uint32_t hi = tile16[(2 * j + 1) * 2 * RS + c];
+            x[k] = lo | (hi << 16);
+        }
+#pragma unroll
+        for (int k = 0; k < PER; ++k) {
+            int c, j;
+            run_word(k, c, j);
+            if (run_ok(c, j)) dst[run_index(c, j)] = x[k];
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < PER; ++k) {
+            int c, j;
+            run_word(k, c, j);
+            x[k] = run_ok(c, j) ? src[run_index(c, j)] : 0u;
+        }
+#pragma unroll
+        for (int k = 0; k < PER; ++k) {
+            int c, j;
+            run_word(k, c, j);
+            tile16[(2 * j) * 2 * RS + c] = (uint16_t)(x[k] & 0xffffu);
+            tile16[(2 * j + 1) * 2 * RS + c] = (uint16_t)(x[k] >> 16);
+        }
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < PER; ++k) {
+            int tr, wc;
+            row_word(k, tr, wc);
+            x[k] = tile[tr * RS + wc];
+        }
+#pragma unroll
+        for (int k = 0; k < PER; ++k) {
+            int tr, wc;
+            row_word(k, tr, wc);
+            if (row_ok(tr, wc)) dst[row_index(tr, wc)] = x[k];
+        }
+    }
+}
+
+hyena_status stage_bf16_launch(const StageArgs& a, int ntensors, bool to_cols, hipStream_t s)
+{
+    const dim3 grid((unsigned)((a.cols + 63) / 64), (unsigned)((a.N + kStageTT - 1) / kStageTT),
                     (unsigned)(a.B * ntensors));
-    if (to_pm)
-        HY_LAUNCH(kernel_label("hyena_stage_pairs", type_label<IO>(), true),
-                  (hyena_stage_pairs<IO, true>), grid, dim3(256), 0, s, a);
+    if (to_cols)
+        HY_LAUNCH(kernel_label("hyena_stage_bf16", true), (hyena_stage_bf16<true>), grid, dim3(256),
+                  0, s, a);
     else
-        HY_LAUNCH(kernel_label("hyena_stage_pairs", type_label<IO>(), false),
-                  (hyena_stage_pairs<IO, false>), grid, dim3(256), 0, s, a);
+        HY_LAUNCH(kernel_label("hyena_stage_bf16", false), (hyena_stage_bf16<false>), grid,
+                  dim3(256), 0, s, a);
     const hipError_t e = hipGetLastError();
     return e == hipSuccess ? HYENA_OK : fail(HYENA_ERR_DEVICE, hipGetErrorString(e));
+}
+
+template <typename E>
+const char* elem_label();
+template <>
+const char* elem_label<float2>() { return "HIP_vector_type<float, 2u>"; }
+template <>
+const char* elem_label<uint32_t>() { return "unsigned int"; }
+template <>
+const char* elem_label<float>() { return "float"; }
+template <>
+const char* elem_label<uint16_t>() { return "unsigned short"; }
+
+template <typename E>
+hyena_status stage_launch(const StageArgs& a, int ntensors, bool to_cols, hipStream_t s)
+{
+    constexpr int TP = 128 / (int)sizeof(E);
+    const dim3 grid((unsigned)((a.cols + TP - 1) / TP), (unsigned)((a.N + kStageTT - 1) / kStageTT),
+                    (unsigned)(a.B * ntensors));
+    if (to_cols)
+        HY_LAUNCH(kernel_label("hyena_stage", elem_label<E>(), true), (hyena_stage<E, true>), grid,
+                  dim3(256), 0, s, a);
+    else
+        HY_LAUNCH(kernel_label("hyena_stage", elem_label<E>(), false), (hyena_stage<E, false>), grid,
+                  dim3(256), 0, s, a);
+    const hipError_t e = hipGetLastError();
+    return e == hipSuccess ? HYENA_OK : fail(HYENA_ERR_DEVICE, hipGetErrorString(e));
+}
+
+// Stage u and the gates (to_cols) or y (back) for the pair-major or
+// channel-major layout of the plan.
+hyena_status stage_plan(const Plan& p, const StageArgs& a, int ntensors, bool to_cols, hipStream_t s)
+{
+    StageArgs b = a;
+    if (p.lds_io == IO_REAL) {
+        b.cols = p.d;
+        if (p.io_dtype == HYENA_F32) return stage_launch<float>(b, ntensors, to_cols, s);
+        if (p.d % 2 == 0) return stage_bf16_launch(b, ntensors, to_cols, s);
+        return stage_launch<uint16_t>(b, ntensors, to_cols, s);
+    }
+    b.cols = p.npairs;
+    return p.io_dtype == HYENA_F32 ? stage_launch<float2>(b, ntensors, to_cols, s)
+                                   : stage_launch<uint32_t>(b, ntensors, to_cols, s);
 }
 
 hyena_status launch_lds1d_forward(const Plan& p, const void* u, const void* const* gates,
@@ -278,15 +483,17 @@ hyena_status launch_lds1d_forward(const Plan& p, const void* u, const void* cons
         K = 16384 / p.M < 16 ? 16384 / p.M : 16;
     }
     a.nblocks = p.B * ((p.npairs + K - 1) / K);
+    a.B = p.B;
+    a.twm = static_cast<const float2*>(ws) + p.seg[4].off;
+    const bool staged = mode == IO_PAIRMAJOR || mode == IO_REAL;
+    if (mode == IO_REAL) a.nblocks = p.B * p.d;
     StageArgs st{};
-    if (mode == IO_PAIRMAJOR) {
+    if (staged) {
         const size_t esz = p.io_dtype == HYENA_F32 ? 4 : 2;
         const size_t tensor = (size_t)p.B * p.N * p.d * esz;
         char* base = const_cast<char*>(static_cast<const char*>(ws)) + p.stage_offset;
         st.B = p.B;
         st.N = p.N;
-        st.d = p.d;
-        st.npairs = p.npairs;
         st.src[0] = u;
         st.dst[0] = base;
         for (int n = 0; n < p.order; ++n) {
@@ -296,24 +503,27 @@ hyena_status launch_lds1d_forward(const Plan& p, const void* u, const void* cons
         a.u = base;
         for (int n = 0; n < p.order; ++n) a.gates[n] = base + (size_t)(1 + n) * tensor;
         a.y = base + (size_t)(1 + p.order) * tensor;
-        const hyena_status r = p.io_dtype == HYENA_F32 ? stage_launch<float>(st, 1 + p.order, true, s)
-                                                       : stage_launch<uint16_t>(st, 1 + p.order, true, s);
+        const hyena_status r = stage_plan(p, st, 1 + p.order, true, s);
         if (r != HYENA_OK) return r;
     }
     hyena_status r;
-    if (p.io_dtype == HYENA_F32) r = fwd_by_m<float, float>(p.M, a, mode, s);
-    else if (p.spec_dtype == HYENA_BF16) r = fwd_by_m<uint16_t, uint16_t>(p.M, a, mode, s);
-    else r = fwd_by_m<uint16_t, float>(p.M, a, mode, s);
-    if (r != HYENA_OK || mode != IO_PAIRMAJOR) return r;
+    if (mode == IO_REAL) {
+        const int64_t L = p.M / 2;
+        if (p.io_dtype == HYENA_F32) r = real_fwd_by_l<float, float>(L, a, s);
+        else if (p.spec_dtype == HYENA_BF16) r = real_fwd_by_l<uint16_t, uint16_t>(L, a, s);
+        else r = real_fwd_by_l<uint16_t, float>(L, a, s);
+    } else {
+        if (p.io_dtype == HYENA_F32) r = fwd_by_m<float, float>(p.M, a, mode, s);
+        else if (p.spec_dtype == HYENA_BF16) r = fwd_by_m<uint16_t, uint16_t>(p.M, a, mode, s);
+        else r = fwd_by_m<uint16_t, float>(p.M, a, mode, s);
+    }
+    if (r != HYENA_OK || !staged) return r;
     StageArgs out{};
     out.B = p.B;
     out.N = p.N;
-    out.d = p.d;
-    out.npairs = p.npairs;
     out.src[0] = a.y;
     out.dst[0] = y;
-    return p.io_dtype == HYENA_F32 ? stage_launch<float>(out, 1, false, s)
-                                   : stage_launch<uint16_t>(out, 1, false, s);
+    return stage_plan(p, out, 1, false, s);
 }
 
 hyena_status launch_lds1d_spectrum(const Plan& p, const void* h, void* H, const void* ws,
@@ -329,6 +539,14 @@ hyena_status launch_lds1d_spectrum(const Plan& p, const void* h, void* H, const 
     a.nblocks = (int64_t)p.order * p.npairs;
     a.tw_off = lds1d_offsets(p);
     const hipStream_t s = (hipStream_t)stream;
+    if (p.lds_io == IO_REAL) {
+        const int64_t L = p.M / 2;
+        a.nblocks = (int64_t)p.order * p.d;
+        a.twm = static_cast<const float2*>(ws) + p.seg[4].off;
+        if (p.io_dtype == HYENA_F32) return real_spec_by_l<float, float>(L, a, s);
+        if (p.spec_dtype == HYENA_BF16) return real_spec_by_l<uint16_t, uint16_t>(L, a, s);
+        return real_spec_by_l<uint16_t, float>(L, a, s);
+    }
     if (p.io_dtype == HYENA_F32) return spec_by_m<float, float>(p.M, a, s);
     if (p.spec_dtype == HYENA_BF16) return spec_by_m<uint16_t, uint16_t>(p.M, a, s);
     return spec_by_m<uint16_t, float>(p.M, a, s);

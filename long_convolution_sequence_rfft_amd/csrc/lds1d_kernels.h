@@ -29,7 +29,8 @@ struct Lds1dFwdArgs {
     const void* spec;
     const float* D;
     const float2* tw;
-    int64_t N, d, npairs, nblocks;
+    const float2* twm;  // single-channel kernels: exp(-2 pi i k / M), k < M/2
+    int64_t N, d, npairs, nblocks, B;
     int32_t order;
     TwOffsets tw_off;
 };
@@ -38,6 +39,7 @@ struct Lds1dSpecArgs {
     const void* h;
     void* spec;
     const float2* tw;
+    const float2* twm;
     int64_t N, d, npairs, nblocks;
     TwOffsets tw_off;
 };
@@ -51,7 +53,9 @@ struct Lds1dSpecArgs {
 //   IO_PAIRMAJOR: u, gates and y are staged pair-major ([B][pairs][N]) in the
 //                 workspace by separate transpose kernels; every access is a
 //                 contiguous run.  Used when only one pair fits a workgroup.
-enum Lds1dIo { IO_DIRECT = 0, IO_TILED = 1, IO_PAIRMAJOR = 2 };
+//   IO_REAL:      single-channel kernels (hyena_lds1d_real_forward) on u,
+//                 gates and y staged channel-major ([B][d][N]).
+enum Lds1dIo { IO_DIRECT = 0, IO_TILED = 1, IO_PAIRMAJOR = 2, IO_REAL = 3 };
 
 // Channel pairs per workgroup in IO_TILED mode: as many length-M regions as
 // fit 16384 points of LDS, at most 16.
@@ -285,6 +289,128 @@ hyena_lds1d_spectrum(Lds1dSpecArgs a)
     store_spectrum_entries<M, SP>(v, spec, tau, 0.5f / (float)M);
 }
 
+// ---------------------------------------------------------------------------
+// Single-channel forms (transform length L = M/2, one real channel per
+// workgroup; see real_product).  Half the LDS of the channel-pair kernel, so
+// twice as many workgroups share a CU and one's exchanges and barriers
+// overlap another's arithmetic.  Activations are staged channel-major
+// ([B][d][N]); sample pair (2m, 2m+1) is one aligned PairRaw element.
+// ---------------------------------------------------------------------------
+template <int L, typename IO, typename SP>
+__global__ void __launch_bounds__(FftShape<L>::T, 2) hyena_lds1d_real_forward(Lds1dFwdArgs a)
+{
+    using S = FftShape<L>;
+    constexpr int T = S::T, PTS = S::PTS, R0 = S::R0, LW = S::LW;
+    __shared__ float smem[2 * LW];
+    __shared__ float sxs[4 * S::RL];
+    float* re = smem;
+    float* im = smem + LW;
+
+    const int tau = threadIdx.x;
+    const int64_t lin = xcd_remap(blockIdx.x, a.nblocks);
+    // batch row fastest: the B workgroups of a channel share its spectrum in L2
+    const int64_t c = lin / a.B;
+    const int64_t b = lin - c * a.B;
+    const int j1 = tau, j2 = tau ? 2 * T - tau : T;
+    const int64_t row = (b * a.d + c) * a.N;  // this (b, c)'s run in the staged tensors
+    const float2 wbase = a.twm[tau ? tau : T];
+    const float invL = 1.0f / (float)L;
+
+    float2 v[PTS];
+    const IO* ubase = static_cast<const IO*>(a.u) + row;
+#pragma unroll
+    for (int q = 0; q < S::Q0; ++q) {
+        const uint32_t lane_off = (uint32_t)(tau + q * T) * 2u * (uint32_t)sizeof(IO);
+#pragma unroll
+        for (int r = 0; r < R0 / 2; ++r)
+            v[q * R0 + r] = widen_pair<IO>(load_pair_raw(ubase + (size_t)r * (L / R0) * 2, lane_off));
+    }
+
+    for (int n = 0; n < a.order; ++n) {
+        const SP* spec = static_cast<const SP*>(a.spec) +
+                         ((int64_t)n * a.d + c) * (int64_t)(L / 2) * kEntryElems;
+        typename EntryRaw<SP>::type ent[S::RL];
+        fwd_transform<L>(v, re, im, a.tw, a.tw_off, tau, j1, j2, n > 0,
+                         [&] { load_entries<L, SP>(ent, spec, tau); });
+        real_product<L, SP>(v, ent, tau, a.D[(int64_t)n * a.d + c] * invL, wbase, sxs);
+
+        const IO* g = static_cast<const IO*>(a.gates[n]) + row;
+        typename PairRaw<IO>::type graw[S::Q0][R0 / 2];
+        inv_transform<L>(v, re, im, a.tw, a.tw_off, tau, j1, j2, [&] {
+#pragma unroll
+            for (int q = 0; q < S::Q0; ++q) {
+                const uint32_t lane_off = (uint32_t)(tau + q * T) * 2u * (uint32_t)sizeof(IO);
+#pragma unroll
+                for (int r = 0; r < R0 / 2; ++r)
+                    graw[q][r] = load_pair_raw(g + (size_t)r * (L / R0) * 2, lane_off);
+            }
+        });
+#pragma unroll
+        for (int q = 0; q < S::Q0; ++q)
+#pragma unroll
+            for (int r = 0; r < R0 / 2; ++r) {
+                const float2 gg = widen_pair<IO>(graw[q][r]);
+                float2& x = v[q * R0 + r];
+                x = make_float2(x.x * gg.x, x.y * gg.y);
+            }
+    }
+
+    IO* ybase = static_cast<IO*>(a.y) + row;
+#pragma unroll
+    for (int q = 0; q < S::Q0; ++q) {
+        const uint32_t lane_off = (uint32_t)(tau + q * T) * 2u * (uint32_t)sizeof(IO);
+#pragma unroll
+        for (int r = 0; r < R0 / 2; ++r)
+            store_pair_at(ybase + (size_t)r * (L / R0) * 2, lane_off, v[q * R0 + r]);
+    }
+}
+
+// Filter spectrum, single-channel form: one workgroup per (filter n, channel
+// c); entries (S, Dl) / L, the 1/L of the unscaled inverse transform folded in.
+template <int L, typename IO, typename SP>
+__global__ void __launch_bounds__(FftShape<L>::T, 2) hyena_lds1d_real_spectrum(Lds1dSpecArgs a)
+{
+    using S = FftShape<L>;
+    constexpr int T = S::T, PTS = S::PTS, R0 = S::R0;
+    __shared__ float smem[2 * S::LW];
+    const int tau = threadIdx.x;
+    const int64_t lin = blockIdx.x;  // n * d + c
+    const int j1 = tau, j2 = tau ? 2 * T - tau : T;
+    const IO* h = static_cast<const IO*>(a.h) + lin * a.N;
+
+    float2 v[PTS];
+#pragma unroll
+    for (int q = 0; q < S::Q0; ++q) {
+        const uint32_t lane_off = (uint32_t)(tau + q * T) * 2u * (uint32_t)sizeof(IO);
+#pragma unroll
+        for (int r = 0; r < R0 / 2; ++r)
+            v[q * R0 + r] = widen_pair<IO>(load_pair_raw(h + (size_t)r * (L / R0) * 2, lane_off));
+    }
+    fwd_transform<L>(v, smem, smem + S::LW, a.tw, a.tw_off, tau, j1, j2, false, [] {});
+    SP* spec = static_cast<SP*>(a.spec) + lin * (int64_t)(L / 2) * kEntryElems;
+    store_real_entries<L, SP>(v, spec, tau, 1.0f / (float)L, a.twm[tau ? tau : T]);
+}
+
+template <int L, typename IO, typename SP>
+hyena_status lds1d_real_forward_launch(const Lds1dFwdArgs& a, hipStream_t s)
+{
+    HY_LAUNCH(kernel_label("hyena_lds1d_real_forward", L, type_label<IO>(), type_label<SP>()),
+              (hyena_lds1d_real_forward<L, IO, SP>), dim3((unsigned)a.nblocks),
+              dim3(FftShape<L>::T), 0, s, a);
+    const hipError_t e = hipGetLastError();
+    return e == hipSuccess ? HYENA_OK : fail(HYENA_ERR_DEVICE, hipGetErrorString(e));
+}
+
+template <int L, typename IO, typename SP>
+hyena_status lds1d_real_spectrum_launch(const Lds1dSpecArgs& a, hipStream_t s)
+{
+    HY_LAUNCH(kernel_label("hyena_lds1d_real_spectrum", L, type_label<IO>(), type_label<SP>()),
+              (hyena_lds1d_real_spectrum<L, IO, SP>), dim3((unsigned)a.nblocks),
+              dim3(FftShape<L>::T), 0, s, a);
+    const hipError_t e = hipGetLastError();
+    return e == hipSuccess ? HYENA_OK : fail(HYENA_ERR_DEVICE, hipGetErrorString(e));
+}
+
 template <int M, typename IO, typename SP>
 hyena_status lds1d_forward_launch(const Lds1dFwdArgs& a, int mode, hipStream_t s)
 {
@@ -320,6 +446,10 @@ hyena_status lds1d_spectrum_launch(const Lds1dSpecArgs& a, hipStream_t s)
     X(512, IO, SP) X(1024, IO, SP) X(2048, IO, SP) X(4096, IO, SP) X(8192, IO, SP)       \
     X(16384, IO, SP)
 
+#define HY_LDS1D_REAL_SIZES(X, IO, SP) \
+    X(8, IO, SP) X(16, IO, SP) X(32, IO, SP) X(64, IO, SP) X(128, IO, SP) X(256, IO, SP) \
+    X(512, IO, SP) X(1024, IO, SP) X(2048, IO, SP) X(4096, IO, SP) X(8192, IO, SP)
+
 #define HY_LDS1D_INSTANTIATE(M, IO, SP)                                                      \
     template hyena_status lds1d_forward_launch<M, IO, SP>(const Lds1dFwdArgs&, int,          \
                                                           hipStream_t);                      \
@@ -330,5 +460,15 @@ hyena_status lds1d_spectrum_launch(const Lds1dSpecArgs& a, hipStream_t s)
                                                                  hipStream_t);                   \
     extern template hyena_status lds1d_spectrum_launch<M, IO, SP>(const Lds1dSpecArgs&,          \
                                                                   hipStream_t);
+
+#define HY_LDS1D_REAL_INSTANTIATE(L, IO, SP)                                                      \
+    template hyena_status lds1d_real_forward_launch<L, IO, SP>(const Lds1dFwdArgs&, hipStream_t); \
+    template hyena_status lds1d_real_spectrum_launch<L, IO, SP>(const Lds1dSpecArgs&, hipStream_t);
+
+#define HY_LDS1D_REAL_EXTERN(L, IO, SP)                                                       \
+    extern template hyena_status lds1d_real_forward_launch<L, IO, SP>(const Lds1dFwdArgs&,    \
+                                                                      hipStream_t);           \
+    extern template hyena_status lds1d_real_spectrum_launch<L, IO, SP>(const Lds1dSpecArgs&,  \
+                                                                       hipStream_t);
 
 }  // namespace hy

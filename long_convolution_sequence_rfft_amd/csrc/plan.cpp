@@ -108,16 +108,21 @@ hyena_status plan_build(Plan& p, int64_t B, int64_t N, int64_t d, int32_t order,
         p.path = path;
         p.spec_entries_per_pair = p.M / 2;
         if (path == HYENA_PATH_LDS1D) {
-            const int M = (int)p.M;
-            p.R0 = lds1d_r0(M);
-            p.R1 = lds1d_r1(M);
-            p.RL = lds1d_rl(M);
-            add_transform_segments(p, off, p.M);
-            // activation access: staged pair-major in the workspace (measured
-            // faster than multi-pair workgroups with LDS tiles at 2K and 8K);
-            // odd d or N < M/2 take the per-lane path.
-            const bool fast = (d % 2 == 0) && (2 * N == p.M);
-            p.lds_io = !fast ? 0 : 2;
+            // N = M/2 (a power of two): single-channel kernels, one real
+            // channel per length-M/2 complex transform, on activations staged
+            // channel-major in the workspace (half the LDS of a channel pair,
+            // so twice the workgroups per CU; measured faster at 2K and 8K).
+            // Other N: channel-pair kernels reading channels-last rows per lane.
+            const bool real = 2 * N == p.M && p.M >= 16;
+            p.lds_io = real ? 3 : 0;
+            const int64_t L = real ? p.M / 2 : p.M;
+            p.R0 = lds1d_r0((int)L);
+            p.R1 = lds1d_r1((int)L);
+            p.RL = lds1d_rl((int)L);
+            add_transform_segments(p, off, L);
+            // exp(-2 pi i k / M), k < M/2: the bin twiddles of the
+            // single-channel product
+            add_segment(p, off, p.M / 2, 2);
         } else {
             fourstep_split(p.M, p.M1, p.M2);
             // outer (column, length M1) and inner (row, length M2) transforms use
@@ -150,6 +155,8 @@ hyena_status plan_build(Plan& p, int64_t B, int64_t N, int64_t d, int32_t order,
     p.tw_bytes = align_up((size_t)off * 8, 256);
     p.spectrum_bytes = (size_t)p.order * (size_t)p.npairs * (size_t)p.spec_entries_per_pair *
                        p.spec_entry_bytes;
+    if (p.path == HYENA_PATH_LDS1D && p.lds_io == 3)  // M/4 entries per channel
+        p.spectrum_bytes = (size_t)p.order * (size_t)d * (size_t)(p.M / 4) * p.spec_entry_bytes;
 
     // intermediate spectra of the multi-pass paths: one complex64 value per
     // transform point of the zero-padded half that is kept, for a chunk of
@@ -175,7 +182,7 @@ hyena_status plan_build(Plan& p, int64_t B, int64_t N, int64_t d, int32_t order,
         const int64_t need = chunk * (fwd_pair > spec_pair ? fwd_pair : spec_pair);
         p.inter_bytes = align_up((size_t)need, 256);
     }
-    if (p.path == HYENA_PATH_LDS1D && p.lds_io == 2) {
+    if (p.path == HYENA_PATH_LDS1D && (p.lds_io == 2 || p.lds_io == 3)) {
         // u, every gate and y, pair-major
         p.stage_offset = p.inter_offset + p.inter_bytes;
         p.stage_bytes = align_up((size_t)(p.order + 2) * (size_t)B * (size_t)N * (size_t)d *

@@ -529,6 +529,175 @@ __device__ __forceinline__ void store_spectrum_entries(const float2* v, SP* spec
     }
 }
 
+// ---------------------------------------------------------------------------
+// Single-channel spectral product.  One real channel x of the length-M
+// zero-padded sequence rides in z[m] = x[2m] + i x[2m+1], a complex signal of
+// length L = M/2 with Z = DFT_L(z).  E and O, the transforms of the even and
+// odd samples, are E[k] = (Z[k] + conj Z[L-k])/2 and
+// O[k] = (Z[k] - conj Z[L-k])/2i, and X[k] = E[k] + W^k O[k],
+// X[k+L] = E[k] - W^k O[k] with W = exp(-2 pi i/M).  Multiplying X by the
+// filter's transfer function H and packing the product the same way gives
+//   Z'[k]   = (S - s Dl) Z[k] + i c Dl conj Z[L-k]
+//   Z'[L-k] = conj(S + s Dl) Z[L-k] + i c conj(Dl) conj Z[k]
+// with S = (H[k] + conj H[L-k])/2, Dl = (H[k] - conj H[L-k])/2 and
+// W^k = c - i s; the inverse DFT_L of Z' then holds y[2m] + i y[2m+1].  One
+// entry (S, Dl) serves a bin and its mirror.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void real_pair_product(float2& zk, float2& zm, float2 S, float2 Dl,
+                                                  float c, float s)
+{
+    const float2 U = make_float2(Dl.x * s, Dl.y * s);
+    const float2 V = make_float2(Dl.x * c, Dl.y * c);
+    const float2 A = make_float2(S.x - U.x, S.y - U.y);   // coefficient of Z[k]
+    const float2 Ap = make_float2(S.x + U.x, S.y + U.y);  // conj of the coefficient of Z[L-k]
+    const float ykx = fmaf(A.x, zk.x, fmaf(-A.y, zk.y, fmaf(-V.y, zm.x, V.x * zm.y)));
+    const float yky = fmaf(A.x, zk.y, fmaf(A.y, zk.x, fmaf(V.x, zm.x, V.y * zm.y)));
+    const float ymx = fmaf(Ap.x, zm.x, fmaf(Ap.y, zm.y, fmaf(V.y, zk.x, V.x * zk.y)));
+    const float ymy = fmaf(Ap.x, zm.y, fmaf(-Ap.y, zm.x, fmaf(V.x, zk.x, -V.y * zk.y)));
+    zk = make_float2(ykx, yky);
+    zm = make_float2(ymx, ymy);
+}
+
+// Filter side: the entry (S, Dl) * scale of bin k from Z = DFT_L of the packed
+// filter at k and L-k: S = E[k], Dl = W^k O[k].
+__device__ __forceinline__ void entry_from_real(float2 zk, float2 zm, float c, float s, float scale,
+                                                float2& S, float2& Dl)
+{
+    S = make_float2(0.5f * (zk.x + zm.x) * scale, 0.5f * (zk.y - zm.y) * scale);
+    // O = (Z[k] - conj Z[L-k]) / 2i
+    const float ox = 0.5f * (zk.y + zm.y), oy = -0.5f * (zk.x - zm.x);
+    Dl = make_float2((c * ox + s * oy) * scale, (c * oy - s * ox) * scale);
+}
+
+// exp(-2 pi i e / (2 RL)), the step between a thread's last-pass outputs.
+template <int RL>
+__device__ __forceinline__ float2 out_step_root(int e)
+{
+    const int m = e * (32 / (2 * RL));
+    return make_float2(cos32(m), -sin32(m));
+}
+
+// W^k of output e of a thread's first last-pass butterfly (bin base + e L/RL),
+// from W^base: cos and sin of 2 pi k / M.
+template <int RL>
+__device__ __forceinline__ void bin_cs(float2 wbase, int e, float& c, float& s)
+{
+    const float2 r = out_step_root<RL>(e);
+    const float2 w = cmul(wbase, r);
+    c = w.x;
+    s = -w.y;
+}
+
+// Single-channel product on the last-pass registers of one length-L
+// transform (same register layout and thread-0 handling as spectral_product).
+//   tau > 0: entry e is bin k = tau + e L/RL (output e of butterfly tau) with
+//            its mirror L - k (output RL-1-e of butterfly 2T - tau).
+//   tau = 0: entry 0 packs the self-mirrored bins 0 and L/2 as
+//            ((S0, Re H[L/2]), (Dl0, Im H[L/2])); entries 1..RL/2-1 are bins
+//            e L/RL of butterfly 0, entries RL/2.. bins T + (e - RL/2) L/RL of
+//            butterfly T.
+// wbase = W^tau (tau > 0) or W^T (tau = 0); dp = D/L (folded feedthrough).
+template <int L, typename SP>
+__device__ __forceinline__ void real_product(float2* v, const typename EntryRaw<SP>::type* ent,
+                                             int tau, float dp, float2 wbase, float* xs)
+{
+    using S = FftShape<L>;
+    constexpr int RL = S::RL;
+    float2 Sv, Dv;
+    float c, s;
+    if (tau == 0) {
+        widen_entry<SP>(ent[0], Sv, Dv);
+        const float S0 = Sv.x + dp, Hr = Sv.y + dp, D0 = Dv.x, Hi = Dv.y;
+        const float2 z0 = v[0], zh = v[RL / 2];
+        xs[0] = fmaf(S0, z0.x, D0 * z0.y);
+        xs[1] = fmaf(S0, z0.y, D0 * z0.x);
+        xs[RL] = fmaf(Hr, zh.x, Hi * zh.y);
+        xs[RL + 1] = fmaf(Hr, zh.y, -Hi * zh.x);
+#pragma unroll
+        for (int e = 1; e < RL / 2; ++e) {
+            widen_entry<SP>(ent[e], Sv, Dv);
+            Sv.x += dp;
+            const float2 r = out_step_root<RL>(e);
+            float2 a = v[e], b = v[RL - e];
+            real_pair_product(a, b, Sv, Dv, r.x, -r.y);
+            xs[2 * e] = a.x;
+            xs[2 * e + 1] = a.y;
+            xs[2 * (RL - e)] = b.x;
+            xs[2 * (RL - e) + 1] = b.y;
+        }
+#pragma unroll
+        for (int e = RL / 2; e < RL; ++e) {
+            const int s2 = e - RL / 2;
+            widen_entry<SP>(ent[e], Sv, Dv);
+            Sv.x += dp;
+            bin_cs<RL>(wbase, s2, c, s);
+            float2 a = v[RL + s2], b = v[2 * RL - 1 - s2];
+            real_pair_product(a, b, Sv, Dv, c, s);
+            xs[2 * (RL + s2)] = a.x;
+            xs[2 * (RL + s2) + 1] = a.y;
+            xs[2 * (2 * RL - 1 - s2)] = b.x;
+            xs[2 * (2 * RL - 1 - s2) + 1] = b.y;
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < RL; ++e) {
+        widen_entry<SP>(ent[e], Sv, Dv);
+        Sv.x += dp;
+        bin_cs<RL>(wbase, e, c, s);
+        real_pair_product(v[e], v[2 * RL - 1 - e], Sv, Dv, c, s);
+    }
+    if (tau == 0) {
+#pragma unroll
+        for (int i = 0; i < 2 * RL; ++i) v[i] = make_float2(xs[2 * i], xs[2 * i + 1]);
+    }
+}
+
+// Filter side of the single-channel layout: write the entries of one transform.
+template <int L, typename SP>
+__device__ __forceinline__ void store_real_entries(const float2* v, SP* spec, int tau, float scale,
+                                                   float2 wbase)
+{
+    using S = FftShape<L>;
+    constexpr int T = S::T, RL = S::RL;
+    float2 Sv, Dv;
+    float c, s;
+    if (tau != 0) {
+#pragma unroll
+        for (int e = 0; e < RL; ++e) {
+            bin_cs<RL>(wbase, e, c, s);
+            entry_from_real(v[e], v[2 * RL - 1 - e], c, s, scale, Sv, Dv);
+            store_entry(spec, e * T + tau, Sv, Dv);
+        }
+    } else {
+        // bins 0 and L/2: S0 = Re Z[0], Dl0 = Im Z[0], H[L/2] = conj Z[L/2]
+        const float2 z0 = v[0], zh = v[RL / 2];
+        store_entry(spec, 0, make_float2(z0.x * scale, zh.x * scale),
+                    make_float2(z0.y * scale, -zh.y * scale));
+#pragma unroll
+        for (int e = 1; e < RL / 2; ++e) {
+            const float2 r = out_step_root<RL>(e);
+            entry_from_real(v[e], v[RL - e], r.x, -r.y, scale, Sv, Dv);
+            store_entry(spec, e * T, Sv, Dv);
+        }
+#pragma unroll
+        for (int e = RL / 2; e < RL; ++e) {
+            const int s2 = e - RL / 2;
+            bin_cs<RL>(wbase, s2, c, s);
+            entry_from_real(v[RL + s2], v[2 * RL - 1 - s2], c, s, scale, Sv, Dv);
+            store_entry(spec, e * T, Sv, Dv);
+        }
+    }
+}
+
+// Bin k of single-channel entry (tau, e); its mirror is L - k.  Entry (0, 0)
+// holds bins 0 and L/2.
+__host__ __device__ inline int64_t real_entry_bin(int64_t L, int64_t T, int64_t tau, int64_t e)
+{
+    const int64_t RL = L / (2 * T);
+    if (tau == 0) return e < RL / 2 ? e * 2 * T : T + (e - RL / 2) * 2 * T;
+    return tau + e * 2 * T;
+}
+
 // Bin of entry (tau, e) of a length-L transform (entry (0, 0) also holds L/2).
 __host__ __device__ inline int64_t entry_bin(int64_t L, int64_t T, int64_t tau, int64_t e)
 {

@@ -140,7 +140,7 @@ def test_full_size_config_all_channels(cfg):
 
 
 def test_launch_timing_records_every_kernel():
-    # per-launch timing: each forward on the pair-major LDS path is three
+    # per-launch timing: each forward on the single-channel LDS path is three
     # launches (stage in, transform chain, stage out), all recorded by name
     import torch
     from long_convolution_sequence_rfft_amd import hyena
@@ -158,9 +158,9 @@ def test_launch_timing_records_every_kernel():
     recs, dropped = hyena.hyena_timing_end()
     hyena.hyena_timing_release()
     assert dropped == 0
-    assert sorted(recs) == ["hy::hyena_lds1d_forward<4096, float, float, 2>",
-                            "hy::hyena_stage_pairs<float, false>",
-                            "hy::hyena_stage_pairs<float, true>"]
+    assert sorted(recs) == ["hy::hyena_lds1d_real_forward<2048, float, float>",
+                            "hy::hyena_stage<float, false>",
+                            "hy::hyena_stage<float, true>"]
     for r in recs.values():
         assert r["launches"] == 3
         assert 0.0 < r["min_ms"] <= r["max_ms"] and r["total_ms"] >= 3 * r["min_ms"] * 0.999
@@ -169,3 +169,12 @@ def test_launch_timing_records_every_kernel():
     plan.forward(u, gates, H, D, y_ref)
     torch.cuda.synchronize()
     assert torch.equal(y, y_ref)
+
+
+@pytest.mark.parametrize("N,d,B", [(1024, 7, 3), (8, 3, 2), (16, 1, 1), (4096, 9, 2)])
+def test_single_channel_path_odd_widths(N, d, B):
+    # N = M/2 takes the single-channel kernels, which need no channel pairing:
+    # odd d, one channel, and the smallest transforms
+    inp = synth.make_1d(B=B, N=N, d=d, order=2, seed=9)
+    y, _, _ = run_gpu(inp)
+    assert rel_err(y, oracle_ref(inp, method=oracle.DIRECT)) < TOL_F32
