@@ -161,11 +161,11 @@ hyena_status launch_lds1d_export(const Plan& p, const void* H, void* out, void* 
 namespace {
 
 template <typename IO, typename SP>
-hyena_status fwd_by_m(int64_t M, const Lds1dFwdArgs& a, int mode, hipStream_t s)
+hyena_status fwd_by_m(int64_t M, const Lds1dFwdArgs& a, hipStream_t s)
 {
     switch (M) {
 #define HY_CASE(MM, I, S_) \
-    case MM: return lds1d_forward_launch<MM, IO, SP>(a, mode, s);
+    case MM: return lds1d_forward_launch<MM, IO, SP>(a, s);
         HY_LDS1D_SIZES(HY_CASE, IO, SP)
 #undef HY_CASE
         default: return fail(HYENA_ERR_UNSUPPORTED, "LDS1D: unsupported transform length");
@@ -420,10 +420,6 @@ hyena_status stage_bf16_launch(const StageArgs& a, int ntensors, bool to_cols, h
 template <typename E>
 const char* elem_label();
 template <>
-const char* elem_label<float2>() { return "HIP_vector_type<float, 2u>"; }
-template <>
-const char* elem_label<uint32_t>() { return "unsigned int"; }
-template <>
 const char* elem_label<float>() { return "float"; }
 template <>
 const char* elem_label<uint16_t>() { return "unsigned short"; }
@@ -444,20 +440,14 @@ hyena_status stage_launch(const StageArgs& a, int ntensors, bool to_cols, hipStr
     return e == hipSuccess ? HYENA_OK : fail(HYENA_ERR_DEVICE, hipGetErrorString(e));
 }
 
-// Stage u and the gates (to_cols) or y (back) for the pair-major or
-// channel-major layout of the plan.
+// Stage u and the gates (to_cols) or y (back) channel-major.
 hyena_status stage_plan(const Plan& p, const StageArgs& a, int ntensors, bool to_cols, hipStream_t s)
 {
     StageArgs b = a;
-    if (p.lds_io == IO_REAL) {
-        b.cols = p.d;
-        if (p.io_dtype == HYENA_F32) return stage_launch<float>(b, ntensors, to_cols, s);
-        if (p.d % 2 == 0) return stage_bf16_launch(b, ntensors, to_cols, s);
-        return stage_launch<uint16_t>(b, ntensors, to_cols, s);
-    }
-    b.cols = p.npairs;
-    return p.io_dtype == HYENA_F32 ? stage_launch<float2>(b, ntensors, to_cols, s)
-                                   : stage_launch<uint32_t>(b, ntensors, to_cols, s);
+    b.cols = p.d;
+    if (p.io_dtype == HYENA_F32) return stage_launch<float>(b, ntensors, to_cols, s);
+    if (p.d % 2 == 0) return stage_bf16_launch(b, ntensors, to_cols, s);
+    return stage_launch<uint16_t>(b, ntensors, to_cols, s);
 }
 
 hyena_status launch_lds1d_forward(const Plan& p, const void* u, const void* const* gates,
@@ -477,16 +467,11 @@ hyena_status launch_lds1d_forward(const Plan& p, const void* u, const void* cons
     a.npairs = p.npairs;
     a.order = p.order;
     a.tw_off = lds1d_offsets(p);
-    const int mode = p.lds_io;
-    int64_t K = 1;
-    if (mode == IO_TILED) {
-        K = 16384 / p.M < 16 ? 16384 / p.M : 16;
-    }
-    a.nblocks = p.B * ((p.npairs + K - 1) / K);
     a.B = p.B;
+    a.nblocks = p.B * p.npairs;
     a.twm = static_cast<const float2*>(ws) + p.seg[4].off;
-    const bool staged = mode == IO_PAIRMAJOR || mode == IO_REAL;
-    if (mode == IO_REAL) a.nblocks = p.B * p.d;
+    const bool staged = p.lds_io == IO_REAL;
+    if (staged) a.nblocks = p.B * p.d;
     StageArgs st{};
     if (staged) {
         const size_t esz = p.io_dtype == HYENA_F32 ? 4 : 2;
@@ -507,15 +492,15 @@ hyena_status launch_lds1d_forward(const Plan& p, const void* u, const void* cons
         if (r != HYENA_OK) return r;
     }
     hyena_status r;
-    if (mode == IO_REAL) {
+    if (staged) {
         const int64_t L = p.M / 2;
         if (p.io_dtype == HYENA_F32) r = real_fwd_by_l<float, float>(L, a, s);
         else if (p.spec_dtype == HYENA_BF16) r = real_fwd_by_l<uint16_t, uint16_t>(L, a, s);
         else r = real_fwd_by_l<uint16_t, float>(L, a, s);
     } else {
-        if (p.io_dtype == HYENA_F32) r = fwd_by_m<float, float>(p.M, a, mode, s);
-        else if (p.spec_dtype == HYENA_BF16) r = fwd_by_m<uint16_t, uint16_t>(p.M, a, mode, s);
-        else r = fwd_by_m<uint16_t, float>(p.M, a, mode, s);
+        if (p.io_dtype == HYENA_F32) r = fwd_by_m<float, float>(p.M, a, s);
+        else if (p.spec_dtype == HYENA_BF16) r = fwd_by_m<uint16_t, uint16_t>(p.M, a, s);
+        else r = fwd_by_m<uint16_t, float>(p.M, a, s);
     }
     if (r != HYENA_OK || !staged) return r;
     StageArgs out{};

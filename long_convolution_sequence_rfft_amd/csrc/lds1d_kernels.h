@@ -44,211 +44,96 @@ struct Lds1dSpecArgs {
     TwOffsets tw_off;
 };
 
-// How the forward kernel reaches the activations (channels last in memory).
-//   IO_DIRECT:    each lane loads its own channel pair (generic; odd d,
-//                 sequences shorter than M/2).
-//   IO_TILED:     a workgroup owns K channel pairs; rows move between memory
-//                 and LDS as tiles of K pairs (K consecutive lanes per row), so
-//                 each cache line touched carries K pairs instead of one.
-//   IO_PAIRMAJOR: u, gates and y are staged pair-major ([B][pairs][N]) in the
-//                 workspace by separate transpose kernels; every access is a
-//                 contiguous run.  Used when only one pair fits a workgroup.
-//   IO_REAL:      single-channel kernels (hyena_lds1d_real_forward) on u,
-//                 gates and y staged channel-major ([B][d][N]).
-enum Lds1dIo { IO_DIRECT = 0, IO_TILED = 1, IO_PAIRMAJOR = 2, IO_REAL = 3 };
+// How the forward pass reaches the activations (channels last in memory).
+//   IO_PAIR: channel-pair kernel (hyena_lds1d_forward), each lane loading its
+//            own channel pair from the channels-last rows.  The general form:
+//            any N (including lengths below M/2) and any d.
+//   IO_REAL: single-channel kernels (hyena_lds1d_real_forward) on u, gates and
+//            y staged channel-major ([B][d][N]) in the workspace; used when
+//            N = M/2.
+enum Lds1dIo { IO_PAIR = 0, IO_REAL = 3 };
 
-// Channel pairs per workgroup in IO_TILED mode: as many length-M regions as
-// fit 16384 points of LDS, at most 16.
-template <int M>
-struct Lds1dPairs {
-    static constexpr int K = 16384 / M < 16 ? 16384 / M : 16;
-};
-
-template <int M, int MODE>
-struct Lds1dBlock {
-    static constexpr int K = MODE == IO_TILED ? Lds1dPairs<M>::K : 1;
-    static constexpr int THREADS = K * FftShape<M>::T;
-};
-
-template <int M, typename IO, typename SP, int MODE>
-__global__ void __launch_bounds__((Lds1dBlock<M, MODE>::THREADS), 2)
-hyena_lds1d_forward(Lds1dFwdArgs a)
+// Channel-pair form: one workgroup owns one (batch row b, channel pair c,
+// c+1) and reads and writes the channels-last rows directly, masking the
+// samples past N and a missing partner channel.
+template <int M, typename IO, typename SP>
+__global__ void __launch_bounds__(FftShape<M>::T, 2) hyena_lds1d_forward(Lds1dFwdArgs a)
 {
     using S = FftShape<M>;
     constexpr int T = S::T, PTS = S::PTS, R0 = S::R0, LW = S::LW;
-    constexpr int K = Lds1dBlock<M, MODE>::K;
-    constexpr int NT = Lds1dBlock<M, MODE>::THREADS;
-    // one region per pair: [re block | im block], so real and imaginary
-    // parts of an element are LW words apart and share one base address
-    __shared__ float smem[K * 2 * LW];
-    __shared__ float sxs[K * 4 * S::RL];
+    // [re block | im block]: real and imaginary parts of an element are LW
+    // words apart and share one base address
+    __shared__ float smem[2 * LW];
+    __shared__ float sxs[4 * S::RL];
 
-    const int k = threadIdx.x / T;  // pair within the workgroup
-    const int tau = threadIdx.x - k * T;
+    const int tau = threadIdx.x;
     const int64_t lin = xcd_remap(blockIdx.x, a.nblocks);
-    // batch row fastest: the B workgroups of one channel group run back to
-    // back on one XCD, so the group's spectrum is fetched from HBM once and
+    // batch row fastest: the B workgroups of one channel pair run back to
+    // back on one XCD, so the pair's spectrum is fetched from HBM once and
     // then found in that XCD's L2
-    const int64_t groups_per_b = (a.npairs + K - 1) / K;
-    const int64_t nb = a.nblocks / groups_per_b;
-    const int64_t pg = lin / nb;
-    const int64_t b = lin - pg * nb;
-    const int64_t p = pg * K + k;
-    const bool live = p < a.npairs;
-    const int64_t pc = live ? p : a.npairs - 1;  // clamped for address arithmetic
+    const int64_t pc = lin / a.B;
+    const int64_t b = lin - pc * a.B;
     const int64_t c0 = 2 * pc;
     const bool has_b = c0 + 1 < a.d;
     const uint32_t dd = (uint32_t)a.d;
     const uint32_t N = (uint32_t)a.N;
     const int j1 = tau, j2 = tau ? 2 * T - tau : T;
     const float inv2M = 0.5f / (float)M;
-    float* re = smem + k * 2 * LW;
-    float* im = re + LW;
-
-    // IO_DIRECT / IO_TILED address channels-last rows; IO_PAIRMAJOR addresses
-    // [B][pairs][N] runs of PairRaw elements.
-    const int64_t row0 = MODE == IO_PAIRMAJOR ? (b * a.npairs + pc) * a.N * 2 : b * a.N * a.d + c0;
-
-    // Cooperative tile transfer (IO_TILED): index -> (pair kq, sample t);
-    // K consecutive lanes cover the group's K pairs of one row.  Offsets are
-    // elements from the start of batch row b (32-bit: N d is checked).
-    const int64_t brow = b * a.N * a.d;
-    auto tile = [&](auto&& fn) {
-        const int total = (int)a.N * K;
-        for (int idx = threadIdx.x; idx < total; idx += NT) {
-            const int kq = idx % K;
-            const int t = idx / K;
-            const int64_t pq = pg * K + kq;
-            fn(kq, t, pq < a.npairs, (uint32_t)t * dd + (uint32_t)(2 * pq));
-        }
-    };
-    auto load_tile = [&](const IO* base) {
-        base += brow;
-        tile([&](int kq, int t, bool ok, uint32_t off) {
-            const float2 x = ok ? widen_pair<IO>(load_pair_raw(base, off * (uint32_t)sizeof(IO)))
-                                : make_float2(0.0f, 0.0f);
-            smem[kq * 2 * LW + lpad(t)] = x.x;
-            smem[kq * 2 * LW + LW + lpad(t)] = x.y;
-        });
-    };
+    float* re = smem;
+    float* im = smem + LW;
+    const int64_t row0 = b * a.N * a.d + c0;
 
     float2 v[PTS];
-    // ---- stage input
-    if constexpr (MODE == IO_TILED) {
-        load_tile(static_cast<const IO*>(a.u));
-        __syncthreads();
+    const IO* ubase = static_cast<const IO*>(a.u) + row0;
 #pragma unroll
-        for (int q = 0; q < S::Q0; ++q) lds_read_first<R0 / 2, R0, M>(re, im, &v[q * R0], tau + q * T);
-    } else {
-        const IO* ubase = static_cast<const IO*>(a.u) + row0;
-        const uint32_t stride = MODE == IO_PAIRMAJOR ? 2u : dd;  // elements per sample
+    for (int q = 0; q < S::Q0; ++q)
 #pragma unroll
-        for (int q = 0; q < S::Q0; ++q) {
-            const uint32_t lane_off = (uint32_t)(tau + q * T) * stride * (uint32_t)sizeof(IO);
-#pragma unroll
-            for (int r = 0; r < R0 / 2; ++r) {
-                if constexpr (MODE == IO_PAIRMAJOR) {
-                    v[q * R0 + r] = widen_pair<IO>(
-                        load_pair_raw(ubase + (size_t)r * (M / R0) * 2, lane_off));
-                } else {
-                    const uint32_t t = tau + q * T + r * (M / R0);
-                    v[q * R0 + r] = t < N ? load_pair<IO, false>(ubase + (size_t)t * dd, has_b)
-                                          : make_float2(0.0f, 0.0f);
-                }
-            }
+        for (int r = 0; r < R0 / 2; ++r) {
+            const uint32_t t = tau + q * T + r * (M / R0);
+            v[q * R0 + r] = t < N ? load_pair<IO, false>(ubase + (size_t)t * dd, has_b)
+                                  : make_float2(0.0f, 0.0f);
         }
-    }
 
     for (int n = 0; n < a.order; ++n) {
         const SP* spec = static_cast<const SP*>(a.spec) +
                          ((int64_t)n * a.npairs + pc) * (int64_t)(M / 2) * kEntryElems;
         typename EntryRaw<SP>::type ent[S::RL];
-        fwd_transform<M>(v, re, im, a.tw, a.tw_off, tau, j1, j2, n > 0 || MODE == IO_TILED,
+        fwd_transform<M>(v, re, im, a.tw, a.tw_off, tau, j1, j2, n > 0,
                          [&] { load_entries<M, SP>(ent, spec, tau); });
 
         const float Da = a.D[(int64_t)n * a.d + c0];
         const float Db = has_b ? a.D[(int64_t)n * a.d + c0 + 1] : 0.0f;
-        spectral_product<M, SP>(v, ent, tau, (Da + Db) * inv2M, (Da - Db) * inv2M,
-                                sxs + k * 4 * S::RL);
+        spectral_product<M, SP>(v, ent, tau, (Da + Db) * inv2M, (Da - Db) * inv2M, sxs);
 
-        const IO* g = static_cast<const IO*>(a.gates[n]) + (MODE == IO_TILED ? 0 : row0);
-        if constexpr (MODE == IO_TILED) {
-            inv_transform<M>(v, re, im, a.tw, a.tw_off, tau, j1, j2, [] {});
-            __syncthreads();
-            load_tile(g);
-            __syncthreads();
-#pragma unroll
-            for (int q = 0; q < S::Q0; ++q) {
-                float2 gg[R0 / 2];
-                lds_read_first<R0 / 2, R0, M>(re, im, gg, tau + q * T);
-#pragma unroll
-                for (int r = 0; r < R0 / 2; ++r) {
-                    float2& x = v[q * R0 + r];
-                    x = make_float2(x.x * gg[r].x, x.y * gg[r].y);
-                }
-            }
-        } else {
-            typename PairRaw<IO>::type graw[S::Q0][R0 / 2];
-            float2 gv[S::Q0][R0 / 2];
-            inv_transform<M>(v, re, im, a.tw, a.tw_off, tau, j1, j2, [&] {
-                const uint32_t stride = MODE == IO_PAIRMAJOR ? 2u : dd;
-#pragma unroll
-                for (int q = 0; q < S::Q0; ++q) {
-                    const uint32_t lane_off = (uint32_t)(tau + q * T) * stride * (uint32_t)sizeof(IO);
-#pragma unroll
-                    for (int r = 0; r < R0 / 2; ++r) {
-                        if constexpr (MODE == IO_PAIRMAJOR) {
-                            graw[q][r] = load_pair_raw(g + (size_t)r * (M / R0) * 2, lane_off);
-                        } else {
-                            const uint32_t t = tau + q * T + r * (M / R0);
-                            gv[q][r] = t < N ? load_pair<IO, false>(g + (size_t)t * dd, has_b)
-                                             : make_float2(0.0f, 0.0f);
-                        }
-                    }
-                }
-            });
+        const IO* g = static_cast<const IO*>(a.gates[n]) + row0;
+        float2 gv[S::Q0][R0 / 2];
+        inv_transform<M>(v, re, im, a.tw, a.tw_off, tau, j1, j2, [&] {
 #pragma unroll
             for (int q = 0; q < S::Q0; ++q)
 #pragma unroll
                 for (int r = 0; r < R0 / 2; ++r) {
-                    const float2 gg = MODE == IO_PAIRMAJOR ? widen_pair<IO>(graw[q][r]) : gv[q][r];
-                    float2& x = v[q * R0 + r];
-                    x = make_float2(x.x * gg.x, x.y * gg.y);
+                    const uint32_t t = tau + q * T + r * (M / R0);
+                    gv[q][r] = t < N ? load_pair<IO, false>(g + (size_t)t * dd, has_b)
+                                     : make_float2(0.0f, 0.0f);
                 }
-        }
-    }
-
-    // ---- store y
-    if constexpr (MODE == IO_TILED) {
-        __syncthreads();
-#pragma unroll
-        for (int q = 0; q < S::Q0; ++q) lds_write_first<R0 / 2, R0, M>(re, im, &v[q * R0], tau + q * T);
-        __syncthreads();
-        IO* y = static_cast<IO*>(a.y) + brow;
-        tile([&](int kq, int t, bool ok, uint32_t off) {
-            if (ok)
-                store_pair_at(y, off * (uint32_t)sizeof(IO),
-                              make_float2(smem[kq * 2 * LW + lpad(t)],
-                                          smem[kq * 2 * LW + LW + lpad(t)]));
         });
-    } else {
-        if (!live) return;
-        IO* ybase = static_cast<IO*>(a.y) + row0;
 #pragma unroll
-        for (int q = 0; q < S::Q0; ++q) {
-            const uint32_t lane_off =
-                (uint32_t)(tau + q * T) * (MODE == IO_PAIRMAJOR ? 2u : dd) * (uint32_t)sizeof(IO);
+        for (int q = 0; q < S::Q0; ++q)
 #pragma unroll
             for (int r = 0; r < R0 / 2; ++r) {
-                if constexpr (MODE == IO_PAIRMAJOR) {
-                    store_pair_at(ybase + (size_t)r * (M / R0) * 2, lane_off, v[q * R0 + r]);
-                } else {
-                    const uint32_t t = tau + q * T + r * (M / R0);
-                    if (t < N) store_pair<IO, false>(ybase + (size_t)t * dd, v[q * R0 + r], has_b);
-                }
+                float2& x = v[q * R0 + r];
+                x = make_float2(x.x * gv[q][r].x, x.y * gv[q][r].y);
             }
-        }
     }
+
+    IO* ybase = static_cast<IO*>(a.y) + row0;
+#pragma unroll
+    for (int q = 0; q < S::Q0; ++q)
+#pragma unroll
+        for (int r = 0; r < R0 / 2; ++r) {
+            const uint32_t t = tau + q * T + r * (M / R0);
+            if (t < N) store_pair<IO, false>(ybase + (size_t)t * dd, v[q * R0 + r], has_b);
+        }
 }
 
 // Filter spectrum: one workgroup per (filter n, channel pair).
@@ -412,21 +297,11 @@ hyena_status lds1d_real_spectrum_launch(const Lds1dSpecArgs& a, hipStream_t s)
 }
 
 template <int M, typename IO, typename SP>
-hyena_status lds1d_forward_launch(const Lds1dFwdArgs& a, int mode, hipStream_t s)
+hyena_status lds1d_forward_launch(const Lds1dFwdArgs& a, hipStream_t s)
 {
-    const dim3 grid((unsigned)a.nblocks);
-    const auto label = [&] {
-        return kernel_label("hyena_lds1d_forward", M, type_label<IO>(), type_label<SP>(), mode);
-    };
-    if (mode == IO_TILED)
-        HY_LAUNCH(label(), (hyena_lds1d_forward<M, IO, SP, IO_TILED>), grid,
-                  dim3(Lds1dBlock<M, IO_TILED>::THREADS), 0, s, a);
-    else if (mode == IO_PAIRMAJOR)
-        HY_LAUNCH(label(), (hyena_lds1d_forward<M, IO, SP, IO_PAIRMAJOR>), grid,
-                  dim3(Lds1dBlock<M, IO_PAIRMAJOR>::THREADS), 0, s, a);
-    else
-        HY_LAUNCH(label(), (hyena_lds1d_forward<M, IO, SP, IO_DIRECT>), grid,
-                  dim3(Lds1dBlock<M, IO_DIRECT>::THREADS), 0, s, a);
+    HY_LAUNCH(kernel_label("hyena_lds1d_forward", M, type_label<IO>(), type_label<SP>()),
+              (hyena_lds1d_forward<M, IO, SP>), dim3((unsigned)a.nblocks), dim3(FftShape<M>::T), 0,
+              s, a);
     const hipError_t e = hipGetLastError();
     return e == hipSuccess ? HYENA_OK : fail(HYENA_ERR_DEVICE, hipGetErrorString(e));
 }
@@ -451,12 +326,11 @@ hyena_status lds1d_spectrum_launch(const Lds1dSpecArgs& a, hipStream_t s)
     X(512, IO, SP) X(1024, IO, SP) X(2048, IO, SP) X(4096, IO, SP) X(8192, IO, SP)
 
 #define HY_LDS1D_INSTANTIATE(M, IO, SP)                                                      \
-    template hyena_status lds1d_forward_launch<M, IO, SP>(const Lds1dFwdArgs&, int,          \
-                                                          hipStream_t);                      \
+    template hyena_status lds1d_forward_launch<M, IO, SP>(const Lds1dFwdArgs&, hipStream_t);    \
     template hyena_status lds1d_spectrum_launch<M, IO, SP>(const Lds1dSpecArgs&, hipStream_t);
 
 #define HY_LDS1D_EXTERN(M, IO, SP)                                                               \
-    extern template hyena_status lds1d_forward_launch<M, IO, SP>(const Lds1dFwdArgs&, int,       \
+    extern template hyena_status lds1d_forward_launch<M, IO, SP>(const Lds1dFwdArgs&,            \
                                                                  hipStream_t);                   \
     extern template hyena_status lds1d_spectrum_launch<M, IO, SP>(const Lds1dSpecArgs&,          \
                                                                   hipStream_t);

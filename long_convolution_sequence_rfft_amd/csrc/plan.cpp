@@ -182,8 +182,8 @@ hyena_status plan_build(Plan& p, int64_t B, int64_t N, int64_t d, int32_t order,
         const int64_t need = chunk * (fwd_pair > spec_pair ? fwd_pair : spec_pair);
         p.inter_bytes = align_up((size_t)need, 256);
     }
-    if (p.path == HYENA_PATH_LDS1D && (p.lds_io == 2 || p.lds_io == 3)) {
-        // u, every gate and y, pair-major
+    if (p.path == HYENA_PATH_LDS1D && p.lds_io == 3) {
+        // u, every gate and y, staged channel-major
         p.stage_offset = p.inter_offset + p.inter_bytes;
         p.stage_bytes = align_up((size_t)(p.order + 2) * (size_t)B * (size_t)N * (size_t)d *
                                      (io_dtype == HYENA_F32 ? 4u : 2u), 256);

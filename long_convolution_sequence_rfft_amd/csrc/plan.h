@@ -57,12 +57,14 @@ struct Plan {
     int64_t M = 0;       // 1D transform length (power of two >= 2N)
     int64_t npairs = 0;  // channel pairs (two real channels per complex transform)
 
-    // LDS1D: forward radices R0, R1 (1 if absent), RL; inverse runs them reversed.
+    // LDS1D: forward radices R0, R1 (1 if absent), RL of the transform the
+    // kernels run (length M, or M/2 for the single-channel form); the inverse
+    // runs them reversed.
     int32_t R0 = 0, R1 = 1, RL = 0;
-    // LDS1D activation access: 0 direct per-lane, 1 tiled K pairs per
-    // workgroup, 2 pair-major staging in the workspace (transposed in and out)
+    // LDS1D form: 0 channel pairs on channels-last rows, 3 single channels on
+    // activations staged channel-major in the workspace (N = M/2)
     int32_t lds_io = 0;
-    size_t stage_offset = 0, stage_bytes = 0;  // pair-major staging in the workspace
+    size_t stage_offset = 0, stage_bytes = 0;  // channel-major staging in the workspace
 
     // FOURSTEP1D: M = M1 * M2; columns of length M1 (time index t = M2 n1 + n2),
     // rows of length M2.  ROWCOL2D: P1 = 2X (columns), P2 = 2Y (rows).
