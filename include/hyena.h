@@ -90,8 +90,9 @@ typedef enum hyena_path {
 
 /*
  * Create a plan.  B >= 1 batch rows, d >= 1 channels, 1 <= order <= 8.
- * ndims = 1: dims = {N}, 4 <= N <= 65536 (any N; M is the power of two
- *            >= 2N; N == the N argument).
+ * ndims = 1: dims = {N}, 4 <= N <= 524288 (any N; M is the power of two
+ *            >= 2N; N == the N argument).  M <= 16384 runs in one workgroup
+ *            per channel (pair); longer transforms take the four-step path.
  * ndims = 2: dims = {X, Y}, X and Y powers of two in [4, 512]; N must equal
  *            X * Y.
  * io_dtype, spectrum_dtype: hyena_dtype values.  path: hyena_path value.

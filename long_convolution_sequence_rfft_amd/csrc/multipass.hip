@@ -48,8 +48,12 @@ MpGeom base_geom(const Plan& p)
         g.so = p.Y;
         g.tw_step = 0;
     }
+    // pairs per outer workgroup: up to 16 (a 128-byte row of float32 pairs),
+    // and no more than the workgroup's transforms of the outer length
+    const int nf = kMpThreads / threads_per_transform(g.La);
+    const int kp_max = nf < 16 ? nf : 16;
     int kp = 1;
-    while (kp < 16 && kp < p.npairs) kp <<= 1;
+    while (kp < kp_max && kp < p.npairs) kp <<= 1;
     g.kp_log2 = 0;
     while ((1 << g.kp_log2) < kp) ++g.kp_log2;
     g.groups_per_b = (int32_t)((p.npairs + kp - 1) / kp);

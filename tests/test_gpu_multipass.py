@@ -142,3 +142,23 @@ def test_full_size_2d_sampled():
     e = rel_err(y[..., ch], ref)
     say(f"2D 256x256 full-size sampled rel_err={e:.3e}")
     assert e < TOL_F32
+
+
+@pytest.mark.parametrize("N,d", [(100000, 2), (262144, 1), (524288, 1)])
+def test_fourstep_longer_than_64k(N, d):
+    # transforms of 2^18..2^20 points (outer and inner lengths up to 1024)
+    inp = synth.make_1d(B=1, N=N, d=d, order=2, alpha_range=(1e-6, 1e-4), seed=31)
+    y, _, _ = run_gpu(inp)
+    e = rel_err(y, oracle_ref(inp, method=oracle.FFT))
+    say(f"[gpu] N={N} rel err {e:.3e}")
+    assert e < TOL_F32_LONG
+
+
+@pytest.mark.parametrize("X,Y,d", [(512, 512, 2), (4, 512, 3), (512, 8, 2)])
+def test_rowcol2d_largest_sides(X, Y, d):
+    # 1024-point transforms along either axis (at most 8 pairs per outer workgroup)
+    inp = synth.make_2d(B=1, X=X, Y=Y, d=d, order=2, seed=32)
+    y, _, _ = run_gpu(inp)
+    e = rel_err(y, oracle_ref(inp, method=oracle.FFT))
+    say(f"[gpu] {X}x{Y} rel err {e:.3e}")
+    assert e < TOL_F32
