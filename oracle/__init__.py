@@ -15,6 +15,8 @@ Functions follow the pages cited in ``oracle.c``:
     2D convolution on the native grid
   * ``fft`` -- [P2] "Counting the cost" radix-2 FFT
   * ``circular_conv`` -- [P2] "Linear vs circular" (the unpadded contrast)
+  * ``implicit_filter`` -- [P2] "Implicit filters" and "The decay window":
+    taps window(t) * FFN(gamma(t)) from a sine MLP over positions
 
 Every function has at least one pin in ``tests/test_oracle_pins.py`` that does
 not go through this code (printed worked example, numpy routines, closed
@@ -77,6 +79,9 @@ def _load():
             lib.oracle_conv2d_fft.restype = ctypes.c_int
             lib.oracle_hyena2d.argtypes = [i64, i64, i64, i64, i32, p, p, p, p, p, i32]
             lib.oracle_hyena2d.restype = ctypes.c_int
+            lib.oracle_implicit_filter.argtypes = [i64, i64, i32, i32, i32, ctypes.c_double,
+                                                   p, p, p, p, p, p, p, p]
+            lib.oracle_implicit_filter.restype = None
             _lib = lib
     return _lib
 
@@ -173,3 +178,24 @@ def hyena2d(u, gates, K, D, method: int = DIRECT) -> np.ndarray:
     if rc != 0:
         raise MemoryError("oracle_hyena2d failed")
     return y
+
+
+IMPLICIT_MAX_FREQS = 64
+IMPLICIT_MAX_HIDDEN = 256
+
+
+def implicit_filter(N, d, order, omega, W1, b1, W2, b2, W3, b3, alpha) -> np.ndarray:
+    """Taps h [order, d, N] = exp(-alpha t) * FFN(gamma(t)); W1 [H, 2K+1],
+    W2 [H, H], W3 [order*d, H], alpha [order, d] (see oracle.c)."""
+    W1, b1, W2, b2 = _f64(W1), _f64(b1), _f64(W2), _f64(b2)
+    W3, b3, alpha = _f64(W3), _f64(b3), _f64(alpha)
+    H, m = W1.shape
+    K = (m - 1) // 2
+    assert m == 2 * K + 1 and K <= IMPLICIT_MAX_FREQS and H <= IMPLICIT_MAX_HIDDEN
+    assert b1.shape == (H,) and W2.shape == (H, H) and b2.shape == (H,)
+    assert W3.shape == (order * d, H) and b3.shape == (order * d,)
+    assert alpha.shape == (order, d)
+    h = np.empty((order, d, N))
+    _load().oracle_implicit_filter(N, d, order, K, H, float(omega), _ptr(W1), _ptr(b1),
+                                   _ptr(W2), _ptr(b2), _ptr(W3), _ptr(b3), _ptr(alpha), _ptr(h))
+    return h

@@ -370,3 +370,55 @@ int oracle_hyena2d(int64_t B, int64_t X, int64_t Y, int64_t d, int32_t order, co
     free(z); free(w);
     return rc;
 }
+
+/* ------------------------------------------------------------------------ */
+/* Implicit filter ([P2] "Implicit filters: an MLP over positions" and "The  */
+/* decay window")                                                            */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * Filter taps generated by a small MLP over positions instead of stored:
+ *   h_n[c, t] = exp(-alpha[n][c] t) * FFN(gamma(t))[n d + c],  t = 0..N-1
+ * gamma(t) is the positional encoding [t/N, cos(2 pi j t/N), sin(2 pi j t/N)]
+ * for j = 1..K (m = 2K + 1 features, in that order: t/N first, then for each
+ * j its cosine and its sine).  FFN : R^m -> R^(order d) is shared over all t:
+ *   z1 = sin(omega (W1 gamma + b1))      W1 [H][m],  b1 [H]
+ *   z2 = sin(omega (W2 z1 + b2))         W2 [H][H],  b2 [H]
+ *   out = W3 z2 + b3                     W3 [order d][H], b3 [order d]
+ * (the sine activations of [P3] "1. An implicit filter", whose filter network
+ * is a sine MLP; the pages leave depth and width open: two hidden layers).
+ * Output h [order][d][N].
+ */
+void oracle_implicit_filter(int64_t N, int64_t d, int32_t order, int32_t K, int32_t H,
+                            double omega, const double* W1, const double* b1,
+                            const double* W2, const double* b2, const double* W3,
+                            const double* b3, const double* alpha, double* h)
+{
+    const int64_t m = 2 * (int64_t)K + 1;
+    const int64_t nout = (int64_t)order * d;
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < N; ++t) {
+        double g[2 * 64 + 1], z1[256], z2[256];
+        const double tn = (double)t / (double)N;
+        g[0] = tn;
+        for (int64_t j = 1; j <= K; ++j) {
+            g[2 * j - 1] = cos(2.0 * M_PI * (double)j * tn);
+            g[2 * j] = sin(2.0 * M_PI * (double)j * tn);
+        }
+        for (int64_t i = 0; i < H; ++i) {
+            double acc = b1[i];
+            for (int64_t k = 0; k < m; ++k) acc += W1[i * m + k] * g[k];
+            z1[i] = sin(omega * acc);
+        }
+        for (int64_t i = 0; i < H; ++i) {
+            double acc = b2[i];
+            for (int64_t k = 0; k < H; ++k) acc += W2[i * H + k] * z1[k];
+            z2[i] = sin(omega * acc);
+        }
+        for (int64_t o = 0; o < nout; ++o) {
+            double acc = b3[o];
+            for (int64_t k = 0; k < H; ++k) acc += W3[o * H + k] * z2[k];
+            h[o * N + t] = exp(-alpha[o] * (double)t) * acc;
+        }
+    }
+}

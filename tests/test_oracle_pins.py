@@ -441,3 +441,84 @@ def test_inputs_are_seeded_and_reproducible():
     assert np.array_equal(a.u, b.u) and np.array_equal(a.h, b.h)
     c = synth.make_config(0, seed=100)
     assert not np.array_equal(a.u, c.u)
+
+
+# --------------------------------------------------------------------------
+# Implicit filter ([P2] "Implicit filters: an MLP over positions", "The decay
+# window"): h_n[c,t] = exp(-alpha t) FFN(gamma(t))
+# --------------------------------------------------------------------------
+
+def _mlp_weights(rng, K, H, d, order, scale=1.0):
+    m = 2 * K + 1
+    return dict(W1=rng.normal(size=(H, m)) * scale, b1=rng.normal(size=H) * scale,
+                W2=rng.normal(size=(H, H)) * scale / np.sqrt(H), b2=rng.normal(size=H) * scale,
+                W3=rng.normal(size=(order * d, H)) / np.sqrt(H), b3=rng.normal(size=order * d))
+
+
+def test_implicit_filter_constant_network_gives_the_window():
+    # W3 = 0, b3 = 1: the network emits 1 everywhere and h is the decay window
+    rng = np.random.default_rng(40)
+    N, d, order, K, H = 300, 3, 2, 4, 6
+    w = _mlp_weights(rng, K, H, d, order)
+    w["W3"][:] = 0.0
+    w["b3"][:] = 1.0
+    alpha = rng.uniform(0.0, 0.05, size=(order, d))
+    h = oracle.implicit_filter(N, d, order, 3.0, alpha=alpha, **w)
+    t = np.arange(N)
+    assert _rel(h, np.exp(-alpha[:, :, None] * t)) < 1e-15
+
+
+def test_implicit_filter_window_factors_out():
+    # h(alpha) / h(0) = exp(-alpha t) for any network
+    rng = np.random.default_rng(41)
+    N, d, order, K, H = 128, 2, 2, 3, 5
+    w = _mlp_weights(rng, K, H, d, order)
+    alpha = rng.uniform(0.0, 0.1, size=(order, d))
+    h0 = oracle.implicit_filter(N, d, order, 2.0, alpha=np.zeros((order, d)), **w)
+    h1 = oracle.implicit_filter(N, d, order, 2.0, alpha=alpha, **w)
+    assert _rel(h1, h0 * np.exp(-alpha[:, :, None] * np.arange(N))) < 1e-13
+
+
+def test_implicit_filter_scalar_network_closed_form():
+    # K = 0 (gamma = t/N), H = 1, one channel: the two sine layers written out
+    N, w1, c1, w2, c2, w3, c3, om, al = 50, 1.7, -0.3, 0.9, 0.25, -1.3, 0.4, 2.5, 0.02
+    h = oracle.implicit_filter(N, 1, 1, om, W1=[[w1]], b1=[c1], W2=[[w2]], b2=[c2],
+                               W3=[[w3]], b3=[c3], alpha=[[al]])
+    t = np.arange(N)
+    ref = np.exp(-al * t) * (w3 * np.sin(om * (w2 * np.sin(om * (w1 * t / N + c1)) + c2)) + c3)
+    assert _rel(h[0, 0], ref) < 1e-14
+
+
+def test_implicit_filter_positional_encoding_layout():
+    # W1 = W2 = I and a tiny omega: sin(omega x) ~ omega x, so output o is
+    # omega^2 gamma_o(t): t/N, then cos and sin of 2 pi j t/N for j = 1, 2, ...
+    K, N, om = 3, 40, 1e-5
+    m = 2 * K + 1
+    h = oracle.implicit_filter(N, m, 1, om, W1=np.eye(m), b1=np.zeros(m), W2=np.eye(m),
+                               b2=np.zeros(m), W3=np.eye(m), b3=np.zeros(m),
+                               alpha=np.zeros((1, m)))[0] / om ** 2
+    tn = np.arange(N) / N
+    expect = [tn]
+    for j in range(1, K + 1):
+        expect += [np.cos(2 * np.pi * j * tn), np.sin(2 * np.pi * j * tn)]
+    assert np.max(np.abs(h - np.array(expect))) < 1e-9
+
+
+def test_implicit_filter_small_omega_is_the_matrix_product():
+    # omega -> 0 with b2 = b3 = 0: h ~ omega^2 exp(-alpha t) W3 W2 (W1 gamma + b1),
+    # evaluated here with numpy matrix products
+    rng = np.random.default_rng(42)
+    N, d, order, K, H, om = 64, 3, 2, 5, 7, 1e-4
+    w = _mlp_weights(rng, K, H, d, order)
+    w["b2"][:] = 0.0
+    w["b3"][:] = 0.0
+    alpha = rng.uniform(0.0, 0.05, size=(order, d))
+    h = oracle.implicit_filter(N, d, order, om, alpha=alpha, **w)
+    tn = np.arange(N) / N
+    feats = [tn]
+    for j in range(1, K + 1):
+        feats += [np.cos(2 * np.pi * j * tn), np.sin(2 * np.pi * j * tn)]
+    gamma = np.array(feats)  # [m, N]
+    lin = om ** 2 * (w["W3"] @ (w["W2"] @ (w["W1"] @ gamma + w["b1"][:, None])))
+    ref = lin.reshape(order, d, N) * np.exp(-alpha[:, :, None] * np.arange(N))
+    assert _rel(h, ref) < 1e-7
