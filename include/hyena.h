@@ -137,6 +137,51 @@ hyena_status hyena_forward(hyena_plan_t plan, const void* u, const void* const* 
                            void* stream);
 
 /*
+ * Implicit filters ("Hyena -- Long Convolutions Math", sections "Implicit
+ * filters: an MLP over positions" and "The decay window"): instead of taps,
+ * the caller passes a small sine MLP shared over positions, and
+ *   h_n[c, t] = exp(-alpha[n][c] t) * FFN(gamma(t))[n d + c],  t = 0..N-1,
+ *   gamma(t)  = [t/N, cos(2 pi t/N), sin(2 pi t/N), ..., cos(2 pi K t/N),
+ *                sin(2 pi K t/N)]                    (m = 2K + 1 features)
+ *   z1 = sin(omega (W1 gamma + b1)),  z2 = sin(omega (W2 z1 + b2)),
+ *   FFN(gamma) = W3 z2 + b3.
+ * All weights are float32 device arrays, row-major: W1 [H][m], b1 [H],
+ * W2 [H][H], b2 [H], W3 [order d][H], b3 [order d], alpha [order][d].
+ * 0 <= K <= 64, 1 <= H <= 256.  Only ndims = 1 plans.
+ */
+typedef struct hyena_implicit_filter {
+    int32_t n_freqs; /* K */
+    int32_t hidden;  /* H */
+    float omega;
+    const float* W1;
+    const float* b1;
+    const float* W2;
+    const float* b2;
+    const float* W3;
+    const float* b3;
+    const float* alpha;
+} hyena_implicit_filter;
+
+/* Bytes of the caller-owned scratch buffer hyena_filter_spectrum_implicit
+ * needs for this plan and hidden width (hidden features of every position;
+ * on paths other than the single-channel one also the taps themselves). */
+hyena_status hyena_implicit_scratch_bytes(hyena_plan_t plan, int32_t hidden, size_t* bytes);
+
+/*
+ * hyena_filter_spectrum with the taps generated from `f` on the device.  On
+ * the single-channel path (N = M/2 <= 8192) the taps are evaluated inside the
+ * spectrum kernel and never stored; elsewhere they are written to `scratch`
+ * (in the plan's io dtype) and transformed as by hyena_filter_spectrum.
+ * scratch: device buffer of hyena_implicit_scratch_bytes, 16-byte aligned,
+ * not shared with concurrently running calls.  `f` is read on the host
+ * during the call; the arrays it points to must stay alive until the stream
+ * work completes.
+ */
+hyena_status hyena_filter_spectrum_implicit(hyena_plan_t plan, const hyena_implicit_filter* f,
+                                            void* H, void* workspace, void* scratch,
+                                            void* stream);
+
+/*
  * Test/inspection helper: expand H into natural-order transfer functions,
  * complex64 (re, im) pairs, unscaled (the plain DFT of the zero-padded
  * filter).  ndims = 1: [order][d][M/2 + 1] bins k = 0..M/2.

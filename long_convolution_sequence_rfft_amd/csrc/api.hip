@@ -150,6 +150,46 @@ hyena_status hyena_forward(hyena_plan_t plan, const void* u, const void* const* 
     }
 }
 
+hyena_status hyena_implicit_scratch_bytes(hyena_plan_t plan, int32_t hidden, size_t* bytes)
+{
+    if (plan == nullptr || bytes == nullptr)
+        return fail(HYENA_ERR_INVALID_ARGUMENT, "plan or output pointer is NULL");
+    if (plan->p.ndims != 1) return fail(HYENA_ERR_UNSUPPORTED, "implicit filters need ndims = 1");
+    if (hidden < 1 || hidden > 256)
+        return fail(HYENA_ERR_UNSUPPORTED, "implicit filter: hidden must be in 1..256");
+    *bytes = hy::implicit_scratch_bytes(plan->p, hidden);
+    return HYENA_OK;
+}
+
+hyena_status hyena_filter_spectrum_implicit(hyena_plan_t plan, const hyena_implicit_filter* f,
+                                            void* H, void* workspace, void* scratch, void* stream)
+{
+    if (plan == nullptr) return fail(HYENA_ERR_INVALID_ARGUMENT, "plan is NULL");
+    const hy::Plan& p = plan->p;
+    if (p.ndims != 1) return fail(HYENA_ERR_UNSUPPORTED, "implicit filters need ndims = 1");
+    if (f == nullptr || H == nullptr || scratch == nullptr)
+        return fail(HYENA_ERR_INVALID_ARGUMENT, "filter description, H or scratch is NULL");
+    if (f->W1 == nullptr || f->b1 == nullptr || f->W2 == nullptr || f->b2 == nullptr ||
+        f->W3 == nullptr || f->b3 == nullptr || f->alpha == nullptr)
+        return fail(HYENA_ERR_INVALID_ARGUMENT, "an implicit-filter weight pointer is NULL");
+    if (f->n_freqs < 0 || f->n_freqs > 64)
+        return fail(HYENA_ERR_UNSUPPORTED, "implicit filter: n_freqs must be in 0..64");
+    if (f->hidden < 1 || f->hidden > 256)
+        return fail(HYENA_ERR_UNSUPPORTED, "implicit filter: hidden must be in 1..256");
+    if (!aligned16(H) || !aligned16(scratch))
+        return fail(HYENA_ERR_INVALID_ARGUMENT, "H and scratch must be 16-byte aligned");
+    const size_t nscratch = hy::implicit_scratch_bytes(p, f->hidden);
+    if (overlaps(H, p.spectrum_bytes, scratch, nscratch))
+        return fail(HYENA_ERR_INVALID_ARGUMENT, "H overlaps the scratch");
+    hyena_status st = check_ws(p, workspace);
+    if (st != HYENA_OK) return st;
+    if (overlaps(workspace, p.workspace_bytes, H, p.spectrum_bytes))
+        return fail(HYENA_ERR_INVALID_ARGUMENT, "H overlaps the workspace");
+    if (overlaps(workspace, p.workspace_bytes, scratch, nscratch))
+        return fail(HYENA_ERR_INVALID_ARGUMENT, "the scratch overlaps the workspace");
+    return hy::launch_implicit_spectrum(p, *f, H, workspace, scratch, stream);
+}
+
 hyena_status hyena_spectrum_export(hyena_plan_t plan, const void* H, void* natural, void* stream)
 {
     if (plan == nullptr) return fail(HYENA_ERR_INVALID_ARGUMENT, "plan is NULL");

@@ -196,12 +196,12 @@ hyena_status real_fwd_by_l(int64_t L, const Lds1dFwdArgs& a, hipStream_t s)
     }
 }
 
-template <typename IO, typename SP>
+template <typename IO, typename SP, bool IMPL = false>
 hyena_status real_spec_by_l(int64_t L, const Lds1dSpecArgs& a, hipStream_t s)
 {
     switch (L) {
 #define HY_CASE(LL, I, S_) \
-    case LL: return lds1d_real_spectrum_launch<LL, IO, SP>(a, s);
+    case LL: return lds1d_real_spectrum_launch<LL, IO, SP, IMPL>(a, s);
         HY_LDS1D_REAL_SIZES(HY_CASE, IO, SP)
 #undef HY_CASE
         default: return fail(HYENA_ERR_UNSUPPORTED, "LDS1D: unsupported single-channel length");

@@ -120,4 +120,9 @@ hyena_status launch_rowcol2d_forward(const Plan& p, const void* u, const void* c
                                      void* stream);
 hyena_status launch_rowcol2d_export(const Plan& p, const void* H, void* out, void* stream);
 
+// implicit.hip
+size_t implicit_scratch_bytes(const Plan& p, int32_t hidden);
+hyena_status launch_implicit_spectrum(const Plan& p, const hyena_implicit_filter& f, void* H,
+                                      void* ws, void* scratch, void* stream);
+
 }  // namespace hy

@@ -34,8 +34,17 @@ EXPORTED_SYMBOLS = (
     "hyena_plan_create", "hyena_plan_query", "hyena_workspace_init", "hyena_filter_spectrum",
     "hyena_forward", "hyena_spectrum_export", "hyena_plan_destroy", "hyena_status_string",
     "hyena_last_error", "hyena_timing_begin", "hyena_timing_end", "hyena_timing_kernel",
-    "hyena_timing_release",
+    "hyena_timing_release", "hyena_implicit_scratch_bytes", "hyena_filter_spectrum_implicit",
 )
+
+
+class ImplicitFilter(ctypes.Structure):
+    """hyena_implicit_filter: weights of the sine MLP that generates the taps
+    (device pointers as ints; see include/hyena.h)."""
+    _fields_ = [("n_freqs", ctypes.c_int32), ("hidden", ctypes.c_int32),
+                ("omega", ctypes.c_float), ("W1", ctypes.c_void_p), ("b1", ctypes.c_void_p),
+                ("W2", ctypes.c_void_p), ("b2", ctypes.c_void_p), ("W3", ctypes.c_void_p),
+                ("b3", ctypes.c_void_p), ("alpha", ctypes.c_void_p)]
 
 _lock = threading.Lock()
 _lib = None
@@ -77,10 +86,14 @@ def load():
                                                 ctypes.POINTER(i64)] + \
                 [ctypes.POINTER(ctypes.c_double)] * 3
             lib.hyena_timing_release.argtypes = []
+            lib.hyena_implicit_scratch_bytes.argtypes = [p, i32, ctypes.POINTER(sz)]
+            lib.hyena_filter_spectrum_implicit.argtypes = [p, ctypes.POINTER(ImplicitFilter), p, p,
+                                                           p, p]
             for name in ("hyena_plan_create", "hyena_plan_query", "hyena_workspace_init",
                          "hyena_filter_spectrum", "hyena_forward", "hyena_spectrum_export",
                          "hyena_plan_destroy", "hyena_timing_begin", "hyena_timing_end",
-                         "hyena_timing_kernel", "hyena_timing_release"):
+                         "hyena_timing_kernel", "hyena_timing_release",
+                         "hyena_implicit_scratch_bytes", "hyena_filter_spectrum_implicit"):
                 getattr(lib, name).restype = ctypes.c_int
             _lib = lib
     return _lib
@@ -142,6 +155,18 @@ def hyena_filter_spectrum(plan, h, H, workspace, stream=0):
 def hyena_forward(plan, u, gates, H, D, y, workspace, stream=0):
     arr = (ctypes.c_void_p * max(1, len(gates)))(*gates)
     return load().hyena_forward(plan, u, arr, H, D, y, workspace, stream)
+
+
+def hyena_implicit_scratch_bytes(plan, hidden):
+    """Returns (status, bytes)."""
+    n = ctypes.c_size_t()
+    st = load().hyena_implicit_scratch_bytes(plan, int(hidden), ctypes.byref(n))
+    return st, n.value
+
+
+def hyena_filter_spectrum_implicit(plan, f, H, workspace, scratch, stream=0):
+    return load().hyena_filter_spectrum_implicit(plan, ctypes.byref(f) if f is not None else None,
+                                                 H, workspace, scratch, stream)
 
 
 def hyena_spectrum_export(plan, H, natural, stream=0):
@@ -233,6 +258,28 @@ class Plan:
         _check(hyena_filter_spectrum(self.handle, h.data_ptr(), H.data_ptr(),
                                      self.workspace.data_ptr(), self.stream()),
                "hyena_filter_spectrum")
+        return H
+
+    def spectrum_implicit(self, W1, b1, W2, b2, W3, b3, alpha, omega, H=None):
+        """Spectrum from an implicit filter; weights are float32 device tensors
+        W1 [hidden, 2K+1], b1 [hidden], W2 [hidden, hidden], b2 [hidden],
+        W3 [order*d, hidden], b3 [order*d], alpha [order, d]."""
+        ws = [W1, b1, W2, b2, W3, b3, alpha]
+        for t in ws:
+            if t.dtype != self.torch.float32 or not t.is_contiguous() or t.device != self.device:
+                raise ValueError(f"implicit-filter weights must be contiguous float32 on {self.device}")
+        hidden, m = W1.shape
+        f = ImplicitFilter((m - 1) // 2, hidden, float(omega), *[t.data_ptr() for t in ws])
+        st, nbytes = hyena_implicit_scratch_bytes(self.handle, hidden)
+        _check(st, "hyena_implicit_scratch_bytes")
+        scratch = self.torch.empty(max(nbytes, 256), dtype=self.torch.uint8, device=self.device)
+        if H is None:
+            H = self.torch.empty(self.spectrum_bytes, dtype=self.torch.uint8, device=self.device)
+        _check(hyena_filter_spectrum_implicit(self.handle, f, H.data_ptr(),
+                                              self.workspace.data_ptr(), scratch.data_ptr(),
+                                              self.stream()),
+               "hyena_filter_spectrum_implicit")
+        self._implicit_scratch = scratch  # alive until the stream work is done
         return H
 
     def forward(self, u, gates, H, D, y=None):

@@ -158,3 +158,45 @@ def make_config(idx: int, seed: int | None = None, **override) -> Inputs:
                        cfg["dtype"], seed)
     return make_2d(cfg["B"], cfg["X"], cfg["Y"], cfg["d"], cfg["order"], cfg["sigma_range"],
                    cfg["dtype"], seed)
+
+
+@dataclass
+class ImplicitWeights:
+    """Weights of the implicit filter's sine MLP, stored float32 (the oracle
+    gets the same values upcast)."""
+    K: int
+    H: int
+    omega: float
+    W1: np.ndarray
+    b1: np.ndarray
+    W2: np.ndarray
+    b2: np.ndarray
+    W3: np.ndarray
+    b3: np.ndarray
+    alpha: np.ndarray
+
+    def arrays(self):
+        return dict(W1=self.W1, b1=self.b1, W2=self.W2, b2=self.b2, W3=self.W3, b3=self.b3,
+                    alpha=self.alpha)
+
+
+def make_implicit(d: int, order: int, K: int = 8, H: int = 64, omega: float = 8.0,
+                  alpha_range=(1e-4, 1e-2), seed: int = 0) -> ImplicitWeights:
+    """Random (untrained) sine-MLP weights: uniform first layer in
+    [-1/m, 1/m], hidden and output layers uniform in +-sqrt(6/H)/omega and
+    +-sqrt(6/H), biases uniform in [-0.5, 0.5] (first two) and N(0, 0.1)
+    (output), decay rates uniform in alpha_range.  Draw order: W1, b1, W2, b2,
+    W3, b3, alpha."""
+    rng = np.random.default_rng(seed)
+    m = 2 * K + 1
+    W1 = rng.uniform(-1.0 / m, 1.0 / m, size=(H, m))
+    b1 = rng.uniform(-0.5, 0.5, size=H)
+    lim = np.sqrt(6.0 / H)
+    W2 = rng.uniform(-lim / omega, lim / omega, size=(H, H))
+    b2 = rng.uniform(-0.5, 0.5, size=H)
+    W3 = rng.uniform(-lim, lim, size=(order * d, H))
+    b3 = rng.normal(0.0, 0.1, size=order * d)
+    alpha = rng.uniform(*alpha_range, size=(order, d))
+    f32 = lambda a: np.ascontiguousarray(a, dtype=np.float32)
+    return ImplicitWeights(K, H, float(np.float32(omega)), f32(W1), f32(b1), f32(W2), f32(b2),
+                           f32(W3), f32(b3), f32(alpha))

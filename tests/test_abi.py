@@ -186,3 +186,34 @@ def test_timing_argument_errors():
     assert lib.hyena_timing_kernel(0, None, None, None, None, None) == hyena.HYENA_ERR_INVALID_ARGUMENT
     assert "out of range" in hyena.hyena_last_error()
     hyena.hyena_timing_release()
+
+
+def test_implicit_scratch_sizes_and_validation():
+    # single-channel path: hidden features only (N x hidden rounded up to 4)
+    _, plan = hyena.hyena_plan_create(2, 2048, 6, 2, [2048])
+    st, n = hyena.hyena_implicit_scratch_bytes(plan, 62)
+    assert st == hyena.HYENA_OK and n == 2048 * 64 * 4
+    assert hyena.hyena_implicit_scratch_bytes(plan, 0)[0] == hyena.HYENA_ERR_UNSUPPORTED
+    assert hyena.hyena_implicit_scratch_bytes(plan, 257)[0] == hyena.HYENA_ERR_UNSUPPORTED
+    f = hyena.ImplicitFilter(8, 64, 8.0, 16, 16, 16, 16, 16, 16, 16)
+    # NULL H, NULL weights, out-of-range sizes: rejected before any GPU work
+    assert hyena.hyena_filter_spectrum_implicit(plan, f, None, 16, 16) == \
+        hyena.HYENA_ERR_INVALID_ARGUMENT
+    assert hyena.hyena_filter_spectrum_implicit(plan, None, 16, 16, 16) == \
+        hyena.HYENA_ERR_INVALID_ARGUMENT
+    bad = hyena.ImplicitFilter(65, 64, 8.0, 16, 16, 16, 16, 16, 16, 16)
+    assert hyena.hyena_filter_spectrum_implicit(plan, bad, 16, 16, 16) == \
+        hyena.HYENA_ERR_UNSUPPORTED
+    nul = hyena.ImplicitFilter(8, 64, 8.0, 16, 16, None, 16, 16, 16, 16)
+    assert hyena.hyena_filter_spectrum_implicit(plan, nul, 16, 16, 16) == \
+        hyena.HYENA_ERR_INVALID_ARGUMENT
+    hyena.hyena_plan_destroy(plan)
+    # other paths also hold the taps: + order * d * N * 4 bytes
+    _, plan = hyena.hyena_plan_create(1, 20000, 3, 2, [20000])
+    st, n = hyena.hyena_implicit_scratch_bytes(plan, 64)
+    assert n == 20000 * 64 * 4 + (2 * 3 * 20000 * 4 + 255) // 256 * 256
+    hyena.hyena_plan_destroy(plan)
+    # grids have no implicit filters here
+    _, plan = hyena.hyena_plan_create(1, 64, 2, 1, [8, 8])
+    assert hyena.hyena_implicit_scratch_bytes(plan, 64)[0] == hyena.HYENA_ERR_UNSUPPORTED
+    hyena.hyena_plan_destroy(plan)
