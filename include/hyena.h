@@ -72,9 +72,13 @@ typedef enum hyena_status {
     HYENA_ERR_DEVICE = 4            /* a HIP launch or query failed */
 } hyena_status;
 
+/* Storage types.  HYENA_F16 (IEEE binary16, round to nearest even on store;
+ * magnitudes above 65504 become infinite) is an io_dtype only and takes a
+ * float32 spectrum. */
 typedef enum hyena_dtype {
     HYENA_F32 = 0,
-    HYENA_BF16 = 1
+    HYENA_BF16 = 1,
+    HYENA_F16 = 2
 } hyena_dtype;
 
 /* Which kernel family runs the transform.  AUTO picks: LDS1D when ndims = 1

@@ -10,6 +10,7 @@
 //   other paths:           hyena_implicit_taps writes the taps to the scratch
 //                          in the plan's storage type, then the plan's usual
 //                          spectrum launch transforms them.
+#include "dispatch.h"
 #include "lds1d_kernels.h"
 
 namespace hy {
@@ -17,6 +18,7 @@ namespace hy {
 HY_LDS1D_REAL_SIZES(HY_LDS1D_REAL_EXTERN, float, float)
 HY_LDS1D_REAL_SIZES(HY_LDS1D_REAL_EXTERN, uint16_t, uint16_t)
 HY_LDS1D_REAL_SIZES(HY_LDS1D_REAL_EXTERN, uint16_t, float)
+HY_LDS1D_REAL_SIZES(HY_LDS1D_REAL_EXTERN, _Float16, float)
 
 namespace {
 
@@ -168,26 +170,26 @@ hyena_status launch_implicit_spectrum(const Plan& p, const hyena_implicit_filter
                              (int32_t)p.seg[3].off};
         a.imp = im;
         const int64_t L = p.M / 2;
-        hyena_status r = HYENA_ERR_UNSUPPORTED;
-        switch (L) {
-#define HY_CASE(LL, I_, S_)                                                                  \
-    case LL:                                                                                 \
-        if (p.io_dtype == HYENA_F32) r = lds1d_real_spectrum_launch<LL, float, float, true>(a, s); \
-        else if (p.spec_dtype == HYENA_BF16)                                                 \
-            r = lds1d_real_spectrum_launch<LL, uint16_t, uint16_t, true>(a, s);              \
-        else r = lds1d_real_spectrum_launch<LL, uint16_t, float, true>(a, s);                 \
-        break;
-            HY_LDS1D_REAL_SIZES(HY_CASE, 0, 0)
+        return by_storage(p, [&](auto io, auto sp) -> hyena_status {
+            using IO = typename decltype(io)::type;
+            using SP = typename decltype(sp)::type;
+            switch (L) {
+#define HY_CASE(LL, I_, S_) \
+    case LL: return lds1d_real_spectrum_launch<LL, IO, SP, true>(a, s);
+                HY_LDS1D_REAL_SIZES(HY_CASE, 0, 0)
 #undef HY_CASE
-            default: return fail(HYENA_ERR_UNSUPPORTED, "implicit filter: unsupported length");
-        }
-        return r;
+                default: return fail(HYENA_ERR_UNSUPPORTED, "implicit filter: unsupported length");
+            }
+        });
     }
     char* taps = static_cast<char*>(scratch) + align256((size_t)p.N * (size_t)h.hp * 4u);
     const dim3 grid((unsigned)((p.N + 255) / 256), (unsigned)(p.order * p.d));
     if (p.io_dtype == HYENA_F32)
         HY_LAUNCH(kernel_label("hyena_implicit_taps", "float"), hyena_implicit_taps<float>, grid,
                   dim3(256), 0, s, im, reinterpret_cast<float*>(taps), p.N);
+    else if (p.io_dtype == HYENA_F16)
+        HY_LAUNCH(kernel_label("hyena_implicit_taps", "_Float16"), hyena_implicit_taps<_Float16>,
+                  grid, dim3(256), 0, s, im, reinterpret_cast<_Float16*>(taps), p.N);
     else
         HY_LAUNCH(kernel_label("hyena_implicit_taps", "unsigned short"), hyena_implicit_taps<uint16_t>,
                   grid, dim3(256), 0, s, im, reinterpret_cast<uint16_t*>(taps), p.N);

@@ -1,6 +1,7 @@
 // lds1d.hip -- launch side of the single-workgroup path (kernels in
 // lds1d_kernels.h, instantiated per storage type in lds1d_f32.hip and
 // lds1d_bf16.hip), the spectrum export and the twiddle-table writer.
+#include "dispatch.h"
 #include "lds1d_kernels.h"
 
 namespace hy {
@@ -12,6 +13,8 @@ HY_LDS1D_SIZES(HY_LDS1D_EXTERN, uint16_t, float)
 HY_LDS1D_REAL_SIZES(HY_LDS1D_REAL_EXTERN, float, float)
 HY_LDS1D_REAL_SIZES(HY_LDS1D_REAL_EXTERN, uint16_t, uint16_t)
 HY_LDS1D_REAL_SIZES(HY_LDS1D_REAL_EXTERN, uint16_t, float)
+HY_LDS1D_SIZES(HY_LDS1D_EXTERN, _Float16, float)
+HY_LDS1D_REAL_SIZES(HY_LDS1D_REAL_EXTERN, _Float16, float)
 
 // ---------------------------------------------------------------------------
 // Twiddle tables: double-precision roots of unity rounded once to float.
@@ -491,17 +494,11 @@ hyena_status launch_lds1d_forward(const Plan& p, const void* u, const void* cons
         const hyena_status r = stage_plan(p, st, 1 + p.order, true, s);
         if (r != HYENA_OK) return r;
     }
-    hyena_status r;
-    if (staged) {
-        const int64_t L = p.M / 2;
-        if (p.io_dtype == HYENA_F32) r = real_fwd_by_l<float, float>(L, a, s);
-        else if (p.spec_dtype == HYENA_BF16) r = real_fwd_by_l<uint16_t, uint16_t>(L, a, s);
-        else r = real_fwd_by_l<uint16_t, float>(L, a, s);
-    } else {
-        if (p.io_dtype == HYENA_F32) r = fwd_by_m<float, float>(p.M, a, s);
-        else if (p.spec_dtype == HYENA_BF16) r = fwd_by_m<uint16_t, uint16_t>(p.M, a, s);
-        else r = fwd_by_m<uint16_t, float>(p.M, a, s);
-    }
+    const hyena_status r = by_storage(p, [&](auto io, auto sp) {
+        using IO = typename decltype(io)::type;
+        using SP = typename decltype(sp)::type;
+        return staged ? real_fwd_by_l<IO, SP>(p.M / 2, a, s) : fwd_by_m<IO, SP>(p.M, a, s);
+    });
     if (r != HYENA_OK || !staged) return r;
     StageArgs out{};
     out.B = p.B;
@@ -524,17 +521,16 @@ hyena_status launch_lds1d_spectrum(const Plan& p, const void* h, void* H, const 
     a.nblocks = (int64_t)p.order * p.npairs;
     a.tw_off = lds1d_offsets(p);
     const hipStream_t s = (hipStream_t)stream;
-    if (p.lds_io == IO_REAL) {
-        const int64_t L = p.M / 2;
+    const bool real = p.lds_io == IO_REAL;
+    if (real) {
         a.nblocks = (int64_t)p.order * p.d;
         a.twm = static_cast<const float2*>(ws) + p.seg[4].off;
-        if (p.io_dtype == HYENA_F32) return real_spec_by_l<float, float>(L, a, s);
-        if (p.spec_dtype == HYENA_BF16) return real_spec_by_l<uint16_t, uint16_t>(L, a, s);
-        return real_spec_by_l<uint16_t, float>(L, a, s);
     }
-    if (p.io_dtype == HYENA_F32) return spec_by_m<float, float>(p.M, a, s);
-    if (p.spec_dtype == HYENA_BF16) return spec_by_m<uint16_t, uint16_t>(p.M, a, s);
-    return spec_by_m<uint16_t, float>(p.M, a, s);
+    return by_storage(p, [&](auto io, auto sp) {
+        using IO = typename decltype(io)::type;
+        using SP = typename decltype(sp)::type;
+        return real ? real_spec_by_l<IO, SP>(p.M / 2, a, s) : spec_by_m<IO, SP>(p.M, a, s);
+    });
 }
 
 }  // namespace hy

@@ -7,6 +7,7 @@ namespace hy {
 
 HY_MP_LENGTHS(HY_MP_OUTER_INST, float, extern)
 HY_MP_LENGTHS(HY_MP_OUTER_INST, uint16_t, extern)
+HY_MP_LENGTHS(HY_MP_OUTER_INST, _Float16, extern)
 HY_MP_LENGTHS(HY_MP_INNER_INST, float, extern)
 HY_MP_LENGTHS(HY_MP_INNER_INST, uint16_t, extern)
 
@@ -97,8 +98,9 @@ hyena_status inner_go(int L, int mode, bool half_b, const InnerArgs& a, int64_t 
 hyena_status outer(const Plan& p, int mode, bool half_spec, const OuterArgs& a, int64_t nb,
                    hipStream_t s)
 {
-    return p.io_dtype == HYENA_F32 ? outer_go<float>(a.g.La, mode, half_spec, a, nb, s)
-                                   : outer_go<uint16_t>(a.g.La, mode, half_spec, a, nb, s);
+    if (p.io_dtype == HYENA_F32) return outer_go<float>(a.g.La, mode, half_spec, a, nb, s);
+    if (p.io_dtype == HYENA_F16) return outer_go<_Float16>(a.g.La, mode, half_spec, a, nb, s);
+    return outer_go<uint16_t>(a.g.La, mode, half_spec, a, nb, s);
 }
 
 hyena_status inner(const Plan& p, int mode, const InnerArgs& a, int64_t nb, hipStream_t s)

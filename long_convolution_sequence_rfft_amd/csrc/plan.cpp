@@ -69,11 +69,11 @@ hyena_status plan_build(Plan& p, int64_t B, int64_t N, int64_t d, int32_t order,
     if (dims == nullptr) return fail(HYENA_ERR_INVALID_ARGUMENT, "dims is NULL");
     if (order < 1 || order > kMaxOrder)
         return fail(HYENA_ERR_UNSUPPORTED, "order must be in 1..8");
-    if (io_dtype != HYENA_F32 && io_dtype != HYENA_BF16)
+    if (io_dtype != HYENA_F32 && io_dtype != HYENA_BF16 && io_dtype != HYENA_F16)
         return fail(HYENA_ERR_UNSUPPORTED, "unknown io_dtype");
     if (spec_dtype != HYENA_F32 && spec_dtype != HYENA_BF16)
         return fail(HYENA_ERR_UNSUPPORTED, "unknown spectrum_dtype");
-    if (io_dtype == HYENA_F32 && spec_dtype == HYENA_BF16)
+    if (io_dtype != HYENA_BF16 && spec_dtype == HYENA_BF16)
         return fail(HYENA_ERR_UNSUPPORTED, "a bfloat16 spectrum needs bfloat16 io");
     if (path < HYENA_PATH_AUTO || path > HYENA_PATH_ROWCOL2D)
         return fail(HYENA_ERR_UNSUPPORTED, "unknown path");

@@ -35,7 +35,7 @@ struct FftShape {
 };
 
 // ---------------------------------------------------------------------------
-// storage access (float32 or bfloat16 stored as uint16_t)
+// storage access (float32, bfloat16 stored as uint16_t, or _Float16)
 //
 // Global accesses take a wave-uniform base pointer and a 32-bit per-lane byte
 // offset, which maps onto the scalar-base + vector-offset addressing form
@@ -52,32 +52,75 @@ __device__ __forceinline__ T& at_bytes(void* base, uint32_t off)
     return *reinterpret_cast<T*>(static_cast<char*>(base) + off);
 }
 
+// Storage types: float (float32), uint16_t (bfloat16 bits) and _Float16
+// (IEEE binary16).  Two 16-bit values travel as one dword, the first in the
+// low half.
+template <typename IO>
+constexpr bool is_bf16() { return sizeof(IO) == 2 && !__is_same(IO, _Float16); }
+
+__device__ __forceinline__ float f16_bits_to_f32(uint32_t b)
+{
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)b);
+}
+__device__ __forceinline__ uint32_t f32_to_f16_bits(float f)
+{
+    // hardware conversion, round to nearest even; beyond 65504 gives +-inf
+    return __builtin_bit_cast(uint16_t, (_Float16)f);
+}
+
 template <typename IO>
 __device__ __forceinline__ float ld1(const IO* p)
 {
     if constexpr (sizeof(IO) == 4) return *p;
-    else return bf16_to_f32(*p);
+    else if constexpr (is_bf16<IO>()) return bf16_to_f32(*p);
+    else return (float)*p;
 }
 
 template <typename IO>
 __device__ __forceinline__ void st1(IO* p, float v)
 {
     if constexpr (sizeof(IO) == 4) *p = v;
-    else *p = f32_to_bf16(v);
+    else if constexpr (is_bf16<IO>()) *p = f32_to_bf16(v);
+    else *p = (_Float16)v;
+}
+
+// Raw channel-pair (or sample-pair) value as stored (float2 for f32, one
+// dword for two 16-bit values); widened at use so prefetched values occupy as
+// few VGPRs as possible.
+template <typename IO>
+struct PairRaw {
+    using type = uint32_t;
+};
+template <>
+struct PairRaw<float> {
+    using type = float2;
+};
+
+template <typename IO>
+__device__ __forceinline__ float2 widen_pair(const typename PairRaw<IO>::type& w)
+{
+    if constexpr (sizeof(IO) == 4) return w;
+    else if constexpr (is_bf16<IO>())
+        return make_float2(__uint_as_float(w << 16), __uint_as_float(w & 0xffff0000u));
+    else return make_float2(f16_bits_to_f32(w & 0xffffu), f16_bits_to_f32(w >> 16));
+}
+
+template <typename IO>
+__device__ __forceinline__ typename PairRaw<IO>::type narrow_pair(float2 v)
+{
+    if constexpr (sizeof(IO) == 4) return v;
+    else if constexpr (is_bf16<IO>())
+        return (uint32_t)f32_to_bf16(v.x) | ((uint32_t)f32_to_bf16(v.y) << 16);
+    else return f32_to_f16_bits(v.x) | (f32_to_f16_bits(v.y) << 16);
 }
 
 // Channel pair (c, c+1) of a channels-last row.  EVEN: d is even, so the
-// pair is one aligned 8-byte (f32) or 4-byte (bf16) access.
+// pair is one aligned 8-byte (f32) or 4-byte (16-bit types) access.
 template <typename IO, bool EVEN>
 __device__ __forceinline__ float2 load_pair(const IO* row, bool has_b)
 {
     if constexpr (EVEN) {
-        if constexpr (sizeof(IO) == 4) {
-            return *reinterpret_cast<const float2*>(row);
-        } else {
-            const uint32_t w = *reinterpret_cast<const uint32_t*>(row);
-            return make_float2(__uint_as_float(w << 16), __uint_as_float(w & 0xffff0000u));
-        }
+        return widen_pair<IO>(*reinterpret_cast<const typename PairRaw<IO>::type*>(row));
     } else {
         return make_float2(ld1<IO>(row), has_b ? ld1<IO>(row + 1) : 0.0f);
     }
@@ -87,36 +130,11 @@ template <typename IO, bool EVEN>
 __device__ __forceinline__ void store_pair(IO* row, float2 v, bool has_b)
 {
     if constexpr (EVEN) {
-        if constexpr (sizeof(IO) == 4) {
-            *reinterpret_cast<float2*>(row) = v;
-        } else {
-            const uint32_t w = (uint32_t)f32_to_bf16(v.x) | ((uint32_t)f32_to_bf16(v.y) << 16);
-            *reinterpret_cast<uint32_t*>(row) = w;
-        }
+        *reinterpret_cast<typename PairRaw<IO>::type*>(row) = narrow_pair<IO>(v);
     } else {
         st1<IO>(row, v.x);
         if (has_b) st1<IO>(row + 1, v.y);
     }
-}
-
-// Raw channel-pair value as stored (float2 for f32, one dword for a bf16
-// pair); widened at use so prefetched values occupy as few VGPRs as possible.
-template <typename IO>
-struct PairRaw;
-template <>
-struct PairRaw<float> {
-    using type = float2;
-};
-template <>
-struct PairRaw<uint16_t> {
-    using type = uint32_t;
-};
-
-template <typename IO>
-__device__ __forceinline__ float2 widen_pair(const typename PairRaw<IO>::type& w)
-{
-    if constexpr (sizeof(IO) == 4) return w;
-    else return make_float2(__uint_as_float(w << 16), __uint_as_float(w & 0xffff0000u));
 }
 
 // EVEN pair at byte offset `off` from a uniform base.
@@ -129,12 +147,7 @@ __device__ __forceinline__ typename PairRaw<IO>::type load_pair_raw(const IO* ba
 template <typename IO>
 __device__ __forceinline__ void store_pair_at(IO* base, uint32_t off, float2 v)
 {
-    if constexpr (sizeof(IO) == 4) {
-        at_bytes<float2>(base, off) = v;
-    } else {
-        at_bytes<uint32_t>(base, off) =
-            (uint32_t)f32_to_bf16(v.x) | ((uint32_t)f32_to_bf16(v.y) << 16);
-    }
+    at_bytes<typename PairRaw<IO>::type>(base, off) = narrow_pair<IO>(v);
 }
 
 // One spectrum entry (P, Q): a float4 for f32, four bfloat16 in 8 bytes.

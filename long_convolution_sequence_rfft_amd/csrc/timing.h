@@ -20,6 +20,7 @@ void timing_mark_end(hipStream_t s, const std::string& label);
 template <typename T> inline const char* type_label();
 template <> inline const char* type_label<float>() { return "float"; }
 template <> inline const char* type_label<uint16_t>() { return "unsigned short"; }
+template <> inline const char* type_label<_Float16>() { return "_Float16"; }
 
 inline void label_arg(std::ostringstream& o, int v) { o << v; }
 inline void label_arg(std::ostringstream& o, bool v) { o << (v ? "true" : "false"); }

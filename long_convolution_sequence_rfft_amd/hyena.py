@@ -24,6 +24,7 @@ HYENA_ERR_DEVICE = 4
 
 HYENA_F32 = 0
 HYENA_BF16 = 1
+HYENA_F16 = 2
 
 HYENA_PATH_AUTO = 0
 HYENA_PATH_LDS1D = 1
@@ -125,7 +126,7 @@ def hyena_plan_create(B, N, d, order, dims, io_dtype=HYENA_F32, spectrum_dtype=N
     """Returns (status, plan handle or None)."""
     lib = load()
     if spectrum_dtype is None:
-        spectrum_dtype = io_dtype
+        spectrum_dtype = HYENA_F32 if io_dtype == HYENA_F16 else io_dtype
     dims_arr = (ctypes.c_int64 * max(1, len(dims)))(*[int(x) for x in dims])
     h = ctypes.c_void_p()
     st = lib.hyena_plan_create(ctypes.byref(h), int(B), int(N), int(d), int(order), dims_arr,
@@ -225,7 +226,9 @@ class Plan:
             N *= int(v)
         self.B, self.N, self.d, self.order, self.dims = int(B), N, int(d), int(order), tuple(dims)
         self.io_dtype = io_dtype
-        self.spectrum_dtype = io_dtype if spectrum_dtype is None else spectrum_dtype
+        if spectrum_dtype is None:  # binary16 io takes a float32 spectrum
+            spectrum_dtype = HYENA_F32 if io_dtype == HYENA_F16 else io_dtype
+        self.spectrum_dtype = spectrum_dtype
         _, self.handle = hyena_plan_create(B, N, d, order, dims, io_dtype, self.spectrum_dtype,
                                            path)
         self.spectrum_bytes, self.workspace_bytes, self.path = hyena_plan_query(self.handle)
@@ -243,7 +246,8 @@ class Plan:
 
     @property
     def torch_io_dtype(self):
-        return self.torch.float32 if self.io_dtype == HYENA_F32 else self.torch.bfloat16
+        return {HYENA_F32: self.torch.float32, HYENA_BF16: self.torch.bfloat16,
+                HYENA_F16: self.torch.float16}[self.io_dtype]
 
     def _io(self, t, name):
         if t.dtype != self.torch_io_dtype or not t.is_contiguous() or t.device != self.device:

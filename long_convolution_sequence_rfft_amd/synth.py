@@ -24,6 +24,7 @@ import numpy as np
 
 F32 = "f32"
 BF16 = "bf16"
+F16 = "f16"   # IEEE binary16 storage (numpy float16, round to nearest even)
 
 
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
@@ -42,12 +43,20 @@ def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
 
 def _store(x64: np.ndarray, dtype: str) -> np.ndarray:
     x32 = x64.astype(np.float32)
+    if dtype == F16:
+        return x32.astype(np.float16)
     return f32_to_bf16_bits(x32) if dtype == BF16 else x32
+
+
+def _np_storage(dtype: str):
+    return {F32: np.float32, BF16: np.uint16, F16: np.float16}[dtype]
 
 
 def stored_to_f64(a: np.ndarray, dtype: str) -> np.ndarray:
     if dtype == BF16:
         return bf16_bits_to_f32(a).astype(np.float64)
+    if dtype == F16:
+        return np.asarray(a, dtype=np.float16).astype(np.float64)
     return np.asarray(a, dtype=np.float32).astype(np.float64)
 
 
@@ -87,7 +96,7 @@ def make_1d(B: int, N: int, d: int, order: int, alpha_range=(1e-3, 5e-2),
     """Inputs for the 1D causal chain: u, gates ~ N(0,1); damped-sinusoid filters."""
     rng = np.random.default_rng(seed)
     t = np.arange(N, dtype=np.float64)
-    h = np.empty((order, d, N), dtype=np.float32 if dtype == F32 else np.uint16)
+    h = np.empty((order, d, N), dtype=_np_storage(dtype))
     for n in range(order):
         w = rng.uniform(0.0, np.pi, size=d)
         phi = rng.uniform(0.0, 2.0 * np.pi, size=d)
@@ -112,7 +121,7 @@ def make_2d(B: int, X: int, Y: int, d: int, order: int, sigma_range=(16.0, 128.0
     j = np.arange(-(Y - 1), Y, dtype=np.float64)
     r2 = i[:, None] ** 2 + j[None, :] ** 2
     K = np.empty((order, d, 2 * X - 1, 2 * Y - 1),
-                 dtype=np.float32 if dtype == F32 else np.uint16)
+                 dtype=_np_storage(dtype))
     for n in range(order):
         w = rng.uniform(0.0, np.pi, size=(d, 2))
         phi = rng.uniform(0.0, 2.0 * np.pi, size=d)

@@ -19,6 +19,8 @@ def to_torch(a: np.ndarray, dtype: str, device="cuda"):
     import torch
     if dtype == synth.BF16:
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(device)
+    if dtype == synth.F16:
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float16)).to(device)
     return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(device)
 
 
@@ -34,7 +36,8 @@ def run_gpu(inp: synth.Inputs, path=0, spectrum_dtype=None, plan=None, reps=1):
     """Spectrum + forward through the C ABI.  Returns (y float64, plan, H)."""
     import torch
     from long_convolution_sequence_rfft_amd import hyena
-    io = hyena.HYENA_F32 if inp.dtype == synth.F32 else hyena.HYENA_BF16
+    io = {synth.F32: hyena.HYENA_F32, synth.BF16: hyena.HYENA_BF16,
+          synth.F16: hyena.HYENA_F16}[inp.dtype]
     say(f"[gpu] B={inp.B} dims={inp.dims} d={inp.d} order={inp.order} dtype={inp.dtype} "
         f"path={path} spec={spectrum_dtype}")
     if plan is None:

@@ -50,6 +50,10 @@ def test_status_strings():
     (dict(B=1, N=64, d=2, order=1, dims=[64], io_dtype=hyena.HYENA_F32,
           spectrum_dtype=hyena.HYENA_BF16), hyena.HYENA_ERR_UNSUPPORTED),
     (dict(B=1, N=64, d=2, order=1, dims=[64], io_dtype=7), hyena.HYENA_ERR_UNSUPPORTED),
+    (dict(B=1, N=64, d=2, order=1, dims=[64], io_dtype=hyena.HYENA_F16,
+          spectrum_dtype=hyena.HYENA_BF16), hyena.HYENA_ERR_UNSUPPORTED),
+    (dict(B=1, N=64, d=2, order=1, dims=[64], io_dtype=hyena.HYENA_F16,
+          spectrum_dtype=hyena.HYENA_F16), hyena.HYENA_ERR_UNSUPPORTED),
     (dict(B=1, N=64, d=2, order=1, dims=[64], path=9), hyena.HYENA_ERR_UNSUPPORTED),
 ])
 def test_plan_create_rejects(args, code):

@@ -178,3 +178,20 @@ def test_single_channel_path_odd_widths(N, d, B):
     inp = synth.make_1d(B=B, N=N, d=d, order=2, seed=9)
     y, _, _ = run_gpu(inp)
     assert rel_err(y, oracle_ref(inp, method=oracle.DIRECT)) < TOL_F32
+
+
+# binary16 storage: every stored value carries up to 2^-11 relative rounding
+# (u, gates, h and y); with float32 arithmetic in between, the output's
+# max-normalised error stays within a few times 2^-11.  Filters decay fast
+# enough that |y| stays far below the binary16 maximum (65504).
+TOL_F16 = 5e-3
+
+
+@pytest.mark.parametrize("N,d,B", [(2048, 6, 2), (1000, 5, 2), (8192, 4, 1)])
+def test_f16_storage(N, d, B):
+    inp = synth.make_1d(B=B, N=N, d=d, order=2, alpha_range=(1e-3, 1e-2), dtype=synth.F16,
+                        seed=60)
+    y, _, _ = run_gpu(inp)
+    e = rel_err(y, oracle_ref(inp, method=oracle.FFT))
+    say(f"[gpu] f16 N={N} rel err {e:.3e}")
+    assert e < TOL_F16

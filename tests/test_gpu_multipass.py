@@ -162,3 +162,14 @@ def test_rowcol2d_largest_sides(X, Y, d):
     e = rel_err(y, oracle_ref(inp, method=oracle.FFT))
     say(f"[gpu] {X}x{Y} rel err {e:.3e}")
     assert e < TOL_F32
+
+
+def test_f16_storage_multipass():
+    # binary16 storage on the four-step and the 2D paths (float32 spectrum)
+    for inp in (synth.make_1d(B=1, N=16384, d=3, order=2, alpha_range=(1e-3, 1e-2),
+                              dtype=synth.F16, seed=61),
+                synth.make_2d(B=1, X=16, Y=32, d=3, order=2, dtype=synth.F16, seed=62)):
+        y, _, _ = run_gpu(inp)
+        e = rel_err(y, oracle_ref(inp, method=oracle.FFT))
+        say(f"[gpu] f16 dims={inp.dims} rel err {e:.3e}")
+        assert e < 5e-3

@@ -522,3 +522,13 @@ def test_implicit_filter_small_omega_is_the_matrix_product():
     lin = om ** 2 * (w["W3"] @ (w["W2"] @ (w["W1"] @ gamma + w["b1"][:, None])))
     ref = lin.reshape(order, d, N) * np.exp(-alpha[:, :, None] * np.arange(N))
     assert _rel(h, ref) < 1e-7
+
+
+def test_f16_storage_rounding_is_ieee_nearest_even():
+    # the generator stores binary16 with numpy (round to nearest even)
+    x = np.array([1.0, 1.0 + 2.0 ** -11, 1.0 + 3 * 2.0 ** -11, 65504.0, 2.0 ** -14], dtype=np.float64)
+    s = synth._store(x, synth.F16)
+    back = synth.stored_to_f64(s, synth.F16)
+    assert back[1] == 1.0                    # tie to even
+    assert back[2] == 1.0 + 2.0 ** -9        # tie to even (up)
+    assert back[3] == 65504.0 and back[4] == 2.0 ** -14
