@@ -15,6 +15,8 @@ Functions follow the pages cited in ``oracle.c``:
     2D convolution on the native grid
   * ``fft`` -- [P2] "Counting the cost" radix-2 FFT
   * ``circular_conv`` -- [P2] "Linear vs circular" (the unpadded contrast)
+  * ``circular_conv_direct`` / ``hyena1d_circular`` -- the chain with periodic
+    (unpadded, length-N circular) convolutions
   * ``implicit_filter`` -- [P2] "Implicit filters" and "The decay window":
     taps window(t) * FFN(gamma(t)) from a sine MLP over positions
 
@@ -79,6 +81,10 @@ def _load():
             lib.oracle_conv2d_fft.restype = ctypes.c_int
             lib.oracle_hyena2d.argtypes = [i64, i64, i64, i64, i32, p, p, p, p, p, i32]
             lib.oracle_hyena2d.restype = ctypes.c_int
+            lib.oracle_circular_conv_direct.argtypes = [i64, i64, i64, p, p, p, p]
+            lib.oracle_circular_conv_direct.restype = None
+            lib.oracle_hyena1d_circular.argtypes = [i64, i64, i64, i32, p, p, p, p, p, i32]
+            lib.oracle_hyena1d_circular.restype = ctypes.c_int
             lib.oracle_implicit_filter.argtypes = [i64, i64, i32, i32, i32, ctypes.c_double,
                                                    p, p, p, p, p, p, p, p]
             lib.oracle_implicit_filter.restype = None
@@ -199,3 +205,28 @@ def implicit_filter(N, d, order, omega, W1, b1, W2, b2, W3, b3, alpha) -> np.nda
     _load().oracle_implicit_filter(N, d, order, K, H, float(omega), _ptr(W1), _ptr(b1),
                                    _ptr(W2), _ptr(b2), _ptr(W3), _ptr(b3), _ptr(alpha), _ptr(h))
     return h
+
+
+def circular_conv_direct(z, h, D) -> np.ndarray:
+    """w[b,t,c] = sum_s h[c,s] z[b,(t-s) mod N,c] + D[c] z[b,t,c] (written out)."""
+    z, h, D = _f64(z), _f64(h), _f64(D)
+    B, N, d = z.shape
+    assert h.shape == (d, N) and D.shape == (d,)
+    w = np.empty_like(z)
+    _load().oracle_circular_conv_direct(B, N, d, _ptr(z), _ptr(h), _ptr(D), _ptr(w))
+    return w
+
+
+def hyena1d_circular(u, gates, h, D, method: int = DIRECT) -> np.ndarray:
+    """Order-N chain with periodic convolutions (shapes as hyena1d)."""
+    u, gates, h, D = _f64(u), _f64(gates), _f64(h), _f64(D)
+    B, N, d = u.shape
+    order = gates.shape[0]
+    assert gates.shape == (order, B, N, d)
+    assert h.shape == (order, d, N) and D.shape == (order, d)
+    y = np.empty_like(u)
+    rc = _load().oracle_hyena1d_circular(B, N, d, order, _ptr(u), _ptr(gates), _ptr(h), _ptr(D),
+                                         _ptr(y), method)
+    if rc != 0:
+        raise ValueError("oracle_hyena1d_circular failed (FFT route needs N a power of two)")
+    return y

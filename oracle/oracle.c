@@ -422,3 +422,64 @@ void oracle_implicit_filter(int64_t N, int64_t d, int32_t order, int32_t K, int3
         }
     }
 }
+
+/* ------------------------------------------------------------------------ */
+/* Periodic (circular) boundary: the unpadded convolution as an operator     */
+/* ([P2] "Linear vs circular" contrasts it with the padded, causal one; the  */
+/* ops layer of [P3] lists periodic boundaries as a variant)                  */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * w[b,t,c] = sum_{s=0}^{N-1} h[c,s] z[b,(t-s) mod N,c] + D[c] z[b,t,c]
+ * (the sum written out; any N).
+ */
+void oracle_circular_conv_direct(int64_t B, int64_t N, int64_t d, const double* z,
+                                 const double* h, const double* D, double* w)
+{
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t b = 0; b < B; ++b)
+        for (int64_t c = 0; c < d; ++c)
+            for (int64_t t = 0; t < N; ++t) {
+                double acc = 0.0;
+                for (int64_t s = 0; s < N; ++s) {
+                    int64_t r = (t - s) % N;
+                    if (r < 0) r += N;
+                    acc += h[c * N + s] * z[(b * N + r) * d + c];
+                }
+                w[(b * N + t) * d + c] = acc + D[c] * z[(b * N + t) * d + c];
+            }
+}
+
+/*
+ * The order-N chain with periodic convolutions:
+ *   z_n = gates[n-1] . (h_n (*)_N z_{n-1} + D_n z_{n-1})
+ * method 0 = direct sum, 1 = FFT route (oracle_circular_conv_fft + D z;
+ * N a power of two).
+ */
+int oracle_hyena1d_circular(int64_t B, int64_t N, int64_t d, int32_t order, const double* u,
+                            const double* gates, const double* h, const double* D, double* y,
+                            int32_t method)
+{
+    const int64_t E = B * N * d;
+    double* z = (double*)malloc(sizeof(double) * E);
+    double* w = (double*)malloc(sizeof(double) * E);
+    if (!z || !w) { free(z); free(w); return -1; }
+    memcpy(z, u, sizeof(double) * E);
+    int rc = 0;
+    for (int32_t n = 0; n < order && rc == 0; ++n) {
+        const double* hn = h + (int64_t)n * d * N;
+        const double* Dn = D + (int64_t)n * d;
+        if (method == 0) {
+            oracle_circular_conv_direct(B, N, d, z, hn, Dn, w);
+        } else {
+            rc = oracle_circular_conv_fft(B, N, d, z, hn, w);
+            if (rc == 0)
+                for (int64_t i = 0; i < E; ++i) w[i] += Dn[i % d] * z[i];
+        }
+        const double* g = gates + (int64_t)n * E;
+        for (int64_t i = 0; i < E; ++i) z[i] = g[i] * w[i];
+    }
+    if (rc == 0) memcpy(y, z, sizeof(double) * E);
+    free(z); free(w);
+    return rc;
+}

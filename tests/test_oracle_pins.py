@@ -532,3 +532,43 @@ def test_f16_storage_rounding_is_ieee_nearest_even():
     assert back[1] == 1.0                    # tie to even
     assert back[2] == 1.0 + 2.0 ** -9        # tie to even (up)
     assert back[3] == 65504.0 and back[4] == 2.0 ** -14
+
+
+# --------------------------------------------------------------------------
+# Periodic boundary: the unpadded (circular) convolution as an operator
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("method", [oracle.DIRECT, oracle.FFT])
+def test_circular_chain_worked_example(method):
+    # the printed example's wrapped value at t = 0, through the chain
+    g = _worked()
+    x = np.array(g["x"]).reshape(1, 4, 1)
+    h = np.array(g["h"]).reshape(1, 1, 4)
+    y = oracle.hyena1d_circular(x, np.ones((1, 1, 4, 1)), h, np.zeros((1, 1)), method)
+    assert abs(y[0, 0, 0] - g["circular_y0"]) < 1e-15
+
+
+def test_circular_direct_is_numpy_fft_product():
+    # textbook: circular convolution = IDFT(DFT(h) DFT(z)) (numpy's FFT)
+    rng = np.random.default_rng(70)
+    B, N, d = 2, 48, 3
+    z, h, D = rng.normal(size=(B, N, d)), rng.normal(size=(d, N)), rng.normal(size=d)
+    w = oracle.circular_conv_direct(z, h, D)
+    ref = np.real(np.fft.ifft(np.fft.fft(h.T[None], axis=1) * np.fft.fft(z, axis=1), axis=1))
+    assert _rel(w, ref + D * z) < 1e-12
+
+
+def test_circular_chain_routes_agree_and_commute_with_rotation():
+    rng = np.random.default_rng(71)
+    B, N, d, order = 2, 64, 3, 2
+    u = rng.normal(size=(B, N, d))
+    g = rng.normal(size=(order, B, N, d))
+    h = rng.normal(size=(order, d, N))
+    D = rng.normal(size=(order, d))
+    y0 = oracle.hyena1d_circular(u, g, h, D, oracle.DIRECT)
+    y1 = oracle.hyena1d_circular(u, g, h, D, oracle.FFT)
+    assert _rel(y1, y0) < 1e-12
+    # rotating u and the gates rotates y (no edge: every position is alike)
+    s = 13
+    yr = oracle.hyena1d_circular(np.roll(u, s, axis=1), np.roll(g, s, axis=2), h, D, oracle.DIRECT)
+    assert _rel(yr, np.roll(y0, s, axis=1)) < 1e-12
