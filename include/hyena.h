@@ -107,6 +107,22 @@ hyena_status hyena_plan_create(hyena_plan_t* plan, int64_t B, int64_t N, int64_t
                                int32_t order, const int64_t* dims, int32_t ndims,
                                int32_t io_dtype, int32_t spectrum_dtype, int32_t path);
 
+/*
+ * hyena_plan_create with flags.  HYENA_FLAG_CIRCULAR: periodic boundary,
+ * the unpadded length-N circular convolution of "Hyena -- Long Convolutions
+ * Math", section "Linear vs circular" as the operator:
+ *   z_n[b,t,c] = gate_n[b,t,c] * ( sum_{s=0}^{N-1} h_n[c,s] z_{n-1}[b,(t-s) mod N,c]
+ *                                  + D_n[c] z_{n-1}[b,t,c] ),
+ * for ndims = 1 and N a power of two in 16..16384 (the transform is the
+ * sequence itself; LDS1D path).  hyena_spectrum_export then gives bins
+ * k = 0..N/2 of the unpadded length-N transform.
+ */
+#define HYENA_FLAG_CIRCULAR 1
+hyena_status hyena_plan_create_ex(hyena_plan_t* plan, int64_t B, int64_t N, int64_t d,
+                                  int32_t order, const int64_t* dims, int32_t ndims,
+                                  int32_t io_dtype, int32_t spectrum_dtype, int32_t path,
+                                  int32_t flags);
+
 /* Sizes in bytes of the spectrum buffer H and of the workspace, and the path
  * the plan resolved to (any output pointer may be NULL). */
 hyena_status hyena_plan_query(hyena_plan_t plan, size_t* spectrum_bytes,

@@ -16,7 +16,8 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(os.path.dirname(HERE), "_build")
 LIB = os.path.join(HERE, "libhyena_mi355x.so")
 SOURCES = ["api.hip", "lds1d.hip", "lds1d_f32.hip", "lds1d_bf16.hip", "lds1d_f16.hip",
-           "lds1d_real_f32.hip", "lds1d_real_bf16.hip", "lds1d_real_f16.hip", "multipass.hip",
+           "lds1d_real_f32.hip", "lds1d_real_bf16.hip", "lds1d_real_f16.hip",
+           "lds1d_circ_f32.hip", "lds1d_circ_bf16.hip", "lds1d_circ_f16.hip", "multipass.hip",
            "multipass_outer_f32.hip", "multipass_outer_bf16.hip", "multipass_outer_f16.hip",
            "multipass_inner.hip",
            "implicit.hip", "lds1d_implicit.hip", "timing.hip", "plan.cpp"]

@@ -52,21 +52,30 @@ hyena_status check_ws(const hy::Plan& p, const void* ws)
 
 extern "C" {
 
-hyena_status hyena_plan_create(hyena_plan_t* plan, int64_t B, int64_t N, int64_t d,
-                               int32_t order, const int64_t* dims, int32_t ndims,
-                               int32_t io_dtype, int32_t spectrum_dtype, int32_t path)
+hyena_status hyena_plan_create_ex(hyena_plan_t* plan, int64_t B, int64_t N, int64_t d,
+                                  int32_t order, const int64_t* dims, int32_t ndims,
+                                  int32_t io_dtype, int32_t spectrum_dtype, int32_t path,
+                                  int32_t flags)
 {
     if (plan == nullptr) return fail(HYENA_ERR_INVALID_ARGUMENT, "plan output pointer is NULL");
     hyena_plan_s* s = new (std::nothrow) hyena_plan_s;
     if (s == nullptr) return fail(HYENA_ERR_INVALID_ARGUMENT, "out of host memory");
     const hyena_status st =
-        hy::plan_build(s->p, B, N, d, order, dims, ndims, io_dtype, spectrum_dtype, path);
+        hy::plan_build(s->p, B, N, d, order, dims, ndims, io_dtype, spectrum_dtype, path, flags);
     if (st != HYENA_OK) {
         delete s;
         return st;
     }
     *plan = s;
     return HYENA_OK;
+}
+
+hyena_status hyena_plan_create(hyena_plan_t* plan, int64_t B, int64_t N, int64_t d,
+                               int32_t order, const int64_t* dims, int32_t ndims,
+                               int32_t io_dtype, int32_t spectrum_dtype, int32_t path)
+{
+    return hyena_plan_create_ex(plan, B, N, d, order, dims, ndims, io_dtype, spectrum_dtype, path,
+                                0);
 }
 
 hyena_status hyena_plan_query(hyena_plan_t plan, size_t* spectrum_bytes, size_t* workspace_bytes,

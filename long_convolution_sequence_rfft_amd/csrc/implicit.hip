@@ -175,7 +175,9 @@ hyena_status launch_implicit_spectrum(const Plan& p, const hyena_implicit_filter
             using SP = typename decltype(sp)::type;
             switch (L) {
 #define HY_CASE(LL, I_, S_) \
-    case LL: return lds1d_real_spectrum_launch<LL, IO, SP, true>(a, s);
+    case LL:                                                                      \
+        return p.circular ? lds1d_real_spectrum_launch<LL, IO, SP, true, true>(a, s) \
+                          : lds1d_real_spectrum_launch<LL, IO, SP, true, false>(a, s);
                 HY_LDS1D_REAL_SIZES(HY_CASE, 0, 0)
 #undef HY_CASE
                 default: return fail(HYENA_ERR_UNSUPPORTED, "implicit filter: unsupported length");

@@ -188,23 +188,27 @@ hyena_status spec_by_m(int64_t M, const Lds1dSpecArgs& a, hipStream_t s)
 }
 
 template <typename IO, typename SP>
-hyena_status real_fwd_by_l(int64_t L, const Lds1dFwdArgs& a, hipStream_t s)
+hyena_status real_fwd_by_l(int64_t L, bool circ, const Lds1dFwdArgs& a, hipStream_t s)
 {
     switch (L) {
-#define HY_CASE(LL, I, S_) \
-    case LL: return lds1d_real_forward_launch<LL, IO, SP>(a, s);
+#define HY_CASE(LL, I, S_)                                                    \
+    case LL:                                                                  \
+        return circ ? lds1d_real_forward_launch<LL, IO, SP, true>(a, s)       \
+                    : lds1d_real_forward_launch<LL, IO, SP, false>(a, s);
         HY_LDS1D_REAL_SIZES(HY_CASE, IO, SP)
 #undef HY_CASE
         default: return fail(HYENA_ERR_UNSUPPORTED, "LDS1D: unsupported single-channel length");
     }
 }
 
-template <typename IO, typename SP, bool IMPL = false>
-hyena_status real_spec_by_l(int64_t L, const Lds1dSpecArgs& a, hipStream_t s)
+template <typename IO, typename SP>
+hyena_status real_spec_by_l(int64_t L, bool circ, const Lds1dSpecArgs& a, hipStream_t s)
 {
     switch (L) {
-#define HY_CASE(LL, I, S_) \
-    case LL: return lds1d_real_spectrum_launch<LL, IO, SP, IMPL>(a, s);
+#define HY_CASE(LL, I, S_)                                                          \
+    case LL:                                                                        \
+        return circ ? lds1d_real_spectrum_launch<LL, IO, SP, false, true>(a, s)     \
+                    : lds1d_real_spectrum_launch<LL, IO, SP, false, false>(a, s);
         HY_LDS1D_REAL_SIZES(HY_CASE, IO, SP)
 #undef HY_CASE
         default: return fail(HYENA_ERR_UNSUPPORTED, "LDS1D: unsupported single-channel length");
@@ -497,7 +501,8 @@ hyena_status launch_lds1d_forward(const Plan& p, const void* u, const void* cons
     const hyena_status r = by_storage(p, [&](auto io, auto sp) {
         using IO = typename decltype(io)::type;
         using SP = typename decltype(sp)::type;
-        return staged ? real_fwd_by_l<IO, SP>(p.M / 2, a, s) : fwd_by_m<IO, SP>(p.M, a, s);
+        return staged ? real_fwd_by_l<IO, SP>(p.M / 2, p.circular != 0, a, s)
+                      : fwd_by_m<IO, SP>(p.M, a, s);
     });
     if (r != HYENA_OK || !staged) return r;
     StageArgs out{};
@@ -529,7 +534,8 @@ hyena_status launch_lds1d_spectrum(const Plan& p, const void* h, void* H, const 
     return by_storage(p, [&](auto io, auto sp) {
         using IO = typename decltype(io)::type;
         using SP = typename decltype(sp)::type;
-        return real ? real_spec_by_l<IO, SP>(p.M / 2, a, s) : spec_by_m<IO, SP>(p.M, a, s);
+        return real ? real_spec_by_l<IO, SP>(p.M / 2, p.circular != 0, a, s)
+                    : spec_by_m<IO, SP>(p.M, a, s);
     });
 }
 

@@ -210,11 +210,14 @@ hyena_lds1d_spectrum(Lds1dSpecArgs a)
 // overlap another's arithmetic.  Activations are staged channel-major
 // ([B][d][N]); sample pair (2m, 2m+1) is one aligned PairRaw element.
 // ---------------------------------------------------------------------------
-template <int L, typename IO, typename SP>
+// CIRC: periodic boundary -- the transform is the sequence itself (M = N,
+// no zero padding), so every sample is loaded and every output kept.
+template <int L, typename IO, typename SP, bool CIRC>
 __global__ void __launch_bounds__(FftShape<L>::T, 2) hyena_lds1d_real_forward(Lds1dFwdArgs a)
 {
     using S = FftShape<L>;
     constexpr int T = S::T, PTS = S::PTS, R0 = S::R0, LW = S::LW;
+    constexpr int RIN = CIRC ? R0 : R0 / 2;  // live R0-pass samples per butterfly
     __shared__ float smem[2 * LW];
     __shared__ float sxs[4 * S::RL];
     float* re = smem;
@@ -236,7 +239,7 @@ __global__ void __launch_bounds__(FftShape<L>::T, 2) hyena_lds1d_real_forward(Ld
     for (int q = 0; q < S::Q0; ++q) {
         const uint32_t lane_off = (uint32_t)(tau + q * T) * 2u * (uint32_t)sizeof(IO);
 #pragma unroll
-        for (int r = 0; r < R0 / 2; ++r)
+        for (int r = 0; r < RIN; ++r)
             v[q * R0 + r] = widen_pair<IO>(load_pair_raw(ubase + (size_t)r * (L / R0) * 2, lane_off));
     }
 
@@ -244,25 +247,25 @@ __global__ void __launch_bounds__(FftShape<L>::T, 2) hyena_lds1d_real_forward(Ld
         const SP* spec = static_cast<const SP*>(a.spec) +
                          ((int64_t)n * a.d + c) * (int64_t)(L / 2) * kEntryElems;
         typename EntryRaw<SP>::type ent[S::RL];
-        fwd_transform<L>(v, re, im, a.tw, a.tw_off, tau, j1, j2, n > 0,
+        fwd_transform<L, !CIRC>(v, re, im, a.tw, a.tw_off, tau, j1, j2, n > 0,
                          [&] { load_entries<L, SP>(ent, spec, tau); });
         real_product<L, SP>(v, ent, tau, a.D[(int64_t)n * a.d + c] * invL, wbase, sxs);
 
         const IO* g = static_cast<const IO*>(a.gates[n]) + row;
-        typename PairRaw<IO>::type graw[S::Q0][R0 / 2];
-        inv_transform<L>(v, re, im, a.tw, a.tw_off, tau, j1, j2, [&] {
+        typename PairRaw<IO>::type graw[S::Q0][RIN];
+        inv_transform<L, !CIRC>(v, re, im, a.tw, a.tw_off, tau, j1, j2, [&] {
 #pragma unroll
             for (int q = 0; q < S::Q0; ++q) {
                 const uint32_t lane_off = (uint32_t)(tau + q * T) * 2u * (uint32_t)sizeof(IO);
 #pragma unroll
-                for (int r = 0; r < R0 / 2; ++r)
+                for (int r = 0; r < RIN; ++r)
                     graw[q][r] = load_pair_raw(g + (size_t)r * (L / R0) * 2, lane_off);
             }
         });
 #pragma unroll
         for (int q = 0; q < S::Q0; ++q)
 #pragma unroll
-            for (int r = 0; r < R0 / 2; ++r) {
+            for (int r = 0; r < RIN; ++r) {
                 const float2 gg = widen_pair<IO>(graw[q][r]);
                 float2& x = v[q * R0 + r];
                 x = make_float2(x.x * gg.x, x.y * gg.y);
@@ -274,7 +277,7 @@ __global__ void __launch_bounds__(FftShape<L>::T, 2) hyena_lds1d_real_forward(Ld
     for (int q = 0; q < S::Q0; ++q) {
         const uint32_t lane_off = (uint32_t)(tau + q * T) * 2u * (uint32_t)sizeof(IO);
 #pragma unroll
-        for (int r = 0; r < R0 / 2; ++r)
+        for (int r = 0; r < RIN; ++r)
             store_pair_at(ybase + (size_t)r * (L / R0) * 2, lane_off, v[q * R0 + r]);
     }
 }
@@ -282,11 +285,13 @@ __global__ void __launch_bounds__(FftShape<L>::T, 2) hyena_lds1d_real_forward(Ld
 // Filter spectrum, single-channel form: one workgroup per (filter n, channel
 // c); entries (S, Dl) / L, the 1/L of the unscaled inverse transform folded in.
 // IMPL: the taps come from the implicit filter (a.imp) instead of a.h.
-template <int L, typename IO, typename SP, bool IMPL>
+// CIRC: periodic boundary (N = M taps, no zero padding).
+template <int L, typename IO, typename SP, bool IMPL, bool CIRC>
 __global__ void __launch_bounds__(FftShape<L>::T, 2) hyena_lds1d_real_spectrum(Lds1dSpecArgs a)
 {
     using S = FftShape<L>;
     constexpr int T = S::T, PTS = S::PTS, R0 = S::R0;
+    constexpr int RIN = CIRC ? R0 : R0 / 2;
     __shared__ float smem[2 * S::LW];
     __shared__ float w3s[IMPL ? 256 : 1];
     const int tau = threadIdx.x;
@@ -302,7 +307,7 @@ __global__ void __launch_bounds__(FftShape<L>::T, 2) hyena_lds1d_real_spectrum(L
 #pragma unroll
         for (int q = 0; q < S::Q0; ++q)
 #pragma unroll
-            for (int r = 0; r < R0 / 2; ++r) {
+            for (int r = 0; r < RIN; ++r) {
                 const int64_t t = 2 * (int64_t)(tau + q * T + r * (L / R0));
                 v[q * R0 + r] = make_float2(implicit_tap(a.imp, w3s, b3, al, t),
                                             implicit_tap(a.imp, w3s, b3, al, t + 1));
@@ -313,30 +318,31 @@ __global__ void __launch_bounds__(FftShape<L>::T, 2) hyena_lds1d_real_spectrum(L
         for (int q = 0; q < S::Q0; ++q) {
             const uint32_t lane_off = (uint32_t)(tau + q * T) * 2u * (uint32_t)sizeof(IO);
 #pragma unroll
-            for (int r = 0; r < R0 / 2; ++r)
+            for (int r = 0; r < RIN; ++r)
                 v[q * R0 + r] = widen_pair<IO>(load_pair_raw(h + (size_t)r * (L / R0) * 2, lane_off));
         }
     }
-    fwd_transform<L>(v, smem, smem + S::LW, a.tw, a.tw_off, tau, j1, j2, false, [] {});
+    fwd_transform<L, !CIRC>(v, smem, smem + S::LW, a.tw, a.tw_off, tau, j1, j2, false, [] {});
     SP* spec = static_cast<SP*>(a.spec) + lin * (int64_t)(L / 2) * kEntryElems;
     store_real_entries<L, SP>(v, spec, tau, 1.0f / (float)L, a.twm[tau ? tau : T]);
 }
 
-template <int L, typename IO, typename SP>
+template <int L, typename IO, typename SP, bool CIRC>
 hyena_status lds1d_real_forward_launch(const Lds1dFwdArgs& a, hipStream_t s)
 {
-    HY_LAUNCH(kernel_label("hyena_lds1d_real_forward", L, type_label<IO>(), type_label<SP>()),
-              (hyena_lds1d_real_forward<L, IO, SP>), dim3((unsigned)a.nblocks),
+    HY_LAUNCH(kernel_label("hyena_lds1d_real_forward", L, type_label<IO>(), type_label<SP>(), CIRC),
+              (hyena_lds1d_real_forward<L, IO, SP, CIRC>), dim3((unsigned)a.nblocks),
               dim3(FftShape<L>::T), 0, s, a);
     const hipError_t e = hipGetLastError();
     return e == hipSuccess ? HYENA_OK : fail(HYENA_ERR_DEVICE, hipGetErrorString(e));
 }
 
-template <int L, typename IO, typename SP, bool IMPL>
+template <int L, typename IO, typename SP, bool IMPL, bool CIRC>
 hyena_status lds1d_real_spectrum_launch(const Lds1dSpecArgs& a, hipStream_t s)
 {
-    HY_LAUNCH(kernel_label("hyena_lds1d_real_spectrum", L, type_label<IO>(), type_label<SP>(), IMPL),
-              (hyena_lds1d_real_spectrum<L, IO, SP, IMPL>), dim3((unsigned)a.nblocks),
+    HY_LAUNCH(kernel_label("hyena_lds1d_real_spectrum", L, type_label<IO>(), type_label<SP>(), IMPL,
+                           CIRC),
+              (hyena_lds1d_real_spectrum<L, IO, SP, IMPL, CIRC>), dim3((unsigned)a.nblocks),
               dim3(FftShape<L>::T), 0, s, a);
     const hipError_t e = hipGetLastError();
     return e == hipSuccess ? HYENA_OK : fail(HYENA_ERR_DEVICE, hipGetErrorString(e));
@@ -381,20 +387,25 @@ hyena_status lds1d_spectrum_launch(const Lds1dSpecArgs& a, hipStream_t s)
     extern template hyena_status lds1d_spectrum_launch<M, IO, SP>(const Lds1dSpecArgs&,          \
                                                                   hipStream_t);
 
-#define HY_LDS1D_REAL_INSTANTIATE(L, IO, SP)                                                      \
-    template hyena_status lds1d_real_forward_launch<L, IO, SP>(const Lds1dFwdArgs&, hipStream_t); \
-    template hyena_status lds1d_real_spectrum_launch<L, IO, SP, false>(const Lds1dSpecArgs&,      \
-                                                                      hipStream_t);
+// single-channel kernels: (L, IO, SP) x {zero-padded, periodic}; the
+// implicit-filter spectrum variants are instantiated separately
+#define HY_LDS1D_REAL_INST_B(L, IO, SP, CIRC, EXT)                                                 \
+    EXT template hyena_status lds1d_real_forward_launch<L, IO, SP, CIRC>(const Lds1dFwdArgs&,      \
+                                                                        hipStream_t);             \
+    EXT template hyena_status lds1d_real_spectrum_launch<L, IO, SP, false, CIRC>(                 \
+        const Lds1dSpecArgs&, hipStream_t);
+#define HY_LDS1D_IMPL_INST_B(L, IO, SP, EXT)                                                       \
+    EXT template hyena_status lds1d_real_spectrum_launch<L, IO, SP, true, false>(                 \
+        const Lds1dSpecArgs&, hipStream_t);                                                        \
+    EXT template hyena_status lds1d_real_spectrum_launch<L, IO, SP, true, true>(                  \
+        const Lds1dSpecArgs&, hipStream_t);
 
-#define HY_LDS1D_REAL_EXTERN(L, IO, SP)                                                            \
-    extern template hyena_status lds1d_real_forward_launch<L, IO, SP>(const Lds1dFwdArgs&,         \
-                                                                      hipStream_t);                \
-    extern template hyena_status lds1d_real_spectrum_launch<L, IO, SP, false>(const Lds1dSpecArgs&,\
-                                                                             hipStream_t);        \
-    extern template hyena_status lds1d_real_spectrum_launch<L, IO, SP, true>(const Lds1dSpecArgs&, \
-                                                                            hipStream_t);
-
-#define HY_LDS1D_IMPLICIT_INSTANTIATE(L, IO, SP) \
-    template hyena_status lds1d_real_spectrum_launch<L, IO, SP, true>(const Lds1dSpecArgs&, hipStream_t);
+#define HY_LDS1D_REAL_INSTANTIATE(L, IO, SP) HY_LDS1D_REAL_INST_B(L, IO, SP, false, )
+#define HY_LDS1D_CIRC_INSTANTIATE(L, IO, SP) HY_LDS1D_REAL_INST_B(L, IO, SP, true, )
+#define HY_LDS1D_IMPLICIT_INSTANTIATE(L, IO, SP) HY_LDS1D_IMPL_INST_B(L, IO, SP, )
+#define HY_LDS1D_REAL_EXTERN(L, IO, SP)                 \
+    HY_LDS1D_REAL_INST_B(L, IO, SP, false, extern)      \
+    HY_LDS1D_REAL_INST_B(L, IO, SP, true, extern)       \
+    HY_LDS1D_IMPL_INST_B(L, IO, SP, extern)
 
 }  // namespace hy

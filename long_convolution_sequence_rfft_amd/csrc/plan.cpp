@@ -61,8 +61,10 @@ static void fourstep_split(int64_t M, int64_t& M1, int64_t& M2)
 
 hyena_status plan_build(Plan& p, int64_t B, int64_t N, int64_t d, int32_t order,
                         const int64_t* dims, int32_t ndims, int32_t io_dtype,
-                        int32_t spec_dtype, int32_t path)
+                        int32_t spec_dtype, int32_t path, int32_t flags)
 {
+    if (flags & ~HYENA_FLAG_CIRCULAR) return fail(HYENA_ERR_UNSUPPORTED, "unknown flags");
+    p.circular = (flags & HYENA_FLAG_CIRCULAR) ? 1 : 0;
     if (B < 1) return fail(HYENA_ERR_INVALID_ARGUMENT, "B must be >= 1");
     if (d < 1) return fail(HYENA_ERR_INVALID_ARGUMENT, "d must be >= 1");
     if (N < 1) return fail(HYENA_ERR_INVALID_ARGUMENT, "N must be >= 1");
@@ -99,6 +101,17 @@ hyena_status plan_build(Plan& p, int64_t B, int64_t N, int64_t d, int32_t order,
         if (N < 4 || N > kFourStepMaxM / 2)
             return fail(HYENA_ERR_UNSUPPORTED, "1D sequence length must be in 4..524288");
         p.M = next_pow2(2 * N);
+        if (p.circular) {
+            // periodic boundary: the transform is the sequence itself, on the
+            // single-channel path (a power of two, 16..16384)
+            if (!is_pow2(N) || N < 16 || N > kLdsMaxM)
+                return fail(HYENA_ERR_UNSUPPORTED,
+                            "periodic boundary needs N a power of two in 16..16384");
+            if (path != HYENA_PATH_AUTO && path != HYENA_PATH_LDS1D)
+                return fail(HYENA_ERR_UNSUPPORTED, "periodic boundary runs on the LDS1D path");
+            p.M = N;
+            path = HYENA_PATH_LDS1D;
+        }
         if (path == HYENA_PATH_AUTO) path = p.M <= kLdsMaxM ? HYENA_PATH_LDS1D : HYENA_PATH_FOURSTEP1D;
         if (path == HYENA_PATH_ROWCOL2D)
             return fail(HYENA_ERR_UNSUPPORTED, "ROWCOL2D needs ndims = 2");
@@ -114,7 +127,7 @@ hyena_status plan_build(Plan& p, int64_t B, int64_t N, int64_t d, int32_t order,
             // channel-major in the workspace (half the LDS of a channel pair,
             // so twice the workgroups per CU; measured faster at 2K and 8K).
             // Other N: channel-pair kernels reading channels-last rows per lane.
-            const bool real = 2 * N == p.M && p.M >= 16;
+            const bool real = (2 * N == p.M || p.circular) && p.M >= 16;
             p.lds_io = real ? 3 : 0;
             const int64_t L = real ? p.M / 2 : p.M;
             p.R0 = lds1d_r0((int)L);
@@ -134,6 +147,7 @@ hyena_status plan_build(Plan& p, int64_t B, int64_t N, int64_t d, int32_t order,
             add_segment(p, off, p.M1, p.M2);
         }
     } else {
+        if (p.circular) return fail(HYENA_ERR_UNSUPPORTED, "periodic boundary: ndims = 1 only");
         const int64_t X = dims[0], Y = dims[1];
         if (!is_pow2(X) || !is_pow2(Y) || X < 4 || Y < 4 || X > 512 || Y > 512)
             return fail(HYENA_ERR_UNSUPPORTED, "2D grid sides must be powers of two in 4..512");

@@ -53,6 +53,7 @@ struct Plan {
     int64_t X = 0, Y = 0;  // 2D grid
     int32_t io_dtype = HYENA_F32, spec_dtype = HYENA_F32;
     int32_t path = HYENA_PATH_AUTO;
+    int32_t circular = 0;  // periodic boundary: transform length N, no padding
 
     int64_t M = 0;       // 1D transform length (power of two >= 2N)
     int64_t npairs = 0;  // channel pairs (two real channels per complex transform)
@@ -96,7 +97,7 @@ struct Plan {
 // Implemented in plan.cpp (pure host code).
 hyena_status plan_build(Plan& p, int64_t B, int64_t N, int64_t d, int32_t order,
                         const int64_t* dims, int32_t ndims, int32_t io_dtype,
-                        int32_t spec_dtype, int32_t path);
+                        int32_t spec_dtype, int32_t path, int32_t flags);
 void set_error(const std::string& msg);
 hyena_status fail(hyena_status s, const std::string& msg);
 

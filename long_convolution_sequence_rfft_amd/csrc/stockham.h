@@ -278,7 +278,8 @@ struct TwOffsets {
 // caller, whose latency then overlaps the last pass's arithmetic).
 // Every pass with Q > 1 butterflies per thread shares one twiddle set in the
 // R1 pass (T is a multiple of R0 whenever R1 > 1).
-template <int L, typename F>
+// HALF_IN = false: all R0 inputs per butterfly hold data (no zero padding).
+template <int L, bool HALF_IN = true, typename F>
 __device__ __forceinline__ void fwd_transform(float2* v, float* sre, float* sim, const float2* tw,
                                               TwOffsets o, int tau, int j1, int j2,
                                               bool sync_first, F&& prefetch)
@@ -287,7 +288,7 @@ __device__ __forceinline__ void fwd_transform(float2* v, float* sre, float* sim,
     constexpr int T = S::T, R0 = S::R0, R1 = S::R1, RL = S::RL;
     constexpr int NSL = L / RL;
 #pragma unroll
-    for (int q = 0; q < S::Q0; ++q) dft<R0, -1, true, false>(&v[q * R0]);
+    for (int q = 0; q < S::Q0; ++q) dft<R0, -1, HALF_IN, false>(&v[q * R0]);
     if (sync_first) __syncthreads();
 #pragma unroll
     for (int q = 0; q < S::Q0; ++q) lds_write<R0, 1>(sre, sim, &v[q * R0], tau + q * T);
@@ -325,7 +326,8 @@ __device__ __forceinline__ void fwd_transform(float2* v, float* sre, float* sim,
 // tau + q T + s L/R0.  Only the first half of the samples is produced.
 // `prefetch` runs after the last exchange's reads (global loads for the
 // caller, e.g. the gate values, whose latency overlaps the last pass).
-template <int L, typename F>
+// HALF_OUT = false: all L samples are produced (v[q R0 + s], s < R0).
+template <int L, bool HALF_OUT = true, typename F>
 __device__ __forceinline__ void inv_transform(float2* v, float* sre, float* sim, const float2* tw,
                                               TwOffsets o, int tau, int j1, int j2, F&& prefetch)
 {
@@ -364,7 +366,7 @@ __device__ __forceinline__ void inv_transform(float2* v, float* sre, float* sim,
     }
     prefetch();
 #pragma unroll
-    for (int q = 0; q < S::Q0; ++q) dft<R0, +1, false, true>(&v[q * R0]);
+    for (int q = 0; q < S::Q0; ++q) dft<R0, +1, false, HALF_OUT>(&v[q * R0]);
 }
 
 // ---------------------------------------------------------------------------

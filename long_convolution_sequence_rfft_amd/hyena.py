@@ -36,7 +36,10 @@ EXPORTED_SYMBOLS = (
     "hyena_forward", "hyena_spectrum_export", "hyena_plan_destroy", "hyena_status_string",
     "hyena_last_error", "hyena_timing_begin", "hyena_timing_end", "hyena_timing_kernel",
     "hyena_timing_release", "hyena_implicit_scratch_bytes", "hyena_filter_spectrum_implicit",
+    "hyena_plan_create_ex",
 )
+
+HYENA_FLAG_CIRCULAR = 1
 
 
 class ImplicitFilter(ctypes.Structure):
@@ -70,6 +73,8 @@ def load():
             i64, i32, p, sz = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t
             lib.hyena_plan_create.argtypes = [ctypes.POINTER(p), i64, i64, i64, i32,
                                               ctypes.POINTER(i64), i32, i32, i32, i32]
+            lib.hyena_plan_create_ex.argtypes = [ctypes.POINTER(p), i64, i64, i64, i32,
+                                                 ctypes.POINTER(i64), i32, i32, i32, i32, i32]
             lib.hyena_plan_query.argtypes = [p, ctypes.POINTER(sz), ctypes.POINTER(sz),
                                              ctypes.POINTER(i32)]
             lib.hyena_workspace_init.argtypes = [p, p, p]
@@ -90,7 +95,7 @@ def load():
             lib.hyena_implicit_scratch_bytes.argtypes = [p, i32, ctypes.POINTER(sz)]
             lib.hyena_filter_spectrum_implicit.argtypes = [p, ctypes.POINTER(ImplicitFilter), p, p,
                                                            p, p]
-            for name in ("hyena_plan_create", "hyena_plan_query", "hyena_workspace_init",
+            for name in ("hyena_plan_create", "hyena_plan_create_ex", "hyena_plan_query", "hyena_workspace_init",
                          "hyena_filter_spectrum", "hyena_forward", "hyena_spectrum_export",
                          "hyena_plan_destroy", "hyena_timing_begin", "hyena_timing_end",
                          "hyena_timing_kernel", "hyena_timing_release",
@@ -122,15 +127,20 @@ def _check(status: int, where: str):
 # --------------------------------------------------------------------------
 
 def hyena_plan_create(B, N, d, order, dims, io_dtype=HYENA_F32, spectrum_dtype=None,
-                      path=HYENA_PATH_AUTO, check=True):
-    """Returns (status, plan handle or None)."""
+                      path=HYENA_PATH_AUTO, check=True, flags=0):
+    """Returns (status, plan handle or None); flags go through hyena_plan_create_ex."""
     lib = load()
     if spectrum_dtype is None:
         spectrum_dtype = HYENA_F32 if io_dtype == HYENA_F16 else io_dtype
     dims_arr = (ctypes.c_int64 * max(1, len(dims)))(*[int(x) for x in dims])
     h = ctypes.c_void_p()
-    st = lib.hyena_plan_create(ctypes.byref(h), int(B), int(N), int(d), int(order), dims_arr,
-                               len(dims), int(io_dtype), int(spectrum_dtype), int(path))
+    if flags:
+        st = lib.hyena_plan_create_ex(ctypes.byref(h), int(B), int(N), int(d), int(order),
+                                      dims_arr, len(dims), int(io_dtype), int(spectrum_dtype),
+                                      int(path), int(flags))
+    else:
+        st = lib.hyena_plan_create(ctypes.byref(h), int(B), int(N), int(d), int(order), dims_arr,
+                                   len(dims), int(io_dtype), int(spectrum_dtype), int(path))
     if check:
         _check(st, "hyena_plan_create")
     return st, (h.value if st == HYENA_OK else None)
@@ -218,7 +228,7 @@ class Plan:
     """
 
     def __init__(self, B, d, order, dims, io_dtype=HYENA_F32, spectrum_dtype=None,
-                 path=HYENA_PATH_AUTO, device="cuda"):
+                 path=HYENA_PATH_AUTO, device="cuda", circular=False):
         import torch
         self.torch = torch
         N = 1
@@ -229,8 +239,9 @@ class Plan:
         if spectrum_dtype is None:  # binary16 io takes a float32 spectrum
             spectrum_dtype = HYENA_F32 if io_dtype == HYENA_F16 else io_dtype
         self.spectrum_dtype = spectrum_dtype
+        self.circular = bool(circular)
         _, self.handle = hyena_plan_create(B, N, d, order, dims, io_dtype, self.spectrum_dtype,
-                                           path)
+                                           path, flags=HYENA_FLAG_CIRCULAR if circular else 0)
         self.spectrum_bytes, self.workspace_bytes, self.path = hyena_plan_query(self.handle)
         dev = torch.device(device)
         if dev.type == "cuda" and dev.index is None:
@@ -304,7 +315,7 @@ class Plan:
     def export_spectrum(self, H):
         if len(self.dims) == 1:
             M = 1
-            while M < 2 * self.N:
+            while M < (self.N if self.circular else 2 * self.N):
                 M *= 2
             shape = (self.order, self.d, M // 2 + 1, 2)
         else:

@@ -221,3 +221,23 @@ def test_implicit_scratch_sizes_and_validation():
     _, plan = hyena.hyena_plan_create(1, 64, 2, 1, [8, 8])
     assert hyena.hyena_implicit_scratch_bytes(plan, 64)[0] == hyena.HYENA_ERR_UNSUPPORTED
     hyena.hyena_plan_destroy(plan)
+
+
+@pytest.mark.parametrize("N,dims,path,flags,code", [
+    (1024, [1024], 0, 1, hyena.HYENA_OK),
+    (16384, [16384], 1, 1, hyena.HYENA_OK),
+    (1000, [1000], 0, 1, hyena.HYENA_ERR_UNSUPPORTED),       # not a power of two
+    (8, [8], 0, 1, hyena.HYENA_ERR_UNSUPPORTED),             # below 16
+    (32768, [32768], 0, 1, hyena.HYENA_ERR_UNSUPPORTED),     # beyond one workgroup
+    (4096, [4096], 2, 1, hyena.HYENA_ERR_UNSUPPORTED),       # four-step path
+    (64, [8, 8], 0, 1, hyena.HYENA_ERR_UNSUPPORTED),         # grids
+    (64, [64], 0, 2, hyena.HYENA_ERR_UNSUPPORTED),           # unknown flag
+])
+def test_periodic_boundary_plans(N, dims, path, flags, code):
+    st, plan = hyena.hyena_plan_create(1, N, 4, 2, dims, path=path, flags=flags, check=False)
+    assert st == code, hyena.hyena_last_error()
+    if st == hyena.HYENA_OK:
+        spec, _, p = hyena.hyena_plan_query(plan)
+        assert p == 1
+        assert spec == 2 * 4 * (N // 4) * 16  # order * d * (N/4 entries) * 16 bytes
+        hyena.hyena_plan_destroy(plan)

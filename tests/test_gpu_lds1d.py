@@ -158,7 +158,7 @@ def test_launch_timing_records_every_kernel():
     recs, dropped = hyena.hyena_timing_end()
     hyena.hyena_timing_release()
     assert dropped == 0
-    assert sorted(recs) == ["hy::hyena_lds1d_real_forward<2048, float, float>",
+    assert sorted(recs) == ["hy::hyena_lds1d_real_forward<2048, float, float, false>",
                             "hy::hyena_stage<float, false>",
                             "hy::hyena_stage<float, true>"]
     for r in recs.values():
@@ -195,3 +195,27 @@ def test_f16_storage(N, d, B):
     e = rel_err(y, oracle_ref(inp, method=oracle.FFT))
     say(f"[gpu] f16 N={N} rel err {e:.3e}")
     assert e < TOL_F16
+
+
+@pytest.mark.parametrize("N,d,B,dtype", [(16, 3, 2, synth.F32), (256, 5, 1, synth.F32),
+                                         (2048, 6, 2, synth.F32), (16384, 2, 1, synth.F32),
+                                         (4096, 4, 2, synth.BF16), (1024, 3, 1, synth.F16)])
+def test_periodic_boundary(N, d, B, dtype):
+    # HYENA_FLAG_CIRCULAR: unpadded length-N circular convolutions in the chain
+    from long_convolution_sequence_rfft_amd import hyena
+    inp = synth.make_1d(B=B, N=N, d=d, order=2, alpha_range=(1e-3, 1e-2), dtype=dtype, seed=80)
+    io = {synth.F32: hyena.HYENA_F32, synth.BF16: hyena.HYENA_BF16,
+          synth.F16: hyena.HYENA_F16}[dtype]
+    plan = hyena.Plan(B, d, 2, (N,), io_dtype=io, circular=True)
+    y, _, H = run_gpu(inp, plan=plan)
+    u, g, h, D = inp.f64()
+    e = rel_err(y, oracle.hyena1d_circular(u, g, h, D, oracle.FFT))
+    say(f"[gpu] periodic N={N} {dtype} rel err {e:.3e}")
+    assert e < {synth.F32: TOL_F32, synth.BF16: TOL_BF16, synth.F16: TOL_F16}[dtype]
+    if dtype == synth.F32:
+        # the spectrum is the unpadded length-N transform of the taps
+        nat = plan.export_spectrum(H).cpu().numpy().astype(np.float64)
+        nat = nat[..., 0] + 1j * nat[..., 1]
+        for n in range(2):
+            for c in range(d):
+                assert rel_err(nat[n, c], oracle.fft(h[n, c])[:N // 2 + 1]) < 2e-6
