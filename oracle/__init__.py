@@ -17,6 +17,8 @@ Functions follow the pages cited in ``oracle.c``:
   * ``circular_conv`` -- [P2] "Linear vs circular" (the unpadded contrast)
   * ``circular_conv_direct`` / ``hyena1d_circular`` -- the chain with periodic
     (unpadded, length-N circular) convolutions
+  * ``dwconv3x3`` / ``hyena2d_block`` -- [P3] "Putting it together": short
+    conv, inner gate q . SiLU(k), 2D long conv, outer gate SiLU(v)
   * ``implicit_filter`` -- [P2] "Implicit filters" and "The decay window":
     taps window(t) * FFN(gamma(t)) from a sine MLP over positions
 
@@ -85,6 +87,10 @@ def _load():
             lib.oracle_circular_conv_direct.restype = None
             lib.oracle_hyena1d_circular.argtypes = [i64, i64, i64, i32, p, p, p, p, p, i32]
             lib.oracle_hyena1d_circular.restype = ctypes.c_int
+            lib.oracle_dwconv3x3.argtypes = [i64, i64, i64, i64, p, p, p, p]
+            lib.oracle_dwconv3x3.restype = None
+            lib.oracle_hyena2d_block.argtypes = [i64, i64, i64, i64, p, p, p, p, p, p, p, p, i32]
+            lib.oracle_hyena2d_block.restype = ctypes.c_int
             lib.oracle_implicit_filter.argtypes = [i64, i64, i32, i32, i32, ctypes.c_double,
                                                    p, p, p, p, p, p, p, p]
             lib.oracle_implicit_filter.restype = None
@@ -229,4 +235,32 @@ def hyena1d_circular(u, gates, h, D, method: int = DIRECT) -> np.ndarray:
                                          _ptr(y), method)
     if rc != 0:
         raise ValueError("oracle_hyena1d_circular failed (FFT route needs N a power of two)")
+    return y
+
+
+def dwconv3x3(x, w, bias=None) -> np.ndarray:
+    """Depthwise 3x3 cross-correlation, zero padding 1: x [B,X,Y,d], w [d,3,3]."""
+    x, w = _f64(x), _f64(w)
+    B, X, Y, d = x.shape
+    assert w.shape == (d, 3, 3)
+    b = _f64(bias) if bias is not None else None
+    o = np.empty_like(x)
+    _load().oracle_dwconv3x3(B, X, Y, d, _ptr(x), _ptr(w), _ptr(b) if b is not None else None,
+                             _ptr(o))
+    return o
+
+
+def hyena2d_block(q, k, v, sw, sb, K, D, method: int = DIRECT) -> np.ndarray:
+    """HyenaND mixer: q, k, v [B,X,Y,d]; sw [3,d,3,3]; sb [3,d] or None;
+    K [d,2X-1,2Y-1]; D [d]."""
+    q, k, v, sw, K, D = _f64(q), _f64(k), _f64(v), _f64(sw), _f64(K), _f64(D)
+    B, X, Y, d = q.shape
+    assert sw.shape == (3, d, 3, 3) and K.shape == (d, 2 * X - 1, 2 * Y - 1) and D.shape == (d,)
+    b = _f64(sb) if sb is not None else None
+    y = np.empty_like(q)
+    rc = _load().oracle_hyena2d_block(B, X, Y, d, _ptr(q), _ptr(k), _ptr(v), _ptr(sw),
+                                      _ptr(b) if b is not None else None, _ptr(K), _ptr(D),
+                                      _ptr(y), method)
+    if rc != 0:
+        raise MemoryError("oracle_hyena2d_block failed")
     return y

@@ -572,3 +572,49 @@ def test_circular_chain_routes_agree_and_commute_with_rotation():
     s = 13
     yr = oracle.hyena1d_circular(np.roll(u, s, axis=1), np.roll(g, s, axis=2), h, D, oracle.DIRECT)
     assert _rel(yr, np.roll(y0, s, axis=1)) < 1e-12
+
+
+# --------------------------------------------------------------------------
+# HyenaND block ([P3] "Putting it together: the HyenaND operator")
+# --------------------------------------------------------------------------
+
+def test_dwconv3x3_is_scipy_correlate():
+    # zero-padded 3x3 cross-correlation per channel (scipy's 2D correlate)
+    from scipy.signal import correlate2d
+    rng = np.random.default_rng(90)
+    B, X, Y, d = 2, 7, 9, 3
+    x, w, b = rng.normal(size=(B, X, Y, d)), rng.normal(size=(d, 3, 3)), rng.normal(size=d)
+    o = oracle.dwconv3x3(x, w, b)
+    for bb in range(B):
+        for c in range(d):
+            ref = correlate2d(x[bb, :, :, c], w[c], mode="same", boundary="fill") + b[c]
+            assert _rel(o[bb, :, :, c], ref) < 1e-14
+
+
+def test_hyena2d_block_reduces_to_the_gated_chain():
+    # identity short convolutions: y = SiLU(v) . (K * (q . SiLU(k)) + D (q . SiLU(k)))
+    rng = np.random.default_rng(91)
+    B, X, Y, d = 1, 6, 5, 2
+    q, k, v = (rng.normal(size=(B, X, Y, d)) for _ in range(3))
+    K = rng.normal(size=(d, 2 * X - 1, 2 * Y - 1))
+    D = rng.normal(size=d)
+    sw = np.zeros((3, d, 3, 3))
+    sw[:, :, 1, 1] = 1.0
+    silu = lambda x: x / (1.0 + np.exp(-x))
+    for method in (oracle.DIRECT, oracle.FFT):
+        y = oracle.hyena2d_block(q, k, v, sw, None, K, D, method)
+        ref = oracle.hyena2d(q * silu(k), silu(v)[None], K[None], D[None], oracle.DIRECT)
+        assert _rel(y, ref) < 1e-12
+
+
+def test_hyena2d_block_silu_and_biases():
+    # K = 0, D = 1 and constant 1-tap short convs with biases: every output is
+    # SiLU(bv) * (bq * SiLU(bk)) away from the data -- the SiLU closed form
+    B, X, Y, d = 1, 4, 4, 2
+    z = np.zeros((B, X, Y, d))
+    sw = np.zeros((3, d, 3, 3))
+    sb = np.array([[0.5, -1.5], [2.0, -0.25], [1.0, 3.0]])
+    y = oracle.hyena2d_block(z, z, z, sw, sb, np.zeros((d, 2 * X - 1, 2 * Y - 1)), np.ones(d))
+    s = lambda x: x / (1.0 + np.exp(-x))
+    expect = s(sb[2]) * sb[0] * s(sb[1])
+    assert np.max(np.abs(y - expect)) < 1e-15
