@@ -159,6 +159,31 @@ hyena_status hyena_forward(hyena_plan_t plan, const void* u, const void* const* 
     }
 }
 
+hyena_status hyena_nd_mixer_forward(hyena_plan_t plan, const hyena_nd_mixer* m, const void* H,
+                                    const float* D, void* y, void* workspace, void* stream)
+{
+    if (plan == nullptr) return fail(HYENA_ERR_INVALID_ARGUMENT, "plan is NULL");
+    const hy::Plan& p = plan->p;
+    if (p.ndims != 2 || p.order != 1)
+        return fail(HYENA_ERR_UNSUPPORTED, "the HyenaND mixer needs an ndims = 2, order 1 plan");
+    if (m == nullptr || m->q == nullptr || m->k == nullptr || m->v == nullptr ||
+        m->short_w == nullptr || H == nullptr || D == nullptr || y == nullptr)
+        return fail(HYENA_ERR_INVALID_ARGUMENT, "a required pointer is NULL");
+    if (!aligned16(m->q) || !aligned16(m->k) || !aligned16(m->v) || !aligned16(H) ||
+        !aligned16(D) || !aligned16(y))
+        return fail(HYENA_ERR_INVALID_ARGUMENT, "q, k, v, H, D and y must be 16-byte aligned");
+    const size_t nio = io_bytes(p);
+    if (overlaps(y, nio, m->q, nio) || overlaps(y, nio, m->k, nio) || overlaps(y, nio, m->v, nio))
+        return fail(HYENA_ERR_INVALID_ARGUMENT, "y overlaps q, k or v");
+    if (overlaps(y, nio, H, p.spectrum_bytes)) return fail(HYENA_ERR_INVALID_ARGUMENT, "y overlaps H");
+    if (overlaps(y, nio, D, (size_t)p.d * 4u)) return fail(HYENA_ERR_INVALID_ARGUMENT, "y overlaps D");
+    hyena_status st = check_ws(p, workspace);
+    if (st != HYENA_OK) return st;
+    if (overlaps(y, nio, workspace, p.workspace_bytes))
+        return fail(HYENA_ERR_INVALID_ARGUMENT, "y overlaps the workspace");
+    return hy::launch_rowcol2d_block(p, *m, H, D, y, workspace, stream);
+}
+
 hyena_status hyena_implicit_scratch_bytes(hyena_plan_t plan, int32_t hidden, size_t* bytes)
 {
     if (plan == nullptr || bytes == nullptr)

@@ -122,7 +122,8 @@ int64_t spec_elems_per_filter(const Plan& p)
 }
 
 hyena_status mp_forward(const Plan& p, const void* u, const void* const* gates, const void* H,
-                        const float* D, void* y, void* ws, void* stream)
+                        const float* D, void* y, void* ws, void* stream,
+                        const BlockArgs* blk = nullptr)
 {
     const hipStream_t s = (hipStream_t)stream;
     MpGeom g = base_geom(p);
@@ -146,6 +147,7 @@ hyena_status mp_forward(const Plan& p, const void* u, const void* const* gates, 
         oa.act = u;
         oa.F = F;
         oa.tw = tw;
+        if (blk) oa.blk = *blk;
         hyena_status st = outer(p, OUTER_IN, true, oa, col_blocks * g.ngroups, s);
         if (st != HYENA_OK) return st;
         for (int n = 0; n < p.order; ++n) {
@@ -157,7 +159,7 @@ hyena_status mp_forward(const Plan& p, const void* u, const void* const* gates, 
             ia.tw = tw;
             st = inner(p, INNER_CHAIN, ia, unit_blocks * g.ngroups * KP, s);
             if (st != HYENA_OK) return st;
-            oa.act = gates[n];
+            oa.act = blk ? nullptr : gates[n];
             oa.out = y;
             st = outer(p, n + 1 < p.order ? OUTER_MID : OUTER_OUT, true, oa, col_blocks * g.ngroups, s);
             if (st != HYENA_OK) return st;
@@ -313,6 +315,18 @@ hyena_status launch_rowcol2d_forward(const Plan& p, const void* u, const void* c
                                      void* stream)
 {
     return mp_forward(p, u, gates, H, D, y, ws, stream);
+}
+hyena_status launch_rowcol2d_block(const Plan& p, const hyena_nd_mixer& m, const void* H,
+                                   const float* D, void* y, void* ws, void* stream)
+{
+    BlockArgs b{};
+    b.q = m.q;
+    b.k = m.k;
+    b.v = m.v;
+    b.sw = m.short_w;
+    b.sb = m.short_b;
+    b.on = 1;
+    return mp_forward(p, nullptr, nullptr, H, D, y, ws, stream, &b);
 }
 hyena_status launch_rowcol2d_spectrum(const Plan& p, const void* h, void* H, void* ws, void* stream)
 {

@@ -24,6 +24,19 @@ struct MpShape {
     static constexpr int LW = FftShape<L>::LW | 1;
 };
 
+// HyenaND mixer inputs ("How HyenaND works", section "Putting it together:
+// the HyenaND operator"): with `on`, OUTER_IN reads q . SiLU(k) and OUTER_OUT
+// gates with SiLU(v), where q, k, v first pass a depthwise 3x3 short
+// convolution (zero padding) on the X x Y grid.
+struct BlockArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const float* sw;  // [3][d][3][3] short-conv taps of q, k, v
+    const float* sb;  // [3][d] biases, or NULL
+    int32_t on;
+};
+
 struct OuterArgs {
     MpGeom g;
     const void* act;   // u (IN), gate (MID, OUT)
@@ -31,6 +44,7 @@ struct OuterArgs {
     const void* filt;  // filter taps (SPEC), this filter index
     float2* F;         // workspace intermediate of this chunk
     const float2* tw;
+    BlockArgs blk;
 };
 
 struct InnerArgs {
@@ -52,6 +66,48 @@ __device__ __forceinline__ float2 act_load(const IO* base, int64_t row, int64_t 
         return make_float2(ld1<IO>(r), ld1<IO>(r + 1));
     }
     return make_float2(ld1<IO>(r), 0.0f);
+}
+
+__device__ __forceinline__ float silu(float x) { return x / (1.0f + expf(-x)); }
+
+// Short-conv taps of one channel pair (c0, c0 + 1) of tensor j (0 q, 1 k, 2 v).
+struct PairTaps {
+    float w[2][9];
+    float b[2];
+};
+
+__device__ __forceinline__ PairTaps pair_taps(const BlockArgs& k, int j, int64_t c0, int64_t d)
+{
+    PairTaps t;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const bool live = c0 + h < d;
+        const int64_t c = live ? c0 + h : c0;
+#pragma unroll
+        for (int i = 0; i < 9; ++i) t.w[h][i] = live ? k.sw[((int64_t)j * d + c) * 9 + i] : 0.0f;
+        t.b[h] = (live && k.sb) ? k.sb[(int64_t)j * d + c] : 0.0f;
+    }
+    return t;
+}
+
+// Depthwise 3x3 short convolution of one channel pair at grid point (p, q)
+// of batch row b: row = b X Y + p Y + q is the point's activation row.
+template <typename IO>
+__device__ __forceinline__ float2 short_conv(const IO* x, const PairTaps& t, int64_t row,
+                                             int64_t p, int64_t q, int64_t X, int64_t Y,
+                                             int64_t c0, int64_t d)
+{
+    float2 acc = make_float2(t.b[0], t.b[1]);
+#pragma unroll
+    for (int a = -1; a <= 1; ++a)
+#pragma unroll
+        for (int e = -1; e <= 1; ++e) {
+            if (p + a < 0 || p + a >= X || q + e < 0 || q + e >= Y) continue;
+            const float2 xv = act_load<IO>(x, row + a * Y + e, c0, d);
+            acc.x = fmaf(t.w[0][(a + 1) * 3 + e + 1], xv.x, acc.x);
+            acc.y = fmaf(t.w[1][(a + 1) * 3 + e + 1], xv.y, acc.y);
+        }
+    return acc;
 }
 
 template <typename IO>
@@ -190,9 +246,31 @@ __global__ void __launch_bounds__(kMpThreads, 2) hyena_mp_outer(OuterArgs a)
         // latencies overlap instead of adding up
         const IO* u = static_cast<const IO*>(a.act);
         float2 xin[GT];
-        tile_rows([&](int it, int, int, int64_t pq, bool ok, int64_t row) {
-            xin[it] = ok ? act_load<IO>(u, row, 2 * pq, g.d) : make_float2(0.0f, 0.0f);
-        });
+        if (a.blk.on) {
+            // HyenaND mixer input q . SiLU(k) after the short convolutions;
+            // this thread's channel pair is the same in every tile element
+            int64_t bq0, pq0;
+            bool l0;
+            pair_of_slot(g, group, (int)(threadIdx.x & (KP - 1)), bq0, pq0, l0);
+            const PairTaps tq = pair_taps(a.blk, 0, 2 * pq0, g.d);
+            const PairTaps tk = pair_taps(a.blk, 1, 2 * pq0, g.d);
+            const IO* qx = static_cast<const IO*>(a.blk.q);
+            const IO* kx = static_cast<const IO*>(a.blk.k);
+            tile_rows([&](int it, int, int s, int64_t pq, bool ok, int64_t row) {
+                float2 z = make_float2(0.0f, 0.0f);
+                if (ok) {
+                    const int64_t pp = (row % g.N) / g.so, qq = s;
+                    const float2 qv = short_conv<IO>(qx, tq, row, pp, qq, g.Lb_live, g.so, 2 * pq, g.d);
+                    const float2 kv = short_conv<IO>(kx, tk, row, pp, qq, g.Lb_live, g.so, 2 * pq, g.d);
+                    z = make_float2(qv.x * silu(kv.x), qv.y * silu(kv.y));
+                }
+                xin[it] = z;
+            });
+        } else {
+            tile_rows([&](int it, int, int, int64_t pq, bool ok, int64_t row) {
+                xin[it] = ok ? act_load<IO>(u, row, 2 * pq, g.d) : make_float2(0.0f, 0.0f);
+            });
+        }
         tile_rows([&](int it, int fq, int s, int64_t, bool, int64_t) {
             sre[fq * LW + lpad(s)] = xin[it].x;
             sim[fq * LW + lpad(s)] = xin[it].y;
@@ -241,9 +319,27 @@ __global__ void __launch_bounds__(kMpThreads, 2) hyena_mp_outer(OuterArgs a)
         load_column<LA, +1>(v, Fcol, twstep, tau, col_live, g.four_step && o > 0);
         const IO* gate = static_cast<const IO*>(a.act);
         float2 gval[GT];
-        tile_rows([&](int it, int, int, int64_t pq, bool ok, int64_t row) {
-            gval[it] = ok ? act_load<IO>(gate, row, 2 * pq, g.d) : make_float2(0.0f, 0.0f);
-        });
+        if (MODE == OUTER_OUT && a.blk.on) {
+            // HyenaND outer gate SiLU(v) after the short convolution
+            int64_t bq0, pq0;
+            bool l0;
+            pair_of_slot(g, group, (int)(threadIdx.x & (KP - 1)), bq0, pq0, l0);
+            const PairTaps tv = pair_taps(a.blk, 2, 2 * pq0, g.d);
+            const IO* vx = static_cast<const IO*>(a.blk.v);
+            tile_rows([&](int it, int, int s, int64_t pq, bool ok, int64_t row) {
+                float2 gv = make_float2(0.0f, 0.0f);
+                if (ok) {
+                    const int64_t pp = (row % g.N) / g.so;
+                    const float2 vv = short_conv<IO>(vx, tv, row, pp, s, g.Lb_live, g.so, 2 * pq, g.d);
+                    gv = make_float2(silu(vv.x), silu(vv.y));
+                }
+                gval[it] = gv;
+            });
+        } else {
+            tile_rows([&](int it, int, int, int64_t pq, bool ok, int64_t row) {
+                gval[it] = ok ? act_load<IO>(gate, row, 2 * pq, g.d) : make_float2(0.0f, 0.0f);
+            });
+        }
         inv_lds_to_regs<LA, true, true>(v, re, im, a.tw, g.tw_a, tau);
         __syncthreads();
         tile_rows([&](int it, int fq, int s, int64_t, bool, int64_t) {

@@ -36,8 +36,14 @@ EXPORTED_SYMBOLS = (
     "hyena_forward", "hyena_spectrum_export", "hyena_plan_destroy", "hyena_status_string",
     "hyena_last_error", "hyena_timing_begin", "hyena_timing_end", "hyena_timing_kernel",
     "hyena_timing_release", "hyena_implicit_scratch_bytes", "hyena_filter_spectrum_implicit",
-    "hyena_plan_create_ex",
+    "hyena_plan_create_ex", "hyena_nd_mixer_forward",
 )
+
+
+class NdMixer(ctypes.Structure):
+    """hyena_nd_mixer: q, k, v and the short-convolution taps (device pointers)."""
+    _fields_ = [("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+                ("short_w", ctypes.c_void_p), ("short_b", ctypes.c_void_p)]
 
 HYENA_FLAG_CIRCULAR = 1
 
@@ -93,13 +99,15 @@ def load():
                 [ctypes.POINTER(ctypes.c_double)] * 3
             lib.hyena_timing_release.argtypes = []
             lib.hyena_implicit_scratch_bytes.argtypes = [p, i32, ctypes.POINTER(sz)]
+            lib.hyena_nd_mixer_forward.argtypes = [p, ctypes.POINTER(NdMixer), p, p, p, p, p]
             lib.hyena_filter_spectrum_implicit.argtypes = [p, ctypes.POINTER(ImplicitFilter), p, p,
                                                            p, p]
             for name in ("hyena_plan_create", "hyena_plan_create_ex", "hyena_plan_query", "hyena_workspace_init",
                          "hyena_filter_spectrum", "hyena_forward", "hyena_spectrum_export",
                          "hyena_plan_destroy", "hyena_timing_begin", "hyena_timing_end",
                          "hyena_timing_kernel", "hyena_timing_release",
-                         "hyena_implicit_scratch_bytes", "hyena_filter_spectrum_implicit"):
+                         "hyena_implicit_scratch_bytes", "hyena_filter_spectrum_implicit",
+                         "hyena_nd_mixer_forward"):
                 getattr(lib, name).restype = ctypes.c_int
             _lib = lib
     return _lib
@@ -178,6 +186,11 @@ def hyena_implicit_scratch_bytes(plan, hidden):
 def hyena_filter_spectrum_implicit(plan, f, H, workspace, scratch, stream=0):
     return load().hyena_filter_spectrum_implicit(plan, ctypes.byref(f) if f is not None else None,
                                                  H, workspace, scratch, stream)
+
+
+def hyena_nd_mixer_forward(plan, mixer, H, D, y, workspace, stream=0):
+    return load().hyena_nd_mixer_forward(plan, ctypes.byref(mixer) if mixer is not None else None,
+                                         H, D, y, workspace, stream)
 
 
 def hyena_spectrum_export(plan, H, natural, stream=0):
@@ -310,6 +323,22 @@ class Plan:
                              H.data_ptr(), D.data_ptr(), y.data_ptr(), self.workspace.data_ptr(),
                              self.stream()),
                "hyena_forward")
+        return y
+
+    def nd_mixer(self, q, k, v, short_w, short_b, H, D, y=None):
+        """HyenaND mixer (ndims = 2, order 1): y = SiLU(sc(v)) . (K * z + D z),
+        z = sc(q) . SiLU(sc(k)); short_w float32 [3, d, 3, 3], short_b [3, d] or None."""
+        q, k, v = self._io(q, "q"), self._io(k, "k"), self._io(v, "v")
+        for t in (short_w, D) + ((short_b,) if short_b is not None else ()):
+            if t.dtype != self.torch.float32 or not t.is_contiguous():
+                raise ValueError("short-conv taps, biases and D must be contiguous float32")
+        if y is None:
+            y = self.torch.empty_like(q)
+        m = NdMixer(q.data_ptr(), k.data_ptr(), v.data_ptr(), short_w.data_ptr(),
+                    short_b.data_ptr() if short_b is not None else None)
+        _check(hyena_nd_mixer_forward(self.handle, m, H.data_ptr(), D.data_ptr(), y.data_ptr(),
+                                      self.workspace.data_ptr(), self.stream()),
+               "hyena_nd_mixer_forward")
         return y
 
     def export_spectrum(self, H):

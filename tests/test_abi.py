@@ -241,3 +241,24 @@ def test_periodic_boundary_plans(N, dims, path, flags, code):
         assert p == 1
         assert spec == 2 * 4 * (N // 4) * 16  # order * d * (N/4 entries) * 16 bytes
         hyena.hyena_plan_destroy(plan)
+
+
+def test_nd_mixer_validation():
+    m = hyena.NdMixer(16, 16, 16, 16, None)
+    _, p1 = hyena.hyena_plan_create(1, 64, 4, 1, [64])
+    assert hyena.hyena_nd_mixer_forward(p1, m, 16, 16, 16, 16) == hyena.HYENA_ERR_UNSUPPORTED
+    hyena.hyena_plan_destroy(p1)
+    _, p2 = hyena.hyena_plan_create(1, 64, 4, 2, [8, 8])
+    assert hyena.hyena_nd_mixer_forward(p2, m, 16, 16, 16, 16) == hyena.HYENA_ERR_UNSUPPORTED
+    hyena.hyena_plan_destroy(p2)
+    _, p3 = hyena.hyena_plan_create(1, 64, 4, 1, [8, 8])
+    assert hyena.hyena_nd_mixer_forward(p3, None, 16, 16, 16, 16) == \
+        hyena.HYENA_ERR_INVALID_ARGUMENT
+    bad = hyena.NdMixer(16, None, 16, 16, None)
+    assert hyena.hyena_nd_mixer_forward(p3, bad, 16, 16, 16, 16) == \
+        hyena.HYENA_ERR_INVALID_ARGUMENT
+    # y on top of q
+    same = hyena.NdMixer(4096, 16, 16, 16, None)
+    assert hyena.hyena_nd_mixer_forward(p3, same, 16, 16, 4096, 16) == \
+        hyena.HYENA_ERR_INVALID_ARGUMENT
+    hyena.hyena_plan_destroy(p3)

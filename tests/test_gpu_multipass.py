@@ -173,3 +173,34 @@ def test_f16_storage_multipass():
         e = rel_err(y, oracle_ref(inp, method=oracle.FFT))
         say(f"[gpu] f16 dims={inp.dims} rel err {e:.3e}")
         assert e < 5e-3
+
+
+@pytest.mark.parametrize("X,Y,d,dtype,bias", [(8, 8, 3, synth.F32, True), (16, 32, 4, synth.F32, False),
+                                              (64, 64, 2, synth.F32, True),
+                                              (16, 16, 4, synth.BF16, True)])
+def test_hyenand_mixer(X, Y, d, dtype, bias):
+    # short convs + q . SiLU(k) fused into the first 2D pass, SiLU(v) into the last
+    import torch
+    from gpu_util import from_torch, to_torch
+    from long_convolution_sequence_rfft_amd import hyena
+    inp = synth.make_2d(B=2, X=X, Y=Y, d=d, order=1, dtype=dtype, seed=95)
+    rng = np.random.default_rng(96)
+    k = synth._store(rng.standard_normal((2, X, Y, d)), dtype)
+    v = synth._store(rng.standard_normal((2, X, Y, d)), dtype)
+    sw = rng.normal(size=(3, d, 3, 3)).astype(np.float32) * 0.5
+    sb = rng.normal(size=(3, d)).astype(np.float32) * 0.1 if bias else None
+    io = hyena.HYENA_F32 if dtype == synth.F32 else hyena.HYENA_BF16
+    say(f"[gpu] mixer {X}x{Y} d={d} {dtype} bias={bias}")
+    plan = hyena.Plan(2, d, 1, (X, Y), io_dtype=io)
+    H = plan.spectrum(to_torch(inp.h, dtype))
+    y = plan.nd_mixer(to_torch(inp.u, dtype), to_torch(k, dtype), to_torch(v, dtype),
+                      torch.from_numpy(sw).cuda(),
+                      torch.from_numpy(sb).cuda() if bias else None, H,
+                      torch.from_numpy(inp.D[0].copy()).cuda())
+    torch.cuda.synchronize()
+    q64, _, K64, D64 = inp.f64()
+    ref = oracle.hyena2d_block(q64, synth.stored_to_f64(k, dtype), synth.stored_to_f64(v, dtype),
+                               sw, sb, K64[0], D64[0], oracle.FFT)
+    e = rel_err(from_torch(y, dtype), ref)
+    say(f"[gpu] mixer rel err {e:.3e}")
+    assert e < (TOL_F32 if dtype == synth.F32 else TOL_BF16)
