@@ -170,6 +170,21 @@ def run_workload(idx, steps, warmup, min_rotation_bytes=600 << 20):
     torch.cuda.synchronize()
     spectrum_ms = e0.elapsed_time(e1) / 3
     del h
+    # spectrum from an implicit filter (sine MLP over positions, K = 8
+    # frequencies, width 64): the taps are generated on the device
+    implicit_ms = None
+    if cfg["kind"] == "1d":
+        w = synth.make_implicit(cfg["d"], cfg["order"], K=8, H=64, seed=idx)
+        devw = {k: torch.from_numpy(v).cuda() for k, v in w.arrays().items()}
+        Hi = plan.spectrum_implicit(omega=w.omega, **devw)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(3):
+            plan.spectrum_implicit(omega=w.omega, H=Hi, **devw)
+        e1.record()
+        torch.cuda.synchronize()
+        implicit_ms = e0.elapsed_time(e1) / 3
+        del Hi, devw
 
     bytes_alg = algorithmic_bytes(cfg, "bf16" if spec_dtype == hyena.HYENA_BF16 else "f32")
     nsets = max(1, min(4, int(math.ceil(min_rotation_bytes / bytes_alg))))
@@ -228,6 +243,7 @@ def run_workload(idx, steps, warmup, min_rotation_bytes=600 << 20):
         "ms_per_step": ms,
         "tc_per_s": tc / (ms * 1e-3),
         "spectrum_ms": spectrum_ms,
+        "implicit_spectrum_ms": implicit_ms,
         "rotation_sets": nsets,
         "algorithmic_bytes": bytes_alg,
         "algorithmic_flops": flops,
