@@ -206,15 +206,17 @@ typedef struct hyena_implicit_filter {
 } hyena_implicit_filter;
 
 /* Bytes of the caller-owned scratch buffer hyena_filter_spectrum_implicit
- * needs for this plan and hidden width (hidden features of every position;
- * on paths other than the single-channel one also the taps themselves). */
+ * needs for this plan and hidden width: the hidden features of every
+ * position (float32, width rounded up to 16) and the taps [order][d][N] in
+ * the plan's io dtype. */
 hyena_status hyena_implicit_scratch_bytes(hyena_plan_t plan, int32_t hidden, size_t* bytes);
 
 /*
- * hyena_filter_spectrum with the taps generated from `f` on the device.  On
- * the single-channel path (N = M/2 <= 8192) the taps are evaluated inside the
- * spectrum kernel and never stored; elsewhere they are written to `scratch`
- * (in the plan's io dtype) and transformed as by hyena_filter_spectrum.
+ * hyena_filter_spectrum with the taps generated from `f` on the device: the
+ * hidden features z2 of every position, then the taps as one dense
+ * contraction W3 z2 (times the window), written to `scratch` in the plan's
+ * io dtype and transformed as by hyena_filter_spectrum.  The caller never
+ * holds the taps.  order * d must be at most 4194240.
  * scratch: device buffer of hyena_implicit_scratch_bytes, 16-byte aligned,
  * not shared with concurrently running calls.  `f` is read on the host
  * during the call; the arrays it points to must stay alive until the stream

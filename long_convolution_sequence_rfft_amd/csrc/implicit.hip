@@ -5,28 +5,26 @@
 //
 //   hyena_implicit_hidden: z2[t] = sin(omega (W2 sin(omega (W1 gamma(t) + b1))
 //                          + b2)) for every position t, into the scratch.
-//   single-channel path:   the spectrum kernel forms the taps from z2 itself
-//                          (hyena_lds1d_real_spectrum<..., true>).
-//   other paths:           hyena_implicit_taps writes the taps to the scratch
-//                          in the plan's storage type, then the plan's usual
-//                          spectrum launch transforms them.
+//   hyena_implicit_taps:   h = window . (W3 z2 + b3), a dense [order d] x [N]
+//                          contraction over the hidden width, tiled through
+//                          LDS, written to the scratch in the plan's storage
+//                          type; then the plan's usual spectrum launch
+//                          transforms the taps.
 #include "dispatch.h"
 #include "lds1d_kernels.h"
 
 namespace hy {
-
-HY_LDS1D_REAL_SIZES(HY_LDS1D_REAL_EXTERN, float, float)
-HY_LDS1D_REAL_SIZES(HY_LDS1D_REAL_EXTERN, uint16_t, uint16_t)
-HY_LDS1D_REAL_SIZES(HY_LDS1D_REAL_EXTERN, uint16_t, float)
-HY_LDS1D_REAL_SIZES(HY_LDS1D_REAL_EXTERN, _Float16, float)
 
 namespace {
 
 constexpr int kImpMaxFreqs = 64;
 constexpr int kImpMaxHidden = 256;
 constexpr int kImpPos = 16;  // positions per workgroup of the hidden kernel
+constexpr int kTapTile = 64;  // taps tile: 64 filter rows x 64 positions
+constexpr int kTapK = 16;     // hidden features per LDS chunk
 
-int64_t hidden_pad(int32_t H) { return (H + 3) / 4 * 4; }
+// hidden width padded to whole chunks of the taps contraction (zero features)
+int64_t hidden_pad(int32_t H) { return (H + kTapK - 1) / kTapK * kTapK; }
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
 struct HiddenArgs {
@@ -99,31 +97,101 @@ __global__ void __launch_bounds__(kImpMaxHidden) hyena_implicit_hidden(HiddenArg
     }
 }
 
-// Taps [order d][N] in the storage type, one thread per tap.
-template <typename IO>
-__global__ void __launch_bounds__(256) hyena_implicit_taps(ImplicitTaps im, IO* h, int64_t N)
-{
-    __shared__ float w3s[kImpMaxHidden];
-    const int64_t o = blockIdx.y;
-    for (int i = threadIdx.x; i < im.hp; i += blockDim.x)
-        w3s[i] = i < im.H ? im.W3[o * im.H + i] : 0.0f;
-    __syncthreads();
-    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (t >= N) return;
-    st1<IO>(h + o * N + t, implicit_tap(im, w3s, im.b3[o], im.alpha[o], t));
-}
+struct TapArgs {
+    const float* z2;  // [N][hp]
+    const float* W3;  // [rows][H]
+    const float* b3;
+    const float* alpha;
+    void* h;  // [rows][N], storage type
+    int64_t N, rows;
+    int32_t H, hp;
+};
 
-bool single_channel(const Plan& p) { return p.path == HYENA_PATH_LDS1D && p.lds_io == 3; }
+// Taps h[o][t] = exp(-alpha[o] t) (b3[o] + sum_j W3[o][j] z2[t][j]) for one
+// tile of 64 filter rows o = n d + c by 64 positions t.  256 threads, each
+// accumulating a 4 x 4 block; the contraction over the hidden width runs in
+// chunks of kTapK features, both operands staged through LDS transposed
+// ([j][o] and [j][t]) so the inner loop reads one float4 of each.
+template <typename IO>
+__global__ void __launch_bounds__(256) hyena_implicit_taps(TapArgs a)
+{
+    constexpr int TT = kTapTile, KC = kTapK, LDW = TT + 4;
+    __shared__ __align__(16) float ws[KC][LDW];
+    __shared__ __align__(16) float zs[KC][LDW];
+    const int e = threadIdx.x;
+    const int tx = e & 15, ty = e >> 4;
+    const int64_t t0 = (int64_t)blockIdx.x * TT, o0 = (int64_t)blockIdx.y * TT;
+    // staging roles: row (or position) e / 4 of the tile, features 4 (e % 4) ..
+    const int sl = e >> 2, sj = (e & 3) * 4;
+    const int64_t so = o0 + sl, st = t0 + sl;
+
+    float acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) acc[i][k] = 0.0f;
+
+    for (int j0 = 0; j0 < a.hp; j0 += KC) {
+        float wv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int j = j0 + sj + i;
+            wv[i] = (so < a.rows && j < a.H) ? a.W3[so * a.H + j] : 0.0f;
+        }
+        const float4 zv = st < a.N ? *reinterpret_cast<const float4*>(a.z2 + st * a.hp + j0 + sj)
+                                   : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        __syncthreads();  // previous chunk fully consumed
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ws[sj + i][sl] = wv[i];
+        zs[sj + 0][sl] = zv.x;
+        zs[sj + 1][sl] = zv.y;
+        zs[sj + 2][sl] = zv.z;
+        zs[sj + 3][sl] = zv.w;
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < KC; ++k) {
+            const float4 wa = *reinterpret_cast<const float4*>(&ws[k][4 * ty]);
+            const float4 zb = *reinterpret_cast<const float4*>(&zs[k][4 * tx]);
+            const float wr[4] = {wa.x, wa.y, wa.z, wa.w};
+            const float zc[4] = {zb.x, zb.y, zb.z, zb.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int c = 0; c < 4; ++c) acc[i][c] = fmaf(wr[i], zc[c], acc[i][c]);
+        }
+    }
+
+    IO* h = static_cast<IO*>(a.h);
+    const int64_t t = t0 + 4 * tx;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int64_t o = o0 + 4 * ty + i;
+        if (o >= a.rows) break;
+        const float b3 = a.b3[o], al = a.alpha[o];
+        float val[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) val[c] = expf(-al * (float)(t + c)) * (b3 + acc[i][c]);
+        IO* row = h + o * a.N + t;
+        if ((a.N & 3) == 0 && t + 3 < a.N) {
+            // row start and t are multiples of 4: two aligned sample pairs
+            using PR = typename PairRaw<IO>::type;
+            reinterpret_cast<PR*>(row)[0] = narrow_pair<IO>(make_float2(val[0], val[1]));
+            reinterpret_cast<PR*>(row)[1] = narrow_pair<IO>(make_float2(val[2], val[3]));
+        } else {
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+                if (t + c < a.N) st1<IO>(row + c, val[c]);
+        }
+    }
+}
 
 }  // namespace
 
 size_t implicit_scratch_bytes(const Plan& p, int32_t hidden)
 {
-    size_t b = align256((size_t)p.N * (size_t)hidden_pad(hidden) * 4u);
-    if (!single_channel(p))
-        b += align256((size_t)p.order * (size_t)p.d * (size_t)p.N *
-                      (p.io_dtype == HYENA_F32 ? 4u : 2u));
-    return b;
+    return align256((size_t)p.N * (size_t)hidden_pad(hidden) * 4u) +
+           align256((size_t)p.order * (size_t)p.d * (size_t)p.N *
+                    (p.io_dtype == HYENA_F32 ? 4u : 2u));
 }
 
 hyena_status launch_implicit_spectrum(const Plan& p, const hyena_implicit_filter& f, void* H,
@@ -134,6 +202,8 @@ hyena_status launch_implicit_spectrum(const Plan& p, const hyena_implicit_filter
         return fail(HYENA_ERR_UNSUPPORTED, "implicit filter: n_freqs must be in 0..64");
     if (f.hidden < 1 || f.hidden > kImpMaxHidden)
         return fail(HYENA_ERR_UNSUPPORTED, "implicit filter: hidden must be in 1..256");
+    if ((int64_t)p.order * p.d > 65535ll * kTapTile)
+        return fail(HYENA_ERR_UNSUPPORTED, "implicit filter: order * d must be at most 4194240");
     HiddenArgs h{};
     h.W1 = f.W1;
     h.b1 = f.b1;
@@ -150,51 +220,28 @@ hyena_status launch_implicit_spectrum(const Plan& p, const hyena_implicit_filter
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(HYENA_ERR_DEVICE, hipGetErrorString(e));
 
-    ImplicitTaps im{};
-    im.z2 = h.z2;
-    im.W3 = f.W3;
-    im.b3 = f.b3;
-    im.alpha = f.alpha;
-    im.H = f.hidden;
-    im.hp = h.hp;
-    if (single_channel(p)) {
-        Lds1dSpecArgs a{};
-        a.spec = H;
-        a.tw = static_cast<const float2*>(ws);
-        a.twm = a.tw + p.seg[4].off;
-        a.N = p.N;
-        a.d = p.d;
-        a.npairs = p.npairs;
-        a.nblocks = (int64_t)p.order * p.d;
-        a.tw_off = TwOffsets{(int32_t)p.seg[0].off, (int32_t)p.seg[1].off, (int32_t)p.seg[2].off,
-                             (int32_t)p.seg[3].off};
-        a.imp = im;
-        const int64_t L = p.M / 2;
-        return by_storage(p, [&](auto io, auto sp) -> hyena_status {
-            using IO = typename decltype(io)::type;
-            using SP = typename decltype(sp)::type;
-            switch (L) {
-#define HY_CASE(LL, I_, S_) \
-    case LL:                                                                      \
-        return p.circular ? lds1d_real_spectrum_launch<LL, IO, SP, true, true>(a, s) \
-                          : lds1d_real_spectrum_launch<LL, IO, SP, true, false>(a, s);
-                HY_LDS1D_REAL_SIZES(HY_CASE, 0, 0)
-#undef HY_CASE
-                default: return fail(HYENA_ERR_UNSUPPORTED, "implicit filter: unsupported length");
-            }
-        });
-    }
+    TapArgs ta{};
+    ta.z2 = h.z2;
+    ta.W3 = f.W3;
+    ta.b3 = f.b3;
+    ta.alpha = f.alpha;
+    ta.N = p.N;
+    ta.rows = (int64_t)p.order * p.d;
+    ta.H = f.hidden;
+    ta.hp = h.hp;
     char* taps = static_cast<char*>(scratch) + align256((size_t)p.N * (size_t)h.hp * 4u);
-    const dim3 grid((unsigned)((p.N + 255) / 256), (unsigned)(p.order * p.d));
+    ta.h = taps;
+    const dim3 grid((unsigned)((p.N + kTapTile - 1) / kTapTile),
+                    (unsigned)((ta.rows + kTapTile - 1) / kTapTile));
     if (p.io_dtype == HYENA_F32)
         HY_LAUNCH(kernel_label("hyena_implicit_taps", "float"), hyena_implicit_taps<float>, grid,
-                  dim3(256), 0, s, im, reinterpret_cast<float*>(taps), p.N);
+                  dim3(256), 0, s, ta);
     else if (p.io_dtype == HYENA_F16)
         HY_LAUNCH(kernel_label("hyena_implicit_taps", "_Float16"), hyena_implicit_taps<_Float16>,
-                  grid, dim3(256), 0, s, im, reinterpret_cast<_Float16*>(taps), p.N);
+                  grid, dim3(256), 0, s, ta);
     else
         HY_LAUNCH(kernel_label("hyena_implicit_taps", "unsigned short"), hyena_implicit_taps<uint16_t>,
-                  grid, dim3(256), 0, s, im, reinterpret_cast<uint16_t*>(taps), p.N);
+                  grid, dim3(256), 0, s, ta);
     e = hipGetLastError();
     if (e != hipSuccess) return fail(HYENA_ERR_DEVICE, hipGetErrorString(e));
     if (p.path == HYENA_PATH_LDS1D) return launch_lds1d_spectrum(p, taps, H, ws, stream);

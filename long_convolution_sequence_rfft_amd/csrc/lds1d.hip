@@ -207,8 +207,8 @@ hyena_status real_spec_by_l(int64_t L, bool circ, const Lds1dSpecArgs& a, hipStr
     switch (L) {
 #define HY_CASE(LL, I, S_)                                                          \
     case LL:                                                                        \
-        return circ ? lds1d_real_spectrum_launch<LL, IO, SP, false, true>(a, s)     \
-                    : lds1d_real_spectrum_launch<LL, IO, SP, false, false>(a, s);
+        return circ ? lds1d_real_spectrum_launch<LL, IO, SP, true>(a, s)     \
+                    : lds1d_real_spectrum_launch<LL, IO, SP, false>(a, s);
         HY_LDS1D_REAL_SIZES(HY_CASE, IO, SP)
 #undef HY_CASE
         default: return fail(HYENA_ERR_UNSUPPORTED, "LDS1D: unsupported single-channel length");

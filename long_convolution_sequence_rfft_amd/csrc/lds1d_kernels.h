@@ -35,17 +35,6 @@ struct Lds1dFwdArgs {
     TwOffsets tw_off;
 };
 
-// Implicit-filter taps evaluated on the fly: h[o][t] = exp(-alpha[o] t)
-// (b3[o] + W3[o] . z2[t]), o = n d + c, with z2 the hidden features
-// [N][hp] (hp = H rounded up to 4, zero padded).
-struct ImplicitTaps {
-    const float* z2;
-    const float* W3;  // [order d][H]
-    const float* b3;
-    const float* alpha;
-    int32_t H, hp;
-};
-
 struct Lds1dSpecArgs {
     const void* h;
     void* spec;
@@ -53,25 +42,7 @@ struct Lds1dSpecArgs {
     const float2* twm;
     int64_t N, d, npairs, nblocks;
     TwOffsets tw_off;
-    ImplicitTaps imp;
 };
-
-// Tap t of filter row `o` from the hidden features (w3: the row of W3 in LDS,
-// zero padded to hp).
-__device__ __forceinline__ float implicit_tap(const ImplicitTaps& im, const float* w3, float b3,
-                                              float alpha, int64_t t)
-{
-    const float4* z = reinterpret_cast<const float4*>(im.z2 + t * im.hp);
-    float acc = b3;
-    for (int i = 0; i < im.hp / 4; ++i) {
-        const float4 zz = z[i];
-        acc = fmaf(w3[4 * i], zz.x, acc);
-        acc = fmaf(w3[4 * i + 1], zz.y, acc);
-        acc = fmaf(w3[4 * i + 2], zz.z, acc);
-        acc = fmaf(w3[4 * i + 3], zz.w, acc);
-    }
-    return expf(-alpha * (float)t) * acc;
-}
 
 // How the forward pass reaches the activations (channels last in memory).
 //   IO_PAIR: channel-pair kernel (hyena_lds1d_forward), each lane loading its
@@ -284,43 +255,26 @@ __global__ void __launch_bounds__(FftShape<L>::T, 2) hyena_lds1d_real_forward(Ld
 
 // Filter spectrum, single-channel form: one workgroup per (filter n, channel
 // c); entries (S, Dl) / L, the 1/L of the unscaled inverse transform folded in.
-// IMPL: the taps come from the implicit filter (a.imp) instead of a.h.
 // CIRC: periodic boundary (N = M taps, no zero padding).
-template <int L, typename IO, typename SP, bool IMPL, bool CIRC>
+template <int L, typename IO, typename SP, bool CIRC>
 __global__ void __launch_bounds__(FftShape<L>::T, 2) hyena_lds1d_real_spectrum(Lds1dSpecArgs a)
 {
     using S = FftShape<L>;
     constexpr int T = S::T, PTS = S::PTS, R0 = S::R0;
     constexpr int RIN = CIRC ? R0 : R0 / 2;
     __shared__ float smem[2 * S::LW];
-    __shared__ float w3s[IMPL ? 256 : 1];
     const int tau = threadIdx.x;
     const int64_t lin = blockIdx.x;  // n * d + c
     const int j1 = tau, j2 = tau ? 2 * T - tau : T;
 
     float2 v[PTS];
-    if constexpr (IMPL) {
-        for (int i = tau; i < a.imp.hp; i += T)
-            w3s[i] = i < a.imp.H ? a.imp.W3[lin * a.imp.H + i] : 0.0f;
-        const float b3 = a.imp.b3[lin], al = a.imp.alpha[lin];
-        __syncthreads();
+    const IO* h = static_cast<const IO*>(a.h) + lin * a.N;
 #pragma unroll
-        for (int q = 0; q < S::Q0; ++q)
+    for (int q = 0; q < S::Q0; ++q) {
+        const uint32_t lane_off = (uint32_t)(tau + q * T) * 2u * (uint32_t)sizeof(IO);
 #pragma unroll
-            for (int r = 0; r < RIN; ++r) {
-                const int64_t t = 2 * (int64_t)(tau + q * T + r * (L / R0));
-                v[q * R0 + r] = make_float2(implicit_tap(a.imp, w3s, b3, al, t),
-                                            implicit_tap(a.imp, w3s, b3, al, t + 1));
-            }
-    } else {
-        const IO* h = static_cast<const IO*>(a.h) + lin * a.N;
-#pragma unroll
-        for (int q = 0; q < S::Q0; ++q) {
-            const uint32_t lane_off = (uint32_t)(tau + q * T) * 2u * (uint32_t)sizeof(IO);
-#pragma unroll
-            for (int r = 0; r < RIN; ++r)
-                v[q * R0 + r] = widen_pair<IO>(load_pair_raw(h + (size_t)r * (L / R0) * 2, lane_off));
-        }
+        for (int r = 0; r < RIN; ++r)
+            v[q * R0 + r] = widen_pair<IO>(load_pair_raw(h + (size_t)r * (L / R0) * 2, lane_off));
     }
     fwd_transform<L, !CIRC>(v, smem, smem + S::LW, a.tw, a.tw_off, tau, j1, j2, false, [] {});
     SP* spec = static_cast<SP*>(a.spec) + lin * (int64_t)(L / 2) * kEntryElems;
@@ -337,12 +291,11 @@ hyena_status lds1d_real_forward_launch(const Lds1dFwdArgs& a, hipStream_t s)
     return e == hipSuccess ? HYENA_OK : fail(HYENA_ERR_DEVICE, hipGetErrorString(e));
 }
 
-template <int L, typename IO, typename SP, bool IMPL, bool CIRC>
+template <int L, typename IO, typename SP, bool CIRC>
 hyena_status lds1d_real_spectrum_launch(const Lds1dSpecArgs& a, hipStream_t s)
 {
-    HY_LAUNCH(kernel_label("hyena_lds1d_real_spectrum", L, type_label<IO>(), type_label<SP>(), IMPL,
-                           CIRC),
-              (hyena_lds1d_real_spectrum<L, IO, SP, IMPL, CIRC>), dim3((unsigned)a.nblocks),
+    HY_LAUNCH(kernel_label("hyena_lds1d_real_spectrum", L, type_label<IO>(), type_label<SP>(), CIRC),
+              (hyena_lds1d_real_spectrum<L, IO, SP, CIRC>), dim3((unsigned)a.nblocks),
               dim3(FftShape<L>::T), 0, s, a);
     const hipError_t e = hipGetLastError();
     return e == hipSuccess ? HYENA_OK : fail(HYENA_ERR_DEVICE, hipGetErrorString(e));
@@ -387,25 +340,17 @@ hyena_status lds1d_spectrum_launch(const Lds1dSpecArgs& a, hipStream_t s)
     extern template hyena_status lds1d_spectrum_launch<M, IO, SP>(const Lds1dSpecArgs&,          \
                                                                   hipStream_t);
 
-// single-channel kernels: (L, IO, SP) x {zero-padded, periodic}; the
-// implicit-filter spectrum variants are instantiated separately
+// single-channel kernels: (L, IO, SP) x {zero-padded, periodic}
 #define HY_LDS1D_REAL_INST_B(L, IO, SP, CIRC, EXT)                                                 \
     EXT template hyena_status lds1d_real_forward_launch<L, IO, SP, CIRC>(const Lds1dFwdArgs&,      \
                                                                         hipStream_t);             \
-    EXT template hyena_status lds1d_real_spectrum_launch<L, IO, SP, false, CIRC>(                 \
-        const Lds1dSpecArgs&, hipStream_t);
-#define HY_LDS1D_IMPL_INST_B(L, IO, SP, EXT)                                                       \
-    EXT template hyena_status lds1d_real_spectrum_launch<L, IO, SP, true, false>(                 \
-        const Lds1dSpecArgs&, hipStream_t);                                                        \
-    EXT template hyena_status lds1d_real_spectrum_launch<L, IO, SP, true, true>(                  \
-        const Lds1dSpecArgs&, hipStream_t);
+    EXT template hyena_status lds1d_real_spectrum_launch<L, IO, SP, CIRC>(const Lds1dSpecArgs&,    \
+                                                                         hipStream_t);
 
 #define HY_LDS1D_REAL_INSTANTIATE(L, IO, SP) HY_LDS1D_REAL_INST_B(L, IO, SP, false, )
 #define HY_LDS1D_CIRC_INSTANTIATE(L, IO, SP) HY_LDS1D_REAL_INST_B(L, IO, SP, true, )
-#define HY_LDS1D_IMPLICIT_INSTANTIATE(L, IO, SP) HY_LDS1D_IMPL_INST_B(L, IO, SP, )
 #define HY_LDS1D_REAL_EXTERN(L, IO, SP)                 \
     HY_LDS1D_REAL_INST_B(L, IO, SP, false, extern)      \
-    HY_LDS1D_REAL_INST_B(L, IO, SP, true, extern)       \
-    HY_LDS1D_IMPL_INST_B(L, IO, SP, extern)
+    HY_LDS1D_REAL_INST_B(L, IO, SP, true, extern)
 
 }  // namespace hy

@@ -300,14 +300,19 @@ class Plan:
         f = ImplicitFilter((m - 1) // 2, hidden, float(omega), *[t.data_ptr() for t in ws])
         st, nbytes = hyena_implicit_scratch_bytes(self.handle, hidden)
         _check(st, "hyena_implicit_scratch_bytes")
-        scratch = self.torch.empty(max(nbytes, 256), dtype=self.torch.uint8, device=self.device)
+        # kept with the plan and reused, like the workspace (calls of one plan
+        # must not run concurrently on different streams)
+        scratch = getattr(self, "_implicit_scratch", None)
+        if scratch is None or scratch.numel() < nbytes:
+            scratch = self._implicit_scratch = None
+            scratch = self.torch.empty(max(nbytes, 256), dtype=self.torch.uint8, device=self.device)
         if H is None:
             H = self.torch.empty(self.spectrum_bytes, dtype=self.torch.uint8, device=self.device)
         _check(hyena_filter_spectrum_implicit(self.handle, f, H.data_ptr(),
                                               self.workspace.data_ptr(), scratch.data_ptr(),
                                               self.stream()),
                "hyena_filter_spectrum_implicit")
-        self._implicit_scratch = scratch  # alive until the stream work is done
+        self._implicit_scratch = scratch
         return H
 
     def forward(self, u, gates, H, D, y=None):

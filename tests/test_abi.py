@@ -193,10 +193,11 @@ def test_timing_argument_errors():
 
 
 def test_implicit_scratch_sizes_and_validation():
-    # single-channel path: hidden features only (N x hidden rounded up to 4)
+    # hidden features (N x hidden rounded up to 16, float32) + the taps
+    # [order][d][N] in the io dtype, each region 256-byte aligned
     _, plan = hyena.hyena_plan_create(2, 2048, 6, 2, [2048])
     st, n = hyena.hyena_implicit_scratch_bytes(plan, 62)
-    assert st == hyena.HYENA_OK and n == 2048 * 64 * 4
+    assert st == hyena.HYENA_OK and n == 2048 * 64 * 4 + 2 * 6 * 2048 * 4
     assert hyena.hyena_implicit_scratch_bytes(plan, 0)[0] == hyena.HYENA_ERR_UNSUPPORTED
     assert hyena.hyena_implicit_scratch_bytes(plan, 257)[0] == hyena.HYENA_ERR_UNSUPPORTED
     f = hyena.ImplicitFilter(8, 64, 8.0, 16, 16, 16, 16, 16, 16, 16)
@@ -212,10 +213,13 @@ def test_implicit_scratch_sizes_and_validation():
     assert hyena.hyena_filter_spectrum_implicit(plan, nul, 16, 16, 16) == \
         hyena.HYENA_ERR_INVALID_ARGUMENT
     hyena.hyena_plan_destroy(plan)
-    # other paths also hold the taps: + order * d * N * 4 bytes
     _, plan = hyena.hyena_plan_create(1, 20000, 3, 2, [20000])
-    st, n = hyena.hyena_implicit_scratch_bytes(plan, 64)
+    st, n = hyena.hyena_implicit_scratch_bytes(plan, 50)
     assert n == 20000 * 64 * 4 + (2 * 3 * 20000 * 4 + 255) // 256 * 256
+    hyena.hyena_plan_destroy(plan)
+    _, plan = hyena.hyena_plan_create(1, 4096, 4, 2, [4096], hyena.HYENA_BF16, hyena.HYENA_BF16)
+    st, n = hyena.hyena_implicit_scratch_bytes(plan, 64)
+    assert n == 4096 * 64 * 4 + 2 * 4 * 4096 * 2
     hyena.hyena_plan_destroy(plan)
     # grids have no implicit filters here
     _, plan = hyena.hyena_plan_create(1, 64, 2, 1, [8, 8])

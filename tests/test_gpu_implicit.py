@@ -39,16 +39,23 @@ def _run(N, d, B, dtype, seed, K=8, H=64):
 
 @pytest.mark.parametrize("N,d,B", [(2048, 6, 2), (256, 3, 1), (8192, 2, 1)])
 def test_implicit_single_channel_path(N, d, B):
-    # taps evaluated inside the spectrum kernel
     y, ref, plan, _, _ = _run(N, d, B, synth.F32, seed=50)
     assert plan.path == 1
     assert rel_err(y, ref) < 1e-5
 
 
 @pytest.mark.parametrize("N,d,B", [(1000, 5, 2), (20000, 3, 1)])
-def test_implicit_materialised_taps(N, d, B):
-    # ragged N (channel-pair kernels) and the four-step path: taps in scratch
+def test_implicit_other_paths(N, d, B):
+    # ragged N (channel-pair kernels) and the four-step path
     y, ref, _, _, _ = _run(N, d, B, synth.F32, seed=51)
+    assert rel_err(y, ref) < 1e-5
+
+
+@pytest.mark.parametrize("N,d,H", [(1001, 37, 50), (4096, 40, 16), (2048, 3, 1)])
+def test_implicit_ragged_tiles(N, d, H):
+    # taps tiles of 64 rows x 64 positions: order d not a multiple of 64, N
+    # not a multiple of 4 (scalar stores), hidden widths off the 16-chunk
+    y, ref, _, _, _ = _run(N, d, 1, synth.F32, seed=54, K=5, H=H)
     assert rel_err(y, ref) < 1e-5
 
 
