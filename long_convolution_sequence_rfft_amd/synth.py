@@ -66,6 +66,7 @@ class Inputs:
 
     1D: u [B,N,d], gates [order,B,N,d], h [order,d,N]
     2D: u [B,X,Y,d], gates [order,B,X,Y,d], h [order,d,2X-1,2Y-1]
+    3D: u [B,X,Y,Z,d], gates [order,B,X,Y,Z,d], h [order,d,2X-1,2Y-1,2Z-1]
     D is always float32 [order,d].
     """
     u: np.ndarray
@@ -136,6 +137,34 @@ def make_2d(B: int, X: int, Y: int, d: int, order: int, sigma_range=(16.0, 128.0
     for n in range(order):
         gates[n] = _store(rng.standard_normal((B, X, Y, d)), dtype)
     return Inputs(u=u, gates=gates, h=K, D=D, dtype=dtype, dims=(X, Y), B=B, d=d, order=order,
+                  meta={"sigma_range": tuple(sigma_range), "seed": seed})
+
+
+def make_3d(B: int, X: int, Y: int, Z: int, d: int, order: int, sigma_range=(4.0, 32.0),
+            dtype: str = F32, seed: int = 0) -> Inputs:
+    """Inputs for the 3D non-causal chain: taps at every offset in
+    [-(X-1), X-1] x [-(Y-1), Y-1] x [-(Z-1), Z-1], the 2D law with a third axis:
+    sin(w . (i, j, l) + phi) exp(-(i^2 + j^2 + l^2) / (2 sigma^2))."""
+    rng = np.random.default_rng(seed)
+    i = np.arange(-(X - 1), X, dtype=np.float64)[:, None, None]
+    j = np.arange(-(Y - 1), Y, dtype=np.float64)[None, :, None]
+    l = np.arange(-(Z - 1), Z, dtype=np.float64)[None, None, :]
+    r2 = i ** 2 + j ** 2 + l ** 2
+    K = np.empty((order, d, 2 * X - 1, 2 * Y - 1, 2 * Z - 1), dtype=_np_storage(dtype))
+    for n in range(order):
+        w = rng.uniform(0.0, np.pi, size=(d, 3))
+        phi = rng.uniform(0.0, 2.0 * np.pi, size=d)
+        sigma = rng.uniform(sigma_range[0], sigma_range[1], size=d)
+        for c in range(d):
+            kc = np.sin(w[c, 0] * i + w[c, 1] * j + w[c, 2] * l + phi[c]) * \
+                np.exp(-r2 / (2.0 * sigma[c] ** 2))
+            K[n, c] = _store(kc, dtype)
+    D = np.stack([rng.standard_normal(d) for _ in range(order)]).astype(np.float32)
+    u = _store(rng.standard_normal((B, X, Y, Z, d)), dtype)
+    gates = np.empty((order, B, X, Y, Z, d), dtype=u.dtype)
+    for n in range(order):
+        gates[n] = _store(rng.standard_normal((B, X, Y, Z, d)), dtype)
+    return Inputs(u=u, gates=gates, h=K, D=D, dtype=dtype, dims=(X, Y, Z), B=B, d=d, order=order,
                   meta={"sigma_range": tuple(sigma_range), "seed": seed})
 
 

@@ -13,6 +13,7 @@ Functions follow the pages cited in ``oracle.c``:
     "The Toeplitz picture" (gate after each convolution)
   * ``conv2d`` / ``hyena2d`` -- [P3] "How HyenaND works", non-causal zero-padded
     2D convolution on the native grid
+  * ``conv3d`` / ``hyena3d`` -- the same on a 3D grid
   * ``fft`` -- [P2] "Counting the cost" radix-2 FFT
   * ``circular_conv`` -- [P2] "Linear vs circular" (the unpadded contrast)
   * ``circular_conv_direct`` / ``hyena1d_circular`` -- the chain with periodic
@@ -83,6 +84,12 @@ def _load():
             lib.oracle_conv2d_fft.restype = ctypes.c_int
             lib.oracle_hyena2d.argtypes = [i64, i64, i64, i64, i32, p, p, p, p, p, i32]
             lib.oracle_hyena2d.restype = ctypes.c_int
+            lib.oracle_conv3d_direct.argtypes = [i64, i64, i64, i64, i64, p, p, p, p]
+            lib.oracle_conv3d_direct.restype = None
+            lib.oracle_conv3d_fft.argtypes = [i64, i64, i64, i64, i64, p, p, p, p]
+            lib.oracle_conv3d_fft.restype = ctypes.c_int
+            lib.oracle_hyena3d.argtypes = [i64, i64, i64, i64, i64, i32, p, p, p, p, p, i32]
+            lib.oracle_hyena3d.restype = ctypes.c_int
             lib.oracle_circular_conv_direct.argtypes = [i64, i64, i64, p, p, p, p]
             lib.oracle_circular_conv_direct.restype = None
             lib.oracle_hyena1d_circular.argtypes = [i64, i64, i64, i32, p, p, p, p, p, i32]
@@ -248,6 +255,38 @@ def dwconv3x3(x, w, bias=None) -> np.ndarray:
     _load().oracle_dwconv3x3(B, X, Y, d, _ptr(x), _ptr(w), _ptr(b) if b is not None else None,
                              _ptr(o))
     return o
+
+
+def conv3d(z, K, D, method: int = DIRECT) -> np.ndarray:
+    """Non-causal 3D conv: z [B,X,Y,Z,d], K [d,2X-1,2Y-1,2Z-1] (offset (i,j,l) at
+    (i+X-1, j+Y-1, l+Z-1))."""
+    z, K, D = _f64(z), _f64(K), _f64(D)
+    B, X, Y, Z, d = z.shape
+    assert K.shape == (d, 2 * X - 1, 2 * Y - 1, 2 * Z - 1) and D.shape == (d,)
+    w = np.empty_like(z)
+    lib = _load()
+    if method == DIRECT:
+        lib.oracle_conv3d_direct(B, X, Y, Z, d, _ptr(z), _ptr(K), _ptr(D), _ptr(w))
+    else:
+        if lib.oracle_conv3d_fft(B, X, Y, Z, d, _ptr(z), _ptr(K), _ptr(D), _ptr(w)) != 0:
+            raise MemoryError("oracle_conv3d_fft failed")
+    return w
+
+
+def hyena3d(u, gates, K, D, method: int = DIRECT) -> np.ndarray:
+    """3D chain: u [B,X,Y,Z,d], gates [order,B,X,Y,Z,d], K [order,d,2X-1,2Y-1,2Z-1],
+    D [order,d]."""
+    u, gates, K, D = _f64(u), _f64(gates), _f64(K), _f64(D)
+    B, X, Y, Z, d = u.shape
+    order = gates.shape[0]
+    assert gates.shape == (order, B, X, Y, Z, d)
+    assert K.shape == (order, d, 2 * X - 1, 2 * Y - 1, 2 * Z - 1) and D.shape == (order, d)
+    y = np.empty_like(u)
+    rc = _load().oracle_hyena3d(B, X, Y, Z, d, order, _ptr(u), _ptr(gates), _ptr(K), _ptr(D),
+                                _ptr(y), method)
+    if rc != 0:
+        raise MemoryError("oracle_hyena3d failed")
+    return y
 
 
 def hyena2d_block(q, k, v, sw, sb, K, D, method: int = DIRECT) -> np.ndarray:

@@ -1,6 +1,6 @@
 /*
  * oracle.c -- plain float64 CPU reference for the Hyena operator's long
- * convolution chain (1D causal and 2D non-causal).
+ * convolution chain (1D causal, 2D and 3D non-causal).
  *
  * TEST INFRASTRUCTURE ONLY.  Nothing in the GPU library links, includes or
  * calls this file, and this file uses nothing from the GPU library.  Only the
@@ -28,6 +28,9 @@
  *   2D: z, u, gates[n], y : [B][X][Y][d];
  *       K : [order][d][2X-1][2Y-1], tap at signed offset (i, j) stored at
  *       index (i + X - 1, j + Y - 1);  D : [order][d]
+ *   3D: z, u, gates[n], y : [B][X][Y][Z][d];
+ *       K : [order][d][2X-1][2Y-1][2Z-1], offset (i, j, l) at
+ *       (i + X - 1, j + Y - 1, l + Z - 1)
  *
  * Parity pins (all in tests/): the printed worked example of [P2] "Linear vs
  * circular"; numpy.convolve / numpy.fft / the O(M^2) DFT definition; closed
@@ -363,6 +366,149 @@ int oracle_hyena2d(int64_t B, int64_t X, int64_t Y, int64_t d, int32_t order, co
             oracle_conv2d_direct(B, X, Y, d, z, Kn, Dn, w);
         else
             rc = oracle_conv2d_fft(B, X, Y, d, z, Kn, Dn, w);
+        const double* g = gates + (int64_t)n * E;
+        for (int64_t i = 0; i < E; ++i) z[i] = g[i] * w[i];
+    }
+    if (rc == 0) memcpy(y, z, sizeof(double) * E);
+    free(z); free(w);
+    return rc;
+}
+
+/* ------------------------------------------------------------------------ */
+/* 3D non-causal convolution with skip ([P3]: the same operator on a native  */
+/* 3D grid; the convolution theorem holds along each axis)                   */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * Direct sum over the whole X x Y x Z grid (zero outside it, "same" output
+ * positions):
+ *   w[b,p,q,r,c] = sum_{p',q',r'} K[c][p-p'][q-q'][r-r'] z[b,p',q',r',c] + D[c] z[b,p,q,r,c]
+ * K[c] holds the tap at signed offset (i, j, l) at index
+ * (i + X - 1, j + Y - 1, l + Z - 1) of a (2X-1) x (2Y-1) x (2Z-1) array.
+ */
+void oracle_conv3d_direct(int64_t B, int64_t X, int64_t Y, int64_t Z, int64_t d,
+                          const double* z, const double* K, const double* D, double* w)
+{
+    const int64_t KX = 2 * X - 1, KY = 2 * Y - 1, KZ = 2 * Z - 1;
+#pragma omp parallel for collapse(3) schedule(dynamic)
+    for (int64_t b = 0; b < B; ++b)
+        for (int64_t c = 0; c < d; ++c)
+            for (int64_t p = 0; p < X; ++p)
+                for (int64_t q = 0; q < Y; ++q)
+                    for (int64_t r = 0; r < Z; ++r) {
+                        double acc = 0.0;
+                        for (int64_t pp = 0; pp < X; ++pp)
+                            for (int64_t qq = 0; qq < Y; ++qq)
+                                for (int64_t rr = 0; rr < Z; ++rr)
+                                    acc += K[((c * KX + (p - pp + X - 1)) * KY + (q - qq + Y - 1)) * KZ +
+                                             (r - rr + Z - 1)] *
+                                           z[(((b * X + pp) * Y + qq) * Z + rr) * d + c];
+                        const int64_t o = (((b * X + p) * Y + q) * Z + r) * d + c;
+                        w[o] = acc + D[c] * z[o];
+                    }
+}
+
+/* 3D DFT of a P1 x P2 x P3 array (r fastest): 1D DFTs along r, then q, then p. */
+static void fft3d(int64_t P1, int64_t P2, int64_t P3, double* re, double* im, int sign,
+                  double* lr, double* li)
+{
+    for (int64_t row = 0; row < P1 * P2; ++row) oracle_fft(P3, re + row * P3, im + row * P3, sign);
+    for (int64_t p = 0; p < P1; ++p)
+        for (int64_t r = 0; r < P3; ++r) {
+            const int64_t base = p * P2 * P3 + r;
+            for (int64_t q = 0; q < P2; ++q) { lr[q] = re[base + q * P3]; li[q] = im[base + q * P3]; }
+            oracle_fft(P2, lr, li, sign);
+            for (int64_t q = 0; q < P2; ++q) { re[base + q * P3] = lr[q]; im[base + q * P3] = li[q]; }
+        }
+    for (int64_t qr = 0; qr < P2 * P3; ++qr) {
+        for (int64_t p = 0; p < P1; ++p) { lr[p] = re[p * P2 * P3 + qr]; li[p] = im[p * P2 * P3 + qr]; }
+        oracle_fft(P1, lr, li, sign);
+        for (int64_t p = 0; p < P1; ++p) { re[p * P2 * P3 + qr] = lr[p]; im[p * P2 * P3 + qr] = li[p]; }
+    }
+}
+
+/*
+ * The same through the 3D convolution theorem: grid and taps in a
+ * P1 x P2 x P3 periodic array (each a power of two >= twice the side), the
+ * tap at offset (i, j, l) at (i mod P1, j mod P2, l mod P3); bin-by-bin
+ * product; inverse with 1/(P1 P2 P3); keep the input grid; add D z.
+ */
+int oracle_conv3d_fft(int64_t B, int64_t X, int64_t Y, int64_t Z, int64_t d, const double* z,
+                      const double* K, const double* D, double* w)
+{
+    const int64_t P1 = next_pow2(2 * X), P2 = next_pow2(2 * Y), P3 = next_pow2(2 * Z);
+    const int64_t KX = 2 * X - 1, KY = 2 * Y - 1, KZ = 2 * Z - 1;
+    const int64_t S = P1 * P2 * P3;
+    const int64_t Lmax = P1 > P2 ? (P1 > P3 ? P1 : P3) : (P2 > P3 ? P2 : P3);
+    int fail = 0;
+#pragma omp parallel
+    {
+        double* xr = (double*)malloc(sizeof(double) * S);
+        double* xi = (double*)malloc(sizeof(double) * S);
+        double* kr = (double*)malloc(sizeof(double) * S);
+        double* ki = (double*)malloc(sizeof(double) * S);
+        double* lr = (double*)malloc(sizeof(double) * Lmax);
+        double* li = (double*)malloc(sizeof(double) * Lmax);
+        if (!xr || !xi || !kr || !ki || !lr || !li) {
+#pragma omp atomic write
+            fail = 1;
+        } else {
+#pragma omp for collapse(2) schedule(dynamic)
+            for (int64_t b = 0; b < B; ++b)
+                for (int64_t c = 0; c < d; ++c) {
+                    memset(xr, 0, sizeof(double) * S); memset(xi, 0, sizeof(double) * S);
+                    memset(kr, 0, sizeof(double) * S); memset(ki, 0, sizeof(double) * S);
+                    for (int64_t p = 0; p < X; ++p)
+                        for (int64_t q = 0; q < Y; ++q)
+                            for (int64_t r = 0; r < Z; ++r)
+                                xr[(p * P2 + q) * P3 + r] = z[(((b * X + p) * Y + q) * Z + r) * d + c];
+                    for (int64_t i = -(X - 1); i <= X - 1; ++i)
+                        for (int64_t j = -(Y - 1); j <= Y - 1; ++j)
+                            for (int64_t l = -(Z - 1); l <= Z - 1; ++l) {
+                                const int64_t ri = (i + P1) % P1, rj = (j + P2) % P2, rl = (l + P3) % P3;
+                                kr[(ri * P2 + rj) * P3 + rl] =
+                                    K[((c * KX + (i + X - 1)) * KY + (j + Y - 1)) * KZ + (l + Z - 1)];
+                            }
+                    fft3d(P1, P2, P3, xr, xi, -1, lr, li);
+                    fft3d(P1, P2, P3, kr, ki, -1, lr, li);
+                    for (int64_t k = 0; k < S; ++k) {
+                        const double pr = xr[k] * kr[k] - xi[k] * ki[k];
+                        const double pi = xr[k] * ki[k] + xi[k] * kr[k];
+                        xr[k] = pr; xi[k] = pi;
+                    }
+                    fft3d(P1, P2, P3, xr, xi, +1, lr, li);
+                    for (int64_t p = 0; p < X; ++p)
+                        for (int64_t q = 0; q < Y; ++q)
+                            for (int64_t r = 0; r < Z; ++r) {
+                                const int64_t o = (((b * X + p) * Y + q) * Z + r) * d + c;
+                                w[o] = xr[(p * P2 + q) * P3 + r] / (double)S + D[c] * z[o];
+                            }
+                }
+        }
+        free(xr); free(xi); free(kr); free(ki); free(lr); free(li);
+    }
+    return fail ? -1 : 0;
+}
+
+/* Order-N chain on a 3D grid, gated as in 1D and 2D. */
+int oracle_hyena3d(int64_t B, int64_t X, int64_t Y, int64_t Z, int64_t d, int32_t order,
+                   const double* u, const double* gates, const double* K, const double* D,
+                   double* y, int32_t method)
+{
+    const int64_t E = B * X * Y * Z * d;
+    const int64_t KS = (2 * X - 1) * (2 * Y - 1) * (2 * Z - 1);
+    double* z = (double*)malloc(sizeof(double) * E);
+    double* w = (double*)malloc(sizeof(double) * E);
+    if (!z || !w) { free(z); free(w); return -1; }
+    memcpy(z, u, sizeof(double) * E);
+    int rc = 0;
+    for (int32_t n = 0; n < order && rc == 0; ++n) {
+        const double* Kn = K + (int64_t)n * d * KS;
+        const double* Dn = D + (int64_t)n * d;
+        if (method == 0)
+            oracle_conv3d_direct(B, X, Y, Z, d, z, Kn, Dn, w);
+        else
+            rc = oracle_conv3d_fft(B, X, Y, Z, d, z, Kn, Dn, w);
         const double* g = gates + (int64_t)n * E;
         for (int64_t i = 0; i < E; ++i) z[i] = g[i] * w[i];
     }

@@ -618,3 +618,93 @@ def test_hyena2d_block_silu_and_biases():
     s = lambda x: x / (1.0 + np.exp(-x))
     expect = s(sb[2]) * sb[0] * s(sb[1])
     assert np.max(np.abs(y - expect)) < 1e-15
+
+
+# ---------------------------------------------------------------------------
+# 3D grids ("How HyenaND works": the same operator on a native 3D grid)
+# ---------------------------------------------------------------------------
+
+def _scipy_same3(z, Kc):
+    X, Y, Z = z.shape
+    full = scipy.signal.convolve(z, Kc, mode="full", method="direct")
+    return full[X - 1:2 * X - 1, Y - 1:2 * Y - 1, Z - 1:2 * Z - 1]
+
+
+@pytest.mark.parametrize("method", [oracle.DIRECT, oracle.FFT])
+@pytest.mark.parametrize("X,Y,Z", [(1, 1, 1), (2, 3, 4), (4, 4, 4), (3, 5, 2), (8, 4, 6)])
+def test_conv3d_matches_scipy(method, X, Y, Z):
+    rng = np.random.default_rng(X * 97 + Y * 13 + Z)
+    B, d = 2, 2
+    z = rng.standard_normal((B, X, Y, Z, d))
+    K = rng.standard_normal((d, 2 * X - 1, 2 * Y - 1, 2 * Z - 1))
+    D = rng.standard_normal(d)
+    w = oracle.conv3d(z, K, D, method)
+    for b in range(B):
+        for c in range(d):
+            ref = _scipy_same3(z[b, ..., c], K[c]) + D[c] * z[b, ..., c]
+            assert _rel(w[b, ..., c], ref) < 1e-12
+
+
+@pytest.mark.parametrize("X,off", [(8, (7, -7, 0)), (8, (-7, 3, 7)), (6, (0, 0, -5)),
+                                   (32, (31, -31, 31)), (32, (-31, 5, -2))])
+def test_conv3d_delta_kernel_shifts_without_wrap(X, off):
+    # a single tap at offset (i0, j0, l0): the grid shifted by it, zero fill,
+    # nothing wraps around the periodic transform grid
+    i0, j0, l0 = off
+    Y = Z = X
+    rng = np.random.default_rng(abs(X + 7 * i0 + 3 * j0 + l0) + 100)
+    z = rng.standard_normal((1, X, Y, Z, 1))
+    K = np.zeros((1, 2 * X - 1, 2 * Y - 1, 2 * Z - 1))
+    K[0, i0 + X - 1, j0 + Y - 1, l0 + Z - 1] = 1.0
+    ps, qs, rs = np.meshgrid(np.arange(X), np.arange(Y), np.arange(Z), indexing="ij")
+    sp, sq, sr = ps - i0, qs - j0, rs - l0
+    ok = (sp >= 0) & (sp < X) & (sq >= 0) & (sq < Y) & (sr >= 0) & (sr < Z)
+    ref = np.zeros((X, Y, Z))
+    ref[ok] = z[0, sp[ok], sq[ok], sr[ok], 0]
+    methods = [oracle.FFT] if X > 8 else [oracle.DIRECT, oracle.FFT]
+    for m in methods:
+        w = oracle.conv3d(z, K, np.zeros(1), m)
+        assert np.max(np.abs(w[0, ..., 0] - ref)) < 1e-12
+
+
+def test_conv3d_separable_kernel_reduces_to_1d():
+    rng = np.random.default_rng(78)
+    X, Y, Z = 8, 6, 10
+    a, bv, cv = (rng.standard_normal(2 * n - 1) for n in (X, Y, Z))
+    K = np.einsum("i,j,l->ijl", a, bv, cv)[None]
+    z = rng.standard_normal((1, X, Y, Z, 1))
+    w = oracle.conv3d(z, K, np.zeros(1), oracle.FFT)[0, ..., 0]
+    # non-causal 1D convs along each axis in turn ("same" window)
+    t = z[0, ..., 0]
+    t = np.apply_along_axis(lambda v: np.convolve(cv, v)[Z - 1:2 * Z - 1], 2, t)
+    t = np.apply_along_axis(lambda v: np.convolve(bv, v)[Y - 1:2 * Y - 1], 1, t)
+    t = np.apply_along_axis(lambda v: np.convolve(a, v)[X - 1:2 * X - 1], 0, t)
+    assert _rel(w, t) < 1e-12
+
+
+def test_conv3d_flat_grid_is_the_2d_convolution():
+    # Z = 1: the only tap offset along z is 0, so the 3D operator is the 2D one
+    rng = np.random.default_rng(79)
+    X, Y, d = 6, 5, 3
+    z = rng.standard_normal((2, X, Y, d))
+    K = rng.standard_normal((d, 2 * X - 1, 2 * Y - 1))
+    D = rng.standard_normal(d)
+    ref = oracle.conv2d(z, K, D, oracle.DIRECT)
+    for m in (oracle.DIRECT, oracle.FFT):
+        w = oracle.conv3d(z[:, :, :, None, :], K[..., None], D, m)[:, :, :, 0, :]
+        assert _rel(w, ref) < 1e-12
+
+
+@pytest.mark.parametrize("method", [oracle.DIRECT, oracle.FFT])
+def test_hyena3d_chain_by_hand(method):
+    inp = synth.make_3d(B=2, X=4, Y=6, Z=5, d=3, order=2, sigma_range=(1.0, 4.0), seed=5)
+    u, g, K, D = inp.f64()
+    y = oracle.hyena3d(u, g, K, D, method)
+    z = u
+    for n in range(2):
+        w = np.empty_like(z)
+        for b in range(2):
+            for c in range(3):
+                w[b, ..., c] = _scipy_same3(z[b, ..., c], K[n, c]) + D[n, c] * z[b, ..., c]
+        z = g[n] * w
+    assert _rel(y, z) < 1e-12
