@@ -19,13 +19,17 @@
  * non-causal linear 2D convolution of "How HyenaND works" (section "The
  * convolution theorem (FFT)"; worked trace with zero padding and
  * is_causal=False): taps at every signed offset (i, j), |i| <= X-1,
- * |j| <= Y-1, output kept on the input grid.
+ * |j| <= Y-1, output kept on the input grid.  ndims = 3 is the same on an
+ * X x Y x Z grid (the page's native ND transform, here on 3D grids).
  *
  * Layouts (row-major, channels last; d is the fastest axis):
- *   u, gates[n], y : [B][N][d] (ndims = 1) or [B][X][Y][d] (ndims = 2)
+ *   u, gates[n], y : [B][N][d] (ndims = 1), [B][X][Y][d] (ndims = 2) or
+ *                    [B][X][Y][Z][d] (ndims = 3)
  *   h              : [order][d][N] (ndims = 1);
  *                    [order][d][2X-1][2Y-1] (ndims = 2), the tap at offset
- *                    (i, j) stored at index (i + X - 1, j + Y - 1)
+ *                    (i, j) stored at index (i + X - 1, j + Y - 1);
+ *                    [order][d][2X-1][2Y-1][2Z-1] (ndims = 3), offset
+ *                    (i, j, l) at (i + X - 1, j + Y - 1, l + Z - 1)
  *   D              : float32 [order][d]
  *   H (spectrum)   : opaque, spectrum_bytes long, laid out in the order the
  *                    forward kernels consume it (see hyena_spectrum_export)
@@ -83,13 +87,15 @@ typedef enum hyena_dtype {
 
 /* Which kernel family runs the transform.  AUTO picks: LDS1D when ndims = 1
  * and M <= 16384, FOURSTEP1D when ndims = 1 and M > 16384, ROWCOL2D when
- * ndims = 2.  FOURSTEP1D may be forced for any M >= 1024 (tests use this to
- * check it against the single-pass kernels at small N). */
+ * ndims = 2, ROWCOL3D when ndims = 3.  FOURSTEP1D may be forced for any
+ * M >= 1024 (tests use this to check it against the single-pass kernels at
+ * small N). */
 typedef enum hyena_path {
     HYENA_PATH_AUTO = 0,
     HYENA_PATH_LDS1D = 1,
     HYENA_PATH_FOURSTEP1D = 2,
-    HYENA_PATH_ROWCOL2D = 3
+    HYENA_PATH_ROWCOL2D = 3,
+    HYENA_PATH_ROWCOL3D = 4
 } hyena_path;
 
 /*
@@ -99,6 +105,8 @@ typedef enum hyena_path {
  *            per channel (pair); longer transforms take the four-step path.
  * ndims = 2: dims = {X, Y}, X and Y powers of two in [4, 512]; N must equal
  *            X * Y.
+ * ndims = 3: dims = {X, Y, Z}, powers of two in [4, 256], X * Y * Z <= 2^20;
+ *            N must equal X * Y * Z.
  * io_dtype, spectrum_dtype: hyena_dtype values.  path: hyena_path value.
  * On success *plan receives a new plan (release with hyena_plan_destroy).
  * This call touches no GPU state.
@@ -231,6 +239,7 @@ hyena_status hyena_filter_spectrum_implicit(hyena_plan_t plan, const hyena_impli
  * complex64 (re, im) pairs, unscaled (the plain DFT of the zero-padded
  * filter).  ndims = 1: [order][d][M/2 + 1] bins k = 0..M/2.
  * ndims = 2: [order][d][P1][P2/2 + 1] with P1 = 2X, P2 = 2Y.
+ * ndims = 3: [order][d][P1][P2][P3/2 + 1] with P3 = 2Z.
  */
 hyena_status hyena_spectrum_export(hyena_plan_t plan, const void* H, void* natural,
                                    void* stream);

@@ -19,7 +19,7 @@ SOURCES = ["api.hip", "lds1d.hip", "lds1d_f32.hip", "lds1d_bf16.hip", "lds1d_f16
            "lds1d_real_f32.hip", "lds1d_real_bf16.hip", "lds1d_real_f16.hip",
            "lds1d_circ_f32.hip", "lds1d_circ_bf16.hip", "lds1d_circ_f16.hip", "multipass.hip",
            "multipass_outer_f32.hip", "multipass_outer_bf16.hip", "multipass_outer_f16.hip",
-           "multipass_inner.hip",
+           "multipass_inner.hip", "multipass_mid.hip",
            "implicit.hip", "timing.hip", "plan.cpp"]
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -28,7 +28,9 @@ size_t io_bytes(const hy::Plan& p)
 
 size_t filter_bytes(const hy::Plan& p)
 {
-    const size_t taps = p.ndims == 1 ? (size_t)p.N : (size_t)(2 * p.X - 1) * (size_t)(2 * p.Y - 1);
+    size_t taps = (size_t)p.N;
+    if (p.ndims == 2) taps = (size_t)(2 * p.X - 1) * (size_t)(2 * p.Y - 1);
+    if (p.ndims == 3) taps = (size_t)(2 * p.X - 1) * (size_t)(2 * p.Y - 1) * (size_t)(2 * p.Z - 1);
     return (size_t)p.order * (size_t)p.d * taps * (p.io_dtype == HYENA_F32 ? 4u : 2u);
 }
 
@@ -119,6 +121,7 @@ hyena_status hyena_filter_spectrum(hyena_plan_t plan, const void* h, void* H, vo
         case HYENA_PATH_LDS1D: return hy::launch_lds1d_spectrum(p, h, H, workspace, stream);
         case HYENA_PATH_FOURSTEP1D: return hy::launch_fourstep_spectrum(p, h, H, workspace, stream);
         case HYENA_PATH_ROWCOL2D: return hy::launch_rowcol2d_spectrum(p, h, H, workspace, stream);
+        case HYENA_PATH_ROWCOL3D: return hy::launch_rowcol3d_spectrum(p, h, H, workspace, stream);
         default: return fail(HYENA_ERR_UNSUPPORTED, "unknown path");
     }
 }
@@ -155,6 +158,8 @@ hyena_status hyena_forward(hyena_plan_t plan, const void* u, const void* const* 
             return hy::launch_fourstep_forward(p, u, gates, H, D, y, workspace, stream);
         case HYENA_PATH_ROWCOL2D:
             return hy::launch_rowcol2d_forward(p, u, gates, H, D, y, workspace, stream);
+        case HYENA_PATH_ROWCOL3D:
+            return hy::launch_rowcol3d_forward(p, u, gates, H, D, y, workspace, stream);
         default: return fail(HYENA_ERR_UNSUPPORTED, "unknown path");
     }
 }
@@ -236,6 +241,7 @@ hyena_status hyena_spectrum_export(hyena_plan_t plan, const void* H, void* natur
         case HYENA_PATH_LDS1D: return hy::launch_lds1d_export(p, H, natural, stream);
         case HYENA_PATH_FOURSTEP1D: return hy::launch_fourstep_export(p, H, natural, stream);
         case HYENA_PATH_ROWCOL2D: return hy::launch_rowcol2d_export(p, H, natural, stream);
+        case HYENA_PATH_ROWCOL3D: return hy::launch_rowcol3d_export(p, H, natural, stream);
         default: return fail(HYENA_ERR_UNSUPPORTED, "unknown path");
     }
 }

@@ -6,6 +6,10 @@
 //     W_M^{n2 k1}, length-M2 row DFTs over n2.
 //   2D (row-column): a P1 x P2 (= 2X x 2Y) periodic grid; length-P2 DFTs
 //     along q for every grid row p, then length-P1 DFTs along p.
+//   3D: a P1 x P2 x P3 (= 2X x 2Y x 2Z) grid; length-P3 DFTs along z (the
+//     outer pass, rows (x, y)), length-P2 DFTs along y (a middle pass between
+//     two intermediates), then length-P1 DFTs along x (the inner pass, whose
+//     outer index is the composite bin (ky, kz)).
 // ("Hyena -- Long Convolutions Math", section "The convolution theorem";
 // "How HyenaND works", section "The convolution theorem (FFT)": the ND
 // transform on the native grid, here as 1D transforms along each axis.)
@@ -187,6 +191,12 @@ struct MpGeom {
     int32_t order_n;       // filter index for INNER and the gate index for OUTER_MID/OUT
     TwOffsets tw_a, tw_b;  // twiddle tables of the outer / inner lengths
     int64_t tw_step;       // float2 offset of the W_M^{n2 k1} table (four-step)
+    // 3D: grid sides (outer pass: filter tap placement and rows (x, y)) and,
+    // for the inner pass, the length P3 of the composite outer index
+    // a = ky P3 + kz
+    int32_t three_d;
+    int32_t gx, gy, gz;
+    int32_t Lc;
 };
 
 __device__ __forceinline__ void pair_of_slot(const MpGeom& g, int64_t group, int kp, int64_t& b,

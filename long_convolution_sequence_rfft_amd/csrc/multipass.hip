@@ -10,6 +10,7 @@ HY_MP_LENGTHS(HY_MP_OUTER_INST, uint16_t, extern)
 HY_MP_LENGTHS(HY_MP_OUTER_INST, _Float16, extern)
 HY_MP_LENGTHS(HY_MP_INNER_INST, float, extern)
 HY_MP_LENGTHS(HY_MP_INNER_INST, uint16_t, extern)
+HY_MP_LENGTHS(HY_MP_MID_INST, 0, extern)
 
 namespace {
 
@@ -23,6 +24,19 @@ TwOffsets offsets_at(const Plan& p, int first)
     o.i1 = (int32_t)p.seg[first + 2].off;
     o.i0 = (int32_t)p.seg[first + 3].off;
     return o;
+}
+
+// Pairs per outer workgroup: up to 16 (a 128-byte row of float32 pairs), and
+// no more than the workgroup's transforms of the outer length g.La.
+void set_pair_groups(const Plan& p, MpGeom& g)
+{
+    const int nf = kMpThreads / threads_per_transform(g.La);
+    const int kp_max = nf < 16 ? nf : 16;
+    int kp = 1;
+    while (kp < kp_max && kp < p.npairs) kp <<= 1;
+    g.kp_log2 = 0;
+    while ((1 << g.kp_log2) < kp) ++g.kp_log2;
+    g.groups_per_b = (int32_t)((p.npairs + kp - 1) / kp);
 }
 
 // Geometry common to all passes of a plan (chunk fields filled per launch).
@@ -49,15 +63,7 @@ MpGeom base_geom(const Plan& p)
         g.so = p.Y;
         g.tw_step = 0;
     }
-    // pairs per outer workgroup: up to 16 (a 128-byte row of float32 pairs),
-    // and no more than the workgroup's transforms of the outer length
-    const int nf = kMpThreads / threads_per_transform(g.La);
-    const int kp_max = nf < 16 ? nf : 16;
-    int kp = 1;
-    while (kp < kp_max && kp < p.npairs) kp <<= 1;
-    g.kp_log2 = 0;
-    while ((1 << g.kp_log2) < kp) ++g.kp_log2;
-    g.groups_per_b = (int32_t)((p.npairs + kp - 1) / kp);
+    set_pair_groups(p, g);
     g.tw_a = offsets_at(p, 0);
     g.tw_b = offsets_at(p, 4);
     return g;
@@ -294,6 +300,253 @@ hyena_status mp_export(const Plan& p, const void* H, void* out, void* stream)
     return e == hipSuccess ? HYENA_OK : fail(HYENA_ERR_DEVICE, hipGetErrorString(e));
 }
 
+// ---------------------------------------------------------------------------
+// 3D grids: outer pass along z (rows (x, y), intermediate F1), middle pass
+// along y (F1 <-> F2), inner pass along x on F2 with the composite outer
+// index (ky, kz).
+// ---------------------------------------------------------------------------
+MpGeom base_geom3(const Plan& p)
+{
+    MpGeom g{};
+    g.N = p.N;
+    g.d = p.d;
+    g.npairs = p.npairs;
+    g.B = p.B;
+    g.four_step = 0;
+    g.three_d = 1;
+    g.La = (int32_t)p.P3;
+    g.Lb = (int32_t)(p.P1 * p.P2);  // rows (x, y) of the filter spectrum
+    g.Lb_live = (int32_t)(p.X * p.Y);  // rows (x, y) of the chain
+    g.sa = 1;  // t = Z (x Y + y) + z
+    g.so = p.Z;
+    g.tw_step = 0;
+    g.gx = (int32_t)p.X;
+    g.gy = (int32_t)p.Y;
+    g.gz = (int32_t)p.Z;
+    set_pair_groups(p, g);
+    g.tw_a = offsets_at(p, 0);
+    g.tw_b = offsets_at(p, 4);
+    return g;
+}
+
+MpGeom geom3_inner(const Plan& p, const MpGeom& go)
+{
+    MpGeom g = go;
+    g.La = (int32_t)(p.P2 * p.P3);
+    g.Lb = (int32_t)p.P1;
+    g.Lb_live = (int32_t)p.X;
+    g.Lc = (int32_t)p.P3;
+    return g;
+}
+
+hyena_status mid(int LY, int mode, bool half, const MidArgs& a, int64_t nb, hipStream_t s)
+{
+    switch (LY) {
+#define HY_CASE(LL, A_, B_)                                                          \
+    case LL:                                                                         \
+        if (mode == MID_INV) return mp_mid_launch<LL, MID_INV, true>(a, nb, s);      \
+        if (half) return mp_mid_launch<LL, MID_FWD, true>(a, nb, s);                 \
+        return mp_mid_launch<LL, MID_FWD, false>(a, nb, s);
+        HY_MP_LENGTHS(HY_CASE, 0, 0)
+#undef HY_CASE
+        default: return fail(HYENA_ERR_UNSUPPORTED, "multi-pass: unsupported middle length");
+    }
+}
+
+MidArgs mid_args(const Plan& p, const MpGeom& g, float2* F1, float2* F2, bool spec, int mode,
+                 const float2* tw)
+{
+    MidArgs m{};
+    m.src = mode == MID_FWD ? F1 : F2;
+    m.dst = mode == MID_FWD ? F2 : F1;
+    m.tw = tw;
+    m.tw_y = offsets_at(p, 8);
+    m.f1_pair = (spec ? p.spec_pair_bytes : p.fwd_pair_bytes) / 8;
+    m.f2_pair = (spec ? p.spec_pair_bytes2 : p.fwd_pair_bytes2) / 8;
+    m.ncols = (spec ? p.P1 : p.X) * p.P3;
+    m.nslots = g.ngroups * ((int64_t)1 << g.kp_log2);
+    m.P3 = (int32_t)p.P3;
+    m.ylen1 = (int32_t)(spec ? p.P2 : p.Y);
+    return m;
+}
+
+int64_t mid_blocks(const Plan& p, const MidArgs& m)
+{
+    const int64_t nf = kMpThreads / threads_per_transform((int)p.P2);
+    return (m.ncols + nf - 1) / nf * m.nslots;
+}
+
+hyena_status mp3_forward(const Plan& p, const void* u, const void* const* gates, const void* H,
+                         const float* D, void* y, void* ws, void* stream)
+{
+    const hipStream_t s = (hipStream_t)stream;
+    MpGeom go = base_geom3(p);
+    const int KP = 1 << go.kp_log2;
+    const int C = (kMpThreads / threads_per_transform(go.La)) / KP;
+    const int64_t col_blocks = (go.Lb_live + C - 1) / C;
+    MpGeom gi = geom3_inner(p, go);
+    const int U = (kMpThreads / threads_per_transform(gi.Lb)) / 2;
+    const int64_t unit_blocks = (gi.La / 2 + U - 1) / U;
+    const int64_t total_groups = (int64_t)p.B * go.groups_per_b;
+    int64_t chunk_groups = p.chunk_pairs / KP;
+    if (chunk_groups < 1) chunk_groups = 1;
+    float2* F1 = reinterpret_cast<float2*>(static_cast<char*>(ws) + p.inter_offset);
+    float2* F2 = reinterpret_cast<float2*>(static_cast<char*>(ws) + p.inter2_offset);
+    const float2* tw = static_cast<const float2*>(ws);
+    const size_t esz = p.spec_dtype == HYENA_F32 ? 4 : 2;
+    go.pair_bytes = p.fwd_pair_bytes;
+    gi.pair_bytes = p.fwd_pair_bytes2;
+    for (int64_t g0 = 0; g0 < total_groups; g0 += chunk_groups) {
+        go.group0 = gi.group0 = g0;
+        go.ngroups = gi.ngroups = total_groups - g0 < chunk_groups ? total_groups - g0 : chunk_groups;
+        OuterArgs oa{};
+        oa.g = go;
+        oa.act = u;
+        oa.F = F1;
+        oa.tw = tw;
+        hyena_status st = outer(p, OUTER_IN, true, oa, col_blocks * go.ngroups, s);
+        if (st != HYENA_OK) return st;
+        const MidArgs mf = mid_args(p, go, F1, F2, false, MID_FWD, tw);
+        const MidArgs mi = mid_args(p, go, F1, F2, false, MID_INV, tw);
+        for (int n = 0; n < p.order; ++n) {
+            st = mid((int)p.P2, MID_FWD, true, mf, mid_blocks(p, mf), s);
+            if (st != HYENA_OK) return st;
+            InnerArgs ia{};
+            ia.g = gi;
+            ia.F = F2;
+            ia.spec = static_cast<const char*>(H) + (size_t)n * spec_elems_per_filter(p) * esz;
+            ia.D = D + (int64_t)n * p.d;
+            ia.tw = tw;
+            st = inner(p, INNER_CHAIN, ia, unit_blocks * gi.ngroups * KP, s);
+            if (st != HYENA_OK) return st;
+            st = mid((int)p.P2, MID_INV, true, mi, mid_blocks(p, mi), s);
+            if (st != HYENA_OK) return st;
+            oa.act = gates[n];
+            oa.out = y;
+            st = outer(p, n + 1 < p.order ? OUTER_MID : OUTER_OUT, true, oa, col_blocks * go.ngroups, s);
+            if (st != HYENA_OK) return st;
+        }
+    }
+    return HYENA_OK;
+}
+
+hyena_status mp3_spectrum(const Plan& p, const void* h, void* H, void* ws, void* stream)
+{
+    const hipStream_t s = (hipStream_t)stream;
+    MpGeom go = base_geom3(p);
+    go.B = 1;  // filters have no batch axis
+    const int KP = 1 << go.kp_log2;
+    const int C = (kMpThreads / threads_per_transform(go.La)) / KP;
+    const int64_t col_blocks = (go.Lb + C - 1) / C;
+    MpGeom gi = geom3_inner(p, go);
+    const int U = (kMpThreads / threads_per_transform(gi.Lb)) / 2;
+    const int64_t unit_blocks = (gi.La / 2 + U - 1) / U;
+    const int64_t total_groups = go.groups_per_b;
+    int64_t chunk_groups = p.chunk_pairs / KP;
+    if (chunk_groups < 1) chunk_groups = 1;
+    float2* F1 = reinterpret_cast<float2*>(static_cast<char*>(ws) + p.inter_offset);
+    float2* F2 = reinterpret_cast<float2*>(static_cast<char*>(ws) + p.inter2_offset);
+    const float2* tw = static_cast<const float2*>(ws);
+    const size_t esz = p.spec_dtype == HYENA_F32 ? 4 : 2;
+    const int64_t taps = (2 * p.X - 1) * (2 * p.Y - 1) * (2 * p.Z - 1);
+    go.pair_bytes = p.spec_pair_bytes;
+    gi.pair_bytes = p.spec_pair_bytes2;
+    for (int n = 0; n < p.order; ++n) {
+        for (int64_t g0 = 0; g0 < total_groups; g0 += chunk_groups) {
+            go.group0 = gi.group0 = g0;
+            go.ngroups = gi.ngroups =
+                total_groups - g0 < chunk_groups ? total_groups - g0 : chunk_groups;
+            OuterArgs oa{};
+            oa.g = go;
+            oa.filt = static_cast<const char*>(h) + (size_t)n * p.d * taps * io_size(p);
+            oa.F = F1;
+            oa.tw = tw;
+            hyena_status st = outer(p, OUTER_SPEC, false, oa, col_blocks * go.ngroups, s);
+            if (st != HYENA_OK) return st;
+            const MidArgs mf = mid_args(p, go, F1, F2, true, MID_FWD, tw);
+            st = mid((int)p.P2, MID_FWD, false, mf, mid_blocks(p, mf), s);
+            if (st != HYENA_OK) return st;
+            InnerArgs ia{};
+            ia.g = gi;
+            ia.F = F2;
+            ia.spec_out = static_cast<char*>(H) + (size_t)n * spec_elems_per_filter(p) * esz;
+            ia.tw = tw;
+            st = inner(p, INNER_SPEC, ia, unit_blocks * gi.ngroups * KP, s);
+            if (st != HYENA_OK) return st;
+        }
+    }
+    return HYENA_OK;
+}
+
+// One thread per entry (n, pair, unit, e) of a 3D spectrum; writes natural-
+// order unscaled transfer functions [order][d][P1][P2][P3/2 + 1].  A bin and
+// its mirror (-k) carry conjugate values; each is written where it falls in
+// the stored half (kz <= P3/2).
+template <typename SP>
+__global__ void hyena_mp3_export(const SP* spec, float2* out, int64_t npairs, int64_t d, MpGeom g,
+                                 int64_t total)
+{
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= total) return;
+    const int La = g.La, Lb = g.Lb, P3 = g.Lc, P2 = La / P3, W = P3 / 2 + 1;
+    const int64_t per_pair = (int64_t)(La / 2) * Lb;
+    const int64_t np = i / per_pair;
+    const int64_t rem = i - np * per_pair;
+    const int kk = (int)(rem / Lb), e = (int)(rem % Lb);
+    const int64_t n = np / npairs, p = np - n * npairs;
+    const int64_t c0 = 2 * p;
+    const bool has_b = c0 + 1 < d;
+    float2 P, Q;
+    load_entry(spec, i, P, Q);
+    const float M = (float)La * (float)Lb;
+    const float2 ha = make_float2((P.x + Q.x) * M, (P.y + Q.y) * M);
+    const float2 hb = make_float2((P.x - Q.x) * M, (P.y - Q.y) * M);
+    float2* oa = out + (n * d + c0) * (int64_t)Lb * P2 * W;
+    float2* ob = oa + (int64_t)Lb * P2 * W;
+    auto put = [&](int kx, int col, float2 va, float2 vb) {
+        const int ky = col / P3, kz = col - ky * P3;
+        if (kz > P3 / 2) return;
+        const int64_t at = ((int64_t)kx * P2 + ky) * W + kz;
+        oa[at] = va;
+        if (has_b) ob[at] = vb;
+    };
+    auto conj2 = [](float2 v) { return make_float2(v.x, -v.y); };
+    int col0, col1;
+    bool self;
+    unit_columns(g, kk, col0, col1, self);
+    if (!self) {
+        put(e, col0, ha, hb);
+        put((Lb - e) & (Lb - 1), col1, conj2(ha), conj2(hb));
+    } else if (e == 0 || e == Lb / 2) {
+        const int col = e == 0 ? col0 : col1;
+        put(0, col, make_float2(ha.x, 0.0f), make_float2(hb.x, 0.0f));
+        put(Lb / 2, col, make_float2(ha.y, 0.0f), make_float2(hb.y, 0.0f));
+    } else {
+        const int col = e < Lb / 2 ? col0 : col1;
+        const int kx = e < Lb / 2 ? e : e - Lb / 2;
+        put(kx, col, ha, hb);
+        put(Lb - kx, col, conj2(ha), conj2(hb));
+    }
+}
+
+hyena_status mp3_export(const Plan& p, const void* H, void* out, void* stream)
+{
+    const MpGeom g = geom3_inner(p, base_geom3(p));
+    const int64_t total = (int64_t)p.order * p.npairs * p.spec_entries_per_pair;
+    const int bs = 256;
+    const int64_t nb = (total + bs - 1) / bs;
+    if (p.spec_dtype == HYENA_F32)
+        HY_LAUNCH(kernel_label("hyena_mp3_export", "float"), hyena_mp3_export<float>,
+                  dim3((unsigned)nb), dim3(bs), 0, (hipStream_t)stream, (const float*)H,
+                  (float2*)out, p.npairs, p.d, g, total);
+    else
+        HY_LAUNCH(kernel_label("hyena_mp3_export", "unsigned short"), hyena_mp3_export<uint16_t>,
+                  dim3((unsigned)nb), dim3(bs), 0, (hipStream_t)stream, (const uint16_t*)H,
+                  (float2*)out, p.npairs, p.d, g, total);
+    const hipError_t e = hipGetLastError();
+    return e == hipSuccess ? HYENA_OK : fail(HYENA_ERR_DEVICE, hipGetErrorString(e));
+}
+
 }  // namespace
 
 hyena_status launch_fourstep_forward(const Plan& p, const void* u, const void* const* gates,
@@ -335,6 +588,25 @@ hyena_status launch_rowcol2d_spectrum(const Plan& p, const void* h, void* H, voi
 hyena_status launch_rowcol2d_export(const Plan& p, const void* H, void* out, void* stream)
 {
     return mp_export(p, H, out, stream);
+}
+
+}  // namespace hy
+
+namespace hy {
+
+hyena_status launch_rowcol3d_forward(const Plan& p, const void* u, const void* const* gates,
+                                     const void* H, const float* D, void* y, void* ws,
+                                     void* stream)
+{
+    return mp3_forward(p, u, gates, H, D, y, ws, stream);
+}
+hyena_status launch_rowcol3d_spectrum(const Plan& p, const void* h, void* H, void* ws, void* stream)
+{
+    return mp3_spectrum(p, h, H, ws, stream);
+}
+hyena_status launch_rowcol3d_export(const Plan& p, const void* H, void* out, void* stream)
+{
+    return mp3_export(p, H, out, stream);
 }
 
 }  // namespace hy

@@ -294,6 +294,18 @@ __global__ void __launch_bounds__(kMpThreads, 2) hyena_mp_outer(OuterArgs a)
                         const int64_t t = g.sa * s + g.so * o;
                         if (t < g.N) idx = t;
                         stride = g.N;
+                    } else if (g.three_d) {
+                        // row o = (x, y) of the P1 x P2 periodic grid, column s = z;
+                        // offset (i, j, l) sits at (i mod P1, j mod P2, l mod P3)
+                        const int64_t X2 = g.gx, Y2 = g.gy, Z2 = g.gz;
+                        const int64_t xr = o / (2 * Y2), yr = o - xr * (2 * Y2);
+                        const int64_t i = xr < X2 ? xr : xr - 2 * X2;
+                        const int64_t j = yr < Y2 ? yr : yr - 2 * Y2;
+                        const int64_t l = s < Z2 ? s : s - 2 * Z2;
+                        if (xr != X2 && yr != Y2 && s != Z2)
+                            idx = ((i + X2 - 1) * (2 * Y2 - 1) + (j + Y2 - 1)) * (2 * Z2 - 1) +
+                                  (l + Z2 - 1);
+                        stride = (2 * X2 - 1) * (2 * Y2 - 1) * (2 * Z2 - 1);
                     } else {
                         // periodic placement: tap offset (i, j) sits at (i mod P1, j mod P2);
                         // row o = i mod P1, column s = j mod P2
@@ -397,12 +409,50 @@ __global__ void __launch_bounds__(kMpThreads, 2) hyena_mp_outer(OuterArgs a)
 //     primary (0, e); e = LB/2 packs (La/2: 0, LB/2); e > LB/2: primary
 //     (La/2, e - LB/2).
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ void unit_pairing(bool four_step, int kk, int e, int LB, int& fa, int& ka,
-                                             int& fb, int& kb, int& self)
+// Outer columns (side 0, side 1) of unit kk; `self` when both are mirrored
+// onto themselves (2D: unit 0 = columns 0 and La/2).  3D (composite outer
+// index a = ky P3 + kz, mirror ((-ky) mod P2, (-kz) mod P3)):
+//   units 0, 1:           the self-mirrored columns (ky, 0) and (ky, P3/2) of
+//                         ky = 0 and ky = P2/2;
+//   next 2 (P3/2 - 1):    (ky, kz) <-> (ky, P3 - kz), 0 < kz < P3/2, for
+//                         ky = 0 and ky = P2/2;
+//   the rest:             (ky, kz) <-> (P2 - ky, (-kz) mod P3), 0 < ky < P2/2.
+__device__ __forceinline__ void unit_columns(const MpGeom& g, int kk, int& c0, int& c1, bool& self)
+{
+    if (!g.three_d) {
+        self = kk == 0;
+        c0 = kk;
+        c1 = kk == 0 ? g.La / 2 : g.La - kk;
+        return;
+    }
+    const int P3 = g.Lc, H3 = P3 / 2, P2 = g.La / P3, H2 = P2 / 2;
+    if (kk < 2) {
+        self = true;
+        c0 = kk * H2 * P3;
+        c1 = c0 + H3;
+        return;
+    }
+    self = false;
+    int u = kk - 2;
+    if (u < 2 * (H3 - 1)) {
+        const int row = u / (H3 - 1), kz = 1 + u % (H3 - 1);
+        const int base = row * H2 * P3;
+        c0 = base + kz;
+        c1 = base + P3 - kz;
+        return;
+    }
+    u -= 2 * (H3 - 1);
+    const int ky = 1 + u / P3, kz = u % P3;
+    c0 = ky * P3 + kz;
+    c1 = (P2 - ky) * P3 + ((P3 - kz) & (P3 - 1));
+}
+
+__device__ __forceinline__ void unit_pairing(bool four_step, bool self_unit, int e, int LB, int& fa,
+                                             int& ka, int& fb, int& kb, int& self)
 {
     // fa/fb: side (0 or 1), ka/kb: bin index; self: 0 = pair, 1 = packed self bins (ka, kb in side fa)
     self = 0;
-    if (kk > 0) {
+    if (!self_unit) {
         fa = 0;
         ka = e;
         fb = 1;
@@ -472,8 +522,10 @@ __global__ void __launch_bounds__(kMpThreads, 2) hyena_mp_inner(InnerArgs a)
     // units of this workgroup: kk0 .. kk0 + nu - 1 (nu <= U)
     const int nu = min(U, La / 2 - kk0);
     auto col_of = [&](int u, int side) {
-        const int kk = kk0 + u;
-        return side == 0 ? kk : (kk == 0 ? La / 2 : La - kk);
+        int c0, c1;
+        bool sf;
+        unit_columns(g, kk0 + u, c0, c1, sf);
+        return side == 0 ? c0 : c1;
     };
 
     // this thread's share of the mirror-paired product: unit u, entries
@@ -483,6 +535,11 @@ __global__ void __launch_bounds__(kMpThreads, 2) hyena_mp_inner(InnerArgs a)
     const int tu = (f & 1) * TB + tau;  // 0 .. 2 TB - 1
     const int kk_me = kk0 + u_me;
     const bool unit_ok = u_me < nu && live;
+    bool self_me;
+    {
+        int c0, c1;
+        unit_columns(g, kk_me, c0, c1, self_me);
+    }
     const int64_t ebase = p * (int64_t)(La / 2) * LB + (int64_t)kk_me * LB;
     typename EntryRaw<SP>::type ent[EPT];
     if constexpr (MODE == INNER_CHAIN) {
@@ -559,7 +616,7 @@ __global__ void __launch_bounds__(kMpThreads, 2) hyena_mp_inner(InnerArgs a)
         for (int i = 0; i < EPT; ++i) {
             const int e = tu + i * 2 * TB;
             int fa, ka, fb, kb, self;
-            unit_pairing(g.four_step != 0, kk_me, e, LB, fa, ka, fb, kb, self);
+            unit_pairing(g.four_step != 0, self_me, e, LB, fa, ka, fb, kb, self);
             const int ia = fa * LW + lpad(ka), ib = fb * LW + lpad(kb);
             float2 za = make_float2(ure[ia], uim[ia]);
             float2 zb = make_float2(ure[ib], uim[ib]);
@@ -630,6 +687,91 @@ __global__ void __launch_bounds__(kMpThreads, 2) hyena_mp_inner(InnerArgs a)
     }
 }
 
+// ---------------------------------------------------------------------------
+// Middle pass (3D): length-LY transforms along y between the two
+// intermediates of a pair slot, F1 [x][y][kz] (y < ylen1) and F2
+// [x][ky][kz].  Transform j = x P3 + kz of the slot; a workgroup takes NF
+// consecutive j, with transform f = threadIdx % NF and lane tau = threadIdx /
+// NF, so the lanes of one register slot touch consecutive kz.
+//   MID_FWD: F1 -> F2; HALF: only y < LY/2 hold data (the zero padding).
+//   MID_INV: F2 -> F1 (unscaled inverse), keeping y < LY/2.
+// ---------------------------------------------------------------------------
+enum MidMode { MID_FWD = 0, MID_INV = 1 };
+
+struct MidArgs {
+    const float2* src;
+    float2* dst;
+    const float2* tw;
+    TwOffsets tw_y;
+    int64_t f1_pair, f2_pair;  // float2 elements per pair slot of F1 / F2
+    int64_t ncols;             // transforms per slot: x rows times P3
+    int64_t nslots;            // pair slots in this chunk
+    int32_t P3;
+    int32_t ylen1;             // y extent of F1 (Y in the chain, P2 for spectra)
+};
+
+template <int LY, int MODE, bool HALF>
+__global__ void __launch_bounds__(kMpThreads, 2) hyena_mp_mid(MidArgs a)
+{
+    using S = FftShape<LY>;
+    using X = MpShape<LY>;
+    constexpr int T = X::T, NF = X::NF, LW = X::LW, R0 = S::R0, RL = S::RL, QL = S::PTS / RL;
+    constexpr int RIN = HALF ? R0 / 2 : R0;
+    __shared__ float sre[NF * LW];
+    __shared__ float sim[NF * LW];
+    const int f = (int)threadIdx.x % NF;
+    const int tau = (int)threadIdx.x / NF;
+    const int64_t slot = blockIdx.x % a.nslots;
+    const int64_t j = (int64_t)(blockIdx.x / a.nslots) * NF + f;
+    const bool live = j < a.ncols;
+    const int64_t x = live ? j / a.P3 : 0;
+    const int64_t kz = live ? j - x * a.P3 : 0;
+    float* re = sre + f * LW;
+    float* im = sim + f * LW;
+    const int64_t e1 = slot * a.f1_pair + x * a.ylen1 * a.P3 + kz;  // F1 (x, 0, kz)
+    const int64_t e2 = slot * a.f2_pair + x * (int64_t)LY * a.P3 + kz;  // F2 (x, 0, kz)
+    float2 v[S::PTS];
+    if constexpr (MODE == MID_FWD) {
+        // R0-pass layout: v[q R0 + r] = sample y = tau + q T + r LY/R0
+#pragma unroll
+        for (int q = 0; q < S::Q0; ++q)
+#pragma unroll
+            for (int r = 0; r < RIN; ++r) {
+                const int y = tau + q * T + r * (LY / R0);
+                v[q * R0 + r] = live ? a.src[e1 + (int64_t)y * a.P3] : make_float2(0.0f, 0.0f);
+            }
+        fwd_regs_to_lds<LY, HALF, true>(v, re, im, a.tw, a.tw_y, tau);
+        if (live) {
+#pragma unroll
+            for (int q = 0; q < QL; ++q)
+#pragma unroll
+                for (int r = 0; r < RL; ++r) {
+                    const int ky = tau + q * T + r * (LY / RL);
+                    a.dst[e2 + (int64_t)ky * a.P3] = v[q * RL + r];
+                }
+        }
+    } else {
+        // the inverse's first pass reads bins ky = tau + q T + r LY/RL
+#pragma unroll
+        for (int q = 0; q < QL; ++q)
+#pragma unroll
+            for (int r = 0; r < RL; ++r) {
+                const int ky = tau + q * T + r * (LY / RL);
+                v[q * RL + r] = live ? a.src[e2 + (int64_t)ky * a.P3] : make_float2(0.0f, 0.0f);
+            }
+        inv_lds_to_regs<LY, true, true>(v, re, im, a.tw, a.tw_y, tau);
+        if (live) {
+#pragma unroll
+            for (int q = 0; q < S::Q0; ++q)
+#pragma unroll
+                for (int r = 0; r < R0 / 2; ++r) {
+                    const int y = tau + q * T + r * (LY / R0);
+                    a.dst[e1 + (int64_t)y * a.P3] = v[q * R0 + r];
+                }
+        }
+    }
+}
+
 }  // namespace hy
 
 namespace hy {
@@ -654,6 +796,15 @@ hyena_status mp_inner_launch(const InnerArgs& a, int64_t nblocks, hipStream_t s)
     return e == hipSuccess ? HYENA_OK : fail(HYENA_ERR_DEVICE, hipGetErrorString(e));
 }
 
+template <int LY, int MODE, bool HALF>
+hyena_status mp_mid_launch(const MidArgs& a, int64_t nblocks, hipStream_t s)
+{
+    HY_LAUNCH(kernel_label("hyena_mp_mid", LY, MODE, HALF), (hyena_mp_mid<LY, MODE, HALF>),
+              dim3((unsigned)nblocks), dim3(kMpThreads), 0, s, a);
+    const hipError_t e = hipGetLastError();
+    return e == hipSuccess ? HYENA_OK : fail(HYENA_ERR_DEVICE, hipGetErrorString(e));
+}
+
 #define HY_MP_LENGTHS(X, A, B) X(8, A, B) X(16, A, B) X(32, A, B) X(64, A, B) X(128, A, B) \
     X(256, A, B) X(512, A, B) X(1024, A, B)
 
@@ -668,6 +819,14 @@ hyena_status mp_inner_launch(const InnerArgs& a, int64_t nblocks, hipStream_t s)
                                                                        int64_t, hipStream_t); \
     EXT template hyena_status mp_outer_launch<L, IO, OUTER_SPEC, false>(const OuterArgs&,     \
                                                                         int64_t, hipStream_t);
+
+#define HY_MP_MID_INST(L, A_, EXT)                                                            \
+    EXT template hyena_status mp_mid_launch<L, MID_FWD, true>(const MidArgs&, int64_t,        \
+                                                              hipStream_t);                   \
+    EXT template hyena_status mp_mid_launch<L, MID_FWD, false>(const MidArgs&, int64_t,       \
+                                                               hipStream_t);                  \
+    EXT template hyena_status mp_mid_launch<L, MID_INV, true>(const MidArgs&, int64_t,        \
+                                                              hipStream_t);
 
 #define HY_MP_INNER_INST(L, SP, EXT)                                                          \
     EXT template hyena_status mp_inner_launch<L, SP, INNER_CHAIN, true>(const InnerArgs&,     \

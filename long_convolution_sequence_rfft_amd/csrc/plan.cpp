@@ -77,9 +77,9 @@ hyena_status plan_build(Plan& p, int64_t B, int64_t N, int64_t d, int32_t order,
         return fail(HYENA_ERR_UNSUPPORTED, "unknown spectrum_dtype");
     if (io_dtype != HYENA_BF16 && spec_dtype == HYENA_BF16)
         return fail(HYENA_ERR_UNSUPPORTED, "a bfloat16 spectrum needs bfloat16 io");
-    if (path < HYENA_PATH_AUTO || path > HYENA_PATH_ROWCOL2D)
+    if (path < HYENA_PATH_AUTO || path > HYENA_PATH_ROWCOL3D)
         return fail(HYENA_ERR_UNSUPPORTED, "unknown path");
-    if (ndims != 1 && ndims != 2) return fail(HYENA_ERR_UNSUPPORTED, "ndims must be 1 or 2");
+    if (ndims < 1 || ndims > 3) return fail(HYENA_ERR_UNSUPPORTED, "ndims must be 1, 2 or 3");
     // per-row element offsets are 32-bit inside the kernels
     if ((double)N * (double)d * 4.0 >= 2147483648.0)
         return fail(HYENA_ERR_UNSUPPORTED, "N * d * 4 must stay below 2^31 bytes");
@@ -113,8 +113,8 @@ hyena_status plan_build(Plan& p, int64_t B, int64_t N, int64_t d, int32_t order,
             path = HYENA_PATH_LDS1D;
         }
         if (path == HYENA_PATH_AUTO) path = p.M <= kLdsMaxM ? HYENA_PATH_LDS1D : HYENA_PATH_FOURSTEP1D;
-        if (path == HYENA_PATH_ROWCOL2D)
-            return fail(HYENA_ERR_UNSUPPORTED, "ROWCOL2D needs ndims = 2");
+        if (path == HYENA_PATH_ROWCOL2D || path == HYENA_PATH_ROWCOL3D)
+            return fail(HYENA_ERR_UNSUPPORTED, "the row-column paths need ndims = 2 or 3");
         if (path == HYENA_PATH_LDS1D && p.M > kLdsMaxM)
             return fail(HYENA_ERR_UNSUPPORTED, "LDS1D path holds transforms up to 16384 points");
         if (path == HYENA_PATH_FOURSTEP1D && p.M < 1024)
@@ -146,7 +146,7 @@ hyena_status plan_build(Plan& p, int64_t B, int64_t N, int64_t d, int32_t order,
             add_transform_segments(p, off, p.M2);
             add_segment(p, off, p.M1, p.M2);
         }
-    } else {
+    } else if (ndims == 2) {
         if (p.circular) return fail(HYENA_ERR_UNSUPPORTED, "periodic boundary: ndims = 1 only");
         const int64_t X = dims[0], Y = dims[1];
         if (!is_pow2(X) || !is_pow2(Y) || X < 4 || Y < 4 || X > 512 || Y > 512)
@@ -164,6 +164,31 @@ hyena_status plan_build(Plan& p, int64_t B, int64_t N, int64_t d, int32_t order,
         // outer transforms run along q (length P2), inner along p (length P1)
         add_transform_segments(p, off, p.P2);
         add_transform_segments(p, off, p.P1);
+    } else {
+        if (p.circular) return fail(HYENA_ERR_UNSUPPORTED, "periodic boundary: ndims = 1 only");
+        const int64_t X = dims[0], Y = dims[1], Z = dims[2];
+        if (!is_pow2(X) || !is_pow2(Y) || !is_pow2(Z) || X < 4 || Y < 4 || Z < 4 || X > 256 ||
+            Y > 256 || Z > 256)
+            return fail(HYENA_ERR_UNSUPPORTED, "3D grid sides must be powers of two in 4..256");
+        if (X * Y * Z > (1 << 20))
+            return fail(HYENA_ERR_UNSUPPORTED, "3D grids hold at most 2^20 points");
+        if (X * Y * Z != N) return fail(HYENA_ERR_INVALID_ARGUMENT, "N must equal X * Y * Z");
+        if (path == HYENA_PATH_AUTO) path = HYENA_PATH_ROWCOL3D;
+        if (path != HYENA_PATH_ROWCOL3D)
+            return fail(HYENA_ERR_UNSUPPORTED, "3D grids use the ROWCOL3D path");
+        p.path = path;
+        p.X = X;
+        p.Y = Y;
+        p.Z = Z;
+        p.P1 = 2 * X;
+        p.P2 = 2 * Y;
+        p.P3 = 2 * Z;
+        p.spec_entries_per_pair = p.P1 * p.P2 * p.P3 / 2;
+        // outer transforms along z (length P3, on the activations), inner
+        // along x (length P1, with the product), and the middle pass along y
+        add_transform_segments(p, off, p.P3);
+        add_transform_segments(p, off, p.P1);
+        add_transform_segments(p, off, p.P2);
     }
 
     p.tw_elems = off;
@@ -196,6 +221,27 @@ hyena_status plan_build(Plan& p, int64_t B, int64_t N, int64_t d, int32_t order,
         p.spec_pair_bytes = spec_pair;
         const int64_t need = chunk * (fwd_pair > spec_pair ? fwd_pair : spec_pair);
         p.inter_bytes = align_up((size_t)need, 256);
+    }
+    if (p.path == HYENA_PATH_ROWCOL3D) {
+        // per channel pair: F1 after the z transforms ([x][y][kz]; the chain
+        // keeps x < X, y < Y, the spectrum every x, y) and F2 after the y
+        // transforms ([x][ky][kz])
+        const int64_t fwd1 = p.X * p.Y * p.P3 * 8, fwd2 = p.X * p.P2 * p.P3 * 8;
+        const int64_t spec1 = p.P1 * p.P2 * p.P3 * 8, spec2 = spec1;
+        int64_t chunk = (int64_t)(96ll << 20) / (fwd1 + fwd2);
+        chunk = chunk / 16 * 16;
+        if (chunk < 16) chunk = 16;
+        const int64_t total_slots = p.B * ((p.npairs + 15) / 16) * 16;
+        if (chunk > total_slots) chunk = total_slots;
+        p.chunk_pairs = chunk;
+        p.fwd_pair_bytes = fwd1;
+        p.fwd_pair_bytes2 = fwd2;
+        p.spec_pair_bytes = spec1;
+        p.spec_pair_bytes2 = spec2;
+        const size_t r1 = align_up((size_t)(chunk * (fwd1 > spec1 ? fwd1 : spec1)), 256);
+        const size_t r2 = align_up((size_t)(chunk * (fwd2 > spec2 ? fwd2 : spec2)), 256);
+        p.inter2_offset = p.inter_offset + r1;
+        p.inter_bytes = r1 + r2;
     }
     if (p.path == HYENA_PATH_LDS1D && p.lds_io == 3) {
         // u, every gate and y, staged channel-major

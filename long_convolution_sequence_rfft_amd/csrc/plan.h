@@ -50,7 +50,7 @@ struct Plan {
     int64_t B = 0, N = 0, d = 0;
     int32_t order = 0;
     int32_t ndims = 1;
-    int64_t X = 0, Y = 0;  // 2D grid
+    int64_t X = 0, Y = 0, Z = 0;  // 2D / 3D grid sides
     int32_t io_dtype = HYENA_F32, spec_dtype = HYENA_F32;
     int32_t path = HYENA_PATH_AUTO;
     int32_t circular = 0;  // periodic boundary: transform length N, no padding
@@ -69,11 +69,16 @@ struct Plan {
 
     // FOURSTEP1D: M = M1 * M2; columns of length M1 (time index t = M2 n1 + n2),
     // rows of length M2.  ROWCOL2D: P1 = 2X (columns), P2 = 2Y (rows).
+    // ROWCOL3D: P1 = 2X, P2 = 2Y, P3 = 2Z.
     int64_t M1 = 0, M2 = 0;
-    int64_t P1 = 0, P2 = 0;
+    int64_t P1 = 0, P2 = 0, P3 = 0;
     int64_t chunk_pairs = 0;      // channel-pair slots per pass over the intermediate buffer
     int64_t fwd_pair_bytes = 0;   // intermediate bytes per pair slot, forward chain
     int64_t spec_pair_bytes = 0;  // intermediate bytes per pair slot, filter spectrum
+    // ROWCOL3D: a second intermediate (after the transform along y) per pair
+    // slot, placed after the first one's chunk in the workspace
+    int64_t fwd_pair_bytes2 = 0, spec_pair_bytes2 = 0;
+    size_t inter2_offset = 0;
 
     // twiddle tables
     TwSegment seg[kMaxTwSegments];
@@ -122,6 +127,12 @@ hyena_status launch_rowcol2d_forward(const Plan& p, const void* u, const void* c
 hyena_status launch_rowcol2d_export(const Plan& p, const void* H, void* out, void* stream);
 hyena_status launch_rowcol2d_block(const Plan& p, const hyena_nd_mixer& m, const void* H,
                                    const float* D, void* y, void* ws, void* stream);
+
+hyena_status launch_rowcol3d_spectrum(const Plan& p, const void* h, void* H, void* ws, void* stream);
+hyena_status launch_rowcol3d_forward(const Plan& p, const void* u, const void* const* gates,
+                                     const void* H, const float* D, void* y, void* ws,
+                                     void* stream);
+hyena_status launch_rowcol3d_export(const Plan& p, const void* H, void* out, void* stream);
 
 // implicit.hip
 size_t implicit_scratch_bytes(const Plan& p, int32_t hidden);

@@ -30,6 +30,7 @@ HYENA_PATH_AUTO = 0
 HYENA_PATH_LDS1D = 1
 HYENA_PATH_FOURSTEP1D = 2
 HYENA_PATH_ROWCOL2D = 3
+HYENA_PATH_ROWCOL3D = 4
 
 EXPORTED_SYMBOLS = (
     "hyena_plan_create", "hyena_plan_query", "hyena_workspace_init", "hyena_filter_spectrum",
@@ -236,7 +237,7 @@ def hyena_timing_release():
 class Plan:
     """One plan plus its workspace on a torch device.
 
-    ``dims`` is ``(N,)`` for sequences or ``(X, Y)`` for grids.  Tensors are
+    ``dims`` is ``(N,)`` for sequences, ``(X, Y)`` or ``(X, Y, Z)`` for grids.  Tensors are
     float32 or bfloat16 (io), channels last; see include/hyena.h for layouts.
     """
 
@@ -352,9 +353,12 @@ class Plan:
             while M < (self.N if self.circular else 2 * self.N):
                 M *= 2
             shape = (self.order, self.d, M // 2 + 1, 2)
-        else:
+        elif len(self.dims) == 2:
             X, Y = self.dims
             shape = (self.order, self.d, 2 * X, Y + 1, 2)
+        else:
+            X, Y, Z = self.dims
+            shape = (self.order, self.d, 2 * X, 2 * Y, Z + 1, 2)
         out = self.torch.zeros(shape, dtype=self.torch.float32, device=self.device)
         _check(hyena_spectrum_export(self.handle, H.data_ptr(), out.data_ptr(), self.stream()),
                "hyena_spectrum_export")

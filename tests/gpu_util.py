@@ -64,7 +64,9 @@ def oracle_ref(inp: synth.Inputs, channels=None, method=oracle.FFT) -> np.ndarra
         h = h[:, ch]
     if len(inp.dims) == 1:
         return oracle.hyena1d(u, g, h, D, method)
-    return oracle.hyena2d(u, g, h, D, method)
+    if len(inp.dims) == 2:
+        return oracle.hyena2d(u, g, h, D, method)
+    return oracle.hyena3d(u, g, h, D, method)
 
 
 def rel_err(y, ref) -> float:

@@ -55,6 +55,19 @@ def test_status_strings():
     (dict(B=1, N=64, d=2, order=1, dims=[64], io_dtype=hyena.HYENA_F16,
           spectrum_dtype=hyena.HYENA_F16), hyena.HYENA_ERR_UNSUPPORTED),
     (dict(B=1, N=64, d=2, order=1, dims=[64], path=9), hyena.HYENA_ERR_UNSUPPORTED),
+    # 3D grids: power-of-two sides in 4..256, at most 2^20 points, N = X Y Z
+    (dict(B=1, N=6 * 8 * 8, d=2, order=1, dims=[6, 8, 8]), hyena.HYENA_ERR_UNSUPPORTED),
+    (dict(B=1, N=2 * 8 * 8, d=2, order=1, dims=[2, 8, 8]), hyena.HYENA_ERR_UNSUPPORTED),
+    (dict(B=1, N=512 * 8 * 8, d=2, order=1, dims=[512, 8, 8]), hyena.HYENA_ERR_UNSUPPORTED),
+    (dict(B=1, N=256 * 256 * 32, d=2, order=1, dims=[256, 256, 32]), hyena.HYENA_ERR_UNSUPPORTED),
+    (dict(B=1, N=512, d=2, order=1, dims=[8, 8, 4]), hyena.HYENA_ERR_INVALID_ARGUMENT),
+    (dict(B=1, N=512, d=2, order=1, dims=[8, 8, 8], path=hyena.HYENA_PATH_ROWCOL2D),
+     hyena.HYENA_ERR_UNSUPPORTED),
+    (dict(B=1, N=512, d=2, order=1, dims=[8, 8, 8], flags=hyena.HYENA_FLAG_CIRCULAR),
+     hyena.HYENA_ERR_UNSUPPORTED),
+    (dict(B=1, N=64, d=2, order=1, dims=[64], path=hyena.HYENA_PATH_ROWCOL3D),
+     hyena.HYENA_ERR_UNSUPPORTED),
+    (dict(B=1, N=64, d=2, order=1, dims=[4, 4, 2, 2]), hyena.HYENA_ERR_UNSUPPORTED),
 ])
 def test_plan_create_rejects(args, code):
     st, plan = hyena.hyena_plan_create(check=False, **args)
@@ -88,6 +101,23 @@ def test_2d_plan_sizes():
     spec, ws, p = hyena.hyena_plan_query(plan)
     assert p == hyena.HYENA_PATH_ROWCOL2D
     assert spec == 2 * 128 * (512 * 512 // 2) * 16
+    hyena.hyena_plan_destroy(plan)
+
+
+@pytest.mark.parametrize("X,Y,Z,d", [(64, 64, 64, 32), (4, 8, 16, 3), (256, 64, 64, 1)])
+def test_3d_plan_sizes(X, Y, Z, d):
+    _, plan = hyena.hyena_plan_create(2, X * Y * Z, d, 2, [X, Y, Z])
+    spec, ws, p = hyena.hyena_plan_query(plan)
+    assert p == hyena.HYENA_PATH_ROWCOL3D
+    # the Hermitian half of a 2X x 2Y x 2Z grid: 8XYZ reals per channel and filter
+    assert spec == 2 * ((d + 1) // 2) * (8 * X * Y * Z // 2) * 16
+    # two intermediates per pair slot (after z: X Y 2Z, after y: X 2Y 2Z
+    # complex64 in the chain; 8 X Y Z each for spectra), at least one slot
+    assert ws >= 2 * 8 * X * Y * Z * 8
+    hyena.hyena_plan_destroy(plan)
+    # the mixer and implicit filters are not defined for 3D plans
+    _, plan = hyena.hyena_plan_create(1, X * Y * Z, d, 1, [X, Y, Z])
+    assert hyena.hyena_implicit_scratch_bytes(plan, 64)[0] == hyena.HYENA_ERR_UNSUPPORTED
     hyena.hyena_plan_destroy(plan)
 
 
@@ -255,6 +285,9 @@ def test_nd_mixer_validation():
     _, p2 = hyena.hyena_plan_create(1, 64, 4, 2, [8, 8])
     assert hyena.hyena_nd_mixer_forward(p2, m, 16, 16, 16, 16) == hyena.HYENA_ERR_UNSUPPORTED
     hyena.hyena_plan_destroy(p2)
+    _, p4 = hyena.hyena_plan_create(1, 512, 4, 1, [8, 8, 8])
+    assert hyena.hyena_nd_mixer_forward(p4, m, 16, 16, 16, 16) == hyena.HYENA_ERR_UNSUPPORTED
+    hyena.hyena_plan_destroy(p4)
     _, p3 = hyena.hyena_plan_create(1, 64, 4, 1, [8, 8])
     assert hyena.hyena_nd_mixer_forward(p3, None, 16, 16, 16, 16) == \
         hyena.HYENA_ERR_INVALID_ARGUMENT

@@ -204,3 +204,86 @@ def test_hyenand_mixer(X, Y, d, dtype, bias):
     e = rel_err(from_torch(y, dtype), ref)
     say(f"[gpu] mixer rel err {e:.3e}")
     assert e < (TOL_F32 if dtype == synth.F32 else TOL_BF16)
+
+
+# ---------------------------------------------------------------------------
+# 3D grids: transforms along z (outer), y (middle) and x (inner, with the
+# product), "How HyenaND works" on a native 3D grid
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("X,Y,Z,d,order", [(4, 4, 4, 3, 1), (8, 4, 16, 5, 2), (16, 8, 4, 2, 3),
+                                           (4, 16, 8, 1, 2), (32, 32, 32, 4, 2)])
+def test_rowcol3d_small(X, Y, Z, d, order):
+    inp = synth.make_3d(B=2, X=X, Y=Y, Z=Z, d=d, order=order, sigma_range=(1.0, 8.0),
+                        seed=X + 3 * Y + 7 * Z + d)
+    y, plan, _ = run_gpu(inp)
+    assert plan.path == hyena.HYENA_PATH_ROWCOL3D
+    ref = oracle_ref(inp, method=oracle.DIRECT if X * Y * Z <= 128 else oracle.FFT)
+    e = rel_err(y, ref)
+    say(f"3D {X}x{Y}x{Z} d={d} order={order} rel_err={e:.3e}")
+    assert e < TOL_F32
+
+
+@pytest.mark.parametrize("off", [(15, -15, 15), (-15, 7, -15), (0, 0, 0), (3, -15, 1)])
+def test_rowcol3d_delta_kernel_is_exact_shift(off):
+    X = Y = Z = 16
+    i0, j0, l0 = off
+    inp = synth.make_3d(B=1, X=X, Y=Y, Z=Z, d=3, order=1, seed=sum(abs(v) for v in off))
+    inp.h[:] = 0.0
+    inp.h[0, :, i0 + X - 1, j0 + Y - 1, l0 + Z - 1] = 1.0
+    inp.gates[:] = 1.0
+    inp.D[:] = 0.0
+    y, _, _ = run_gpu(inp)
+    u = inp.u.astype(np.float64)
+    ref = np.zeros_like(u)
+    ps, qs, rs = np.meshgrid(np.arange(X), np.arange(Y), np.arange(Z), indexing="ij")
+    sp, sq, sr = ps - i0, qs - j0, rs - l0
+    ok = (sp >= 0) & (sp < X) & (sq >= 0) & (sq < Y) & (sr >= 0) & (sr < Z)
+    ref[0][ok] = u[0][sp[ok], sq[ok], sr[ok]]
+    assert np.max(np.abs(y - ref)) < 1e-5 * np.max(np.abs(u))
+
+
+def test_rowcol3d_spectrum_export():
+    X, Y, Z = 8, 4, 16
+    inp = synth.make_3d(B=1, X=X, Y=Y, Z=Z, d=3, order=1, sigma_range=(1.0, 8.0), seed=12)
+    _, plan, H = run_gpu(inp)
+    nat = plan.export_spectrum(H).cpu().numpy().astype(np.float64)
+    nat = nat[..., 0] + 1j * nat[..., 1]
+    K = inp.f64()[2][0]
+    for c in range(3):
+        per = np.zeros((2 * X, 2 * Y, 2 * Z))
+        for i in range(-(X - 1), X):
+            for j in range(-(Y - 1), Y):
+                for l in range(-(Z - 1), Z):
+                    per[i % (2 * X), j % (2 * Y), l % (2 * Z)] = K[c, i + X - 1, j + Y - 1, l + Z - 1]
+        ref = np.fft.fftn(per)[:, :, :Z + 1]
+        assert rel_err(nat[0, c], ref) < 2e-6
+
+
+def test_rowcol3d_storage_types():
+    for dtype, tol in ((synth.BF16, 1e-2), (synth.F16, 5e-3)):
+        inp = synth.make_3d(B=1, X=8, Y=16, Z=8, d=3, order=2, sigma_range=(1.0, 8.0),
+                            dtype=dtype, seed=13)
+        y, _, _ = run_gpu(inp)
+        e = rel_err(y, oracle_ref(inp, method=oracle.FFT))
+        say(f"[gpu] 3D {dtype} rel err {e:.3e}")
+        assert e < tol
+
+
+def test_rowcol3d_deterministic_bitwise():
+    inp = synth.make_3d(B=1, X=16, Y=16, Z=16, d=6, order=2, seed=14)
+    y1, plan, _ = run_gpu(inp)
+    y2, _, _ = run_gpu(inp, plan=plan)
+    assert np.array_equal(y1, y2)
+
+
+def test_full_size_3d_sampled():
+    # 64^3 grid, width 32, order 2: sampled channels against the oracle
+    inp = synth.make_3d(B=1, X=64, Y=64, Z=64, d=32, order=2, sigma_range=(4.0, 32.0), seed=15)
+    y, plan, _ = run_gpu(inp)
+    rng = np.random.default_rng(15)
+    ch = np.unique(np.concatenate([[0, 1, inp.d - 1], rng.choice(inp.d, 3, replace=False)]))
+    ref = oracle_ref(inp, channels=ch, method=oracle.FFT)
+    e = rel_err(y[..., ch], ref)
+    say(f"3D 64^3 d=32 sampled rel_err={e:.3e}")
+    assert e < TOL_F32
