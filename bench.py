@@ -37,7 +37,7 @@ HBM_PEAK_GBPS = 8000.0
 # 256 CUs x 4 SIMDs x 16 lanes x 2 flop (FMA) x 2.4 GHz
 ALU_PEAK_TFLOPS = 256 * 4 * 16 * 2 * 2.4e9 / 1e12
 HEADLINE = 2
-ORDER_OF_RUN = [2, 1, 3, 4]
+ORDER_OF_RUN = [2, 1, 3, 4, 5]
 
 
 def log(msg):
@@ -52,19 +52,28 @@ def io_bytes(dtype):
     return 2 if dtype == "bf16" else 4
 
 
+def grid_points(cfg):
+    """Tokens per batch row: N (1D), X Y (2D) or X Y Z (3D)."""
+    if cfg["kind"] == "1d":
+        return cfg["N"]
+    if cfg["kind"] == "2d":
+        return cfg["X"] * cfg["Y"]
+    return cfg["X"] * cfg["Y"] * cfg["Z"]
+
+
+def spectrum_reals(cfg):
+    """Reals of one filter's Hermitian half-spectrum: 2N (1D), 4XY (2D), 8XYZ (3D)."""
+    return (2 ** (1 if cfg["kind"] == "1d" else 2 if cfg["kind"] == "2d" else 3)) * grid_points(cfg)
+
+
 def algorithmic_bytes(cfg, spec_dtype):
-    """(2 + order) activations (u, gates, y) + order spectra (2N reals per
-    channel, 4XY in 2D) + order*d feedthrough scalars; each read or written once."""
+    """(2 + order) activations (u, gates, y) + order spectra + order*d
+    feedthrough scalars; each read or written once."""
     s_io = io_bytes(cfg["dtype"])
     s_sp = io_bytes(spec_dtype)
     order, d, B = cfg["order"], cfg["d"], cfg["B"]
-    if cfg["kind"] == "1d":
-        tokens = B * cfg["N"]
-        spec_reals = 2 * cfg["N"]
-    else:
-        tokens = B * cfg["X"] * cfg["Y"]
-        spec_reals = 4 * cfg["X"] * cfg["Y"]
-    return (2 + order) * tokens * d * s_io + order * d * spec_reals * s_sp + order * d * 4
+    tokens = B * grid_points(cfg)
+    return (2 + order) * tokens * d * s_io + order * d * spectrum_reals(cfg) * s_sp + order * d * 4
 
 
 def transform_points(cfg):
@@ -73,7 +82,7 @@ def transform_points(cfg):
         while M < 2 * cfg["N"]:
             M *= 2
         return M
-    return 4 * cfg["X"] * cfg["Y"]
+    return spectrum_reals(cfg)
 
 
 def algorithmic_flops(cfg):
@@ -81,7 +90,7 @@ def algorithmic_flops(cfg):
     real data; a forward and an inverse per stage; 9 flops per output for the
     spectral product, feedthrough and gate."""
     M = transform_points(cfg)
-    tokens = cfg["B"] * (cfg["N"] if cfg["kind"] == "1d" else cfg["X"] * cfg["Y"])
+    tokens = cfg["B"] * grid_points(cfg)
     per_tc = cfg["order"] * (2 * 5 * (M / 2) * math.log2(M) / (M / 2) + 9)
     return per_tc * tokens * cfg["d"]
 
@@ -136,7 +145,8 @@ def run_workload(idx, steps, warmup, min_rotation_bytes=600 << 20):
     name = CONFIG_NAMES[idx]
     io = hyena.HYENA_F32 if cfg["dtype"] == synth.F32 else hyena.HYENA_BF16
     spec_dtype = io
-    dims = (cfg["N"],) if cfg["kind"] == "1d" else (cfg["X"], cfg["Y"])
+    dims = {"1d": lambda: (cfg["N"],), "2d": lambda: (cfg["X"], cfg["Y"]),
+            "3d": lambda: (cfg["X"], cfg["Y"], cfg["Z"])}[cfg["kind"]]()
     log(f"[bench] {name}: building plan")
     try:
         plan = hyena.Plan(cfg["B"], cfg["d"], cfg["order"], dims, io_dtype=io,
@@ -230,13 +240,13 @@ def run_workload(idx, steps, warmup, min_rotation_bytes=600 << 20):
     if dropped:
         log(f"[bench] {name}: {dropped} launches not timed")
 
-    tokens = cfg["B"] * (cfg["N"] if cfg["kind"] == "1d" else cfg["X"] * cfg["Y"])
+    tokens = cfg["B"] * grid_points(cfg)
     tc = tokens * cfg["d"]
     ms = total_ms / steps
     flops = algorithmic_flops(cfg)
     res = {
         "workload": name,
-        "path": {1: "LDS1D", 2: "FOURSTEP1D", 3: "ROWCOL2D"}[plan.path],
+        "path": {1: "LDS1D", 2: "FOURSTEP1D", 3: "ROWCOL2D", 4: "ROWCOL3D"}[plan.path],
         "B": cfg["B"], "d": cfg["d"], "order": cfg["order"],
         "dims": list(dims), "storage": cfg["dtype"],
         "spectrum": "bf16" if spec_dtype == hyena.HYENA_BF16 else "f32",
@@ -272,15 +282,15 @@ def kernel_share(cfg, kernel):
     Per token*channel and stage the flop model gives 5 log2 M to each of the
     forward and the inverse transform and 9 to the spectral product,
     feedthrough and gate; a multi-pass transform of length M = La * Lb
-    splits its 5 log2 M as 5 log2 La (outer pass) + 5 log2 Lb (inner pass).
+    splits its 5 log2 M as 5 log2 La (outer pass) + 5 log2 Lb (inner pass),
+    and on 3D grids M = P3 P2 P1 as outer, middle and inner passes.
     Bytes: the activations, spectra and feedthrough a kernel consumes or
     produces; staging copies move no algorithmic bytes."""
-    tc = cfg["B"] * cfg["d"] * (cfg["N"] if cfg["kind"] == "1d" else cfg["X"] * cfg["Y"])
+    tc = cfg["B"] * cfg["d"] * grid_points(cfg)
     s_io = io_bytes(cfg["dtype"])
     s_sp = io_bytes(cfg["dtype"])
     order, d = cfg["order"], cfg["d"]
-    spec = order * d * (2 * cfg["N"] if cfg["kind"] == "1d" else 4 * cfg["X"] * cfg["Y"]) * s_sp \
-        + order * d * 4
+    spec = order * d * spectrum_reals(cfg) * s_sp + order * d * 4
     act = tc * s_io
     M = transform_points(cfg)
     short = kernel.split("<")[0].replace("hy::", "")
@@ -300,6 +310,10 @@ def kernel_share(cfg, kernel):
             f, b = table[mode]
             return f * tc, b
         return 0.0, 0.0
+    if short == "hyena_mp_mid":
+        # 3D: the transforms along y, one forward and one inverse per stage
+        ly, mode = int(args[0]), int(args[1])
+        return order * 5 * math.log2(ly) * tc, 0.0
     if short == "hyena_mp_inner":
         lb, mode = int(args[0]), int(args[2])
         if mode == 0:
@@ -352,14 +366,12 @@ def cpu_baseline(idx, max_channels, min_seconds=10.0, max_seconds=30.0):
     u, g, D = np.ascontiguousarray(u[..., ch]), np.ascontiguousarray(g[..., ch]), D[:, ch]
     h = np.ascontiguousarray(h[:, ch])
     method = oracle.DIRECT if (cfg["kind"] == "1d" and cfg["N"] <= 2048) else oracle.FFT
-    tokens = cfg["B"] * (cfg["N"] if cfg["kind"] == "1d" else cfg["X"] * cfg["Y"])
+    tokens = cfg["B"] * grid_points(cfg)
     reps = 0
     t0 = time.time()
     while True:
-        if cfg["kind"] == "1d":
-            oracle.hyena1d(u, g, h, D, method)
-        else:
-            oracle.hyena2d(u, g, h, D, method)
+        {"1d": oracle.hyena1d, "2d": oracle.hyena2d, "3d": oracle.hyena3d}[cfg["kind"]](
+            u, g, h, D, method)
         reps += 1
         dt = time.time() - t0
         if dt >= min_seconds or dt * (reps + 1) / reps > max_seconds:

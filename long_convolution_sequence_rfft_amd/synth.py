@@ -168,14 +168,16 @@ def make_3d(B: int, X: int, Y: int, Z: int, d: int, order: int, sigma_range=(4.0
                   meta={"sigma_range": tuple(sigma_range), "seed": seed})
 
 
-# The five workloads: an order-1 smoke shape, the 2K / 8K / 64K language-model
-# lengths at width 768, and a 256x256 image grid at width 256.
+# The workloads: an order-1 smoke shape, the 2K / 8K / 64K language-model
+# lengths at width 768, a 256x256 image grid at width 256, and a 64^3 volume
+# at width 64.
 CONFIGS = {
     0: dict(kind="1d", B=1, N=256, d=4, order=1, alpha_range=(1e-3, 5e-2), dtype=F32),
     1: dict(kind="1d", B=4, N=2048, d=768, order=2, alpha_range=(1e-4, 1e-2), dtype=F32),
     2: dict(kind="1d", B=2, N=8192, d=768, order=2, alpha_range=(1e-5, 1e-3), dtype=BF16),
     3: dict(kind="1d", B=1, N=65536, d=768, order=2, alpha_range=(1e-6, 1e-4), dtype=F32),
     4: dict(kind="2d", B=1, X=256, Y=256, d=256, order=2, sigma_range=(16.0, 128.0), dtype=F32),
+    5: dict(kind="3d", B=1, X=64, Y=64, Z=64, d=64, order=2, sigma_range=(4.0, 32.0), dtype=F32),
 }
 
 CONFIG_NAMES = {
@@ -184,6 +186,7 @@ CONFIG_NAMES = {
     2: "order2_B2_N8192_d768_bf16",
     3: "order2_B1_N65536_d768_f32",
     4: "order2_2d_B1_256x256_d256_f32",
+    5: "order2_3d_B1_64x64x64_d64_f32",
 }
 
 
@@ -191,9 +194,13 @@ def make_config(idx: int, seed: int | None = None, **override) -> Inputs:
     cfg = dict(CONFIGS[idx])
     cfg.update(override)
     seed = idx if seed is None else seed
-    if cfg.pop("kind") == "1d":
+    kind = cfg.pop("kind")
+    if kind == "1d":
         return make_1d(cfg["B"], cfg["N"], cfg["d"], cfg["order"], cfg["alpha_range"],
                        cfg["dtype"], seed)
+    if kind == "3d":
+        return make_3d(cfg["B"], cfg["X"], cfg["Y"], cfg["Z"], cfg["d"], cfg["order"],
+                       cfg["sigma_range"], cfg["dtype"], seed)
     return make_2d(cfg["B"], cfg["X"], cfg["Y"], cfg["d"], cfg["order"], cfg["sigma_range"],
                    cfg["dtype"], seed)
 
