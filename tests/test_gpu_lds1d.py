@@ -8,7 +8,7 @@ import pytest
 
 import oracle
 from long_convolution_sequence_rfft_amd import synth
-from gpu_util import oracle_ref, rel_err, run_gpu, say
+from gpu_util import from_torch, oracle_ref, rel_err, run_gpu, say, to_torch
 
 pytestmark = pytest.mark.gpu
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -219,3 +219,30 @@ def test_periodic_boundary(N, d, B, dtype):
         for n in range(2):
             for c in range(d):
                 assert rel_err(nat[n, c], oracle.fft(h[n, c])[:N // 2 + 1]) < 2e-6
+
+
+@pytest.mark.parametrize("d,dtype,tol", [(200, synth.F32, TOL_F32), (200, synth.BF16, TOL_BF16),
+                                         (131, synth.BF16, TOL_BF16), (131, synth.F16, TOL_F16),
+                                         (768, synth.F32, TOL_F32)])
+def test_single_channel_wide_and_odd(d, dtype, tol):
+    # staging tiles of 64 channels with a ragged last tile, odd d (16-bit
+    # channels moved one at a time), and the forward issued from a non-default
+    # stream twice in a row
+    import torch
+    inp = synth.make_1d(B=2, N=1024, d=d, order=2, alpha_range=(1e-3, 1e-2), dtype=dtype, seed=70)
+    y, plan, H = run_gpu(inp)
+    assert plan.path == 1
+    e = rel_err(y, oracle_ref(inp, method=oracle.FFT))
+    say(f"[gpu] pipeline d={d} {dtype} rel err {e:.3e}")
+    assert e < tol
+    # the same forward issued from another torch stream, twice in a row
+    # without a host wait in between: identical bits
+    u = to_torch(inp.u, dtype)
+    gates = [to_torch(g, dtype) for g in inp.gates]
+    D = torch.from_numpy(inp.D).cuda()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        y1 = plan.forward(u, gates, H, D)
+        y2 = plan.forward(u, gates, H, D)
+    s.synchronize()
+    assert np.array_equal(from_torch(y1, dtype), y) and np.array_equal(from_torch(y2, dtype), y)
