@@ -558,25 +558,24 @@ __global__ void __launch_bounds__(kMpThreads, 2) hyena_mp_inner(InnerArgs a)
     constexpr int NLIVE = MODE == INNER_SPEC ? LB : (HALF_B ? LB / 2 : LB);
     constexpr int PER = NLIVE * 2 * U / kMpThreads;
     static_assert(NLIVE * 2 * U % kMpThreads == 0, "inner tile split");
+    // fast path: 2U divides the thread count, so a thread's (unit, side) --
+    // hence its column -- is the same in every iteration; inner positions
+    // step by kMpThreads / (2U)
+    static_assert(kMpThreads % (2 * U) == 0, "inner tile rows");
+    constexpr int OPS = kMpThreads / (2 * U);
+    const int u_t = (int)threadIdx.x % U;
+    const int side_t = ((int)threadIdx.x / U) & 1;
+    const int op_t = (int)threadIdx.x / (2 * U);
+    const int fq_t = 2 * u_t + side_t;
     if (nu == U) {
+        const float2* src = Fp + col_of(u_t, side_t);
         float2 xin[PER];
 #pragma unroll
-        for (int it = 0; it < PER; ++it) {
-            const int idx = (int)threadIdx.x + it * kMpThreads;
-            const int u = idx % U;
-            const int side = (idx / U) & 1;
-            const int op = idx / (2 * U);
-            xin[it] = Fp[(int64_t)op * La + col_of(u, side)];
-        }
+        for (int it = 0; it < PER; ++it) xin[it] = src[(int64_t)(op_t + it * OPS) * La];
 #pragma unroll
         for (int it = 0; it < PER; ++it) {
-            const int idx = (int)threadIdx.x + it * kMpThreads;
-            const int u = idx % U;
-            const int side = (idx / U) & 1;
-            const int op = idx / (2 * U);
-            const int fq = 2 * u + side;
-            sre[fq * LW + lpad(op)] = xin[it].x;
-            sim[fq * LW + lpad(op)] = xin[it].y;
+            sre[fq_t * LW + lpad(op_t + it * OPS)] = xin[it].x;
+            sim[fq_t * LW + lpad(op_t + it * OPS)] = xin[it].y;
         }
     } else {
         const int total = nlive * nu * 2;
@@ -656,24 +655,14 @@ __global__ void __launch_bounds__(kMpThreads, 2) hyena_mp_inner(InnerArgs a)
     regs_to_lds<LB, HALF_B>(v, re, im, tau);
     __syncthreads();
     if (nu == U) {
+        float2* dst = Fp + col_of(u_t, side_t);
         float2 xout[PER];
 #pragma unroll
-        for (int it = 0; it < PER; ++it) {
-            const int idx = (int)threadIdx.x + it * kMpThreads;
-            const int u = idx % U;
-            const int side = (idx / U) & 1;
-            const int op = idx / (2 * U);
-            const int fq = 2 * u + side;
-            xout[it] = make_float2(sre[fq * LW + lpad(op)], sim[fq * LW + lpad(op)]);
-        }
+        for (int it = 0; it < PER; ++it)
+            xout[it] = make_float2(sre[fq_t * LW + lpad(op_t + it * OPS)],
+                                   sim[fq_t * LW + lpad(op_t + it * OPS)]);
 #pragma unroll
-        for (int it = 0; it < PER; ++it) {
-            const int idx = (int)threadIdx.x + it * kMpThreads;
-            const int u = idx % U;
-            const int side = (idx / U) & 1;
-            const int op = idx / (2 * U);
-            Fp[(int64_t)op * La + col_of(u, side)] = xout[it];
-        }
+        for (int it = 0; it < PER; ++it) dst[(int64_t)(op_t + it * OPS) * La] = xout[it];
     } else {
         const int total_out = g.Lb_live * nu * 2;
         for (int idx = threadIdx.x; idx < total_out; idx += kMpThreads) {
