@@ -33,7 +33,8 @@ sys.path.insert(0, ROOT)
 
 METRIC = "Hyena FFTConv fwd token·channels/s + HBM GB/s (% peak) at N=8K and 64K"
 HBM_PEAK_GBPS = 8000.0
-# float32 vector peak with packed-FP32 instructions disabled:
+# float32 vector peak with packed-FP32 instructions disabled (all HIP code is
+# compiled that way):
 # 256 CUs x 4 SIMDs x 16 lanes x 2 flop (FMA) x 2.4 GHz
 ALU_PEAK_TFLOPS = 256 * 4 * 16 * 2 * 2.4e9 / 1e12
 HEADLINE = 2
@@ -133,16 +134,16 @@ def load_traffic(workload, kernel):
 
 def make_inputs(idx, seed):
     from long_convolution_sequence_rfft_amd import synth
-    return synth.make_config(idx, seed=seed)
+    return synth.make_workload(idx, seed=seed)
 
 
 def run_workload(idx, steps, warmup, min_rotation_bytes=600 << 20):
     import torch
     from long_convolution_sequence_rfft_amd import hyena, synth
-    from long_convolution_sequence_rfft_amd.synth import CONFIGS, CONFIG_NAMES
+    from long_convolution_sequence_rfft_amd.synth import WORKLOADS, WORKLOAD_NAMES
 
-    cfg = dict(CONFIGS[idx])
-    name = CONFIG_NAMES[idx]
+    cfg = dict(WORKLOADS[idx])
+    name = WORKLOAD_NAMES[idx]
     io = hyena.HYENA_F32 if cfg["dtype"] == synth.F32 else hyena.HYENA_BF16
     spec_dtype = io
     dims = {"1d": lambda: (cfg["N"],), "2d": lambda: (cfg["X"], cfg["Y"]),
@@ -358,8 +359,8 @@ def cpu_baseline(idx, max_channels, min_seconds=10.0, max_seconds=30.0):
     """The float64 oracle on the workload's first `max_channels` channels (all
     tokens), repeated until about `min_seconds` of wall time have passed."""
     import oracle
-    from long_convolution_sequence_rfft_amd.synth import CONFIGS
-    cfg = CONFIGS[idx]
+    from long_convolution_sequence_rfft_amd.synth import WORKLOADS
+    cfg = WORKLOADS[idx]
     inp = make_inputs(idx, seed=idx)
     ch = np.arange(min(max_channels, cfg["d"]))
     u, g, h, D = inp.f64()
@@ -412,13 +413,13 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; the path shards over "
-                          "channels with no communication (see DESIGN.md), but no multi-GPU "
+        print(json.dumps({"error": "bench.py runs on one GPU only; the path shards over "
+                          "channels with no communication between GPUs, but no multi-GPU "
                           "run is provided", "n_gpus": args.gpus}), flush=True)
         sys.exit(2)
 
     import torch
-    from long_convolution_sequence_rfft_amd.synth import CONFIG_NAMES
+    from long_convolution_sequence_rfft_amd.synth import WORKLOAD_NAMES
     if not torch.cuda.is_available():
         print(json.dumps({"error": "no GPU visible"}), flush=True)
         sys.exit(1)
@@ -429,7 +430,7 @@ def main():
 
     results = {}
     for idx in ORDER_OF_RUN:
-        if args.only and CONFIG_NAMES[idx] != args.only and str(idx) != args.only:
+        if args.only and WORKLOAD_NAMES[idx] != args.only and str(idx) != args.only:
             continue
         r = run_workload(idx, args.steps, args.warmup)
         if r is not None:

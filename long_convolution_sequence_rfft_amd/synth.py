@@ -171,7 +171,7 @@ def make_3d(B: int, X: int, Y: int, Z: int, d: int, order: int, sigma_range=(4.0
 # The workloads: an order-1 smoke shape, the 2K / 8K / 64K language-model
 # lengths at width 768, a 256x256 image grid at width 256, and a 64^3 volume
 # at width 64.
-CONFIGS = {
+WORKLOADS = {
     0: dict(kind="1d", B=1, N=256, d=4, order=1, alpha_range=(1e-3, 5e-2), dtype=F32),
     1: dict(kind="1d", B=4, N=2048, d=768, order=2, alpha_range=(1e-4, 1e-2), dtype=F32),
     2: dict(kind="1d", B=2, N=8192, d=768, order=2, alpha_range=(1e-5, 1e-3), dtype=BF16),
@@ -180,7 +180,7 @@ CONFIGS = {
     5: dict(kind="3d", B=1, X=64, Y=64, Z=64, d=64, order=2, sigma_range=(4.0, 32.0), dtype=F32),
 }
 
-CONFIG_NAMES = {
+WORKLOAD_NAMES = {
     0: "order1_B1_N256_d4_f32",
     1: "order2_B4_N2048_d768_f32",
     2: "order2_B2_N8192_d768_bf16",
@@ -190,8 +190,8 @@ CONFIG_NAMES = {
 }
 
 
-def make_config(idx: int, seed: int | None = None, **override) -> Inputs:
-    cfg = dict(CONFIGS[idx])
+def make_workload(idx: int, seed: int | None = None, **override) -> Inputs:
+    cfg = dict(WORKLOADS[idx])
     cfg.update(override)
     seed = idx if seed is None else seed
     kind = cfg.pop("kind")

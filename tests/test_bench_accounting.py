@@ -12,13 +12,13 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 sys.path.insert(0, ROOT)
 
 import bench  # noqa: E402
-from long_convolution_sequence_rfft_amd.synth import CONFIGS  # noqa: E402
+from long_convolution_sequence_rfft_amd.synth import WORKLOADS  # noqa: E402
 
 
 @pytest.mark.parametrize("idx,mb", [(1, 125.8), (2, 151.0), (3, 1610.6), (4, 805.3), (5, 1342.2)])
 def test_algorithmic_bytes(idx, mb):
     # (2 + order) activations + order Hermitian half-spectra + feedthrough
-    cfg = CONFIGS[idx]
+    cfg = WORKLOADS[idx]
     spec = "bf16" if cfg["dtype"] == "bf16" else "f32"
     assert abs(bench.algorithmic_bytes(cfg, spec) / 1e6 - mb) < 0.1
 
@@ -42,7 +42,7 @@ def test_kernel_shares_cover_the_forward(idx, kernels):
     # the flops of the model and the algorithmic bytes are each attributed
     # once across the kernels of one forward (flops up to the 8-vs-9 per-tc
     # rounding of the product term in the multi-pass split)
-    cfg = CONFIGS[idx]
+    cfg = WORKLOADS[idx]
     parts = _split(cfg, kernels)
     flops = sum(p[0] for p in parts)
     nbytes = sum(p[1] for p in parts)
@@ -52,7 +52,7 @@ def test_kernel_shares_cover_the_forward(idx, kernels):
 
 
 def test_roofline_record_fields():
-    cfg = CONFIGS[2]
+    cfg = WORKLOADS[2]
     name = "hy::hyena_lds1d_real_forward<8192, unsigned short, unsigned short, false>"
     res = {"cfg": cfg, "workload": "no-such-workload",
            "kernels": {name: {"launches_per_forward": 1.0, "avg_launch_ms": 0.1,

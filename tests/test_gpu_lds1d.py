@@ -30,8 +30,8 @@ def test_worked_example_on_gpu():
 
 
 @pytest.mark.parametrize("seed", [0, 100, 200])
-def test_config0_parity(seed):
-    inp = synth.make_config(0, seed=seed)
+def test_smallest_workload_parity(seed):
+    inp = synth.make_workload(0, seed=seed)
     y, _, _ = run_gpu(inp)
     ref = oracle_ref(inp, method=oracle.DIRECT)
     assert rel_err(y, ref) < TOL_F32
@@ -118,24 +118,24 @@ def test_causality_on_gpu():
 
 
 @pytest.mark.parametrize("cfg", [1, 2])
-def test_full_size_config_sampled(cfg):
-    inp = synth.make_config(cfg)
+def test_full_size_workload_sampled(cfg):
+    inp = synth.make_workload(cfg)
     y, _, _ = run_gpu(inp)
     rng = np.random.default_rng(cfg)
     ch = np.unique(np.concatenate([[0, 1, inp.d - 2, inp.d - 1], rng.choice(inp.d, 12, replace=False)]))
     ref = oracle_ref(inp, channels=ch, method=oracle.DIRECT)
     e = rel_err(y[..., ch], ref)
-    say(f"config {cfg} sampled-channel rel_err={e:.3e}")
+    say(f"workload {cfg} sampled-channel rel_err={e:.3e}")
     assert e < (TOL_F32 if inp.dtype == synth.F32 else TOL_BF16)
 
 
 @pytest.mark.parametrize("cfg", [1, 2])
-def test_full_size_config_all_channels(cfg):
-    inp = synth.make_config(cfg, seed=cfg + 100)
+def test_full_size_workload_all_channels(cfg):
+    inp = synth.make_workload(cfg, seed=cfg + 100)
     y, _, _ = run_gpu(inp)
     ref = oracle_ref(inp, method=oracle.FFT)
     e = rel_err(y, ref)
-    say(f"config {cfg} all-channel rel_err={e:.3e}")
+    say(f"workload {cfg} all-channel rel_err={e:.3e}")
     assert e < (TOL_F32 if inp.dtype == synth.F32 else TOL_BF16)
 
 

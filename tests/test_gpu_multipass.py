@@ -123,7 +123,7 @@ def test_multipass_deterministic_bitwise():
 
 
 def test_full_size_64k_sampled():
-    inp = synth.make_config(3)
+    inp = synth.make_workload(3)
     y, plan, _ = run_gpu(inp)
     rng = np.random.default_rng(3)
     ch = np.unique(np.concatenate([[0, 1, inp.d - 1], rng.choice(inp.d, 13, replace=False)]))
@@ -134,7 +134,7 @@ def test_full_size_64k_sampled():
 
 
 def test_full_size_2d_sampled():
-    inp = synth.make_config(4)
+    inp = synth.make_workload(4)
     y, plan, _ = run_gpu(inp)
     rng = np.random.default_rng(4)
     ch = np.unique(np.concatenate([[0, 1, inp.d - 1], rng.choice(inp.d, 5, replace=False)]))
@@ -286,4 +286,15 @@ def test_full_size_3d_sampled():
     ref = oracle_ref(inp, channels=ch, method=oracle.FFT)
     e = rel_err(y[..., ch], ref)
     say(f"3D 64^3 d=32 sampled rel_err={e:.3e}")
+    assert e < TOL_F32
+
+
+@pytest.mark.parametrize("X,Y,Z,d", [(256, 64, 64, 1), (4, 256, 256, 2), (256, 256, 4, 1)])
+def test_rowcol3d_largest_sides(X, Y, Z, d):
+    # 512-point transforms along each axis in turn; the largest 3D grids
+    # (2^20 and 2^18 points)
+    inp = synth.make_3d(B=1, X=X, Y=Y, Z=Z, d=d, order=2, sigma_range=(2.0, 16.0), seed=16)
+    y, _, _ = run_gpu(inp)
+    e = rel_err(y, oracle_ref(inp, method=oracle.FFT))
+    say(f"[gpu] 3D {X}x{Y}x{Z} rel err {e:.3e}")
     assert e < TOL_F32

@@ -436,10 +436,10 @@ def test_bf16_rounding_is_nearest_even():
 
 
 def test_inputs_are_seeded_and_reproducible():
-    a = synth.make_config(0)
-    b = synth.make_config(0)
+    a = synth.make_workload(0)
+    b = synth.make_workload(0)
     assert np.array_equal(a.u, b.u) and np.array_equal(a.h, b.h)
-    c = synth.make_config(0, seed=100)
+    c = synth.make_workload(0, seed=100)
     assert not np.array_equal(a.u, c.u)
 
 
