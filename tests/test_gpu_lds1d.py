@@ -246,3 +246,42 @@ def test_single_channel_wide_and_odd(d, dtype, tol):
         y2 = plan.forward(u, gates, H, D)
     s.synchronize()
     assert np.array_equal(from_torch(y1, dtype), y) and np.array_equal(from_torch(y2, dtype), y)
+
+
+@pytest.mark.parametrize("shape", [("1d", 2048, 96, synth.BF16), ("1d", 20000, 5, synth.F32),
+                                   ("2d", (16, 32), 6, synth.F32)])
+def test_forward_in_a_hip_graph(shape):
+    # the forward captured into a HIP graph (no allocation or memset inside
+    # the library's launches) and replayed several times, with eager work and
+    # host waits between replays: every replay equals the eager result
+    import torch
+    from long_convolution_sequence_rfft_amd import hyena
+    kind, dims, d, dtype = shape
+    if kind == "1d":
+        inp = synth.make_1d(B=2, N=dims, d=d, order=2, alpha_range=(1e-3, 1e-2), dtype=dtype,
+                            seed=71)
+    else:
+        inp = synth.make_2d(B=1, X=dims[0], Y=dims[1], d=d, order=2, sigma_range=(1.0, 8.0),
+                            seed=72)
+    y_eager, plan, H = run_gpu(inp)
+    u = to_torch(inp.u, dtype)
+    gates = [to_torch(g, dtype) for g in inp.gates]
+    D = torch.from_numpy(inp.D).cuda()
+    y = torch.empty_like(u)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):  # warm-up on the capture stream
+        plan.forward(u, gates, H, D, y)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    say(f"[gpu] graph capture {kind} dims={dims} d={d} {dtype}")
+    with torch.cuda.graph(g):
+        plan.forward(u, gates, H, D, y)
+    for r in range(3):
+        y.fill_(0)
+        plan.forward(u, gates, H, D, torch.empty_like(u))  # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(from_torch(y, dtype), y_eager), f"replay {r}"
