@@ -14,6 +14,8 @@ Functions follow the pages cited in ``oracle.c``:
   * ``conv2d`` / ``hyena2d`` -- [P3] "How HyenaND works", non-causal zero-padded
     2D convolution on the native grid
   * ``conv3d`` / ``hyena3d`` -- the same on a 3D grid
+  * ``dwconv3x3x3`` / ``hyena3d_block`` -- the mixer on a 3D grid (3x3x3 short
+    convolutions)
   * ``fft`` -- [P2] "Counting the cost" radix-2 FFT
   * ``circular_conv`` -- [P2] "Linear vs circular" (the unpadded contrast)
   * ``circular_conv_direct`` / ``hyena1d_circular`` -- the chain with periodic
@@ -90,6 +92,11 @@ def _load():
             lib.oracle_conv3d_fft.restype = ctypes.c_int
             lib.oracle_hyena3d.argtypes = [i64, i64, i64, i64, i64, i32, p, p, p, p, p, i32]
             lib.oracle_hyena3d.restype = ctypes.c_int
+            lib.oracle_dwconv3x3x3.argtypes = [i64, i64, i64, i64, i64, p, p, p, p]
+            lib.oracle_dwconv3x3x3.restype = None
+            lib.oracle_hyena3d_block.argtypes = [i64, i64, i64, i64, i64, p, p, p, p, p, p, p, p,
+                                                 i32]
+            lib.oracle_hyena3d_block.restype = ctypes.c_int
             lib.oracle_circular_conv_direct.argtypes = [i64, i64, i64, p, p, p, p]
             lib.oracle_circular_conv_direct.restype = None
             lib.oracle_hyena1d_circular.argtypes = [i64, i64, i64, i32, p, p, p, p, p, i32]
@@ -302,4 +309,33 @@ def hyena2d_block(q, k, v, sw, sb, K, D, method: int = DIRECT) -> np.ndarray:
                                       _ptr(y), method)
     if rc != 0:
         raise MemoryError("oracle_hyena2d_block failed")
+    return y
+
+
+def dwconv3x3x3(x, w, bias=None) -> np.ndarray:
+    """Depthwise 3x3x3 cross-correlation, zero padding 1: x [B,X,Y,Z,d], w [d,3,3,3]."""
+    x, w = _f64(x), _f64(w)
+    B, X, Y, Z, d = x.shape
+    assert w.shape == (d, 3, 3, 3)
+    b = _f64(bias) if bias is not None else None
+    o = np.empty_like(x)
+    _load().oracle_dwconv3x3x3(B, X, Y, Z, d, _ptr(x), _ptr(w),
+                               _ptr(b) if b is not None else None, _ptr(o))
+    return o
+
+
+def hyena3d_block(q, k, v, sw, sb, K, D, method: int = DIRECT) -> np.ndarray:
+    """HyenaND mixer on a 3D grid: q, k, v [B,X,Y,Z,d]; sw [3,d,3,3,3]; sb [3,d] or None;
+    K [d,2X-1,2Y-1,2Z-1]; D [d]."""
+    q, k, v, sw, K, D = _f64(q), _f64(k), _f64(v), _f64(sw), _f64(K), _f64(D)
+    B, X, Y, Z, d = q.shape
+    assert sw.shape == (3, d, 3, 3, 3) and D.shape == (d,)
+    assert K.shape == (d, 2 * X - 1, 2 * Y - 1, 2 * Z - 1)
+    b = _f64(sb) if sb is not None else None
+    y = np.empty_like(q)
+    rc = _load().oracle_hyena3d_block(B, X, Y, Z, d, _ptr(q), _ptr(k), _ptr(v), _ptr(sw),
+                                      _ptr(b) if b is not None else None, _ptr(K), _ptr(D),
+                                      _ptr(y), method)
+    if rc != 0:
+        raise MemoryError("oracle_hyena3d_block failed")
     return y

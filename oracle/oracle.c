@@ -693,3 +693,64 @@ int oracle_hyena2d_block(int64_t B, int64_t X, int64_t Y, int64_t d, const doubl
     free(qs); free(ks); free(vs); free(w);
     return rc;
 }
+
+/* ------------------------------------------------------------------------ */
+/* HyenaND mixer on a 3D grid: the same block with 3x3x3 short convolutions */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * Depthwise 3x3x3 cross-correlation with zero padding of one:
+ *   o[b,p,q,r,c] = bias[c] + sum_{a,e,f in -1..1} w[c][a+1][e+1][f+1] x[b,p+a,q+e,r+f,c]
+ * x and o [B][X][Y][Z][d]; w [d][3][3][3]; bias [d] or NULL.
+ */
+void oracle_dwconv3x3x3(int64_t B, int64_t X, int64_t Y, int64_t Z, int64_t d, const double* x,
+                        const double* w, const double* bias, double* o)
+{
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t b = 0; b < B; ++b)
+        for (int64_t p = 0; p < X; ++p)
+            for (int64_t q = 0; q < Y; ++q)
+                for (int64_t r = 0; r < Z; ++r)
+                    for (int64_t c = 0; c < d; ++c) {
+                        double acc = bias ? bias[c] : 0.0;
+                        for (int a = -1; a <= 1; ++a)
+                            for (int e = -1; e <= 1; ++e)
+                                for (int f = -1; f <= 1; ++f) {
+                                    const int64_t pp = p + a, qq = q + e, rr = r + f;
+                                    if (pp < 0 || pp >= X || qq < 0 || qq >= Y || rr < 0 || rr >= Z)
+                                        continue;
+                                    acc += w[((c * 3 + (a + 1)) * 3 + (e + 1)) * 3 + (f + 1)] *
+                                           x[(((b * X + pp) * Y + qq) * Z + rr) * d + c];
+                                }
+                        o[(((b * X + p) * Y + q) * Z + r) * d + c] = acc;
+                    }
+}
+
+/*
+ * The mixer on a 3D grid:
+ *   qs, ks, vs = dwconv3x3x3(q | k | v)   (sw [3][d][3][3][3], sb [3][d] or NULL)
+ *   z = qs . SiLU(ks)
+ *   y = SiLU(vs) . (K * z + D z)          (K as in oracle_conv3d_direct)
+ */
+int oracle_hyena3d_block(int64_t B, int64_t X, int64_t Y, int64_t Z, int64_t d, const double* q,
+                         const double* k, const double* v, const double* sw, const double* sb,
+                         const double* K, const double* D, double* y, int32_t method)
+{
+    const int64_t E = B * X * Y * Z * d;
+    double* qs = (double*)malloc(sizeof(double) * E);
+    double* ks = (double*)malloc(sizeof(double) * E);
+    double* vs = (double*)malloc(sizeof(double) * E);
+    double* w = (double*)malloc(sizeof(double) * E);
+    if (!qs || !ks || !vs || !w) { free(qs); free(ks); free(vs); free(w); return -1; }
+    oracle_dwconv3x3x3(B, X, Y, Z, d, q, sw, sb ? sb : NULL, qs);
+    oracle_dwconv3x3x3(B, X, Y, Z, d, k, sw + 27 * d, sb ? sb + d : NULL, ks);
+    oracle_dwconv3x3x3(B, X, Y, Z, d, v, sw + 54 * d, sb ? sb + 2 * d : NULL, vs);
+    for (int64_t i = 0; i < E; ++i) qs[i] *= silu(ks[i]);
+    int rc = 0;
+    if (method == 0) oracle_conv3d_direct(B, X, Y, Z, d, qs, K, D, w);
+    else rc = oracle_conv3d_fft(B, X, Y, Z, d, qs, K, D, w);
+    if (rc == 0)
+        for (int64_t i = 0; i < E; ++i) y[i] = silu(vs[i]) * w[i];
+    free(qs); free(ks); free(vs); free(w);
+    return rc;
+}

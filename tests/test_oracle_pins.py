@@ -708,3 +708,48 @@ def test_hyena3d_chain_by_hand(method):
                 w[b, ..., c] = _scipy_same3(z[b, ..., c], K[n, c]) + D[n, c] * z[b, ..., c]
         z = g[n] * w
     assert _rel(y, z) < 1e-12
+
+
+def test_dwconv3x3x3_is_scipy_correlate():
+    # zero-padded 3x3x3 cross-correlation per channel (scipy's n-D correlate)
+    rng = np.random.default_rng(92)
+    B, X, Y, Z, d = 2, 5, 6, 7, 3
+    x, w, b = rng.normal(size=(B, X, Y, Z, d)), rng.normal(size=(d, 3, 3, 3)), rng.normal(size=d)
+    o = oracle.dwconv3x3x3(x, w, b)
+    for bb in range(B):
+        for c in range(d):
+            ref = scipy.signal.correlate(x[bb, ..., c], w[c], mode="same", method="direct") + b[c]
+            assert _rel(o[bb, ..., c], ref) < 1e-14
+
+
+def test_hyena3d_block_reduces_to_the_gated_chain():
+    # identity short convolutions: y = SiLU(v) . (K * (q . SiLU(k)) + D (q . SiLU(k)))
+    rng = np.random.default_rng(93)
+    B, X, Y, Z, d = 1, 4, 3, 5, 2
+    q, k, v = (rng.normal(size=(B, X, Y, Z, d)) for _ in range(3))
+    K = rng.normal(size=(d, 2 * X - 1, 2 * Y - 1, 2 * Z - 1))
+    D = rng.normal(size=d)
+    sw = np.zeros((3, d, 3, 3, 3))
+    sw[:, :, 1, 1, 1] = 1.0
+    silu = lambda x: x / (1.0 + np.exp(-x))
+    for method in (oracle.DIRECT, oracle.FFT):
+        y = oracle.hyena3d_block(q, k, v, sw, None, K, D, method)
+        ref = oracle.hyena3d(q * silu(k), silu(v)[None], K[None], D[None], oracle.DIRECT)
+        assert _rel(y, ref) < 1e-12
+
+
+def test_hyena3d_block_flat_grid_is_the_2d_mixer():
+    # Z = 1: only the middle z-slice of each 3x3x3 short kernel meets data, so
+    # the 3D mixer is the (pinned) 2D mixer with those 3x3 taps
+    rng = np.random.default_rng(94)
+    B, X, Y, d = 2, 5, 4, 3
+    q, k, v = (rng.normal(size=(B, X, Y, d)) for _ in range(3))
+    sw = rng.normal(size=(3, d, 3, 3, 3))
+    sb = rng.normal(size=(3, d))
+    K = rng.normal(size=(d, 2 * X - 1, 2 * Y - 1))
+    D = rng.normal(size=d)
+    ref = oracle.hyena2d_block(q, k, v, sw[..., 1], sb, K, D, oracle.DIRECT)
+    e3 = lambda a: a[:, :, :, None, :]
+    for method in (oracle.DIRECT, oracle.FFT):
+        y = oracle.hyena3d_block(e3(q), e3(k), e3(v), sw, sb, K[..., None], D, method)
+        assert _rel(y[:, :, :, 0, :], ref) < 1e-12
