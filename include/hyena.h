@@ -166,15 +166,16 @@ hyena_status hyena_forward(hyena_plan_t plan, const void* u, const void* const* 
 
 /*
  * HyenaND mixer ("How HyenaND works", section "Putting it together: the
- * HyenaND operator"), for ndims = 2 plans of order 1: the depthwise 3x3 short
- * convolution (zero padding; taps short_w [3][d][3][3] for q, k, v, biases
- * short_b [3][d] or NULL, float32), the inner gate, the long convolution and
- * the outer gate, in the passes of the 2D transform:
+ * HyenaND operator"), for ndims = 2 or 3 plans of order 1: the depthwise
+ * short convolution (zero padding; 3x3 taps short_w [3][d][3][3] on 2D
+ * grids, 3x3x3 taps short_w [3][d][3][3][3] on 3D grids, for q, k, v; biases
+ * short_b [3][d] or NULL; float32), the inner gate, the long convolution and
+ * the outer gate, in the passes of the grid transform:
  *   qs, ks, vs = shortconv(q), shortconv(k), shortconv(v)
  *   z = qs . SiLU(ks),   y = SiLU(vs) . (K * z + D z),   SiLU(x) = x / (1 + e^-x)
- * q, k, v, y: [B][X][Y][d] in the plan's io dtype; y must not overlap q, k, v,
- * H, D or the workspace.  The projections producing q, k, v and the norms
- * around the mixer are the caller's.
+ * q, k, v, y: [B][X][Y][d] or [B][X][Y][Z][d] in the plan's io dtype; y must
+ * not overlap q, k, v, H, D or the workspace.  The projections producing
+ * q, k, v and the norms around the mixer are the caller's.
  */
 typedef struct hyena_nd_mixer {
     const void* q;

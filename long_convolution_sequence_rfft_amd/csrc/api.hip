@@ -169,8 +169,8 @@ hyena_status hyena_nd_mixer_forward(hyena_plan_t plan, const hyena_nd_mixer* m, 
 {
     if (plan == nullptr) return fail(HYENA_ERR_INVALID_ARGUMENT, "plan is NULL");
     const hy::Plan& p = plan->p;
-    if (p.ndims != 2 || p.order != 1)
-        return fail(HYENA_ERR_UNSUPPORTED, "the HyenaND mixer needs an ndims = 2, order 1 plan");
+    if ((p.ndims != 2 && p.ndims != 3) || p.order != 1)
+        return fail(HYENA_ERR_UNSUPPORTED, "the HyenaND mixer needs an ndims = 2 or 3, order 1 plan");
     if (m == nullptr || m->q == nullptr || m->k == nullptr || m->v == nullptr ||
         m->short_w == nullptr || H == nullptr || D == nullptr || y == nullptr)
         return fail(HYENA_ERR_INVALID_ARGUMENT, "a required pointer is NULL");
@@ -186,6 +186,7 @@ hyena_status hyena_nd_mixer_forward(hyena_plan_t plan, const hyena_nd_mixer* m, 
     if (st != HYENA_OK) return st;
     if (overlaps(y, nio, workspace, p.workspace_bytes))
         return fail(HYENA_ERR_INVALID_ARGUMENT, "y overlaps the workspace");
+    if (p.ndims == 3) return hy::launch_rowcol3d_block(p, *m, H, D, y, workspace, stream);
     return hy::launch_rowcol2d_block(p, *m, H, D, y, workspace, stream);
 }
 

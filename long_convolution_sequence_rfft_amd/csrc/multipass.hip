@@ -377,7 +377,8 @@ int64_t mid_blocks(const Plan& p, const MidArgs& m)
 }
 
 hyena_status mp3_forward(const Plan& p, const void* u, const void* const* gates, const void* H,
-                         const float* D, void* y, void* ws, void* stream)
+                         const float* D, void* y, void* ws, void* stream,
+                         const BlockArgs* blk = nullptr)
 {
     const hipStream_t s = (hipStream_t)stream;
     MpGeom go = base_geom3(p);
@@ -404,6 +405,7 @@ hyena_status mp3_forward(const Plan& p, const void* u, const void* const* gates,
         oa.act = u;
         oa.F = F1;
         oa.tw = tw;
+        if (blk) oa.blk = *blk;
         hyena_status st = outer(p, OUTER_IN, true, oa, col_blocks * go.ngroups, s);
         if (st != HYENA_OK) return st;
         const MidArgs mf = mid_args(p, go, F1, F2, false, MID_FWD, tw);
@@ -421,7 +423,7 @@ hyena_status mp3_forward(const Plan& p, const void* u, const void* const* gates,
             if (st != HYENA_OK) return st;
             st = mid((int)p.P2, MID_INV, true, mi, mid_blocks(p, mi), s);
             if (st != HYENA_OK) return st;
-            oa.act = gates[n];
+            oa.act = blk ? nullptr : gates[n];
             oa.out = y;
             st = outer(p, n + 1 < p.order ? OUTER_MID : OUTER_OUT, true, oa, col_blocks * go.ngroups, s);
             if (st != HYENA_OK) return st;
@@ -607,6 +609,18 @@ hyena_status launch_rowcol3d_spectrum(const Plan& p, const void* h, void* H, voi
 hyena_status launch_rowcol3d_export(const Plan& p, const void* H, void* out, void* stream)
 {
     return mp3_export(p, H, out, stream);
+}
+hyena_status launch_rowcol3d_block(const Plan& p, const hyena_nd_mixer& m, const void* H,
+                                   const float* D, void* y, void* ws, void* stream)
+{
+    BlockArgs b{};
+    b.q = m.q;
+    b.k = m.k;
+    b.v = m.v;
+    b.sw = m.short_w;
+    b.sb = m.short_b;
+    b.on = 1;
+    return mp3_forward(p, nullptr, nullptr, H, D, y, ws, stream, &b);
 }
 
 }  // namespace hy

@@ -26,13 +26,13 @@ struct MpShape {
 
 // HyenaND mixer inputs ("How HyenaND works", section "Putting it together:
 // the HyenaND operator"): with `on`, OUTER_IN reads q . SiLU(k) and OUTER_OUT
-// gates with SiLU(v), where q, k, v first pass a depthwise 3x3 short
-// convolution (zero padding) on the X x Y grid.
+// gates with SiLU(v), where q, k, v first pass a depthwise short convolution
+// with zero padding: 3x3 on an X x Y grid, 3x3x3 on an X x Y x Z grid.
 struct BlockArgs {
     const void* q;
     const void* k;
     const void* v;
-    const float* sw;  // [3][d][3][3] short-conv taps of q, k, v
+    const float* sw;  // [3][d][3][3] (2D) or [3][d][3][3][3] (3D) taps of q, k, v
     const float* sb;  // [3][d] biases, or NULL
     int32_t on;
 };
@@ -70,21 +70,24 @@ __device__ __forceinline__ float2 act_load(const IO* base, int64_t row, int64_t 
 
 __device__ __forceinline__ float silu(float x) { return x / (1.0f + expf(-x)); }
 
-// Short-conv taps of one channel pair (c0, c0 + 1) of tensor j (0 q, 1 k, 2 v).
+// Short-conv taps of one channel pair (c0, c0 + 1) of tensor j (0 q, 1 k,
+// 2 v): NT = 9 (3x3) or 27 (3x3x3) taps per channel.
+template <int NT>
 struct PairTaps {
-    float w[2][9];
+    float w[2][NT];
     float b[2];
 };
 
-__device__ __forceinline__ PairTaps pair_taps(const BlockArgs& k, int j, int64_t c0, int64_t d)
+template <int NT>
+__device__ __forceinline__ PairTaps<NT> pair_taps(const BlockArgs& k, int j, int64_t c0, int64_t d)
 {
-    PairTaps t;
+    PairTaps<NT> t;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
         const bool live = c0 + h < d;
         const int64_t c = live ? c0 + h : c0;
 #pragma unroll
-        for (int i = 0; i < 9; ++i) t.w[h][i] = live ? k.sw[((int64_t)j * d + c) * 9 + i] : 0.0f;
+        for (int i = 0; i < NT; ++i) t.w[h][i] = live ? k.sw[((int64_t)j * d + c) * NT + i] : 0.0f;
         t.b[h] = (live && k.sb) ? k.sb[(int64_t)j * d + c] : 0.0f;
     }
     return t;
@@ -93,7 +96,7 @@ __device__ __forceinline__ PairTaps pair_taps(const BlockArgs& k, int j, int64_t
 // Depthwise 3x3 short convolution of one channel pair at grid point (p, q)
 // of batch row b: row = b X Y + p Y + q is the point's activation row.
 template <typename IO>
-__device__ __forceinline__ float2 short_conv(const IO* x, const PairTaps& t, int64_t row,
+__device__ __forceinline__ float2 short_conv(const IO* x, const PairTaps<9>& t, int64_t row,
                                              int64_t p, int64_t q, int64_t X, int64_t Y,
                                              int64_t c0, int64_t d)
 {
@@ -107,6 +110,30 @@ __device__ __forceinline__ float2 short_conv(const IO* x, const PairTaps& t, int
             acc.x = fmaf(t.w[0][(a + 1) * 3 + e + 1], xv.x, acc.x);
             acc.y = fmaf(t.w[1][(a + 1) * 3 + e + 1], xv.y, acc.y);
         }
+    return acc;
+}
+
+// Depthwise 3x3x3 short convolution of one channel pair at grid point
+// (p, q, r) of batch row b: row = b X Y Z + (p Y + q) Z + r.
+template <typename IO>
+__device__ __forceinline__ float2 short_conv3(const IO* x, const PairTaps<27>& t, int64_t row,
+                                              int64_t p, int64_t q, int64_t r, int64_t X,
+                                              int64_t Y, int64_t Z, int64_t c0, int64_t d)
+{
+    float2 acc = make_float2(t.b[0], t.b[1]);
+#pragma unroll
+    for (int a = -1; a <= 1; ++a)
+#pragma unroll
+        for (int e = -1; e <= 1; ++e)
+#pragma unroll
+            for (int f = -1; f <= 1; ++f) {
+                if (p + a < 0 || p + a >= X || q + e < 0 || q + e >= Y || r + f < 0 || r + f >= Z)
+                    continue;
+                const float2 xv = act_load<IO>(x, row + (a * Y + e) * Z + f, c0, d);
+                const int i = ((a + 1) * 3 + e + 1) * 3 + f + 1;
+                acc.x = fmaf(t.w[0][i], xv.x, acc.x);
+                acc.y = fmaf(t.w[1][i], xv.y, acc.y);
+            }
     return acc;
 }
 
@@ -246,14 +273,42 @@ __global__ void __launch_bounds__(kMpThreads, 2) hyena_mp_outer(OuterArgs a)
         // latencies overlap instead of adding up
         const IO* u = static_cast<const IO*>(a.act);
         float2 xin[GT];
-        if (a.blk.on) {
+        if (a.blk.on && g.three_d) {
+            // the mixer on a 3D grid: rows o = x Y + y, samples s = z; q and
+            // k are convolved one after the other so only one tap set is live
+            int64_t bq0, pq0;
+            bool l0;
+            pair_of_slot(g, group, (int)(threadIdx.x & (KP - 1)), bq0, pq0, l0);
+            const IO* qx = static_cast<const IO*>(a.blk.q);
+            const IO* kx = static_cast<const IO*>(a.blk.k);
+            auto conv3 = [&](const IO* x, const PairTaps<27>& t, int s, int64_t pq, int64_t row) {
+                const int64_t o3 = (row % g.N) / g.so;
+                const int64_t px = o3 / g.gy, py = o3 - px * g.gy;
+                return short_conv3<IO>(x, t, row, px, py, s, g.gx, g.gy, g.gz, 2 * pq, g.d);
+            };
+            {
+                const PairTaps<27> tq = pair_taps<27>(a.blk, 0, 2 * pq0, g.d);
+                tile_rows([&](int it, int, int s, int64_t pq, bool ok, int64_t row) {
+                    xin[it] = ok ? conv3(qx, tq, s, pq, row) : make_float2(0.0f, 0.0f);
+                });
+            }
+            {
+                const PairTaps<27> tk = pair_taps<27>(a.blk, 1, 2 * pq0, g.d);
+                tile_rows([&](int it, int, int s, int64_t pq, bool ok, int64_t row) {
+                    if (ok) {
+                        const float2 kv = conv3(kx, tk, s, pq, row);
+                        xin[it] = make_float2(xin[it].x * silu(kv.x), xin[it].y * silu(kv.y));
+                    }
+                });
+            }
+        } else if (a.blk.on) {
             // HyenaND mixer input q . SiLU(k) after the short convolutions;
             // this thread's channel pair is the same in every tile element
             int64_t bq0, pq0;
             bool l0;
             pair_of_slot(g, group, (int)(threadIdx.x & (KP - 1)), bq0, pq0, l0);
-            const PairTaps tq = pair_taps(a.blk, 0, 2 * pq0, g.d);
-            const PairTaps tk = pair_taps(a.blk, 1, 2 * pq0, g.d);
+            const PairTaps<9> tq = pair_taps<9>(a.blk, 0, 2 * pq0, g.d);
+            const PairTaps<9> tk = pair_taps<9>(a.blk, 1, 2 * pq0, g.d);
             const IO* qx = static_cast<const IO*>(a.blk.q);
             const IO* kx = static_cast<const IO*>(a.blk.k);
             tile_rows([&](int it, int, int s, int64_t pq, bool ok, int64_t row) {
@@ -331,12 +386,30 @@ __global__ void __launch_bounds__(kMpThreads, 2) hyena_mp_outer(OuterArgs a)
         load_column<LA, +1>(v, Fcol, twstep, tau, col_live, g.four_step && o > 0);
         const IO* gate = static_cast<const IO*>(a.act);
         float2 gval[GT];
-        if (MODE == OUTER_OUT && a.blk.on) {
+        if (MODE == OUTER_OUT && a.blk.on && g.three_d) {
+            // HyenaND outer gate SiLU(v) after the 3x3x3 short convolution
+            int64_t bq0, pq0;
+            bool l0;
+            pair_of_slot(g, group, (int)(threadIdx.x & (KP - 1)), bq0, pq0, l0);
+            const PairTaps<27> tv = pair_taps<27>(a.blk, 2, 2 * pq0, g.d);
+            const IO* vx = static_cast<const IO*>(a.blk.v);
+            tile_rows([&](int it, int, int s, int64_t pq, bool ok, int64_t row) {
+                float2 gv = make_float2(0.0f, 0.0f);
+                if (ok) {
+                    const int64_t o3 = (row % g.N) / g.so;
+                    const int64_t px = o3 / g.gy, py = o3 - px * g.gy;
+                    const float2 vv = short_conv3<IO>(vx, tv, row, px, py, s, g.gx, g.gy, g.gz,
+                                                      2 * pq, g.d);
+                    gv = make_float2(silu(vv.x), silu(vv.y));
+                }
+                gval[it] = gv;
+            });
+        } else if (MODE == OUTER_OUT && a.blk.on) {
             // HyenaND outer gate SiLU(v) after the short convolution
             int64_t bq0, pq0;
             bool l0;
             pair_of_slot(g, group, (int)(threadIdx.x & (KP - 1)), bq0, pq0, l0);
-            const PairTaps tv = pair_taps(a.blk, 2, 2 * pq0, g.d);
+            const PairTaps<9> tv = pair_taps<9>(a.blk, 2, 2 * pq0, g.d);
             const IO* vx = static_cast<const IO*>(a.blk.v);
             tile_rows([&](int it, int, int s, int64_t pq, bool ok, int64_t row) {
                 float2 gv = make_float2(0.0f, 0.0f);

@@ -133,6 +133,8 @@ hyena_status launch_rowcol3d_forward(const Plan& p, const void* u, const void* c
                                      const void* H, const float* D, void* y, void* ws,
                                      void* stream);
 hyena_status launch_rowcol3d_export(const Plan& p, const void* H, void* out, void* stream);
+hyena_status launch_rowcol3d_block(const Plan& p, const hyena_nd_mixer& m, const void* H,
+                                   const float* D, void* y, void* ws, void* stream);
 
 // implicit.hip
 size_t implicit_scratch_bytes(const Plan& p, int32_t hidden);

@@ -332,8 +332,9 @@ class Plan:
         return y
 
     def nd_mixer(self, q, k, v, short_w, short_b, H, D, y=None):
-        """HyenaND mixer (ndims = 2, order 1): y = SiLU(sc(v)) . (K * z + D z),
-        z = sc(q) . SiLU(sc(k)); short_w float32 [3, d, 3, 3], short_b [3, d] or None."""
+        """HyenaND mixer (ndims = 2 or 3, order 1): y = SiLU(sc(v)) . (K * z + D z),
+        z = sc(q) . SiLU(sc(k)); short_w float32 [3, d, 3, 3] (2D) or [3, d, 3, 3, 3]
+        (3D), short_b [3, d] or None."""
         q, k, v = self._io(q, "q"), self._io(k, "k"), self._io(v, "v")
         for t in (short_w, D) + ((short_b,) if short_b is not None else ()):
             if t.dtype != self.torch.float32 or not t.is_contiguous():

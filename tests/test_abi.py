@@ -285,7 +285,7 @@ def test_nd_mixer_validation():
     _, p2 = hyena.hyena_plan_create(1, 64, 4, 2, [8, 8])
     assert hyena.hyena_nd_mixer_forward(p2, m, 16, 16, 16, 16) == hyena.HYENA_ERR_UNSUPPORTED
     hyena.hyena_plan_destroy(p2)
-    _, p4 = hyena.hyena_plan_create(1, 512, 4, 1, [8, 8, 8])
+    _, p4 = hyena.hyena_plan_create(1, 512, 4, 2, [8, 8, 8])
     assert hyena.hyena_nd_mixer_forward(p4, m, 16, 16, 16, 16) == hyena.HYENA_ERR_UNSUPPORTED
     hyena.hyena_plan_destroy(p4)
     _, p3 = hyena.hyena_plan_create(1, 64, 4, 1, [8, 8])

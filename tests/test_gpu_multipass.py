@@ -298,3 +298,37 @@ def test_rowcol3d_largest_sides(X, Y, Z, d):
     e = rel_err(y, oracle_ref(inp, method=oracle.FFT))
     say(f"[gpu] 3D {X}x{Y}x{Z} rel err {e:.3e}")
     assert e < TOL_F32
+
+
+@pytest.mark.parametrize("X,Y,Z,d,dtype,bias", [(8, 4, 16, 3, synth.F32, True),
+                                                (16, 16, 8, 4, synth.F32, False),
+                                                (32, 32, 32, 2, synth.F32, True),
+                                                (8, 8, 8, 5, synth.BF16, True)])
+def test_hyenand_mixer_3d(X, Y, Z, d, dtype, bias):
+    # 3x3x3 short convs + q . SiLU(k) fused into the first z pass, SiLU(v)
+    # into the last
+    import torch
+    from gpu_util import from_torch, to_torch
+    from long_convolution_sequence_rfft_amd import hyena
+    inp = synth.make_3d(B=2, X=X, Y=Y, Z=Z, d=d, order=1, sigma_range=(1.0, 8.0), dtype=dtype,
+                        seed=97)
+    rng = np.random.default_rng(98)
+    k = synth._store(rng.standard_normal((2, X, Y, Z, d)), dtype)
+    v = synth._store(rng.standard_normal((2, X, Y, Z, d)), dtype)
+    sw = rng.normal(size=(3, d, 3, 3, 3)).astype(np.float32) * 0.3
+    sb = rng.normal(size=(3, d)).astype(np.float32) * 0.1 if bias else None
+    io = hyena.HYENA_F32 if dtype == synth.F32 else hyena.HYENA_BF16
+    say(f"[gpu] mixer 3D {X}x{Y}x{Z} d={d} {dtype} bias={bias}")
+    plan = hyena.Plan(2, d, 1, (X, Y, Z), io_dtype=io)
+    H = plan.spectrum(to_torch(inp.h, dtype))
+    y = plan.nd_mixer(to_torch(inp.u, dtype), to_torch(k, dtype), to_torch(v, dtype),
+                      torch.from_numpy(sw).cuda(),
+                      torch.from_numpy(sb).cuda() if bias else None, H,
+                      torch.from_numpy(inp.D[0].copy()).cuda())
+    torch.cuda.synchronize()
+    q64, _, K64, D64 = inp.f64()
+    ref = oracle.hyena3d_block(q64, synth.stored_to_f64(k, dtype), synth.stored_to_f64(v, dtype),
+                               sw, sb, K64[0], D64[0], oracle.FFT)
+    e = rel_err(from_torch(y, dtype), ref)
+    say(f"[gpu] mixer 3D rel err {e:.3e}")
+    assert e < (TOL_F32 if dtype == synth.F32 else TOL_BF16)
