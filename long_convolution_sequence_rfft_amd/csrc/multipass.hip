@@ -78,6 +78,8 @@ hyena_status outer_go(int L, int mode, bool half_spec, const OuterArgs& a, int64
         if (mode == OUTER_IN) return mp_outer_launch<LL, IO, OUTER_IN, true>(a, nb, s);     \
         if (mode == OUTER_MID) return mp_outer_launch<LL, IO, OUTER_MID, true>(a, nb, s);   \
         if (mode == OUTER_OUT) return mp_outer_launch<LL, IO, OUTER_OUT, true>(a, nb, s);   \
+        if (mode == OUTER_IN3) return mp_outer_launch<LL, IO, OUTER_IN3, true>(a, nb, s);   \
+        if (mode == OUTER_OUT3) return mp_outer_launch<LL, IO, OUTER_OUT3, true>(a, nb, s); \
         if (half_spec) return mp_outer_launch<LL, IO, OUTER_SPEC, true>(a, nb, s);          \
         return mp_outer_launch<LL, IO, OUTER_SPEC, false>(a, nb, s);
         HY_MP_LENGTHS(HY_CASE, 0, 0)
@@ -406,7 +408,7 @@ hyena_status mp3_forward(const Plan& p, const void* u, const void* const* gates,
         oa.F = F1;
         oa.tw = tw;
         if (blk) oa.blk = *blk;
-        hyena_status st = outer(p, OUTER_IN, true, oa, col_blocks * go.ngroups, s);
+        hyena_status st = outer(p, blk ? OUTER_IN3 : OUTER_IN, true, oa, col_blocks * go.ngroups, s);
         if (st != HYENA_OK) return st;
         const MidArgs mf = mid_args(p, go, F1, F2, false, MID_FWD, tw);
         const MidArgs mi = mid_args(p, go, F1, F2, false, MID_INV, tw);
@@ -425,7 +427,8 @@ hyena_status mp3_forward(const Plan& p, const void* u, const void* const* gates,
             if (st != HYENA_OK) return st;
             oa.act = blk ? nullptr : gates[n];
             oa.out = y;
-            st = outer(p, n + 1 < p.order ? OUTER_MID : OUTER_OUT, true, oa, col_blocks * go.ngroups, s);
+            const int last = blk ? OUTER_OUT3 : OUTER_OUT;
+            st = outer(p, n + 1 < p.order ? OUTER_MID : last, true, oa, col_blocks * go.ngroups, s);
             if (st != HYENA_OK) return st;
         }
     }

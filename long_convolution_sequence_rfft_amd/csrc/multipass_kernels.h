@@ -6,7 +6,11 @@
 
 namespace hy {
 
-enum OuterMode { OUTER_IN = 0, OUTER_MID = 1, OUTER_OUT = 2, OUTER_SPEC = 3 };
+// OUTER_IN3 / OUTER_OUT3: OUTER_IN / OUTER_OUT with the HyenaND mixer's
+// 3x3x3 short convolutions of a 3D grid (kept apart so that the plain passes
+// compile without that code)
+enum OuterMode { OUTER_IN = 0, OUTER_MID = 1, OUTER_OUT = 2, OUTER_SPEC = 3, OUTER_IN3 = 4,
+                 OUTER_OUT3 = 5 };
 enum InnerMode { INNER_CHAIN = 0, INNER_SPEC = 1 };
 
 // Workgroup of kMpThreads threads, one length-L transform per
@@ -231,6 +235,8 @@ __global__ void __launch_bounds__(kMpThreads, 2) hyena_mp_outer(OuterArgs a)
     const int cb = blockIdx.x / g.ngroups;
     const int kp = f & (KP - 1);
     const int o = cb * C + (f >> g.kp_log2);  // this transform's outer column
+    constexpr bool IN = MODE == OUTER_IN || MODE == OUTER_IN3;
+    constexpr bool OUT = MODE == OUTER_OUT || MODE == OUTER_OUT3;
     const int n_outer = MODE == OUTER_SPEC ? g.Lb : g.Lb_live;
     const bool col_live = o < n_outer;
     float* re = sre + f * LW;
@@ -268,12 +274,12 @@ __global__ void __launch_bounds__(kMpThreads, 2) hyena_mp_outer(OuterArgs a)
     // tile elements per thread in tile_rows
     constexpr int GT = (LA / 2) * NF / kMpThreads;
     float2 v[S::PTS];
-    if constexpr (MODE == OUTER_IN) {
+    if constexpr (IN) {
         // all tile loads are issued before the first LDS store, so their
         // latencies overlap instead of adding up
         const IO* u = static_cast<const IO*>(a.act);
         float2 xin[GT];
-        if (a.blk.on && g.three_d) {
+        if constexpr (MODE == OUTER_IN3) {
             // the mixer on a 3D grid: rows o = x Y + y, samples s = z; q and
             // k are convolved one after the other so only one tap set is live
             int64_t bq0, pq0;
@@ -386,7 +392,7 @@ __global__ void __launch_bounds__(kMpThreads, 2) hyena_mp_outer(OuterArgs a)
         load_column<LA, +1>(v, Fcol, twstep, tau, col_live, g.four_step && o > 0);
         const IO* gate = static_cast<const IO*>(a.act);
         float2 gval[GT];
-        if (MODE == OUTER_OUT && a.blk.on && g.three_d) {
+        if constexpr (MODE == OUTER_OUT3) {
             // HyenaND outer gate SiLU(v) after the 3x3x3 short convolution
             int64_t bq0, pq0;
             bool l0;
@@ -441,7 +447,7 @@ __global__ void __launch_bounds__(kMpThreads, 2) hyena_mp_outer(OuterArgs a)
                 x = make_float2(x.x * re[i], x.y * im[i]);
             }
         __syncthreads();
-        if constexpr (MODE == OUTER_OUT) {
+        if constexpr (OUT) {
             regs_to_lds<LA, true>(v, re, im, tau);
             __syncthreads();
             IO* y = static_cast<IO*>(a.out);
@@ -880,7 +886,11 @@ hyena_status mp_mid_launch(const MidArgs& a, int64_t nblocks, hipStream_t s)
     EXT template hyena_status mp_outer_launch<L, IO, OUTER_SPEC, true>(const OuterArgs&,      \
                                                                        int64_t, hipStream_t); \
     EXT template hyena_status mp_outer_launch<L, IO, OUTER_SPEC, false>(const OuterArgs&,     \
-                                                                        int64_t, hipStream_t);
+                                                                        int64_t, hipStream_t); \
+    EXT template hyena_status mp_outer_launch<L, IO, OUTER_IN3, true>(const OuterArgs&,       \
+                                                                      int64_t, hipStream_t);  \
+    EXT template hyena_status mp_outer_launch<L, IO, OUTER_OUT3, true>(const OuterArgs&,      \
+                                                                       int64_t, hipStream_t);
 
 #define HY_MP_MID_INST(L, A_, EXT)                                                            \
     EXT template hyena_status mp_mid_launch<L, MID_FWD, true>(const MidArgs&, int64_t,        \
