@@ -1,6 +1,6 @@
 // api.hip -- the extern "C" entry points declared in include/hyena.h.
 // Validation happens here, before anything is enqueued; the launchers in
-// lds1d.hip, fourstep.hip and rowcol2d.hip only enqueue kernels.
+// lds1d.hip, multipass.hip and implicit.hip only enqueue kernels.
 #include <hip/hip_runtime.h>
 
 #include <new>

@@ -1,6 +1,7 @@
 // lds1d.hip -- launch side of the single-workgroup path (kernels in
-// lds1d_kernels.h, instantiated per storage type in lds1d_f32.hip and
-// lds1d_bf16.hip), the spectrum export and the twiddle-table writer.
+// lds1d_kernels.h, instantiated per storage type in lds1d_{f32,bf16,f16}.hip,
+// lds1d_real_*.hip and lds1d_circ_*.hip): the staging transposes, the
+// spectrum export and the twiddle-table writer.
 #include "dispatch.h"
 #include "lds1d_kernels.h"
 
@@ -228,10 +229,9 @@ TwOffsets lds1d_offsets(const Plan& p)
 }  // namespace
 
 // ---------------------------------------------------------------------------
-// Staging transposes between channels-last [B][N][d] and column-major
-// [B][cols][N] runs, for an element E that is either a channel pair
-// (PairRaw, cols = d/2: pair-major) or one channel (IO, cols = d:
-// channel-major).  Tile: kStageTT samples x one 128-byte line of elements.
+// Staging transposes between channels-last [B][N][d] and channel-major
+// [B][d][N] runs (cols = d), one element E per channel.  Tile: kStageTT
+// samples x one 128-byte line of channels.
 // Each thread first issues all of its loads, then writes LDS; after the
 // barrier it reads all of its LDS values, then stores, so the memory
 // latencies of one thread overlap.

@@ -1,9 +1,12 @@
 // lds1d_kernels.h -- single-workgroup FFT convolution chain for transforms of
-// length M <= 16384 (sequence length N <= 8192).
+// length M <= 16384 (sequence length N <= 8192), in two forms: one real
+// channel per half-length complex transform (N = M/2, and periodic plans;
+// hyena_lds1d_real_*), or a channel pair per full-length complex transform
+// (any other N; hyena_lds1d_forward / hyena_lds1d_spectrum).
 //
-// One workgroup owns one (batch row b, channel pair c, c+1); the two real
-// channels ride in one complex signal, and the whole order-N chain stays in
-// registers and LDS:
+// Channel-pair form: one workgroup owns one (batch row b, channel pair c,
+// c+1); the two real channels ride in one complex signal, and the whole
+// order-N chain stays in registers and LDS:
 //   load u (first N samples; the zero-padded half is never loaded)
 //   for n = 1..order:
 //     forward transform  (R0 pass with half-zero input, R1 pass, RL pass)

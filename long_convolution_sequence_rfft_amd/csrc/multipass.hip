@@ -1,6 +1,6 @@
 // multipass.hip -- launch side of the four-step (1D, transforms longer than
-// 16384 points, or forced) and row-column (2D) paths: chunk loop over channel
-// pairs, per-length dispatch, and the spectrum export.
+// 16384 points, or forced) and row-column (2D and 3D) paths: chunk loop over
+// channel pairs, per-length dispatch, and the spectrum export.
 #include "multipass_kernels.h"
 
 namespace hy {

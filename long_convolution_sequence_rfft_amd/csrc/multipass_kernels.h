@@ -1,5 +1,6 @@
-// multipass_kernels.h -- the outer and inner passes of the four-step (1D) and
-// row-column (2D) paths; see multipass.h for the structure.
+// multipass_kernels.h -- the outer, inner and (3D) middle passes of the
+// four-step (1D) and row-column (2D, 3D) paths; see multipass.h for the
+// structure.
 #pragma once
 
 #include "multipass.h"

@@ -1,6 +1,7 @@
 // stockham.h -- one length-L complex transform held by a group of threads,
 // radix passes in registers, exchanges through LDS (Stockham autosort: no
-// bit-reversal pass), plus the channel-pair spectral product.
+// bit-reversal pass), plus the spectral products of the channel-pair and the
+// single-channel (packed real) forms.
 //
 // A radix-R pass with sub-transform length NS reads butterfly j's inputs at
 // j + r L/R, multiplies input r by W_{NS R}^{r k} (k = j mod NS), takes a
