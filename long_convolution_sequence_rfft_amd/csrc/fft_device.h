@@ -160,10 +160,8 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b)
 }
 __device__ __forceinline__ uint16_t f32_to_bf16(float f)
 {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu)) return (uint16_t)((u >> 16) | 0x40);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
+    // the hardware conversion: round to nearest even, NaN stays a (quiet) NaN
+    return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
 // XCD-aware block order: the dispatcher hands consecutive workgroup ids to

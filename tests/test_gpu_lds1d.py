@@ -285,3 +285,26 @@ def test_forward_in_a_hip_graph(shape):
         g.replay()
         torch.cuda.synchronize()
         assert np.array_equal(from_torch(y, dtype), y_eager), f"replay {r}"
+
+
+@pytest.mark.parametrize("kind,dims", [("1d", (2048,)), ("1d", (1000,)), ("1d", (20000,)),
+                                       ("2d", (16, 32))])
+def test_bf16_spectrum_is_rounded_to_nearest_even(kind, dims):
+    # the same filter transformed into a float32 and a bfloat16 spectrum: every
+    # bfloat16 word is the round-to-nearest-even of the float32 word at the
+    # same place (the two layouts differ only in the element type)
+    import torch
+    from long_convolution_sequence_rfft_amd import hyena
+    if kind == "1d":
+        inp = synth.make_1d(B=1, N=dims[0], d=6, order=2, alpha_range=(1e-4, 1e-2),
+                            dtype=synth.BF16, seed=73)
+    else:
+        inp = synth.make_2d(B=1, X=dims[0], Y=dims[1], d=6, order=2, sigma_range=(1.0, 8.0),
+                            dtype=synth.BF16, seed=74)
+    h = to_torch(inp.h, synth.BF16)
+    p32 = hyena.Plan(1, 6, 2, dims, io_dtype=hyena.HYENA_BF16, spectrum_dtype=hyena.HYENA_F32)
+    p16 = hyena.Plan(1, 6, 2, dims, io_dtype=hyena.HYENA_BF16, spectrum_dtype=hyena.HYENA_BF16)
+    H32 = p32.spectrum(h).cpu().numpy().view(np.float32)
+    H16 = p16.spectrum(h).cpu().numpy().view(np.uint16)
+    assert H32.size == H16.size
+    assert np.array_equal(synth.f32_to_bf16_bits(H32), H16)
