@@ -100,7 +100,7 @@ typedef enum hyena_path {
 
 /*
  * Create a plan.  B >= 1 batch rows, d >= 1 channels, 1 <= order <= 8.
- * ndims = 1: dims = {N}, 4 <= N <= 524288 (any N; M is the power of two
+ * ndims = 1: dims = {N}, 4 <= N <= 2097152 (any N; M is the power of two
  *            >= 2N; N == the N argument).  M <= 16384 runs in one workgroup
  *            per channel (pair); longer transforms take the four-step path.
  * ndims = 2: dims = {X, Y}, X and Y powers of two in [4, 512]; N must equal

@@ -8,8 +8,8 @@ namespace hy {
 HY_MP_LENGTHS(HY_MP_OUTER_INST, float, extern)
 HY_MP_LENGTHS(HY_MP_OUTER_INST, uint16_t, extern)
 HY_MP_LENGTHS(HY_MP_OUTER_INST, _Float16, extern)
-HY_MP_LENGTHS(HY_MP_INNER_INST, float, extern)
-HY_MP_LENGTHS(HY_MP_INNER_INST, uint16_t, extern)
+HY_MP_INNER_LENGTHS(HY_MP_INNER_INST, float, extern)
+HY_MP_INNER_LENGTHS(HY_MP_INNER_INST, uint16_t, extern)
 HY_MP_LENGTHS(HY_MP_MID_INST, 0, extern)
 
 namespace {
@@ -97,7 +97,7 @@ hyena_status inner_go(int L, int mode, bool half_b, const InnerArgs& a, int64_t 
         if (mode == INNER_SPEC) return mp_inner_launch<LL, SP, INNER_SPEC, false>(a, nb, s);  \
         if (half_b) return mp_inner_launch<LL, SP, INNER_CHAIN, true>(a, nb, s);              \
         return mp_inner_launch<LL, SP, INNER_CHAIN, false>(a, nb, s);
-        HY_MP_LENGTHS(HY_CASE, 0, 0)
+        HY_MP_INNER_LENGTHS(HY_CASE, 0, 0)
 #undef HY_CASE
         default: return fail(HYENA_ERR_UNSUPPORTED, "multi-pass: unsupported inner length");
     }

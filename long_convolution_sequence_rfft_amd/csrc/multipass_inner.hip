@@ -3,6 +3,6 @@
 #include "multipass_kernels.h"
 
 namespace hy {
-HY_MP_LENGTHS(HY_MP_INNER_INST, float, )
-HY_MP_LENGTHS(HY_MP_INNER_INST, uint16_t, )
+HY_MP_INNER_LENGTHS(HY_MP_INNER_INST, float, )
+HY_MP_INNER_LENGTHS(HY_MP_INNER_INST, uint16_t, )
 }  // namespace hy

@@ -876,6 +876,9 @@ hyena_status mp_mid_launch(const MidArgs& a, int64_t nblocks, hipStream_t s)
 
 #define HY_MP_LENGTHS(X, A, B) X(8, A, B) X(16, A, B) X(32, A, B) X(64, A, B) X(128, A, B) \
     X(256, A, B) X(512, A, B) X(1024, A, B)
+// inner (F-facing) passes also come in 2048 and 4096 points: four-step
+// transforms up to 1024 x 4096
+#define HY_MP_INNER_LENGTHS(X, A, B) HY_MP_LENGTHS(X, A, B) X(2048, A, B) X(4096, A, B)
 
 #define HY_MP_OUTER_INST(L, IO, EXT)                                                          \
     EXT template hyena_status mp_outer_launch<L, IO, OUTER_IN, true>(const OuterArgs&,        \

@@ -52,10 +52,11 @@ const char* last_error_text() { return g_last_error.c_str(); }
 static void fourstep_split(int64_t M, int64_t& M1, int64_t& M2)
 {
     // columns carry the zero-padded half, rows are kept short enough for one
-    // workgroup to hold a mirrored pair of them in LDS; both at most 1024
+    // workgroup to hold a mirrored pair of them in LDS; columns at most 1024
+    // (they move the activations), rows at most 4096
     M1 = 512;
     while (M1 > 32 && M / M1 < 32) M1 >>= 1;
-    if (M / M1 > 1024) M1 = M / 1024;
+    if (M / M1 > 1024) M1 = M / 1024 < 1024 ? M / 1024 : 1024;
     M2 = M / M1;
 }
 
@@ -99,7 +100,7 @@ hyena_status plan_build(Plan& p, int64_t B, int64_t N, int64_t d, int32_t order,
     if (ndims == 1) {
         if (dims[0] != N) return fail(HYENA_ERR_INVALID_ARGUMENT, "dims[0] must equal N");
         if (N < 4 || N > kFourStepMaxM / 2)
-            return fail(HYENA_ERR_UNSUPPORTED, "1D sequence length must be in 4..524288");
+            return fail(HYENA_ERR_UNSUPPORTED, "1D sequence length must be in 4..2097152");
         p.M = next_pow2(2 * N);
         if (p.circular) {
             // periodic boundary: the transform is the sequence itself, on the

@@ -19,7 +19,7 @@ namespace hy {
 constexpr int kMaxOrder = 8;
 constexpr int kMaxTwSegments = 12;
 constexpr int64_t kLdsMaxM = 16384;       // largest transform held in one workgroup's LDS
-constexpr int64_t kFourStepMaxM = 1 << 20;  // largest 1D transform (N = 524288): 1024 x 1024
+constexpr int64_t kFourStepMaxM = 1 << 22;  // largest 1D transform (N = 2097152): 1024 x 4096
 
 // Radix plan of the single-workgroup transform of length M (8 <= M <= 16384):
 // 32 complex values per thread (M >= 64), forward passes R0, R1, RL with

@@ -38,7 +38,7 @@ def test_status_strings():
     (dict(B=1, N=8, d=2, order=9, dims=[8]), hyena.HYENA_ERR_UNSUPPORTED),
     (dict(B=1, N=8, d=2, order=1, dims=[4]), hyena.HYENA_ERR_INVALID_ARGUMENT),
     (dict(B=1, N=2, d=2, order=1, dims=[2]), hyena.HYENA_ERR_UNSUPPORTED),
-    (dict(B=1, N=524289, d=2, order=1, dims=[524289]), hyena.HYENA_ERR_UNSUPPORTED),
+    (dict(B=1, N=2097153, d=2, order=1, dims=[2097153]), hyena.HYENA_ERR_UNSUPPORTED),
     (dict(B=1, N=64, d=2, order=1, dims=[8, 8], path=hyena.HYENA_PATH_LDS1D),
      hyena.HYENA_ERR_UNSUPPORTED),
     (dict(B=1, N=60, d=2, order=1, dims=[6, 10]), hyena.HYENA_ERR_UNSUPPORTED),
@@ -86,7 +86,8 @@ def test_plan_create_null_output_pointer():
 @pytest.mark.parametrize("N,path,M", [(4, 1, 8), (256, 1, 512), (2048, 1, 4096),
                                       (5000, 1, 16384), (8192, 1, 16384), (65536, 2, 131072),
                                       (16385, 2, 65536), (65537, 2, 262144),
-                                      (524288, 2, 1 << 20)])
+                                      (524288, 2, 1 << 20), (1000000, 2, 1 << 21),
+                                      (2097152, 2, 1 << 22)])
 def test_path_choice_and_sizes(N, path, M):
     _, plan = hyena.hyena_plan_create(2, N, 6, 2, [N])
     spec, ws, p = hyena.hyena_plan_query(plan)

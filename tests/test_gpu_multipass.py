@@ -144,9 +144,10 @@ def test_full_size_2d_sampled():
     assert e < TOL_F32
 
 
-@pytest.mark.parametrize("N,d", [(100000, 2), (262144, 1), (524288, 1)])
+@pytest.mark.parametrize("N,d", [(100000, 2), (262144, 1), (524288, 1), (1000000, 1),
+                                 (2097152, 1)])
 def test_fourstep_longer_than_64k(N, d):
-    # transforms of 2^18..2^20 points (outer and inner lengths up to 1024)
+    # transforms of 2^18..2^22 points (columns up to 1024, rows up to 4096)
     inp = synth.make_1d(B=1, N=N, d=d, order=2, alpha_range=(1e-6, 1e-4), seed=31)
     y, _, _ = run_gpu(inp)
     e = rel_err(y, oracle_ref(inp, method=oracle.FFT))
