@@ -333,3 +333,20 @@ def test_hyenand_mixer_3d(X, Y, Z, d, dtype, bias):
     e = rel_err(from_torch(y, dtype), ref)
     say(f"[gpu] mixer 3D rel err {e:.3e}")
     assert e < (TOL_F32 if dtype == synth.F32 else TOL_BF16)
+
+
+@pytest.mark.parametrize("kind", ["fourstep", "2d", "3d"])
+def test_multipass_order_8(kind):
+    # the longest chain: seven middle passes between the first and the last
+    if kind == "fourstep":
+        inp = synth.make_1d(B=1, N=4096, d=3, order=8, alpha_range=(1e-3, 1e-2), seed=17)
+        y, _, _ = run_gpu(inp, path=FOUR)
+    elif kind == "2d":
+        inp = synth.make_2d(B=1, X=16, Y=8, d=3, order=8, sigma_range=(1.0, 4.0), seed=18)
+        y, _, _ = run_gpu(inp)
+    else:
+        inp = synth.make_3d(B=1, X=8, Y=4, Z=8, d=3, order=8, sigma_range=(1.0, 4.0), seed=19)
+        y, _, _ = run_gpu(inp)
+    e = rel_err(y, oracle_ref(inp, method=oracle.FFT))
+    say(f"[gpu] order 8 {kind} rel err {e:.3e}")
+    assert e < TOL_F32
