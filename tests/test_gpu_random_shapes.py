@@ -1,0 +1,65 @@
+"""A seeded sweep of small random shapes across every path, storage type and
+boundary, each checked element by element against the float64 oracle (the
+same bounds as the targeted tests: 1e-5 float32, 1e-2 bfloat16, 5e-3
+binary16)."""
+import numpy as np
+import pytest
+
+import oracle
+from long_convolution_sequence_rfft_amd import synth
+from gpu_util import oracle_ref, rel_err, run_gpu, say
+
+pytestmark = pytest.mark.gpu
+
+TOL = {synth.F32: 1e-5, synth.BF16: 1e-2, synth.F16: 5e-3}
+
+
+def _cases(n=36, seed=2024):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        kind = ["1d", "1d", "1d", "circ", "2d", "3d"][i % 6]
+        dtype = [synth.F32, synth.BF16, synth.F16][int(rng.integers(3))]
+        order = int(rng.integers(1, 4))
+        B = int(rng.integers(1, 3))
+        d = int(rng.integers(1, 12))
+        if kind == "1d":
+            dims = (int(rng.integers(4, 20000)),)
+        elif kind == "circ":
+            dims = (int(2 ** rng.integers(4, 13)),)
+        elif kind == "2d":
+            dims = tuple(int(2 ** rng.integers(2, 6)) for _ in range(2))
+        else:
+            dims = tuple(int(2 ** rng.integers(2, 5)) for _ in range(3))
+        out.append((i, kind, dims, dtype, order, B, d))
+    return out
+
+
+@pytest.mark.parametrize("case", _cases(), ids=lambda c: f"{c[0]}-{c[1]}-{'x'.join(map(str, c[2]))}-{c[3]}")
+def test_random_shape(case):
+    from long_convolution_sequence_rfft_amd import hyena
+    i, kind, dims, dtype, order, B, d = case
+    seed = 1000 + i
+    if kind in ("1d", "circ"):
+        inp = synth.make_1d(B=B, N=dims[0], d=d, order=order, alpha_range=(1e-3, 3e-2),
+                            dtype=dtype, seed=seed)
+    elif kind == "2d":
+        inp = synth.make_2d(B=B, X=dims[0], Y=dims[1], d=d, order=order, sigma_range=(1.0, 8.0),
+                            dtype=dtype, seed=seed)
+    else:
+        inp = synth.make_3d(B=B, X=dims[0], Y=dims[1], Z=dims[2], d=d, order=order,
+                            sigma_range=(1.0, 8.0), dtype=dtype, seed=seed)
+    say(f"[gpu] random case {i}: {kind} dims={dims} {dtype} order={order} B={B} d={d}")
+    if kind == "circ":
+        io = {synth.F32: hyena.HYENA_F32, synth.BF16: hyena.HYENA_BF16,
+              synth.F16: hyena.HYENA_F16}[dtype]
+        plan = hyena.Plan(B, d, order, dims, io_dtype=io, circular=True)
+        y, _, _ = run_gpu(inp, plan=plan)
+        u, g, h, D = inp.f64()
+        ref = oracle.hyena1d_circular(u, g, h, D, oracle.FFT)
+    else:
+        y, _, _ = run_gpu(inp)
+        ref = oracle_ref(inp, method=oracle.FFT)
+    e = rel_err(y, ref)
+    say(f"[gpu] random case {i}: rel err {e:.3e}")
+    assert e < TOL[dtype]
