@@ -98,7 +98,8 @@ __global__ void hyena_lds1d_export(const SP* spec, float2* out, int64_t npairs, 
 }
 
 // Single-channel layout: entry (S, Dl) of bin k gives H[k] = L (S + Dl) and
-// H[L-k] = L conj(S - Dl); entry (0, 0) gives H[0], H[L] and H[L/2].
+// H[L-k] = L conj(S - Dl); entry (tau 0, slot RL/2) gives H[0], H[L] and
+// H[L/2].
 template <typename SP>
 __global__ void hyena_lds1d_real_export(const SP* spec, float2* out, int64_t L, int64_t T,
                                         int64_t total)
@@ -113,7 +114,7 @@ __global__ void hyena_lds1d_real_export(const SP* spec, float2* out, int64_t L, 
     load_entry(spec, i, S, Dl);
     const float sc = (float)L;
     float2* o = out + nc * (L + 1);
-    if (tau == 0 && e == 0) {
+    if (tau == 0 && e == L / (4 * T)) {
         o[0] = make_float2((S.x + Dl.x) * sc, 0.0f);
         o[L] = make_float2((S.x - Dl.x) * sc, 0.0f);
         o[L / 2] = make_float2(S.y * sc, Dl.y * sc);

@@ -193,7 +193,6 @@ __global__ void __launch_bounds__(FftShape<L>::T, 2) hyena_lds1d_real_forward(Ld
     constexpr int T = S::T, PTS = S::PTS, R0 = S::R0, LW = S::LW;
     constexpr int RIN = CIRC ? R0 : R0 / 2;  // live R0-pass samples per butterfly
     __shared__ float smem[2 * LW];
-    __shared__ float sxs[4 * S::RL];
     float* re = smem;
     float* im = smem + LW;
 
@@ -223,7 +222,7 @@ __global__ void __launch_bounds__(FftShape<L>::T, 2) hyena_lds1d_real_forward(Ld
         typename EntryRaw<SP>::type ent[S::RL];
         fwd_transform<L, !CIRC>(v, re, im, a.tw, a.tw_off, tau, j1, j2, n > 0,
                          [&] { load_entries<L, SP>(ent, spec, tau); });
-        real_product<L, SP>(v, ent, tau, a.D[(int64_t)n * a.d + c] * invL, wbase, sxs);
+        real_product<L, SP>(v, ent, tau, a.D[(int64_t)n * a.d + c] * invL, wbase);
 
         const IO* g = static_cast<const IO*>(a.gates[n]) + row;
         typename PairRaw<IO>::type graw[S::Q0][RIN];

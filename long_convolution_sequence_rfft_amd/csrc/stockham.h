@@ -605,66 +605,65 @@ __device__ __forceinline__ void bin_cs(float2 wbase, int e, float& c, float& s)
 }
 
 // Single-channel product on the last-pass registers of one length-L
-// transform (same register layout and thread-0 handling as spectral_product).
-//   tau > 0: entry e is bin k = tau + e L/RL (output e of butterfly tau) with
-//            its mirror L - k (output RL-1-e of butterfly 2T - tau).
-//   tau = 0: entry 0 packs the self-mirrored bins 0 and L/2 as
-//            ((S0, Re H[L/2]), (Dl0, Im H[L/2])); entries 1..RL/2-1 are bins
-//            e L/RL of butterfly 0, entries RL/2.. bins T + (e - RL/2) L/RL of
-//            butterfly T.
+// transform.  Thread tau holds butterflies tau and 2T - tau (0 and T for
+// tau = 0); slot e = 0..RL-1 is one bin k and its mirror L - k:
+//   tau > 0: k = tau + e L/RL (output e of butterfly tau), mirror output
+//            RL-1-e of butterfly 2T - tau.
+//   tau = 0: butterflies 0 and T are their own mirrors.  Slots e < RL/2:
+//            k = T + e L/RL, outputs (e, RL-1-e) of butterfly T; slots
+//            e > RL/2: k = e L/RL, outputs (e, RL-e) of butterfly 0; slot
+//            RL/2 packs the self-mirrored bins 0 and L/2 as
+//            ((S0, Re H[L/2]), (Dl0, Im H[L/2])).
+// Every lane runs the same instruction stream: thread 0's operands, twiddles
+// and results differ from the others' only through selects, so the wave that
+// holds thread 0 does no extra pass of its own.
 // wbase = W^tau (tau > 0) or W^T (tau = 0); dp = D/L (folded feedthrough).
 template <int L, typename SP>
 __device__ __forceinline__ void real_product(float2* v, const typename EntryRaw<SP>::type* ent,
-                                             int tau, float dp, float2 wbase, float* xs)
+                                             int tau, float dp, float2 wbase)
 {
     using S = FftShape<L>;
-    constexpr int RL = S::RL;
-    float2 Sv, Dv;
-    float c, s;
-    if (tau == 0) {
-        widen_entry<SP>(ent[0], Sv, Dv);
-        const float S0 = Sv.x + dp, Hr = Sv.y + dp, D0 = Dv.x, Hi = Dv.y;
-        const float2 z0 = v[0], zh = v[RL / 2];
-        xs[0] = fmaf(S0, z0.x, D0 * z0.y);
-        xs[1] = fmaf(S0, z0.y, D0 * z0.x);
-        xs[RL] = fmaf(Hr, zh.x, Hi * zh.y);
-        xs[RL + 1] = fmaf(Hr, zh.y, -Hi * zh.x);
-#pragma unroll
-        for (int e = 1; e < RL / 2; ++e) {
-            widen_entry<SP>(ent[e], Sv, Dv);
-            Sv.x += dp;
-            const float2 r = out_step_root<RL>(e);
-            float2 a = v[e], b = v[RL - e];
-            real_pair_product(a, b, Sv, Dv, r.x, -r.y);
-            xs[2 * e] = a.x;
-            xs[2 * e + 1] = a.y;
-            xs[2 * (RL - e)] = b.x;
-            xs[2 * (RL - e) + 1] = b.y;
-        }
-#pragma unroll
-        for (int e = RL / 2; e < RL; ++e) {
-            const int s2 = e - RL / 2;
-            widen_entry<SP>(ent[e], Sv, Dv);
-            Sv.x += dp;
-            bin_cs<RL>(wbase, s2, c, s);
-            float2 a = v[RL + s2], b = v[2 * RL - 1 - s2];
-            real_pair_product(a, b, Sv, Dv, c, s);
-            xs[2 * (RL + s2)] = a.x;
-            xs[2 * (RL + s2) + 1] = a.y;
-            xs[2 * (2 * RL - 1 - s2)] = b.x;
-            xs[2 * (2 * RL - 1 - s2) + 1] = b.y;
-        }
-    }
+    constexpr int RL = S::RL, H = RL / 2;
+    const bool t0 = tau == 0;
+    float2 ya[RL], yb[RL];
 #pragma unroll
     for (int e = 0; e < RL; ++e) {
+        float2 Sv, Dv;
         widen_entry<SP>(ent[e], Sv, Dv);
         Sv.x += dp;
+        float c, s;
         bin_cs<RL>(wbase, e, c, s);
-        real_pair_product(v[e], v[2 * RL - 1 - e], Sv, Dv, c, s);
+        float2 a = v[e], b = v[2 * RL - 1 - e];
+        if (e < H) {
+            a = t0 ? v[RL + e] : a;
+        } else if (e > H) {
+            const float2 r = out_step_root<RL>(e);
+            b = t0 ? v[RL - e] : b;
+            c = t0 ? r.x : c;
+            s = t0 ? -r.y : s;
+        }
+        float2 z0h, z00;
+        if (e == H) {
+            // thread 0: bin L/2 (zh = v[H]) and bin 0 (z0 = v[0])
+            const float2 zh = v[H], z0 = v[0];
+            const float Hr = Sv.y + dp, Hi = Dv.y;
+            z0h = make_float2(fmaf(Hr, zh.x, Hi * zh.y), fmaf(Hr, zh.y, -Hi * zh.x));
+            z00 = make_float2(fmaf(Sv.x, z0.x, Dv.x * z0.y), fmaf(Sv.x, z0.y, Dv.x * z0.x));
+        }
+        real_pair_product(a, b, Sv, Dv, c, s);
+        if (e == H) {
+            a = t0 ? z0h : a;
+            b = t0 ? z00 : b;
+        }
+        ya[e] = a;
+        yb[e] = b;
     }
-    if (tau == 0) {
 #pragma unroll
-        for (int i = 0; i < 2 * RL; ++i) v[i] = make_float2(xs[2 * i], xs[2 * i + 1]);
+    for (int e = 0; e < H; ++e) {
+        v[e] = t0 ? (e == 0 ? yb[H] : yb[RL - e]) : ya[e];
+        v[RL + e] = t0 ? ya[e] : yb[RL - 1 - e];
+        v[H + e] = ya[H + e];
+        v[2 * RL - 1 - e] = yb[e];
     }
 }
 
@@ -685,32 +684,33 @@ __device__ __forceinline__ void store_real_entries(const float2* v, SP* spec, in
             store_entry(spec, e * T + tau, Sv, Dv);
         }
     } else {
-        // bins 0 and L/2: S0 = Re Z[0], Dl0 = Im Z[0], H[L/2] = conj Z[L/2]
-        const float2 z0 = v[0], zh = v[RL / 2];
-        store_entry(spec, 0, make_float2(z0.x * scale, zh.x * scale),
-                    make_float2(z0.y * scale, -zh.y * scale));
+        // thread 0 in the product's slot order
+        constexpr int H = RL / 2;
 #pragma unroll
-        for (int e = 1; e < RL / 2; ++e) {
-            const float2 r = out_step_root<RL>(e);
-            entry_from_real(v[e], v[RL - e], r.x, -r.y, scale, Sv, Dv);
+        for (int e = 0; e < H; ++e) {
+            bin_cs<RL>(wbase, e, c, s);
+            entry_from_real(v[RL + e], v[2 * RL - 1 - e], c, s, scale, Sv, Dv);
             store_entry(spec, e * T, Sv, Dv);
         }
+        // bins 0 and L/2: S0 = Re Z[0], Dl0 = Im Z[0], H[L/2] = conj Z[L/2]
+        const float2 z0 = v[0], zh = v[H];
+        store_entry(spec, H * T, make_float2(z0.x * scale, zh.x * scale),
+                    make_float2(z0.y * scale, -zh.y * scale));
 #pragma unroll
-        for (int e = RL / 2; e < RL; ++e) {
-            const int s2 = e - RL / 2;
-            bin_cs<RL>(wbase, s2, c, s);
-            entry_from_real(v[RL + s2], v[2 * RL - 1 - s2], c, s, scale, Sv, Dv);
+        for (int e = H + 1; e < RL; ++e) {
+            const float2 r = out_step_root<RL>(e);
+            entry_from_real(v[e], v[RL - e], r.x, -r.y, scale, Sv, Dv);
             store_entry(spec, e * T, Sv, Dv);
         }
     }
 }
 
-// Bin k of single-channel entry (tau, e); its mirror is L - k.  Entry (0, 0)
-// holds bins 0 and L/2.
+// Bin k of single-channel entry (tau, e); its mirror is L - k.  Entry
+// (0, RL/2) holds bins 0 and L/2 instead.
 __host__ __device__ inline int64_t real_entry_bin(int64_t L, int64_t T, int64_t tau, int64_t e)
 {
     const int64_t RL = L / (2 * T);
-    if (tau == 0) return e < RL / 2 ? e * 2 * T : T + (e - RL / 2) * 2 * T;
+    if (tau == 0) return e < RL / 2 ? T + e * 2 * T : e * 2 * T;
     return tau + e * 2 * T;
 }
 
