@@ -83,7 +83,7 @@ __global__ void hyena_lds1d_export(const SP* spec, float2* out, int64_t npairs, 
     float2* oa = out + (n * d + c0) * (half + 1);
     float2* ob = oa + (half + 1);
     const bool has_b = c0 + 1 < d;
-    if (tau == 0 && e == 0) {
+    if (tau == 0 && e == M / (4 * T)) {
         oa[0] = make_float2((P.x + Q.x) * sc, 0.0f);
         oa[half] = make_float2((P.y + Q.y) * sc, 0.0f);
         if (has_b) {

@@ -67,7 +67,6 @@ __global__ void __launch_bounds__(FftShape<M>::T, 2) hyena_lds1d_forward(Lds1dFw
     // [re block | im block]: real and imaginary parts of an element are LW
     // words apart and share one base address
     __shared__ float smem[2 * LW];
-    __shared__ float sxs[4 * S::RL];
 
     const int tau = threadIdx.x;
     const int64_t lin = xcd_remap(blockIdx.x, a.nblocks);
@@ -106,7 +105,7 @@ __global__ void __launch_bounds__(FftShape<M>::T, 2) hyena_lds1d_forward(Lds1dFw
 
         const float Da = a.D[(int64_t)n * a.d + c0];
         const float Db = has_b ? a.D[(int64_t)n * a.d + c0 + 1] : 0.0f;
-        spectral_product<M, SP>(v, ent, tau, (Da + Db) * inv2M, (Da - Db) * inv2M, sxs);
+        spectral_product<M, SP>(v, ent, tau, (Da + Db) * inv2M, (Da - Db) * inv2M);
 
         const IO* g = static_cast<const IO*>(a.gates[n]) + row0;
         float2 gv[S::Q0][R0 / 2];

@@ -445,70 +445,58 @@ __device__ __forceinline__ void load_entries(typename EntryRaw<SP>::type* ent, c
 }
 
 // Mirror-paired product on the last-pass registers of one length-L transform.
-//   tau > 0: last-pass butterflies tau and 2T - tau; entry e pairs output e of
+//   tau > 0: last-pass butterflies tau and 2T - tau; slot e pairs output e of
 //            the first with output RL-1-e of the second; the bin <= L/2 is
 //            the first's for e < RL/2, the second's otherwise.
-//   tau = 0: butterflies 0 and T; entry 0 packs the self-mirrored bins 0 and
-//            L/2 (real P, Q), entries 1..RL/2-1 pair outputs (e, RL-e) of
-//            butterfly 0, entries RL/2.. pair outputs (s, RL-1-s) of butterfly T.
+//   tau = 0: butterflies 0 and T are their own mirrors.  Slots e < RL/2 pair
+//            outputs (e, RL-1-e) of butterfly T, slots e > RL/2 outputs
+//            (RL-e, e) of butterfly 0, and slot RL/2 packs the self-mirrored
+//            bins 0 and L/2 (real P, Q).
 // dp, dq: real offsets added to every P and Q (the folded feedthrough).
-// Thread 0's pairing differs from everyone else's.  It only reads v inside
-// its branch and parks its results in a 4*RL-float LDS scratch `xs`; every
-// lane then runs the common pairing, and thread 0 finally overwrites all of
-// its registers from the scratch.  (A branch that rewrote v in a different
-// pattern would make the register array fall back to private memory.)
+// Every lane runs the same instruction stream; thread 0's operands and
+// results differ only through selects.
 template <int L, typename SP>
 __device__ __forceinline__ void spectral_product(float2* v, const typename EntryRaw<SP>::type* ent,
-                                                 int tau, float dp, float dq, float* xs)
+                                                 int tau, float dp, float dq)
 {
     using S = FftShape<L>;
-    constexpr int RL = S::RL;
-    float2 P, Q;
-    if (tau == 0) {
-        widen_entry<SP>(ent[0], P, Q);
-        const float2 y0 = self_product(v[0], P.x + dp, Q.x + dq);
-        const float2 yh = self_product(v[RL / 2], P.y + dp, Q.y + dq);
-        xs[0] = y0.x;
-        xs[1] = y0.y;
-        xs[RL] = yh.x;
-        xs[RL + 1] = yh.y;
-#pragma unroll
-        for (int e = 1; e < RL / 2; ++e) {
-            widen_entry<SP>(ent[e], P, Q);
-            P.x += dp;
-            Q.x += dq;
-            float2 a = v[e], b = v[RL - e];
-            pair_product(a, b, P, Q);
-            xs[2 * e] = a.x;
-            xs[2 * e + 1] = a.y;
-            xs[2 * (RL - e)] = b.x;
-            xs[2 * (RL - e) + 1] = b.y;
-        }
-#pragma unroll
-        for (int e = RL / 2; e < RL; ++e) {
-            const int s2 = e - RL / 2;
-            widen_entry<SP>(ent[e], P, Q);
-            P.x += dp;
-            Q.x += dq;
-            float2 a = v[RL + s2], b = v[2 * RL - 1 - s2];
-            pair_product(a, b, P, Q);
-            xs[2 * (RL + s2)] = a.x;
-            xs[2 * (RL + s2) + 1] = a.y;
-            xs[2 * (2 * RL - 1 - s2)] = b.x;
-            xs[2 * (2 * RL - 1 - s2) + 1] = b.y;
-        }
-    }
+    constexpr int RL = S::RL, H = RL / 2;
+    const bool t0 = tau == 0;
+    float2 yp[RL], ym[RL];
 #pragma unroll
     for (int e = 0; e < RL; ++e) {
+        float2 P, Q;
         widen_entry<SP>(ent[e], P, Q);
+        float2 y0, yh;
+        if (e == H) {
+            // thread 0: the self-mirrored bins 0 (v[0]) and L/2 (v[H])
+            y0 = self_product(v[0], P.x + dp, Q.x + dq);
+            yh = self_product(v[H], P.y + dp, Q.y + dq);
+        }
         P.x += dp;
         Q.x += dq;
-        if (e < RL / 2) pair_product(v[e], v[2 * RL - 1 - e], P, Q);
-        else pair_product(v[2 * RL - 1 - e], v[e], P, Q);
+        const int ip = e < H ? e : 2 * RL - 1 - e;  // the bin <= L/2
+        const int im = e < H ? 2 * RL - 1 - e : e;
+        float2 p = v[ip];
+        if (e < H) p = t0 ? v[RL + e] : p;
+        if (e > H) p = t0 ? v[RL - e] : p;
+        float2 m = v[im];
+        pair_product(p, m, P, Q);
+        if (e == H) {
+            p = t0 ? y0 : p;
+            m = t0 ? yh : m;
+        }
+        yp[e] = p;
+        ym[e] = m;
     }
-    if (tau == 0) {
+    // general: v[ip(e)] = yp[e], v[im(e)] = ym[e]; thread 0 writes butterfly
+    // 0's low half and butterfly T's low half from its own slots
 #pragma unroll
-        for (int i = 0; i < 2 * RL; ++i) v[i] = make_float2(xs[2 * i], xs[2 * i + 1]);
+    for (int e = 0; e < H; ++e) {
+        v[e] = t0 ? (e == 0 ? yp[H] : yp[RL - e]) : yp[e];
+        v[RL + e] = t0 ? yp[e] : yp[RL - 1 - e];
+        v[H + e] = ym[H + e];
+        v[2 * RL - 1 - e] = ym[e];
     }
 }
 
@@ -528,18 +516,19 @@ __device__ __forceinline__ void store_spectrum_entries(const float2* v, SP* spec
             store_entry(spec, e * T + tau, P, Q);
         }
     } else {
-        const float2 z0 = v[0], zh = v[RL / 2];
-        store_entry(spec, 0, make_float2((z0.x + z0.y) * scale, (zh.x + zh.y) * scale),
-                    make_float2((z0.x - z0.y) * scale, (zh.x - zh.y) * scale));
+        // thread 0 in the product's slot order
+        constexpr int H = RL / 2;
 #pragma unroll
-        for (int e = 1; e < RL / 2; ++e) {
-            entry_from_pair(v[e], v[RL - e], scale, P, Q);
+        for (int e = 0; e < H; ++e) {
+            entry_from_pair(v[RL + e], v[2 * RL - 1 - e], scale, P, Q);
             store_entry(spec, e * T, P, Q);
         }
+        const float2 z0 = v[0], zh = v[H];
+        store_entry(spec, H * T, make_float2((z0.x + z0.y) * scale, (zh.x + zh.y) * scale),
+                    make_float2((z0.x - z0.y) * scale, (zh.x - zh.y) * scale));
 #pragma unroll
-        for (int e = RL / 2; e < RL; ++e) {
-            const int s = e - RL / 2;
-            entry_from_pair(v[RL + s], v[2 * RL - 1 - s], scale, P, Q);
+        for (int e = H + 1; e < RL; ++e) {
+            entry_from_pair(v[RL - e], v[e], scale, P, Q);
             store_entry(spec, e * T, P, Q);
         }
     }
@@ -714,11 +703,12 @@ __host__ __device__ inline int64_t real_entry_bin(int64_t L, int64_t T, int64_t 
     return tau + e * 2 * T;
 }
 
-// Bin of entry (tau, e) of a length-L transform (entry (0, 0) also holds L/2).
+// Bin (<= L/2) of entry (tau, e) of a length-L transform; entry (0, RL/2)
+// holds bins 0 and L/2 instead.
 __host__ __device__ inline int64_t entry_bin(int64_t L, int64_t T, int64_t tau, int64_t e)
 {
     const int64_t RL = L / (2 * T);
-    if (tau == 0) return e < RL / 2 ? e * 2 * T : T + (e - RL / 2) * 2 * T;
+    if (tau == 0) return e < RL / 2 ? T + e * 2 * T : (RL - e) * 2 * T;
     return e < RL / 2 ? tau + e * 2 * T : (2 * T - tau) + (RL - 1 - e) * 2 * T;
 }
 
