@@ -246,16 +246,23 @@ __device__ __forceinline__ void lds_write_first(float* sre, float* sim, const fl
 // Twiddles of butterfly k of a pass with sub-transform length NS: input r
 // takes tab[(r - 1) NS + k].  Loaded into registers ahead of the barrier that
 // precedes the pass, so the load latency overlaps the LDS exchange.
-// `tab` is wave-uniform.  The empty asm re-defines it in place, so the
-// per-row bases tab + (r-1) NS are recomputed with scalar adds at each use
-// instead of being hoisted out of the order loop as VGPR address pairs.
+// `tab` is wave-uniform.  Raw buffer loads: the table base sits in a scalar
+// descriptor, the row offset (r - 1) NS in a scalar register and the lane
+// offset in one VGPR, so no load needs address arithmetic of its own (a
+// global load would need a 64-bit add per row, since the rows are further
+// apart than its immediate offset reaches).
 template <int R, int NS>
 __device__ __forceinline__ void load_tw(float2* w, const float2* tab, uint32_t k)
 {
-    asm volatile("" : "+s"(tab));
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<float2*>(tab), (short)0, 0x7fffffff, 0x00020000);
     const uint32_t koff = k * 8u;
 #pragma unroll
-    for (int r = 1; r < R; ++r) w[r - 1] = at_bytes<float2>(tab + (r - 1) * NS, koff);
+    for (int r = 1; r < R; ++r) {
+        typedef float f2v __attribute__((ext_vector_type(2)));
+        const f2v t = __builtin_bit_cast(f2v, __builtin_amdgcn_raw_buffer_load_b64(rs, koff, (r - 1) * NS * 8, 0));
+        w[r - 1] = make_float2(t.x, t.y);
+    }
 }
 
 template <int R, int DIR>
@@ -615,13 +622,22 @@ __device__ __forceinline__ void real_product(float2* v, const typename EntryRaw<
     constexpr int RL = S::RL, H = RL / 2;
     const bool t0 = tau == 0;
     float2 ya[RL], yb[RL];
+    // W^k of slot e + RL/2 is -i W^k of slot e: (c, s) -> (-s, c)
+    float cs_c[H], cs_s[H];
 #pragma unroll
     for (int e = 0; e < RL; ++e) {
         float2 Sv, Dv;
         widen_entry<SP>(ent[e], Sv, Dv);
         Sv.x += dp;
         float c, s;
-        bin_cs<RL>(wbase, e, c, s);
+        if (e < H) {
+            bin_cs<RL>(wbase, e, c, s);
+            cs_c[e] = c;
+            cs_s[e] = s;
+        } else {
+            c = -cs_s[e - H];
+            s = cs_c[e - H];
+        }
         float2 a = v[e], b = v[2 * RL - 1 - e];
         if (e < H) {
             a = t0 ? v[RL + e] : a;
