@@ -438,17 +438,34 @@ __device__ __forceinline__ void widen_entry(const typename EntryRaw<SP>::type& r
 }
 
 // Entries e = 0..RL-1 of thread tau of one length-L transform (entry index
-// e T + tau: lanes read consecutive entries).
+// e T + tau: lanes read consecutive entries).  Raw buffer loads from the
+// transform's (wave-uniform) entry base: the entry offset e T sits in a
+// scalar register and the lane offset in one VGPR, where global loads would
+// need a 64-bit address add for every entry beyond the immediate-offset
+// range.  All offsets are below L/2 entries.
 template <int L, typename SP>
 __device__ __forceinline__ void load_entries(typename EntryRaw<SP>::type* ent, const SP* spec,
                                              int tau)
 {
     using S = FftShape<L>;
     using Raw = typename EntryRaw<SP>::type;
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<SP*>(spec), (short)0, 0x7fffffff, 0x00020000);
     const uint32_t off = (uint32_t)tau * (uint32_t)sizeof(Raw);
 #pragma unroll
-    for (int e = 0; e < S::RL; ++e)
-        ent[e] = at_bytes<Raw>(reinterpret_cast<const Raw*>(spec) + e * S::T, off);
+    for (int e = 0; e < S::RL; ++e) {
+        const uint32_t soff = (uint32_t)(e * S::T) * (uint32_t)sizeof(Raw);
+        if constexpr (sizeof(Raw) == 16) {
+            typedef float v4 __attribute__((ext_vector_type(4)));
+            const v4 t = __builtin_bit_cast(v4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, soff, 0));
+            ent[e] = make_float4(t.x, t.y, t.z, t.w);
+        } else {
+            static_assert(sizeof(Raw) == 8, "entry width");
+            typedef unsigned v2 __attribute__((ext_vector_type(2)));
+            const v2 t = __builtin_bit_cast(v2, __builtin_amdgcn_raw_buffer_load_b64(rs, off, soff, 0));
+            ent[e] = make_uint2(t.x, t.y);
+        }
+    }
 }
 
 // Mirror-paired product on the last-pass registers of one length-L transform.
