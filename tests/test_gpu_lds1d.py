@@ -249,7 +249,8 @@ def test_single_channel_wide_and_odd(d, dtype, tol):
 
 
 @pytest.mark.parametrize("shape", [("1d", 2048, 96, synth.BF16), ("1d", 20000, 5, synth.F32),
-                                   ("2d", (16, 32), 6, synth.F32)])
+                                   ("2d", (16, 32), 6, synth.F32),
+                                   ("3d", (8, 16, 4), 5, synth.F32)])
 def test_forward_in_a_hip_graph(shape):
     # the forward captured into a HIP graph (no allocation or memset inside
     # the library's launches) and replayed several times, with eager work and
@@ -260,9 +261,12 @@ def test_forward_in_a_hip_graph(shape):
     if kind == "1d":
         inp = synth.make_1d(B=2, N=dims, d=d, order=2, alpha_range=(1e-3, 1e-2), dtype=dtype,
                             seed=71)
-    else:
+    elif kind == "2d":
         inp = synth.make_2d(B=1, X=dims[0], Y=dims[1], d=d, order=2, sigma_range=(1.0, 8.0),
                             seed=72)
+    else:
+        inp = synth.make_3d(B=1, X=dims[0], Y=dims[1], Z=dims[2], d=d, order=2,
+                            sigma_range=(1.0, 4.0), seed=74)
     y_eager, plan, H = run_gpu(inp)
     u = to_torch(inp.u, dtype)
     gates = [to_torch(g, dtype) for g in inp.gates]

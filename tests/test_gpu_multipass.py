@@ -207,6 +207,44 @@ def test_hyenand_mixer(X, Y, d, dtype, bias):
     assert e < (TOL_F32 if dtype == synth.F32 else TOL_BF16)
 
 
+def test_hyenand_mixer_in_a_hip_graph():
+    # the mixer captured into a HIP graph and replayed with eager work and host
+    # waits between replays: every replay equals the eager result bit for bit
+    import torch
+    from gpu_util import from_torch, to_torch
+    from long_convolution_sequence_rfft_amd import hyena
+    X, Y, d = 16, 8, 5
+    inp = synth.make_2d(B=1, X=X, Y=Y, d=d, order=1, seed=97)
+    rng = np.random.default_rng(98)
+    q = to_torch(inp.u, synth.F32)
+    k = to_torch(synth._store(rng.standard_normal((1, X, Y, d)), synth.F32), synth.F32)
+    v = to_torch(synth._store(rng.standard_normal((1, X, Y, d)), synth.F32), synth.F32)
+    sw = torch.from_numpy(rng.normal(size=(3, d, 3, 3)).astype(np.float32) * 0.5).cuda()
+    sb = torch.from_numpy(rng.normal(size=(3, d)).astype(np.float32) * 0.1).cuda()
+    D = torch.from_numpy(inp.D[0].copy()).cuda()
+    plan = hyena.Plan(1, d, 1, (X, Y), io_dtype=hyena.HYENA_F32)
+    H = plan.spectrum(to_torch(inp.h, synth.F32))
+    y_eager = from_torch(plan.nd_mixer(q, k, v, sw, sb, H, D), synth.F32)
+    y = torch.empty_like(q)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):  # warm-up on the capture stream
+        plan.nd_mixer(q, k, v, sw, sb, H, D, y)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    say(f"[gpu] graph capture mixer {X}x{Y} d={d}")
+    with torch.cuda.graph(g):
+        plan.nd_mixer(q, k, v, sw, sb, H, D, y)
+    for r in range(3):
+        y.fill_(0)
+        plan.nd_mixer(q, k, v, sw, sb, H, D)  # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(from_torch(y, synth.F32), y_eager), f"replay {r}"
+
+
 # ---------------------------------------------------------------------------
 # 3D grids: transforms along z (outer), y (middle) and x (inner, with the
 # product), "How HyenaND works" on a native 3D grid
