@@ -210,9 +210,9 @@ hyena_status plan_build(Plan& p, int64_t B, int64_t N, int64_t d, int32_t order,
         // positions; the filter spectrum needs every inner position
         const int64_t fwd_pair = p.path == HYENA_PATH_FOURSTEP1D ? p.M * 8 : p.X * p.P2 * 8;
         const int64_t spec_pair = p.path == HYENA_PATH_FOURSTEP1D ? p.M * 8 : p.P1 * p.P2 * 8;
-        // keep the chunk's intermediate near 96 MiB so it stays in the 256 MB
-        // last-level cache between passes; whole groups of 16 pairs
-        int64_t chunk = (int64_t)(96ll << 20) / fwd_pair;
+        // keep the chunk's intermediate near kChunkBytes so it stays in the
+        // 256 MB last-level cache between passes; whole groups of 16 pairs
+        int64_t chunk = kChunkBytes / fwd_pair;
         chunk = chunk / 16 * 16;
         if (chunk < 16) chunk = 16;
         const int64_t total_slots = p.B * ((p.npairs + 15) / 16) * 16;
@@ -229,7 +229,7 @@ hyena_status plan_build(Plan& p, int64_t B, int64_t N, int64_t d, int32_t order,
         // transforms ([x][ky][kz])
         const int64_t fwd1 = p.X * p.Y * p.P3 * 8, fwd2 = p.X * p.P2 * p.P3 * 8;
         const int64_t spec1 = p.P1 * p.P2 * p.P3 * 8, spec2 = spec1;
-        int64_t chunk = (int64_t)(96ll << 20) / (fwd1 + fwd2);
+        int64_t chunk = kChunkBytes / (fwd1 + fwd2);
         chunk = chunk / 16 * 16;
         if (chunk < 16) chunk = 16;
         const int64_t total_slots = p.B * ((p.npairs + 15) / 16) * 16;

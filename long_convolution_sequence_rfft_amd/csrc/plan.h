@@ -20,6 +20,12 @@ constexpr int kMaxOrder = 8;
 constexpr int kMaxTwSegments = 12;
 constexpr int64_t kLdsMaxM = 16384;       // largest transform held in one workgroup's LDS
 constexpr int64_t kFourStepMaxM = 1 << 22;  // largest 1D transform (N = 2097152): 1024 x 4096
+// Multi-pass paths walk the channel pairs in chunks whose intermediate is
+// about this large: fewer, larger chunks mean fewer launches and partial last
+// waves, while the intermediate still mostly fits the 256 MB last-level cache
+// between passes (measured at 48, 96, 160, 192, 256 and 384 MiB; 192 was best
+// at 64K tokens and on the 256 x 256 grid).
+constexpr int64_t kChunkBytes = 192ll << 20;
 
 // Radix plan of the single-workgroup transform of length M (8 <= M <= 16384):
 // 32 complex values per thread (M >= 64), forward passes R0, R1, RL with

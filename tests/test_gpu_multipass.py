@@ -144,6 +144,19 @@ def test_full_size_2d_sampled():
     assert e < TOL_F32
 
 
+def test_rowcol2d_several_chunks():
+    # 512 x 512 grid, 3 batch rows of 17 channel pairs: 96 pair slots against
+    # chunks of 48 (192 MiB of 4 MiB intermediates), so the chain walks two
+    # chunks; sampled channels against the oracle
+    inp = synth.make_2d(B=3, X=512, Y=512, d=34, order=2, sigma_range=(8.0, 64.0), seed=41)
+    y, plan, _ = run_gpu(inp)
+    ch = np.array([0, 1, 16, 33])
+    ref = oracle_ref(inp, channels=ch, method=oracle.FFT)
+    e = rel_err(y[..., ch], ref)
+    say(f"2D 512x512 B=3 d=34 sampled rel_err={e:.3e}")
+    assert e < TOL_F32
+
+
 @pytest.mark.parametrize("N,d", [(100000, 2), (262144, 1), (524288, 1), (1000000, 1),
                                  (2097152, 1)])
 def test_fourstep_longer_than_64k(N, d):
@@ -317,8 +330,9 @@ def test_rowcol3d_deterministic_bitwise():
 
 
 def test_full_size_3d_sampled():
-    # 64^3 grid, width 32, order 2: sampled channels against the oracle
-    inp = synth.make_3d(B=1, X=64, Y=64, Z=64, d=32, order=2, sigma_range=(4.0, 32.0), seed=15)
+    # 64^3 grid, width 32, two batch rows, order 2 (32 pair slots: two chunks
+    # of 16): sampled channels against the oracle
+    inp = synth.make_3d(B=2, X=64, Y=64, Z=64, d=32, order=2, sigma_range=(4.0, 32.0), seed=15)
     y, plan, _ = run_gpu(inp)
     rng = np.random.default_rng(15)
     ch = np.unique(np.concatenate([[0, 1, inp.d - 1], rng.choice(inp.d, 3, replace=False)]))
