@@ -97,8 +97,11 @@ def algorithmic_flops(cfg):
 
 
 def kernel_source_sha():
+    """Hash of the kernel sources and of the build script (its compiler flags
+    shape the generated code as much as the sources do)."""
     h = hashlib.sha256()
-    for f in sorted(glob.glob(os.path.join(ROOT, "long_convolution_sequence_rfft_amd", "csrc", "*"))):
+    pkg = os.path.join(ROOT, "long_convolution_sequence_rfft_amd")
+    for f in sorted(glob.glob(os.path.join(pkg, "csrc", "*"))) + [os.path.join(pkg, "build.py")]:
         with open(f, "rb") as fh:
             h.update(os.path.basename(f).encode())
             h.update(fh.read())

@@ -24,8 +24,12 @@ SOURCES = ["api.hip", "lds1d.hip", "lds1d_f32.hip", "lds1d_bf16.hip", "lds1d_f16
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
+# The scheduler that groups memory instructions into clauses measured 1-3%
+# faster than the default on the 8K, 64K and 2D workloads (and no slower on
+# the others).
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          "-mllvm", "-amdgpu-sched-strategy=max-memory-clause",
           "-Wno-unused-command-line-argument", "-I", INCLUDE]
 
 
