@@ -302,8 +302,17 @@ def kernel_share(cfg, kernel):
         if "<" in kernel else []
     if short in ("hyena_lds1d_forward", "hyena_lds1d_real_forward"):
         # the whole chain runs in this one kernel (on staged copies of the
-        # activations, which move the same bytes)
-        return algorithmic_flops(cfg), algorithmic_bytes(cfg, cfg["dtype"])
+        # activations, which move the same bytes) -- except, for float32
+        # storage on the single-channel kernels, the last gate, which the
+        # gated stage-out applies
+        f, b_ = algorithmic_flops(cfg), algorithmic_bytes(cfg, cfg["dtype"])
+        if short == "hyena_lds1d_real_forward" and len(args) > 1 and args[1] == "float":
+            return f - tc, b_ - act
+        return f, b_
+    if short == "hyena_stage" and "gated" in args:
+        # float32 stage-out with the chain's last gate: one multiply and the
+        # gate read per token*channel
+        return float(tc), act
     if short == "hyena_mp_outer":
         la, mode = int(args[0]), int(args[2])
         lg = math.log2(la)

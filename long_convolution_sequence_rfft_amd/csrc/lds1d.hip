@@ -240,14 +240,20 @@ TwOffsets lds1d_offsets(const Plan& p)
 struct StageArgs {
     const void* src[kMaxOrder + 1];
     void* dst[kMaxOrder + 1];
+    const void* gate;  // GATED (back to channels-last): y = gate . staged value
     int64_t B, N, cols;
 };
 
 constexpr int kStageTT = 128;
 
-template <typename E, bool TO_COLS>
+// GATED (channel-major -> channels-last only): each output is multiplied by
+// the gate at its own channels-last position, read with the same coalesced
+// index as the store.  The chain's last gate is applied here for float32
+// storage, so that gate is never staged.
+template <typename E, bool TO_COLS, bool GATED = false>
 __global__ void __launch_bounds__(256) hyena_stage(StageArgs a)
 {
+    static_assert(!GATED || (!TO_COLS && sizeof(E) == 4), "gate on the way out, float32");
     constexpr int TP = 128 / (int)sizeof(E);  // elements per 128-byte line
     constexpr int TT = kStageTT;              // samples per tile
     constexpr int PER = TT * TP / 256;        // elements per thread
@@ -283,6 +289,16 @@ __global__ void __launch_bounds__(256) hyena_stage(StageArgs a)
     };
     auto in_range = [&](int tr, int pc) { return full || (t0 + tr < a.N && p0 + pc < P); };
 
+    E gv[GATED ? PER : 1];
+    if constexpr (GATED) {
+        const E* gate = static_cast<const E*>(a.gate);
+#pragma unroll
+        for (int k = 0; k < PER; ++k) {
+            int tr, pc;
+            rowwise(k, tr, pc);
+            if (in_range(tr, pc)) gv[k] = gate[dst_index(tr, pc)];
+        }
+    }
     E x[PER];
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
@@ -311,7 +327,11 @@ __global__ void __launch_bounds__(256) hyena_stage(StageArgs a)
         int tr, pc;
         if (TO_COLS) colwise(k, tr, pc);
         else rowwise(k, tr, pc);
-        if (in_range(tr, pc)) dst[dst_index(tr, pc)] = x[k];
+        if constexpr (GATED) {
+            if (in_range(tr, pc)) dst[dst_index(tr, pc)] = x[k] * gv[k];
+        } else {
+            if (in_range(tr, pc)) dst[dst_index(tr, pc)] = x[k];
+        }
     }
 }
 
@@ -438,6 +458,14 @@ hyena_status stage_launch(const StageArgs& a, int ntensors, bool to_cols, hipStr
     constexpr int TP = 128 / (int)sizeof(E);
     const dim3 grid((unsigned)((a.cols + TP - 1) / TP), (unsigned)((a.N + kStageTT - 1) / kStageTT),
                     (unsigned)(a.B * ntensors));
+    if constexpr (sizeof(E) == 4) {
+        if (a.gate) {
+            HY_LAUNCH(kernel_label("hyena_stage", elem_label<E>(), "gated"),
+                      (hyena_stage<E, false, true>), grid, dim3(256), 0, s, a);
+            const hipError_t e = hipGetLastError();
+            return e == hipSuccess ? HYENA_OK : fail(HYENA_ERR_DEVICE, hipGetErrorString(e));
+        }
+    }
     if (to_cols)
         HY_LAUNCH(kernel_label("hyena_stage", elem_label<E>(), true), (hyena_stage<E, true>), grid,
                   dim3(256), 0, s, a);
@@ -487,16 +515,20 @@ hyena_status launch_lds1d_forward(const Plan& p, const void* u, const void* cons
         char* base = const_cast<char*>(static_cast<const char*>(ws)) + p.stage_offset;
         st.B = p.B;
         st.N = p.N;
+        // float32 storage: the last gate is applied on the way back out
+        // (same single multiply, one tensor fewer staged)
+        a.last_gate_out = p.io_dtype == HYENA_F32;
+        const int staged_gates = p.order - a.last_gate_out;
         st.src[0] = u;
         st.dst[0] = base;
-        for (int n = 0; n < p.order; ++n) {
+        for (int n = 0; n < staged_gates; ++n) {
             st.src[1 + n] = gates[n];
             st.dst[1 + n] = base + (size_t)(1 + n) * tensor;
         }
         a.u = base;
         for (int n = 0; n < p.order; ++n) a.gates[n] = base + (size_t)(1 + n) * tensor;
         a.y = base + (size_t)(1 + p.order) * tensor;
-        const hyena_status r = stage_plan(p, st, 1 + p.order, true, s);
+        const hyena_status r = stage_plan(p, st, 1 + staged_gates, true, s);
         if (r != HYENA_OK) return r;
     }
     const hyena_status r = by_storage(p, [&](auto io, auto sp) {
@@ -511,6 +543,7 @@ hyena_status launch_lds1d_forward(const Plan& p, const void* u, const void* cons
     out.N = p.N;
     out.src[0] = a.y;
     out.dst[0] = y;
+    out.gate = a.last_gate_out ? gates[p.order - 1] : nullptr;
     return stage_plan(p, out, 1, false, s);
 }
 

@@ -35,6 +35,7 @@ struct Lds1dFwdArgs {
     const float2* twm;  // single-channel kernels: exp(-2 pi i k / M), k < M/2
     int64_t N, d, npairs, nblocks, B;
     int32_t order;
+    int32_t last_gate_out;  // single-channel kernels: the last gate is applied by the stage-out
     TwOffsets tw_off;
 };
 
@@ -224,8 +225,11 @@ __global__ void __launch_bounds__(FftShape<L>::T, 2) hyena_lds1d_real_forward(Ld
         real_product<L, SP>(v, ent, tau, a.D[(int64_t)n * a.d + c] * invL, wbase);
 
         const IO* g = static_cast<const IO*>(a.gates[n]) + row;
+        // the last gate may be left to the stage-out kernel (uniform)
+        const bool gate_here = n + 1 < a.order || !a.last_gate_out;
         typename PairRaw<IO>::type graw[S::Q0][RIN];
         inv_transform<L, !CIRC>(v, re, im, a.tw, a.tw_off, tau, j1, j2, [&] {
+            if (!gate_here) return;
 #pragma unroll
             for (int q = 0; q < S::Q0; ++q) {
                 const uint32_t lane_off = (uint32_t)(tau + q * T) * 2u * (uint32_t)sizeof(IO);
@@ -234,14 +238,16 @@ __global__ void __launch_bounds__(FftShape<L>::T, 2) hyena_lds1d_real_forward(Ld
                     graw[q][r] = load_pair_raw(g + (size_t)r * (L / R0) * 2, lane_off);
             }
         });
+        if (gate_here) {
 #pragma unroll
-        for (int q = 0; q < S::Q0; ++q)
+            for (int q = 0; q < S::Q0; ++q)
 #pragma unroll
-            for (int r = 0; r < RIN; ++r) {
-                const float2 gg = widen_pair<IO>(graw[q][r]);
-                float2& x = v[q * R0 + r];
-                x = make_float2(x.x * gg.x, x.y * gg.y);
-            }
+                for (int r = 0; r < RIN; ++r) {
+                    const float2 gg = widen_pair<IO>(graw[q][r]);
+                    float2& x = v[q * R0 + r];
+                    x = make_float2(x.x * gg.x, x.y * gg.y);
+                }
+        }
     }
 
     IO* ybase = static_cast<IO*>(a.y) + row;
