@@ -309,7 +309,7 @@ def kernel_share(cfg, kernel):
         if short == "hyena_lds1d_real_forward" and len(args) > 1 and args[1] == "float":
             return f - tc, b_ - act
         return f, b_
-    if short == "hyena_stage" and "gated" in args:
+    if short == "hyena_stage" and len(args) > 2 and args[2] == "true":
         # float32 stage-out with the chain's last gate: one multiply and the
         # gate read per token*channel
         return float(tc), act

@@ -460,18 +460,18 @@ hyena_status stage_launch(const StageArgs& a, int ntensors, bool to_cols, hipStr
                     (unsigned)(a.B * ntensors));
     if constexpr (sizeof(E) == 4) {
         if (a.gate) {
-            HY_LAUNCH(kernel_label("hyena_stage", elem_label<E>(), "gated"),
+            HY_LAUNCH(kernel_label("hyena_stage", elem_label<E>(), false, true),
                       (hyena_stage<E, false, true>), grid, dim3(256), 0, s, a);
             const hipError_t e = hipGetLastError();
             return e == hipSuccess ? HYENA_OK : fail(HYENA_ERR_DEVICE, hipGetErrorString(e));
         }
     }
     if (to_cols)
-        HY_LAUNCH(kernel_label("hyena_stage", elem_label<E>(), true), (hyena_stage<E, true>), grid,
-                  dim3(256), 0, s, a);
+        HY_LAUNCH(kernel_label("hyena_stage", elem_label<E>(), true, false), (hyena_stage<E, true>),
+                  grid, dim3(256), 0, s, a);
     else
-        HY_LAUNCH(kernel_label("hyena_stage", elem_label<E>(), false), (hyena_stage<E, false>), grid,
-                  dim3(256), 0, s, a);
+        HY_LAUNCH(kernel_label("hyena_stage", elem_label<E>(), false, false), (hyena_stage<E, false>),
+                  grid, dim3(256), 0, s, a);
     const hipError_t e = hipGetLastError();
     return e == hipSuccess ? HYENA_OK : fail(HYENA_ERR_DEVICE, hipGetErrorString(e));
 }

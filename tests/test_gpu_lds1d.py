@@ -160,8 +160,8 @@ def test_launch_timing_records_every_kernel():
     hyena.hyena_timing_release()
     assert dropped == 0
     assert sorted(recs) == ["hy::hyena_lds1d_real_forward<2048, float, float, false>",
-                            "hy::hyena_stage<float, gated>",
-                            "hy::hyena_stage<float, true>"]
+                            "hy::hyena_stage<float, false, true>",
+                            "hy::hyena_stage<float, true, false>"]
     for r in recs.values():
         assert r["launches"] == 3
         assert 0.0 < r["min_ms"] <= r["max_ms"] and r["total_ms"] >= 3 * r["min_ms"] * 0.999
