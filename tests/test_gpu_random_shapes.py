@@ -14,17 +14,21 @@ pytestmark = pytest.mark.gpu
 TOL = {synth.F32: 1e-5, synth.BF16: 1e-2, synth.F16: 5e-3}
 
 
-def _cases(n=36, seed=2024):
+def _cases(n=36, seed=2024, kinds=("1d", "1d", "1d", "circ", "2d", "3d"), first=0):
     rng = np.random.default_rng(seed)
     out = []
-    for i in range(n):
-        kind = ["1d", "1d", "1d", "circ", "2d", "3d"][i % 6]
+    for i in range(first, first + n):
+        kind = kinds[i % len(kinds)]
         dtype = [synth.F32, synth.BF16, synth.F16][int(rng.integers(3))]
         order = int(rng.integers(1, 4))
         B = int(rng.integers(1, 3))
         d = int(rng.integers(1, 12))
         if kind == "1d":
             dims = (int(rng.integers(4, 20000)),)
+        elif kind == "pow2":
+            # N = M/2: the single-channel kernels (staging, and for float32
+            # the last gate in the stage-out)
+            dims = (int(2 ** rng.integers(2, 14)),)
         elif kind == "circ":
             dims = (int(2 ** rng.integers(4, 13)),)
         elif kind == "2d":
@@ -35,12 +39,13 @@ def _cases(n=36, seed=2024):
     return out
 
 
-@pytest.mark.parametrize("case", _cases(), ids=lambda c: f"{c[0]}-{c[1]}-{'x'.join(map(str, c[2]))}-{c[3]}")
+@pytest.mark.parametrize("case", _cases() + _cases(n=24, seed=2025, kinds=("pow2",), first=36),
+                         ids=lambda c: f"{c[0]}-{c[1]}-{'x'.join(map(str, c[2]))}-{c[3]}")
 def test_random_shape(case):
     from long_convolution_sequence_rfft_amd import hyena
     i, kind, dims, dtype, order, B, d = case
     seed = 1000 + i
-    if kind in ("1d", "circ"):
+    if kind in ("1d", "pow2", "circ"):
         inp = synth.make_1d(B=B, N=dims[0], d=d, order=order, alpha_range=(1e-3, 3e-2),
                             dtype=dtype, seed=seed)
     elif kind == "2d":
