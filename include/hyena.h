@@ -51,10 +51,14 @@
  * thread-local description.  HYENA_ERR_DEVICE reports a failed launch;
  * faults inside a kernel surface at the caller's next synchronisation.
  *
- * Thread safety.  A plan is immutable after creation except for its record of
- * initialised workspaces, which is internally locked; plans may be shared by
- * host threads.  The forward pass uses no atomics, so the same plan and inputs
- * give bitwise-identical y.
+ * Thread safety.  A plan is immutable after creation; the record of
+ * initialised workspaces is process-wide and internally locked; plans may be
+ * shared by host threads.  The forward pass uses no atomics, so the same plan
+ * and inputs give bitwise-identical y.
+ *
+ * Diagnostics.  With the environment variable HYENA_LOG set (to anything but
+ * "" or "0") the host side reports plan decisions, workspace records, errors
+ * and every kernel launch (name, grid, block, stream) on stderr.
  */
 #ifndef HYENA_MI355X_H
 #define HYENA_MI355X_H
@@ -138,8 +142,24 @@ hyena_status hyena_plan_query(hyena_plan_t plan, size_t* spectrum_bytes,
 
 /* Write the plan's twiddle tables into a caller-allocated workspace of at
  * least workspace_bytes (16-byte aligned).  Required once per (plan,
- * workspace) before hyena_filter_spectrum or hyena_forward use it. */
+ * workspace) before hyena_filter_spectrum or hyena_forward use it.
+ *
+ * The library keeps a process-wide record of which plan's tables each
+ * workspace holds, keyed by its first byte.  A call with a workspace that is
+ * not recorded for its plan returns HYENA_ERR_WORKSPACE before anything is
+ * enqueued.  A record is dropped by hyena_workspace_release, by
+ * hyena_plan_destroy, and when another plan initialises, or runs a call on,
+ * a workspace whose bytes overlap it (its tables may then be overwritten).
+ * The library cannot see the caller's allocator: before a workspace is freed
+ * (and its memory possibly handed out again at the same address), release it
+ * or destroy the plan; using an address whose record outlived its memory is
+ * undefined and may give wrong results. */
 hyena_status hyena_workspace_init(hyena_plan_t plan, void* workspace, void* stream);
+
+/* Drop the record that `workspace` holds this plan's tables (no GPU work;
+ * HYENA_OK also when there was none).  Call before freeing a workspace that
+ * the plan will not use again. */
+hyena_status hyena_workspace_release(hyena_plan_t plan, void* workspace);
 
 /*
  * Filter spectrum ("Hyena -- Long Convolutions Math", section "The

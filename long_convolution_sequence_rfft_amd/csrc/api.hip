@@ -40,13 +40,19 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb)
     return a0 < b0 + nb && b0 < a0 + na;
 }
 
+// Last check before a call enqueues work that uses the workspace: it must
+// hold this plan's tables (recorded by hyena_workspace_init and not released,
+// overwritten by another plan's initialisation, or overlapped by another
+// plan's intermediates since).
 hyena_status check_ws(const hy::Plan& p, const void* ws)
 {
     if (ws == nullptr) return fail(HYENA_ERR_INVALID_ARGUMENT, "workspace is NULL");
     if (!aligned16(ws)) return fail(HYENA_ERR_INVALID_ARGUMENT, "workspace is not 16-byte aligned");
-    std::lock_guard<std::mutex> lock(p.mu);
-    if (p.ready_ws.count(ws) == 0)
-        return fail(HYENA_ERR_WORKSPACE, "workspace was not initialised with hyena_workspace_init for this plan");
+    if (!hy::ws_record_use(ws, p.workspace_bytes, p.token))
+        return fail(HYENA_ERR_WORKSPACE,
+                    "workspace does not hold this plan's tables: call hyena_workspace_init "
+                    "(it was never initialised for this plan, was released, or another plan "
+                    "has initialised or used memory overlapping it since)");
     return HYENA_OK;
 }
 
@@ -98,8 +104,15 @@ hyena_status hyena_workspace_init(hyena_plan_t plan, void* workspace, void* stre
         return fail(HYENA_ERR_INVALID_ARGUMENT, "workspace is not 16-byte aligned");
     const hyena_status st = hy::launch_tw_init(plan->p, workspace, stream);
     if (st != HYENA_OK) return st;
-    std::lock_guard<std::mutex> lock(plan->p.mu);
-    plan->p.ready_ws.insert(workspace);
+    hy::ws_record_init(workspace, plan->p.workspace_bytes, plan->p.token);
+    return HYENA_OK;
+}
+
+hyena_status hyena_workspace_release(hyena_plan_t plan, void* workspace)
+{
+    if (plan == nullptr) return fail(HYENA_ERR_INVALID_ARGUMENT, "plan is NULL");
+    if (workspace == nullptr) return fail(HYENA_ERR_INVALID_ARGUMENT, "workspace is NULL");
+    hy::ws_record_release(workspace, plan->p.token);
     return HYENA_OK;
 }
 
@@ -113,10 +126,10 @@ hyena_status hyena_filter_spectrum(hyena_plan_t plan, const void* h, void* H, vo
         return fail(HYENA_ERR_INVALID_ARGUMENT, "h and H must be 16-byte aligned");
     if (overlaps(h, filter_bytes(p), H, p.spectrum_bytes))
         return fail(HYENA_ERR_INVALID_ARGUMENT, "H overlaps h");
-    hyena_status st = check_ws(p, workspace);
-    if (st != HYENA_OK) return st;
     if (overlaps(workspace, p.workspace_bytes, H, p.spectrum_bytes))
         return fail(HYENA_ERR_INVALID_ARGUMENT, "H overlaps the workspace");
+    const hyena_status st = check_ws(p, workspace);
+    if (st != HYENA_OK) return st;
     switch (p.path) {
         case HYENA_PATH_LDS1D: return hy::launch_lds1d_spectrum(p, h, H, workspace, stream);
         case HYENA_PATH_FOURSTEP1D: return hy::launch_fourstep_spectrum(p, h, H, workspace, stream);
@@ -147,10 +160,10 @@ hyena_status hyena_forward(hyena_plan_t plan, const void* u, const void* const* 
     if (overlaps(y, nio, u, nio)) return fail(HYENA_ERR_INVALID_ARGUMENT, "y overlaps u");
     if (overlaps(y, nio, H, p.spectrum_bytes)) return fail(HYENA_ERR_INVALID_ARGUMENT, "y overlaps H");
     if (overlaps(y, nio, D, nD)) return fail(HYENA_ERR_INVALID_ARGUMENT, "y overlaps D");
-    hyena_status st = check_ws(p, workspace);
-    if (st != HYENA_OK) return st;
     if (overlaps(y, nio, workspace, p.workspace_bytes))
         return fail(HYENA_ERR_INVALID_ARGUMENT, "y overlaps the workspace");
+    const hyena_status st = check_ws(p, workspace);
+    if (st != HYENA_OK) return st;
     switch (p.path) {
         case HYENA_PATH_LDS1D:
             return hy::launch_lds1d_forward(p, u, gates, H, D, y, workspace, stream);
@@ -182,10 +195,10 @@ hyena_status hyena_nd_mixer_forward(hyena_plan_t plan, const hyena_nd_mixer* m, 
         return fail(HYENA_ERR_INVALID_ARGUMENT, "y overlaps q, k or v");
     if (overlaps(y, nio, H, p.spectrum_bytes)) return fail(HYENA_ERR_INVALID_ARGUMENT, "y overlaps H");
     if (overlaps(y, nio, D, (size_t)p.d * 4u)) return fail(HYENA_ERR_INVALID_ARGUMENT, "y overlaps D");
-    hyena_status st = check_ws(p, workspace);
-    if (st != HYENA_OK) return st;
     if (overlaps(y, nio, workspace, p.workspace_bytes))
         return fail(HYENA_ERR_INVALID_ARGUMENT, "y overlaps the workspace");
+    const hyena_status st = check_ws(p, workspace);
+    if (st != HYENA_OK) return st;
     if (p.ndims == 3) return hy::launch_rowcol3d_block(p, *m, H, D, y, workspace, stream);
     return hy::launch_rowcol2d_block(p, *m, H, D, y, workspace, stream);
 }
@@ -221,12 +234,12 @@ hyena_status hyena_filter_spectrum_implicit(hyena_plan_t plan, const hyena_impli
     const size_t nscratch = hy::implicit_scratch_bytes(p, f->hidden);
     if (overlaps(H, p.spectrum_bytes, scratch, nscratch))
         return fail(HYENA_ERR_INVALID_ARGUMENT, "H overlaps the scratch");
-    hyena_status st = check_ws(p, workspace);
-    if (st != HYENA_OK) return st;
     if (overlaps(workspace, p.workspace_bytes, H, p.spectrum_bytes))
         return fail(HYENA_ERR_INVALID_ARGUMENT, "H overlaps the workspace");
     if (overlaps(workspace, p.workspace_bytes, scratch, nscratch))
         return fail(HYENA_ERR_INVALID_ARGUMENT, "the scratch overlaps the workspace");
+    const hyena_status st = check_ws(p, workspace);
+    if (st != HYENA_OK) return st;
     return hy::launch_implicit_spectrum(p, *f, H, workspace, scratch, stream);
 }
 
@@ -249,6 +262,10 @@ hyena_status hyena_spectrum_export(hyena_plan_t plan, const void* H, void* natur
 
 hyena_status hyena_plan_destroy(hyena_plan_t plan)
 {
+    if (plan != nullptr) {
+        hy::ws_record_drop(plan->p.token);
+        hy::log_msg("plan %llu destroyed", (unsigned long long)plan->p.token);
+    }
     delete plan;
     return HYENA_OK;
 }

@@ -1,6 +1,13 @@
 // plan.cpp -- argument validation, path choice and byte layouts.  Pure host
 // code: no HIP runtime call is made here, so plans can be created and
 // inspected on a machine without a GPU.
+#include <stdarg.h>
+#include <stdio.h>
+#include <stdlib.h>
+
+#include <atomic>
+#include <map>
+#include <mutex>
 #include <string>
 
 #include "plan.h"
@@ -43,9 +50,112 @@ void set_error(const std::string& msg) { g_last_error = msg; }
 hyena_status fail(hyena_status s, const std::string& msg)
 {
     g_last_error = msg;
+    log_msg("error %d: %s", (int)s, msg.c_str());
     return s;
 }
 const char* last_error_text() { return g_last_error.c_str(); }
+
+bool log_on()
+{
+    static const bool on = [] {
+        const char* v = getenv("HYENA_LOG");
+        return v != nullptr && v[0] != '\0' && !(v[0] == '0' && v[1] == '\0');
+    }();
+    return on;
+}
+
+void log_msg(const char* fmt, ...)
+{
+    if (!log_on()) return;
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    fprintf(stderr, "[hyena] %s\n", buf);
+    fflush(stderr);
+}
+
+// ---------------------------------------------------------------------------
+// workspace record
+// ---------------------------------------------------------------------------
+namespace {
+struct WsEntry {
+    size_t bytes;
+    uint64_t token;
+};
+std::mutex g_ws_mu;
+std::map<uintptr_t, WsEntry> g_ws;  // first byte -> entry
+std::atomic<uint64_t> g_next_token{1};
+
+// Drop every entry overlapping [a, a + n) except the one at `keep` made by
+// `keep_token` (keep = 0: none kept).  Caller holds g_ws_mu.
+void drop_overlapping(uintptr_t a, size_t n, uintptr_t keep, uint64_t keep_token)
+{
+    if (n == 0) n = 1;
+    // entries start below a + n; walk back from there while they may reach a
+    auto it = g_ws.lower_bound(a + n);
+    while (it != g_ws.begin()) {
+        --it;
+        const uintptr_t s = it->first;
+        const size_t m = it->second.bytes ? it->second.bytes : 1;
+        if (s + m <= a) {
+            // entries further down start lower; one of them could still be
+            // long enough to reach a, so keep walking (records are few)
+            continue;
+        }
+        if (s == keep && it->second.token == keep_token) continue;
+        log_msg("workspace record %p (plan %llu) dropped: overlapped by [%p, +%zu)", (void*)s,
+                (unsigned long long)it->second.token, (void*)a, n);
+        it = g_ws.erase(it);
+    }
+}
+}  // namespace
+
+void ws_record_init(const void* ws, size_t bytes, uint64_t token)
+{
+    std::lock_guard<std::mutex> lock(g_ws_mu);
+    const uintptr_t a = (uintptr_t)ws;
+    drop_overlapping(a, bytes, 0, 0);
+    g_ws[a] = WsEntry{bytes, token};
+    log_msg("workspace %p (+%zu bytes) holds the tables of plan %llu", ws, bytes,
+            (unsigned long long)token);
+}
+
+bool ws_record_use(const void* ws, size_t bytes, uint64_t token)
+{
+    std::lock_guard<std::mutex> lock(g_ws_mu);
+    const uintptr_t a = (uintptr_t)ws;
+    auto it = g_ws.find(a);
+    if (it == g_ws.end() || it->second.token != token) return false;
+    drop_overlapping(a, bytes, a, token);
+    return true;
+}
+
+bool ws_record_release(const void* ws, uint64_t token)
+{
+    std::lock_guard<std::mutex> lock(g_ws_mu);
+    auto it = g_ws.find((uintptr_t)ws);
+    if (it == g_ws.end() || it->second.token != token) return false;
+    g_ws.erase(it);
+    log_msg("workspace %p released by plan %llu", ws, (unsigned long long)token);
+    return true;
+}
+
+void ws_record_drop(uint64_t token)
+{
+    std::lock_guard<std::mutex> lock(g_ws_mu);
+    for (auto it = g_ws.begin(); it != g_ws.end();) {
+        if (it->second.token == token) it = g_ws.erase(it);
+        else ++it;
+    }
+}
+
+size_t ws_record_count()
+{
+    std::lock_guard<std::mutex> lock(g_ws_mu);
+    return g_ws.size();
+}
 
 // Four-step split of a 1D transform of length M into columns of length M1
 // (sample t = M2 * n1 + n2) and rows of length M2.
@@ -85,6 +195,7 @@ hyena_status plan_build(Plan& p, int64_t B, int64_t N, int64_t d, int32_t order,
     if ((double)N * (double)d * 4.0 >= 2147483648.0)
         return fail(HYENA_ERR_UNSUPPORTED, "N * d * 4 must stay below 2^31 bytes");
 
+    p.token = g_next_token.fetch_add(1);
     p.B = B;
     p.N = N;
     p.d = d;
@@ -251,6 +362,14 @@ hyena_status plan_build(Plan& p, int64_t B, int64_t N, int64_t d, int32_t order,
                                      (io_dtype == HYENA_F32 ? 4u : 2u), 256);
     }
     p.workspace_bytes = p.inter_offset + p.inter_bytes + p.stage_bytes;
+    static const char* kPathName[] = {"AUTO", "LDS1D", "FOURSTEP1D", "ROWCOL2D", "ROWCOL3D"};
+    log_msg("plan %llu: B=%lld N=%lld d=%lld order=%d ndims=%d io=%d spectrum=%d circular=%d -> "
+            "path %s, M=%lld (M1=%lld M2=%lld P=%lldx%lldx%lld), spectrum %zu B, workspace %zu B, "
+            "chunk %lld pair slots",
+            (unsigned long long)p.token, (long long)B, (long long)N, (long long)d, order, ndims,
+            io_dtype, spec_dtype, p.circular, kPathName[p.path], (long long)p.M, (long long)p.M1,
+            (long long)p.M2, (long long)p.P1, (long long)p.P2, (long long)p.P3, p.spectrum_bytes,
+            p.workspace_bytes, (long long)p.chunk_pairs);
     return HYENA_OK;
 }
 

@@ -8,8 +8,6 @@
 #include <stddef.h>
 #include <stdint.h>
 
-#include <mutex>
-#include <set>
 #include <string>
 
 #include "hyena.h"
@@ -100,9 +98,8 @@ struct Plan {
     size_t inter_bytes = 0;
     size_t workspace_bytes = 0;
 
-    // record of workspaces that hold this plan's twiddles
-    mutable std::mutex mu;
-    std::set<const void*> ready_ws;
+    // identifies the plan in the workspace record (unique in the process)
+    uint64_t token = 0;
 };
 
 // Implemented in plan.cpp (pure host code).
@@ -111,6 +108,30 @@ hyena_status plan_build(Plan& p, int64_t B, int64_t N, int64_t d, int32_t order,
                         int32_t spec_dtype, int32_t path, int32_t flags);
 void set_error(const std::string& msg);
 hyena_status fail(hyena_status s, const std::string& msg);
+
+// HYENA_LOG: with the environment variable HYENA_LOG set to a non-empty value
+// other than "0", the host side reports plan decisions, workspace records and
+// every kernel launch on stderr.  Read once per process.
+bool log_on();
+void log_msg(const char* fmt, ...) __attribute__((format(printf, 1, 2)));
+
+// Process-wide record of which plan's twiddle tables each workspace holds
+// (implemented in plan.cpp, pure host code, internally locked).  A workspace
+// is recorded by its first byte and the byte count the plan uses.
+//   ws_record_init:    `token`'s tables were written at ws; every record whose
+//                      bytes overlap [ws, ws + bytes) is dropped first (the
+//                      write clobbered them).
+//   ws_record_use:     true when ws holds `token`'s tables; then every other
+//                      record overlapping [ws, ws + bytes) is dropped (the call
+//                      about to run writes its intermediates there).
+//   ws_record_release: drop the record of ws if `token` made it; returns
+//                      whether one was dropped.
+//   ws_record_drop:    drop every record of `token` (plan destroyed).
+void ws_record_init(const void* ws, size_t bytes, uint64_t token);
+bool ws_record_use(const void* ws, size_t bytes, uint64_t token);
+bool ws_record_release(const void* ws, uint64_t token);
+void ws_record_drop(uint64_t token);
+size_t ws_record_count();
 
 // Implemented in the .hip launchers.
 hyena_status launch_tw_init(const Plan& p, void* ws, void* stream);

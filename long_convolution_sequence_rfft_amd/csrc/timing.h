@@ -14,6 +14,8 @@
 namespace hy {
 
 bool timing_on();
+bool log_on();
+void log_msg(const char* fmt, ...) __attribute__((format(printf, 1, 2)));
 void timing_mark_begin(hipStream_t s);
 void timing_mark_end(hipStream_t s, const std::string& label);
 
@@ -44,11 +46,16 @@ std::string kernel_label(const char* name, A... args)
 }  // namespace hy
 
 // Launch `kern` like hipLaunchKernelGGL; LABEL is an expression giving the
-// label (evaluated only while timing is on).
-#define HY_LAUNCH(LABEL, kern, grid, block, lds, stream, ...)                \
-    do {                                                                    \
-        const bool hy_timed_ = ::hy::timing_on();                           \
-        if (hy_timed_) ::hy::timing_mark_begin(stream);                     \
-        hipLaunchKernelGGL(kern, grid, block, lds, stream, __VA_ARGS__);    \
-        if (hy_timed_) ::hy::timing_mark_end(stream, LABEL);                \
+// label (evaluated only while timing or HYENA_LOG is on).
+#define HY_LAUNCH(LABEL, kern, grid, block, lds, stream, ...)                          \
+    do {                                                                              \
+        const bool hy_timed_ = ::hy::timing_on();                                     \
+        if (::hy::log_on()) {                                                         \
+            const dim3 hy_g_ = (grid), hy_b_ = (block);                               \
+            ::hy::log_msg("launch %s grid %u block %u stream %p", std::string(LABEL).c_str(), \
+                          hy_g_.x, hy_b_.x, (void*)(stream));                         \
+        }                                                                             \
+        if (hy_timed_) ::hy::timing_mark_begin(stream);                               \
+        hipLaunchKernelGGL(kern, grid, block, lds, stream, __VA_ARGS__);              \
+        if (hy_timed_) ::hy::timing_mark_end(stream, LABEL);                          \
     } while (0)

@@ -37,7 +37,7 @@ EXPORTED_SYMBOLS = (
     "hyena_forward", "hyena_spectrum_export", "hyena_plan_destroy", "hyena_status_string",
     "hyena_last_error", "hyena_timing_begin", "hyena_timing_end", "hyena_timing_kernel",
     "hyena_timing_release", "hyena_implicit_scratch_bytes", "hyena_filter_spectrum_implicit",
-    "hyena_plan_create_ex", "hyena_nd_mixer_forward",
+    "hyena_plan_create_ex", "hyena_nd_mixer_forward", "hyena_workspace_release",
 )
 
 
@@ -85,6 +85,7 @@ def load():
             lib.hyena_plan_query.argtypes = [p, ctypes.POINTER(sz), ctypes.POINTER(sz),
                                              ctypes.POINTER(i32)]
             lib.hyena_workspace_init.argtypes = [p, p, p]
+            lib.hyena_workspace_release.argtypes = [p, p]
             lib.hyena_filter_spectrum.argtypes = [p, p, p, p, p]
             lib.hyena_forward.argtypes = [p, p, ctypes.POINTER(p), p, p, p, p, p]
             lib.hyena_spectrum_export.argtypes = [p, p, p, p]
@@ -103,7 +104,8 @@ def load():
             lib.hyena_nd_mixer_forward.argtypes = [p, ctypes.POINTER(NdMixer), p, p, p, p, p]
             lib.hyena_filter_spectrum_implicit.argtypes = [p, ctypes.POINTER(ImplicitFilter), p, p,
                                                            p, p]
-            for name in ("hyena_plan_create", "hyena_plan_create_ex", "hyena_plan_query", "hyena_workspace_init",
+            for name in ("hyena_plan_create", "hyena_plan_create_ex", "hyena_plan_query",
+                         "hyena_workspace_init", "hyena_workspace_release",
                          "hyena_filter_spectrum", "hyena_forward", "hyena_spectrum_export",
                          "hyena_plan_destroy", "hyena_timing_begin", "hyena_timing_end",
                          "hyena_timing_kernel", "hyena_timing_release",
@@ -166,6 +168,10 @@ def hyena_plan_query(plan):
 
 def hyena_workspace_init(plan, workspace, stream=0):
     return load().hyena_workspace_init(plan, workspace, stream)
+
+
+def hyena_workspace_release(plan, workspace):
+    return load().hyena_workspace_release(plan, workspace)
 
 
 def hyena_filter_spectrum(plan, h, H, workspace, stream=0):
@@ -274,16 +280,55 @@ class Plan:
         return {HYENA_F32: self.torch.float32, HYENA_BF16: self.torch.bfloat16,
                 HYENA_F16: self.torch.float16}[self.io_dtype]
 
-    def _io(self, t, name):
-        if t.dtype != self.torch_io_dtype or not t.is_contiguous() or t.device != self.device:
-            raise ValueError(f"{name} must be a contiguous {self.torch_io_dtype} tensor on "
-                             f"{self.device}")
+    # ------------------------------------------------------------------
+    # argument checks: every tensor is checked (dtype, contiguity, device,
+    # shape or byte count) before anything is enqueued, so an undersized or
+    # misplaced buffer raises ValueError instead of reaching a kernel
+    # ------------------------------------------------------------------
+    @property
+    def act_shape(self):
+        """Shape of u, the gates and y: [B, *dims, d]."""
+        return (self.B,) + self.dims + (self.d,)
+
+    @property
+    def filter_shape(self):
+        """Shape of the taps h: [order, d, N] or [order, d, 2X-1, 2Y-1(, 2Z-1)]."""
+        if len(self.dims) == 1:
+            return (self.order, self.d, self.N)
+        return (self.order, self.d) + tuple(2 * int(s) - 1 for s in self.dims)
+
+    def _tensor(self, t, name, dtype, shape=None, min_bytes=None):
+        torch = self.torch
+        if not isinstance(t, torch.Tensor):
+            raise ValueError(f"{name} must be a torch tensor")
+        if t.dtype != dtype:
+            raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        if t.device != self.device:
+            raise ValueError(f"{name} must be on {self.device}, got {t.device}")
+        if shape is not None and tuple(t.shape) != tuple(shape):
+            raise ValueError(f"{name} must have shape {list(shape)}, got {list(t.shape)}")
+        if min_bytes is not None and t.numel() * t.element_size() < min_bytes:
+            raise ValueError(f"{name} must hold at least {min_bytes} bytes, got "
+                             f"{t.numel() * t.element_size()}")
         return t
 
+    def _io(self, t, name, shape=None):
+        return self._tensor(t, name, self.torch_io_dtype,
+                            self.act_shape if shape is None else shape)
+
+    def _spec(self, H, name="H"):
+        return self._tensor(H, name, self.torch.uint8, min_bytes=self.spectrum_bytes)
+
+    def _f32(self, t, name, shape):
+        return self._tensor(t, name, self.torch.float32, shape)
+
     def spectrum(self, h, H=None):
-        h = self._io(h, "h")
+        h = self._io(h, "h", self.filter_shape)
         if H is None:
             H = self.torch.empty(self.spectrum_bytes, dtype=self.torch.uint8, device=self.device)
+        self._spec(H)
         _check(hyena_filter_spectrum(self.handle, h.data_ptr(), H.data_ptr(),
                                      self.workspace.data_ptr(), self.stream()),
                "hyena_filter_spectrum")
@@ -294,10 +339,17 @@ class Plan:
         W1 [hidden, 2K+1], b1 [hidden], W2 [hidden, hidden], b2 [hidden],
         W3 [order*d, hidden], b3 [order*d], alpha [order, d]."""
         ws = [W1, b1, W2, b2, W3, b3, alpha]
-        for t in ws:
-            if t.dtype != self.torch.float32 or not t.is_contiguous() or t.device != self.device:
-                raise ValueError(f"implicit-filter weights must be contiguous float32 on {self.device}")
-        hidden, m = W1.shape
+        if not isinstance(W1, self.torch.Tensor) or W1.dim() != 2:
+            raise ValueError("W1 must be a 2-D tensor [hidden, 2K+1]")
+        hidden, m = (int(x) for x in W1.shape)
+        if m % 2 != 1:
+            raise ValueError(f"W1 must have an odd width 2K+1, got {m}")
+        nd = self.order * self.d
+        for t, name, shape in ((W1, "W1", (hidden, m)), (b1, "b1", (hidden,)),
+                               (W2, "W2", (hidden, hidden)), (b2, "b2", (hidden,)),
+                               (W3, "W3", (nd, hidden)), (b3, "b3", (nd,)),
+                               (alpha, "alpha", (self.order, self.d))):
+            self._f32(t, name, shape)
         f = ImplicitFilter((m - 1) // 2, hidden, float(omega), *[t.data_ptr() for t in ws])
         st, nbytes = hyena_implicit_scratch_bytes(self.handle, hidden)
         _check(st, "hyena_implicit_scratch_bytes")
@@ -309,6 +361,7 @@ class Plan:
             scratch = self.torch.empty(max(nbytes, 256), dtype=self.torch.uint8, device=self.device)
         if H is None:
             H = self.torch.empty(self.spectrum_bytes, dtype=self.torch.uint8, device=self.device)
+        self._spec(H)
         _check(hyena_filter_spectrum_implicit(self.handle, f, H.data_ptr(),
                                               self.workspace.data_ptr(), scratch.data_ptr(),
                                               self.stream()),
@@ -318,13 +371,15 @@ class Plan:
 
     def forward(self, u, gates, H, D, y=None):
         u = self._io(u, "u")
-        gates = [self._io(g, "gate") for g in gates]
+        gates = list(gates)
         if len(gates) != self.order:
-            raise ValueError("need one gate per filter")
-        if D.dtype != self.torch.float32 or not D.is_contiguous():
-            raise ValueError("D must be contiguous float32 [order, d]")
+            raise ValueError(f"need one gate per filter ({self.order}), got {len(gates)}")
+        gates = [self._io(g, f"gate {n}") for n, g in enumerate(gates)]
+        self._spec(H)
+        self._f32(D, "D", (self.order, self.d))
         if y is None:
             y = self.torch.empty_like(u)
+        self._io(y, "y")
         _check(hyena_forward(self.handle, u.data_ptr(), [g.data_ptr() for g in gates],
                              H.data_ptr(), D.data_ptr(), y.data_ptr(), self.workspace.data_ptr(),
                              self.stream()),
@@ -336,11 +391,15 @@ class Plan:
         z = sc(q) . SiLU(sc(k)); short_w float32 [3, d, 3, 3] (2D) or [3, d, 3, 3, 3]
         (3D), short_b [3, d] or None."""
         q, k, v = self._io(q, "q"), self._io(k, "k"), self._io(v, "v")
-        for t in (short_w, D) + ((short_b,) if short_b is not None else ()):
-            if t.dtype != self.torch.float32 or not t.is_contiguous():
-                raise ValueError("short-conv taps, biases and D must be contiguous float32")
+        taps = (3,) * len(self.dims)
+        self._f32(short_w, "short_w", (3, self.d) + taps)
+        if short_b is not None:
+            self._f32(short_b, "short_b", (3, self.d))
+        self._f32(D, "D", (self.order, self.d))
+        self._spec(H)
         if y is None:
             y = self.torch.empty_like(q)
+        self._io(y, "y")
         m = NdMixer(q.data_ptr(), k.data_ptr(), v.data_ptr(), short_w.data_ptr(),
                     short_b.data_ptr() if short_b is not None else None)
         _check(hyena_nd_mixer_forward(self.handle, m, H.data_ptr(), D.data_ptr(), y.data_ptr(),
@@ -349,6 +408,7 @@ class Plan:
         return y
 
     def export_spectrum(self, H):
+        self._spec(H)
         if len(self.dims) == 1:
             M = 1
             while M < (self.N if self.circular else 2 * self.N):
