@@ -324,6 +324,13 @@ class Plan:
     def _f32(self, t, name, shape):
         return self._tensor(t, name, self.torch.float32, shape)
 
+    def _feedthrough(self, D):
+        """D: float32 [order, d] ([d] is accepted for order 1)."""
+        shape = (self.order, self.d)
+        if self.order == 1 and isinstance(D, self.torch.Tensor) and D.dim() == 1:
+            shape = (self.d,)
+        return self._f32(D, "D", shape)
+
     def spectrum(self, h, H=None):
         h = self._io(h, "h", self.filter_shape)
         if H is None:
@@ -376,7 +383,7 @@ class Plan:
             raise ValueError(f"need one gate per filter ({self.order}), got {len(gates)}")
         gates = [self._io(g, f"gate {n}") for n, g in enumerate(gates)]
         self._spec(H)
-        self._f32(D, "D", (self.order, self.d))
+        self._feedthrough(D)
         if y is None:
             y = self.torch.empty_like(u)
         self._io(y, "y")
@@ -395,7 +402,7 @@ class Plan:
         self._f32(short_w, "short_w", (3, self.d) + taps)
         if short_b is not None:
             self._f32(short_b, "short_b", (3, self.d))
-        self._f32(D, "D", (self.order, self.d))
+        self._feedthrough(D)
         self._spec(H)
         if y is None:
             y = self.torch.empty_like(q)
