@@ -185,6 +185,27 @@ hyena_status hyena_forward(hyena_plan_t plan, const void* u, const void* const* 
                            void* stream);
 
 /*
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.
+ * hyena_forward with the workspace taken from a fixed device array inside the
+ * library (HYENA_NOALLOC_SCRATCH_BYTES per GPU, held from its first use on
+ * that GPU until the process ends) instead of a caller buffer.  The call
+ * allocates nothing: the caller still passes u, the gates, H, D and y, as for
+ * hyena_forward.  It writes the plan's twiddle tables into the array itself
+ * when they are not already there, so no hyena_workspace_init is needed.
+ * Plans whose workspace_bytes exceed HYENA_NOALLOC_SCRATCH_BYTES are refused
+ * with HYENA_ERR_UNSUPPORTED (the single-workgroup paths of the 2K and 8K
+ * width-768 workloads fit; the multi-pass paths' chunked intermediates
+ * usually do not).  The array is shared by every call on a GPU and keeps the
+ * last call's contents, so calls that overlap on one GPU (different streams,
+ * or different host threads) race and must be serialised by the caller.
+ * The kernels and results are those of hyena_forward.
+ */
+#define HYENA_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+hyena_status hyena_forward_noalloc(hyena_plan_t plan, const void* u, const void* const* gates,
+                                   const void* H, const float* D, void* y, void* stream);
+
+/*
  * HyenaND mixer ("How HyenaND works", section "Putting it together: the
  * HyenaND operator"), for ndims = 2 or 3 plans of order 1: the depthwise
  * short convolution (zero padding; 3x3 taps short_w [3][d][3][3] on 2D

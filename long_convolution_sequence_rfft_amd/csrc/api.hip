@@ -139,11 +139,15 @@ hyena_status hyena_filter_spectrum(hyena_plan_t plan, const void* h, void* H, vo
     }
 }
 
-hyena_status hyena_forward(hyena_plan_t plan, const void* u, const void* const* gates,
-                           const void* H, const float* D, void* y, void* workspace, void* stream)
+}  // extern "C"
+
+namespace hy {
+
+// Argument checks of hyena_forward other than the workspace record; `ws` is
+// the workspace the call will use (its first workspace_bytes bytes).
+hyena_status check_forward_args(const Plan& p, const void* u, const void* const* gates,
+                                const void* H, const float* D, const void* y, const void* ws)
 {
-    if (plan == nullptr) return fail(HYENA_ERR_INVALID_ARGUMENT, "plan is NULL");
-    const hy::Plan& p = plan->p;
     if (u == nullptr || gates == nullptr || H == nullptr || D == nullptr || y == nullptr)
         return fail(HYENA_ERR_INVALID_ARGUMENT, "a required pointer is NULL");
     if (!aligned16(u) || !aligned16(H) || !aligned16(D) || !aligned16(y))
@@ -160,21 +164,40 @@ hyena_status hyena_forward(hyena_plan_t plan, const void* u, const void* const* 
     if (overlaps(y, nio, u, nio)) return fail(HYENA_ERR_INVALID_ARGUMENT, "y overlaps u");
     if (overlaps(y, nio, H, p.spectrum_bytes)) return fail(HYENA_ERR_INVALID_ARGUMENT, "y overlaps H");
     if (overlaps(y, nio, D, nD)) return fail(HYENA_ERR_INVALID_ARGUMENT, "y overlaps D");
-    if (overlaps(y, nio, workspace, p.workspace_bytes))
+    if (overlaps(y, nio, ws, p.workspace_bytes))
         return fail(HYENA_ERR_INVALID_ARGUMENT, "y overlaps the workspace");
-    const hyena_status st = check_ws(p, workspace);
-    if (st != HYENA_OK) return st;
+    return HYENA_OK;
+}
+
+// Enqueue the whole chain (arguments already checked).
+hyena_status run_forward(const Plan& p, const void* u, const void* const* gates, const void* H,
+                         const float* D, void* y, void* ws, void* stream)
+{
     switch (p.path) {
-        case HYENA_PATH_LDS1D:
-            return hy::launch_lds1d_forward(p, u, gates, H, D, y, workspace, stream);
-        case HYENA_PATH_FOURSTEP1D:
-            return hy::launch_fourstep_forward(p, u, gates, H, D, y, workspace, stream);
-        case HYENA_PATH_ROWCOL2D:
-            return hy::launch_rowcol2d_forward(p, u, gates, H, D, y, workspace, stream);
-        case HYENA_PATH_ROWCOL3D:
-            return hy::launch_rowcol3d_forward(p, u, gates, H, D, y, workspace, stream);
+        case HYENA_PATH_LDS1D: return launch_lds1d_forward(p, u, gates, H, D, y, ws, stream);
+        case HYENA_PATH_FOURSTEP1D: return launch_fourstep_forward(p, u, gates, H, D, y, ws, stream);
+        case HYENA_PATH_ROWCOL2D: return launch_rowcol2d_forward(p, u, gates, H, D, y, ws, stream);
+        case HYENA_PATH_ROWCOL3D: return launch_rowcol3d_forward(p, u, gates, H, D, y, ws, stream);
         default: return fail(HYENA_ERR_UNSUPPORTED, "unknown path");
     }
+}
+
+const Plan* plan_of(hyena_plan_t plan) { return plan ? &plan->p : nullptr; }
+
+}  // namespace hy
+
+extern "C" {
+
+hyena_status hyena_forward(hyena_plan_t plan, const void* u, const void* const* gates,
+                           const void* H, const float* D, void* y, void* workspace, void* stream)
+{
+    if (plan == nullptr) return fail(HYENA_ERR_INVALID_ARGUMENT, "plan is NULL");
+    const hy::Plan& p = plan->p;
+    hyena_status st = hy::check_forward_args(p, u, gates, H, D, y, workspace);
+    if (st != HYENA_OK) return st;
+    st = check_ws(p, workspace);
+    if (st != HYENA_OK) return st;
+    return hy::run_forward(p, u, gates, H, D, y, workspace, stream);
 }
 
 hyena_status hyena_nd_mixer_forward(hyena_plan_t plan, const hyena_nd_mixer* m, const void* H,

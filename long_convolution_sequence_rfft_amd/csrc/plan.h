@@ -133,6 +133,14 @@ bool ws_record_release(const void* ws, uint64_t token);
 void ws_record_drop(uint64_t token);
 size_t ws_record_count();
 
+// api.hip: the checks and dispatch shared by hyena_forward and the
+// allocation-free hyena_forward_noalloc (static_scratch.hip).
+hyena_status check_forward_args(const Plan& p, const void* u, const void* const* gates,
+                                const void* H, const float* D, const void* y, const void* ws);
+hyena_status run_forward(const Plan& p, const void* u, const void* const* gates, const void* H,
+                         const float* D, void* y, void* ws, void* stream);
+const Plan* plan_of(hyena_plan_t plan);
+
 // Implemented in the .hip launchers.
 hyena_status launch_tw_init(const Plan& p, void* ws, void* stream);
 hyena_status launch_lds1d_spectrum(const Plan& p, const void* h, void* H, const void* ws, void* stream);

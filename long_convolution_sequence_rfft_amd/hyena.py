@@ -38,7 +38,10 @@ EXPORTED_SYMBOLS = (
     "hyena_last_error", "hyena_timing_begin", "hyena_timing_end", "hyena_timing_kernel",
     "hyena_timing_release", "hyena_implicit_scratch_bytes", "hyena_filter_spectrum_implicit",
     "hyena_plan_create_ex", "hyena_nd_mixer_forward", "hyena_workspace_release",
+    "hyena_forward_noalloc",
 )
+
+HYENA_NOALLOC_SCRATCH_BYTES = 128 << 20
 
 
 class NdMixer(ctypes.Structure):
@@ -88,6 +91,7 @@ def load():
             lib.hyena_workspace_release.argtypes = [p, p]
             lib.hyena_filter_spectrum.argtypes = [p, p, p, p, p]
             lib.hyena_forward.argtypes = [p, p, ctypes.POINTER(p), p, p, p, p, p]
+            lib.hyena_forward_noalloc.argtypes = [p, p, ctypes.POINTER(p), p, p, p, p]
             lib.hyena_spectrum_export.argtypes = [p, p, p, p]
             lib.hyena_plan_destroy.argtypes = [p]
             lib.hyena_status_string.argtypes = [ctypes.c_int]
@@ -106,7 +110,8 @@ def load():
                                                            p, p]
             for name in ("hyena_plan_create", "hyena_plan_create_ex", "hyena_plan_query",
                          "hyena_workspace_init", "hyena_workspace_release",
-                         "hyena_filter_spectrum", "hyena_forward", "hyena_spectrum_export",
+                         "hyena_filter_spectrum", "hyena_forward", "hyena_forward_noalloc",
+                         "hyena_spectrum_export",
                          "hyena_plan_destroy", "hyena_timing_begin", "hyena_timing_end",
                          "hyena_timing_kernel", "hyena_timing_release",
                          "hyena_implicit_scratch_bytes", "hyena_filter_spectrum_implicit",
@@ -181,6 +186,11 @@ def hyena_filter_spectrum(plan, h, H, workspace, stream=0):
 def hyena_forward(plan, u, gates, H, D, y, workspace, stream=0):
     arr = (ctypes.c_void_p * max(1, len(gates)))(*gates)
     return load().hyena_forward(plan, u, arr, H, D, y, workspace, stream)
+
+
+def hyena_forward_noalloc(plan, u, gates, H, D, y, stream=0):
+    arr = (ctypes.c_void_p * max(1, len(gates)))(*gates)
+    return load().hyena_forward_noalloc(plan, u, arr, H, D, y, stream)
 
 
 def hyena_implicit_scratch_bytes(plan, hidden):

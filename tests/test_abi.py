@@ -314,3 +314,25 @@ def test_nd_mixer_validation():
     assert hyena.hyena_nd_mixer_forward(p3, same, 16, 16, 4096, 16) == \
         hyena.HYENA_ERR_INVALID_ARGUMENT
     hyena.hyena_plan_destroy(p3)
+
+
+def test_noalloc_refuses_before_touching_the_gpu():
+    # the size check comes first, so these need no GPU
+    assert hyena.hyena_forward_noalloc(None, 16, [16], 16, 16, 16) == \
+        hyena.HYENA_ERR_INVALID_ARGUMENT
+    st, big = hyena.hyena_plan_create(1, 65536, 768, 2, [65536])
+    try:
+        _, ws, _ = hyena.hyena_plan_query(big)
+        assert ws > hyena.HYENA_NOALLOC_SCRATCH_BYTES
+        assert hyena.hyena_forward_noalloc(big, 16, [16, 16], 16, 16, 16) == \
+            hyena.HYENA_ERR_UNSUPPORTED
+        assert "static scratch" in hyena.hyena_last_error()
+    finally:
+        hyena.hyena_plan_destroy(big)
+    # the 2K and 8K width-768 workloads fit the array
+    for B, N, io in ((4, 2048, hyena.HYENA_F32), (2, 8192, hyena.HYENA_BF16)):
+        st, p = hyena.hyena_plan_create(B, N, 768, 2, [N], io)
+        try:
+            assert hyena.hyena_plan_query(p)[1] <= hyena.HYENA_NOALLOC_SCRATCH_BYTES
+        finally:
+            hyena.hyena_plan_destroy(p)
