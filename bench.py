@@ -37,7 +37,10 @@ HBM_PEAK_GBPS = 8000.0
 # compiled that way):
 # 256 CUs x 4 SIMDs x 16 lanes x 2 flop (FMA) x 2.4 GHz
 ALU_PEAK_TFLOPS = 256 * 4 * 16 * 2 * 2.4e9 / 1e12
+# MI355X's published dense fp32 vector figure (with packed FP32), for context
+FP32_PUBLISHED_TFLOPS = 157.3
 HEADLINE = 2
+SECOND = 3  # the metric's second length (64K tokens)
 ORDER_OF_RUN = [2, 1, 3, 4, 5]
 
 
@@ -231,6 +234,21 @@ def run_workload(idx, steps, warmup, min_rotation_bytes=600 << 20):
     # its own pair of events on that stream (hyena_timing_*): per-kernel
     # launch durations.  The event markers add a few microseconds between
     # launches, so the whole-job time above comes from the clean region.
+    # Per-step distribution: the same `steps` forwards with an event between
+    # consecutive steps (one marker per step; the whole-job time above stays
+    # the clean region's).
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    marks[0].record()
+    for i in range(steps):
+        step(i)
+        marks[i + 1].record()
+    torch.cuda.synchronize()
+    step_ms = sorted(marks[i].elapsed_time(marks[i + 1]) for i in range(steps))
+
+    def pct(q):
+        # nearest-rank percentile of the per-step times
+        return step_ms[min(len(step_ms) - 1, max(0, int(math.ceil(q * len(step_ms))) - 1))]
+
     hyena.hyena_timing_begin(steps * 64)
     start2, stop2 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start2.record()
@@ -255,6 +273,7 @@ def run_workload(idx, steps, warmup, min_rotation_bytes=600 << 20):
         "dims": list(dims), "storage": cfg["dtype"],
         "spectrum": "bf16" if spec_dtype == hyena.HYENA_BF16 else "f32",
         "ms_per_step": ms,
+        "step_ms_p10": pct(0.10), "step_ms_p50": pct(0.50), "step_ms_p90": pct(0.90),
         "tc_per_s": tc / (ms * 1e-3),
         "spectrum_ms": spectrum_ms,
         "implicit_spectrum_ms": implicit_ms,
@@ -350,14 +369,22 @@ def roofline_of(res):
     t_alu = per_launch_f / (ALU_PEAK_TFLOPS * 1e12)
     out = {"kernel": name, "launches_per_forward": k["launches_per_forward"],
            "avg_launch_us": round(k["avg_launch_ms"] * 1e3, 2)}
+    a_alu = per_launch_f / sec / 1e12
+    a_hbm = per_launch_b / sec / 1e9
     if t_alu >= t_hbm:
-        a = per_launch_f / sec / 1e12
-        out.update({"bound": "alu", "achieved": round(a, 3), "peak": round(ALU_PEAK_TFLOPS, 2),
-                    "unit": "TFLOP/s", "frac": round(a / ALU_PEAK_TFLOPS, 4)})
+        out.update({"bound": "alu", "achieved": round(a_alu, 3), "peak": round(ALU_PEAK_TFLOPS, 2),
+                    "unit": "TFLOP/s", "frac": round(a_alu / ALU_PEAK_TFLOPS, 4),
+                    "peak_kind": "fp32 VALU without packed-FP32 instructions "
+                                 "(256 CU x 4 SIMD x 16 lanes x 2 flop x 2.4 GHz)",
+                    "frac_of_published_fp32": round(a_alu / FP32_PUBLISHED_TFLOPS, 4)})
     else:
-        a = per_launch_b / sec / 1e9
-        out.update({"bound": "hbm", "achieved": round(a, 1), "peak": HBM_PEAK_GBPS,
-                    "unit": "GB/s", "frac": round(a / HBM_PEAK_GBPS, 4)})
+        out.update({"bound": "hbm", "achieved": round(a_hbm, 1), "peak": HBM_PEAK_GBPS,
+                    "unit": "GB/s", "frac": round(a_hbm / HBM_PEAK_GBPS, 4)})
+    # the metric's own roofline (HBM), whatever bounds the kernel
+    out["hbm"] = {"achieved": round(a_hbm, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                  "frac": round(a_hbm / HBM_PEAK_GBPS, 4)}
+    out["alu"] = {"achieved": round(a_alu, 3), "peak": round(ALU_PEAK_TFLOPS, 2),
+                  "unit": "TFLOP/s", "frac": round(a_alu / ALU_PEAK_TFLOPS, 4)}
     out["algorithmic_per_launch"] = {"flops": per_launch_f, "bytes": per_launch_b}
     out["traffic"] = traffic
     return out
@@ -371,7 +398,7 @@ def cpu_baseline(idx, max_channels, min_seconds=10.0, max_seconds=30.0):
     """The float64 oracle on the workload's first `max_channels` channels (all
     tokens), repeated until about `min_seconds` of wall time have passed."""
     import oracle
-    from long_convolution_sequence_rfft_amd.synth import WORKLOADS
+    from long_convolution_sequence_rfft_amd.synth import WORKLOADS, WORKLOAD_NAMES
     cfg = WORKLOADS[idx]
     inp = make_inputs(idx, seed=idx)
     ch = np.arange(min(max_channels, cfg["d"]))
@@ -391,13 +418,54 @@ def cpu_baseline(idx, max_channels, min_seconds=10.0, max_seconds=30.0):
             break
     tc = tokens * len(ch) * reps
     return {"value": tc / dt, "unit": "token·channels/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
+            "kind": "oracle", "workload": WORKLOAD_NAMES[idx], **host_info(),
             "sample": f"{len(ch)} of {cfg['d']} channels, all {tokens} tokens per channel, "
                       f"{'direct Toeplitz sum' if method == oracle.DIRECT else 'radix-2 FFT'}"
                       f" route, float64, {reps} repetitions; {dt:.1f} s wall"}
 
 
+def host_info():
+    """The host the oracle ran on: CPUs this process may use, the CPU model,
+    and the OpenMP thread setting."""
+    model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        affinity = os.cpu_count()
+    return {"host_cpus_available": affinity, "cpu_model": model,
+            "omp_num_threads_env": os.environ.get("OMP_NUM_THREADS")}
+
+
 # ---------------------------------------------------------------------------
+
+def copy_rate(mib=1024, reps=10):
+    """Device-to-device copy rate of a plain contiguous copy (torch), GB/s of
+    bytes read plus written: the practical streaming rate, as context."""
+    import torch
+    n = (mib << 20) // 4
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del a, b
+    torch.cuda.empty_cache()
+    return {"bytes_moved": 2 * (mib << 20), "GBps": round(2 * (mib << 20) / (ms * 1e-3) / 1e9, 1),
+            "kind": "torch copy_, float32, read + write"}
+
 
 def copy_calibration(mb):
     """A plain elementwise kernel of known traffic (reads mb MiB, writes mb MiB;
@@ -455,10 +523,17 @@ def main():
     head = results[head_idx]
 
     cpu = None
+    cpu_64k = None
     if not args.no_cpu_baseline:
         log("[bench] CPU baseline (oracle) ...")
         cpu = cpu_baseline(head_idx, args.cpu_channels)
         log(f"[bench] oracle: {cpu['value'] / 1e6:.2f} M tc/s on {cpu['cores']} threads")
+        if SECOND in results and SECOND != head_idx:
+            # the metric names both lengths: the oracle at 64K tokens too
+            cpu_64k = cpu_baseline(SECOND, args.cpu_channels)
+            log(f"[bench] oracle at 64K: {cpu_64k['value'] / 1e6:.2f} M tc/s")
+    copy = copy_rate()
+    log(f"[bench] plain copy: {copy['GBps']:.0f} GB/s")
 
     workloads = {}
     for idx, r in results.items():
@@ -477,6 +552,7 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
+        "storage_dtype": head["storage"],
         "data": "synthetic (seeded; damped-sinusoid filters, N(0,1) activations)",
         "config": {"workload": head["workload"], "B": head["B"], "dims": head["dims"],
                    "d": head["d"], "order": head["order"], "storage": head["storage"],
@@ -484,8 +560,19 @@ def main():
                    "parallelism": "single GPU"},
         "hbm": {"achieved": round(head["hbm_GBps"], 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(head["hbm_frac"], 4)},
+        "step_ms": {"p10": head["step_ms_p10"], "p50": head["step_ms_p50"],
+                    "p90": head["step_ms_p90"]},
         "roofline": roofline_of(head),
+        "roofline_hbm": roofline_of(head)["hbm"],
         "cpu_baseline": cpu,
+        "cpu_baseline_64k": cpu_64k,
+        "plain_copy": copy,
+        "second_length": ({"workload": results[SECOND]["workload"],
+                           "value": results[SECOND]["tc_per_s"],
+                           "ms_per_step": results[SECOND]["ms_per_step"],
+                           "hbm_frac": round(results[SECOND]["hbm_frac"], 4),
+                           "roofline": roofline_of(results[SECOND])}
+                          if SECOND in results else None),
         "workloads": workloads,
         "kernel_source_sha": kernel_source_sha(),
     }

@@ -72,3 +72,24 @@ def test_more_than_one_gpu_is_refused():
     assert out.returncode == 2
     msg = json.loads(out.stdout.strip().splitlines()[-1])
     assert "one GPU" in msg["error"]
+
+
+def test_roofline_reports_the_hbm_fraction_beside_the_alu_one():
+    cfg = WORKLOADS[2]
+    name = "hy::hyena_lds1d_real_forward<8192, unsigned short, unsigned short, false>"
+    res = {"cfg": cfg, "workload": "no-such-workload",
+           "kernels": {name: {"launches_per_forward": 1.0, "avg_launch_ms": 0.1,
+                              "ms_per_forward": 0.1}}}
+    r = bench.roofline_of(res)
+    gbps = bench.algorithmic_bytes(cfg, "bf16") / 1e-4 / 1e9
+    assert abs(r["hbm"]["achieved"] - gbps) < 0.1
+    assert abs(r["hbm"]["frac"] - gbps / 8000.0) < 1e-4
+    assert r["alu"]["frac"] == r["frac"]
+    assert "packed" in r["peak_kind"]
+    assert abs(r["frac_of_published_fp32"] - r["achieved"] / 157.3) < 1e-3
+
+
+def test_host_info_fields():
+    info = bench.host_info()
+    assert info["host_cpus_available"] >= 1
+    assert set(info) == {"host_cpus_available", "cpu_model", "omp_num_threads_env"}
