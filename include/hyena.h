@@ -107,8 +107,8 @@ typedef enum hyena_path {
  * ndims = 1: dims = {N}, 4 <= N <= 2097152 (any N; M is the power of two
  *            >= 2N; N == the N argument).  M <= 16384 runs in one workgroup
  *            per channel (pair); longer transforms take the four-step path.
- * ndims = 2: dims = {X, Y}, X and Y powers of two in [4, 512]; N must equal
- *            X * Y.
+ * ndims = 2: dims = {X, Y}, X and Y powers of two in [4, 1024]; N must equal
+ *            X * Y (and N * d * 4 below 2^31).
  * ndims = 3: dims = {X, Y, Z}, powers of two in [4, 256], X * Y * Z <= 2^20;
  *            N must equal X * Y * Z.
  * io_dtype, spectrum_dtype: hyena_dtype values.  path: hyena_path value.

@@ -5,9 +5,9 @@
 
 namespace hy {
 
-HY_MP_LENGTHS(HY_MP_OUTER_INST, float, extern)
-HY_MP_LENGTHS(HY_MP_OUTER_INST, uint16_t, extern)
-HY_MP_LENGTHS(HY_MP_OUTER_INST, _Float16, extern)
+HY_MP_OUTER_LENGTHS(HY_MP_OUTER_INST, float, extern)
+HY_MP_OUTER_LENGTHS(HY_MP_OUTER_INST, uint16_t, extern)
+HY_MP_OUTER_LENGTHS(HY_MP_OUTER_INST, _Float16, extern)
 HY_MP_INNER_LENGTHS(HY_MP_INNER_INST, float, extern)
 HY_MP_INNER_LENGTHS(HY_MP_INNER_INST, uint16_t, extern)
 HY_MP_LENGTHS(HY_MP_MID_INST, 0, extern)
@@ -72,17 +72,25 @@ MpGeom base_geom(const Plan& p)
 template <typename IO>
 hyena_status outer_go(int L, int mode, bool half_spec, const OuterArgs& a, int64_t nb, hipStream_t s)
 {
+    const bool paired = a.g.three_d == 0;
     switch (L) {
-#define HY_CASE(LL, A_, B_)                                                                 \
-    case LL:                                                                                \
-        if (mode == OUTER_IN) return mp_outer_launch<LL, IO, OUTER_IN, true>(a, nb, s);     \
-        if (mode == OUTER_MID) return mp_outer_launch<LL, IO, OUTER_MID, true>(a, nb, s);   \
-        if (mode == OUTER_OUT) return mp_outer_launch<LL, IO, OUTER_OUT, true>(a, nb, s);   \
-        if (mode == OUTER_IN3) return mp_outer_launch<LL, IO, OUTER_IN3, true>(a, nb, s);   \
-        if (mode == OUTER_OUT3) return mp_outer_launch<LL, IO, OUTER_OUT3, true>(a, nb, s); \
-        if (half_spec) return mp_outer_launch<LL, IO, OUTER_SPEC, true>(a, nb, s);          \
-        return mp_outer_launch<LL, IO, OUTER_SPEC, false>(a, nb, s);
-        HY_MP_LENGTHS(HY_CASE, 0, 0)
+#define HY_CASE(LL, A_, B_)                                                                        \
+    case LL:                                                                                       \
+        if (mode == OUTER_IN3) return mp_outer_launch<LL, IO, OUTER_IN3, true, false>(a, nb, s);   \
+        if (mode == OUTER_OUT3) return mp_outer_launch<LL, IO, OUTER_OUT3, true, false>(a, nb, s); \
+        if (paired) {                                                                              \
+            if (mode == OUTER_IN) return mp_outer_launch<LL, IO, OUTER_IN, true, true>(a, nb, s);   \
+            if (mode == OUTER_MID) return mp_outer_launch<LL, IO, OUTER_MID, true, true>(a, nb, s); \
+            if (mode == OUTER_OUT) return mp_outer_launch<LL, IO, OUTER_OUT, true, true>(a, nb, s); \
+            if (half_spec) return mp_outer_launch<LL, IO, OUTER_SPEC, true, true>(a, nb, s);        \
+            return mp_outer_launch<LL, IO, OUTER_SPEC, false, true>(a, nb, s);                      \
+        }                                                                                          \
+        if (mode == OUTER_IN) return mp_outer_launch<LL, IO, OUTER_IN, true, false>(a, nb, s);     \
+        if (mode == OUTER_MID) return mp_outer_launch<LL, IO, OUTER_MID, true, false>(a, nb, s);   \
+        if (mode == OUTER_OUT) return mp_outer_launch<LL, IO, OUTER_OUT, true, false>(a, nb, s);   \
+        if (!half_spec) return mp_outer_launch<LL, IO, OUTER_SPEC, false, false>(a, nb, s);        \
+        return fail(HYENA_ERR_UNSUPPORTED, "multi-pass: no half-input spectrum pass on 3D grids");
+        HY_MP_OUTER_LENGTHS(HY_CASE, 0, 0)
 #undef HY_CASE
         default: return fail(HYENA_ERR_UNSUPPORTED, "multi-pass: unsupported outer length");
     }

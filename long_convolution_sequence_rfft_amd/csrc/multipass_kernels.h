@@ -158,8 +158,36 @@ __device__ __forceinline__ void act_store(IO* base, int64_t row, int64_t c0, int
     }
 }
 
+// Accesses to the intermediate F: plain, or carrying the nontemporal hint
+// (HY_F_NT bit 0 on loads, bit 1 on stores), fixed at build time.
+#ifndef HY_F_NT
+#define HY_F_NT 0
+#endif
+typedef float f2vec __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float2 f_load(const float2* p)
+{
+    if constexpr ((HY_F_NT & 1) != 0) {
+        const f2vec t = __builtin_nontemporal_load(reinterpret_cast<const f2vec*>(p));
+        return make_float2(t.x, t.y);
+    } else {
+        return *p;
+    }
+}
+__device__ __forceinline__ void f_store(float2* p, float2 v)
+{
+    if constexpr ((HY_F_NT & 2) != 0) {
+        f2vec t;
+        t.x = v.x;
+        t.y = v.y;
+        __builtin_nontemporal_store(t, reinterpret_cast<f2vec*>(p));
+    } else {
+        *p = v;
+    }
+}
+
 // One outer column of F in the last-pass register layout of a length-L
-// transform: v[q RL + r] <-> bin (tau + q T) + r L/RL.  With `tw`, bins are
+// transform: v[q RL + r] <-> bin (tau + q T) + r L/RL, in natural bin order
+// (the 3D path, whose middle pass reads these rows).  With `tw`, bins are
 // multiplied by the four-step twiddle twstep[bin] (conjugated for DIR = +1,
 // the inverse direction).  All loads are issued before any is used.
 template <int L, int DIR>
@@ -176,7 +204,7 @@ __device__ __forceinline__ void load_column(float2* v, const float2* Fcol, const
 #pragma unroll
     for (int q = 0; q < QL; ++q)
 #pragma unroll
-        for (int r = 0; r < RL; ++r) v[q * RL + r] = Fcol[tau + q * T + r * (L / RL)];
+        for (int r = 0; r < RL; ++r) v[q * RL + r] = f_load(&Fcol[tau + q * T + r * (L / RL)]);
     if (tw) {
         float2 w[S::PTS];
 #pragma unroll
@@ -204,12 +232,174 @@ __device__ __forceinline__ void store_column(const float2* v, float2* Fcol, cons
         for (int q = 0; q < QL; ++q)
 #pragma unroll
             for (int r = 0; r < RL; ++r)
-                Fcol[tau + q * T + r * (L / RL)] = ctw<-1>(v[q * RL + r], w[q * RL + r]);
+                f_store(&Fcol[tau + q * T + r * (L / RL)], ctw<-1>(v[q * RL + r], w[q * RL + r]));
     } else {
 #pragma unroll
         for (int q = 0; q < QL; ++q)
 #pragma unroll
-            for (int r = 0; r < RL; ++r) Fcol[tau + q * T + r * (L / RL)] = v[q * RL + r];
+            for (int r = 0; r < RL; ++r) f_store(&Fcol[tau + q * T + r * (L / RL)], v[q * RL + r]);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Mirror-paired F rows (1D and 2D paths).  An F row holds the L outer bins of
+// one inner position with every bin beside its mirror (L - a) mod L: bins 0
+// and L/2 at positions 0 and 1, and for 0 < a < L/2 bin a at 2a, bin L - a
+// at 2a + 1.  The inner pass takes each bin with its mirror, so its
+// workgroups read and write whole cache lines (in natural order the mirrors
+// of an aligned run of columns straddle two lines, each shared with another
+// workgroup).  The outer pass runs its last forward pass (and the inverse's
+// first) on butterflies j1 = tau, j2 = 2T - tau (j2 = T for tau = 0), as the
+// single-workgroup kernels do, so each thread holds bin pairs and moves each
+// pair as one 16-byte access.
+//
+// Registers: v[s] = bin j1 + s L/RL, v[RL + s] = bin j2 + s L/RL.  Slot s of
+// thread tau > 0 pairs v[s] (bin a = tau + s L/RL) with v[2RL-1-s] (bin
+// L - a), at position 2a (s < RL/2, lower bin first) or 2 (L - a) (mirror
+// first).  Thread 0 holds the self-mirrored butterflies 0 and T: slot
+// s < RL/2 pairs v[RL+s] with v[2RL-1-s] (bins T + s L/RL and its mirror),
+// slot RL/2 packs bins 0 and L/2 (v[0], v[RL/2]) at position 0, slots
+// s > RL/2 pair v[RL-s] with v[s].  Every lane runs the same instructions;
+// thread 0 differs only through selects.
+// ---------------------------------------------------------------------------
+template <int L>
+struct PairSlot {
+    float2 lo, hi;  // the two values as stored: position p and p + 1
+    int pos;        // float2 position of lo
+};
+
+template <int L>
+__device__ __forceinline__ PairSlot<L> pair_slot(const float2* v, int tau, int s)
+{
+    using S = FftShape<L>;
+    constexpr int T = S::T, RL = S::RL, NSL = L / RL, H = RL / 2;
+    const bool t0 = tau == 0;
+    PairSlot<L> r;
+    if (s < H) {
+        const float2 A = t0 ? v[RL + s] : v[s];
+        r.lo = A;
+        r.hi = v[2 * RL - 1 - s];
+        r.pos = 2 * ((t0 ? T : tau) + s * NSL);
+    } else {
+        const float2 B = t0 ? (s == H ? v[0] : v[RL - s]) : v[2 * RL - 1 - s];
+        r.lo = B;
+        r.hi = v[s];
+        r.pos = (t0 && s == H) ? 0 : 2 * (L - tau - s * NSL);
+    }
+    return r;
+}
+
+// Bin index of the value stored at pos + k (k = 0, 1) of slot s: for the
+// four-step twiddles, which depend on the bin.
+template <int L>
+__device__ __forceinline__ void pair_bins(int tau, int s, int& bin_lo, int& bin_hi)
+{
+    using S = FftShape<L>;
+    constexpr int T = S::T, RL = S::RL, NSL = L / RL, H = RL / 2;
+    const bool t0 = tau == 0;
+    if (s < H) {
+        bin_lo = (t0 ? T : tau) + s * NSL;
+        bin_hi = L - bin_lo;
+    } else if (t0 && s == H) {
+        bin_lo = 0;
+        bin_hi = L / 2;
+    } else {
+        bin_hi = tau + s * NSL;
+        bin_lo = L - bin_hi;
+    }
+}
+
+typedef float f4vec __attribute__((ext_vector_type(4)));
+
+// Store the forward transform's outputs (registers as above) to an F row,
+// times the four-step twiddle of each bin when `tw`.
+// Frow and the twiddle table never overlap (the table lives at the start of
+// the workspace, the rows after it), so twiddle loads may move ahead of the
+// stores.
+template <int L>
+__device__ __forceinline__ void store_pairs(const float2* v, float2* __restrict__ Frow,
+                                            const float2* __restrict__ twstep, int tau, bool tw)
+{
+    constexpr int RL = FftShape<L>::RL;
+    // slots in groups of G: the group's twiddle loads are all issued before
+    // its first store, so their latencies overlap (per slot they would not:
+    // the compiler keeps loads behind earlier stores)
+    constexpr int G = RL < 8 ? RL : 8;
+#pragma unroll
+    for (int s0 = 0; s0 < RL; s0 += G) {
+        float2 wlo[G], whi[G];
+        if (tw) {
+#pragma unroll
+            for (int i = 0; i < G; ++i) {
+                int blo, bhi;
+                pair_bins<L>(tau, s0 + i, blo, bhi);
+                wlo[i] = twstep[blo];
+                whi[i] = twstep[bhi];
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < G; ++i) {
+            PairSlot<L> p = pair_slot<L>(v, tau, s0 + i);
+            if (tw) {
+                p.lo = ctw<-1>(p.lo, wlo[i]);
+                p.hi = ctw<-1>(p.hi, whi[i]);
+            }
+            f4vec t;
+            t.x = p.lo.x;
+            t.y = p.lo.y;
+            t.z = p.hi.x;
+            t.w = p.hi.y;
+            if constexpr ((HY_F_NT & 2) != 0)
+                __builtin_nontemporal_store(t, reinterpret_cast<f4vec*>(Frow + p.pos));
+            else
+                *reinterpret_cast<f4vec*>(Frow + p.pos) = t;
+        }
+    }
+}
+
+// Load an F row into the inverse's first-pass registers (the layout
+// store_pairs reads), times the conjugate four-step twiddle when `tw`.
+template <int L>
+__device__ __forceinline__ void load_pairs(float2* v, const float2* Frow, const float2* twstep,
+                                           int tau, bool live, bool tw)
+{
+    using S = FftShape<L>;
+    constexpr int RL = S::RL, H = RL / 2;
+    const bool t0 = tau == 0;
+    float2 lo[RL], hi[RL];
+#pragma unroll
+    for (int s = 0; s < RL; ++s) {
+        int pos;
+        if (s < H) pos = 2 * ((t0 ? S::T : tau) + s * (L / RL));
+        else pos = (t0 && s == H) ? 0 : 2 * (L - tau - s * (L / RL));
+        f4vec t = {0.0f, 0.0f, 0.0f, 0.0f};
+        if (live) {
+            if constexpr ((HY_F_NT & 1) != 0)
+                t = __builtin_nontemporal_load(reinterpret_cast<const f4vec*>(Frow + pos));
+            else
+                t = *reinterpret_cast<const f4vec*>(Frow + pos);
+        }
+        lo[s] = make_float2(t.x, t.y);
+        hi[s] = make_float2(t.z, t.w);
+    }
+    if (tw && live) {
+#pragma unroll
+        for (int s = 0; s < RL; ++s) {
+            int blo, bhi;
+            pair_bins<L>(tau, s, blo, bhi);
+            lo[s] = ctw<+1>(lo[s], twstep[blo]);
+            hi[s] = ctw<+1>(hi[s], twstep[bhi]);
+        }
+    }
+    // general: v[s] = A of slot s (hi for s >= RL/2, lo below), v[2RL-1-s] =
+    // the other.  Thread 0: v[0] = lo of slot RL/2, v[s] (0 < s < RL/2) = lo
+    // of slot RL - s, v[RL + s] (s < RL/2) = lo of slot s.
+#pragma unroll
+    for (int s = 0; s < H; ++s) {
+        v[s] = t0 ? (s == 0 ? lo[H] : lo[RL - s]) : lo[s];
+        v[RL + s] = t0 ? lo[s] : lo[RL - 1 - s];
+        v[H + s] = hi[H + s];
+        v[2 * RL - 1 - s] = hi[s];
     }
 }
 
@@ -217,7 +407,9 @@ __device__ __forceinline__ void store_column(const float2* v, float2* Fcol, cons
 // Outer pass.  Workgroup = KP pair slots x C outer columns (C KP = NF).
 // blockIdx.x = column block * ngroups + group-in-chunk.
 // ---------------------------------------------------------------------------
-template <int LA, typename IO, int MODE, bool HALF_SPEC>
+// PAIRED: the 1D and 2D paths, whose F rows hold mirror pairs (load_pairs);
+// the 3D path keeps natural bin order for its middle pass.
+template <int LA, typename IO, int MODE, bool HALF_SPEC, bool PAIRED>
 __global__ void __launch_bounds__(kMpThreads, 2) hyena_mp_outer(OuterArgs a)
 {
     using S = FftShape<LA>;
@@ -236,6 +428,11 @@ __global__ void __launch_bounds__(kMpThreads, 2) hyena_mp_outer(OuterArgs a)
     const int cb = blockIdx.x / g.ngroups;
     const int kp = f & (KP - 1);
     const int o = cb * C + (f >> g.kp_log2);  // this transform's outer column
+    // 1D and 2D: F rows hold mirror pairs, and the last forward / first
+    // inverse pass runs on butterflies tau and 2T - tau (see load_pairs)
+    constexpr bool paired = PAIRED;
+    static_assert(!PAIRED || (MODE != OUTER_IN3 && MODE != OUTER_OUT3), "3D modes keep natural rows");
+    const int j1 = tau, j2 = tau ? 2 * TA - tau : TA;
     constexpr bool IN = MODE == OUTER_IN || MODE == OUTER_IN3;
     constexpr bool OUT = MODE == OUTER_OUT || MODE == OUTER_OUT3;
     const int n_outer = MODE == OUTER_SPEC ? g.Lb : g.Lb_live;
@@ -390,7 +587,8 @@ __global__ void __launch_bounds__(kMpThreads, 2) hyena_mp_outer(OuterArgs a)
         // bins).  The gate tile is fetched next, so its latency overlaps the
         // inverse outer DFT.
         static_assert(GT >= 1 && (LA / 2) * NF % kMpThreads == 0, "gate tile");
-        load_column<LA, +1>(v, Fcol, twstep, tau, col_live, g.four_step && o > 0);
+        if (paired) load_pairs<LA>(v, Fcol, twstep, tau, col_live, g.four_step && o > 0);
+        else load_column<LA, +1>(v, Fcol, twstep, tau, col_live, g.four_step && o > 0);
         const IO* gate = static_cast<const IO*>(a.act);
         float2 gval[GT];
         if constexpr (MODE == OUTER_OUT3) {
@@ -432,7 +630,8 @@ __global__ void __launch_bounds__(kMpThreads, 2) hyena_mp_outer(OuterArgs a)
                 gval[it] = ok ? act_load<IO>(gate, row, 2 * pq, g.d) : make_float2(0.0f, 0.0f);
             });
         }
-        inv_lds_to_regs<LA, true, true>(v, re, im, a.tw, g.tw_a, tau);
+        if (paired) inv_transform<LA, true>(v, re, im, a.tw, g.tw_a, tau, j1, j2, [] {});
+        else inv_lds_to_regs<LA, true, true>(v, re, im, a.tw, g.tw_a, tau);
         __syncthreads();
         tile_rows([&](int it, int fq, int s, int64_t, bool, int64_t) {
             sre[fq * LW + lpad(s)] = gval[it].x;
@@ -462,8 +661,13 @@ __global__ void __launch_bounds__(kMpThreads, 2) hyena_mp_outer(OuterArgs a)
 
     // forward outer DFT -> (twiddle) -> F column, straight from the last
     // pass's registers (lanes of a transform hold consecutive bins)
-    fwd_regs_to_lds<LA, HALF_IN, true>(v, re, im, a.tw, g.tw_a, tau);
-    if (col_live) store_column<LA>(v, Fcol, twstep, tau, g.four_step && o > 0);
+    if (paired) {
+        fwd_transform<LA, HALF_IN>(v, re, im, a.tw, g.tw_a, tau, j1, j2, false, [] {});
+        if (col_live) store_pairs<LA>(v, Fcol, twstep, tau, g.four_step && o > 0);
+    } else {
+        fwd_regs_to_lds<LA, HALF_IN, true>(v, re, im, a.tw, g.tw_a, tau);
+        if (col_live) store_column<LA>(v, Fcol, twstep, tau, g.four_step && o > 0);
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -601,7 +805,11 @@ __global__ void __launch_bounds__(kMpThreads, 2) hyena_mp_inner(InnerArgs a)
 
     // units of this workgroup: kk0 .. kk0 + nu - 1 (nu <= U)
     const int nu = min(U, La / 2 - kk0);
+    // F position of (unit, side): on the 1D and 2D paths the outer pass
+    // stores a bin next to its mirror (fpos), so unit kk sits at 2 kk and
+    // 2 kk + 1; 3D intermediates keep the composite bins in natural order
     auto col_of = [&](int u, int side) {
+        if (!g.three_d) return 2 * (kk0 + u) + side;
         int c0, c1;
         bool sf;
         unit_columns(g, kk0 + u, c0, c1, sf);
@@ -640,18 +848,20 @@ __global__ void __launch_bounds__(kMpThreads, 2) hyena_mp_inner(InnerArgs a)
     static_assert(NLIVE * 2 * U % kMpThreads == 0, "inner tile split");
     // fast path: 2U divides the thread count, so a thread's (unit, side) --
     // hence its column -- is the same in every iteration; inner positions
-    // step by kMpThreads / (2U)
+    // step by kMpThreads / (2U).  Neighbouring lanes take the two sides of a
+    // unit, then the next unit: consecutive F positions on the 1D and 2D
+    // paths, and consecutive LDS regions.
     static_assert(kMpThreads % (2 * U) == 0, "inner tile rows");
     constexpr int OPS = kMpThreads / (2 * U);
-    const int u_t = (int)threadIdx.x % U;
-    const int side_t = ((int)threadIdx.x / U) & 1;
+    const int u_t = ((int)threadIdx.x >> 1) % U;
+    const int side_t = (int)threadIdx.x & 1;
     const int op_t = (int)threadIdx.x / (2 * U);
     const int fq_t = 2 * u_t + side_t;
     if (nu == U) {
         const float2* src = Fp + col_of(u_t, side_t);
         float2 xin[PER];
 #pragma unroll
-        for (int it = 0; it < PER; ++it) xin[it] = src[(int64_t)(op_t + it * OPS) * La];
+        for (int it = 0; it < PER; ++it) xin[it] = f_load(&src[(int64_t)(op_t + it * OPS) * La]);
 #pragma unroll
         for (int it = 0; it < PER; ++it) {
             sre[fq_t * LW + lpad(op_t + it * OPS)] = xin[it].x;
@@ -660,10 +870,10 @@ __global__ void __launch_bounds__(kMpThreads, 2) hyena_mp_inner(InnerArgs a)
     } else {
         const int total = nlive * nu * 2;
         for (int idx = threadIdx.x; idx < total; idx += kMpThreads) {
-            const int u = idx % nu;
-            const int side = (idx / nu) & 1;
+            const int u = (idx >> 1) % nu;
+            const int side = idx & 1;
             const int op = idx / (2 * nu);
-            const float2 x = Fp[(int64_t)op * La + col_of(u, side)];
+            const float2 x = f_load(&Fp[(int64_t)op * La + col_of(u, side)]);
             const int fq = 2 * u + side;
             sre[fq * LW + lpad(op)] = x.x;
             sim[fq * LW + lpad(op)] = x.y;
@@ -742,16 +952,16 @@ __global__ void __launch_bounds__(kMpThreads, 2) hyena_mp_inner(InnerArgs a)
             xout[it] = make_float2(sre[fq_t * LW + lpad(op_t + it * OPS)],
                                    sim[fq_t * LW + lpad(op_t + it * OPS)]);
 #pragma unroll
-        for (int it = 0; it < PER; ++it) dst[(int64_t)(op_t + it * OPS) * La] = xout[it];
+        for (int it = 0; it < PER; ++it) f_store(&dst[(int64_t)(op_t + it * OPS) * La], xout[it]);
     } else {
         const int total_out = g.Lb_live * nu * 2;
         for (int idx = threadIdx.x; idx < total_out; idx += kMpThreads) {
-            const int u = idx % nu;
-            const int side = (idx / nu) & 1;
+            const int u = (idx >> 1) % nu;
+            const int side = idx & 1;
             const int op = idx / (2 * nu);
             const int fq = 2 * u + side;
-            Fp[(int64_t)op * La + col_of(u, side)] =
-                make_float2(sre[fq * LW + lpad(op)], sim[fq * LW + lpad(op)]);
+            f_store(&Fp[(int64_t)op * La + col_of(u, side)],
+                    make_float2(sre[fq * LW + lpad(op)], sim[fq * LW + lpad(op)]));
         }
     }
 }
@@ -845,11 +1055,13 @@ __global__ void __launch_bounds__(kMpThreads, 2) hyena_mp_mid(MidArgs a)
 
 namespace hy {
 
-template <int LA, typename IO, int MODE, bool HALF_SPEC>
+template <int LA, typename IO, int MODE, bool HALF_SPEC, bool PAIRED>
 hyena_status mp_outer_launch(const OuterArgs& a, int64_t nblocks, hipStream_t s)
 {
-    HY_LAUNCH(kernel_label("hyena_mp_outer", LA, type_label<IO>(), MODE, HALF_SPEC),
-              (hyena_mp_outer<LA, IO, MODE, HALF_SPEC>), dim3((unsigned)nblocks), dim3(kMpThreads),
+    if (PAIRED == (a.g.three_d != 0))
+        return fail(HYENA_ERR_UNSUPPORTED, "multi-pass: outer row layout does not match the path");
+    HY_LAUNCH(kernel_label("hyena_mp_outer", LA, type_label<IO>(), MODE, HALF_SPEC, PAIRED),
+              (hyena_mp_outer<LA, IO, MODE, HALF_SPEC, PAIRED>), dim3((unsigned)nblocks), dim3(kMpThreads),
               0, s, a);
     const hipError_t e = hipGetLastError();
     return e == hipSuccess ? HYENA_OK : fail(HYENA_ERR_DEVICE, hipGetErrorString(e));
@@ -879,22 +1091,25 @@ hyena_status mp_mid_launch(const MidArgs& a, int64_t nblocks, hipStream_t s)
 // inner (F-facing) passes also come in 2048 and 4096 points: four-step
 // transforms up to 1024 x 4096
 #define HY_MP_INNER_LENGTHS(X, A, B) HY_MP_LENGTHS(X, A, B) X(2048, A, B) X(4096, A, B)
+// outer passes also come in 2048 points: 2D grids with sides up to 1024
+// (transforms of 2048 points along either axis)
+#define HY_MP_OUTER_LENGTHS(X, A, B) HY_MP_LENGTHS(X, A, B) X(2048, A, B)
 
-#define HY_MP_OUTER_INST(L, IO, EXT)                                                          \
-    EXT template hyena_status mp_outer_launch<L, IO, OUTER_IN, true>(const OuterArgs&,        \
-                                                                     int64_t, hipStream_t);   \
-    EXT template hyena_status mp_outer_launch<L, IO, OUTER_MID, true>(const OuterArgs&,       \
-                                                                      int64_t, hipStream_t);  \
-    EXT template hyena_status mp_outer_launch<L, IO, OUTER_OUT, true>(const OuterArgs&,       \
-                                                                      int64_t, hipStream_t);  \
-    EXT template hyena_status mp_outer_launch<L, IO, OUTER_SPEC, true>(const OuterArgs&,      \
-                                                                       int64_t, hipStream_t); \
-    EXT template hyena_status mp_outer_launch<L, IO, OUTER_SPEC, false>(const OuterArgs&,     \
-                                                                        int64_t, hipStream_t); \
-    EXT template hyena_status mp_outer_launch<L, IO, OUTER_IN3, true>(const OuterArgs&,       \
-                                                                      int64_t, hipStream_t);  \
-    EXT template hyena_status mp_outer_launch<L, IO, OUTER_OUT3, true>(const OuterArgs&,      \
-                                                                       int64_t, hipStream_t);
+#define HY_MP_OUTER_ONE(L, IO, MODE, HS, PR, EXT) \
+    EXT template hyena_status mp_outer_launch<L, IO, MODE, HS, PR>(const OuterArgs&, int64_t, hipStream_t);
+// 1D / 2D (mirror-paired rows) and 3D (natural rows, and the mixer's modes)
+#define HY_MP_OUTER_INST(L, IO, EXT)                   \
+    HY_MP_OUTER_ONE(L, IO, OUTER_IN, true, true, EXT)    \
+    HY_MP_OUTER_ONE(L, IO, OUTER_MID, true, true, EXT)   \
+    HY_MP_OUTER_ONE(L, IO, OUTER_OUT, true, true, EXT)   \
+    HY_MP_OUTER_ONE(L, IO, OUTER_SPEC, true, true, EXT)  \
+    HY_MP_OUTER_ONE(L, IO, OUTER_SPEC, false, true, EXT) \
+    HY_MP_OUTER_ONE(L, IO, OUTER_IN, true, false, EXT)   \
+    HY_MP_OUTER_ONE(L, IO, OUTER_MID, true, false, EXT)  \
+    HY_MP_OUTER_ONE(L, IO, OUTER_OUT, true, false, EXT)  \
+    HY_MP_OUTER_ONE(L, IO, OUTER_SPEC, false, false, EXT) \
+    HY_MP_OUTER_ONE(L, IO, OUTER_IN3, true, false, EXT)  \
+    HY_MP_OUTER_ONE(L, IO, OUTER_OUT3, true, false, EXT)
 
 #define HY_MP_MID_INST(L, A_, EXT)                                                            \
     EXT template hyena_status mp_mid_launch<L, MID_FWD, true>(const MidArgs&, int64_t,        \

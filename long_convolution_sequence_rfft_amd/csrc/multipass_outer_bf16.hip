@@ -2,5 +2,5 @@
 #include "multipass_kernels.h"
 
 namespace hy {
-HY_MP_LENGTHS(HY_MP_OUTER_INST, uint16_t, )
+HY_MP_OUTER_LENGTHS(HY_MP_OUTER_INST, uint16_t, )
 }  // namespace hy

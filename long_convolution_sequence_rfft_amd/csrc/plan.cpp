@@ -261,8 +261,8 @@ hyena_status plan_build(Plan& p, int64_t B, int64_t N, int64_t d, int32_t order,
     } else if (ndims == 2) {
         if (p.circular) return fail(HYENA_ERR_UNSUPPORTED, "periodic boundary: ndims = 1 only");
         const int64_t X = dims[0], Y = dims[1];
-        if (!is_pow2(X) || !is_pow2(Y) || X < 4 || Y < 4 || X > 512 || Y > 512)
-            return fail(HYENA_ERR_UNSUPPORTED, "2D grid sides must be powers of two in 4..512");
+        if (!is_pow2(X) || !is_pow2(Y) || X < 4 || Y < 4 || X > 1024 || Y > 1024)
+            return fail(HYENA_ERR_UNSUPPORTED, "2D grid sides must be powers of two in 4..1024");
         if (X * Y != N) return fail(HYENA_ERR_INVALID_ARGUMENT, "N must equal X * Y");
         if (path == HYENA_PATH_AUTO) path = HYENA_PATH_ROWCOL2D;
         if (path != HYENA_PATH_ROWCOL2D)

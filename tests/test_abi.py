@@ -43,6 +43,10 @@ def test_status_strings():
      hyena.HYENA_ERR_UNSUPPORTED),
     (dict(B=1, N=60, d=2, order=1, dims=[6, 10]), hyena.HYENA_ERR_UNSUPPORTED),
     (dict(B=1, N=64, d=2, order=1, dims=[8, 4]), hyena.HYENA_ERR_INVALID_ARGUMENT),
+    # 2D sides: powers of two in 4..1024, and N * d * 4 below 2^31
+    (dict(B=1, N=2048 * 8, d=2, order=1, dims=[2048, 8]), hyena.HYENA_ERR_UNSUPPORTED),
+    (dict(B=1, N=8 * 2048, d=2, order=1, dims=[8, 2048]), hyena.HYENA_ERR_UNSUPPORTED),
+    (dict(B=1, N=1024 * 1024, d=512, order=1, dims=[1024, 1024]), hyena.HYENA_ERR_UNSUPPORTED),
     (dict(B=1, N=16384, d=2, order=1, dims=[16384], path=hyena.HYENA_PATH_LDS1D),
      hyena.HYENA_ERR_UNSUPPORTED),
     (dict(B=1, N=256, d=2, order=1, dims=[256], path=hyena.HYENA_PATH_FOURSTEP1D),
@@ -334,5 +338,16 @@ def test_noalloc_refuses_before_touching_the_gpu():
         st, p = hyena.hyena_plan_create(B, N, 768, 2, [N], io)
         try:
             assert hyena.hyena_plan_query(p)[1] <= hyena.HYENA_NOALLOC_SCRATCH_BYTES
+        finally:
+            hyena.hyena_plan_destroy(p)
+
+
+def test_2d_plans_up_to_1024_sides():
+    for X, Y, d in ((1024, 1024, 511), (1024, 4, 3), (4, 1024, 3)):
+        st, p = hyena.hyena_plan_create(1, X * Y, d, 2, [X, Y])
+        try:
+            spec, ws, path = hyena.hyena_plan_query(p)
+            assert path == hyena.HYENA_PATH_ROWCOL2D
+            assert spec == 2 * ((d + 1) // 2) * (2 * X * 2 * Y // 2) * 16
         finally:
             hyena.hyena_plan_destroy(p)

@@ -32,12 +32,12 @@ def _split(cfg, kernels):
          "hy::hyena_stage<float, true, false>", "hy::hyena_stage<float, false, true>"]),
     (2, ["hy::hyena_lds1d_real_forward<8192, unsigned short, unsigned short, false>",
          "hy::hyena_stage_bf16<true>", "hy::hyena_stage_bf16<false>"]),
-    (3, ["hy::hyena_mp_outer<512, float, 0, true>", "hy::hyena_mp_outer<512, float, 1, true>",
-         "hy::hyena_mp_outer<512, float, 2, true>", "hy::hyena_mp_inner<256, float, 0, false>"]),
-    (4, ["hy::hyena_mp_outer<512, float, 0, true>", "hy::hyena_mp_outer<512, float, 1, true>",
-         "hy::hyena_mp_outer<512, float, 2, true>", "hy::hyena_mp_inner<512, float, 0, true>"]),
-    (5, ["hy::hyena_mp_outer<128, float, 0, true>", "hy::hyena_mp_outer<128, float, 1, true>",
-         "hy::hyena_mp_outer<128, float, 2, true>", "hy::hyena_mp_mid<128, 0, true>",
+    (3, ["hy::hyena_mp_outer<512, float, 0, true, true>", "hy::hyena_mp_outer<512, float, 1, true, true>",
+         "hy::hyena_mp_outer<512, float, 2, true, true>", "hy::hyena_mp_inner<256, float, 0, false>"]),
+    (4, ["hy::hyena_mp_outer<512, float, 0, true, true>", "hy::hyena_mp_outer<512, float, 1, true, true>",
+         "hy::hyena_mp_outer<512, float, 2, true, true>", "hy::hyena_mp_inner<512, float, 0, true>"]),
+    (5, ["hy::hyena_mp_outer<128, float, 0, true, false>", "hy::hyena_mp_outer<128, float, 1, true, false>",
+         "hy::hyena_mp_outer<128, float, 2, true, false>", "hy::hyena_mp_mid<128, 0, true>",
          "hy::hyena_mp_mid<128, 1, true>", "hy::hyena_mp_inner<128, float, 0, true>"]),
 ])
 def test_kernel_shares_cover_the_forward(idx, kernels):

@@ -81,10 +81,12 @@ def test_rowcol2d_small(X, Y, d, order):
     assert e < TOL_F32
 
 
-@pytest.mark.parametrize("i0,j0", [(255, -255), (-255, 255), (17, -3)])
-def test_rowcol2d_delta_kernel_is_exact_shift(i0, j0):
-    X = Y = 256
-    inp = synth.make_2d(B=1, X=X, Y=Y, d=2, order=1, seed=abs(i0) + abs(j0))
+@pytest.mark.parametrize("X,i0,j0", [(256, 255, -255), (256, -255, 255), (256, 17, -3),
+                                     (1024, 1023, -1023), (1024, -1023, 1023), (1024, -5, 1023)])
+def test_rowcol2d_delta_kernel_is_exact_shift(X, i0, j0):
+    Y = X
+    inp = synth.make_2d(B=1, X=X, Y=Y, d=2, order=1, sigma_range=(1.0, 2.0),
+                        seed=abs(i0) + abs(j0))
     inp.h[:] = 0.0
     inp.h[0, :, i0 + X - 1, j0 + Y - 1] = 1.0
     inp.gates[:] = 1.0
@@ -168,9 +170,11 @@ def test_fourstep_longer_than_64k(N, d):
     assert e < TOL_F32_LONG
 
 
-@pytest.mark.parametrize("X,Y,d", [(512, 512, 2), (4, 512, 3), (512, 8, 2)])
+@pytest.mark.parametrize("X,Y,d", [(512, 512, 2), (4, 512, 3), (512, 8, 2), (1024, 1024, 2),
+                                   (1024, 8, 2), (8, 1024, 3), (1024, 512, 1)])
 def test_rowcol2d_largest_sides(X, Y, d):
-    # 1024-point transforms along either axis (at most 8 pairs per outer workgroup)
+    # transforms of up to 2048 points along either axis (at most 4 pairs per
+    # outer workgroup at 2048)
     inp = synth.make_2d(B=1, X=X, Y=Y, d=d, order=2, seed=32)
     y, _, _ = run_gpu(inp)
     e = rel_err(y, oracle_ref(inp, method=oracle.FFT))
