@@ -4,12 +4,16 @@
 // sine MLP shared over positions.
 //
 //   hyena_implicit_hidden: z2[t] = sin(omega (W2 sin(omega (W1 gamma(t) + b1))
-//                          + b2)) for every position t, into the scratch.
-//   hyena_implicit_taps:   h = window . (W3 z2 + b3), a dense [order d] x [N]
-//                          contraction over the hidden width, tiled through
-//                          LDS, written to the scratch in the plan's storage
-//                          type; then the plan's usual spectrum launch
-//                          transforms the taps.
+//                          + b2)) for every position t, into the scratch
+//                          (the only buffer the call needs besides H).
+//   The spectrum kernels then evaluate every tap where the transform needs
+//   it, h = window . (W3 z2 + b3), in registers, straight into their forward
+//   transform, so the taps never exist in memory:
+//     hyena_implicit_real_spectrum   single-channel form, two filter rows per
+//                                    workgroup sharing each z2 load;
+//     hyena_implicit_pair_spectrum   channel-pair form (a pair per workgroup);
+//     four-step path: the outer pass's OUTER_SPEC_IMP mode, which stages the
+//     z2 rows of its column in LDS for its 16 channel pairs.
 #include "dispatch.h"
 #include "lds1d_kernels.h"
 
@@ -32,9 +36,10 @@ struct HiddenArgs {
     const float* b1;
     const float* W2;
     const float* b2;
-    float* z2;  // [N][hp]
+    float* z2;  // [N][hp], or [hp][N] when feature_major
     int64_t N;
     int32_t K, H, hp;
+    int32_t feature_major;
     float omega;
 };
 
@@ -92,96 +97,215 @@ __global__ void __launch_bounds__(kImpMaxHidden) hyena_implicit_hidden(HiddenArg
 #pragma unroll
         for (int p = 0; p < P; ++p) {
             const int64_t t = t0 + p;
-            if (t < a.N) a.z2[t * a.hp + i] = i < a.H ? sinf(a.omega * acc[p]) : 0.0f;
+            if (t < a.N) {
+                const float zv = i < a.H ? sinf(a.omega * acc[p]) : 0.0f;
+                if (a.feature_major) a.z2[(int64_t)i * a.N + t] = zv;
+                else a.z2[t * a.hp + i] = zv;
+            }
         }
     }
 }
 
-struct TapArgs {
-    const float* z2;  // [N][hp]
+// Output layer of the implicit filter for the fused spectrum kernels.
+struct ImpArgs {
+    const float* z2;  // hidden features, [hp][N] (feature-major)
     const float* W3;  // [rows][H]
     const float* b3;
     const float* alpha;
-    void* h;  // [rows][N], storage type
-    int64_t N, rows;
+    int64_t N, rows;  // rows = order d
     int32_t H, hp;
 };
 
-// Taps h[o][t] = exp(-alpha[o] t) (b3[o] + sum_j W3[o][j] z2[t][j]) for one
-// tile of 64 filter rows o = n d + c by 64 positions t.  256 threads, each
-// accumulating a 4 x 4 block; the contraction over the hidden width runs in
-// chunks of kTapK features, both operands staged through LDS transposed
-// ([j][o] and [j][t]) so the inner loop reads one float4 of each.
-template <typename IO>
-__global__ void __launch_bounds__(256) hyena_implicit_taps(TapArgs a)
+// exp(-alpha t) for the sample pair (t, t + 1): one exponential per pair, the
+// second sample takes the one-step factor.
+__device__ __forceinline__ float2 window_pair(float alpha, float step, int64_t t)
 {
-    constexpr int TT = kTapTile, KC = kTapK, LDW = TT + 4;
-    __shared__ __align__(16) float ws[KC][LDW];
-    __shared__ __align__(16) float zs[KC][LDW];
-    const int e = threadIdx.x;
-    const int tx = e & 15, ty = e >> 4;
-    const int64_t t0 = (int64_t)blockIdx.x * TT, o0 = (int64_t)blockIdx.y * TT;
-    // staging roles: row (or position) e / 4 of the tile, features 4 (e % 4) ..
-    const int sl = e >> 2, sj = (e & 3) * 4;
-    const int64_t so = o0 + sl, st = t0 + sl;
+    const float e = expf(-alpha * (float)t);
+    return make_float2(e, e * step);
+}
 
-    float acc[4][4];
+// Single-channel spectrum (transform length L = M/2, one real channel per
+// transform; CIRC: the periodic plan, M = N) with the taps evaluated in
+// registers.  Workgroup = filter rows o0 = RPW blockIdx (and o0 + 1): with
+// two rows each z2 value loaded serves both (the periodic plans' twice as
+// many live samples per thread leave registers for one).  The R0-pass input
+// of thread tau, slot (q, r), is the sample pair (2m, 2m + 1),
+// m = tau + q T + r L/R0; feature j of that pair is one aligned float2 of the
+// feature-major z2.
+template <int L, typename SP, bool CIRC>
+__global__ void __launch_bounds__(FftShape<L>::T, 2) hyena_implicit_real_spectrum(ImpArgs a, Lds1dSpecArgs s)
+{
+    using S = FftShape<L>;
+    constexpr int T = S::T, PTS = S::PTS, R0 = S::R0;
+    constexpr int RIN = CIRC ? R0 : R0 / 2;
+    constexpr int NS = S::Q0 * RIN;  // sample pairs per thread
+    constexpr int RPW = CIRC ? 1 : 2;  // filter rows per workgroup
+    __shared__ float smem[2 * S::LW];
+    __shared__ float sw[2][kImpMaxHidden];
+    const int tau = threadIdx.x;
+    const int64_t o0 = RPW * (int64_t)blockIdx.x;
+    const bool two = RPW == 2 && o0 + 1 < a.rows;
+    const int j1 = tau, j2 = tau ? 2 * T - tau : T;
+    for (int e = tau; e < 2 * a.hp; e += T) {
+        const int r = e / a.hp, j = e - r * a.hp;
+        const int64_t o = r == 0 || two ? o0 + r : o0;
+        sw[r][j] = j < a.H ? a.W3[o * a.H + j] : 0.0f;
+    }
+    __syncthreads();
+    float2 acc0[NS], acc1[RPW == 2 ? NS : 1];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < NS; ++i) acc0[i] = make_float2(0.0f, 0.0f);
 #pragma unroll
-        for (int k = 0; k < 4; ++k) acc[i][k] = 0.0f;
-
-    for (int j0 = 0; j0 < a.hp; j0 += KC) {
-        float wv[4];
+    for (int i = 0; i < (RPW == 2 ? NS : 1); ++i) acc1[i] = make_float2(0.0f, 0.0f);
+    // features in pairs: both features' loads are issued before either is
+    // used (hp is a multiple of 16), so L2 latencies overlap
+    for (int j = 0; j < a.hp; j += 2) {
+        float2 z[2][NS];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int j = j0 + sj + i;
-            wv[i] = (so < a.rows && j < a.H) ? a.W3[so * a.H + j] : 0.0f;
+        for (int jj = 0; jj < 2; ++jj) {
+            const float* zj = a.z2 + (int64_t)(j + jj) * a.N;
+#pragma unroll
+            for (int q = 0; q < S::Q0; ++q)
+#pragma unroll
+                for (int r = 0; r < RIN; ++r) {
+                    const int64_t m = tau + q * T + r * (L / R0);
+                    z[jj][q * RIN + r] = *reinterpret_cast<const float2*>(zj + 2 * m);
+                }
         }
-        const float4 zv = st < a.N ? *reinterpret_cast<const float4*>(a.z2 + st * a.hp + j0 + sj)
-                                   : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-        __syncthreads();  // previous chunk fully consumed
 #pragma unroll
-        for (int i = 0; i < 4; ++i) ws[sj + i][sl] = wv[i];
-        zs[sj + 0][sl] = zv.x;
-        zs[sj + 1][sl] = zv.y;
-        zs[sj + 2][sl] = zv.z;
-        zs[sj + 3][sl] = zv.w;
-        __syncthreads();
+        for (int jj = 0; jj < 2; ++jj) {
+            const float w0 = sw[0][j + jj], w1 = sw[1][j + jj];
 #pragma unroll
-        for (int k = 0; k < KC; ++k) {
-            const float4 wa = *reinterpret_cast<const float4*>(&ws[k][4 * ty]);
-            const float4 zb = *reinterpret_cast<const float4*>(&zs[k][4 * tx]);
-            const float wr[4] = {wa.x, wa.y, wa.z, wa.w};
-            const float zc[4] = {zb.x, zb.y, zb.z, zb.w};
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int c = 0; c < 4; ++c) acc[i][c] = fmaf(wr[i], zc[c], acc[i][c]);
+            for (int i = 0; i < NS; ++i) {
+                const float2 zz = z[jj][i];
+                float2& c0 = acc0[i];
+                c0 = make_float2(fmaf(w0, zz.x, c0.x), fmaf(w0, zz.y, c0.y));
+                if constexpr (RPW == 2) {
+                    float2& c1 = acc1[i];
+                    c1 = make_float2(fmaf(w1, zz.x, c1.x), fmaf(w1, zz.y, c1.y));
+                }
+            }
         }
     }
+    float2 v[PTS];
+    for (int rowi = 0; rowi < (two ? 2 : 1); ++rowi) {
+        const int64_t o = o0 + rowi;
+        const float al = a.alpha[o], b3 = a.b3[o], step = expf(-al);
+#pragma unroll
+        for (int q = 0; q < S::Q0; ++q)
+#pragma unroll
+            for (int r = 0; r < R0; ++r) {
+                if (r >= RIN) continue;
+                const int64_t m = tau + q * T + r * (L / R0);
+                const float2 w = window_pair(al, step, 2 * m);
+                float2 c = acc0[q * RIN + r];
+                if constexpr (RPW == 2) c = rowi == 0 ? c : acc1[q * RIN + r];
+                v[q * R0 + r] = make_float2(w.x * (b3 + c.x), w.y * (b3 + c.y));
+            }
+        fwd_transform<L, !CIRC>(v, smem, smem + S::LW, s.tw, s.tw_off, tau, j1, j2, rowi > 0,
+                                [] {});
+        SP* spec = static_cast<SP*>(s.spec) + o * (int64_t)(L / 2) * kEntryElems;
+        store_real_entries<L, SP>(v, spec, tau, 1.0f / (float)L, s.twm[tau ? tau : T]);
+    }
+}
 
-    IO* h = static_cast<IO*>(a.h);
-    const int64_t t = t0 + 4 * tx;
+// Channel-pair spectrum (transform length M, any N < M/2 + 1) with the taps
+// of the pair's two channels evaluated in registers: one workgroup per
+// (filter n, channel pair); sample t = tau + q T + r M/R0, r < R0/2.
+template <int M, typename SP>
+__global__ void __launch_bounds__(FftShape<M>::T, 2) hyena_implicit_pair_spectrum(ImpArgs a, Lds1dSpecArgs s)
+{
+    using S = FftShape<M>;
+    constexpr int T = S::T, PTS = S::PTS, R0 = S::R0;
+    constexpr int NS = S::Q0 * (R0 / 2);
+    __shared__ float smem[2 * S::LW];
+    __shared__ float sw[2][kImpMaxHidden];
+    const int tau = threadIdx.x;
+    const int64_t lin = blockIdx.x;  // n * npairs + p
+    const int64_t n = lin / s.npairs;
+    const int64_t c0 = 2 * (lin - n * s.npairs);
+    const bool has_b = c0 + 1 < s.d;
+    const int64_t oa = n * s.d + c0, ob = has_b ? oa + 1 : oa;
+    const int j1 = tau, j2 = tau ? 2 * T - tau : T;
+    for (int e = tau; e < 2 * a.hp; e += T) {
+        const int r = e / a.hp, j = e - r * a.hp;
+        sw[r][j] = j < a.H ? a.W3[(r == 0 ? oa : ob) * a.H + j] : 0.0f;
+    }
+    __syncthreads();
+    float2 acc[NS];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int64_t o = o0 + 4 * ty + i;
-        if (o >= a.rows) break;
-        const float b3 = a.b3[o], al = a.alpha[o];
-        float val[4];
+    for (int i = 0; i < NS; ++i) acc[i] = make_float2(0.0f, 0.0f);
+    for (int j = 0; j < a.hp; ++j) {
+        const float w0 = sw[0][j], w1 = sw[1][j];
+        const float* zj = a.z2 + (int64_t)j * a.N;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) val[c] = expf(-al * (float)(t + c)) * (b3 + acc[i][c]);
-        IO* row = h + o * a.N + t;
-        if ((a.N & 3) == 0 && t + 3 < a.N) {
-            // row start and t are multiples of 4: two aligned sample pairs
-            using PR = typename PairRaw<IO>::type;
-            reinterpret_cast<PR*>(row)[0] = narrow_pair<IO>(make_float2(val[0], val[1]));
-            reinterpret_cast<PR*>(row)[1] = narrow_pair<IO>(make_float2(val[2], val[3]));
-        } else {
+        for (int q = 0; q < S::Q0; ++q)
 #pragma unroll
-            for (int c = 0; c < 4; ++c)
-                if (t + c < a.N) st1<IO>(row + c, val[c]);
+            for (int r = 0; r < R0 / 2; ++r) {
+                const int64_t t = tau + q * T + r * (M / R0);
+                const float z = t < a.N ? zj[t] : 0.0f;
+                float2& c = acc[q * (R0 / 2) + r];
+                c = make_float2(fmaf(w0, z, c.x), fmaf(w1, z, c.y));
+            }
+    }
+    const float ala = a.alpha[oa], alb = a.alpha[ob], ba = a.b3[oa], bb = a.b3[ob];
+    float2 v[PTS];
+#pragma unroll
+    for (int q = 0; q < S::Q0; ++q)
+#pragma unroll
+        for (int r = 0; r < R0 / 2; ++r) {
+            const int64_t t = tau + q * T + r * (M / R0);
+            const float2 c = acc[q * (R0 / 2) + r];
+            const bool live = t < a.N;
+            v[q * R0 + r] = make_float2(live ? expf(-ala * (float)t) * (ba + c.x) : 0.0f,
+                                        (live && has_b) ? expf(-alb * (float)t) * (bb + c.y) : 0.0f);
         }
+    fwd_transform<M>(v, smem, smem + S::LW, s.tw, s.tw_off, tau, j1, j2, false, [] {});
+    SP* spec = static_cast<SP*>(s.spec) + lin * (int64_t)(M / 2) * kEntryElems;
+    store_spectrum_entries<M, SP>(v, spec, tau, 0.5f / (float)M);
+}
+
+template <int L, typename SP, bool CIRC>
+hyena_status imp_real_launch(const ImpArgs& a, const Lds1dSpecArgs& s, hipStream_t st)
+{
+    const int64_t nb = CIRC ? a.rows : (a.rows + 1) / 2;
+    HY_LAUNCH(kernel_label("hyena_implicit_real_spectrum", L, type_label<SP>(), CIRC),
+              (hyena_implicit_real_spectrum<L, SP, CIRC>), dim3((unsigned)nb), dim3(FftShape<L>::T),
+              0, st, a, s);
+    const hipError_t e = hipGetLastError();
+    return e == hipSuccess ? HYENA_OK : fail(HYENA_ERR_DEVICE, hipGetErrorString(e));
+}
+
+template <int M, typename SP>
+hyena_status imp_pair_launch(const ImpArgs& a, const Lds1dSpecArgs& s, hipStream_t st)
+{
+    HY_LAUNCH(kernel_label("hyena_implicit_pair_spectrum", M, type_label<SP>()),
+              (hyena_implicit_pair_spectrum<M, SP>), dim3((unsigned)s.nblocks), dim3(FftShape<M>::T),
+              0, st, a, s);
+    const hipError_t e = hipGetLastError();
+    return e == hipSuccess ? HYENA_OK : fail(HYENA_ERR_DEVICE, hipGetErrorString(e));
+}
+
+template <typename SP>
+hyena_status imp_lds1d(const Plan& p, const ImpArgs& a, const Lds1dSpecArgs& s, hipStream_t st)
+{
+    if (p.lds_io == IO_REAL) {
+        const bool circ = p.circular != 0;
+        switch (p.M / 2) {
+#define HY_CASE(LL, I, S_)                                                            \
+    case LL:                                                                          \
+        return circ ? imp_real_launch<LL, SP, true>(a, s, st) : imp_real_launch<LL, SP, false>(a, s, st);
+            HY_LDS1D_REAL_SIZES(HY_CASE, 0, 0)
+#undef HY_CASE
+            default: return fail(HYENA_ERR_UNSUPPORTED, "implicit filter: unsupported length");
+        }
+    }
+    switch (p.M) {
+#define HY_CASE(MM, I, S_) \
+    case MM: return imp_pair_launch<MM, SP>(a, s, st);
+        HY_LDS1D_SIZES(HY_CASE, 0, 0)
+#undef HY_CASE
+        default: return fail(HYENA_ERR_UNSUPPORTED, "implicit filter: unsupported length");
     }
 }
 
@@ -189,9 +313,8 @@ __global__ void __launch_bounds__(256) hyena_implicit_taps(TapArgs a)
 
 size_t implicit_scratch_bytes(const Plan& p, int32_t hidden)
 {
-    return align256((size_t)p.N * (size_t)hidden_pad(hidden) * 4u) +
-           align256((size_t)p.order * (size_t)p.d * (size_t)p.N *
-                    (p.io_dtype == HYENA_F32 ? 4u : 2u));
+    // the hidden features only: the taps are never stored
+    return align256((size_t)p.N * (size_t)hidden_pad(hidden) * 4u);
 }
 
 hyena_status launch_implicit_spectrum(const Plan& p, const hyena_implicit_filter& f, void* H,
@@ -202,8 +325,7 @@ hyena_status launch_implicit_spectrum(const Plan& p, const hyena_implicit_filter
         return fail(HYENA_ERR_UNSUPPORTED, "implicit filter: n_freqs must be in 0..64");
     if (f.hidden < 1 || f.hidden > kImpMaxHidden)
         return fail(HYENA_ERR_UNSUPPORTED, "implicit filter: hidden must be in 1..256");
-    if ((int64_t)p.order * p.d > 65535ll * kTapTile)
-        return fail(HYENA_ERR_UNSUPPORTED, "implicit filter: order * d must be at most 4194240");
+    const bool four = p.path == HYENA_PATH_FOURSTEP1D;
     HiddenArgs h{};
     h.W1 = f.W1;
     h.b1 = f.b1;
@@ -214,38 +336,29 @@ hyena_status launch_implicit_spectrum(const Plan& p, const hyena_implicit_filter
     h.K = f.n_freqs;
     h.H = f.hidden;
     h.hp = (int32_t)hidden_pad(f.hidden);
+    // the four-step spectrum stages whole rows z2[t][:] of its column in LDS;
+    // the single-workgroup kernels read one feature for many t at a time
+    h.feature_major = four ? 0 : 1;
     h.omega = f.omega;
     HY_LAUNCH(kernel_label("hyena_implicit_hidden"), hyena_implicit_hidden,
               dim3((unsigned)((p.N + kImpPos - 1) / kImpPos)), dim3(kImpMaxHidden), 0, s, h);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(HYENA_ERR_DEVICE, hipGetErrorString(e));
 
-    TapArgs ta{};
-    ta.z2 = h.z2;
-    ta.W3 = f.W3;
-    ta.b3 = f.b3;
-    ta.alpha = f.alpha;
-    ta.N = p.N;
-    ta.rows = (int64_t)p.order * p.d;
-    ta.H = f.hidden;
-    ta.hp = h.hp;
-    char* taps = static_cast<char*>(scratch) + align256((size_t)p.N * (size_t)h.hp * 4u);
-    ta.h = taps;
-    const dim3 grid((unsigned)((p.N + kTapTile - 1) / kTapTile),
-                    (unsigned)((ta.rows + kTapTile - 1) / kTapTile));
-    if (p.io_dtype == HYENA_F32)
-        HY_LAUNCH(kernel_label("hyena_implicit_taps", "float"), hyena_implicit_taps<float>, grid,
-                  dim3(256), 0, s, ta);
-    else if (p.io_dtype == HYENA_F16)
-        HY_LAUNCH(kernel_label("hyena_implicit_taps", "_Float16"), hyena_implicit_taps<_Float16>,
-                  grid, dim3(256), 0, s, ta);
-    else
-        HY_LAUNCH(kernel_label("hyena_implicit_taps", "unsigned short"), hyena_implicit_taps<uint16_t>,
-                  grid, dim3(256), 0, s, ta);
-    e = hipGetLastError();
-    if (e != hipSuccess) return fail(HYENA_ERR_DEVICE, hipGetErrorString(e));
-    if (p.path == HYENA_PATH_LDS1D) return launch_lds1d_spectrum(p, taps, H, ws, stream);
-    return launch_fourstep_spectrum(p, taps, H, ws, stream);
+    ImpArgs ia{};
+    ia.z2 = h.z2;
+    ia.W3 = f.W3;
+    ia.b3 = f.b3;
+    ia.alpha = f.alpha;
+    ia.N = p.N;
+    ia.rows = (int64_t)p.order * p.d;
+    ia.H = f.hidden;
+    ia.hp = h.hp;
+    if (four) return launch_fourstep_spectrum_implicit(p, ia.z2, ia.W3, ia.b3, ia.alpha, ia.hp,
+                                                       ia.H, H, ws, stream);
+    Lds1dSpecArgs sa = lds1d_spec_args(p, H, ws);
+    if (p.spec_dtype == HYENA_F32) return imp_lds1d<float>(p, ia, sa, s);
+    return imp_lds1d<uint16_t>(p, ia, sa, s);
 }
 
 }  // namespace hy

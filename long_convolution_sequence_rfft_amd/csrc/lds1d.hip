@@ -547,11 +547,9 @@ hyena_status launch_lds1d_forward(const Plan& p, const void* u, const void* cons
     return stage_plan(p, out, 1, false, s);
 }
 
-hyena_status launch_lds1d_spectrum(const Plan& p, const void* h, void* H, const void* ws,
-                                   void* stream)
+Lds1dSpecArgs lds1d_spec_args(const Plan& p, void* H, const void* ws)
 {
     Lds1dSpecArgs a{};
-    a.h = h;
     a.spec = H;
     a.tw = static_cast<const float2*>(ws);
     a.N = p.N;
@@ -559,12 +557,20 @@ hyena_status launch_lds1d_spectrum(const Plan& p, const void* h, void* H, const 
     a.npairs = p.npairs;
     a.nblocks = (int64_t)p.order * p.npairs;
     a.tw_off = lds1d_offsets(p);
-    const hipStream_t s = (hipStream_t)stream;
-    const bool real = p.lds_io == IO_REAL;
-    if (real) {
+    if (p.lds_io == IO_REAL) {
         a.nblocks = (int64_t)p.order * p.d;
         a.twm = static_cast<const float2*>(ws) + p.seg[4].off;
     }
+    return a;
+}
+
+hyena_status launch_lds1d_spectrum(const Plan& p, const void* h, void* H, const void* ws,
+                                   void* stream)
+{
+    Lds1dSpecArgs a = lds1d_spec_args(p, H, ws);
+    a.h = h;
+    const hipStream_t s = (hipStream_t)stream;
+    const bool real = p.lds_io == IO_REAL;
     return by_storage(p, [&](auto io, auto sp) {
         using IO = typename decltype(io)::type;
         using SP = typename decltype(sp)::type;

@@ -328,6 +328,9 @@ hyena_status lds1d_spectrum_launch(const Lds1dSpecArgs& a, hipStream_t s)
     return e == hipSuccess ? HYENA_OK : fail(HYENA_ERR_DEVICE, hipGetErrorString(e));
 }
 
+// Spectrum-launch arguments of a plan (everything but the taps pointer).
+Lds1dSpecArgs lds1d_spec_args(const Plan& p, void* H, const void* ws);
+
 #define HY_LDS1D_SIZES(X, IO, SP) \
     X(8, IO, SP) X(16, IO, SP) X(32, IO, SP) X(64, IO, SP) X(128, IO, SP) X(256, IO, SP) \
     X(512, IO, SP) X(1024, IO, SP) X(2048, IO, SP) X(4096, IO, SP) X(8192, IO, SP)       \

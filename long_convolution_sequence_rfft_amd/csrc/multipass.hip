@@ -8,6 +8,7 @@ namespace hy {
 HY_MP_OUTER_LENGTHS(HY_MP_OUTER_INST, float, extern)
 HY_MP_OUTER_LENGTHS(HY_MP_OUTER_INST, uint16_t, extern)
 HY_MP_OUTER_LENGTHS(HY_MP_OUTER_INST, _Float16, extern)
+HY_MP_OUTER_IMP_LENGTHS(HY_MP_OUTER_IMP_INST, 0, extern)
 HY_MP_INNER_LENGTHS(HY_MP_INNER_INST, float, extern)
 HY_MP_INNER_LENGTHS(HY_MP_INNER_INST, uint16_t, extern)
 HY_MP_LENGTHS(HY_MP_MID_INST, 0, extern)
@@ -76,6 +77,11 @@ hyena_status outer_go(int L, int mode, bool half_spec, const OuterArgs& a, int64
     switch (L) {
 #define HY_CASE(LL, A_, B_)                                                                        \
     case LL:                                                                                       \
+        if (mode == OUTER_SPEC_IMP) {                                                              \
+            if constexpr (LL >= 32 && LL <= 1024)                                               \
+                return mp_outer_launch<LL, float, OUTER_SPEC_IMP, true, true>(a, nb, s);          \
+            return fail(HYENA_ERR_UNSUPPORTED, "implicit filter: four-step columns below 32");    \
+        }                                                                                          \
         if (mode == OUTER_IN3) return mp_outer_launch<LL, IO, OUTER_IN3, true, false>(a, nb, s);   \
         if (mode == OUTER_OUT3) return mp_outer_launch<LL, IO, OUTER_OUT3, true, false>(a, nb, s); \
         if (paired) {                                                                              \
@@ -184,7 +190,10 @@ hyena_status mp_forward(const Plan& p, const void* u, const void* const* gates, 
     return HYENA_OK;
 }
 
-hyena_status mp_spectrum(const Plan& p, const void* h, void* H, void* ws, void* stream)
+// imp != nullptr: the taps are evaluated from an implicit filter's hidden
+// features (four-step path) instead of read from h.
+hyena_status mp_spectrum(const Plan& p, const void* h, void* H, void* ws, void* stream,
+                         const ImpOuter* imp = nullptr)
 {
     const hipStream_t s = (hipStream_t)stream;
     MpGeom g = base_geom(p);
@@ -208,10 +217,16 @@ hyena_status mp_spectrum(const Plan& p, const void* h, void* H, void* ws, void* 
             g.ngroups = total_groups - g0 < chunk_groups ? total_groups - g0 : chunk_groups;
             OuterArgs oa{};
             oa.g = g;
-            oa.filt = static_cast<const char*>(h) + (size_t)n * p.d * taps * io_size(p);
+            if (imp) {
+                oa.imp = *imp;
+                oa.imp.n = n;
+            } else {
+                oa.filt = static_cast<const char*>(h) + (size_t)n * p.d * taps * io_size(p);
+            }
             oa.F = F;
             oa.tw = tw;
-            hyena_status st = outer(p, OUTER_SPEC, g.four_step != 0, oa, col_blocks * g.ngroups, s);
+            hyena_status st = outer(p, imp ? OUTER_SPEC_IMP : OUTER_SPEC, g.four_step != 0, oa,
+                                    col_blocks * g.ngroups, s);
             if (st != HYENA_OK) return st;
             InnerArgs ia{};
             ia.g = g;
@@ -571,6 +586,20 @@ hyena_status launch_fourstep_forward(const Plan& p, const void* u, const void* c
 hyena_status launch_fourstep_spectrum(const Plan& p, const void* h, void* H, void* ws, void* stream)
 {
     return mp_spectrum(p, h, H, ws, stream);
+}
+hyena_status launch_fourstep_spectrum_implicit(const Plan& p, const float* z2, const float* W3,
+                                               const float* b3, const float* alpha, int32_t hp,
+                                               int32_t hidden, void* H, void* ws, void* stream)
+{
+    if (hp > kImpHidden) return fail(HYENA_ERR_UNSUPPORTED, "implicit filter: hidden too wide");
+    ImpOuter im{};
+    im.z2 = z2;
+    im.W3 = W3;
+    im.b3 = b3;
+    im.alpha = alpha;
+    im.H = hidden;
+    im.hp = hp;
+    return mp_spectrum(p, nullptr, H, ws, stream, &im);
 }
 hyena_status launch_fourstep_export(const Plan& p, const void* H, void* out, void* stream)
 {

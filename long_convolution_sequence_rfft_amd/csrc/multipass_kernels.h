@@ -10,8 +10,10 @@ namespace hy {
 // OUTER_IN3 / OUTER_OUT3: OUTER_IN / OUTER_OUT with the HyenaND mixer's
 // 3x3x3 short convolutions of a 3D grid (kept apart so that the plain passes
 // compile without that code)
+// OUTER_SPEC_IMP: OUTER_SPEC with the taps evaluated from an implicit
+// filter's hidden features (four-step path)
 enum OuterMode { OUTER_IN = 0, OUTER_MID = 1, OUTER_OUT = 2, OUTER_SPEC = 3, OUTER_IN3 = 4,
-                 OUTER_OUT3 = 5 };
+                 OUTER_OUT3 = 5, OUTER_SPEC_IMP = 6 };
 enum InnerMode { INNER_CHAIN = 0, INNER_SPEC = 1 };
 
 // Workgroup of kMpThreads threads, one length-L transform per
@@ -22,6 +24,8 @@ enum InnerMode { INNER_CHAIN = 0, INNER_SPEC = 1 };
 // loops (adjacent lanes -> same position of adjacent transforms) spread
 // over the LDS banks.
 constexpr int kMpThreads = 256;
+// widest hidden layer of an implicit filter (W3 rows staged by OUTER_SPEC_IMP)
+constexpr int kImpHidden = 256;
 template <int L>
 struct MpShape {
     static constexpr int T = FftShape<L>::T;
@@ -42,6 +46,17 @@ struct BlockArgs {
     int32_t on;
 };
 
+// Implicit filter's output layer for OUTER_SPEC_IMP: taps of filter row
+// o = n d + c at sample t are exp(-alpha[o] t) (b3[o] + W3[o] . z2[t]).
+struct ImpOuter {
+    const float* z2;  // hidden features [N][hp] (row-major)
+    const float* W3;  // [order d][H]
+    const float* b3;
+    const float* alpha;
+    int32_t H, hp;
+    int32_t n;  // filter index
+};
+
 struct OuterArgs {
     MpGeom g;
     const void* act;   // u (IN), gate (MID, OUT)
@@ -50,6 +65,7 @@ struct OuterArgs {
     float2* F;         // workspace intermediate of this chunk
     const float2* tw;
     BlockArgs blk;
+    ImpOuter imp;
 };
 
 struct InnerArgs {
@@ -61,13 +77,36 @@ struct InnerArgs {
     const float2* tw;
 };
 
+// Streams read once per forward (activations, gates, spectrum entries):
+// plain loads, or carrying the nontemporal hint with HY_STREAM_NT, fixed at
+// build time.
+#ifndef HY_STREAM_NT
+#define HY_STREAM_NT 0
+#endif
+template <typename T>
+__device__ __forceinline__ T stream_load(const T* p)
+{
+    if constexpr (HY_STREAM_NT != 0 && sizeof(T) == 4) {
+        return __builtin_bit_cast(T, __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p)));
+    } else if constexpr (HY_STREAM_NT != 0 && sizeof(T) == 8) {
+        typedef unsigned u2v __attribute__((ext_vector_type(2)));
+        return __builtin_bit_cast(T, __builtin_nontemporal_load(reinterpret_cast<const u2v*>(p)));
+    } else if constexpr (HY_STREAM_NT != 0 && sizeof(T) == 16) {
+        typedef unsigned u4v __attribute__((ext_vector_type(4)));
+        return __builtin_bit_cast(T, __builtin_nontemporal_load(reinterpret_cast<const u4v*>(p)));
+    } else {
+        return *p;
+    }
+}
+
 // Sample of channel pair (c0, c0+1) at activation row `row` (element offset).
 template <typename IO>
 __device__ __forceinline__ float2 act_load(const IO* base, int64_t row, int64_t c0, int64_t d)
 {
     const IO* r = base + row * d + c0;
     if (c0 + 1 < d) {
-        if ((d & 1) == 0) return load_pair<IO, true>(r, true);
+        if ((d & 1) == 0)
+            return widen_pair<IO>(stream_load(reinterpret_cast<const typename PairRaw<IO>::type*>(r)));
         return make_float2(ld1<IO>(r), ld1<IO>(r + 1));
     }
     return make_float2(ld1<IO>(r), 0.0f);
@@ -435,7 +474,7 @@ __global__ void __launch_bounds__(kMpThreads, 2) hyena_mp_outer(OuterArgs a)
     const int j1 = tau, j2 = tau ? 2 * TA - tau : TA;
     constexpr bool IN = MODE == OUTER_IN || MODE == OUTER_IN3;
     constexpr bool OUT = MODE == OUTER_OUT || MODE == OUTER_OUT3;
-    const int n_outer = MODE == OUTER_SPEC ? g.Lb : g.Lb_live;
+    const int n_outer = (MODE == OUTER_SPEC || MODE == OUTER_SPEC_IMP) ? g.Lb : g.Lb_live;
     const bool col_live = o < n_outer;
     float* re = sre + f * LW;
     float* im = sim + f * LW;
@@ -537,6 +576,91 @@ __global__ void __launch_bounds__(kMpThreads, 2) hyena_mp_outer(OuterArgs a)
         __syncthreads();
         lds_to_regs<LA, true>(v, re, im, tau);
         __syncthreads();
+    } else if constexpr (MODE == OUTER_SPEC_IMP) {
+        // Taps of an implicit filter, four-step layout: transform f holds
+        // pair kp at column o, samples s = tau + q T + r LA/R0 (r < R0/2),
+        // t = M2 s + o.  Per column of the workgroup, the hidden features of
+        // its samples are staged in sre feature-major (HC features at a
+        // time, rows of LA/2 + 1 words), the pairs' W3 rows in sim.
+        static_assert(HALF_IN, "four-step spectra read the live half");
+        const ImpOuter& im = a.imp;
+        constexpr int HS = LA / 2 + 1;  // staged row length (odd: no bank conflicts)
+        constexpr int HC = 16 * HS <= NF * LW ? 16 : 8;  // features per staging round
+        static_assert(HC * HS <= NF * LW, "implicit staging fits the transform's LDS");
+        static_assert(16 * 2 * kImpHidden <= NF * LW, "W3 rows fit the transform's LDS");
+        float* zs = sre;  // [HC][HS]
+        float* sw = sim;  // [KP][2][hp]
+        const int hh = HC;
+        for (int e = threadIdx.x; e < KP * 2 * im.hp; e += kMpThreads) {
+            const int j = e % im.hp, rc = e / im.hp, kq = rc >> 1, ch = rc & 1;
+            int64_t bq, pq;
+            bool lq;
+            pair_of_slot(g, group, kq, bq, pq, lq);
+            const int64_t c = 2 * pq + ch;
+            sw[e] = (lq && c < g.d && j < im.H) ? im.W3[((int64_t)im.n * g.d + c) * im.H + j] : 0.0f;
+        }
+        constexpr int NSAMP = S::Q0 * (R0 / 2);
+        float2 acc[NSAMP];
+#pragma unroll
+        for (int i = 0; i < NSAMP; ++i) acc[i] = make_float2(0.0f, 0.0f);
+        const float* w0 = sw + (kp * 2 + 0) * im.hp;
+        const float* w1 = sw + (kp * 2 + 1) * im.hp;
+        for (int ci = 0; ci < C; ++ci) {
+            const int oc = cb * C + ci;  // column staged in this round
+            for (int j0 = 0; j0 < im.hp; j0 += hh) {
+                __syncthreads();  // previous half consumed (and W3 rows written)
+                // rows t = M2 s + oc, s < LA/2: lane -> (s, 4-feature chunk)
+                const int nch = hh / 4;
+                for (int e = threadIdx.x; e < (LA / 2) * nch; e += kMpThreads) {
+                    const int sx = e / nch, jc = e - sx * nch;
+                    const int64_t t = g.sa * sx + g.so * oc;
+                    float4 z = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+                    if (oc < n_outer && t < g.N)
+                        z = *reinterpret_cast<const float4*>(im.z2 + t * im.hp + j0 + 4 * jc);
+                    zs[(4 * jc + 0) * HS + sx] = z.x;
+                    zs[(4 * jc + 1) * HS + sx] = z.y;
+                    zs[(4 * jc + 2) * HS + sx] = z.z;
+                    zs[(4 * jc + 3) * HS + sx] = z.w;
+                }
+                __syncthreads();
+                if ((f >> g.kp_log2) == ci) {
+                    for (int j = 0; j < hh; ++j) {
+                        const float wa = w0[j0 + j], wb = w1[j0 + j];
+                        const float* zr = zs + j * HS;
+#pragma unroll
+                        for (int q = 0; q < S::Q0; ++q)
+#pragma unroll
+                            for (int r = 0; r < R0 / 2; ++r) {
+                                const float z = zr[tau + q * TA + r * (LA / R0)];
+                                float2& c = acc[q * (R0 / 2) + r];
+                                c = make_float2(fmaf(wa, z, c.x), fmaf(wb, z, c.y));
+                            }
+                    }
+                }
+            }
+        }
+        const int64_t ca = 2 * p, cbb = 2 * p + 1;
+        const bool has_b = cbb < g.d;
+        const int64_t oa = (int64_t)im.n * g.d + (live ? ca : 0);
+        const int64_t ob = has_b && live ? oa + 1 : oa;
+        const float ala = im.alpha[oa], alb = im.alpha[ob], ba = im.b3[oa], bb = im.b3[ob];
+#pragma unroll
+        for (int q = 0; q < S::Q0; ++q)
+#pragma unroll
+            for (int r = 0; r < R0; ++r) {
+                float2 x = make_float2(0.0f, 0.0f);
+                if (r < R0 / 2) {
+                    const int sx = tau + q * TA + r * (LA / R0);
+                    const int64_t t = g.sa * sx + g.so * o;
+                    const float2 c = acc[q * (R0 / 2) + r];
+                    if (live && col_live && t < g.N) {
+                        x.x = expf(-ala * (float)t) * (ba + c.x);
+                        if (has_b) x.y = expf(-alb * (float)t) * (bb + c.y);
+                    }
+                }
+                v[q * R0 + r] = x;
+            }
+        __syncthreads();  // the staging area becomes the transform's LDS
     } else if constexpr (MODE == OUTER_SPEC) {
         // filter taps straight from their channel-major layout (not timed)
         const IO* h = static_cast<const IO*>(a.filt);
@@ -836,7 +960,7 @@ __global__ void __launch_bounds__(kMpThreads, 2) hyena_mp_inner(InnerArgs a)
             using Raw = typename EntryRaw<SP>::type;
 #pragma unroll
             for (int i = 0; i < EPT; ++i)
-                ent[i] = reinterpret_cast<const Raw*>(a.spec)[ebase + tu + i * 2 * TB];
+                ent[i] = stream_load(&reinterpret_cast<const Raw*>(a.spec)[ebase + tu + i * 2 * TB]);
         }
     }
 
@@ -1095,6 +1219,12 @@ hyena_status mp_mid_launch(const MidArgs& a, int64_t nblocks, hipStream_t s)
 // (transforms of 2048 points along either axis)
 #define HY_MP_OUTER_LENGTHS(X, A, B) HY_MP_LENGTHS(X, A, B) X(2048, A, B)
 
+// the implicit-filter spectrum pass reads no storage-typed input: float only;
+// four-step column lengths (32 .. 1024)
+#define HY_MP_OUTER_IMP_LENGTHS(X, A, B) X(32, A, B) X(64, A, B) X(128, A, B) X(256, A, B) \
+    X(512, A, B) X(1024, A, B)
+#define HY_MP_OUTER_IMP_INST(L, A_, EXT) \
+    EXT template hyena_status mp_outer_launch<L, float, OUTER_SPEC_IMP, true, true>(const OuterArgs&, int64_t, hipStream_t);
 #define HY_MP_OUTER_ONE(L, IO, MODE, HS, PR, EXT) \
     EXT template hyena_status mp_outer_launch<L, IO, MODE, HS, PR>(const OuterArgs&, int64_t, hipStream_t);
 // 1D / 2D (mirror-paired rows) and 3D (natural rows, and the mixer's modes)

@@ -23,7 +23,10 @@ constexpr int64_t kFourStepMaxM = 1 << 22;  // largest 1D transform (N = 2097152
 // waves, while the intermediate still mostly fits the 256 MB last-level cache
 // between passes (measured at 48, 96, 160, 192, 256 and 384 MiB; 192 was best
 // at 64K tokens and on the 256 x 256 grid).
-constexpr int64_t kChunkBytes = 192ll << 20;
+#ifndef HY_CHUNK_MIB
+#define HY_CHUNK_MIB 192
+#endif
+constexpr int64_t kChunkBytes = (int64_t)HY_CHUNK_MIB << 20;
 
 // Radix plan of the single-workgroup transform of length M (8 <= M <= 16384):
 // 32 complex values per thread (M >= 64), forward passes R0, R1, RL with
@@ -154,6 +157,11 @@ hyena_status launch_fourstep_forward(const Plan& p, const void* u, const void* c
                                      const void* H, const float* D, void* y, void* ws,
                                      void* stream);
 hyena_status launch_fourstep_export(const Plan& p, const void* H, void* out, void* stream);
+// taps of an implicit filter evaluated in the spectrum's first pass from its
+// hidden features z2 [N][hp] (the output layer W3, b3 and the window alpha)
+hyena_status launch_fourstep_spectrum_implicit(const Plan& p, const float* z2, const float* W3,
+                                               const float* b3, const float* alpha, int32_t hp,
+                                               int32_t hidden, void* H, void* ws, void* stream);
 
 hyena_status launch_rowcol2d_spectrum(const Plan& p, const void* h, void* H, void* ws, void* stream);
 hyena_status launch_rowcol2d_forward(const Plan& p, const void* u, const void* const* gates,

@@ -59,6 +59,37 @@ def test_implicit_ragged_tiles(N, d, H):
     assert rel_err(y, ref) < 1e-5
 
 
+@pytest.mark.parametrize("N,d,H", [(65536, 3, 64), (32768, 5, 256), (20000, 33, 16)])
+def test_implicit_four_step(N, d, H):
+    # the taps evaluated in the four-step spectrum's first pass; d = 33 walks
+    # several pair groups with a ragged last one, H = 256 the widest layer
+    y, ref, plan, _, _ = _run(N, d, 1, synth.F32, seed=55, H=H)
+    assert plan.path == 2
+    e = rel_err(y, ref)
+    say(f"[gpu] implicit four-step N={N} d={d} H={H}: rel err {e:.3e}")
+    assert e < (5e-5 if N >= 65536 else 1e-5)
+
+
+@pytest.mark.parametrize("N,d", [(4096, 5), (256, 2)])
+def test_implicit_periodic(N, d):
+    # periodic plan: every one of the N taps is live
+    import torch
+    from long_convolution_sequence_rfft_amd import hyena
+    inp = synth.make_1d(B=1, N=N, d=d, order=2, seed=56)
+    w = synth.make_implicit(d, 2, K=8, H=64, seed=57)
+    say(f"[gpu] implicit periodic N={N} d={d}")
+    plan = hyena.Plan(1, d, 2, (N,), circular=True)
+    dev = {k: torch.from_numpy(v).cuda() for k, v in w.arrays().items()}
+    Hs = plan.spectrum_implicit(omega=w.omega, **dev)
+    y = plan.forward(to_torch(inp.u, synth.F32), [to_torch(g, synth.F32) for g in inp.gates], Hs,
+                     torch.from_numpy(inp.D).cuda())
+    torch.cuda.synchronize()
+    u64, g64, _, D64 = inp.f64()
+    h = _oracle_taps(w, N, d, 2)
+    ref = oracle.hyena1d_circular(u64, g64, h, D64, oracle.FFT)
+    assert rel_err(from_torch(y, synth.F32), ref) < 1e-5
+
+
 def test_implicit_bf16_storage():
     y, ref, _, _, _ = _run(4096, 4, 2, synth.BF16, seed=52)
     assert rel_err(y, ref) < 1e-2

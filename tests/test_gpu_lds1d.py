@@ -129,16 +129,6 @@ def test_full_size_workload_sampled(cfg):
     assert e < (TOL_F32 if inp.dtype == synth.F32 else TOL_BF16)
 
 
-@pytest.mark.parametrize("cfg", [1, 2])
-def test_full_size_workload_all_channels(cfg):
-    inp = synth.make_workload(cfg, seed=cfg + 100)
-    y, _, _ = run_gpu(inp)
-    ref = oracle_ref(inp, method=oracle.FFT)
-    e = rel_err(y, ref)
-    say(f"workload {cfg} all-channel rel_err={e:.3e}")
-    assert e < (TOL_F32 if inp.dtype == synth.F32 else TOL_BF16)
-
-
 def test_launch_timing_records_every_kernel():
     # per-launch timing: each forward on the single-channel LDS path is three
     # launches (stage in, transform chain, stage out -- for float32 storage

@@ -124,28 +124,6 @@ def test_multipass_deterministic_bitwise():
     assert np.array_equal(y1, y2)
 
 
-def test_full_size_64k_sampled():
-    inp = synth.make_workload(3)
-    y, plan, _ = run_gpu(inp)
-    rng = np.random.default_rng(3)
-    ch = np.unique(np.concatenate([[0, 1, inp.d - 1], rng.choice(inp.d, 13, replace=False)]))
-    ref = oracle_ref(inp, channels=ch, method=oracle.FFT)
-    e = rel_err(y[..., ch], ref)
-    say(f"64K full-size sampled rel_err={e:.3e}")
-    assert e < TOL_F32_LONG
-
-
-def test_full_size_2d_sampled():
-    inp = synth.make_workload(4)
-    y, plan, _ = run_gpu(inp)
-    rng = np.random.default_rng(4)
-    ch = np.unique(np.concatenate([[0, 1, inp.d - 1], rng.choice(inp.d, 5, replace=False)]))
-    ref = oracle_ref(inp, channels=ch, method=oracle.FFT)
-    e = rel_err(y[..., ch], ref)
-    say(f"2D 256x256 full-size sampled rel_err={e:.3e}")
-    assert e < TOL_F32
-
-
 def test_rowcol2d_several_chunks():
     # 512 x 512 grid, 3 batch rows of 17 channel pairs: 96 pair slots against
     # chunks of 48 (192 MiB of 4 MiB intermediates), so the chain walks two
