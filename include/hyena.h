@@ -125,9 +125,10 @@ hyena_status hyena_plan_create(hyena_plan_t* plan, int64_t B, int64_t N, int64_t
  * Math", section "Linear vs circular" as the operator:
  *   z_n[b,t,c] = gate_n[b,t,c] * ( sum_{s=0}^{N-1} h_n[c,s] z_{n-1}[b,(t-s) mod N,c]
  *                                  + D_n[c] z_{n-1}[b,t,c] ),
- * for ndims = 1 and N a power of two in 16..16384 (the transform is the
- * sequence itself; LDS1D path).  hyena_spectrum_export then gives bins
- * k = 0..N/2 of the unpadded length-N transform.
+ * for ndims = 1 and N a power of two in 16..2097152 (the transform is the
+ * sequence itself: LDS1D path up to 16384, FOURSTEP1D path from 32768).
+ * hyena_spectrum_export then gives bins k = 0..N/2 of the unpadded length-N
+ * transform.
  */
 #define HYENA_FLAG_CIRCULAR 1
 hyena_status hyena_plan_create_ex(hyena_plan_t* plan, int64_t B, int64_t N, int64_t d,

@@ -178,6 +178,7 @@ __device__ __forceinline__ void lds_to_regs(float2* v, const float* sre, const f
 struct MpGeom {
     int64_t N, d, npairs, B;
     int32_t four_step;  // 1: 1D four-step, 0: 2D row-column
+    int32_t full;       // periodic plan: unpadded columns (every sample live)
     // sample index of (outer-axis position a, inner position o):
     //   four-step t = M2 a + o ;  2D t = Y o + a
     int64_t sa, so;

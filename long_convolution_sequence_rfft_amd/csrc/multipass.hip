@@ -8,6 +8,9 @@ namespace hy {
 HY_MP_OUTER_LENGTHS(HY_MP_OUTER_INST, float, extern)
 HY_MP_OUTER_LENGTHS(HY_MP_OUTER_INST, uint16_t, extern)
 HY_MP_OUTER_LENGTHS(HY_MP_OUTER_INST, _Float16, extern)
+HY_MP_OUTER_CIRC_LENGTHS(HY_MP_OUTER_CIRC_INST, float, extern)
+HY_MP_OUTER_CIRC_LENGTHS(HY_MP_OUTER_CIRC_INST, uint16_t, extern)
+HY_MP_OUTER_CIRC_LENGTHS(HY_MP_OUTER_CIRC_INST, _Float16, extern)
 HY_MP_OUTER_IMP_LENGTHS(HY_MP_OUTER_IMP_INST, 0, extern)
 HY_MP_INNER_LENGTHS(HY_MP_INNER_INST, float, extern)
 HY_MP_INNER_LENGTHS(HY_MP_INNER_INST, uint16_t, extern)
@@ -49,6 +52,7 @@ MpGeom base_geom(const Plan& p)
     g.npairs = p.npairs;
     g.B = p.B;
     g.four_step = p.path == HYENA_PATH_FOURSTEP1D;
+    g.full = p.circular;
     if (g.four_step) {
         g.La = (int32_t)p.M1;
         g.Lb = (int32_t)p.M2;
@@ -84,6 +88,14 @@ hyena_status outer_go(int L, int mode, bool half_spec, const OuterArgs& a, int64
         }                                                                                          \
         if (mode == OUTER_IN3) return mp_outer_launch<LL, IO, OUTER_IN3, true, false>(a, nb, s);   \
         if (mode == OUTER_OUT3) return mp_outer_launch<LL, IO, OUTER_OUT3, true, false>(a, nb, s); \
+        if (a.g.full && (mode == OUTER_IN || mode == OUTER_MID || mode == OUTER_OUT)) {           \
+            if constexpr (LL == 512 || LL == 1024) {                                               \
+                if (mode == OUTER_IN) return mp_outer_launch<LL, IO, OUTER_IN, false, true>(a, nb, s);   \
+                if (mode == OUTER_MID) return mp_outer_launch<LL, IO, OUTER_MID, false, true>(a, nb, s); \
+                return mp_outer_launch<LL, IO, OUTER_OUT, false, true>(a, nb, s);                  \
+            }                                                                                      \
+            return fail(HYENA_ERR_UNSUPPORTED, "multi-pass: no periodic columns of this length");  \
+        }                                                                                          \
         if (paired) {                                                                              \
             if (mode == OUTER_IN) return mp_outer_launch<LL, IO, OUTER_IN, true, true>(a, nb, s);   \
             if (mode == OUTER_MID) return mp_outer_launch<LL, IO, OUTER_MID, true, true>(a, nb, s); \
@@ -225,8 +237,8 @@ hyena_status mp_spectrum(const Plan& p, const void* h, void* H, void* ws, void* 
             }
             oa.F = F;
             oa.tw = tw;
-            hyena_status st = outer(p, imp ? OUTER_SPEC_IMP : OUTER_SPEC, g.four_step != 0, oa,
-                                    col_blocks * g.ngroups, s);
+            hyena_status st = outer(p, imp ? OUTER_SPEC_IMP : OUTER_SPEC,
+                                    g.four_step != 0 && !g.full, oa, col_blocks * g.ngroups, s);
             if (st != HYENA_OK) return st;
             InnerArgs ia{};
             ia.g = g;

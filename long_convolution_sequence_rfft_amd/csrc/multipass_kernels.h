@@ -454,7 +454,13 @@ __global__ void __launch_bounds__(kMpThreads, 2) hyena_mp_outer(OuterArgs a)
     using S = FftShape<LA>;
     using X = MpShape<LA>;
     constexpr int TA = X::T, NF = X::NF, LW = X::LW, R0 = S::R0;
-    constexpr bool HALF_IN = MODE == OUTER_SPEC ? HALF_SPEC : true;
+    // HALF_SPEC: zero-padded transforms (only the first LA/2 samples of a
+    // column are live, and the inverse keeps only those).  false: the
+    // periodic plans' unpadded transforms on the chain modes, and the 2D
+    // spectrum.  The 3D and implicit-filter modes are always padded.
+    constexpr bool HALF_IN = (MODE == OUTER_SPEC || MODE == OUTER_IN || MODE == OUTER_MID ||
+                              MODE == OUTER_OUT) ? HALF_SPEC : true;
+    constexpr int NHALF = HALF_IN ? 1 : 2;  // column halves the activation tiles cover
     __shared__ float sre[NF * LW];
     __shared__ float sim[NF * LW];
 
@@ -488,7 +494,8 @@ __global__ void __launch_bounds__(kMpThreads, 2) hyena_mp_outer(OuterArgs a)
     // cooperative move of activation rows between memory and the regions:
     // index -> (pair kp', outer sample s, column c'); KP consecutive lanes
     // cover one row's KP channel pairs (one cache line for KP = 16 f32).
-    auto tile_rows = [&](auto&& fn) {
+    // Half hf of the column: samples s in [hf LA/2, (hf + 1) LA/2).
+    auto tile_rows_half = [&](int hf, auto&& fn) {
         constexpr int total = (LA / 2) * NF;  // = (LA/2) C KP
         static_assert(total % kMpThreads == 0, "tile split");
 #pragma unroll
@@ -496,7 +503,7 @@ __global__ void __launch_bounds__(kMpThreads, 2) hyena_mp_outer(OuterArgs a)
             const int idx = (int)threadIdx.x + it * kMpThreads;
             const int kq = idx & (KP - 1);
             const int rest = idx >> g.kp_log2;
-            const int s = rest % (LA / 2);
+            const int s = hf * (LA / 2) + rest % (LA / 2);
             const int cq = rest / (LA / 2);
             const int fq = cq * KP + kq;
             int64_t bq, pq;
@@ -507,6 +514,7 @@ __global__ void __launch_bounds__(kMpThreads, 2) hyena_mp_outer(OuterArgs a)
             fn(it, fq, s, pq, lq && oq < n_outer && t < g.N, bq * g.N + t);
         }
     };
+    auto tile_rows = [&](auto&& fn) { tile_rows_half(0, fn); };
 
     // tile elements per thread in tile_rows
     constexpr int GT = (LA / 2) * NF / kMpThreads;
@@ -573,8 +581,19 @@ __global__ void __launch_bounds__(kMpThreads, 2) hyena_mp_outer(OuterArgs a)
             sre[fq * LW + lpad(s)] = xin[it].x;
             sim[fq * LW + lpad(s)] = xin[it].y;
         });
+        if constexpr (!HALF_IN) {
+            // unpadded (periodic) column: the second half of the samples
+            static_assert(MODE == OUTER_IN, "unpadded columns on the plain chain only");
+            tile_rows_half(1, [&](int it, int, int, int64_t pq, bool ok, int64_t row) {
+                xin[it] = ok ? act_load<IO>(u, row, 2 * pq, g.d) : make_float2(0.0f, 0.0f);
+            });
+            tile_rows_half(1, [&](int it, int fq, int s, int64_t, bool, int64_t) {
+                sre[fq * LW + lpad(s)] = xin[it].x;
+                sim[fq * LW + lpad(s)] = xin[it].y;
+            });
+        }
         __syncthreads();
-        lds_to_regs<LA, true>(v, re, im, tau);
+        lds_to_regs<LA, HALF_IN>(v, re, im, tau);
         __syncthreads();
     } else if constexpr (MODE == OUTER_SPEC_IMP) {
         // Taps of an implicit filter, four-step layout: transform f holds
@@ -754,31 +773,44 @@ __global__ void __launch_bounds__(kMpThreads, 2) hyena_mp_outer(OuterArgs a)
                 gval[it] = ok ? act_load<IO>(gate, row, 2 * pq, g.d) : make_float2(0.0f, 0.0f);
             });
         }
-        if (paired) inv_transform<LA, true>(v, re, im, a.tw, g.tw_a, tau, j1, j2, [] {});
+        if (paired) inv_transform<LA, HALF_IN>(v, re, im, a.tw, g.tw_a, tau, j1, j2, [] {});
         else inv_lds_to_regs<LA, true, true>(v, re, im, a.tw, g.tw_a, tau);
         __syncthreads();
         tile_rows([&](int it, int fq, int s, int64_t, bool, int64_t) {
             sre[fq * LW + lpad(s)] = gval[it].x;
             sim[fq * LW + lpad(s)] = gval[it].y;
         });
+        if constexpr (!HALF_IN) {
+            // unpadded (periodic) column: the gates of the second half
+            static_assert(MODE == OUTER_MID || MODE == OUTER_OUT, "unpadded columns on the plain chain only");
+            tile_rows_half(1, [&](int it, int, int, int64_t pq, bool ok, int64_t row) {
+                gval[it] = ok ? act_load<IO>(gate, row, 2 * pq, g.d) : make_float2(0.0f, 0.0f);
+            });
+            tile_rows_half(1, [&](int it, int fq, int s, int64_t, bool, int64_t) {
+                sre[fq * LW + lpad(s)] = gval[it].x;
+                sim[fq * LW + lpad(s)] = gval[it].y;
+            });
+        }
         __syncthreads();
 #pragma unroll
         for (int q = 0; q < S::Q0; ++q)
 #pragma unroll
-            for (int r = 0; r < R0 / 2; ++r) {
+            for (int r = 0; r < (HALF_IN ? R0 / 2 : R0); ++r) {
                 const int i = lpad(tau + q * TA + r * (LA / R0));
                 float2& x = v[q * R0 + r];
                 x = make_float2(x.x * re[i], x.y * im[i]);
             }
         __syncthreads();
         if constexpr (OUT) {
-            regs_to_lds<LA, true>(v, re, im, tau);
+            regs_to_lds<LA, HALF_IN>(v, re, im, tau);
             __syncthreads();
             IO* y = static_cast<IO*>(a.out);
-            tile_rows([&](int, int fq, int s, int64_t pq, bool ok, int64_t row) {
-                if (ok) act_store<IO>(y, row, 2 * pq, g.d,
-                                      make_float2(sre[fq * LW + lpad(s)], sim[fq * LW + lpad(s)]));
-            });
+#pragma unroll
+            for (int hf = 0; hf < NHALF; ++hf)
+                tile_rows_half(hf, [&](int, int fq, int s, int64_t pq, bool ok, int64_t row) {
+                    if (ok) act_store<IO>(y, row, 2 * pq, g.d,
+                                          make_float2(sre[fq * LW + lpad(s)], sim[fq * LW + lpad(s)]));
+                });
             return;
         }
     }
@@ -1218,6 +1250,14 @@ hyena_status mp_mid_launch(const MidArgs& a, int64_t nblocks, hipStream_t s)
 // outer passes also come in 2048 points: 2D grids with sides up to 1024
 // (transforms of 2048 points along either axis)
 #define HY_MP_OUTER_LENGTHS(X, A, B) HY_MP_LENGTHS(X, A, B) X(2048, A, B)
+
+// unpadded (periodic) chain modes on the four-step column lengths of
+// periodic plans (N >= 32768: 512 or 1024 samples)
+#define HY_MP_OUTER_CIRC_LENGTHS(X, A, B) X(512, A, B) X(1024, A, B)
+#define HY_MP_OUTER_CIRC_INST(L, IO, EXT)                  \
+    HY_MP_OUTER_ONE(L, IO, OUTER_IN, false, true, EXT)     \
+    HY_MP_OUTER_ONE(L, IO, OUTER_MID, false, true, EXT)    \
+    HY_MP_OUTER_ONE(L, IO, OUTER_OUT, false, true, EXT)
 
 // the implicit-filter spectrum pass reads no storage-typed input: float only;
 // four-step column lengths (32 .. 1024)

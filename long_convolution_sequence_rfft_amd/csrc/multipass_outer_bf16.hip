@@ -3,4 +3,5 @@
 
 namespace hy {
 HY_MP_OUTER_LENGTHS(HY_MP_OUTER_INST, uint16_t, )
+HY_MP_OUTER_CIRC_LENGTHS(HY_MP_OUTER_CIRC_INST, uint16_t, )
 }  // namespace hy

@@ -3,4 +3,5 @@
 
 namespace hy {
 HY_MP_OUTER_LENGTHS(HY_MP_OUTER_INST, _Float16, )
+HY_MP_OUTER_CIRC_LENGTHS(HY_MP_OUTER_CIRC_INST, _Float16, )
 }  // namespace hy

@@ -3,5 +3,6 @@
 
 namespace hy {
 HY_MP_OUTER_LENGTHS(HY_MP_OUTER_INST, float, )
+HY_MP_OUTER_CIRC_LENGTHS(HY_MP_OUTER_CIRC_INST, float, )
 HY_MP_OUTER_IMP_LENGTHS(HY_MP_OUTER_IMP_INST, 0, )
 }  // namespace hy

@@ -214,15 +214,19 @@ hyena_status plan_build(Plan& p, int64_t B, int64_t N, int64_t d, int32_t order,
             return fail(HYENA_ERR_UNSUPPORTED, "1D sequence length must be in 4..2097152");
         p.M = next_pow2(2 * N);
         if (p.circular) {
-            // periodic boundary: the transform is the sequence itself, on the
-            // single-channel path (a power of two, 16..16384)
-            if (!is_pow2(N) || N < 16 || N > kLdsMaxM)
+            // periodic boundary: the transform is the sequence itself (a power
+            // of two), on the single-channel path up to 16384 and on the
+            // four-step path (columns of 512 or 1024) from 32768 on
+            if (!is_pow2(N) || N < 16)
                 return fail(HYENA_ERR_UNSUPPORTED,
-                            "periodic boundary needs N a power of two in 16..16384");
-            if (path != HYENA_PATH_AUTO && path != HYENA_PATH_LDS1D)
-                return fail(HYENA_ERR_UNSUPPORTED, "periodic boundary runs on the LDS1D path");
+                            "periodic boundary needs N a power of two in 16..2097152");
+            const int32_t want = N <= kLdsMaxM ? HYENA_PATH_LDS1D : HYENA_PATH_FOURSTEP1D;
+            if (path != HYENA_PATH_AUTO && path != want)
+                return fail(HYENA_ERR_UNSUPPORTED,
+                            "periodic boundary: N up to 16384 runs on the LDS1D path, longer "
+                            "sequences on the FOURSTEP1D path");
             p.M = N;
-            path = HYENA_PATH_LDS1D;
+            path = want;
         }
         if (path == HYENA_PATH_AUTO) path = p.M <= kLdsMaxM ? HYENA_PATH_LDS1D : HYENA_PATH_FOURSTEP1D;
         if (path == HYENA_PATH_ROWCOL2D || path == HYENA_PATH_ROWCOL3D)

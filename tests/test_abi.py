@@ -281,8 +281,11 @@ def test_implicit_scratch_sizes_and_validation():
     (16384, [16384], 1, 1, hyena.HYENA_OK),
     (1000, [1000], 0, 1, hyena.HYENA_ERR_UNSUPPORTED),       # not a power of two
     (8, [8], 0, 1, hyena.HYENA_ERR_UNSUPPORTED),             # below 16
-    (32768, [32768], 0, 1, hyena.HYENA_ERR_UNSUPPORTED),     # beyond one workgroup
-    (4096, [4096], 2, 1, hyena.HYENA_ERR_UNSUPPORTED),       # four-step path
+    (32768, [32768], 0, 1, hyena.HYENA_OK),                  # four-step path from 32768
+    (2097152, [2097152], 2, 1, hyena.HYENA_OK),
+    (32768, [32768], 1, 1, hyena.HYENA_ERR_UNSUPPORTED),     # beyond one workgroup
+    (4096, [4096], 2, 1, hyena.HYENA_ERR_UNSUPPORTED),       # four-step below 32768
+    (1 << 22, [1 << 22], 0, 1, hyena.HYENA_ERR_UNSUPPORTED),  # longest sequence 2097152
     (64, [8, 8], 0, 1, hyena.HYENA_ERR_UNSUPPORTED),         # grids
     (64, [64], 0, 2, hyena.HYENA_ERR_UNSUPPORTED),           # unknown flag
 ])
@@ -291,8 +294,13 @@ def test_periodic_boundary_plans(N, dims, path, flags, code):
     assert st == code, hyena.hyena_last_error()
     if st == hyena.HYENA_OK:
         spec, _, p = hyena.hyena_plan_query(plan)
-        assert p == 1
-        assert spec == 2 * 4 * (N // 4) * 16  # order * d * (N/4 entries) * 16 bytes
+        if N <= 16384:
+            assert p == 1
+            assert spec == 2 * 4 * (N // 4) * 16  # order * d * (N/4 entries) * 16 bytes
+        else:
+            # four-step: order * channel pairs * (N/2 entries) * 16 bytes
+            assert p == 2
+            assert spec == 2 * 2 * (N // 2) * 16
         hyena.hyena_plan_destroy(plan)
 
 

@@ -384,3 +384,33 @@ def test_multipass_order_8(kind):
     e = rel_err(y, oracle_ref(inp, method=oracle.FFT))
     say(f"[gpu] order 8 {kind} rel err {e:.3e}")
     assert e < TOL_F32
+
+
+@pytest.mark.parametrize("N,d,B,order,dtype", [(65536, 4, 1, 2, synth.F32),
+                                                (1 << 20, 1, 1, 2, synth.F32),
+                                                (32768, 35, 2, 3, synth.F32),
+                                                (65536, 6, 1, 2, synth.BF16),
+                                                (131072, 3, 1, 1, synth.F16)])
+def test_periodic_four_step(N, d, B, order, dtype):
+    # periodic boundary beyond one workgroup: unpadded length-N transforms
+    # (columns of 512 or 1024 samples, every one live) on the four-step path;
+    # d = 35 walks several pair groups with a ragged last one
+    from long_convolution_sequence_rfft_amd import hyena
+    inp = synth.make_1d(B=B, N=N, d=d, order=order, alpha_range=(1e-6, 1e-4), dtype=dtype,
+                        seed=61 + d)
+    io = {synth.F32: hyena.HYENA_F32, synth.BF16: hyena.HYENA_BF16,
+          synth.F16: hyena.HYENA_F16}[dtype]
+    plan = hyena.Plan(B, d, order, (N,), io_dtype=io, circular=True)
+    assert plan.path == FOUR
+    y, _, H = run_gpu(inp, plan=plan)
+    u, g, h, D = inp.f64()
+    e = rel_err(y, oracle.hyena1d_circular(u, g, h, D, oracle.FFT))
+    say(f"[gpu] periodic four-step N={N} d={d} order={order} {dtype} rel err {e:.3e}")
+    assert e < {synth.F32: TOL_F32_LONG, synth.BF16: TOL_BF16, synth.F16: 5e-3}[dtype]
+    if dtype == synth.F32 and N == 65536:
+        # the spectrum is the unpadded length-N transform of the taps
+        nat = plan.export_spectrum(H).cpu().numpy().astype(np.float64)
+        nat = nat[..., 0] + 1j * nat[..., 1]
+        for n in range(order):
+            for c in range(d):
+                assert rel_err(nat[n, c], oracle.fft(h[n, c])[:N // 2 + 1]) < 2e-6
