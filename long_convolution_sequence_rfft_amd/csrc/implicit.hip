@@ -9,8 +9,8 @@
 //   The spectrum kernels then evaluate every tap where the transform needs
 //   it, h = window . (W3 z2 + b3), in registers, straight into their forward
 //   transform, so the taps never exist in memory:
-//     hyena_implicit_real_spectrum   single-channel form, two filter rows per
-//                                    workgroup sharing each z2 load;
+//     hyena_implicit_real_spectrum   single-channel form, two or three filter
+//                                    rows per workgroup sharing each z2 load;
 //     hyena_implicit_pair_spectrum   channel-pair form (a pair per workgroup);
 //     four-step path: the outer pass's OUTER_SPEC_IMP mode, which stages the
 //     z2 rows of its column in LDS for its 16 channel pairs.
@@ -24,11 +24,11 @@ namespace {
 constexpr int kImpMaxFreqs = 64;
 constexpr int kImpMaxHidden = 256;
 constexpr int kImpPos = 16;  // positions per workgroup of the hidden kernel
-constexpr int kTapTile = 64;  // taps tile: 64 filter rows x 64 positions
-constexpr int kTapK = 16;     // hidden features per LDS chunk
+constexpr int kHiddenPad = 16;  // hidden width padded to a multiple of this
 
-// hidden width padded to whole chunks of the taps contraction (zero features)
-int64_t hidden_pad(int32_t H) { return (H + kTapK - 1) / kTapK * kTapK; }
+// hidden width padded with zero features: the contractions walk the features
+// in pairs (single-channel spectrum) and in LDS rounds of 8 or 16 (four-step)
+int64_t hidden_pad(int32_t H) { return (H + kHiddenPad - 1) / kHiddenPad * kHiddenPad; }
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
 struct HiddenArgs {
@@ -126,12 +126,21 @@ __device__ __forceinline__ float2 window_pair(float alpha, float step, int64_t t
 
 // Single-channel spectrum (transform length L = M/2, one real channel per
 // transform; CIRC: the periodic plan, M = N) with the taps evaluated in
-// registers.  Workgroup = filter rows o0 = RPW blockIdx (and o0 + 1): with
-// two rows each z2 value loaded serves both (the periodic plans' twice as
-// many live samples per thread leave registers for one).  The R0-pass input
-// of thread tau, slot (q, r), is the sample pair (2m, 2m + 1),
-// m = tau + q T + r L/R0; feature j of that pair is one aligned float2 of the
-// feature-major z2.
+// registers.  Workgroup = RPW consecutive filter rows o0 = RPW blockIdx ...:
+// every z2 value a thread loads serves all of them, so the hidden features
+// are read from L2 once per RPW rows (the contraction is bound by that
+// traffic).  The accumulators of all RPW rows stay in registers through the
+// rows' transforms, so RPW is what the register file leaves room for: three
+// rows from L = 4096 up (spill-free; 8192 at 768 channels and order 2 then
+// fills the GPU with exactly one round of workgroups, 23% faster than two
+// rows), two below (three measured no faster at 2048), one for the periodic
+// plans (twice as many live samples per thread).  The R0-pass input of
+// thread tau, slot (q, r), is the sample pair (2m, 2m + 1), m = tau + q T +
+// r L/R0; feature j of that pair is one aligned float2 of the feature-major
+// z2.
+template <int L, bool CIRC>
+constexpr int kImpRows = CIRC ? 1 : L >= 4096 ? 3 : 2;
+
 template <int L, typename SP, bool CIRC>
 __global__ void __launch_bounds__(FftShape<L>::T, 2) hyena_implicit_real_spectrum(ImpArgs a, Lds1dSpecArgs s)
 {
@@ -139,24 +148,24 @@ __global__ void __launch_bounds__(FftShape<L>::T, 2) hyena_implicit_real_spectru
     constexpr int T = S::T, PTS = S::PTS, R0 = S::R0;
     constexpr int RIN = CIRC ? R0 : R0 / 2;
     constexpr int NS = S::Q0 * RIN;  // sample pairs per thread
-    constexpr int RPW = CIRC ? 1 : 2;  // filter rows per workgroup
+    constexpr int RPW = kImpRows<L, CIRC>;
     __shared__ float smem[2 * S::LW];
-    __shared__ float sw[2][kImpMaxHidden];
+    __shared__ float sw[RPW][kImpMaxHidden];
     const int tau = threadIdx.x;
     const int64_t o0 = RPW * (int64_t)blockIdx.x;
-    const bool two = RPW == 2 && o0 + 1 < a.rows;
+    const int nrows = (int)(a.rows - o0 < RPW ? a.rows - o0 : RPW);  // rows of this workgroup
     const int j1 = tau, j2 = tau ? 2 * T - tau : T;
-    for (int e = tau; e < 2 * a.hp; e += T) {
+    for (int e = tau; e < RPW * a.hp; e += T) {
         const int r = e / a.hp, j = e - r * a.hp;
-        const int64_t o = r == 0 || two ? o0 + r : o0;
+        const int64_t o = o0 + (r < nrows ? r : 0);
         sw[r][j] = j < a.H ? a.W3[o * a.H + j] : 0.0f;
     }
     __syncthreads();
-    float2 acc0[NS], acc1[RPW == 2 ? NS : 1];
+    float2 acc[RPW][NS];
 #pragma unroll
-    for (int i = 0; i < NS; ++i) acc0[i] = make_float2(0.0f, 0.0f);
+    for (int k = 0; k < RPW; ++k)
 #pragma unroll
-    for (int i = 0; i < (RPW == 2 ? NS : 1); ++i) acc1[i] = make_float2(0.0f, 0.0f);
+        for (int i = 0; i < NS; ++i) acc[k][i] = make_float2(0.0f, 0.0f);
     // features in pairs: both features' loads are issued before either is
     // used (hp is a multiple of 16), so L2 latencies overlap
     for (int j = 0; j < a.hp; j += 2) {
@@ -173,23 +182,23 @@ __global__ void __launch_bounds__(FftShape<L>::T, 2) hyena_implicit_real_spectru
                 }
         }
 #pragma unroll
-        for (int jj = 0; jj < 2; ++jj) {
-            const float w0 = sw[0][j + jj], w1 = sw[1][j + jj];
+        for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
-            for (int i = 0; i < NS; ++i) {
-                const float2 zz = z[jj][i];
-                float2& c0 = acc0[i];
-                c0 = make_float2(fmaf(w0, zz.x, c0.x), fmaf(w0, zz.y, c0.y));
-                if constexpr (RPW == 2) {
-                    float2& c1 = acc1[i];
-                    c1 = make_float2(fmaf(w1, zz.x, c1.x), fmaf(w1, zz.y, c1.y));
+            for (int k = 0; k < RPW; ++k) {
+                const float w = sw[k][j + jj];
+#pragma unroll
+                for (int i = 0; i < NS; ++i) {
+                    const float2 zz = z[jj][i];
+                    float2& c = acc[k][i];
+                    c = make_float2(fmaf(w, zz.x, c.x), fmaf(w, zz.y, c.y));
                 }
             }
-        }
     }
     float2 v[PTS];
-    for (int rowi = 0; rowi < (two ? 2 : 1); ++rowi) {
-        const int64_t o = o0 + rowi;
+#pragma unroll
+    for (int k = 0; k < RPW; ++k) {
+        if (k >= nrows) break;  // uniform
+        const int64_t o = o0 + k;
         const float al = a.alpha[o], b3 = a.b3[o], step = expf(-al);
 #pragma unroll
         for (int q = 0; q < S::Q0; ++q)
@@ -198,12 +207,10 @@ __global__ void __launch_bounds__(FftShape<L>::T, 2) hyena_implicit_real_spectru
                 if (r >= RIN) continue;
                 const int64_t m = tau + q * T + r * (L / R0);
                 const float2 w = window_pair(al, step, 2 * m);
-                float2 c = acc0[q * RIN + r];
-                if constexpr (RPW == 2) c = rowi == 0 ? c : acc1[q * RIN + r];
+                const float2 c = acc[k][q * RIN + r];
                 v[q * R0 + r] = make_float2(w.x * (b3 + c.x), w.y * (b3 + c.y));
             }
-        fwd_transform<L, !CIRC>(v, smem, smem + S::LW, s.tw, s.tw_off, tau, j1, j2, rowi > 0,
-                                [] {});
+        fwd_transform<L, !CIRC>(v, smem, smem + S::LW, s.tw, s.tw_off, tau, j1, j2, k > 0, [] {});
         SP* spec = static_cast<SP*>(s.spec) + o * (int64_t)(L / 2) * kEntryElems;
         store_real_entries<L, SP>(v, spec, tau, 1.0f / (float)L, s.twm[tau ? tau : T]);
     }
@@ -268,7 +275,8 @@ __global__ void __launch_bounds__(FftShape<M>::T, 2) hyena_implicit_pair_spectru
 template <int L, typename SP, bool CIRC>
 hyena_status imp_real_launch(const ImpArgs& a, const Lds1dSpecArgs& s, hipStream_t st)
 {
-    const int64_t nb = CIRC ? a.rows : (a.rows + 1) / 2;
+    constexpr int RPW = kImpRows<L, CIRC>;
+    const int64_t nb = (a.rows + RPW - 1) / RPW;
     HY_LAUNCH(kernel_label("hyena_implicit_real_spectrum", L, type_label<SP>(), CIRC),
               (hyena_implicit_real_spectrum<L, SP, CIRC>), dim3((unsigned)nb), dim3(FftShape<L>::T),
               0, st, a, s);
