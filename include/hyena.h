@@ -44,7 +44,17 @@
  * is the null stream) with no host synchronisation.  The workspace holds
  * twiddle tables (written by hyena_workspace_init) and, on the multi-pass
  * paths, the intermediate spectra; it must not be shared by calls that run
- * concurrently.
+ * concurrently.  A multi-pass forward whose channel pairs take two or more
+ * chunks of the intermediate buffer runs every other chunk on a second
+ * stream of the library's, with its own copy of that buffer in the
+ * workspace: the second stream waits for an event recorded on the given
+ * stream when the call starts, and the given stream waits for one recorded
+ * on the second when the call's work is enqueued, so everything the call
+ * does stays ordered on the given stream (graph capture included).  That
+ * stream and its two events are created on first use, one set per host
+ * thread and device, at default priority, and held until the process ends;
+ * a thread that has none yet while its stream is being captured runs all
+ * chunks on the given stream.
  *
  * Errors.  Argument problems are reported before anything is enqueued and
  * leave every output untouched; hyena_last_error() then returns a

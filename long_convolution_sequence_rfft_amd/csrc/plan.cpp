@@ -325,8 +325,9 @@ hyena_status plan_build(Plan& p, int64_t B, int64_t N, int64_t d, int32_t order,
         // positions; the filter spectrum needs every inner position
         const int64_t fwd_pair = p.path == HYENA_PATH_FOURSTEP1D ? p.M * 8 : p.X * p.P2 * 8;
         const int64_t spec_pair = p.path == HYENA_PATH_FOURSTEP1D ? p.M * 8 : p.P1 * p.P2 * 8;
-        // keep the chunk's intermediate near kChunkBytes so it stays in the
-        // 256 MB last-level cache between passes; whole groups of 16 pairs
+        // the chunk's intermediate near kChunkBytes (a measured size: smaller
+        // chunks, which the last-level cache could hold, were no faster);
+        // whole groups of 16 pairs
         int64_t chunk = kChunkBytes / fwd_pair;
         chunk = chunk / 16 * 16;
         if (chunk < 16) chunk = 16;
@@ -365,15 +366,20 @@ hyena_status plan_build(Plan& p, int64_t B, int64_t N, int64_t d, int32_t order,
         p.stage_bytes = align_up((size_t)(p.order + 2) * (size_t)B * (size_t)N * (size_t)d *
                                      (io_dtype == HYENA_F32 ? 4u : 2u), 256);
     }
-    p.workspace_bytes = p.inter_offset + p.inter_bytes + p.stage_bytes;
+    if (p.chunk_pairs > 0) {
+        const int64_t total_slots = p.B * ((p.npairs + 15) / 16) * 16;
+        if (total_slots > p.chunk_pairs) p.inter_copies = 2;
+    }
+    p.workspace_bytes = p.inter_offset + (size_t)p.inter_copies * p.inter_bytes + p.stage_bytes;
     static const char* kPathName[] = {"AUTO", "LDS1D", "FOURSTEP1D", "ROWCOL2D", "ROWCOL3D"};
     log_msg("plan %llu: B=%lld N=%lld d=%lld order=%d ndims=%d io=%d spectrum=%d circular=%d -> "
             "path %s, M=%lld (M1=%lld M2=%lld P=%lldx%lldx%lld), spectrum %zu B, workspace %zu B, "
-            "chunk %lld pair slots",
+            "chunk %lld pair slots, %d intermediate cop%s",
             (unsigned long long)p.token, (long long)B, (long long)N, (long long)d, order, ndims,
             io_dtype, spec_dtype, p.circular, kPathName[p.path], (long long)p.M, (long long)p.M1,
             (long long)p.M2, (long long)p.P1, (long long)p.P2, (long long)p.P3, p.spectrum_bytes,
-            p.workspace_bytes, (long long)p.chunk_pairs);
+            p.workspace_bytes, (long long)p.chunk_pairs, p.inter_copies,
+            p.inter_copies == 1 ? "y" : "ies");
     return HYENA_OK;
 }
 

@@ -98,7 +98,11 @@ struct Plan {
     size_t spectrum_bytes = 0;
     size_t tw_bytes = 0;
     size_t inter_offset = 0;  // workspace offset of the intermediate buffer
-    size_t inter_bytes = 0;
+    size_t inter_bytes = 0;   // one copy of it (F, and F2 on 3D grids)
+    // copies of the intermediate buffer: 2 when the chain walks two or more
+    // chunks, which then alternate between the caller's stream and a second
+    // one (copy i % 2 for chunk i), so passes of neighbouring chunks overlap
+    int32_t inter_copies = 1;
     size_t workspace_bytes = 0;
 
     // identifies the plan in the workspace record (unique in the process)

@@ -33,7 +33,8 @@ static void check_layout(const hy::Plan& p)
         CHECK(p.seg[s].off >= 0);
         CHECK(p.seg[s].off + (int64_t)(p.seg[s].radix - 1) * p.seg[s].ns <= p.tw_elems);
     }
-    CHECK(p.inter_offset + p.inter_bytes <= p.workspace_bytes);
+    CHECK(p.inter_copies == 1 || p.inter_copies == 2);
+    CHECK(p.inter_offset + (size_t)p.inter_copies * p.inter_bytes <= p.workspace_bytes);
     CHECK(p.stage_offset + p.stage_bytes <= p.workspace_bytes || p.stage_bytes == 0);
     CHECK(p.spectrum_bytes > 0);
     if (p.path == HYENA_PATH_FOURSTEP1D || p.path == HYENA_PATH_ROWCOL2D) {

@@ -109,16 +109,18 @@ def test_2d_plan_sizes():
     hyena.hyena_plan_destroy(plan)
 
 
-@pytest.mark.parametrize("B,d,slots", [(1, 768, 192), (1, 32, 16), (3, 64, 96), (8, 768, 192)])
-def test_fourstep_workspace_holds_one_chunk(B, d, slots):
+@pytest.mark.parametrize("B,d,slots,copies", [(1, 768, 192, 2), (1, 32, 16, 1), (3, 64, 96, 1),
+                                               (8, 768, 192, 2)])
+def test_fourstep_workspace_holds_one_chunk_per_stream(B, d, slots, copies):
     # the 64K-token chain walks its channel pairs in chunks of about 192 MiB
     # of intermediate (1 MiB per pair slot of a 131072-point transform), in
-    # whole groups of 16 pairs: the workspace holds one chunk, never the
-    # whole intermediate of a wide plan
+    # whole groups of 16 pairs; with two or more chunks they alternate
+    # between two streams, each with its own copy: the workspace holds one
+    # or two chunks, never the whole intermediate of a wide plan
     _, plan = hyena.hyena_plan_create(B, 65536, d, 2, [65536])
     _, ws, p = hyena.hyena_plan_query(plan)
     assert p == hyena.HYENA_PATH_FOURSTEP1D
-    inter = slots * 131072 * 8
+    inter = copies * slots * 131072 * 8
     assert inter <= ws < inter + (8 << 20)  # plus the twiddle tables
     hyena.hyena_plan_destroy(plan)
 

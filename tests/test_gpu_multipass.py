@@ -414,3 +414,67 @@ def test_periodic_four_step(N, d, B, order, dtype):
         for n in range(order):
             for c in range(d):
                 assert rel_err(nat[n, c], oracle.fft(h[n, c])[:N // 2 + 1]) < 2e-6
+
+
+@pytest.mark.parametrize("fresh_thread", [False, True])
+def test_two_chunk_forward_in_a_hip_graph(fresh_thread):
+    # A 64K-token plan whose channel pairs take two chunks (13 batch rows x 16
+    # pair slots against chunks of 192, the second one ragged): the odd chunk
+    # runs on the library's second stream with its own intermediate, forked
+    # from and joined to the caller's stream through events, which a graph
+    # capture records as dependencies.  Captured on a thread that has already
+    # run the plan eagerly (the second stream joins the graph) and on a fresh
+    # thread (no second stream yet: both chunks go on the captured stream).
+    # Every replay, with eager work and host waits between, equals the eager
+    # result bit for bit.
+    import threading
+
+    import torch
+    from gpu_util import from_torch, to_torch
+    from long_convolution_sequence_rfft_amd import hyena
+    inp = synth.make_1d(B=13, N=65536, d=32, order=2, alpha_range=(1e-6, 1e-4), dtype=synth.F32,
+                        seed=83)
+    y_eager, plan, H = run_gpu(inp)
+    assert plan.path == FOUR
+    assert plan.workspace_bytes >= 2 * 192 * (1 << 20)  # two copies of the intermediate
+    u = to_torch(inp.u, synth.F32)
+    gates = [to_torch(g, synth.F32) for g in inp.gates]
+    D = torch.from_numpy(inp.D).cuda()
+    y = torch.empty_like(u)
+    g = torch.cuda.CUDAGraph()
+
+    def capture():
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        if not fresh_thread:
+            with torch.cuda.stream(s):  # warm-up on the capture stream
+                plan.forward(u, gates, H, D, y)
+            torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            plan.forward(u, gates, H, D, y)
+        torch.cuda.synchronize()
+
+    say(f"[gpu] graph capture two-chunk four-step, fresh thread {fresh_thread}")
+    if fresh_thread:
+        err = []
+
+        def body():
+            try:
+                capture()
+            except Exception as e:  # re-raised on the test's thread
+                err.append(e)
+        t = threading.Thread(target=body)
+        t.start()
+        t.join()
+        if err:
+            raise err[0]
+    else:
+        capture()
+    for r in range(3):
+        y.fill_(0)
+        plan.forward(u, gates, H, D, torch.empty_like(u))  # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(from_torch(y, synth.F32), y_eager), f"replay {r}"
