@@ -387,6 +387,14 @@ def roofline_of(res):
                   "unit": "TFLOP/s", "frac": round(a_alu / ALU_PEAK_TFLOPS, 4)}
     out["algorithmic_per_launch"] = {"flops": per_launch_f, "bytes": per_launch_b}
     out["traffic"] = traffic
+    # Summed launch durations per forward over the wall time of the same
+    # (event-bracketed) forwards.  Above 1, launches overlap: chains of
+    # several chunks run them on two streams, and each launch's duration then
+    # includes the time it shares the GPU with the other stream's, so the
+    # fractions above understate the kernel's own rate.
+    if res.get("traced_ms_per_step"):
+        busy = sum(v["ms_per_forward"] for v in res["kernels"].values())
+        out["kernel_time_over_step_time"] = round(busy / res["traced_ms_per_step"], 3)
     return out
 
 

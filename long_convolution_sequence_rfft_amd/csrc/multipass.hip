@@ -49,12 +49,13 @@ struct Fork {
 };
 
 constexpr int kMaxForkDevices = 64;
+thread_local int t_single_stream = 0;  // SingleStreamScope depth
 
 hyena_status fork_begin(const Plan& p, hipStream_t s, Fork& f)
 {
     f.caller = s;
     f.ss = nullptr;
-    if (p.inter_copies < 2) return HYENA_OK;
+    if (p.inter_copies < 2 || t_single_stream > 0) return HYENA_OK;
     thread_local SideStream per_dev[kMaxForkDevices];
     int dev = 0;
     hipError_t e = s != nullptr ? hipStreamGetDevice(s, &dev) : hipGetDevice(&dev);
@@ -250,8 +251,7 @@ hyena_status mp_forward_chunks(const Plan& p, const void* u, const void* const* 
     g.pair_bytes = p.fwd_pair_bytes;
     for (int64_t g0 = 0, ci = 0; g0 < total_groups; g0 += chunk_groups, ++ci) {
         const hipStream_t s = fk.stream_of(ci);
-        float2* F = reinterpret_cast<float2*>(static_cast<char*>(ws) + p.inter_offset +
-                                              (size_t)fk.copy_of(ci) * p.inter_bytes);
+        float2* F = reinterpret_cast<float2*>(static_cast<char*>(ws) + p.fwd_offset[fk.copy_of(ci)]);
         g.group0 = g0;
         g.ngroups = total_groups - g0 < chunk_groups ? total_groups - g0 : chunk_groups;
         OuterArgs oa{};
@@ -521,9 +521,9 @@ hyena_status mp3_forward_chunks(const Plan& p, const void* u, const void* const*
     gi.pair_bytes = p.fwd_pair_bytes2;
     for (int64_t g0 = 0, ci = 0; g0 < total_groups; g0 += chunk_groups, ++ci) {
         const hipStream_t s = fk.stream_of(ci);
-        const size_t cp = (size_t)fk.copy_of(ci) * p.inter_bytes;
-        float2* F1 = reinterpret_cast<float2*>(static_cast<char*>(ws) + p.inter_offset + cp);
-        float2* F2 = reinterpret_cast<float2*>(static_cast<char*>(ws) + p.inter2_offset + cp);
+        const int cp = fk.copy_of(ci);
+        float2* F1 = reinterpret_cast<float2*>(static_cast<char*>(ws) + p.fwd_offset[cp]);
+        float2* F2 = reinterpret_cast<float2*>(static_cast<char*>(ws) + p.fwd2_offset[cp]);
         go.group0 = gi.group0 = g0;
         go.ngroups = gi.ngroups = total_groups - g0 < chunk_groups ? total_groups - g0 : chunk_groups;
         OuterArgs oa{};
@@ -687,6 +687,9 @@ hyena_status mp3_export(const Plan& p, const void* H, void* out, void* stream)
 }
 
 }  // namespace
+
+SingleStreamScope::SingleStreamScope() { ++t_single_stream; }
+SingleStreamScope::~SingleStreamScope() { --t_single_stream; }
 
 hyena_status launch_fourstep_forward(const Plan& p, const void* u, const void* const* gates,
                                      const void* H, const float* D, void* y, void* ws,

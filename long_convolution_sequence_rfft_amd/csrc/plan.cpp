@@ -366,11 +366,22 @@ hyena_status plan_build(Plan& p, int64_t B, int64_t N, int64_t d, int32_t order,
         p.stage_bytes = align_up((size_t)(p.order + 2) * (size_t)B * (size_t)N * (size_t)d *
                                      (io_dtype == HYENA_F32 ? 4u : 2u), 256);
     }
+    size_t inter_end = p.inter_offset + p.inter_bytes;
+    p.fwd_offset[0] = p.inter_offset;
+    p.fwd2_offset[0] = p.inter2_offset;
     if (p.chunk_pairs > 0) {
         const int64_t total_slots = p.B * ((p.npairs + 15) / 16) * 16;
-        if (total_slots > p.chunk_pairs) p.inter_copies = 2;
+        if (total_slots > p.chunk_pairs) {
+            // the second copy holds the chain's intermediates only
+            p.inter_copies = 2;
+            p.fwd_offset[1] = inter_end;
+            const size_t f1 = align_up((size_t)(p.chunk_pairs * p.fwd_pair_bytes), 256);
+            p.fwd2_offset[1] = p.fwd_offset[1] + f1;
+            inter_end = p.fwd2_offset[1] +
+                        align_up((size_t)(p.chunk_pairs * p.fwd_pair_bytes2), 256);
+        }
     }
-    p.workspace_bytes = p.inter_offset + (size_t)p.inter_copies * p.inter_bytes + p.stage_bytes;
+    p.workspace_bytes = inter_end + p.stage_bytes;
     static const char* kPathName[] = {"AUTO", "LDS1D", "FOURSTEP1D", "ROWCOL2D", "ROWCOL3D"};
     log_msg("plan %llu: B=%lld N=%lld d=%lld order=%d ndims=%d io=%d spectrum=%d circular=%d -> "
             "path %s, M=%lld (M1=%lld M2=%lld P=%lldx%lldx%lld), spectrum %zu B, workspace %zu B, "

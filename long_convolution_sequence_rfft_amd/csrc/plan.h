@@ -19,12 +19,14 @@ constexpr int kMaxTwSegments = 12;
 constexpr int64_t kLdsMaxM = 16384;       // largest transform held in one workgroup's LDS
 constexpr int64_t kFourStepMaxM = 1 << 22;  // largest 1D transform (N = 2097152): 1024 x 4096
 // Multi-pass paths walk the channel pairs in chunks whose intermediate is
-// about this large: fewer, larger chunks mean fewer launches and partial last
-// waves, while the intermediate still mostly fits the 256 MB last-level cache
-// between passes (measured at 48, 96, 160, 192, 256 and 384 MiB; 192 was best
-// at 64K tokens and on the 256 x 256 grid).
+// about this large (at least 16 pairs).  Chains of two or more chunks run
+// them on two streams, so two chunks' intermediates are live at a time:
+// 64 MiB each (128 MiB together) measured fastest at 64K tokens (32, 48, 64,
+// 80, 96, 128, 192, 256 MiB: 1245, 1206, 1202-1212, 1251-1258, 1240-1256,
+// 1285-1294, 1270-1304, 1302-1304 us) and on the 256 x 256 grid (523-530
+// us against 545-557 at 96 and 192 MiB).
 #ifndef HY_CHUNK_MIB
-#define HY_CHUNK_MIB 192
+#define HY_CHUNK_MIB 64
 #endif
 constexpr int64_t kChunkBytes = (int64_t)HY_CHUNK_MIB << 20;
 
@@ -98,11 +100,16 @@ struct Plan {
     size_t spectrum_bytes = 0;
     size_t tw_bytes = 0;
     size_t inter_offset = 0;  // workspace offset of the intermediate buffer
-    size_t inter_bytes = 0;   // one copy of it (F, and F2 on 3D grids)
-    // copies of the intermediate buffer: 2 when the chain walks two or more
-    // chunks, which then alternate between the caller's stream and a second
-    // one (copy i % 2 for chunk i), so passes of neighbouring chunks overlap
+    size_t inter_bytes = 0;   // its size (F, and F2 on 3D grids; chain and spectrum)
+    // copies of the intermediate for the forward chain: 2 when the chain
+    // walks two or more chunks, which then alternate between the caller's
+    // stream and a second one (copy i % 2 for chunk i), so passes of
+    // neighbouring chunks overlap.  Copy 0 is the buffer above; copy 1, sized
+    // for the chain alone, follows it.  fwd_offset / fwd2_offset: F (F1) and
+    // F2 of each copy.
     int32_t inter_copies = 1;
+    size_t fwd_offset[2] = {0, 0};
+    size_t fwd2_offset[2] = {0, 0};
     size_t workspace_bytes = 0;
 
     // identifies the plan in the workspace record (unique in the process)
@@ -144,6 +151,13 @@ size_t ws_record_count();
 // allocation-free hyena_forward_noalloc (static_scratch.hip).
 hyena_status check_forward_args(const Plan& p, const void* u, const void* const* gates,
                                 const void* H, const float* D, const void* y, const void* ws);
+// While one of these lives on a thread, the multi-pass chains run every
+// chunk on the caller's stream and create no stream or event (for the
+// allocation-free entry point).
+struct SingleStreamScope {
+    SingleStreamScope();
+    ~SingleStreamScope();
+};
 hyena_status run_forward(const Plan& p, const void* u, const void* const* gates, const void* H,
                          const float* D, void* y, void* ws, void* stream);
 const Plan* plan_of(hyena_plan_t plan);

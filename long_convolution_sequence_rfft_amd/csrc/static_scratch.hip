@@ -93,5 +93,8 @@ extern "C" hyena_status hyena_forward_noalloc(hyena_plan_t plan, const void* u,
         if (st != HYENA_OK) return st;
         hy::ws_record_init(ws, p.workspace_bytes, p.token);
     }
+    // one stream only: a chain of several chunks would otherwise create the
+    // library's second stream on first use
+    hy::SingleStreamScope one_stream;
     return hy::run_forward(p, u, gates, H, D, y, ws, stream);
 }

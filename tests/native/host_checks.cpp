@@ -34,7 +34,15 @@ static void check_layout(const hy::Plan& p)
         CHECK(p.seg[s].off + (int64_t)(p.seg[s].radix - 1) * p.seg[s].ns <= p.tw_elems);
     }
     CHECK(p.inter_copies == 1 || p.inter_copies == 2);
-    CHECK(p.inter_offset + (size_t)p.inter_copies * p.inter_bytes <= p.workspace_bytes);
+    CHECK(p.inter_offset + p.inter_bytes <= p.workspace_bytes);
+    if (p.inter_copies == 2) {
+        // the chain's second copy lies after the first and inside the workspace
+        CHECK(p.fwd_offset[0] == p.inter_offset);
+        CHECK(p.fwd_offset[1] >= p.inter_offset + p.inter_bytes);
+        CHECK(p.fwd_offset[1] + (size_t)(p.chunk_pairs * p.fwd_pair_bytes) <= p.fwd2_offset[1]);
+        CHECK(p.fwd2_offset[1] + (size_t)(p.chunk_pairs * p.fwd_pair_bytes2) <= p.workspace_bytes);
+        CHECK(p.fwd_offset[1] + (size_t)(p.chunk_pairs * p.fwd_pair_bytes) <= p.workspace_bytes);
+    }
     CHECK(p.stage_offset + p.stage_bytes <= p.workspace_bytes || p.stage_bytes == 0);
     CHECK(p.spectrum_bytes > 0);
     if (p.path == HYENA_PATH_FOURSTEP1D || p.path == HYENA_PATH_ROWCOL2D) {
@@ -93,6 +101,23 @@ static void plans()
                 }
             }
         }
+    // chains that walk several chunks keep two copies of the intermediate
+    {
+        const int64_t d1[1] = {65536}, d2[2] = {512, 512}, d3[3] = {64, 64, 64};
+        hy::Plan a, b, c, e;
+        CHECK(hy::plan_build(a, 1, 65536, 768, 2, d1, 1, HYENA_F32, HYENA_F32, 0, 0) == HYENA_OK);
+        CHECK(hy::plan_build(b, 3, 512 * 512, 34, 2, d2, 2, HYENA_F32, HYENA_F32, 0, 0) == HYENA_OK);
+        CHECK(hy::plan_build(c, 2, 64 * 64 * 64, 32, 2, d3, 3, HYENA_F32, HYENA_F32, 0, 0) ==
+              HYENA_OK);
+        CHECK(hy::plan_build(e, 1, 65536, 32, 2, d1, 1, HYENA_F32, HYENA_F32, 0, 0) == HYENA_OK);
+        for (const hy::Plan* q : {&a, &b, &c}) {
+            check_layout(*q);
+            CHECK(q->inter_copies == 2);
+        }
+        check_layout(e);
+        CHECK(e.inter_copies == 1);  // 16 pair slots: one chunk
+        ok += 4;
+    }
     // null dims, bad ndims
     hy::Plan p;
     CHECK(hy::plan_build(p, 1, 8, 1, 1, nullptr, 1, 0, 0, 0, 0) == HYENA_ERR_INVALID_ARGUMENT);

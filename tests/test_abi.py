@@ -109,10 +109,10 @@ def test_2d_plan_sizes():
     hyena.hyena_plan_destroy(plan)
 
 
-@pytest.mark.parametrize("B,d,slots,copies", [(1, 768, 192, 2), (1, 32, 16, 1), (3, 64, 96, 1),
-                                               (8, 768, 192, 2)])
+@pytest.mark.parametrize("B,d,slots,copies", [(1, 768, 64, 2), (1, 32, 16, 1), (2, 64, 64, 1),
+                                               (3, 64, 64, 2), (8, 768, 64, 2)])
 def test_fourstep_workspace_holds_one_chunk_per_stream(B, d, slots, copies):
-    # the 64K-token chain walks its channel pairs in chunks of about 192 MiB
+    # the 64K-token chain walks its channel pairs in chunks of about 64 MiB
     # of intermediate (1 MiB per pair slot of a 131072-point transform), in
     # whole groups of 16 pairs; with two or more chunks they alternate
     # between two streams, each with its own copy: the workspace holds one

@@ -93,3 +93,16 @@ def test_host_info_fields():
     info = bench.host_info()
     assert info["host_cpus_available"] >= 1
     assert set(info) == {"host_cpus_available", "cpu_model", "omp_num_threads_env"}
+
+
+def test_roofline_reports_kernel_overlap():
+    # two launches of 0.6 ms each per 1.0 ms forward: the kernels overlap
+    cfg = WORKLOADS[3]
+    a = "hy::hyena_mp_inner<256, float, 0, false>"
+    b = "hy::hyena_mp_outer<512, float, 1, true, true>"
+    res = {"cfg": cfg, "workload": "no-such-workload", "traced_ms_per_step": 1.0,
+           "kernels": {a: {"launches_per_forward": 1.0, "avg_launch_ms": 0.6, "ms_per_forward": 0.6},
+                       b: {"launches_per_forward": 1.0, "avg_launch_ms": 0.6, "ms_per_forward": 0.6}}}
+    assert bench.roofline_of(res)["kernel_time_over_step_time"] == 1.2
+    del res["traced_ms_per_step"]
+    assert "kernel_time_over_step_time" not in bench.roofline_of(res)

@@ -126,8 +126,9 @@ def test_multipass_deterministic_bitwise():
 
 def test_rowcol2d_several_chunks():
     # 512 x 512 grid, 3 batch rows of 17 channel pairs: 96 pair slots against
-    # chunks of 48 (192 MiB of 4 MiB intermediates), so the chain walks two
-    # chunks; sampled channels against the oracle
+    # chunks of 16 (64 MiB of 4 MiB intermediates), so the chain walks six
+    # chunks, alternating between two streams; sampled channels against the
+    # oracle
     inp = synth.make_2d(B=3, X=512, Y=512, d=34, order=2, sigma_range=(8.0, 64.0), seed=41)
     y, plan, _ = run_gpu(inp)
     ch = np.array([0, 1, 16, 33])
@@ -417,10 +418,10 @@ def test_periodic_four_step(N, d, B, order, dtype):
 
 
 @pytest.mark.parametrize("fresh_thread", [False, True])
-def test_two_chunk_forward_in_a_hip_graph(fresh_thread):
-    # A 64K-token plan whose channel pairs take two chunks (13 batch rows x 16
-    # pair slots against chunks of 192, the second one ragged): the odd chunk
-    # runs on the library's second stream with its own intermediate, forked
+def test_multi_chunk_forward_in_a_hip_graph(fresh_thread):
+    # A 64K-token plan whose channel pairs take several chunks (13 batch rows
+    # x 16 pair slots against chunks of 64, the last one ragged): the odd
+    # chunks run on the library's second stream with their own intermediate, forked
     # from and joined to the caller's stream through events, which a graph
     # capture records as dependencies.  Captured on a thread that has already
     # run the plan eagerly (the second stream joins the graph) and on a fresh
@@ -436,7 +437,7 @@ def test_two_chunk_forward_in_a_hip_graph(fresh_thread):
                         seed=83)
     y_eager, plan, H = run_gpu(inp)
     assert plan.path == FOUR
-    assert plan.workspace_bytes >= 2 * 192 * (1 << 20)  # two copies of the intermediate
+    assert plan.workspace_bytes >= 2 * 64 * (1 << 20)  # two copies of the intermediate
     u = to_torch(inp.u, synth.F32)
     gates = [to_torch(g, synth.F32) for g in inp.gates]
     D = torch.from_numpy(inp.D).cuda()
@@ -455,7 +456,7 @@ def test_two_chunk_forward_in_a_hip_graph(fresh_thread):
             plan.forward(u, gates, H, D, y)
         torch.cuda.synchronize()
 
-    say(f"[gpu] graph capture two-chunk four-step, fresh thread {fresh_thread}")
+    say(f"[gpu] graph capture multi-chunk four-step, fresh thread {fresh_thread}")
     if fresh_thread:
         err = []
 
