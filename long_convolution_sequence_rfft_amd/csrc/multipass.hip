@@ -292,10 +292,14 @@ hyena_status mp_forward(const Plan& p, const void* u, const void* const* gates, 
 
 // imp != nullptr: the taps are evaluated from an implicit filter's hidden
 // features (four-step path) instead of read from h.
-hyena_status mp_spectrum(const Plan& p, const void* h, void* H, void* ws, void* stream,
-                         const ImpOuter* imp = nullptr)
+// The filter spectrum walks the same chunks over the whole intermediate
+// area of the workspace (every copy the forward chain uses).  With two
+// copies it splits the area in two and alternates chunks between the two
+// streams, as the chain does, when each half holds at least one group of
+// the spectrum's (larger) rows.
+hyena_status mp_spectrum_chunks(const Plan& p, const void* h, void* H, void* ws, const Fork& fk,
+                                size_t region, const ImpOuter* imp)
 {
-    const hipStream_t s = (hipStream_t)stream;
     MpGeom g = base_geom(p);
     g.B = 1;  // filters have no batch axis
     const int KP = 1 << g.kp_log2;
@@ -304,15 +308,18 @@ hyena_status mp_spectrum(const Plan& p, const void* h, void* H, void* ws, void* 
     const int64_t col_blocks = (g.Lb + C - 1) / C;
     const int64_t unit_blocks = (g.La / 2 + U - 1) / U;
     const int64_t total_groups = g.groups_per_b;
-    int64_t chunk_groups = (int64_t)(p.inter_bytes / (size_t)(p.spec_pair_bytes * KP));
-    if (chunk_groups < 1) chunk_groups = 1;
-    float2* F = reinterpret_cast<float2*>(static_cast<char*>(ws) + p.inter_offset);
+    int64_t chunk_groups = (int64_t)(region / (size_t)(p.spec_pair_bytes * KP));
+    if (chunk_groups < 1) chunk_groups = 1;  // the plan sizes copy 0 for one group at least
     const float2* tw = static_cast<const float2*>(ws);
     const size_t esz = p.spec_dtype == HYENA_F32 ? 4 : 2;
     const int64_t taps = p.ndims == 1 ? p.N : (2 * p.X - 1) * (2 * p.Y - 1);
     g.pair_bytes = p.spec_pair_bytes;
+    int64_t ci = 0;
     for (int n = 0; n < p.order; ++n) {
-        for (int64_t g0 = 0; g0 < total_groups; g0 += chunk_groups) {
+        for (int64_t g0 = 0; g0 < total_groups; g0 += chunk_groups, ++ci) {
+            const hipStream_t s = fk.stream_of(ci);
+            float2* F = reinterpret_cast<float2*>(static_cast<char*>(ws) + p.inter_offset +
+                                                  (size_t)fk.copy_of(ci) * region);
             g.group0 = g0;
             g.ngroups = total_groups - g0 < chunk_groups ? total_groups - g0 : chunk_groups;
             OuterArgs oa{};
@@ -338,6 +345,24 @@ hyena_status mp_spectrum(const Plan& p, const void* h, void* H, void* ws, void* 
         }
     }
     return HYENA_OK;
+}
+
+hyena_status mp_spectrum(const Plan& p, const void* h, void* H, void* ws, void* stream,
+                         const ImpOuter* imp = nullptr)
+{
+    // the intermediate area: copy 0 and the chain's further copies after it
+    const size_t area = p.workspace_bytes - p.stage_bytes - p.inter_offset;
+    const int KP = 1 << base_geom(p).kp_log2;
+    const size_t group = (size_t)p.spec_pair_bytes * (size_t)KP;
+    Fork fk;
+    if (p.inter_copies == 2 && area / 2 / 256 * 256 >= group) {
+        const hyena_status st = fork_begin(p, (hipStream_t)stream, fk);
+        if (st != HYENA_OK) return st;
+    } else {
+        fk.caller = (hipStream_t)stream;
+    }
+    const size_t region = fk.ss ? area / 2 / 256 * 256 : area;
+    return fork_end(fk, mp_spectrum_chunks(p, h, H, ws, fk, region, imp));
 }
 
 // One thread per entry (n, pair, unit kk, e); writes natural-order unscaled
