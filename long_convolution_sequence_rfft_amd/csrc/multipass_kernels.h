@@ -495,20 +495,28 @@ __global__ void __launch_bounds__(kMpThreads, 2) hyena_mp_outer(OuterArgs a)
     // index -> (pair kp', outer sample s, column c'); KP consecutive lanes
     // cover one row's KP channel pairs (one cache line for KP = 16 f32).
     // Half hf of the column: samples s in [hf LA/2, (hf + 1) LA/2).
+    // A thread's pair slot is the same in every element (KP divides the
+    // thread count), so each call works it out once, outside the element
+    // loop -- except in the 3D mixer modes, whose short convolutions leave
+    // too few registers for it (they spill that way) and which recompute it
+    // per element.
+    constexpr bool SLOT_PER_ELEMENT = MODE == OUTER_IN3 || MODE == OUTER_OUT3;
     auto tile_rows_half = [&](int hf, auto&& fn) {
         constexpr int total = (LA / 2) * NF;  // = (LA/2) C KP
-        static_assert(total % kMpThreads == 0, "tile split");
+        static_assert(total % kMpThreads == 0 && kMpThreads % 16 == 0, "tile split");
+        const int kq_t = (int)threadIdx.x & (KP - 1);
+        int64_t bq_t = 0, pq_t = 0;
+        bool lq_t = false;
+        if constexpr (!SLOT_PER_ELEMENT) pair_of_slot(g, group, kq_t, bq_t, pq_t, lq_t);
 #pragma unroll
         for (int it = 0; it < total / kMpThreads; ++it) {
-            const int idx = (int)threadIdx.x + it * kMpThreads;
-            const int kq = idx & (KP - 1);
-            const int rest = idx >> g.kp_log2;
+            const int rest = ((int)threadIdx.x >> g.kp_log2) + it * (kMpThreads >> g.kp_log2);
             const int s = hf * (LA / 2) + rest % (LA / 2);
             const int cq = rest / (LA / 2);
-            const int fq = cq * KP + kq;
-            int64_t bq, pq;
-            bool lq;
-            pair_of_slot(g, group, kq, bq, pq, lq);
+            const int fq = cq * KP + kq_t;
+            int64_t bq = bq_t, pq = pq_t;
+            bool lq = lq_t;
+            if constexpr (SLOT_PER_ELEMENT) pair_of_slot(g, group, kq_t, bq, pq, lq);
             const int oq = cb * C + cq;
             const int64_t t = g.sa * s + g.so * (int64_t)oq;
             fn(it, fq, s, pq, lq && oq < n_outer && t < g.N, bq * g.N + t);
