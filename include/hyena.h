@@ -113,7 +113,10 @@ typedef enum hyena_path {
 } hyena_path;
 
 /*
- * Create a plan.  B >= 1 batch rows, d >= 1 channels, 1 <= order <= 8.
+ * Create a plan ("Hyena -- Long Convolutions Math", sections "The
+ * primitive" and "Linear vs circular": zero-padded causal convolutions;
+ * "How HyenaND works", section "2. The convolution theorem (FFT)": 2D and 3D
+ * grids).  B >= 1 batch rows, d >= 1 channels, 1 <= order <= 8.
  * ndims = 1: dims = {N}, 4 <= N <= 2097152 (any N; M is the power of two
  *            >= 2N; N == the N argument).  M <= 16384 runs in one workgroup
  *            per channel (pair); longer transforms take the four-step path.
@@ -121,16 +124,18 @@ typedef enum hyena_path {
  *            X * Y (and N * d * 4 below 2^31).
  * ndims = 3: dims = {X, Y, Z}, powers of two in [4, 256], X * Y * Z <= 2^20;
  *            N must equal X * Y * Z.
- * io_dtype, spectrum_dtype: hyena_dtype values.  path: hyena_path value.
- * On success *plan receives a new plan (release with hyena_plan_destroy).
- * This call touches no GPU state.
+ * io_dtype, spectrum_dtype: hyena_dtype values.  The path is chosen
+ * automatically (HYENA_PATH_AUTO); hyena_plan_create_ex below takes a path
+ * and flags.  On success *plan receives a new plan (release with
+ * hyena_plan_destroy).  This call touches no GPU state.
  */
 hyena_status hyena_plan_create(hyena_plan_t* plan, int64_t B, int64_t N, int64_t d,
                                int32_t order, const int64_t* dims, int32_t ndims,
-                               int32_t io_dtype, int32_t spectrum_dtype, int32_t path);
+                               int32_t io_dtype, int32_t spectrum_dtype);
 
 /*
- * hyena_plan_create with flags.  HYENA_FLAG_CIRCULAR: periodic boundary,
+ * hyena_plan_create with a path (hyena_path value; HYENA_PATH_AUTO as
+ * above) and flags.  HYENA_FLAG_CIRCULAR: periodic boundary,
  * the unpadded length-N circular convolution of "Hyena -- Long Convolutions
  * Math", section "Linear vs circular" as the operator:
  *   z_n[b,t,c] = gate_n[b,t,c] * ( sum_{s=0}^{N-1} h_n[c,s] z_{n-1}[b,(t-s) mod N,c]
@@ -146,10 +151,13 @@ hyena_status hyena_plan_create_ex(hyena_plan_t* plan, int64_t B, int64_t N, int6
                                   int32_t io_dtype, int32_t spectrum_dtype, int32_t path,
                                   int32_t flags);
 
-/* Sizes in bytes of the spectrum buffer H and of the workspace, and the path
- * the plan resolved to (any output pointer may be NULL). */
+/* Sizes in bytes of the spectrum buffer H and of the workspace (either
+ * output pointer may be NULL). */
 hyena_status hyena_plan_query(hyena_plan_t plan, size_t* spectrum_bytes,
-                              size_t* workspace_bytes, int32_t* path);
+                              size_t* workspace_bytes);
+
+/* The path (hyena_path value) the plan resolved to. */
+hyena_status hyena_plan_path(hyena_plan_t plan, int32_t* path);
 
 /* Write the plan's twiddle tables into a caller-allocated workspace of at
  * least workspace_bytes (16-byte aligned).  Required once per (plan,

@@ -80,19 +80,25 @@ hyena_status hyena_plan_create_ex(hyena_plan_t* plan, int64_t B, int64_t N, int6
 
 hyena_status hyena_plan_create(hyena_plan_t* plan, int64_t B, int64_t N, int64_t d,
                                int32_t order, const int64_t* dims, int32_t ndims,
-                               int32_t io_dtype, int32_t spectrum_dtype, int32_t path)
+                               int32_t io_dtype, int32_t spectrum_dtype)
 {
-    return hyena_plan_create_ex(plan, B, N, d, order, dims, ndims, io_dtype, spectrum_dtype, path,
-                                0);
+    return hyena_plan_create_ex(plan, B, N, d, order, dims, ndims, io_dtype, spectrum_dtype,
+                                HYENA_PATH_AUTO, 0);
 }
 
-hyena_status hyena_plan_query(hyena_plan_t plan, size_t* spectrum_bytes, size_t* workspace_bytes,
-                              int32_t* path)
+hyena_status hyena_plan_query(hyena_plan_t plan, size_t* spectrum_bytes, size_t* workspace_bytes)
 {
     if (plan == nullptr) return fail(HYENA_ERR_INVALID_ARGUMENT, "plan is NULL");
     if (spectrum_bytes) *spectrum_bytes = plan->p.spectrum_bytes;
     if (workspace_bytes) *workspace_bytes = plan->p.workspace_bytes;
-    if (path) *path = plan->p.path;
+    return HYENA_OK;
+}
+
+hyena_status hyena_plan_path(hyena_plan_t plan, int32_t* path)
+{
+    if (plan == nullptr) return fail(HYENA_ERR_INVALID_ARGUMENT, "plan is NULL");
+    if (path == nullptr) return fail(HYENA_ERR_INVALID_ARGUMENT, "path is NULL");
+    *path = plan->p.path;
     return HYENA_OK;
 }
 

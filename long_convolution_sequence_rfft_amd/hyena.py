@@ -38,6 +38,7 @@ EXPORTED_SYMBOLS = (
     "hyena_last_error", "hyena_timing_begin", "hyena_timing_end", "hyena_timing_kernel",
     "hyena_timing_release", "hyena_implicit_scratch_bytes", "hyena_filter_spectrum_implicit",
     "hyena_plan_create_ex", "hyena_nd_mixer_forward", "hyena_workspace_release",
+    "hyena_plan_path",
     "hyena_forward_noalloc",
 )
 
@@ -82,11 +83,11 @@ def load():
             lib = ctypes.CDLL(LIB_PATH)
             i64, i32, p, sz = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t
             lib.hyena_plan_create.argtypes = [ctypes.POINTER(p), i64, i64, i64, i32,
-                                              ctypes.POINTER(i64), i32, i32, i32, i32]
+                                              ctypes.POINTER(i64), i32, i32, i32]
             lib.hyena_plan_create_ex.argtypes = [ctypes.POINTER(p), i64, i64, i64, i32,
                                                  ctypes.POINTER(i64), i32, i32, i32, i32, i32]
-            lib.hyena_plan_query.argtypes = [p, ctypes.POINTER(sz), ctypes.POINTER(sz),
-                                             ctypes.POINTER(i32)]
+            lib.hyena_plan_query.argtypes = [p, ctypes.POINTER(sz), ctypes.POINTER(sz)]
+            lib.hyena_plan_path.argtypes = [p, ctypes.POINTER(i32)]
             lib.hyena_workspace_init.argtypes = [p, p, p]
             lib.hyena_workspace_release.argtypes = [p, p]
             lib.hyena_filter_spectrum.argtypes = [p, p, p, p, p]
@@ -109,6 +110,7 @@ def load():
             lib.hyena_filter_spectrum_implicit.argtypes = [p, ctypes.POINTER(ImplicitFilter), p, p,
                                                            p, p]
             for name in ("hyena_plan_create", "hyena_plan_create_ex", "hyena_plan_query",
+                         "hyena_plan_path",
                          "hyena_workspace_init", "hyena_workspace_release",
                          "hyena_filter_spectrum", "hyena_forward", "hyena_forward_noalloc",
                          "hyena_spectrum_export",
@@ -144,19 +146,20 @@ def _check(status: int, where: str):
 
 def hyena_plan_create(B, N, d, order, dims, io_dtype=HYENA_F32, spectrum_dtype=None,
                       path=HYENA_PATH_AUTO, check=True, flags=0):
-    """Returns (status, plan handle or None); flags go through hyena_plan_create_ex."""
+    """Returns (status, plan handle or None); a path other than AUTO, or flags,
+    go through hyena_plan_create_ex."""
     lib = load()
     if spectrum_dtype is None:
         spectrum_dtype = HYENA_F32 if io_dtype == HYENA_F16 else io_dtype
     dims_arr = (ctypes.c_int64 * max(1, len(dims)))(*[int(x) for x in dims])
     h = ctypes.c_void_p()
-    if flags:
+    if flags or path != HYENA_PATH_AUTO:
         st = lib.hyena_plan_create_ex(ctypes.byref(h), int(B), int(N), int(d), int(order),
                                       dims_arr, len(dims), int(io_dtype), int(spectrum_dtype),
                                       int(path), int(flags))
     else:
         st = lib.hyena_plan_create(ctypes.byref(h), int(B), int(N), int(d), int(order), dims_arr,
-                                   len(dims), int(io_dtype), int(spectrum_dtype), int(path))
+                                   len(dims), int(io_dtype), int(spectrum_dtype))
     if check:
         _check(st, "hyena_plan_create")
     return st, (h.value if st == HYENA_OK else None)
@@ -166,8 +169,8 @@ def hyena_plan_query(plan):
     spec = ctypes.c_size_t()
     ws = ctypes.c_size_t()
     path = ctypes.c_int32()
-    _check(load().hyena_plan_query(plan, ctypes.byref(spec), ctypes.byref(ws), ctypes.byref(path)),
-           "hyena_plan_query")
+    _check(load().hyena_plan_query(plan, ctypes.byref(spec), ctypes.byref(ws)), "hyena_plan_query")
+    _check(load().hyena_plan_path(plan, ctypes.byref(path)), "hyena_plan_path")
     return spec.value, ws.value, path.value
 
 

@@ -83,7 +83,7 @@ def test_plan_create_rejects(args, code):
 def test_plan_create_null_output_pointer():
     lib = hyena.load()
     dims = (ctypes.c_int64 * 1)(8)
-    assert lib.hyena_plan_create(None, 1, 8, 2, 1, dims, 1, 0, 0, 0) == \
+    assert lib.hyena_plan_create(None, 1, 8, 2, 1, dims, 1, 0, 0) == \
         hyena.HYENA_ERR_INVALID_ARGUMENT
 
 
@@ -361,3 +361,23 @@ def test_2d_plans_up_to_1024_sides():
             assert spec == 2 * ((d + 1) // 2) * (2 * X * 2 * Y // 2) * 16
         finally:
             hyena.hyena_plan_destroy(p)
+
+
+def test_plan_create_has_the_boundary_signature_and_path_is_queried_apart():
+    # hyena_plan_create(plan, B, N, d, order, dims, ndims, io_dtype, spectrum_dtype) picks the
+    # path itself; hyena_plan_path reports it, and rejects a NULL output
+    lib = hyena.load()
+    dims = (ctypes.c_int64 * 1)(65536)
+    h = ctypes.c_void_p()
+    assert lib.hyena_plan_create(ctypes.byref(h), 1, 65536, 4, 2, dims, 1, 0, 0) == hyena.HYENA_OK
+    try:
+        spec, ws = ctypes.c_size_t(), ctypes.c_size_t()
+        assert lib.hyena_plan_query(h, ctypes.byref(spec), ctypes.byref(ws)) == hyena.HYENA_OK
+        assert spec.value > 0 and ws.value > 0
+        path = ctypes.c_int32(-1)
+        assert lib.hyena_plan_path(h, ctypes.byref(path)) == hyena.HYENA_OK
+        assert path.value == hyena.HYENA_PATH_FOURSTEP1D
+        assert lib.hyena_plan_path(h, None) == hyena.HYENA_ERR_INVALID_ARGUMENT
+        assert lib.hyena_plan_path(None, ctypes.byref(path)) == hyena.HYENA_ERR_INVALID_ARGUMENT
+    finally:
+        lib.hyena_plan_destroy(h)
