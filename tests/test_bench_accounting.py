@@ -31,7 +31,7 @@ def _split(cfg, kernels):
     (1, ["hy::hyena_lds1d_real_forward<2048, float, float, false>",
          "hy::hyena_stage<float, true, false>", "hy::hyena_stage<float, false, true>"]),
     (2, ["hy::hyena_lds1d_real_forward<8192, unsigned short, unsigned short, false>",
-         "hy::hyena_stage_bf16<true>", "hy::hyena_stage_bf16<false>"]),
+         "hy::hyena_stage16_full<true>", "hy::hyena_stage16_full<false>"]),
     (3, ["hy::hyena_mp_outer<512, float, 0, true, true>", "hy::hyena_mp_outer<512, float, 1, true, true>",
          "hy::hyena_mp_outer<512, float, 2, true, true>", "hy::hyena_mp_inner<256, float, 0, false>"]),
     (4, ["hy::hyena_mp_outer<512, float, 0, true, true>", "hy::hyena_mp_outer<512, float, 1, true, true>",
