@@ -303,3 +303,23 @@ def test_bf16_spectrum_is_rounded_to_nearest_even(kind, dims):
     H16 = p16.spectrum(h).cpu().numpy().view(np.uint16)
     assert H32.size == H16.size
     assert np.array_equal(synth.f32_to_bf16_bits(H32), H16)
+
+
+@pytest.mark.parametrize("B,N,d,order,dtype", [
+    (3, 128, 64, 2, synth.BF16),    # one 16-bit tile per (b, tensor)
+    (1, 256, 128, 3, synth.F16),    # two channel blocks, 16-bit
+    (2, 512, 32, 2, synth.F32),     # one float32 channel block
+    (1, 1024, 96, 1, synth.F32),    # three float32 channel blocks
+    (2, 4096, 192, 2, synth.BF16),  # 32 sample blocks x 3 channel blocks
+])
+def test_full_tile_staging_shapes(B, N, d, order, dtype):
+    # N a multiple of 128 and d of 64 (16-bit) or 32 (float32): the staging
+    # transposes run in their full-tile form, on the smallest and on
+    # multi-block shapes
+    inp = synth.make_1d(B=B, N=N, d=d, order=order, alpha_range=(1e-3, 1e-2), dtype=dtype,
+                        seed=90 + N + d)
+    y, _, _ = run_gpu(inp)
+    ref = oracle_ref(inp, method=oracle.DIRECT if N <= 1024 else oracle.FFT)
+    e = rel_err(y, ref)
+    say(f"[gpu] full-tile staging B={B} N={N} d={d} order={order} {dtype}: rel err {e:.3e}")
+    assert e < {synth.F32: TOL_F32, synth.BF16: TOL_BF16, synth.F16: TOL_F16}[dtype]
