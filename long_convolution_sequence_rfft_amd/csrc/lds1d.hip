@@ -432,8 +432,8 @@ __global__ void __launch_bounds__(256) hyena_stage_bf16(StageArgs a)
 }
 
 // ---------------------------------------------------------------------------
-// 16-bit staging in full tiles (N a multiple of 128, d of 64), the form used
-// whenever the shape allows: one tile of 128 samples x 64 channels per
+// 16-bit staging in full tiles (N a multiple of 64, d of 64), the form used
+// whenever the shape allows: one tile of 64 samples x 64 channels per
 // workgroup.  Words move whole on both sides (two channels of one sample on
 // the row side, two samples of one channel on the run side); each is split
 // into its halves on the way into LDS and read back whole.  Global accesses
@@ -442,11 +442,11 @@ __global__ void __launch_bounds__(256) hyena_stage_bf16(StageArgs a)
 // of scalar instructions: 27 VALU instructions per wave against 568 for the
 // word-transposing form above (the LDS conflict rate is the same 40%).
 // Every offset stays below 2^31 for d below 2^22 (N <= 8192 here).
-// Measured at 8K tokens, bf16: stage-in 32.0 -> 30.0 us, stage-out 12.6 ->
-// 11.7 us; two or four tiles per workgroup (more in flight, fewer
-// workgroups per CU) were no faster.
+// Measured at 8K tokens, bf16: stage-in 32.0 -> 29.3 us, stage-out 12.6 ->
+// 11.3 us; tiles of 128 samples were 0.5 us slower each way, and two or four
+// of them per workgroup (more in flight, fewer workgroups per CU) no faster.
 // ---------------------------------------------------------------------------
-constexpr int kS16TT = kStageTT, kS16TC = 64;
+constexpr int kS16TT = 64, kS16TC = 64;
 
 __device__ __forceinline__ const char* uniform_ptr(const void* p)
 {
@@ -465,9 +465,9 @@ template <bool TO_COLS>
 __global__ void __launch_bounds__(256) hyena_stage16_full(StageArgs a)
 {
     constexpr int NT = 256, TT = kS16TT, TC = kS16TC, TW = TC / 2;
-    constexpr int PER = TT * TW / NT;   // 16 words per thread
+    constexpr int PER = TT * TW / NT;   // 8 words per thread
     constexpr int RROWS = NT / TW;      // 8 row-side samples per pass
-    constexpr int RCH = NT / (TT / 2);  // 4 run-side channels per pass
+    constexpr int RCH = NT / (TT / 2);  // 8 run-side channels per pass
     // TO_COLS: channel-major tile, channel c's samples at c * RSC (16-bit units);
     // back: sample-major tile, sample t's channels at t * RST
     constexpr int RSC = TT + 2, RST = TC + 2;

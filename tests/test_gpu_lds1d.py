@@ -306,14 +306,15 @@ def test_bf16_spectrum_is_rounded_to_nearest_even(kind, dims):
 
 
 @pytest.mark.parametrize("B,N,d,order,dtype", [
-    (3, 128, 64, 2, synth.BF16),    # one 16-bit tile per (b, tensor)
+    (2, 64, 64, 2, synth.F16),      # one 16-bit tile per (b, tensor)
+    (3, 128, 64, 2, synth.BF16),    # two 16-bit sample blocks
     (1, 256, 128, 3, synth.F16),    # two channel blocks, 16-bit
     (2, 512, 32, 2, synth.F32),     # one float32 channel block
     (1, 1024, 96, 1, synth.F32),    # three float32 channel blocks
     (2, 4096, 192, 2, synth.BF16),  # 32 sample blocks x 3 channel blocks
 ])
 def test_full_tile_staging_shapes(B, N, d, order, dtype):
-    # N a multiple of 128 and d of 64 (16-bit) or 32 (float32): the staging
+    # 16-bit: N and d multiples of 64; float32: N of 128, d of 32: the staging
     # transposes run in their full-tile form, on the smallest and on
     # multi-block shapes
     inp = synth.make_1d(B=B, N=N, d=d, order=order, alpha_range=(1e-3, 1e-2), dtype=dtype,
