@@ -138,6 +138,18 @@ def load_traffic(workload, kernel):
 # GPU timing
 # ---------------------------------------------------------------------------
 
+def hold_stream():
+    """Enqueue a short spin kernel on the current stream (outside any timed
+    region): while it runs the host enqueues the first forwards, so a timed
+    region that starts after it holds K forwards running back to back on the
+    GPU rather than also the host's latency to its first launch (the
+    blocking-kernel method of GPU benchmark harnesses).  The host enqueues a
+    forward in less time than the GPU runs one, so the GPU does not wait on it
+    later in the region."""
+    import torch
+    torch.cuda._sleep(1_000_000)
+
+
 def make_inputs(idx, seed):
     from long_convolution_sequence_rfft_amd import synth
     return synth.make_workload(idx, seed=seed)
@@ -224,10 +236,13 @@ def run_workload(idx, steps, warmup, min_rotation_bytes=600 << 20):
     # stream (torch's current stream, which the plan launches on).
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
+    hold_stream()
     start.record()
+    h0 = time.perf_counter()
     for i in range(steps):
         step(i)
     stop.record()
+    host_us = (time.perf_counter() - h0) * 1e6 / steps  # host time to enqueue one forward
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(stop)
     # The same `steps` forwards again with every kernel launch bracketed by
@@ -238,6 +253,7 @@ def run_workload(idx, steps, warmup, min_rotation_bytes=600 << 20):
     # consecutive steps (one marker per step; the whole-job time above stays
     # the clean region's).
     marks = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    hold_stream()
     marks[0].record()
     for i in range(steps):
         step(i)
@@ -251,6 +267,7 @@ def run_workload(idx, steps, warmup, min_rotation_bytes=600 << 20):
 
     hyena.hyena_timing_begin(steps * 64)
     start2, stop2 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    hold_stream()
     start2.record()
     for i in range(steps):
         step(i)
@@ -274,6 +291,7 @@ def run_workload(idx, steps, warmup, min_rotation_bytes=600 << 20):
         "spectrum": "bf16" if spec_dtype == hyena.HYENA_BF16 else "f32",
         "ms_per_step": ms,
         "step_ms_p10": pct(0.10), "step_ms_p50": pct(0.50), "step_ms_p90": pct(0.90),
+        "host_enqueue_us_per_step": round(host_us, 1),
         "tc_per_s": tc / (ms * 1e-3),
         "spectrum_ms": spectrum_ms,
         "implicit_spectrum_ms": implicit_ms,
