@@ -441,7 +441,7 @@ __global__ void __launch_bounds__(256) hyena_stage_bf16(StageArgs a)
 // offset per word and one lane offset, so a tile's addressing is a handful
 // of scalar instructions: 27 VALU instructions per wave against 568 for the
 // word-transposing form above (the LDS conflict rate is the same 40%).
-// Every offset stays below 2^31 for d below 2^22 (N <= 8192 here).
+// Every offset stays below 2^31 for d below 2^22 (N <= 16384 on this path).
 // Measured at 8K tokens, bf16: stage-in 32.0 -> 29.3 us, stage-out 12.6 ->
 // 11.3 us; tiles of 128 samples were 0.5 us slower each way, and two or four
 // of them per workgroup (more in flight, fewer workgroups per CU) no faster.
@@ -680,7 +680,7 @@ hyena_status stage_plan(const Plan& p, const StageArgs& a, int ntensors, bool to
 {
     StageArgs b = a;
     b.cols = p.d;
-    // full tiles: the forms with buffer accesses and conflict-free LDS
+    // full tiles: the forms with scalar-based buffer accesses
     if (p.io_dtype == HYENA_F32 && p.d % 32 == 0 && p.N % kStageTT == 0 && p.d < (int64_t(1) << 22))
         return stage32_full_launch(b, ntensors, to_cols, s);
     if (p.io_dtype == HYENA_F32) return stage_launch<float>(b, ntensors, to_cols, s);
